@@ -1,0 +1,194 @@
+"""CPU oracle for C = ReLU(A.B), fp16 in, fp32 accumulate, fp16 out.
+
+TEST INFRASTRUCTURE. Only the test suite, ``__graft_entry__.smoke()`` and the
+``cpu_baseline`` leg of ``bench.py`` may import this package. The product
+library (``dense_gemm_epilogue_tiled_amd``) never imports, links or calls it,
+and this package imports nothing from the product.
+
+The arithmetic lives in ``oracle_gemm_relu.c`` (plain C, built with gcc
+``-O2 -fno-fast-math -ffp-contract=off``); this module only compiles it and
+marshals numpy arrays of fp16 bit patterns (``uint16``) through ctypes.
+
+Every function here follows the definition written out at the top of the C
+file: fp32 accumulator cleared to zero, products accumulated in increasing k,
+ReLU on the fp32 value, round-to-nearest-even to fp16 (TileLang tutorial,
+chapter "GEMM walkthrough and parameter derivation"; blog "TileLang
+programming basics", section 2, the FP16 GEMM + ReLU listing).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+import threading
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "oracle_gemm_relu.c")
+LIB_PATH = os.path.join(_HERE, "liboracle_gemm_relu.so")
+_CFLAGS = ["-O2", "-std=c11", "-fno-fast-math", "-ffp-contract=off", "-fopenmp",
+           "-fPIC", "-shared", "-Wall", "-Wextra"]
+
+_lock = threading.Lock()
+_lib = None
+
+
+def build(force: bool = True) -> str:
+    """Compile the oracle shared library with gcc; returns its path."""
+    if force or not os.path.exists(LIB_PATH) or os.path.getmtime(LIB_PATH) < os.path.getmtime(_SRC):
+        tmp = LIB_PATH + ".tmp%d" % os.getpid()
+        subprocess.run(["gcc", *_CFLAGS, _SRC, "-o", tmp, "-lm"], check=True)
+        os.replace(tmp, LIB_PATH)
+    return LIB_PATH
+
+
+def _load():
+    global _lib
+    with _lock:
+        if _lib is None:
+            if not os.path.exists(LIB_PATH) or os.path.getmtime(LIB_PATH) < os.path.getmtime(_SRC):
+                build(force=True)
+            lib = ctypes.CDLL(LIB_PATH)
+            i64, p = ctypes.c_int64, ctypes.c_void_p
+            lib.oracle_f16_to_f32.argtypes = [ctypes.c_uint16]
+            lib.oracle_f16_to_f32.restype = ctypes.c_float
+            lib.oracle_f32_to_f16_rne.argtypes = [ctypes.c_float]
+            lib.oracle_f32_to_f16_rne.restype = ctypes.c_uint16
+            lib.oracle_f16_to_f32_array.argtypes = [p, p, i64]
+            lib.oracle_f16_to_f32_array.restype = None
+            lib.oracle_f32_to_f16_array.argtypes = [p, p, i64]
+            lib.oracle_f32_to_f16_array.restype = None
+            lib.oracle_set_threads.argtypes = [ctypes.c_int]
+            lib.oracle_set_threads.restype = None
+            lib.oracle_max_threads.argtypes = []
+            lib.oracle_max_threads.restype = ctypes.c_int
+            lib.oracle_gemm_relu_f16_full.argtypes = [i64, i64, i64, p, i64, p, i64, p, i64]
+            lib.oracle_gemm_relu_f16_rows.argtypes = [i64, i64, i64, p, i64, p, i64, p, i64, p]
+            lib.oracle_gemm_relu_f16_cols.argtypes = [i64, i64, i64, p, i64, p, i64, p, i64, p]
+            lib.oracle_gemm_relu_f16_elems.argtypes = [i64, i64, i64, p, i64, p, i64, p, p, i64, p]
+            for name in ("full", "rows", "cols", "elems"):
+                getattr(lib, "oracle_gemm_relu_f16_" + name).restype = ctypes.c_int
+            _lib = lib
+    return _lib
+
+
+def _ptr(a: np.ndarray) -> int:
+    return a.ctypes.data
+
+
+def _check_operands(A, B, M, N, K, lda, ldb):
+    if A.dtype != np.uint16 or B.dtype != np.uint16:
+        raise TypeError("operands must be uint16 arrays of fp16 bit patterns")
+    if not (A.flags.c_contiguous and B.flags.c_contiguous):
+        raise ValueError("operands must be C-contiguous")
+    if M > 0 and K > 0 and A.size < (M - 1) * lda + K:
+        raise ValueError("A too small for M, K, lda")
+    if K > 0 and N > 0 and B.size < (K - 1) * ldb + N:
+        raise ValueError("B too small for K, N, ldb")
+
+
+def _dims(A, B, M, N, K, lda, ldb):
+    if M is None:
+        M, K = A.shape
+    if N is None:
+        N = B.shape[1]
+    lda = K if lda is None else lda
+    ldb = N if ldb is None else ldb
+    return int(M), int(N), int(K), int(lda), int(ldb)
+
+
+def f16_to_f32(bits: np.ndarray) -> np.ndarray:
+    """Element-wise binary16 -> binary32 through the oracle's own conversion."""
+    lib = _load()
+    flat = np.ascontiguousarray(bits, dtype=np.uint16).ravel()
+    out = np.empty(flat.size, dtype=np.float32)
+    lib.oracle_f16_to_f32_array(_ptr(flat), _ptr(out), flat.size)
+    return out.reshape(np.shape(bits))
+
+
+def f32_to_f16(vals: np.ndarray) -> np.ndarray:
+    """Element-wise binary32 -> binary16 (RNE) through the oracle's own conversion."""
+    lib = _load()
+    flat = np.ascontiguousarray(vals, dtype=np.float32).ravel()
+    out = np.empty(flat.size, dtype=np.uint16)
+    lib.oracle_f32_to_f16_array(_ptr(flat), _ptr(out), flat.size)
+    return out.reshape(np.shape(vals))
+
+
+def gemm_relu_full(A, B, M=None, N=None, K=None, lda=None, ldb=None, threads=None):
+    """The whole M x N result as fp16 bits (packed, ldc = N)."""
+    M, N, K, lda, ldb = _dims(A, B, M, N, K, lda, ldb)
+    _check_operands(A, B, M, N, K, lda, ldb)
+    lib = _load()
+    if threads:
+        lib.oracle_set_threads(int(threads))
+    C = np.zeros((M, N), dtype=np.uint16)
+    if M > 0 and N > 0:
+        rc = lib.oracle_gemm_relu_f16_full(M, N, K, _ptr(A), lda, _ptr(B), ldb, _ptr(C), N)
+        if rc != 0:
+            raise MemoryError("oracle allocation failed")
+    return C
+
+
+def gemm_relu_rows(A, B, rows, M=None, N=None, K=None, lda=None, ldb=None, threads=None):
+    """Full rows ``rows`` of the result: array (len(rows), N) of fp16 bits."""
+    M, N, K, lda, ldb = _dims(A, B, M, N, K, lda, ldb)
+    _check_operands(A, B, M, N, K, lda, ldb)
+    r = np.ascontiguousarray(rows, dtype=np.int64)
+    if r.size and (r.min() < 0 or r.max() >= M):
+        raise IndexError("row index out of range")
+    lib = _load()
+    if threads:
+        lib.oracle_set_threads(int(threads))
+    out = np.zeros((r.size, N), dtype=np.uint16)
+    if r.size and N > 0:
+        rc = lib.oracle_gemm_relu_f16_rows(M, N, K, _ptr(A), lda, _ptr(B), ldb, _ptr(r), r.size, _ptr(out))
+        if rc != 0:
+            raise MemoryError("oracle allocation failed")
+    return out
+
+
+def gemm_relu_cols(A, B, cols, M=None, N=None, K=None, lda=None, ldb=None, threads=None):
+    """Full columns ``cols`` of the result: array (len(cols), M) of fp16 bits."""
+    M, N, K, lda, ldb = _dims(A, B, M, N, K, lda, ldb)
+    _check_operands(A, B, M, N, K, lda, ldb)
+    c = np.ascontiguousarray(cols, dtype=np.int64)
+    if c.size and (c.min() < 0 or c.max() >= N):
+        raise IndexError("column index out of range")
+    lib = _load()
+    if threads:
+        lib.oracle_set_threads(int(threads))
+    out = np.zeros((c.size, M), dtype=np.uint16)
+    if c.size and M > 0:
+        rc = lib.oracle_gemm_relu_f16_cols(M, N, K, _ptr(A), lda, _ptr(B), ldb, _ptr(c), c.size, _ptr(out))
+        if rc != 0:
+            raise MemoryError("oracle allocation failed")
+    return out
+
+
+def gemm_relu_elems(A, B, ii, jj, M=None, N=None, K=None, lda=None, ldb=None, threads=None):
+    """Single elements C[ii[e], jj[e]] as fp16 bits."""
+    M, N, K, lda, ldb = _dims(A, B, M, N, K, lda, ldb)
+    _check_operands(A, B, M, N, K, lda, ldb)
+    i = np.ascontiguousarray(ii, dtype=np.int64)
+    j = np.ascontiguousarray(jj, dtype=np.int64)
+    if i.shape != j.shape:
+        raise ValueError("index arrays differ in length")
+    if i.size and (i.min() < 0 or i.max() >= M or j.min() < 0 or j.max() >= N):
+        raise IndexError("element index out of range")
+    lib = _load()
+    if threads:
+        lib.oracle_set_threads(int(threads))
+    out = np.zeros(i.size, dtype=np.uint16)
+    if i.size:
+        lib.oracle_gemm_relu_f16_elems(M, N, K, _ptr(A), lda, _ptr(B), ldb, _ptr(i), _ptr(j), i.size, _ptr(out))
+    return out
+
+
+def max_threads() -> int:
+    return int(_load().oracle_max_threads())
+
+
+def set_threads(n: int) -> None:
+    _load().oracle_set_threads(int(n))

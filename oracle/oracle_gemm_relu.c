@@ -1,0 +1,269 @@
+/*
+ * CPU oracle for C = ReLU(A * B) with fp16 operands, fp32 accumulation and an
+ * fp16 result.  TEST INFRASTRUCTURE ONLY: the product library never links,
+ * loads or calls this file; only the test suite, the smoke check and the CPU
+ * baseline leg of the benchmark do.  It shares no code with the GPU path.
+ *
+ * What it computes (one element at a time, written out plainly):
+ *
+ *   1. Widen each fp16 operand to fp32.  Every binary16 value, subnormals
+ *      included, is exactly representable in binary32.
+ *   2. acc = +0.0f; for k = 0, 1, ..., K-1 in that order:
+ *          acc = fl32(acc + a[i][k] * b[k][j]).
+ *      The accumulator starts cleared and is fp32, as in the TileLang tutorial
+ *      chapter "GEMM walkthrough and parameter derivation" (T.clear of the fp32
+ *      fragment, then one tile product accumulated per K strip) and the blog
+ *      "TileLang programming basics", section 2 (fp32 fragment, fp16 storage).
+ *      The product of two fp16 numbers needs at most 22 significand bits and
+ *      lies well inside the fp32 normal range, so it is exact in fp32: the only
+ *      rounding in the loop is the addition.  The build flags forbid
+ *      reassociation (-fno-fast-math) and contraction (-ffp-contract=off).
+ *   3. ReLU on the fp32 accumulator: r = acc > 0 ? acc : +0.0f.  The epilogue
+ *      in both GEMM+ReLU listings (blog section 2, and "Writing
+ *      high-performance kernels in TileLang", section "Writing a GEMM") takes
+ *      max(C_local, 0) on the fp32 fragment before the write-back.  Negative
+ *      values, -0 and NaN all map to +0 (the pages leave these open; this is
+ *      the reading stated in the design notes).
+ *   4. Round r to fp16, to nearest with ties to even; values too large become
+ *      +Inf.  The pages only say the cast happens on write-back; RNE is the
+ *      IEEE default and the reading taken here.
+ *
+ * Loop order: the full/rows variants run i, then k, then j with a row of fp32
+ * accumulators.  Each element still sees exactly the sequence of step 2, so
+ * the result is bit-identical to the i-j-k order.  OpenMP (when compiled with
+ * -fopenmp) splits rows only, never k.
+ *
+ * The fp16 <-> fp32 conversions below are written from the IEEE 754 binary16
+ * and binary32 encodings, not taken from any library.
+ */
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+/* ---- IEEE 754 binary16 <-> binary32 -------------------------------------- */
+
+static float bits_to_f32(uint32_t u) {
+    float f;
+    memcpy(&f, &u, sizeof f);
+    return f;
+}
+
+static uint32_t f32_to_bits(float f) {
+    uint32_t u;
+    memcpy(&u, &f, sizeof u);
+    return u;
+}
+
+/* binary16: 1 sign bit, 5 exponent bits (bias 15), 10 fraction bits. */
+float oracle_f16_to_f32(uint16_t h) {
+    uint32_t sign = (uint32_t)(h >> 15) << 31;
+    uint32_t exp = (h >> 10) & 0x1Fu;
+    uint32_t frac = h & 0x3FFu;
+    if (exp == 0x1Fu) {
+        /* Inf (frac == 0) or NaN: keep the payload, widen it by 13 bits. */
+        return bits_to_f32(sign | 0x7F800000u | (frac << 13));
+    }
+    if (exp == 0) {
+        /* zero or subnormal: value = frac * 2^-24, exact in binary32. */
+        float mag = (float)frac * 0x1p-24f;
+        return sign ? -mag : mag;
+    }
+    /* normal: (1 + frac/1024) * 2^(exp-15); rebias the exponent to 127. */
+    return bits_to_f32(sign | ((exp - 15u + 127u) << 23) | (frac << 13));
+}
+
+/* Round a binary32 value to binary16, nearest, ties to even. */
+uint16_t oracle_f32_to_f16_rne(float f) {
+    uint32_t u = f32_to_bits(f);
+    uint16_t sign = (uint16_t)((u >> 16) & 0x8000u);
+    uint32_t exp = (u >> 23) & 0xFFu;
+    uint32_t frac = u & 0x7FFFFFu;
+
+    if (exp == 0xFFu) {
+        if (frac == 0) return (uint16_t)(sign | 0x7C00u);          /* Inf */
+        return (uint16_t)(sign | 0x7E00u | (frac >> 13));          /* quiet NaN */
+    }
+    int e = (int)exp - 127; /* unbiased exponent of a normal binary32 */
+    if (exp == 0) {
+        /* binary32 subnormals are below 2^-126, far under half of the
+           smallest binary16 subnormal (2^-25): they round to zero. */
+        return sign;
+    }
+    if (e >= 16) return (uint16_t)(sign | 0x7C00u); /* >= 2^16: overflow */
+
+    uint32_t sig = frac | 0x800000u; /* 24-bit significand, value sig*2^(e-23) */
+    if (e >= -14) {
+        /* binary16 normal range: keep 10 fraction bits, round off 13. */
+        uint32_t h = ((uint32_t)(e + 15) << 10) | (frac >> 13);
+        uint32_t rem = frac & 0x1FFFu;
+        if (rem > 0x1000u || (rem == 0x1000u && (h & 1u))) h += 1u; /* carry may reach Inf: correct */
+        return (uint16_t)(sign | h);
+    }
+    /* binary16 subnormal range: result is q * 2^-24 with q an integer.
+       value / 2^-24 = sig * 2^(e+1), a right shift by s = -(e+1) >= 14. */
+    int s = -(e + 1);
+    if (s >= 25) return sign; /* value < 2^-25: below half the smallest subnormal */
+    uint32_t q = sig >> s;
+    uint32_t rem = sig & ((1u << s) - 1u);
+    uint32_t half = 1u << (s - 1);
+    if (rem > half || (rem == half && (q & 1u))) q += 1u; /* q may become 0x400: the smallest normal */
+    return (uint16_t)(sign | q);
+}
+
+/* Array forms of the two conversions (used by the conversion pins). */
+void oracle_f16_to_f32_array(const uint16_t* in, float* out, int64_t n) {
+    for (int64_t e = 0; e < n; ++e) out[e] = oracle_f16_to_f32(in[e]);
+}
+
+void oracle_f32_to_f16_array(const float* in, uint16_t* out, int64_t n) {
+    for (int64_t e = 0; e < n; ++e) out[e] = oracle_f32_to_f16_rne(in[e]);
+}
+
+/* ReLU on the fp32 accumulator followed by the fp16 write-back rounding. */
+static uint16_t epilogue(float acc) {
+    float r = (acc > 0.0f) ? acc : 0.0f; /* NaN compares false -> +0 */
+    return oracle_f32_to_f16_rne(r);
+}
+
+/* ---- thread control (used only to time the oracle) ----------------------- */
+
+void oracle_set_threads(int n) {
+#ifdef _OPENMP
+    if (n > 0) omp_set_num_threads(n);
+#else
+    (void)n;
+#endif
+}
+
+int oracle_max_threads(void) {
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}
+
+/* ---- the four entry points ----------------------------------------------- */
+
+/* One full output row i.  bf holds B widened to fp32, packed K x N. */
+static void one_row(int64_t i, int64_t N, int64_t K, const uint16_t* A, int64_t lda,
+                    const float* bf, float* acc, uint16_t* out) {
+    for (int64_t j = 0; j < N; ++j) acc[j] = 0.0f;
+    for (int64_t k = 0; k < K; ++k) {
+        float a = oracle_f16_to_f32(A[i * lda + k]);
+        const float* brow = bf + k * N;
+        for (int64_t j = 0; j < N; ++j) acc[j] = acc[j] + a * brow[j];
+    }
+    for (int64_t j = 0; j < N; ++j) out[j] = epilogue(acc[j]);
+}
+
+static float* widen_b(int64_t N, int64_t K, const uint16_t* B, int64_t ldb) {
+    float* bf = (float*)malloc((size_t)(K > 0 ? K : 1) * (size_t)(N > 0 ? N : 1) * sizeof(float));
+    if (!bf) return NULL;
+    for (int64_t k = 0; k < K; ++k)
+        for (int64_t j = 0; j < N; ++j) bf[k * N + j] = oracle_f16_to_f32(B[k * ldb + j]);
+    return bf;
+}
+
+/* C[i*ldc + j] for all 0 <= i < M, 0 <= j < N.  Returns 0, or -1 on allocation
+   failure.  Columns j >= N of C are not touched. */
+int oracle_gemm_relu_f16_full(int64_t M, int64_t N, int64_t K,
+                              const uint16_t* A, int64_t lda,
+                              const uint16_t* B, int64_t ldb,
+                              uint16_t* C, int64_t ldc) {
+    if (M <= 0 || N <= 0) return 0;
+    float* bf = widen_b(N, K, B, ldb);
+    if (!bf) return -1;
+    int failed = 0;
+#pragma omp parallel
+    {
+        float* acc = (float*)malloc((size_t)N * sizeof(float));
+        if (!acc) {
+#pragma omp atomic write
+            failed = 1;
+        } else {
+#pragma omp for schedule(dynamic, 1)
+            for (int64_t i = 0; i < M; ++i) one_row(i, N, K, A, lda, bf, acc, C + i * ldc);
+            free(acc);
+        }
+    }
+    free(bf);
+    return failed ? -1 : 0;
+}
+
+/* Full rows: out[r*N + j] = C[rows[r]][j] for r < nrows. */
+int oracle_gemm_relu_f16_rows(int64_t M, int64_t N, int64_t K,
+                              const uint16_t* A, int64_t lda,
+                              const uint16_t* B, int64_t ldb,
+                              const int64_t* rows, int64_t nrows, uint16_t* out) {
+    (void)M;
+    if (nrows <= 0 || N <= 0) return 0;
+    float* bf = widen_b(N, K, B, ldb);
+    if (!bf) return -1;
+    int failed = 0;
+#pragma omp parallel
+    {
+        float* acc = (float*)malloc((size_t)N * sizeof(float));
+        if (!acc) {
+#pragma omp atomic write
+            failed = 1;
+        } else {
+#pragma omp for schedule(dynamic, 1)
+            for (int64_t r = 0; r < nrows; ++r) one_row(rows[r], N, K, A, lda, bf, acc, out + r * N);
+            free(acc);
+        }
+    }
+    free(bf);
+    return failed ? -1 : 0;
+}
+
+/* Full columns: out[c*M + i] = C[i][cols[c]] for c < ncols. */
+int oracle_gemm_relu_f16_cols(int64_t M, int64_t N, int64_t K,
+                              const uint16_t* A, int64_t lda,
+                              const uint16_t* B, int64_t ldb,
+                              const int64_t* cols, int64_t ncols, uint16_t* out) {
+    (void)N;
+    if (ncols <= 0 || M <= 0) return 0;
+    int failed = 0;
+#pragma omp parallel
+    {
+        float* bcol = (float*)malloc((size_t)(K > 0 ? K : 1) * sizeof(float));
+        if (!bcol) {
+#pragma omp atomic write
+            failed = 1;
+        } else {
+#pragma omp for schedule(dynamic, 1)
+            for (int64_t c = 0; c < ncols; ++c) {
+                int64_t j = cols[c];
+                for (int64_t k = 0; k < K; ++k) bcol[k] = oracle_f16_to_f32(B[k * ldb + j]);
+                for (int64_t i = 0; i < M; ++i) {
+                    float acc = 0.0f;
+                    for (int64_t k = 0; k < K; ++k) acc = acc + oracle_f16_to_f32(A[i * lda + k]) * bcol[k];
+                    out[c * M + i] = epilogue(acc);
+                }
+            }
+            free(bcol);
+        }
+    }
+    return failed ? -1 : 0;
+}
+
+/* Single elements: out[e] = C[ii[e]][jj[e]] for e < n. */
+int oracle_gemm_relu_f16_elems(int64_t M, int64_t N, int64_t K,
+                               const uint16_t* A, int64_t lda,
+                               const uint16_t* B, int64_t ldb,
+                               const int64_t* ii, const int64_t* jj, int64_t n, uint16_t* out) {
+    (void)M;
+    (void)N;
+#pragma omp parallel for schedule(static)
+    for (int64_t e = 0; e < n; ++e) {
+        float acc = 0.0f;
+        for (int64_t k = 0; k < K; ++k)
+            acc = acc + oracle_f16_to_f32(A[ii[e] * lda + k]) * oracle_f16_to_f32(B[k * ldb + jj[e]]);
+        out[e] = epilogue(acc);
+    }
+    return 0;
+}

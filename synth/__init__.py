@@ -1,0 +1,102 @@
+"""Seeded synthetic inputs shared by the tests, the smoke check and the benchmark.
+
+This module holds no arithmetic of C = ReLU(A.B): it only draws operands. Both
+the CPU oracle and the GPU path consume the very same fp16 bit patterns it
+returns, as ``numpy.uint16`` arrays (row-major, packed unless a pitch is given).
+
+Recipe (one CPU ``torch.Generator`` per workload, A drawn first, then B):
+  * entries i.i.d. normal, drawn in fp32 with ``torch.randn``, as the GEMM+ReLU
+    listings do with ``torch.randn(..., dtype=float16)`` (blog "TileLang
+    programming basics", section 2; "Writing high-performance kernels in
+    TileLang", section "Writing a GEMM");
+  * for the MLP-projection and small-M shapes B is scaled by K^-1/2 in fp32;
+  * each fp32 value is rounded to fp16 (round to nearest even) by torch.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass
+
+import numpy as np
+
+
+@dataclass(frozen=True)
+class Workload:
+    name: str
+    M: int
+    N: int
+    K: int
+    seed: int
+    b_scaled: bool  # B ~ N(0, 1/K) instead of N(0, 1)
+    check: str      # "full" or "sampled"
+
+
+# The five workloads: square 1024^3; square 4096^3 (the headline
+# compute-bound case); a shape dividing no tile; an LLM MLP up-projection;
+# and a GEMV-like small-M product.
+WORKLOADS = {
+    "square1024": Workload("square1024", 1024, 1024, 1024, 1, False, "full"),
+    "square4096": Workload("square4096", 4096, 4096, 4096, 2, False, "sampled"),
+    "ragged4099x3071x2050": Workload("ragged4099x3071x2050", 4099, 3071, 2050, 3, False, "full"),
+    "mlp8192x28672x8192": Workload("mlp8192x28672x8192", 8192, 28672, 8192, 4, True, "sampled"),
+    "smallm8x16384x8192": Workload("smallm8x16384x8192", 8, 16384, 8192, 5, True, "full"),
+}
+
+
+def _torch():
+    import torch  # imported lazily: the oracle pins do not need it
+    return torch
+
+
+def normal_f16(shape, gen, scale: float | None = None) -> np.ndarray:
+    """N(0,1) (times ``scale``) drawn in fp32, rounded to fp16; returns uint16 bits."""
+    torch = _torch()
+    x = torch.randn(*shape, generator=gen, dtype=torch.float32)
+    if scale is not None:
+        x.mul_(scale)
+    return x.to(torch.float16).view(torch.int16).numpy().view(np.uint16)
+
+
+def operands(w: Workload):
+    """(A, B) as packed row-major uint16 arrays for workload ``w``."""
+    torch = _torch()
+    gen = torch.Generator().manual_seed(w.seed)
+    A = normal_f16((w.M, w.K), gen)
+    B = normal_f16((w.K, w.N), gen, scale=(w.K ** -0.5) if w.b_scaled else None)
+    return A, B
+
+
+def random_operands(M: int, N: int, K: int, seed: int, lda: int | None = None,
+                    ldb: int | None = None, pad_value: int | None = None,
+                    b_scale: float | None = None):
+    """Random N(0,1) operands with optional row pitches.
+
+    With ``lda > K`` (``ldb > N``) the padding columns are filled with the fp16
+    bit pattern ``pad_value`` (default: 65504, the largest finite fp16), so a
+    kernel that reads padding produces visibly wrong results.
+    """
+    torch = _torch()
+    gen = torch.Generator().manual_seed(seed)
+    lda = K if lda is None else lda
+    ldb = N if ldb is None else ldb
+    pad = 0x7BFF if pad_value is None else pad_value
+    A = np.full((M, max(lda, 1)), pad, dtype=np.uint16)
+    B = np.full((K, max(ldb, 1)), pad, dtype=np.uint16)
+    if M and K:
+        A[:, :K] = normal_f16((M, K), gen)
+    if K and N:
+        B[:, :N] = normal_f16((K, N), gen, scale=b_scale)
+    return A, B
+
+
+def small_int_operands(M: int, N: int, K: int, seed: int, lo: int = -3, hi: int = 3):
+    """Integer-valued fp16 operands in [lo, hi] (every partial sum stays exact)."""
+    rng = np.random.default_rng(seed)
+    A = rng.integers(lo, hi + 1, size=(M, K)).astype(np.float16).view(np.uint16)
+    B = rng.integers(lo, hi + 1, size=(K, N)).astype(np.float16).view(np.uint16)
+    return A, B
+
+
+def sample_indices(M: int, N: int, count: int, seed: int):
+    """``count`` seeded (i, j) pairs, uniform over the M x N result."""
+    rng = np.random.default_rng(10_000 + seed)
+    return rng.integers(0, M, size=count), rng.integers(0, N, size=count)
