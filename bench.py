@@ -1,0 +1,314 @@
+#!/usr/bin/env python3
+"""Throughput of C = ReLU(A.B) (fp16 in, fp32 accumulate, fp16 out) on one MI355X.
+
+One "step" is one call of the library (``gemm_relu_f16`` through the C ABI) on
+the headline workload, M = N = K = 4096, with A and B already resident in HBM.
+Prints ONE JSON line (rank 0) with the metric, the roofline of the dominant
+kernel measured live with HIP events on the launch stream, and the CPU oracle
+timed on a bounded sample of the same workload.
+
+  python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+                  [--no-workloads] [--workload NAME] [--copy-probe MIB]
+
+``--copy-probe`` runs only a device-to-device copy of known size; it is what
+the HBM-traffic counters are calibrated against.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+import synth  # noqa: E402
+
+MFMA_F16_PEAK_TFLOPS = 2516.6  # MI355X dense fp16 MFMA: 256 CU x 4096 FLOP/clk x 2.4 GHz (published 2.5 PFLOP/s)
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published 8 TB/s
+
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.txt")
+
+
+def kernel_source_hash() -> str:
+    """Hash of the kernel sources; counter-derived traffic is only reported
+    while it matches the hash recorded when the counters were taken."""
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "dense_gemm_epilogue_tiled_amd", "csrc")
+    for f in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, f), "rb") as fh:
+            h.update(f.encode() + b"\0" + fh.read())
+    return h.hexdigest()[:16]
+
+
+def algorithmic(w):
+    flops = 2.0 * w.M * w.N * w.K
+    nbytes = 2.0 * (w.M * w.K + w.K * w.N + w.M * w.N)
+    return flops, nbytes
+
+
+def make_device_operands(torch, w, copies=1):
+    """Seeded N(0,1) fp16 operands generated on the GPU (B scaled by K^-1/2
+    where the workload says so). Same distribution as the CPU generator."""
+    g = torch.Generator(device="cuda").manual_seed(w.seed)
+    A = torch.randn(w.M, w.K, generator=g, device="cuda", dtype=torch.float32).half()
+    Bs = []
+    for _ in range(copies):
+        b = torch.randn(w.K, w.N, generator=g, device="cuda", dtype=torch.float32)
+        if w.b_scaled:
+            b.mul_(w.K ** -0.5)
+        Bs.append(b.half())
+    C = torch.empty(w.M, w.N, device="cuda", dtype=torch.float16)
+    return A, Bs, C
+
+
+def launcher(gr, torch, w, A, B, C, stream):
+    h = stream.cuda_stream
+    a, b, c = A.data_ptr(), B.data_ptr(), C.data_ptr()
+    M, N, K = w.M, w.N, w.K
+    fn = gr.lib().gemm_relu_f16
+
+    def run():
+        st = fn(M, N, K, a, K, b, N, c, N, h)
+        if st != 0:
+            raise gr.GemmReluError(st)
+    return run
+
+
+def time_launches(torch, run, stream, reps):
+    """Per-launch durations (ms) from HIP event pairs on the launch stream."""
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    for s, e in evs:
+        s.record(stream)
+        run()
+        e.record(stream)
+    torch.cuda.synchronize()
+    return [s.elapsed_time(e) for s, e in evs]
+
+
+def cpu_baseline(w, max_seconds=20.0):
+    """The oracle (as it stands) on the host cores, on whole rows of the
+    workload's result: rows are added in chunks until about ``max_seconds``
+    of work is done or the matrix is complete. Work per row is exactly
+    2 N K FLOP, so the rate needs no extrapolation."""
+    import numpy as np
+    import oracle
+
+    threads = len(os.sched_getaffinity(0))
+    if os.environ.get("OMP_NUM_THREADS", "").isdigit():
+        threads = min(threads, int(os.environ["OMP_NUM_THREADS"]))
+    threads = max(1, threads)
+    oracle.set_threads(threads)
+    A, B = synth.operands(w)
+    done, t_total, chunk = 0, 0.0, 64
+    while done < w.M and t_total < max_seconds:
+        rows = np.arange(done, min(w.M, done + chunk))
+        t0 = time.perf_counter()
+        oracle.gemm_relu_rows(A, B, rows)
+        t_total += time.perf_counter() - t0
+        done += rows.size
+        chunk = min(chunk * 2, 1024)
+    flops = 2.0 * done * w.N * w.K
+    model = ""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return {
+        "value": round(flops / t_total / 1e12, 6),
+        "unit": "TFLOP/s",
+        "cores": oracle.max_threads(),
+        "kind": "oracle",
+        "sample": "%d full rows of the %dx%dx%d result (%.1f GFLOP, %.2f s; C triple loop, fp32 "
+                  "accumulation, OpenMP over rows; %s)" % (done, w.M, w.N, w.K, flops / 1e9, t_total, model),
+    }
+
+
+def traffic_for(workload: str, src_hash: str):
+    """HBM bytes per launch (fetched + written) from the committed counter
+    summary, if it was taken on the current kernel sources; else None."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            for line in f:
+                parts = line.split()
+                if len(parts) == 4 and not line.startswith("#") and parts[0] == workload:
+                    if parts[1] != src_hash:
+                        return None
+                    return int(parts[2]) + int(parts[3])
+    except (OSError, ValueError):
+        return None
+    return None
+
+
+def bench_workload(gr, torch, w, reps, cold):
+    """Secondary measurement of one workload: median/min/p90 launch time."""
+    copies = 4 if cold else 1
+    A, Bs, C = make_device_operands(torch, w, copies=copies)
+    stream = torch.cuda.current_stream()
+    runs = [launcher(gr, torch, w, A, B, C, stream) for B in Bs]
+    for r in runs:
+        for _ in range(3):
+            r()
+    torch.cuda.synchronize()
+    if cold:
+        # rotate 4 copies of B (4 x |B| > the 256 MB last-level cache), and
+        # stream a 512 MiB buffer between launches (outside the events)
+        flush = torch.empty(256 * 1024 * 1024, dtype=torch.float16, device="cuda")
+        times = []
+        for i in range(reps):
+            flush.zero_()
+            t = time_launches(torch, runs[i % copies], stream, 1)
+            times.append(t[0])
+        del flush
+    else:
+        times = time_launches(torch, runs[0], stream, reps)
+    del A, Bs, C
+    torch.cuda.empty_cache()
+    times.sort()
+    med = statistics.median(times)
+    flops, nbytes = algorithmic(w)
+    return {
+        "median_us": round(med * 1e3, 2),
+        "min_us": round(times[0] * 1e3, 2),
+        "p90_us": round(times[int(0.9 * (len(times) - 1))] * 1e3, 2),
+        "tflops": round(flops / (med * 1e-3) / 1e12, 1),
+        "gbs": round(nbytes / (med * 1e-3) / 1e9, 1),
+        "frac_mfma": round(flops / (med * 1e-3) / 1e12 / MFMA_F16_PEAK_TFLOPS, 4),
+        "frac_hbm": round(nbytes / (med * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+        "cache": "cold" if cold else "warm",
+        "reps": reps,
+    }
+
+
+def copy_probe(torch, mib):
+    n = mib * 1024 * 1024 // 2
+    src = torch.randn(n, device="cuda", dtype=torch.float32).half()
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    times = time_launches(torch, lambda: dst.copy_(src), torch.cuda.current_stream(), 20)
+    med = statistics.median(times)
+    print(json.dumps({"copy_probe_bytes_read": n * 2, "copy_probe_bytes_written": n * 2,
+                      "median_us": round(med * 1e3, 2), "gbs_rw": round(4.0 * n / (med * 1e-3) / 1e9, 1)}))
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=25)
+    ap.add_argument("--workload", default="square4096", choices=sorted(synth.WORKLOADS))
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-workloads", action="store_true", help="skip the secondary per-workload table")
+    ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU only: this library has no multi-GPU path "
+              "(the product shards on N with no exchange; see the design notes). "
+              "Run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import dense_gemm_epilogue_tiled_amd as gr
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    torch.cuda.set_device(0)
+    gr.lib()  # fail loudly if the HIP library is missing
+
+    if args.copy_probe:
+        copy_probe(torch, args.copy_probe)
+        return
+
+    w = synth.WORKLOADS[args.workload]
+    flops, nbytes = algorithmic(w)
+    A, Bs, C = make_device_operands(torch, w)
+    stream = torch.cuda.current_stream()
+    run = launcher(gr, torch, w, A, Bs[0], C, stream)
+    st, plan = gr.gemm_relu_f16_plan(w.M, w.N, w.K, A.data_ptr(), w.K, Bs[0].data_ptr(), w.N, C.data_ptr(), w.N)
+    assert st == 0
+
+    for _ in range(args.warmup):
+        run()
+    torch.cuda.synchronize()
+
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ev0.record(stream)
+    for _ in range(args.steps):
+        run()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ev_ms = ev0.elapsed_time(ev1) / args.steps
+
+    value = flops * args.steps / wall / 1e12
+    dominant_bound = "hbm" if flops / nbytes < MFMA_F16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9) else "mfma"
+    src_hash = kernel_source_hash()
+    if dominant_bound == "mfma":
+        achieved = flops / (ev_ms * 1e-3) / 1e12
+        roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": MFMA_F16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(achieved / MFMA_F16_PEAK_TFLOPS, 4)}
+    else:
+        achieved = nbytes / (ev_ms * 1e-3) / 1e9
+        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(achieved / HBM_PEAK_GBS, 4)}
+    roof["traffic"] = traffic_for(args.workload, src_hash)
+    roof["kernel_avg_us"] = round(ev_ms * 1e3, 2)
+    roof["algorithmic_flops"] = flops
+    roof["algorithmic_bytes"] = nbytes
+    del A, Bs, C
+    torch.cuda.empty_cache()
+
+    out = {
+        "metric": "TFLOP/s fp16 GEMM+ReLU (fp32 acc) at 4096^3 on 1 GPU; % of MFMA/HBM roofline",
+        "value": round(value, 1),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall * 1e3 / args.steps, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "M": w.M, "N": w.N, "K": w.K, "layout": "row-major A(MxK) B(KxN) C(MxN)",
+                   "accumulate": "fp32", "path": plan["path_name"],
+                   "tile": [plan["block_m"], plan["block_n"], plan["block_k"]], "grid": plan["grid"],
+                   "threads": plan["threads"], "kernel_source_hash": src_hash},
+        "roofline": roof,
+    }
+
+    if not args.no_workloads:
+        table = {}
+        for name, wl in synth.WORKLOADS.items():
+            cold = wl.name.startswith("smallm")
+            reps = 20 if wl.M * wl.N * wl.K > 1e12 else 50
+            table[name] = bench_workload(gr, torch, wl, reps, cold)
+            print("[bench] %s %s" % (name, table[name]), file=sys.stderr, flush=True)
+        out["workloads"] = table
+
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(w)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

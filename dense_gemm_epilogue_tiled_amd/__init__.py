@@ -1,0 +1,157 @@
+"""Python binding of the gfx950 fused fp16 GEMM + ReLU library.
+
+Thin ctypes marshalling over the C ABI declared in ``include/gemm_relu.h``:
+every step of C = ReLU(A.B) runs in the HIP kernels of ``libgemm_relu.so``.
+There is no fallback: if the library has not been built, every call raises.
+PyTorch is only a convenience for device memory and streams
+(``gemm_relu`` accepts CUDA/HIP tensors).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libgemm_relu.so")
+
+GR_OK = 0
+GR_ERR_INVALID_DIM = -1
+GR_ERR_INVALID_LD = -2
+GR_ERR_NULL_PTR = -3
+GR_ERR_ALIAS = -4
+GR_ERR_TOO_LARGE = -5
+GR_ERR_NO_DEVICE = -6
+GR_ERR_UNSUPPORTED_DEVICE = -7
+GR_ERR_LAUNCH = -8
+GR_ERR_INVALID_PATH = -9
+GR_ERR_INVALID_ARG = -10
+
+GR_PATH_NONE = 0
+GR_PATH_TILE = 1
+GR_PATH_TILE_EDGE = 2
+GR_PATH_SMALL_M = 3
+
+PATH_NAMES = {GR_PATH_NONE: "none", GR_PATH_TILE: "tile", GR_PATH_TILE_EDGE: "tile_edge",
+              GR_PATH_SMALL_M: "small_m"}
+
+
+class gr_plan_t(ctypes.Structure):
+    _fields_ = [
+        ("path", ctypes.c_int32),
+        ("block_m", ctypes.c_int32),
+        ("block_n", ctypes.c_int32),
+        ("block_k", ctypes.c_int32),
+        ("stages", ctypes.c_int32),
+        ("threads", ctypes.c_int32),
+        ("grid", ctypes.c_int64),
+        ("vec_a", ctypes.c_int32),
+        ("vec_b", ctypes.c_int32),
+        ("vec_c", ctypes.c_int32),
+        ("group_m", ctypes.c_int32),
+    ]
+
+
+class GemmReluError(RuntimeError):
+    def __init__(self, status: int, what: str = "gemm_relu_f16"):
+        self.status = status
+        super().__init__("%s failed: %s (%d)" % (what, gemm_relu_status_string(status), status))
+
+
+_lock = threading.Lock()
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded C library; raises if it has not been built."""
+    global _lib
+    with _lock:
+        if _lib is None:
+            if not os.path.exists(LIB_PATH):
+                raise RuntimeError(
+                    "libgemm_relu.so is not built (%s); run `python -m dense_gemm_epilogue_tiled_amd.build` "
+                    "or __graft_entry__.build()" % LIB_PATH)
+            l = ctypes.CDLL(LIB_PATH)
+            i64, p, i32 = ctypes.c_int64, ctypes.c_void_p, ctypes.c_int
+            l.gemm_relu_f16.argtypes = [i64, i64, i64, p, i64, p, i64, p, i64, p]
+            l.gemm_relu_f16.restype = i32
+            l.gemm_relu_f16_forced.argtypes = [i64, i64, i64, p, i64, p, i64, p, i64, p, i32]
+            l.gemm_relu_f16_forced.restype = i32
+            l.gemm_relu_f16_plan.argtypes = [i64, i64, i64, p, i64, p, i64, p, i64, ctypes.POINTER(gr_plan_t)]
+            l.gemm_relu_f16_plan.restype = i32
+            l.gemm_relu_status_string.argtypes = [i32]
+            l.gemm_relu_status_string.restype = ctypes.c_char_p
+            l.gemm_relu_version.argtypes = []
+            l.gemm_relu_version.restype = i32
+            _lib = l
+    return _lib
+
+
+def _ptr(x) -> int:
+    return 0 if x is None else int(x)
+
+
+def gemm_relu_f16(M, N, K, A, lda, B, ldb, C, ldc, stream=None) -> int:
+    """C := ReLU(A.B) on device pointers (ints); returns the C status code."""
+    return lib().gemm_relu_f16(M, N, K, _ptr(A), lda, _ptr(B), ldb, _ptr(C), ldc, _ptr(stream))
+
+
+def gemm_relu_f16_forced(M, N, K, A, lda, B, ldb, C, ldc, stream=None, path=GR_PATH_TILE_EDGE) -> int:
+    """As gemm_relu_f16 but on the given path (GR_PATH_*); returns the status code."""
+    return lib().gemm_relu_f16_forced(M, N, K, _ptr(A), lda, _ptr(B), ldb, _ptr(C), ldc, _ptr(stream), path)
+
+
+def gemm_relu_f16_plan(M, N, K, A, lda, B, ldb, C, ldc):
+    """(status, plan dict) from the pure planner; needs no GPU."""
+    plan = gr_plan_t()
+    st = lib().gemm_relu_f16_plan(M, N, K, _ptr(A), lda, _ptr(B), ldb, _ptr(C), ldc, ctypes.byref(plan))
+    d = {name: getattr(plan, name) for name, _ in gr_plan_t._fields_}
+    d["path_name"] = PATH_NAMES.get(d["path"], "?")
+    return st, d
+
+
+def gemm_relu_status_string(status: int) -> str:
+    return lib().gemm_relu_status_string(int(status)).decode()
+
+
+def gemm_relu_version() -> int:
+    return int(lib().gemm_relu_version())
+
+
+def _stream_handle(stream):
+    import torch
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def gemm_relu(a, b, out=None, stream=None, path=None):
+    """Tensor convenience: ``out = ReLU(a @ b)`` for 2-D fp16 tensors on the GPU.
+
+    Row pitches are taken from the tensors' strides (unit column stride
+    required). Raises GemmReluError on a non-zero status.
+    """
+    import torch
+    if a.dtype != torch.float16 or b.dtype != torch.float16:
+        raise TypeError("a and b must be float16")
+    if a.dim() != 2 or b.dim() != 2 or a.shape[1] != b.shape[0]:
+        raise ValueError("shapes do not form a matrix product: %s x %s" % (tuple(a.shape), tuple(b.shape)))
+    M, K = a.shape
+    N = b.shape[1]
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.float16, device=a.device)
+    for t in (a, b, out):
+        if t.numel() and t.stride(1) != 1:
+            raise ValueError("tensors need unit column stride")
+    lda = max(a.stride(0), 1) if M > 1 else max(K, 1)
+    ldb = max(b.stride(0), 1) if K > 1 else max(N, 1)
+    ldc = max(out.stride(0), 1) if M > 1 else max(N, 1)
+    h = _stream_handle(stream)
+    if path is None:
+        st = gemm_relu_f16(M, N, K, a.data_ptr(), lda, b.data_ptr(), ldb, out.data_ptr(), ldc, h)
+    else:
+        st = gemm_relu_f16_forced(M, N, K, a.data_ptr(), lda, b.data_ptr(), ldb, out.data_ptr(), ldc, h, path)
+    if st != GR_OK:
+        raise GemmReluError(st)
+    return out

@@ -1,0 +1,267 @@
+// C ABI of the fused fp16 GEMM + ReLU library for MI355X (gfx950).
+//
+// Host side: argument validation, a pure planner (which kernel, tile and grid)
+// and the launch on the caller's stream.  The operation and its contract are
+// documented in include/gemm_relu.h.  No allocation, no synchronisation and
+// no per-call state: the only state is a once-per-device check that the
+// device is a gfx950.
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <cstdint>
+#include <cstring>
+
+#include "../../include/gemm_relu.h"
+#include "smallm_kernel.hpp"
+#include "tile_kernel.hpp"
+
+namespace {
+
+constexpr int kVersion = 100;  // 0.1.0
+constexpr int64_t kMaxDim = (int64_t(1) << 31) - 1;
+constexpr int64_t kMaxSpanBytes = int64_t(1) << 62;
+constexpr int kGroupM = 4;          // tile rows per workgroup-order group
+constexpr int kSmallMThreshold = 16;  // rows of A handled by the small-M kernel
+constexpr int kSmallMWaves = 8;
+constexpr int kSmallMUnroll = 4;
+
+// Number of bytes spanned by a rows x cols matrix with pitch ld (0 if empty);
+// -1 when it does not fit the library's limits.
+int64_t span_bytes(int64_t rows, int64_t cols, int64_t ld) {
+    if (rows == 0 || cols == 0) return 0;
+    // (rows - 1) * ld + cols elements, checked against 2^62 bytes.
+    const int64_t limit = kMaxSpanBytes / 2;
+    if (rows - 1 > 0 && ld > (limit - cols) / (rows - 1)) return -1;
+    return ((rows - 1) * ld + cols) * 2;
+}
+
+bool overlaps(uintptr_t a, int64_t alen, uintptr_t b, int64_t blen) {
+    if (alen <= 0 || blen <= 0) return false;
+    return a < b + (uintptr_t)blen && b < a + (uintptr_t)alen;
+}
+
+// Widest fp16 vector (8, 2 or 1 elements) every row start of a pitched matrix
+// is aligned to.
+int vec_width(uintptr_t p, int64_t ld) {
+    if (p % 16 == 0 && ld % 8 == 0) return 8;
+    if (p % 4 == 0 && ld % 2 == 0) return 2;
+    return 1;
+}
+
+int vec_width_c(uintptr_t p, int64_t ld) {
+    if (p % 8 == 0 && ld % 4 == 0) return 4;
+    return 1;
+}
+
+int validate(int64_t M, int64_t N, int64_t K, uintptr_t A, int64_t lda, uintptr_t B, int64_t ldb,
+             uintptr_t C, int64_t ldc) {
+    if (M < 0 || N < 0 || K < 0) return GR_ERR_INVALID_DIM;
+    if (M > kMaxDim || N > kMaxDim || K > kMaxDim) return GR_ERR_TOO_LARGE;
+    const int64_t kmin = K > 1 ? K : 1, nmin = N > 1 ? N : 1;
+    if (lda < kmin || ldb < nmin || ldc < nmin) return GR_ERR_INVALID_LD;
+    const bool a_used = M > 0 && K > 0 && N > 0;
+    const bool b_used = K > 0 && N > 0 && M > 0;
+    const bool c_used = M > 0 && N > 0;
+    if ((a_used && !A) || (b_used && !B) || (c_used && !C)) return GR_ERR_NULL_PTR;
+    const int64_t sa = a_used ? span_bytes(M, K, lda) : 0;
+    const int64_t sb = b_used ? span_bytes(K, N, ldb) : 0;
+    const int64_t sc = c_used ? span_bytes(M, N, ldc) : 0;
+    if (sa < 0 || sb < 0 || sc < 0) return GR_ERR_TOO_LARGE;
+    if (overlaps(C, sc, A, sa) || overlaps(C, sc, B, sb)) return GR_ERR_ALIAS;
+    return GR_OK;
+}
+
+bool smallm_ok(int64_t M, int64_t N, int64_t K, uintptr_t A, int64_t lda, uintptr_t B, int64_t ldb) {
+    (void)N;
+    (void)K;
+    return M >= 1 && M <= kSmallMThreshold && A % 16 == 0 && lda % 8 == 0 && B % 8 == 0 && ldb % 4 == 0;
+}
+
+bool tile_fast_ok(int64_t M, int64_t N, int64_t K, uintptr_t A, int64_t lda, uintptr_t B, int64_t ldb,
+                  uintptr_t C, int64_t ldc) {
+    using namespace gr::tile;
+    return M % BM == 0 && N % BN == 0 && K % BK == 0 && K > 0 && vec_width(A, lda) == 8 &&
+           vec_width(B, ldb) == 8 && vec_width_c(C, ldc) == 4;
+}
+
+void fill_plan(int path, int64_t M, int64_t N, int64_t K, uintptr_t A, int64_t lda, uintptr_t B,
+               int64_t ldb, uintptr_t C, int64_t ldc, gr_plan_t* p) {
+    std::memset(p, 0, sizeof(*p));
+    p->path = path;
+    if (path == GR_PATH_TILE || path == GR_PATH_TILE_EDGE) {
+        using namespace gr::tile;
+        p->block_m = BM;
+        p->block_n = BN;
+        p->block_k = BK;
+        p->stages = 2;
+        p->threads = THREADS;
+        p->grid = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
+        p->vec_a = path == GR_PATH_TILE ? 8 : vec_width(A, lda);
+        p->vec_b = path == GR_PATH_TILE ? 8 : vec_width(B, ldb);
+        p->vec_c = vec_width_c(C, ldc);
+        p->group_m = kGroupM;
+    } else if (path == GR_PATH_SMALL_M) {
+        using namespace gr::smallm;
+        p->block_m = MAX_M;
+        p->block_n = NB;
+        p->block_k = KSTEP;
+        p->stages = kSmallMUnroll;
+        p->threads = 64 * kSmallMWaves;
+        p->grid = (N + NB - 1) / NB;
+        p->vec_a = 8;
+        p->vec_b = 4;
+        p->vec_c = 1;
+        p->group_m = 1;
+    }
+}
+
+int choose_path(int64_t M, int64_t N, int64_t K, uintptr_t A, int64_t lda, uintptr_t B, int64_t ldb,
+                uintptr_t C, int64_t ldc) {
+    if (M == 0 || N == 0) return GR_PATH_NONE;
+    if (K > 0 && smallm_ok(M, N, K, A, lda, B, ldb)) return GR_PATH_SMALL_M;
+    if (tile_fast_ok(M, N, K, A, lda, B, ldb, C, ldc)) return GR_PATH_TILE;
+    return GR_PATH_TILE_EDGE;
+}
+
+// ---- device check (once per device) ------------------------------------------
+
+constexpr int kMaxDevices = 64;
+std::atomic<int> g_device_state[kMaxDevices];  // 0 unknown, 1 gfx950, 2 other
+
+int check_device() {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0) return GR_ERR_NO_DEVICE;
+    if (dev >= kMaxDevices) return GR_ERR_UNSUPPORTED_DEVICE;
+    int state = g_device_state[dev].load(std::memory_order_acquire);
+    if (state == 0) {
+        hipDeviceProp_t prop;
+        if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return GR_ERR_NO_DEVICE;
+        state = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : 2;
+        g_device_state[dev].store(state, std::memory_order_release);
+    }
+    return state == 1 ? GR_OK : GR_ERR_UNSUPPORTED_DEVICE;
+}
+
+// ---- launches ----------------------------------------------------------------
+
+template <typename... Args>
+int launch(void (*kernel)(Args...), int64_t grid, int threads, hipStream_t stream, Args... args) {
+    void* argv[] = {static_cast<void*>(&args)...};
+    hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(kernel), dim3((uint32_t)grid), dim3(threads), argv,
+                                   0, stream);
+    return e == hipSuccess ? GR_OK : GR_ERR_LAUNCH;
+}
+
+template <bool GUARD, int VA, int VB>
+int launch_tile(const gr_plan_t& p, int64_t M, int64_t N, int64_t K, const uint16_t* A, int64_t lda,
+                const uint16_t* B, int64_t ldb, uint16_t* C, int64_t ldc, hipStream_t stream) {
+    using namespace gr::tile;
+    const uint32_t tiles_m = (uint32_t)((M + BM - 1) / BM);
+    const uint32_t tiles_n = (uint32_t)((N + BN - 1) / BN);
+    return launch(gemm_relu_tile_kernel<GUARD, VA, VB>, p.grid, THREADS, stream, A, B, C, M, N, K, lda, ldb, ldc,
+                  tiles_m, tiles_n, (uint32_t)p.group_m, (int)p.vec_c);
+}
+
+template <bool GUARD, int VA>
+int launch_tile_vb(const gr_plan_t& p, int64_t M, int64_t N, int64_t K, const uint16_t* A, int64_t lda,
+                   const uint16_t* B, int64_t ldb, uint16_t* C, int64_t ldc, hipStream_t stream) {
+    switch (p.vec_b) {
+        case 8: return launch_tile<GUARD, VA, 8>(p, M, N, K, A, lda, B, ldb, C, ldc, stream);
+        case 2: return launch_tile<GUARD, VA, 2>(p, M, N, K, A, lda, B, ldb, C, ldc, stream);
+        default: return launch_tile<GUARD, VA, 1>(p, M, N, K, A, lda, B, ldb, C, ldc, stream);
+    }
+}
+
+int run(const gr_plan_t& p, int64_t M, int64_t N, int64_t K, const uint16_t* A, int64_t lda, const uint16_t* B,
+        int64_t ldb, uint16_t* C, int64_t ldc, hipStream_t stream) {
+    switch (p.path) {
+        case GR_PATH_NONE: return GR_OK;
+        case GR_PATH_TILE: return launch_tile<false, 8, 8>(p, M, N, K, A, lda, B, ldb, C, ldc, stream);
+        case GR_PATH_TILE_EDGE:
+            switch (p.vec_a) {
+                case 8: return launch_tile_vb<true, 8>(p, M, N, K, A, lda, B, ldb, C, ldc, stream);
+                case 2: return launch_tile_vb<true, 2>(p, M, N, K, A, lda, B, ldb, C, ldc, stream);
+                default: return launch_tile_vb<true, 1>(p, M, N, K, A, lda, B, ldb, C, ldc, stream);
+            }
+        case GR_PATH_SMALL_M: {
+            using namespace gr::smallm;
+            const bool whole = N % NB == 0 && K % KSTEP == 0;
+            if (whole)
+                return launch(gemm_relu_smallm_kernel<kSmallMWaves, kSmallMUnroll, false>, p.grid, p.threads,
+                              stream, A, B, C, M, N, K, lda, ldb, ldc);
+            return launch(gemm_relu_smallm_kernel<kSmallMWaves, kSmallMUnroll, true>, p.grid, p.threads, stream, A,
+                          B, C, M, N, K, lda, ldb, ldc);
+        }
+        default: return GR_ERR_INVALID_PATH;
+    }
+}
+
+int entry(int64_t M, int64_t N, int64_t K, const uint16_t* A, int64_t lda, const uint16_t* B, int64_t ldb,
+          uint16_t* C, int64_t ldc, void* stream, int forced) {
+    const uintptr_t a = (uintptr_t)A, b = (uintptr_t)B, c = (uintptr_t)C;
+    int st = validate(M, N, K, a, lda, b, ldb, c, ldc);
+    if (st != GR_OK) return st;
+    int path = choose_path(M, N, K, a, lda, b, ldb, c, ldc);
+    if (forced >= 0 && path != GR_PATH_NONE) {
+        if (forced == GR_PATH_TILE) {
+            if (!tile_fast_ok(M, N, K, a, lda, b, ldb, c, ldc)) return GR_ERR_INVALID_PATH;
+        } else if (forced == GR_PATH_SMALL_M) {
+            if (K == 0 || !smallm_ok(M, N, K, a, lda, b, ldb)) return GR_ERR_INVALID_PATH;
+        } else if (forced != GR_PATH_TILE_EDGE) {
+            return GR_ERR_INVALID_PATH;
+        }
+        path = forced;
+    }
+    if (path == GR_PATH_NONE) return GR_OK;
+    st = check_device();
+    if (st != GR_OK) return st;
+    gr_plan_t p;
+    fill_plan(path, M, N, K, a, lda, b, ldb, c, ldc, &p);
+    return run(p, M, N, K, A, lda, B, ldb, C, ldc, static_cast<hipStream_t>(stream));
+}
+
+}  // namespace
+
+extern "C" {
+
+int gemm_relu_f16(int64_t M, int64_t N, int64_t K, const uint16_t* A, int64_t lda, const uint16_t* B, int64_t ldb,
+                  uint16_t* C, int64_t ldc, void* stream) {
+    return entry(M, N, K, A, lda, B, ldb, C, ldc, stream, -1);
+}
+
+int gemm_relu_f16_forced(int64_t M, int64_t N, int64_t K, const uint16_t* A, int64_t lda, const uint16_t* B,
+                         int64_t ldb, uint16_t* C, int64_t ldc, void* stream, int path) {
+    if (path != GR_PATH_TILE && path != GR_PATH_TILE_EDGE && path != GR_PATH_SMALL_M) return GR_ERR_INVALID_PATH;
+    return entry(M, N, K, A, lda, B, ldb, C, ldc, stream, path);
+}
+
+int gemm_relu_f16_plan(int64_t M, int64_t N, int64_t K, const uint16_t* A, int64_t lda, const uint16_t* B,
+                       int64_t ldb, const uint16_t* C, int64_t ldc, gr_plan_t* out) {
+    if (!out) return GR_ERR_INVALID_ARG;
+    const uintptr_t a = (uintptr_t)A, b = (uintptr_t)B, c = (uintptr_t)C;
+    int st = validate(M, N, K, a, lda, b, ldb, c, ldc);
+    if (st != GR_OK) return st;
+    fill_plan(choose_path(M, N, K, a, lda, b, ldb, c, ldc), M, N, K, a, lda, b, ldb, c, ldc, out);
+    return GR_OK;
+}
+
+const char* gemm_relu_status_string(int status) {
+    switch (status) {
+        case GR_OK: return "GR_OK";
+        case GR_ERR_INVALID_DIM: return "GR_ERR_INVALID_DIM";
+        case GR_ERR_INVALID_LD: return "GR_ERR_INVALID_LD";
+        case GR_ERR_NULL_PTR: return "GR_ERR_NULL_PTR";
+        case GR_ERR_ALIAS: return "GR_ERR_ALIAS";
+        case GR_ERR_TOO_LARGE: return "GR_ERR_TOO_LARGE";
+        case GR_ERR_NO_DEVICE: return "GR_ERR_NO_DEVICE";
+        case GR_ERR_UNSUPPORTED_DEVICE: return "GR_ERR_UNSUPPORTED_DEVICE";
+        case GR_ERR_LAUNCH: return "GR_ERR_LAUNCH";
+        case GR_ERR_INVALID_PATH: return "GR_ERR_INVALID_PATH";
+        case GR_ERR_INVALID_ARG: return "GR_ERR_INVALID_ARG";
+        default: return "GR_ERR_UNKNOWN";
+    }
+}
+
+int gemm_relu_version(void) { return kVersion; }
+
+}  // extern "C"

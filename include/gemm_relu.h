@@ -1,0 +1,143 @@
+/*
+ * gemm_relu.h -- C ABI of the MI355X (gfx950) fused fp16 GEMM + ReLU library.
+ *
+ * The one operation:  C := ReLU(A * B)
+ *   A  M x K, B  K x N, C  M x N, all IEEE binary16, row-major with a row
+ *   pitch (element (i, k) of A at A[i*lda + k], likewise B and C).
+ *   Products accumulate in fp32 from a cleared accumulator; ReLU acts on the
+ *   fp32 sum; the result is rounded to fp16 (nearest, ties to even) only when
+ *   it is written.  This is the tiled GEMM with a fused elementwise epilogue
+ *   of the TileLang tutorial, chapter "GEMM walkthrough and parameter
+ *   derivation" (fp16 operands, fp32 fragment cleared before the K loop), of
+ *   the blog "TileLang programming basics", section 2 (the FP16 GEMM + ReLU
+ *   listing: max(C_local, 0) on the fp32 fragment, cast on write-back), and of
+ *   "Writing high-performance kernels in TileLang", section "Writing a GEMM"
+ *   (the caller passes C, which is only written).
+ *
+ * Conventions shared by every entry point:
+ *   - Pointers A, B, C are DEVICE pointers (HIP) to fp16 bit patterns, owned
+ *     by the caller.  The library allocates nothing on the call path, keeps no
+ *     per-call state and never frees caller memory.
+ *   - C is never read (there is no beta); elements of C outside the M x N
+ *     window (columns N..ldc-1, rows >= M) are never written.  Padding columns
+ *     of A (K..lda-1) and B (N..ldb-1) are never used.
+ *   - Any M, N, K >= 0 work with the same library: tile shapes are fixed when
+ *     the library is built; edges that do not fill a tile are guarded.
+ *     M == 0 or N == 0: nothing is launched, GR_OK.  K == 0: C = +0.
+ *   - Pitches: lda >= max(1, K), ldb >= max(1, N), ldc >= max(1, N).  Any
+ *     element alignment is accepted; 16-byte aligned rows take faster code.
+ *   - The byte range C spans must not overlap the ranges of A or B.
+ *   - stream: a hipStream_t passed as void* (NULL = the null stream).  The
+ *     call only enqueues work and returns; a fault inside a kernel surfaces at
+ *     the caller's next synchronisation.  There is no implicit device sync.
+ *   - Errors: every entry point returns GR_OK (0) or a negative GR_ERR_* code
+ *     and never throws across the ABI.  Argument checks run before any HIP
+ *     call, so they work without a GPU.  gemm_relu_status_string() names a
+ *     code.
+ *   - Thread safety: calls are reentrant; per-device properties are cached
+ *     once with thread-safe initialisation.
+ */
+#ifndef GEMM_RELU_H_
+#define GEMM_RELU_H_
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ---- status codes --------------------------------------------------------- */
+#define GR_OK                        0
+#define GR_ERR_INVALID_DIM          -1 /* M, N or K negative                              */
+#define GR_ERR_INVALID_LD           -2 /* lda < max(1,K), ldb < max(1,N) or ldc < max(1,N) */
+#define GR_ERR_NULL_PTR             -3 /* NULL pointer for a non-empty operand            */
+#define GR_ERR_ALIAS                -4 /* C's byte range overlaps A's or B's              */
+#define GR_ERR_TOO_LARGE            -5 /* a dimension >= 2^31 or an operand span >= 2^62 B */
+#define GR_ERR_NO_DEVICE            -6 /* no HIP device visible                            */
+#define GR_ERR_UNSUPPORTED_DEVICE   -7 /* current device is not gfx950                     */
+#define GR_ERR_LAUNCH               -8 /* the kernel launch was rejected by the runtime    */
+#define GR_ERR_INVALID_PATH         -9 /* forced path unknown or not applicable            */
+#define GR_ERR_INVALID_ARG         -10 /* a NULL output struct or other bad argument        */
+
+/* ---- execution paths chosen by the planner --------------------------------- */
+#define GR_PATH_NONE       0 /* empty output: nothing to launch                            */
+#define GR_PATH_TILE       1 /* MFMA tile kernel, every edge a whole tile, 16-B rows        */
+#define GR_PATH_TILE_EDGE  2 /* MFMA tile kernel with edge guards and narrow loads          */
+#define GR_PATH_SMALL_M    3 /* bandwidth kernel for GEMV-like shapes (few rows of A)       */
+
+/* What the planner decided for one problem.  Filled by gemm_relu_f16_plan. */
+typedef struct gr_plan_t {
+    int32_t path;        /* GR_PATH_*                                                  */
+    int32_t block_m;     /* rows of C per workgroup                                   */
+    int32_t block_n;     /* columns of C per workgroup                                */
+    int32_t block_k;     /* K step per pipeline stage                                 */
+    int32_t stages;      /* LDS buffers in the K pipeline                             */
+    int32_t threads;     /* threads per workgroup                                     */
+    int64_t grid;        /* workgroups launched (1-D grid)                            */
+    int32_t vec_a;       /* fp16 elements per global load of A (8, 4, 2 or 1)         */
+    int32_t vec_b;       /* fp16 elements per global load of B                        */
+    int32_t vec_c;       /* fp16 elements per global store of C                       */
+    int32_t group_m;     /* tile rows per workgroup-order group (L2 reuse)           */
+} gr_plan_t;
+
+/*
+ * gemm_relu_f16 -- C := ReLU(A * B), fp16 in, fp32 accumulate, fp16 out.
+ *   M, N, K   problem size (>= 0)
+ *   A, lda    device pointer to M x K fp16, row pitch lda elements
+ *   B, ldb    device pointer to K x N fp16, row pitch ldb elements
+ *   C, ldc    device pointer to M x N fp16 output, row pitch ldc elements
+ *   stream    hipStream_t as void* (NULL = null stream)
+ * Returns GR_OK or a GR_ERR_* code (see above); on error nothing is launched.
+ * The path (tile, edge-guarded tile, small-M) is chosen by the same planner
+ * gemm_relu_f16_plan exposes; all paths produce the same result up to fp32
+ * summation order.
+ */
+int gemm_relu_f16(int64_t M, int64_t N, int64_t K,
+                  const uint16_t* A, int64_t lda,
+                  const uint16_t* B, int64_t ldb,
+                  uint16_t* C, int64_t ldc,
+                  void* stream);
+
+/*
+ * gemm_relu_f16_plan -- pure planner: validates the arguments exactly as
+ * gemm_relu_f16 does and reports the path, tile and grid it would launch.
+ * Makes no HIP call and touches no memory behind the pointers: it only uses
+ * their values (for alignment and overlap checks), so it runs without a GPU.
+ *   out   host pointer to a gr_plan_t to fill (must not be NULL)
+ * Returns GR_OK or the GR_ERR_* code gemm_relu_f16 would return for the same
+ * arguments (device errors excepted).
+ */
+int gemm_relu_f16_plan(int64_t M, int64_t N, int64_t K,
+                       const uint16_t* A, int64_t lda,
+                       const uint16_t* B, int64_t ldb,
+                       const uint16_t* C, int64_t ldc,
+                       gr_plan_t* out);
+
+/*
+ * gemm_relu_f16_forced -- as gemm_relu_f16, but runs the given path instead of
+ * the planner's choice, for tests that cross-check the paths on one input.
+ *   path  GR_PATH_TILE, GR_PATH_TILE_EDGE or GR_PATH_SMALL_M.
+ * GR_PATH_TILE is accepted only when the planner's conditions for it hold
+ * (whole tiles, 16-byte aligned rows); GR_PATH_SMALL_M only when the small-M
+ * kernel's alignment conditions hold (see gemm_relu_f16_plan).  Otherwise
+ * GR_ERR_INVALID_PATH and nothing is launched.  GR_PATH_TILE_EDGE accepts any
+ * valid problem.
+ */
+int gemm_relu_f16_forced(int64_t M, int64_t N, int64_t K,
+                         const uint16_t* A, int64_t lda,
+                         const uint16_t* B, int64_t ldb,
+                         uint16_t* C, int64_t ldc,
+                         void* stream, int path);
+
+/* Static, NUL-terminated name of a status code ("GR_OK", "GR_ERR_ALIAS", ...).
+   Unknown codes give "GR_ERR_UNKNOWN". */
+const char* gemm_relu_status_string(int status);
+
+/* Library version as MAJOR*10000 + MINOR*100 + PATCH. */
+int gemm_relu_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GEMM_RELU_H_ */

@@ -1,0 +1,201 @@
+"""The C-ABI boundary, checked without a GPU.
+
+* the built library loads and exports every function include/gemm_relu.h
+  declares;
+* argument validation returns the documented codes before any HIP call;
+* the pure planner picks the documented path for each workload shape;
+* status strings and constants match the header.
+No compute call is made here: the parity tests live in test_parity_gpu.py.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+import dense_gemm_epilogue_tiled_amd as gr
+import synth
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "gemm_relu.h")
+
+# Fake device addresses: only their values are used by validation/planning.
+BASE_A = 0x7F0000000000
+BASE_B = 0x7F2000000000
+BASE_C = 0x7F4000000000
+
+
+def header_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return re.findall(r"^\s*(?:const\s+)?\w+\*?\s+\**(\w+)\s*\(", text, flags=re.M)
+
+
+def header_defines():
+    text = open(HEADER).read()
+    return {m.group(1): int(m.group(2)) for m in re.finditer(r"#define\s+(GR_\w+)\s+(-?\d+)", text)}
+
+
+def test_library_exports_every_declared_symbol():
+    names = header_functions()
+    assert set(names) >= {"gemm_relu_f16", "gemm_relu_f16_plan", "gemm_relu_f16_forced",
+                          "gemm_relu_status_string", "gemm_relu_version"}
+    lib = ctypes.CDLL(gr.LIB_PATH)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_python_constants_match_header():
+    d = header_defines()
+    for k, v in d.items():
+        assert getattr(gr, k) == v, k
+
+
+def test_plan_struct_layout_matches_header():
+    text = open(HEADER).read()
+    body = re.search(r"typedef struct gr_plan_t \{(.*?)\} gr_plan_t;", text, flags=re.S).group(1)
+    fields = re.findall(r"(int32_t|int64_t)\s+(\w+);", body)
+    assert [f for _, f in fields] == [f for f, _ in gr.gr_plan_t._fields_]
+    sizes = {"int32_t": 4, "int64_t": 8}
+    assert [sizes[t] for t, _ in fields] == [ctypes.sizeof(t) for _, t in gr.gr_plan_t._fields_]
+
+
+def test_status_strings():
+    for name, code in header_defines().items():
+        if name.startswith("GR_ERR_") or name == "GR_OK":
+            assert gr.gemm_relu_status_string(code) == name
+    assert gr.gemm_relu_status_string(12345) == "GR_ERR_UNKNOWN"
+    assert gr.gemm_relu_version() >= 100
+
+
+def plan(M, N, K, lda=None, ldb=None, ldc=None, a=BASE_A, b=BASE_B, c=BASE_C):
+    lda = max(K, 1) if lda is None else lda
+    ldb = max(N, 1) if ldb is None else ldb
+    ldc = max(N, 1) if ldc is None else ldc
+    return gr.gemm_relu_f16_plan(M, N, K, a, lda, b, ldb, c, ldc)
+
+
+@pytest.mark.parametrize("args,code", [
+    ((-1, 4, 4), gr.GR_ERR_INVALID_DIM),
+    ((4, -1, 4), gr.GR_ERR_INVALID_DIM),
+    ((4, 4, -1), gr.GR_ERR_INVALID_DIM),
+    ((1 << 31, 4, 4), gr.GR_ERR_TOO_LARGE),
+])
+def test_invalid_dims(args, code):
+    st, _ = plan(*args, lda=8, ldb=8, ldc=8)
+    assert st == code
+
+
+def test_invalid_pitches():
+    assert plan(8, 8, 8, lda=7)[0] == gr.GR_ERR_INVALID_LD
+    assert plan(8, 8, 8, ldb=7)[0] == gr.GR_ERR_INVALID_LD
+    assert plan(8, 8, 8, ldc=7)[0] == gr.GR_ERR_INVALID_LD
+    assert plan(8, 8, 0, lda=0)[0] == gr.GR_ERR_INVALID_LD  # lda >= max(1, K)
+    assert plan(8, 8, 0, lda=1)[0] == gr.GR_OK
+
+
+def test_null_pointers():
+    assert plan(8, 8, 8, a=0)[0] == gr.GR_ERR_NULL_PTR
+    assert plan(8, 8, 8, b=0)[0] == gr.GR_ERR_NULL_PTR
+    assert plan(8, 8, 8, c=0)[0] == gr.GR_ERR_NULL_PTR
+    # empty operands may be NULL
+    assert plan(8, 8, 0, a=0, b=0, lda=1)[0] == gr.GR_OK
+    assert plan(0, 8, 8, a=0, c=0)[0] == gr.GR_OK
+    assert plan(8, 0, 8, b=0, c=0, ldb=1, ldc=1)[0] == gr.GR_OK
+
+
+def test_alias_detection():
+    # C's bytes overlap A's
+    assert plan(8, 8, 8, a=BASE_A, c=BASE_A + 64)[0] == gr.GR_ERR_ALIAS
+    assert plan(8, 8, 8, b=BASE_B, c=BASE_B - 2 * 8 * 8 + 2)[0] == gr.GR_ERR_ALIAS
+    # adjacent but disjoint is fine
+    assert plan(8, 8, 8, a=BASE_A, c=BASE_A + 2 * 8 * 8)[0] == gr.GR_OK
+
+
+def test_span_overflow_is_too_large():
+    assert plan(1 << 30, 8, 8, lda=1 << 40)[0] == gr.GR_ERR_TOO_LARGE
+
+
+def test_plan_for_each_workload():
+    expect = {
+        "square1024": gr.GR_PATH_TILE,
+        "square4096": gr.GR_PATH_TILE,
+        "ragged4099x3071x2050": gr.GR_PATH_TILE_EDGE,
+        "mlp8192x28672x8192": gr.GR_PATH_TILE,
+        "smallm8x16384x8192": gr.GR_PATH_SMALL_M,
+    }
+    for name, w in synth.WORKLOADS.items():
+        st, p = plan(w.M, w.N, w.K)
+        assert st == gr.GR_OK
+        assert p["path"] == expect[name], (name, p)
+        if p["path"] in (gr.GR_PATH_TILE, gr.GR_PATH_TILE_EDGE):
+            tiles = -(-w.M // p["block_m"]) * -(-w.N // p["block_n"])
+            assert p["grid"] == tiles
+        else:
+            assert p["grid"] == -(-w.N // p["block_n"])
+
+
+def test_plan_ragged_vector_widths():
+    # lda = 2050 (even): 4-byte loads; ldb = ldc = 3071 (odd): element loads/stores
+    st, p = plan(4099, 3071, 2050)
+    assert st == gr.GR_OK and (p["vec_a"], p["vec_b"], p["vec_c"]) == (2, 1, 1)
+    # misaligned base pointer drops to narrower loads
+    st, p = plan(512, 512, 512, a=BASE_A + 2)
+    assert p["path"] == gr.GR_PATH_TILE_EDGE and p["vec_a"] == 1
+
+
+def test_plan_empty_and_k_zero():
+    assert plan(0, 8, 8)[1]["path"] == gr.GR_PATH_NONE
+    assert plan(8, 0, 8, ldb=1, ldc=1)[1]["path"] == gr.GR_PATH_NONE
+    st, p = plan(300, 300, 0, lda=1)
+    assert st == gr.GR_OK and p["path"] == gr.GR_PATH_TILE_EDGE
+
+
+def test_plan_small_m_threshold():
+    assert plan(16, 4096, 4096)[1]["path"] == gr.GR_PATH_SMALL_M
+    assert plan(17, 4096, 4096)[1]["path"] == gr.GR_PATH_TILE_EDGE
+    assert plan(1, 1, 1)[1]["path"] == gr.GR_PATH_TILE_EDGE  # B row pitch 1: not 8-byte aligned
+
+
+def test_plan_null_output_struct():
+    lib = gr.lib()
+    assert lib.gemm_relu_f16_plan(8, 8, 8, BASE_A, 8, BASE_B, 8, BASE_C, 8, None) == gr.GR_ERR_INVALID_ARG
+
+
+def test_calls_validate_before_touching_the_device():
+    # Invalid arguments are rejected identically with or without a GPU.
+    assert gr.gemm_relu_f16(-1, 8, 8, BASE_A, 8, BASE_B, 8, BASE_C, 8) == gr.GR_ERR_INVALID_DIM
+    assert gr.gemm_relu_f16(8, 8, 8, BASE_A, 8, BASE_B, 8, BASE_A, 8) == gr.GR_ERR_ALIAS
+    assert gr.gemm_relu_f16_forced(8, 8, 8, BASE_A, 8, BASE_B, 8, BASE_C, 8, None, 99) == gr.GR_ERR_INVALID_PATH
+    # tile path forced on a shape that does not fill whole tiles
+    assert gr.gemm_relu_f16_forced(300, 256, 64, BASE_A, 64, BASE_B, 256, BASE_C, 256, None,
+                                   gr.GR_PATH_TILE) == gr.GR_ERR_INVALID_PATH
+    # small-M forced with too many rows
+    assert gr.gemm_relu_f16_forced(64, 256, 64, BASE_A, 64, BASE_B, 256, BASE_C, 256, None,
+                                   gr.GR_PATH_SMALL_M) == gr.GR_ERR_INVALID_PATH
+    # empty problems succeed without a launch
+    assert gr.gemm_relu_f16(0, 8, 8, 0, 8, BASE_B, 8, 0, 8) == gr.GR_OK
+
+
+def _gpu_visible():
+    try:
+        import torch
+        return torch.cuda.device_count() > 0
+    except Exception:
+        return False
+
+
+@pytest.mark.skipif(_gpu_visible(), reason="checks the no-device error path")
+def test_no_device_error_without_gpu():
+    assert gr.gemm_relu_f16(8, 8, 8, BASE_A, 8, BASE_B, 8, BASE_C, 8) == gr.GR_ERR_NO_DEVICE
+
+
+def test_product_path_never_imports_the_oracle():
+    """The product package and the library sources name nothing from oracle/."""
+    pkg = os.path.join(ROOT, "dense_gemm_epilogue_tiled_amd")
+    for dirpath, _, files in os.walk(pkg):
+        for f in files:
+            if f.endswith((".py", ".hip", ".hpp", ".cpp", ".h")):
+                text = open(os.path.join(dirpath, f)).read()
+                assert "import oracle" not in text and "from oracle" not in text, f
+                assert "oracle_gemm_relu" not in text, f

@@ -1,0 +1,257 @@
+"""GPU parity: the HIP path through the C ABI against the CPU oracle.
+
+Bar: for every checked element |gpu - oracle| <= 1e-2 + 1e-2 |oracle| (the
+tolerance the GEMM+ReLU listings verify with, "Writing high-performance
+kernels in TileLang", section "Writing a GEMM"; the blog "TileLang programming
+basics", section 6, explains why the reference must accumulate in fp32), no
+NaN or Inf, and bit-exact where the closed form is exact.
+"""
+import numpy as np
+import pytest
+
+import dense_gemm_epilogue_tiled_amd as gr
+import oracle
+import synth
+from gpu_util import (as_f64, assert_parity, call, edge_indices, from_dev, full_dev, log,
+                      to_dev)
+
+pytestmark = [pytest.mark.gpu, pytest.mark.usefixtures("oracle_lib")]
+
+SENTINEL = 0x7E5A  # a quiet NaN: the kernel never writes NaN, so any survivor was never written
+
+
+def run_full(A, B, M, N, K, lda=None, ldb=None, ldc=None, path=None, offsets=(0, 0, 0), c_fill=SENTINEL,
+             c_rows=None):
+    lda = max(K, 1) if lda is None else lda
+    ldb = max(N, 1) if ldb is None else ldb
+    ldc = max(N, 1) if ldc is None else ldc
+    dA = to_dev(A) if A.size else None
+    dB = to_dev(B) if B.size else None
+    rows = M if c_rows is None else c_rows
+    dC = full_dev((rows * ldc + offsets[2] + 8,), c_fill)
+    log("M=%d N=%d K=%d lda=%d ldb=%d ldc=%d path=%s offsets=%s" % (M, N, K, lda, ldb, ldc, path, offsets))
+    st = call(M, N, K, dA, lda, dB, ldb, dC, ldc, path=path, offsets=offsets)
+    assert st == gr.GR_OK, gr.gemm_relu_status_string(st)
+    return from_dev(dC)
+
+
+def window(Cflat, M, N, ldc, off=0):
+    return Cflat[off:off + M * ldc].reshape(M, ldc)[:, :N]
+
+
+# ---- the five workloads, in the launch configuration the benchmark times ----
+
+@pytest.mark.parametrize("name", list(synth.WORKLOADS))
+def test_workload_parity(name):
+    w = synth.WORKLOADS[name]
+    A, B = synth.operands(w)
+    M, N, K = w.M, w.N, w.K
+    st, plan = gr.gemm_relu_f16_plan(M, N, K, 0x100000, K, 0x200000000000, N, 0x400000000000, N)
+    log("%s plan=%s" % (name, plan))
+    dA, dB = to_dev(A), to_dev(B)
+    dC = full_dev((M * N,), SENTINEL)
+    assert call(M, N, K, dA, K, dB, N, dC, N) == gr.GR_OK
+    C = from_dev(dC).reshape(M, N)
+    del dA, dB, dC
+    # every element written, none NaN/Inf (the sentinel is a NaN)
+    assert not np.any((C & 0x7C00) == 0x7C00)
+    if w.check == "full":
+        ref = oracle.gemm_relu_full(A, B)
+        rep = assert_parity(C, ref, name)
+    else:
+        bm, bn = max(plan["block_m"], 1), max(plan["block_n"], 1)
+        ii, jj = synth.sample_indices(M, N, 4096, w.seed)
+        rep = assert_parity(C[ii, jj], oracle.gemm_relu_elems(A, B, ii, jj), name + " sampled")
+        rows = edge_indices(M, bm)
+        cols = edge_indices(N, bn)
+        # one seeded interior tile boundary as well
+        rng = np.random.default_rng(w.seed)
+        tr = int(rng.integers(1, max(2, (M - 1) // bm))) * bm
+        tc = int(rng.integers(1, max(2, (N - 1) // bn))) * bn
+        rows = sorted(set(rows) | {r for r in (tr - 1, tr) if 0 <= r < M})
+        cols = sorted(set(cols) | {c for c in (tc - 1, tc) if 0 <= c < N})
+        assert_parity(C[rows, :], oracle.gemm_relu_rows(A, B, rows), name + " rows")
+        assert_parity(C[:, cols].T, oracle.gemm_relu_cols(A, B, cols), name + " cols")
+    log("%s parity %s" % (name, rep))
+    # C >= 0 everywhere, no -0
+    assert not np.any(C & 0x8000)
+
+
+# ---- shapes that do not fill tiles --------------------------------------------
+
+SWEEP = [1, 2, 7, 8, 9, 15, 16, 17, 31, 32, 33, 63, 64, 65, 127, 128, 129, 255, 256, 257]
+
+
+def _sweep_cases(count, seed):
+    rng = np.random.default_rng(seed)
+    cases = set()
+    while len(cases) < count:
+        cases.add(tuple(int(x) for x in rng.choice(SWEEP, 3)))
+    return sorted(cases)
+
+
+@pytest.mark.parametrize("M,N,K", _sweep_cases(60, 7))
+def test_tiny_shape_sweep(M, N, K):
+    A, B = synth.random_operands(M, N, K, seed=M * 7919 + N * 131 + K)
+    C = window(run_full(A, B, M, N, K), M, N, N)
+    assert_parity(C, oracle.gemm_relu_full(A, B), "sweep %dx%dx%d" % (M, N, K))
+
+
+@pytest.mark.parametrize("M,N,K", [(300, 520, 200), (257, 257, 257), (513, 255, 130), (1000, 700, 333)])
+def test_multi_tile_ragged(M, N, K):
+    A, B = synth.random_operands(M, N, K, seed=M + N + K)
+    C = window(run_full(A, B, M, N, K), M, N, N)
+    assert_parity(C, oracle.gemm_relu_full(A, B), "ragged %dx%dx%d" % (M, N, K))
+
+
+# ---- guards: poisoned padding, canaries, unaligned rows -----------------------
+
+@pytest.mark.parametrize("M,N,K,pa,pb,pc", [
+    (300, 270, 100, 9, 5, 3),      # odd pitches: element loads
+    (512, 512, 128, 8, 8, 8),      # aligned pitches larger than the rows
+    (260, 300, 70, 2, 2, 4),       # even pitches: 4-byte loads
+    (8, 1000, 300, 12, 8, 5),      # small-M path with padding
+])
+def test_poisoned_padding_and_canary(M, N, K, pa, pb, pc):
+    lda, ldb, ldc = K + pa, N + pb, N + pc
+    A, B = synth.random_operands(M, N, K, seed=41, lda=lda, ldb=ldb)  # padding = 65504
+    extra_rows = 3
+    Cflat = run_full(A, B, M, N, K, lda=lda, ldb=ldb, ldc=ldc, c_rows=M + extra_rows)
+    C = Cflat[:M * ldc].reshape(M, ldc)
+    assert_parity(C[:, :N], oracle.gemm_relu_full(A, B, M=M, N=N, K=K, lda=lda, ldb=ldb), "padded")
+    assert np.all(C[:, N:] == SENTINEL), "a padding column of C was written"
+    assert np.all(Cflat[M * ldc:] == SENTINEL), "a row past M was written"
+
+
+@pytest.mark.parametrize("offs", [(1, 0, 0), (0, 1, 0), (0, 0, 1), (3, 5, 7)])
+def test_unaligned_base_pointers(offs):
+    M, N, K = 320, 288, 96
+    A, B = synth.random_operands(M, N, K, seed=43)
+    Ap = np.concatenate([np.zeros(offs[0], np.uint16), A.ravel()])
+    Bp = np.concatenate([np.zeros(offs[1], np.uint16), B.ravel()])
+    Cflat = run_full(Ap, Bp, M, N, K, offsets=offs)
+    C = Cflat[offs[2]:offs[2] + M * N].reshape(M, N)
+    assert_parity(C, oracle.gemm_relu_full(A, B), "offsets %s" % (offs,))
+    assert np.all(Cflat[:offs[2]] == SENTINEL)
+    assert np.all(Cflat[offs[2] + M * N:] == SENTINEL)
+
+
+def test_k_zero_writes_zeros():
+    M, N = 300, 260
+    Cflat = run_full(np.zeros((M, 0), np.uint16), np.zeros((0, N), np.uint16), M, N, 0, lda=1)
+    assert np.all(Cflat[:M * N] == 0)
+    assert np.all(Cflat[M * N:] == SENTINEL)
+
+
+def test_empty_problems_launch_nothing():
+    dC = full_dev((64,), SENTINEL)
+    assert call(0, 8, 8, None, 8, None, 8, None, 8) == gr.GR_OK
+    assert call(8, 0, 8, None, 8, None, 1, dC, 1) == gr.GR_OK
+    assert np.all(from_dev(dC) == SENTINEL)
+
+
+# ---- closed forms on the GPU (exact) ------------------------------------------
+
+@pytest.mark.parametrize("M,N,K", [(1024, 1024, 1024), (300, 270, 2050), (8, 16384, 8192), (512, 256, 4096)])
+def test_all_ones_exact(M, N, K):
+    A = np.full((M, K), 0x3C00, np.uint16)
+    B = np.full((K, N), 0x3C00, np.uint16)
+    C = window(run_full(A, B, M, N, K), M, N, N)
+    assert np.all(as_f64(C) == K)
+
+
+def test_minus_one_times_one_exact_zero():
+    M, N, K = 260, 300, 96
+    C = window(run_full(np.full((M, K), 0xBC00, np.uint16), np.full((K, N), 0x3C00, np.uint16), M, N, K), M, N, N)
+    assert np.all(C == 0)
+
+
+@pytest.mark.parametrize("K", [64, 100, 256])
+def test_identity_A_exact(K):
+    A = np.eye(K, dtype=np.float16).view(np.uint16)
+    _, B = synth.random_operands(K, 280, K, seed=K)
+    C = window(run_full(A, B, K, 280, K), K, 280, 280)
+    assert np.array_equal(C, np.where(B.view(np.float16) > 0, B, np.uint16(0)))
+
+
+def test_diagonal_B_exact_rounding():
+    M, K = 512, 256
+    A, _ = synth.random_operands(M, K, K, seed=51)
+    d = (np.random.default_rng(52).standard_normal(K) * 3).astype(np.float16)
+    B = np.diag(d.astype(np.float64)).astype(np.float16).view(np.uint16)
+    C = window(run_full(A, B, M, K, K), M, K, K)
+    prod = A.view(np.float16).astype(np.float64) * d.astype(np.float64)[None, :]
+    assert np.array_equal(C, np.maximum(prod, 0.0).astype(np.float16).view(np.uint16))
+
+
+def test_rank1_powers_of_two_exact():
+    M, N, K = 256, 256, 512
+    p = (np.arange(M) % 9) - 6  # K * 2^(p+q) spans 2^0 .. 2^14: all exact in fp16
+    q = (np.arange(N) % 7) - 3
+    A = np.repeat((2.0 ** p)[:, None], K, axis=1).astype(np.float16).view(np.uint16)
+    B = np.repeat((2.0 ** q)[None, :], K, axis=0).astype(np.float16).view(np.uint16)
+    C = window(run_full(A, B, M, N, K), M, N, N)
+    assert np.array_equal(as_f64(C), K * 2.0 ** (p[:, None] + q[None, :]))
+
+
+# ---- invariants ---------------------------------------------------------------
+
+def test_scaling_by_two_bitwise():
+    M, N, K = 512, 512, 512
+    A, B = synth.random_operands(M, N, K, seed=61)
+    A2 = (A.view(np.float16).astype(np.float32) * 2).astype(np.float16).view(np.uint16)
+    C1 = as_f64(window(run_full(A, B, M, N, K), M, N, N))
+    C2 = as_f64(window(run_full(A2, B, M, N, K), M, N, N))
+    normal = (C1 >= 2.0 ** -14) & (C1 * 2 <= 65504)
+    assert np.array_equal(C2[normal], 2 * C1[normal])
+
+
+def test_deterministic_bitwise():
+    M, N, K = 1024, 768, 512
+    A, B = synth.random_operands(M, N, K, seed=62)
+    C1 = run_full(A, B, M, N, K)
+    C2 = run_full(A, B, M, N, K)
+    assert np.array_equal(C1, C2)
+
+
+def test_tile_and_edge_paths_bitwise_equal():
+    """The guarded variant runs the same MFMA sequence on whole tiles."""
+    M, N, K = 512, 768, 256
+    A, B = synth.random_operands(M, N, K, seed=63)
+    C1 = run_full(A, B, M, N, K, path=gr.GR_PATH_TILE)
+    C2 = run_full(A, B, M, N, K, path=gr.GR_PATH_TILE_EDGE)
+    assert np.array_equal(C1, C2)
+
+
+@pytest.mark.parametrize("M,N,K", [(8, 4096, 4096), (1, 640, 96), (16, 1000, 1000), (5, 128, 8200)])
+def test_small_m_and_tile_paths_agree(M, N, K):
+    A, B = synth.random_operands(M, N, K, seed=64, b_scale=K ** -0.5)
+    Cs = window(run_full(A, B, M, N, K, path=gr.GR_PATH_SMALL_M), M, N, N)
+    Ct = window(run_full(A, B, M, N, K, path=gr.GR_PATH_TILE_EDGE), M, N, N)
+    ref = oracle.gemm_relu_full(A, B)
+    assert_parity(Cs, ref, "small-M")
+    assert_parity(Ct, ref, "tile")
+    assert_parity(Cs, Ct, "small-M vs tile")
+
+
+def test_runs_on_a_side_stream():
+    t = pytest.importorskip("torch")
+    M, N, K = 512, 512, 256
+    A, B = synth.random_operands(M, N, K, seed=65)
+    dA, dB = to_dev(A), to_dev(B)
+    s = t.cuda.Stream()
+    with t.cuda.stream(s):
+        dC = full_dev((M * N,), SENTINEL)
+    assert call(M, N, K, dA, K, dB, N, dC, N, stream=s) == gr.GR_OK
+    assert_parity(from_dev(dC).reshape(M, N), oracle.gemm_relu_full(A, B), "side stream")
+
+
+def test_tensor_convenience_wrapper():
+    t = pytest.importorskip("torch")
+    M, N, K = 300, 200, 100
+    A, B = synth.random_operands(M, N, K, seed=66)
+    a = to_dev(A).view(t.float16).reshape(M, K)
+    b = to_dev(B).view(t.float16).reshape(K, N)
+    c = gr.gemm_relu(a, b)
+    t.cuda.synchronize()
+    assert_parity(c.view(t.int16).cpu().numpy().view(np.uint16), oracle.gemm_relu_full(A, B), "wrapper")
