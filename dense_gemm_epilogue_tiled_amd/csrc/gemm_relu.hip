@@ -13,6 +13,7 @@
 
 #include "../../include/gemm_relu.h"
 #include "smallm_kernel.hpp"
+#include "tile2_kernel.hpp"
 #include "tile_kernel.hpp"
 
 namespace {
@@ -79,16 +80,28 @@ bool smallm_ok(int64_t M, int64_t N, int64_t K, uintptr_t A, int64_t lda, uintpt
 
 bool tile_fast_ok(int64_t M, int64_t N, int64_t K, uintptr_t A, int64_t lda, uintptr_t B, int64_t ldb,
                   uintptr_t C, int64_t ldc) {
-    using namespace gr::tile;
+    using namespace gr::tile2;
     return M % BM == 0 && N % BN == 0 && K % BK == 0 && K > 0 && vec_width(A, lda) == 8 &&
-           vec_width(B, ldb) == 8 && vec_width_c(C, ldc) == 4;
+           vec_width(B, ldb) == 8 && vec_width_c(C, ldc) == 4 && lda <= MAX_LDA && ldb <= MAX_LDB;
 }
 
 void fill_plan(int path, int64_t M, int64_t N, int64_t K, uintptr_t A, int64_t lda, uintptr_t B,
                int64_t ldb, uintptr_t C, int64_t ldc, gr_plan_t* p) {
     std::memset(p, 0, sizeof(*p));
     p->path = path;
-    if (path == GR_PATH_TILE || path == GR_PATH_TILE_EDGE) {
+    if (path == GR_PATH_TILE) {
+        using namespace gr::tile2;
+        p->block_m = BM;
+        p->block_n = BN;
+        p->block_k = BK;
+        p->stages = STAGES;
+        p->threads = THREADS;
+        p->grid = (M / BM) * (N / BN);
+        p->vec_a = 8;
+        p->vec_b = 8;
+        p->vec_c = 4;
+        p->group_m = kGroupM;
+    } else if (path == GR_PATH_TILE_EDGE) {
         using namespace gr::tile;
         p->block_m = BM;
         p->block_n = BN;
@@ -96,8 +109,8 @@ void fill_plan(int path, int64_t M, int64_t N, int64_t K, uintptr_t A, int64_t l
         p->stages = 2;
         p->threads = THREADS;
         p->grid = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
-        p->vec_a = path == GR_PATH_TILE ? 8 : vec_width(A, lda);
-        p->vec_b = path == GR_PATH_TILE ? 8 : vec_width(B, ldb);
+        p->vec_a = vec_width(A, lda);
+        p->vec_b = vec_width(B, ldb);
         p->vec_c = vec_width_c(C, ldc);
         p->group_m = kGroupM;
     } else if (path == GR_PATH_SMALL_M) {
@@ -176,7 +189,11 @@ int run(const gr_plan_t& p, int64_t M, int64_t N, int64_t K, const uint16_t* A, 
         int64_t ldb, uint16_t* C, int64_t ldc, hipStream_t stream) {
     switch (p.path) {
         case GR_PATH_NONE: return GR_OK;
-        case GR_PATH_TILE: return launch_tile<false, 8, 8>(p, M, N, K, A, lda, B, ldb, C, ldc, stream);
+        case GR_PATH_TILE: {
+            using namespace gr::tile2;
+            return launch(gemm_relu_tile2_kernel, p.grid, THREADS, stream, A, B, C, M, N, K, lda, ldb, ldc,
+                          (uint32_t)(M / BM), (uint32_t)(N / BN), (uint32_t)p.group_m);
+        }
         case GR_PATH_TILE_EDGE:
             switch (p.vec_a) {
                 case 8: return launch_tile_vb<true, 8>(p, M, N, K, A, lda, B, ldb, C, ldc, stream);

@@ -223,6 +223,19 @@ def test_tile_and_edge_paths_bitwise_equal():
     assert np.array_equal(C1, C2)
 
 
+@pytest.mark.parametrize("K", [32, 64, 96, 128, 160, 192, 224, 256, 288, 1056])
+def test_tile_pipeline_every_strip_count(K):
+    """Whole tiles through the pipelined kernel, for every K-loop length up to
+    the steady state plus odd and even tails, bitwise against the guarded
+    kernel (both accumulate the same 16-deep MFMA steps in the same order)."""
+    M, N = 512, 256
+    A, B = synth.random_operands(M, N, K, seed=K)
+    C1 = run_full(A, B, M, N, K, path=gr.GR_PATH_TILE)
+    C2 = run_full(A, B, M, N, K, path=gr.GR_PATH_TILE_EDGE)
+    assert_parity(window(C1, M, N, N), oracle.gemm_relu_full(A, B), "tile K=%d" % K)
+    assert np.array_equal(C1, C2)
+
+
 @pytest.mark.parametrize("M,N,K", [(8, 4096, 4096), (1, 640, 96), (16, 1000, 1000), (5, 128, 8200)])
 def test_small_m_and_tile_paths_agree(M, N, K):
     A, B = synth.random_operands(M, N, K, seed=64, b_scale=K ** -0.5)
