@@ -28,9 +28,10 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 import synth  # noqa: E402
+from dense_gemm_epilogue_tiled_amd import roofline  # noqa: E402  (host arithmetic only)
 
-MFMA_F16_PEAK_TFLOPS = 2516.6  # MI355X dense fp16 MFMA: 256 CU x 4096 FLOP/clk x 2.4 GHz (published 2.5 PFLOP/s)
-HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published 8 TB/s
+MFMA_F16_PEAK_TFLOPS = roofline.MI355X_MFMA_F16_TFLOPS
+HBM_PEAK_GBS = roofline.MI355X_HBM_GBS
 
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.txt")
 
@@ -47,9 +48,7 @@ def kernel_source_hash() -> str:
 
 
 def algorithmic(w):
-    flops = 2.0 * w.M * w.N * w.K
-    nbytes = 2.0 * (w.M * w.K + w.K * w.N + w.M * w.N)
-    return flops, nbytes
+    return roofline.algorithmic_flops(w.M, w.N, w.K), roofline.algorithmic_bytes(w.M, w.N, w.K)
 
 
 def make_device_operands(torch, w, copies=1):
@@ -160,15 +159,14 @@ def bench_workload(gr, torch, w, reps, cold):
             r()
     torch.cuda.synchronize()
     if cold:
-        # rotate 4 copies of B (4 x |B| > the 256 MB last-level cache), and
-        # stream a 512 MiB buffer between launches (outside the events)
-        flush = torch.empty(256 * 1024 * 1024, dtype=torch.float16, device="cuda")
+        # Rotate 4 copies of B (4 x |B| is well above the 256 MB last-level
+        # cache), so every launch streams B from HBM.  No flush buffer is
+        # written: its dirty lines would be written back during the timed
+        # launch and count against it.
         times = []
         for i in range(reps):
-            flush.zero_()
             t = time_launches(torch, runs[i % copies], stream, 1)
             times.append(t[0])
-        del flush
     else:
         times = time_launches(torch, runs[0], stream, reps)
     del A, Bs, C

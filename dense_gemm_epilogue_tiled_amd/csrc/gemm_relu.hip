@@ -14,6 +14,7 @@
 #include "../../include/gemm_relu.h"
 #include "smallm_kernel.hpp"
 #include "tile2_kernel.hpp"
+#include "tile_pp_kernel.hpp"
 #include "tile_kernel.hpp"
 
 namespace {
@@ -190,9 +191,15 @@ int run(const gr_plan_t& p, int64_t M, int64_t N, int64_t K, const uint16_t* A, 
     switch (p.path) {
         case GR_PATH_NONE: return GR_OK;
         case GR_PATH_TILE: {
+#ifdef GR_TILE_PP
+            using namespace gr::pp;
+            return launch(gemm_relu_pp_kernel, p.grid, THREADS, stream, A, B, C, M, N, K, lda, ldb, ldc,
+                          (uint32_t)(M / BM), (uint32_t)(N / BN), (uint32_t)p.group_m);
+#else
             using namespace gr::tile2;
             return launch(gemm_relu_tile2_kernel, p.grid, THREADS, stream, A, B, C, M, N, K, lda, ldb, ldc,
                           (uint32_t)(M / BM), (uint32_t)(N / BN), (uint32_t)p.group_m);
+#endif
         }
         case GR_PATH_TILE_EDGE:
             switch (p.vec_a) {
