@@ -14,6 +14,7 @@
 #include "../../include/gemm_relu.h"
 #include "smallm_kernel.hpp"
 #include "tile2_kernel.hpp"
+#include "tile3_kernel.hpp"
 #include "tile_pp_kernel.hpp"
 #include "tile_kernel.hpp"
 
@@ -196,6 +197,11 @@ int run(const gr_plan_t& p, int64_t M, int64_t N, int64_t K, const uint16_t* A, 
             return launch(gemm_relu_pp_kernel, p.grid, THREADS, stream, A, B, C, M, N, K, lda, ldb, ldc,
                           (uint32_t)(M / BM), (uint32_t)(N / BN), (uint32_t)p.group_m);
 #else
+            if (K % gr::tile3::BKA == 0) {
+                using namespace gr::tile3;
+                return launch(gemm_relu_tile3_kernel, p.grid, THREADS, stream, A, B, C, M, N, K, lda, ldb, ldc,
+                              (uint32_t)(M / BM), (uint32_t)(N / BN), (uint32_t)p.group_m);
+            }
             using namespace gr::tile2;
             return launch(gemm_relu_tile2_kernel, p.grid, THREADS, stream, A, B, C, M, N, K, lda, ldb, ldc,
                           (uint32_t)(M / BM), (uint32_t)(N / BN), (uint32_t)p.group_m);

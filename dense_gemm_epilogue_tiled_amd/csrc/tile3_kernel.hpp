@@ -1,0 +1,343 @@
+// Pipelined MFMA tile kernel for whole tiles with K a multiple of 64.
+//
+// The pipelined whole-tile kernel (see tile2_kernel.hpp) with one change in
+// how A is staged: A moves in 64-deep strips (128-byte row segments, one
+// full cache line per row) through a 3-slot ring, while B keeps its 32-deep
+// strips (512-byte row segments) in a 4-slot ring.  With 32-deep A strips
+// every A row segment is half a cache line, and A alone produces two thirds
+// of all L2 requests; full-line segments halve that.  LDS: 4 x 16 KiB (B) +
+// 3 x 32 KiB (A) = 160 KiB, all of it.
+//
+// One step still covers one 32-deep B strip kt (32 MFMAs per wave).  Step kt
+// uses half kt%2 of A strip kt/2.  Every step issues 8 copies per wave: half
+// of A strip kt/2 + 2 and the whole of B strip kt+3, so "everything issued
+// two or more steps ago has landed" is one vmcnt wait in the steady state.
+//   A strip j lives in slot j % 3; it is last read while step 2j runs (the
+//   reads for step 2j+1), so strip j+3 may be copied from step 2j+2 on; the
+//   two halves of strip a+2 are copied in steps 2a and 2a+1.
+//   A tile layout [256 m][64 k]: 128-byte rows, chunk index XOR (m/2)%8, so
+//   16 consecutive rows reading one chunk hit 16 distinct bank groups.
+#pragma once
+
+#include <type_traits>
+
+#include "common.hpp"
+#include "tile2_kernel.hpp"
+
+namespace gr {
+
+namespace tile3 {
+
+constexpr int BM = 256;
+constexpr int BN = 256;
+constexpr int BK = 32;      // K per step (B strip)
+constexpr int BKA = 64;     // K per A strip
+constexpr int B_SLOTS = 4;
+constexpr int A_SLOTS = 3;
+constexpr int THREADS = 256;
+constexpr int WAVE_TM = 128;
+constexpr int WAVE_TN = 128;
+constexpr int FM = WAVE_TM / 32;
+constexpr int FN = WAVE_TN / 32;
+constexpr int KSUB = BK / 16;
+constexpr int B_SLOT_BYTES = BK * BN * 2;     // 16 KiB
+constexpr int A_SLOT_BYTES = BM * BKA * 2;    // 32 KiB
+constexpr int A_BASE = B_SLOTS * B_SLOT_BYTES;  // 64 KiB
+constexpr int LDS_BYTES = A_BASE + A_SLOTS * A_SLOT_BYTES;  // 160 KiB
+constexpr int64_t MAX_LDA = tile2::MAX_LDA;
+constexpr int64_t MAX_LDB = tile2::MAX_LDB;
+
+#define GR_LDS __attribute__((address_space(3)))
+
+// Byte offset of chunk c (8 fp16) of row m of an A slot (128-byte rows).
+__device__ __forceinline__ uint32_t a64_off(uint32_t m, uint32_t c) { return m * 128u + ((c ^ ((m >> 1) & 7u)) << 4); }
+
+struct Frags {
+    f16x8 a[KSUB][FM];
+    f16x8 b[KSUB][FN];
+};
+
+__global__ __launch_bounds__(THREADS, 1) void gemm_relu_tile3_kernel(
+    const uint16_t* __restrict__ A, const uint16_t* __restrict__ B, uint16_t* __restrict__ C, int64_t M, int64_t N,
+    int64_t K, int64_t lda, int64_t ldb, int64_t ldc, uint32_t tiles_m, uint32_t tiles_n, uint32_t group_m) {
+    using tile2::b_off;
+    using tile2::barrier;
+    using tile2::dma16;
+    using tile2::pin;
+    using tile2::read_a_operand;
+    using tile2::read_b_operand;
+    using tile2::wait_vmcnt;
+
+    __shared__ __attribute__((aligned(1024))) uint8_t lds[LDS_BYTES];
+
+    const uint32_t tid = threadIdx.x;
+    const uint32_t lane = tid & 63u;
+    const uint32_t wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const uint32_t wm = wave >> 1;
+    const uint32_t wn = wave & 1u;
+
+    uint32_t tm, tn;
+    tile_of_workgroup(blockIdx.x, gridDim.x, tiles_m, tiles_n, group_m, tm, tn);
+    const int64_t m0 = (int64_t)tm * BM;
+    const int64_t n0 = (int64_t)tn * BN;
+
+    // ---- copies -------------------------------------------------------------
+    // A strip (32 KiB) = 32 blocks of 8 rows x 128 bytes; this wave fills
+    // blocks 8w .. 8w+7, the first four in the even step, the rest in the odd
+    // one.  lane -> row lane/8, slot lane%8 (chunk slot XOR (row/2)%8).
+    // B strip (16 KiB) = 16 blocks of 2 rows x 512 bytes; this wave fills
+    // blocks 4w .. 4w+3.  lane -> row lane/32, slot lane%32.
+    const uint8_t* base_a = reinterpret_cast<const uint8_t*>(A + m0 * lda);
+    const uint8_t* base_b = reinterpret_cast<const uint8_t*>(B + n0);
+    const int64_t step_a = BKA * 2;
+    const int64_t step_b = (int64_t)BK * ldb * 2;
+    // The odd-step half (blocks +4, rows +32) only adds a wave-uniform
+    // 32-row offset: the chunk XOR term, (row/2)%8, is unchanged by it.
+    uint32_t off_a[4], off_b[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const uint32_t blk = 8u * wave + (uint32_t)i;
+        const uint32_t ra = 8u * blk + (lane >> 3);
+        const uint32_t ca = (lane & 7u) ^ ((ra >> 1) & 7u);
+        off_a[i] = (uint32_t)((ra * lda + 8u * ca) * 2);
+    }
+    const int64_t half_a = 32 * lda * 2;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const uint32_t blk = 4u * wave + (uint32_t)i;
+        const uint32_t rb = 2u * blk + (lane >> 5);
+        const uint32_t cb = (lane & 31u) ^ ((rb & 3u) << 2);
+        off_b[i] = (uint32_t)((rb * ldb + 8u * cb) * 2);
+    }
+    const uint32_t lds_base = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(GR_LDS uint8_t*)lds);
+
+    // Copy c (0..3) of half `h` of A strip j, or copy c of B strip d.
+    auto dma_a = [&](uint32_t j, uint32_t h, int c) {
+        const uint32_t blk = 8u * wave + 4u * h + (uint32_t)c;
+        dma16(base_a + (int64_t)j * step_a + (int64_t)h * half_a, off_a[c],
+              lds_base + A_BASE + (j % A_SLOTS) * A_SLOT_BYTES + blk * 1024u);
+    };
+    auto dma_b = [&](uint32_t d, int c) {
+        const uint32_t blk = 4u * wave + (uint32_t)c;
+        dma16(base_b + (int64_t)d * step_b, off_b[c], lds_base + (d % B_SLOTS) * B_SLOT_BYTES + blk * 1024u);
+    };
+
+    // ---- fragment addresses --------------------------------------------------
+    // A operand for half h, MFMA step s, block i: row wm*128 + 32i + lane%32,
+    // chunk 4h + 2s + lane/32 of the 64-deep strip; block i is +4 KiB.  The
+    // chunk of half 1 is the chunk of half 0 plus 4, i.e. XOR 4 (chunks of
+    // half 0 are below 4), and XOR commutes with the row swizzle: half 1's
+    // address is half 0's address XOR 64 (slot and block offsets are
+    // multiples of 1 KiB and leave that bit alone).
+    const GR_LDS uint8_t* lds_p = (const GR_LDS uint8_t*)lds;
+    const uint32_t ar = wm * WAVE_TM + (lane & 31u);
+    uint32_t a_addr[KSUB];
+#pragma unroll
+    for (int s = 0; s < KSUB; ++s)
+        a_addr[s] = (uint32_t)(uintptr_t)(lds_p + A_BASE + a64_off(ar, 2u * s + (lane >> 5)));
+    const uint32_t bk = 8u * (lane >> 5) + ((lane & 15u) >> 2);
+    const GR_LDS uint8_t* b_ptr[FN];
+#pragma unroll
+    for (int j = 0; j < FN; ++j) {
+        const uint32_t n = wn * WAVE_TN + 32u * j + 16u * ((lane >> 4) & 1u) + 4u * (lane & 3u);
+        b_ptr[j] = lds_p + b_off(bk, n >> 3) + 2u * (n & 7u);
+    }
+
+    f32x16 acc[FM][FN];
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j) acc[i][j] = f32x16{};
+
+    // Read r (0..15) of the fragments of a step using half H of the A strip in
+    // slot byte offset `ao` and the B strip at `bo`, in the order the MFMAs
+    // consume them: A(0,0), B(0,0..3), A(0,1..3), A(1,0), B(1,0..3), A(1,1..3).
+    auto read_one = [&](auto h_c, Frags& f, uint32_t ao, uint32_t bo, int r) {
+        constexpr uint32_t H = decltype(h_c)::value;
+        const int s = r >> 3, q = r & 7;
+        if (q == 0 || q > 4) {
+            const int i = q == 0 ? 0 : q - 4;
+            const uint32_t addr = ((a_addr[s] + ao) ^ (64u * H)) + 4096u * i;
+            f.a[s][i] = read_a_operand((const GR_LDS uint8_t*)(uintptr_t)addr);
+        } else {
+            const int j = q - 1;
+            f.b[s][j] = read_b_operand(b_ptr[j] + bo + 8192u * s);
+        }
+    };
+    auto a_slot = [&](uint32_t kt) { return ((kt >> 1) % A_SLOTS) * A_SLOT_BYTES; };
+    auto b_slot = [&](uint32_t kt) { return (kt % B_SLOTS) * B_SLOT_BYTES; };
+    using H0 = std::integral_constant<uint32_t, 0>;
+    using H1 = std::integral_constant<uint32_t, 1>;
+
+    auto mfma_one = [&](const Frags& f, int t) {
+        const int s = t >> 4, i = (t >> 2) & 3, j = t & 3;
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(f.b[s][j], f.a[s][i], acc[i][j], 0, 0, 0);
+    };
+
+    const uint32_t KT = (uint32_t)(K / BK);  // even, >= 2
+    const uint32_t KTA = KT / 2;
+
+    // Prologue copies, in this order: A0, B0, B1, A1, B2.
+#pragma unroll
+    for (int c = 0; c < 4; ++c) dma_a(0, 0, c);
+#pragma unroll
+    for (int c = 0; c < 4; ++c) dma_a(0, 1, c);
+#pragma unroll
+    for (int c = 0; c < 4; ++c) dma_b(0, c);
+    if (KT > 1) {
+#pragma unroll
+        for (int c = 0; c < 4; ++c) dma_b(1, c);
+    }
+    if (KTA > 1) {
+#pragma unroll
+        for (int c = 0; c < 4; ++c) dma_a(1, 0, c);
+#pragma unroll
+        for (int c = 0; c < 4; ++c) dma_a(1, 1, c);
+    }
+    if (KT > 2) {
+#pragma unroll
+        for (int c = 0; c < 4; ++c) dma_b(2, c);
+    }
+    // A0 and B0 landed: the copies after them may stay in flight.
+    {
+        const uint32_t after = 4u * (KT > 1) + 8u * (KTA > 1) + 4u * (KT > 2);
+        if (after == 16) wait_vmcnt<16>();
+        else if (after == 12) wait_vmcnt<12>();
+        else if (after == 4) wait_vmcnt<4>();
+        else wait_vmcnt<0>();
+    }
+    barrier();
+
+    Frags f0, f1;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) read_one(H0{}, f0, a_slot(0), b_slot(0), r);
+
+    // Copies issued in step s (the A half, then the B strip).
+    auto issue_step = [&](uint32_t s) {
+        const uint32_t ja = (s >> 1) + 2;
+        if (ja < KTA) {
+#pragma unroll
+            for (int c = 0; c < 4; ++c) dma_a(ja, s & 1u, c);
+        }
+        if (s + 3 < KT) {
+#pragma unroll
+            for (int c = 0; c < 4; ++c) dma_b(s + 3, c);
+        }
+    };
+    auto n_issued = [&](uint32_t s) -> uint32_t { return 4u * ((s >> 1) + 2 < KTA) + 4u * (s + 3 < KT); };
+
+    // Steady step: every copy of step kt exists and the wait is "only the
+    // previous step's 8 copies may remain".  Same interleaving as the 32-deep
+    // pipelined kernel: 4 MFMAs, wait + barrier, then one memory operation
+    // after each of the next 24 MFMAs.  NH = half of A used by step kt+1.
+    auto step = [&](auto nh_c, uint32_t kt, Frags& cur, Frags& nxt) {
+#pragma unroll
+        for (int t = 0; t < 4; ++t) mfma_one(cur, t);
+        pin();
+        wait_vmcnt<8>();
+        barrier();
+        pin();
+        const uint32_t ja = (kt >> 1) + 2;
+        const uint32_t ao = a_slot(kt + 1), bo = b_slot(kt + 1);
+        int rd = 0, cp = 0;
+#pragma unroll
+        for (int t = 4; t < 32; ++t) {
+            mfma_one(cur, t);
+            pin();
+            const int k = t - 4;
+            if (k < 24) {
+                if (k % 3 == 1) {
+                    if (cp < 4) dma_a(ja, kt & 1u, cp);
+                    else dma_b(kt + 3, cp - 4);
+                    ++cp;
+                } else {
+                    read_one(nh_c, nxt, ao, bo, rd);
+                    ++rd;
+                }
+            }
+            pin();
+        }
+    };
+
+    // Generic step with its decisions taken at run time (first step and the
+    // last few).
+    auto step_any = [&](uint32_t kt, Frags& cur, Frags& nxt) {
+        if (kt >= KT) return;
+        const bool more = kt + 1 < KT;
+#pragma unroll
+        for (int t = 0; t < 4; ++t) mfma_one(cur, t);
+        pin();
+        if (more) {
+            uint32_t allowed;
+            if (kt == 0) allowed = 8u * (KTA > 1) + 4u * (KT > 2);
+            else if (kt == 1) allowed = n_issued(0);
+            else allowed = n_issued(kt - 1);
+            if (allowed >= 12) wait_vmcnt<12>();
+            else if (allowed == 8) wait_vmcnt<8>();
+            else if (allowed == 4) wait_vmcnt<4>();
+            else wait_vmcnt<0>();
+            barrier();
+        }
+        pin();
+        issue_step(kt);
+        pin();
+        if (more) {
+            const uint32_t ao = a_slot(kt + 1), bo = b_slot(kt + 1);
+            if ((kt + 1) & 1u) {
+#pragma unroll
+                for (int r = 0; r < 16; ++r) read_one(H1{}, nxt, ao, bo, r);
+            } else {
+#pragma unroll
+                for (int r = 0; r < 16; ++r) read_one(H0{}, nxt, ao, bo, r);
+            }
+        }
+        pin();
+#pragma unroll
+        for (int t = 4; t < 32; ++t) mfma_one(cur, t);
+        pin();
+    };
+
+    // Step 0 generic; steady steps 1 .. S-1 (an even count, all copies
+    // present: kt < KT - 4); then up to five generic steps.
+    step_any(0, f0, f1);
+    uint32_t kt = 1;
+    const uint32_t last_steady = KT > 5 ? KT - 5 : 0;  // steady steps are kt <= last_steady
+    for (; kt + 1 <= last_steady; kt += 2) {  // kt odd: step kt+1 uses half 0, step kt+2 half 1
+        step(H0{}, kt, f1, f0);
+        step(H1{}, kt + 1, f0, f1);
+    }
+    step_any(kt, f1, f0);
+    step_any(kt + 1, f0, f1);
+    step_any(kt + 2, f1, f0);
+    step_any(kt + 3, f0, f1);
+    step_any(kt + 4, f1, f0);
+    step_any(kt + 5, f0, f1);
+
+    // Epilogue: block (i, j) holds C^T; lane l, register r is C[m][n] with
+    // m = 32i + l%32, n = 32j + 8(r/4) + 4(l/32) + r%4.
+    const uint32_t frag_row = lane & 31u;
+    const uint32_t frag_half = lane >> 5;
+#pragma unroll
+    for (int i = 0; i < FM; ++i) {
+        const int64_t m = m0 + wm * WAVE_TM + 32 * i + frag_row;
+        uint16_t* crow = C + m * ldc;
+#pragma unroll
+        for (int j = 0; j < FN; ++j) {
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int64_t n = n0 + wn * WAVE_TN + 32 * j + 8 * q + 4 * frag_half;
+                u32x2 p;
+                p[0] = relu_pack2(acc[i][j][4 * q + 0], acc[i][j][4 * q + 1]);
+                p[1] = relu_pack2(acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]);
+                *reinterpret_cast<u32x2*>(crow + n) = p;
+            }
+        }
+    }
+    (void)M;
+    (void)N;
+}
+
+#undef GR_LDS
+
+}  // namespace tile3
+}  // namespace gr

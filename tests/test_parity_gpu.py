@@ -223,7 +223,7 @@ def test_tile_and_edge_paths_bitwise_equal():
     assert np.array_equal(C1, C2)
 
 
-@pytest.mark.parametrize("K", [32, 64, 96, 128, 160, 192, 224, 256, 288, 1056])
+@pytest.mark.parametrize("K", [32, 64, 96, 128, 160, 192, 224, 256, 288, 320, 384, 448, 512, 1056, 1088])
 def test_tile_pipeline_every_strip_count(K):
     """Whole tiles through the pipelined kernel, for every K-loop length up to
     the steady state plus odd and even tails, bitwise against the guarded
