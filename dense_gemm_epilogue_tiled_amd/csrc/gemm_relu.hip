@@ -25,8 +25,14 @@ constexpr int64_t kMaxDim = (int64_t(1) << 31) - 1;
 constexpr int64_t kMaxSpanBytes = int64_t(1) << 62;
 constexpr int kGroupM = 4;          // tile rows per workgroup-order group
 constexpr int kSmallMThreshold = 16;  // rows of A handled by the small-M kernel
-constexpr int kSmallMWaves = 8;
-constexpr int kSmallMUnroll = 4;
+#ifndef GR_SMALLM_WAVES
+#define GR_SMALLM_WAVES 8
+#endif
+#ifndef GR_SMALLM_UNROLL
+#define GR_SMALLM_UNROLL 2
+#endif
+constexpr int kSmallMWaves = GR_SMALLM_WAVES;    // waves per small-M workgroup
+constexpr int kSmallMUnroll = GR_SMALLM_UNROLL;  // 32-deep K steps per load group
 
 // Number of bytes spanned by a rows x cols matrix with pitch ld (0 if empty);
 // -1 when it does not fit the library's limits.

@@ -69,14 +69,16 @@ __device__ __forceinline__ uint32_t b_off(uint32_t k, uint32_t c) { return k * 5
 // not track it: otherwise it would make every later LDS read wait for all
 // copies in flight.  The kernel itself waits for them (wait_vmcnt + barrier)
 // before reading.  base is wave-uniform (SGPRs), voff a per-lane byte offset.
+// The LDS address travels in M0 as an explicit operand, so the compiler
+// writes M0 itself and knows the statement reads it; the s_nop covers the
+// wait state between an M0 write and an LDS DMA that reads it.
 __device__ __forceinline__ void dma16(const void* base, uint32_t voff, uint32_t lds_addr) {
     asm volatile(
-        "s_mov_b32 m0, %0\n\t"
         "s_nop 0\n\t"
-        "global_load_lds_dwordx4 %1, %2"
+        "global_load_lds_dwordx4 %0, %1"
         :
-        : "s"(lds_addr), "v"(voff), "s"(base)
-        : "memory", "m0");
+        : "v"(voff), "s"(base), "{m0}"(lds_addr)
+        : "memory");
 }
 
 template <int N>
