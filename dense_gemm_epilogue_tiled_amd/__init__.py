@@ -30,9 +30,10 @@ GR_PATH_NONE = 0
 GR_PATH_TILE = 1
 GR_PATH_TILE_EDGE = 2
 GR_PATH_SMALL_M = 3
+GR_PATH_TILE_PACKED = 4
 
 PATH_NAMES = {GR_PATH_NONE: "none", GR_PATH_TILE: "tile", GR_PATH_TILE_EDGE: "tile_edge",
-              GR_PATH_SMALL_M: "small_m"}
+              GR_PATH_SMALL_M: "small_m", GR_PATH_TILE_PACKED: "tile_packed"}
 
 
 class gr_plan_t(ctypes.Structure):
@@ -48,6 +49,8 @@ class gr_plan_t(ctypes.Structure):
         ("vec_b", ctypes.c_int32),
         ("vec_c", ctypes.c_int32),
         ("group_m", ctypes.c_int32),
+        ("packed", ctypes.c_int32),
+        ("workspace", ctypes.c_int64),
     ]
 
 
@@ -78,6 +81,16 @@ def lib() -> ctypes.CDLL:
             l.gemm_relu_f16_forced.restype = i32
             l.gemm_relu_f16_plan.argtypes = [i64, i64, i64, p, i64, p, i64, p, i64, ctypes.POINTER(gr_plan_t)]
             l.gemm_relu_f16_plan.restype = i32
+            l.gemm_relu_f16_workspace_size.argtypes = [i64, i64, i64, p, i64, p, i64, p, i64,
+                                                       ctypes.POINTER(ctypes.c_int64)]
+            l.gemm_relu_f16_workspace_size.restype = i32
+            l.gemm_relu_f16_ws.argtypes = [i64, i64, i64, p, i64, p, i64, p, i64, p, i64, p]
+            l.gemm_relu_f16_ws.restype = i32
+            l.gemm_relu_f16_forced_ws.argtypes = [i64, i64, i64, p, i64, p, i64, p, i64, p, i64, p, i32]
+            l.gemm_relu_f16_forced_ws.restype = i32
+            l.gemm_relu_f16_plan_ws.argtypes = [i64, i64, i64, p, i64, p, i64, p, i64, i64,
+                                                ctypes.POINTER(gr_plan_t)]
+            l.gemm_relu_f16_plan_ws.restype = i32
             l.gemm_relu_status_string.argtypes = [i32]
             l.gemm_relu_status_string.restype = ctypes.c_char_p
             l.gemm_relu_version.argtypes = []
@@ -100,13 +113,45 @@ def gemm_relu_f16_forced(M, N, K, A, lda, B, ldb, C, ldc, stream=None, path=GR_P
     return lib().gemm_relu_f16_forced(M, N, K, _ptr(A), lda, _ptr(B), ldb, _ptr(C), ldc, _ptr(stream), path)
 
 
+def _plan_dict(plan):
+    d = {name: getattr(plan, name) for name, _ in gr_plan_t._fields_}
+    d["path_name"] = PATH_NAMES.get(d["path"], "?")
+    return d
+
+
 def gemm_relu_f16_plan(M, N, K, A, lda, B, ldb, C, ldc):
     """(status, plan dict) from the pure planner; needs no GPU."""
     plan = gr_plan_t()
     st = lib().gemm_relu_f16_plan(M, N, K, _ptr(A), lda, _ptr(B), ldb, _ptr(C), ldc, ctypes.byref(plan))
-    d = {name: getattr(plan, name) for name, _ in gr_plan_t._fields_}
-    d["path_name"] = PATH_NAMES.get(d["path"], "?")
-    return st, d
+    return st, _plan_dict(plan)
+
+
+def gemm_relu_f16_plan_ws(M, N, K, A, lda, B, ldb, C, ldc, workspace_bytes):
+    """(status, plan dict) for a call with a workspace of the given size."""
+    plan = gr_plan_t()
+    st = lib().gemm_relu_f16_plan_ws(M, N, K, _ptr(A), lda, _ptr(B), ldb, _ptr(C), ldc, int(workspace_bytes),
+                                     ctypes.byref(plan))
+    return st, _plan_dict(plan)
+
+
+def gemm_relu_f16_workspace_size(M, N, K, A, lda, B, ldb, C, ldc):
+    """(status, bytes): workspace that lets the problem take the packed path."""
+    n = ctypes.c_int64(0)
+    st = lib().gemm_relu_f16_workspace_size(M, N, K, _ptr(A), lda, _ptr(B), ldb, _ptr(C), ldc, ctypes.byref(n))
+    return st, int(n.value)
+
+
+def gemm_relu_f16_ws(M, N, K, A, lda, B, ldb, C, ldc, workspace, workspace_bytes, stream=None) -> int:
+    """gemm_relu_f16 with a device workspace (pointer, bytes); returns the status code."""
+    return lib().gemm_relu_f16_ws(M, N, K, _ptr(A), lda, _ptr(B), ldb, _ptr(C), ldc, _ptr(workspace),
+                                  int(workspace_bytes), _ptr(stream))
+
+
+def gemm_relu_f16_forced_ws(M, N, K, A, lda, B, ldb, C, ldc, workspace, workspace_bytes, stream=None,
+                            path=GR_PATH_TILE_PACKED) -> int:
+    """gemm_relu_f16_forced with a device workspace; returns the status code."""
+    return lib().gemm_relu_f16_forced_ws(M, N, K, _ptr(A), lda, _ptr(B), ldb, _ptr(C), ldc, _ptr(workspace),
+                                         int(workspace_bytes), _ptr(stream), path)
 
 
 def gemm_relu_status_string(status: int) -> str:
@@ -126,11 +171,14 @@ def _stream_handle(stream):
     return stream.cuda_stream
 
 
-def gemm_relu(a, b, out=None, stream=None, path=None):
+def gemm_relu(a, b, out=None, stream=None, path=None, workspace="auto"):
     """Tensor convenience: ``out = ReLU(a @ b)`` for 2-D fp16 tensors on the GPU.
 
     Row pitches are taken from the tensors' strides (unit column stride
-    required). Raises GemmReluError on a non-zero status.
+    required). ``workspace``: "auto" allocates (from torch's caching
+    allocator) the scratch the library asks for, if any; a uint8 device
+    tensor is used as given; None means no workspace. Raises GemmReluError on
+    a non-zero status.
     """
     import torch
     if a.dtype != torch.float16 or b.dtype != torch.float16:
@@ -147,11 +195,23 @@ def gemm_relu(a, b, out=None, stream=None, path=None):
     lda = max(a.stride(0), 1) if M > 1 else max(K, 1)
     ldb = max(b.stride(0), 1) if K > 1 else max(N, 1)
     ldc = max(out.stride(0), 1) if M > 1 else max(N, 1)
+    args = (M, N, K, a.data_ptr(), lda, b.data_ptr(), ldb, out.data_ptr(), ldc)
+    if isinstance(workspace, str):
+        if workspace != "auto":
+            raise ValueError("workspace must be 'auto', None or a uint8 tensor")
+        st, size = gemm_relu_f16_workspace_size(*args)
+        if st != GR_OK:
+            raise GemmReluError(st, "gemm_relu_f16_workspace_size")
+        workspace = torch.empty(size, dtype=torch.uint8, device=a.device) if size else None
+        if workspace is not None and stream is not None and not isinstance(stream, int):
+            # the scratch block must not be handed out again before this stream is done with it
+            workspace.record_stream(stream)
+    ws_ptr, ws_bytes = (workspace.data_ptr(), workspace.numel()) if workspace is not None else (0, 0)
     h = _stream_handle(stream)
     if path is None:
-        st = gemm_relu_f16(M, N, K, a.data_ptr(), lda, b.data_ptr(), ldb, out.data_ptr(), ldc, h)
+        st = gemm_relu_f16_ws(*args, ws_ptr, ws_bytes, h)
     else:
-        st = gemm_relu_f16_forced(M, N, K, a.data_ptr(), lda, b.data_ptr(), ldb, out.data_ptr(), ldc, h, path)
+        st = gemm_relu_f16_forced_ws(*args, ws_ptr, ws_bytes, h, path)
     if st != GR_OK:
         raise GemmReluError(st)
     return out

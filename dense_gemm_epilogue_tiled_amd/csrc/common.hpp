@@ -65,4 +65,135 @@ __device__ __forceinline__ void tile_of_workgroup(uint32_t wg, uint32_t n_wg, ui
     tn = in_g / gm;
 }
 
+// Edges for the pipelined whole-tile kernels on matrices whose size is not a
+// multiple of the tile (their rows must still be 16-byte aligned and K a
+// multiple of the strip depth, so every copy stays a whole 16-byte chunk):
+//   * rows: the last tile row is moved up to end at row M (M >= BM), so every
+//     row a tile copies exists; the rows it shares with the tile row above are
+//     computed twice and stored once, by the tile that owns them.
+//   * columns: a copy of a chunk past the last chunk that holds a column < N
+//     reads that last chunk instead.  The chunk holds real bytes of the row
+//     (the pitch is a multiple of 8 elements, so it never runs past the
+//     16-byte block of element N-1); the columns >= N it brings in only
+//     reach outputs that are never stored.
+//   * stores: an output is written only if its row is owned by the tile and
+//     its column is < N; 8-byte stores where C allows them, else 2-byte ones.
+namespace edge {
+
+__device__ __forceinline__ int64_t shifted_row0(int64_t m_tile, int64_t M, int64_t bm) {
+    return m_tile + bm <= M ? m_tile : M - bm;
+}
+
+// Chunk (8 columns) `c` of the tile starting at column n0, clamped to the
+// last chunk holding a column < N.
+__device__ __forceinline__ uint32_t clamp_chunk(uint32_t c, int64_t n0, int64_t N) {
+    const uint32_t last = (uint32_t)((N - 1) / 8 - n0 / 8);
+    return c < last ? c : last;
+}
+
+// Outputs (row, n .. n+3) of one lane, ReLU'd and rounded, where they fall
+// inside the tile's part of C.  vec_c == 4: C and its pitch allow 8-byte
+// stores.
+__device__ __forceinline__ void store4(uint16_t* crow, bool row_owned, int64_t n, int64_t N, int vec_c, float a0,
+                                       float a1, float a2, float a3) {
+    if (!row_owned) return;
+    if (vec_c == 4 && n + 4 <= N) {
+        u32x2 p;
+        p[0] = relu_pack2(a0, a1);
+        p[1] = relu_pack2(a2, a3);
+        *reinterpret_cast<u32x2*>(crow + n) = p;
+        return;
+    }
+    if (n < N) crow[n] = relu_to_f16(a0);
+    if (n + 1 < N) crow[n + 1] = relu_to_f16(a1);
+    if (n + 2 < N) crow[n + 2] = relu_to_f16(a2);
+    if (n + 3 < N) crow[n + 3] = relu_to_f16(a3);
+}
+
+}  // namespace edge
+
+// Write-back of one wave's 128 x 128 tile of C through LDS.
+//
+// The MFMA accumulators hold C^T blocks: a lane owns 4 consecutive columns of
+// one row, and one store instruction of the whole wave would touch 32 rows.
+// Instead the wave first writes its ReLU'd fp16 tile to LDS (row-major, 256
+// bytes per row, the 16-byte chunk c of row r at slot c XOR (r % 16), so that
+// the read-back below is free of bank conflicts), then reads it back so that
+// consecutive lanes hold consecutive columns of C:
+//   vec_c == 8: 16-byte chunks, 16 lanes per 256-byte row segment;
+//   vec_c == 4: the same chunks stored as two 8-byte halves;
+//   vec_c == 1: one element per lane, 64 consecutive columns per store.
+// Every store instruction then covers whole row segments of C.  The caller's
+// LDS must be free: the routine starts with a workgroup barrier (all waves
+// call it), and the wave's 32 KiB region is its own.
+// EDGE: only rows in [row_min, M) and columns < N are stored.
+namespace epi {
+
+constexpr int WAVE_TILE = 128;
+constexpr uint32_t REGION_BYTES = WAVE_TILE * WAVE_TILE * 2;  // 32 KiB per wave
+
+__device__ __forceinline__ uint32_t tile_off(uint32_t row, uint32_t chunk) {
+    return row * 256u + ((chunk ^ (row & 15u)) << 4);
+}
+
+template <bool EDGE>
+__device__ __forceinline__ void store_wave_tile(const f32x16 (&acc)[4][4], uint8_t* region, uint32_t lane,
+                                                uint16_t* __restrict__ C, int64_t ldc, int64_t row0, int64_t col0,
+                                                int64_t row_min, int64_t M, int64_t N, int vec_c) {
+    __syncthreads();
+    const uint32_t r_lane = lane & 31u, half = lane >> 5;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const uint32_t row = 32u * i + r_lane;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                u32x2 p;
+                p[0] = relu_pack2(acc[i][j][4 * q + 0], acc[i][j][4 * q + 1]);
+                p[1] = relu_pack2(acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]);
+                *reinterpret_cast<u32x2*>(region + tile_off(row, 4u * j + q) + 8u * half) = p;
+            }
+        }
+    }
+    __syncthreads();
+    if (vec_c >= 4) {
+        const uint32_t ch = lane & 15u;
+#pragma unroll 8
+        for (uint32_t k = 0; k < 32; ++k) {
+            const uint32_t row = 4u * k + (lane >> 4);
+            const u32x4 v = *reinterpret_cast<const u32x4*>(region + tile_off(row, ch));
+            const int64_t m = row0 + row;
+            const int64_t n = col0 + 8 * ch;
+            uint16_t* dst = C + m * ldc + n;
+            if (EDGE && (m < row_min || m >= M)) continue;
+            if (!EDGE || n + 8 <= N) {
+                if (vec_c == 8) {
+                    *reinterpret_cast<u32x4*>(dst) = v;
+                } else {
+                    *reinterpret_cast<u32x2*>(dst) = u32x2{v[0], v[1]};
+                    *reinterpret_cast<u32x2*>(dst + 4) = u32x2{v[2], v[3]};
+                }
+            } else {
+#pragma unroll
+                for (int e = 0; e < 8; ++e)
+                    if (n + e < N) dst[e] = (uint16_t)(v[e >> 1] >> (16 * (e & 1)));
+            }
+        }
+    } else {
+#pragma unroll 8
+        for (uint32_t k = 0; k < 256; ++k) {
+            const uint32_t row = k >> 1;
+            const uint32_t col = 64u * (k & 1u) + lane;
+            const uint16_t h = *reinterpret_cast<const uint16_t*>(region + tile_off(row, col >> 3) + 2u * (col & 7u));
+            const int64_t m = row0 + row;
+            const int64_t n = col0 + col;
+            if (EDGE && (m < row_min || m >= M || n >= N)) continue;
+            C[m * ldc + n] = h;
+        }
+    }
+}
+
+}  // namespace epi
+
 }  // namespace gr

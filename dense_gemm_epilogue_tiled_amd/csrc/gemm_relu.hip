@@ -4,7 +4,8 @@
 // and the launch on the caller's stream.  The operation and its contract are
 // documented in include/gemm_relu.h.  No allocation, no synchronisation and
 // no per-call state: the only state is a once-per-device check that the
-// device is a gfx950.
+// device is a gfx950.  Scratch memory, where a path uses it, is the caller's
+// workspace.
 #include <hip/hip_runtime.h>
 
 #include <atomic>
@@ -12,10 +13,10 @@
 #include <cstring>
 
 #include "../../include/gemm_relu.h"
+#include "pack_kernel.hpp"
 #include "smallm_kernel.hpp"
 #include "tile2_kernel.hpp"
 #include "tile3_kernel.hpp"
-#include "tile_pp_kernel.hpp"
 #include "tile_kernel.hpp"
 
 namespace {
@@ -25,6 +26,8 @@ constexpr int64_t kMaxDim = (int64_t(1) << 31) - 1;
 constexpr int64_t kMaxSpanBytes = int64_t(1) << 62;
 constexpr int kGroupM = 4;          // tile rows per workgroup-order group
 constexpr int kSmallMThreshold = 16;  // rows of A handled by the small-M kernel
+constexpr int64_t kPackMinMacs = int64_t(1) << 30;  // smallest M*N*K the planner packs for
+constexpr int64_t kWorkspaceAlign = 256;            // required alignment of a workspace (bytes)
 #ifndef GR_SMALLM_WAVES
 #define GR_SMALLM_WAVES 8
 #endif
@@ -57,13 +60,19 @@ int vec_width(uintptr_t p, int64_t ld) {
     return 1;
 }
 
+// Widest store into C (fp16 elements): 8 (16-byte rows), 4 (8-byte rows) or 1.
 int vec_width_c(uintptr_t p, int64_t ld) {
+    if (p % 16 == 0 && ld % 8 == 0) return 8;
     if (p % 8 == 0 && ld % 4 == 0) return 4;
     return 1;
 }
 
+// Argument checks.  The workspace (ws, ws_bytes) is optional: a size of 0
+// means none; a negative size or a misaligned workspace is GR_ERR_INVALID_ARG,
+// NULL with a positive size GR_ERR_NULL_PTR, overlap with A, B or C
+// GR_ERR_ALIAS.
 int validate(int64_t M, int64_t N, int64_t K, uintptr_t A, int64_t lda, uintptr_t B, int64_t ldb,
-             uintptr_t C, int64_t ldc) {
+             uintptr_t C, int64_t ldc, uintptr_t ws = 0, int64_t ws_bytes = 0) {
     if (M < 0 || N < 0 || K < 0) return GR_ERR_INVALID_DIM;
     if (M > kMaxDim || N > kMaxDim || K > kMaxDim) return GR_ERR_TOO_LARGE;
     const int64_t kmin = K > 1 ? K : 1, nmin = N > 1 ? N : 1;
@@ -77,6 +86,13 @@ int validate(int64_t M, int64_t N, int64_t K, uintptr_t A, int64_t lda, uintptr_
     const int64_t sc = c_used ? span_bytes(M, N, ldc) : 0;
     if (sa < 0 || sb < 0 || sc < 0) return GR_ERR_TOO_LARGE;
     if (overlaps(C, sc, A, sa) || overlaps(C, sc, B, sb)) return GR_ERR_ALIAS;
+    if (ws_bytes < 0) return GR_ERR_INVALID_ARG;
+    if (ws_bytes > 0) {
+        if (!ws) return GR_ERR_NULL_PTR;
+        if (ws % kWorkspaceAlign != 0) return GR_ERR_INVALID_ARG;
+        if (overlaps(ws, ws_bytes, A, sa) || overlaps(ws, ws_bytes, B, sb) || overlaps(ws, ws_bytes, C, sc))
+            return GR_ERR_ALIAS;
+    }
     return GR_OK;
 }
 
@@ -86,29 +102,76 @@ bool smallm_ok(int64_t M, int64_t N, int64_t K, uintptr_t A, int64_t lda, uintpt
     return M >= 1 && M <= kSmallMThreshold && A % 16 == 0 && lda % 8 == 0 && B % 8 == 0 && ldb % 4 == 0;
 }
 
-bool tile_fast_ok(int64_t M, int64_t N, int64_t K, uintptr_t A, int64_t lda, uintptr_t B, int64_t ldb,
-                  uintptr_t C, int64_t ldc) {
+// Conditions of the pipelined direct-to-LDS kernels: 16-byte aligned rows of
+// A and B (every copy is a whole 16-byte chunk), K a positive multiple of the
+// 32-deep strip, pitches small enough for 32-bit per-lane copy offsets, and at
+// least one whole tile of rows (a partial last tile row is moved up to end at
+// row M).  Any N and any C layout.
+bool tile_fast_ok(int64_t M, int64_t N, int64_t K, uintptr_t A, int64_t lda, uintptr_t B, int64_t ldb) {
     using namespace gr::tile2;
-    return M % BM == 0 && N % BN == 0 && K % BK == 0 && K > 0 && vec_width(A, lda) == 8 &&
-           vec_width(B, ldb) == 8 && vec_width_c(C, ldc) == 4 && lda <= MAX_LDA && ldb <= MAX_LDB;
+    return M >= BM && N >= 1 && K % BK == 0 && K > 0 && vec_width(A, lda) == 8 && vec_width(B, ldb) == 8 &&
+           lda <= MAX_LDA && ldb <= MAX_LDB;
+}
+
+// Whole tiles: the edge-free variant of those kernels.
+bool tile_whole(int64_t M, int64_t N) {
+    using namespace gr::tile2;
+    return M % BM == 0 && N % BN == 0;
+}
+
+int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
+
+// The packed variant of the pipelined path: which operands are copied into
+// the workspace, and the problem the tile kernel then sees.  K is padded to a
+// multiple of 64 (zeros) unless it already is a multiple of 32; an operand is
+// copied when its rows are not 16-byte aligned or when K is padded.
+struct Pack {
+    bool a = false, b = false;  // operand copied into the workspace
+    int64_t kp = 0;             // K of the packed problem
+    int64_t lda_p = 0, ldb_p = 0;
+    int64_t off_b = 0;          // byte offset of the copy of B in the workspace
+    int64_t bytes = 0;          // workspace bytes used
+};
+
+bool pack_layout(int64_t M, int64_t N, int64_t K, uintptr_t A, int64_t lda, uintptr_t B, int64_t ldb, Pack* pk) {
+    using namespace gr::tile2;
+    if (M < BM || N < 1 || K < 1) return false;
+    Pack q;
+    q.kp = K % BK == 0 ? K : round_up(K, 2 * BK);
+    q.a = vec_width(A, lda) != 8 || lda > MAX_LDA || q.kp != K;
+    q.b = vec_width(B, ldb) != 8 || ldb > MAX_LDB || q.kp != K;
+    if (!q.a && !q.b) return false;  // the pipelined path runs in place
+    q.lda_p = q.a ? q.kp : lda;
+    q.ldb_p = q.b ? round_up(N, 8) : ldb;
+    if (q.lda_p > MAX_LDA || q.ldb_p > MAX_LDB) return false;
+    const int64_t a_bytes = q.a ? round_up(M * q.kp * 2, kWorkspaceAlign) : 0;
+    const int64_t b_bytes = q.b ? q.kp * q.ldb_p * 2 : 0;
+    q.off_b = a_bytes;
+    q.bytes = a_bytes + b_bytes;
+    *pk = q;
+    return true;
 }
 
 void fill_plan(int path, int64_t M, int64_t N, int64_t K, uintptr_t A, int64_t lda, uintptr_t B,
-               int64_t ldb, uintptr_t C, int64_t ldc, gr_plan_t* p) {
+               int64_t ldb, uintptr_t C, int64_t ldc, const Pack& pk, gr_plan_t* p) {
     std::memset(p, 0, sizeof(*p));
     p->path = path;
-    if (path == GR_PATH_TILE) {
+    if (path == GR_PATH_TILE || path == GR_PATH_TILE_PACKED) {
         using namespace gr::tile2;
         p->block_m = BM;
         p->block_n = BN;
         p->block_k = BK;
         p->stages = STAGES;
         p->threads = THREADS;
-        p->grid = (M / BM) * (N / BN);
+        p->grid = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
         p->vec_a = 8;
         p->vec_b = 8;
-        p->vec_c = 4;
+        p->vec_c = vec_width_c(C, ldc);
         p->group_m = kGroupM;
+        if (path == GR_PATH_TILE_PACKED) {
+            p->packed = (pk.a ? 1 : 0) | (pk.b ? 2 : 0);
+            p->workspace = pk.bytes;
+        }
     } else if (path == GR_PATH_TILE_EDGE) {
         using namespace gr::tile;
         p->block_m = BM;
@@ -137,12 +200,18 @@ void fill_plan(int path, int64_t M, int64_t N, int64_t K, uintptr_t A, int64_t l
 }
 
 int choose_path(int64_t M, int64_t N, int64_t K, uintptr_t A, int64_t lda, uintptr_t B, int64_t ldb,
-                uintptr_t C, int64_t ldc) {
+                uintptr_t C, int64_t ldc, int64_t ws_bytes, Pack* pk) {
+    (void)C;
+    (void)ldc;
     if (M == 0 || N == 0) return GR_PATH_NONE;
     if (K > 0 && smallm_ok(M, N, K, A, lda, B, ldb)) return GR_PATH_SMALL_M;
-    if (tile_fast_ok(M, N, K, A, lda, B, ldb, C, ldc)) return GR_PATH_TILE;
+    if (tile_fast_ok(M, N, K, A, lda, B, ldb)) return GR_PATH_TILE;
+    if (ws_bytes > 0 && pack_layout(M, N, K, A, lda, B, ldb, pk) && pk->bytes <= ws_bytes &&
+        (double)M * (double)N * (double)K >= (double)kPackMinMacs)
+        return GR_PATH_TILE_PACKED;
     return GR_PATH_TILE_EDGE;
 }
+
 
 // ---- device check (once per device) ------------------------------------------
 
@@ -193,25 +262,57 @@ int launch_tile_vb(const gr_plan_t& p, int64_t M, int64_t N, int64_t K, const ui
     }
 }
 
+// Copy the operands the layout names into the workspace (one launch).
+int launch_pack(const Pack& pk, int64_t M, int64_t N, int64_t K, const uint16_t* A, int64_t lda,
+                const uint16_t* B, int64_t ldb, uint8_t* ws, hipStream_t stream) {
+    using gr::pack::Job;
+    const Job none{nullptr, nullptr, 0, 8, 0, 0, 0};
+    const Job ja = pk.a ? Job{A, reinterpret_cast<uint16_t*>(ws), lda, pk.lda_p, M, K, M} : none;
+    const Job jb = pk.b ? Job{B, reinterpret_cast<uint16_t*>(ws + pk.off_b), ldb, pk.ldb_p, K, N, pk.kp} : none;
+    // About four 16-byte groups per thread, at most 2048 workgroups per job.
+    auto blocks = [](const Job& j) -> int64_t {
+        const int64_t groups = j.rows_d * (j.ldd / 8);
+        const int64_t b = (groups + 4 * gr::pack::THREADS - 1) / (4 * gr::pack::THREADS);
+        return b < 2048 ? b : 2048;
+    };
+    const int64_t ba = blocks(ja), bb = blocks(jb);
+    if (ba + bb == 0) return GR_OK;
+    return launch(gr::pack::pack_kernel, ba + bb, gr::pack::THREADS, stream, ja, jb, (uint32_t)ba);
+}
+
 int run(const gr_plan_t& p, int64_t M, int64_t N, int64_t K, const uint16_t* A, int64_t lda, const uint16_t* B,
-        int64_t ldb, uint16_t* C, int64_t ldc, hipStream_t stream) {
+        int64_t ldb, uint16_t* C, int64_t ldc, const Pack& pk, uint8_t* ws, hipStream_t stream) {
     switch (p.path) {
         case GR_PATH_NONE: return GR_OK;
+        case GR_PATH_TILE_PACKED: {
+            const int st = launch_pack(pk, M, N, K, A, lda, B, ldb, ws, stream);
+            if (st != GR_OK) return st;
+            gr_plan_t q = p;
+            q.path = GR_PATH_TILE;
+            const uint16_t* Ap = pk.a ? reinterpret_cast<const uint16_t*>(ws) : A;
+            const uint16_t* Bp = pk.b ? reinterpret_cast<const uint16_t*>(ws + pk.off_b) : B;
+            return run(q, M, N, pk.kp, Ap, pk.lda_p, Bp, pk.ldb_p, C, ldc, pk, ws, stream);
+        }
         case GR_PATH_TILE: {
-#ifdef GR_TILE_PP
-            using namespace gr::pp;
-            return launch(gemm_relu_pp_kernel, p.grid, THREADS, stream, A, B, C, M, N, K, lda, ldb, ldc,
-                          (uint32_t)(M / BM), (uint32_t)(N / BN), (uint32_t)p.group_m);
-#else
+            const bool whole = tile_whole(M, N);
+            const uint32_t tiles_m = (uint32_t)((M + gr::tile2::BM - 1) / gr::tile2::BM);
+            const uint32_t tiles_n = (uint32_t)((N + gr::tile2::BN - 1) / gr::tile2::BN);
+            const uint32_t gm = (uint32_t)p.group_m;
+            const int vc = p.vec_c;
             if (K % gr::tile3::BKA == 0) {
                 using namespace gr::tile3;
-                return launch(gemm_relu_tile3_kernel, p.grid, THREADS, stream, A, B, C, M, N, K, lda, ldb, ldc,
-                              (uint32_t)(M / BM), (uint32_t)(N / BN), (uint32_t)p.group_m);
+                if (whole)
+                    return launch(gemm_relu_tile3_kernel<false>, p.grid, THREADS, stream, A, B, C, M, N, K, lda, ldb,
+                                  ldc, tiles_m, tiles_n, gm, vc);
+                return launch(gemm_relu_tile3_kernel<true>, p.grid, THREADS, stream, A, B, C, M, N, K, lda, ldb, ldc,
+                              tiles_m, tiles_n, gm, vc);
             }
             using namespace gr::tile2;
-            return launch(gemm_relu_tile2_kernel, p.grid, THREADS, stream, A, B, C, M, N, K, lda, ldb, ldc,
-                          (uint32_t)(M / BM), (uint32_t)(N / BN), (uint32_t)p.group_m);
-#endif
+            if (whole)
+                return launch(gemm_relu_tile2_kernel<false>, p.grid, THREADS, stream, A, B, C, M, N, K, lda, ldb, ldc,
+                              tiles_m, tiles_n, gm, vc);
+            return launch(gemm_relu_tile2_kernel<true>, p.grid, THREADS, stream, A, B, C, M, N, K, lda, ldb, ldc,
+                          tiles_m, tiles_n, gm, vc);
         }
         case GR_PATH_TILE_EDGE:
             switch (p.vec_a) {
@@ -232,28 +333,48 @@ int run(const gr_plan_t& p, int64_t M, int64_t N, int64_t K, const uint16_t* A, 
     }
 }
 
-int entry(int64_t M, int64_t N, int64_t K, const uint16_t* A, int64_t lda, const uint16_t* B, int64_t ldb,
-          uint16_t* C, int64_t ldc, void* stream, int forced) {
-    const uintptr_t a = (uintptr_t)A, b = (uintptr_t)B, c = (uintptr_t)C;
-    int st = validate(M, N, K, a, lda, b, ldb, c, ldc);
+// Validate, choose (or check a forced) path, fill the plan.  No HIP call.
+// ws_known: the workspace pointer is real and is checked (a plan made from
+// a size alone skips the pointer checks).
+int plan_call(int64_t M, int64_t N, int64_t K, uintptr_t a, int64_t lda, uintptr_t b, int64_t ldb, uintptr_t c,
+              int64_t ldc, uintptr_t ws, int64_t ws_bytes, bool ws_known, int forced, Pack* pk, gr_plan_t* p) {
+    if (ws_bytes < 0) return GR_ERR_INVALID_ARG;
+    int st = ws_known ? validate(M, N, K, a, lda, b, ldb, c, ldc, ws, ws_bytes)
+                      : validate(M, N, K, a, lda, b, ldb, c, ldc);
     if (st != GR_OK) return st;
-    int path = choose_path(M, N, K, a, lda, b, ldb, c, ldc);
+    int path = choose_path(M, N, K, a, lda, b, ldb, c, ldc, ws_bytes, pk);
     if (forced >= 0 && path != GR_PATH_NONE) {
         if (forced == GR_PATH_TILE) {
-            if (!tile_fast_ok(M, N, K, a, lda, b, ldb, c, ldc)) return GR_ERR_INVALID_PATH;
+            if (!tile_fast_ok(M, N, K, a, lda, b, ldb)) return GR_ERR_INVALID_PATH;
         } else if (forced == GR_PATH_SMALL_M) {
             if (K == 0 || !smallm_ok(M, N, K, a, lda, b, ldb)) return GR_ERR_INVALID_PATH;
+        } else if (forced == GR_PATH_TILE_PACKED) {
+            if (!pack_layout(M, N, K, a, lda, b, ldb, pk) || pk->bytes > ws_bytes) return GR_ERR_INVALID_PATH;
         } else if (forced != GR_PATH_TILE_EDGE) {
             return GR_ERR_INVALID_PATH;
         }
         path = forced;
     }
-    if (path == GR_PATH_NONE) return GR_OK;
+    fill_plan(path, M, N, K, a, lda, b, ldb, c, ldc, *pk, p);
+    return GR_OK;
+}
+
+int entry(int64_t M, int64_t N, int64_t K, const uint16_t* A, int64_t lda, const uint16_t* B, int64_t ldb,
+          uint16_t* C, int64_t ldc, void* ws, int64_t ws_bytes, void* stream, int forced) {
+    Pack pk;
+    gr_plan_t p;
+    int st = plan_call(M, N, K, (uintptr_t)A, lda, (uintptr_t)B, ldb, (uintptr_t)C, ldc, (uintptr_t)ws, ws_bytes,
+                       true, forced, &pk, &p);
+    if (st != GR_OK) return st;
+    if (p.path == GR_PATH_NONE) return GR_OK;
     st = check_device();
     if (st != GR_OK) return st;
-    gr_plan_t p;
-    fill_plan(path, M, N, K, a, lda, b, ldb, c, ldc, &p);
-    return run(p, M, N, K, A, lda, B, ldb, C, ldc, static_cast<hipStream_t>(stream));
+    return run(p, M, N, K, A, lda, B, ldb, C, ldc, pk, static_cast<uint8_t*>(ws), static_cast<hipStream_t>(stream));
+}
+
+bool known_path(int path) {
+    return path == GR_PATH_TILE || path == GR_PATH_TILE_EDGE || path == GR_PATH_SMALL_M ||
+           path == GR_PATH_TILE_PACKED;
 }
 
 }  // namespace
@@ -262,23 +383,52 @@ extern "C" {
 
 int gemm_relu_f16(int64_t M, int64_t N, int64_t K, const uint16_t* A, int64_t lda, const uint16_t* B, int64_t ldb,
                   uint16_t* C, int64_t ldc, void* stream) {
-    return entry(M, N, K, A, lda, B, ldb, C, ldc, stream, -1);
+    return entry(M, N, K, A, lda, B, ldb, C, ldc, nullptr, 0, stream, -1);
 }
 
 int gemm_relu_f16_forced(int64_t M, int64_t N, int64_t K, const uint16_t* A, int64_t lda, const uint16_t* B,
                          int64_t ldb, uint16_t* C, int64_t ldc, void* stream, int path) {
-    if (path != GR_PATH_TILE && path != GR_PATH_TILE_EDGE && path != GR_PATH_SMALL_M) return GR_ERR_INVALID_PATH;
-    return entry(M, N, K, A, lda, B, ldb, C, ldc, stream, path);
+    if (!known_path(path) || path == GR_PATH_TILE_PACKED) return GR_ERR_INVALID_PATH;
+    return entry(M, N, K, A, lda, B, ldb, C, ldc, nullptr, 0, stream, path);
 }
 
 int gemm_relu_f16_plan(int64_t M, int64_t N, int64_t K, const uint16_t* A, int64_t lda, const uint16_t* B,
                        int64_t ldb, const uint16_t* C, int64_t ldc, gr_plan_t* out) {
-    if (!out) return GR_ERR_INVALID_ARG;
+    return gemm_relu_f16_plan_ws(M, N, K, A, lda, B, ldb, C, ldc, 0, out);
+}
+
+int gemm_relu_f16_workspace_size(int64_t M, int64_t N, int64_t K, const uint16_t* A, int64_t lda,
+                                 const uint16_t* B, int64_t ldb, const uint16_t* C, int64_t ldc, int64_t* bytes) {
+    if (!bytes) return GR_ERR_INVALID_ARG;
     const uintptr_t a = (uintptr_t)A, b = (uintptr_t)B, c = (uintptr_t)C;
     int st = validate(M, N, K, a, lda, b, ldb, c, ldc);
     if (st != GR_OK) return st;
-    fill_plan(choose_path(M, N, K, a, lda, b, ldb, c, ldc), M, N, K, a, lda, b, ldb, c, ldc, out);
+    *bytes = 0;
+    Pack pk;
+    if (M > 0 && N > 0 && !smallm_ok(M, N, K, a, lda, b, ldb) && !tile_fast_ok(M, N, K, a, lda, b, ldb) &&
+        pack_layout(M, N, K, a, lda, b, ldb, &pk))
+        *bytes = pk.bytes;
     return GR_OK;
+}
+
+int gemm_relu_f16_ws(int64_t M, int64_t N, int64_t K, const uint16_t* A, int64_t lda, const uint16_t* B,
+                     int64_t ldb, uint16_t* C, int64_t ldc, void* workspace, int64_t workspace_bytes, void* stream) {
+    return entry(M, N, K, A, lda, B, ldb, C, ldc, workspace, workspace_bytes, stream, -1);
+}
+
+int gemm_relu_f16_forced_ws(int64_t M, int64_t N, int64_t K, const uint16_t* A, int64_t lda, const uint16_t* B,
+                            int64_t ldb, uint16_t* C, int64_t ldc, void* workspace, int64_t workspace_bytes,
+                            void* stream, int path) {
+    if (!known_path(path)) return GR_ERR_INVALID_PATH;
+    return entry(M, N, K, A, lda, B, ldb, C, ldc, workspace, workspace_bytes, stream, path);
+}
+
+int gemm_relu_f16_plan_ws(int64_t M, int64_t N, int64_t K, const uint16_t* A, int64_t lda, const uint16_t* B,
+                          int64_t ldb, const uint16_t* C, int64_t ldc, int64_t workspace_bytes, gr_plan_t* out) {
+    if (!out) return GR_ERR_INVALID_ARG;
+    Pack pk;
+    return plan_call(M, N, K, (uintptr_t)A, lda, (uintptr_t)B, ldb, (uintptr_t)C, ldc, 0, workspace_bytes, false,
+                     -1, &pk, out);
 }
 
 const char* gemm_relu_status_string(int status) {

@@ -56,6 +56,7 @@ constexpr int A_BYTES = BM * BK * 2;          // 16 KiB
 constexpr int B_BYTES = BK * BN * 2;          // 16 KiB
 constexpr int STAGE_BYTES = A_BYTES + B_BYTES;
 constexpr int LDS_BYTES = STAGES * STAGE_BYTES;  // 128 KiB
+static_assert(LDS_BYTES >= 4 * epi::REGION_BYTES, "the epilogue stages four wave tiles in LDS");
 constexpr int COPIES = A_BYTES / (THREADS * 16);  // 16-byte copies per thread per operand: 4
 
 #define GR_LDS __attribute__((address_space(3)))
@@ -115,9 +116,11 @@ __device__ __forceinline__ void pin() { __builtin_amdgcn_sched_barrier(0); }
 constexpr int64_t MAX_LDA = (int64_t(1) << 31) / (BM * 2);
 constexpr int64_t MAX_LDB = (int64_t(1) << 31) / (BK * 2);
 
+template <bool EDGE>
 __global__ __launch_bounds__(THREADS, 1) void gemm_relu_tile2_kernel(
     const uint16_t* __restrict__ A, const uint16_t* __restrict__ B, uint16_t* __restrict__ C, int64_t M, int64_t N,
-    int64_t K, int64_t lda, int64_t ldb, int64_t ldc, uint32_t tiles_m, uint32_t tiles_n, uint32_t group_m) {
+    int64_t K, int64_t lda, int64_t ldb, int64_t ldc, uint32_t tiles_m, uint32_t tiles_n, uint32_t group_m,
+    int vec_c) {
     __shared__ __attribute__((aligned(1024))) uint8_t lds[LDS_BYTES];
 
     const uint32_t tid = threadIdx.x;
@@ -128,7 +131,8 @@ __global__ __launch_bounds__(THREADS, 1) void gemm_relu_tile2_kernel(
 
     uint32_t tm, tn;
     tile_of_workgroup(blockIdx.x, gridDim.x, tiles_m, tiles_n, group_m, tm, tn);
-    const int64_t m0 = (int64_t)tm * BM;
+    const int64_t m_tile = (int64_t)tm * BM;
+    const int64_t m0 = EDGE ? edge::shifted_row0(m_tile, M, BM) : m_tile;
     const int64_t n0 = (int64_t)tn * BN;
 
     // ---- copies: copy i of this wave fills LDS block 4*wave + i of a slot ---
@@ -147,7 +151,8 @@ __global__ __launch_bounds__(THREADS, 1) void gemm_relu_tile2_kernel(
         const uint32_t ca = (lane & 3u) ^ ((ra >> 2) & 3u);
         off_a[i] = (uint32_t)((ra * lda + 8u * ca) * 2);
         const uint32_t rb = 2u * blk + (lane >> 5);
-        const uint32_t cb = (lane & 31u) ^ ((rb & 3u) << 2);
+        uint32_t cb = (lane & 31u) ^ ((rb & 3u) << 2);
+        if constexpr (EDGE) cb = edge::clamp_chunk(cb, n0, N);
         off_b[i] = (uint32_t)((rb * ldb + 8u * cb) * 2);
     }
     const uint32_t lds_base = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(GR_LDS uint8_t*)lds);
@@ -315,28 +320,10 @@ __global__ __launch_bounds__(THREADS, 1) void gemm_relu_tile2_kernel(
     step_tail(kt + 4, f0, f1);
     step_tail(kt + 5, f1, f0);
 
-    // Epilogue: block (i, j) holds C^T; lane l, register r is C[m][n] with
-    // m = 32i + l%32, n = 32j + 8(r/4) + 4(l/32) + r%4.
-    const uint32_t frag_row = lane & 31u;
-    const uint32_t frag_half = lane >> 5;
-#pragma unroll
-    for (int i = 0; i < FM; ++i) {
-        const int64_t m = m0 + wm * WAVE_TM + 32 * i + frag_row;
-        uint16_t* crow = C + m * ldc;
-#pragma unroll
-        for (int j = 0; j < FN; ++j) {
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const int64_t n = n0 + wn * WAVE_TN + 32 * j + 8 * q + 4 * frag_half;
-                u32x2 p;
-                p[0] = relu_pack2(acc[i][j][4 * q + 0], acc[i][j][4 * q + 1]);
-                p[1] = relu_pack2(acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]);
-                *reinterpret_cast<u32x2*>(crow + n) = p;
-            }
-        }
-    }
-    (void)M;
-    (void)N;
+    // Epilogue: ReLU, fp16 and the store of C, staged through LDS (the
+    // operand ring is no longer needed).
+    epi::store_wave_tile<EDGE>(acc, lds + wave * epi::REGION_BYTES, lane, C, ldc, m0 + wm * WAVE_TM,
+                               n0 + wn * WAVE_TN, m_tile, M, N, vec_c);
 }
 
 #undef GR_LDS

@@ -49,6 +49,8 @@ constexpr int64_t MAX_LDB = tile2::MAX_LDB;
 
 #define GR_LDS __attribute__((address_space(3)))
 
+static_assert(LDS_BYTES >= 4 * epi::REGION_BYTES, "the epilogue stages four wave tiles in LDS");
+
 // Byte offset of chunk c (8 fp16) of row m of an A slot (128-byte rows).
 __device__ __forceinline__ uint32_t a64_off(uint32_t m, uint32_t c) { return m * 128u + ((c ^ ((m >> 1) & 7u)) << 4); }
 
@@ -57,9 +59,11 @@ struct Frags {
     f16x8 b[KSUB][FN];
 };
 
+template <bool EDGE>
 __global__ __launch_bounds__(THREADS, 1) void gemm_relu_tile3_kernel(
     const uint16_t* __restrict__ A, const uint16_t* __restrict__ B, uint16_t* __restrict__ C, int64_t M, int64_t N,
-    int64_t K, int64_t lda, int64_t ldb, int64_t ldc, uint32_t tiles_m, uint32_t tiles_n, uint32_t group_m) {
+    int64_t K, int64_t lda, int64_t ldb, int64_t ldc, uint32_t tiles_m, uint32_t tiles_n, uint32_t group_m,
+    int vec_c) {
     using tile2::b_off;
     using tile2::barrier;
     using tile2::dma16;
@@ -78,7 +82,8 @@ __global__ __launch_bounds__(THREADS, 1) void gemm_relu_tile3_kernel(
 
     uint32_t tm, tn;
     tile_of_workgroup(blockIdx.x, gridDim.x, tiles_m, tiles_n, group_m, tm, tn);
-    const int64_t m0 = (int64_t)tm * BM;
+    const int64_t m_tile = (int64_t)tm * BM;
+    const int64_t m0 = EDGE ? edge::shifted_row0(m_tile, M, BM) : m_tile;
     const int64_t n0 = (int64_t)tn * BN;
 
     // ---- copies -------------------------------------------------------------
@@ -106,7 +111,8 @@ __global__ __launch_bounds__(THREADS, 1) void gemm_relu_tile3_kernel(
     for (int i = 0; i < 4; ++i) {
         const uint32_t blk = 4u * wave + (uint32_t)i;
         const uint32_t rb = 2u * blk + (lane >> 5);
-        const uint32_t cb = (lane & 31u) ^ ((rb & 3u) << 2);
+        uint32_t cb = (lane & 31u) ^ ((rb & 3u) << 2);
+        if constexpr (EDGE) cb = edge::clamp_chunk(cb, n0, N);
         off_b[i] = (uint32_t)((rb * ldb + 8u * cb) * 2);
     }
     const uint32_t lds_base = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(GR_LDS uint8_t*)lds);
@@ -313,28 +319,10 @@ __global__ __launch_bounds__(THREADS, 1) void gemm_relu_tile3_kernel(
     step_any(kt + 4, f1, f0);
     step_any(kt + 5, f0, f1);
 
-    // Epilogue: block (i, j) holds C^T; lane l, register r is C[m][n] with
-    // m = 32i + l%32, n = 32j + 8(r/4) + 4(l/32) + r%4.
-    const uint32_t frag_row = lane & 31u;
-    const uint32_t frag_half = lane >> 5;
-#pragma unroll
-    for (int i = 0; i < FM; ++i) {
-        const int64_t m = m0 + wm * WAVE_TM + 32 * i + frag_row;
-        uint16_t* crow = C + m * ldc;
-#pragma unroll
-        for (int j = 0; j < FN; ++j) {
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const int64_t n = n0 + wn * WAVE_TN + 32 * j + 8 * q + 4 * frag_half;
-                u32x2 p;
-                p[0] = relu_pack2(acc[i][j][4 * q + 0], acc[i][j][4 * q + 1]);
-                p[1] = relu_pack2(acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]);
-                *reinterpret_cast<u32x2*>(crow + n) = p;
-            }
-        }
-    }
-    (void)M;
-    (void)N;
+    // Epilogue: ReLU, fp16 and the store of C, staged through LDS (the
+    // operand ring is no longer needed).
+    epi::store_wave_tile<EDGE>(acc, lds + wave * epi::REGION_BYTES, lane, C, ldc, m0 + wm * WAVE_TM,
+                               n0 + wn * WAVE_TN, m_tile, M, N, vec_c);
 }
 
 #undef GR_LDS

@@ -17,10 +17,14 @@
  * Conventions shared by every entry point:
  *   - Pointers A, B, C are DEVICE pointers (HIP) to fp16 bit patterns, owned
  *     by the caller.  The library allocates nothing on the call path, keeps no
- *     per-call state and never frees caller memory.
+ *     per-call state and never frees caller memory; the only scratch memory
+ *     it uses is a workspace the caller passes (the *_ws calls).
  *   - C is never read (there is no beta); elements of C outside the M x N
  *     window (columns N..ldc-1, rows >= M) are never written.  Padding columns
- *     of A (K..lda-1) and B (N..ldb-1) are never used.
+ *     of A (K..lda-1) and B (N..ldb-1) never affect the result.  Reads stay
+ *     inside the 16-byte aligned blocks that hold elements of A and B: the
+ *     pipelined kernel copies whole 16-byte chunks, so it may read the padding
+ *     of B's rows and up to 14 bytes after B's last element.
  *   - Any M, N, K >= 0 work with the same library: tile shapes are fixed when
  *     the library is built; edges that do not fill a tile are guarded.
  *     M == 0 or N == 0: nothing is launched, GR_OK.  K == 0: C = +0.
@@ -61,9 +65,12 @@ extern "C" {
 
 /* ---- execution paths chosen by the planner --------------------------------- */
 #define GR_PATH_NONE       0 /* empty output: nothing to launch                            */
-#define GR_PATH_TILE       1 /* MFMA tile kernel, every edge a whole tile, 16-B rows        */
+#define GR_PATH_TILE       1 /* pipelined MFMA tile kernel, direct-to-LDS copies: 16-B rows  */
+                             /* of A and B, K % 32 == 0, M >= 256; any N and C layout      */
 #define GR_PATH_TILE_EDGE  2 /* MFMA tile kernel with edge guards and narrow loads          */
 #define GR_PATH_SMALL_M    3 /* bandwidth kernel for GEMV-like shapes (few rows of A)       */
+#define GR_PATH_TILE_PACKED 4 /* copy A and/or B into the caller's workspace (aligned rows, */
+                              /* K zero-padded), then the pipelined kernel; needs workspace */
 
 /* What the planner decided for one problem.  Filled by gemm_relu_f16_plan. */
 typedef struct gr_plan_t {
@@ -76,8 +83,10 @@ typedef struct gr_plan_t {
     int64_t grid;        /* workgroups launched (1-D grid)                            */
     int32_t vec_a;       /* fp16 elements per global load of A (8, 4, 2 or 1)         */
     int32_t vec_b;       /* fp16 elements per global load of B                        */
-    int32_t vec_c;       /* fp16 elements per global store of C                       */
+    int32_t vec_c;       /* fp16 elements per global store of C (8, 4 or 1)           */
     int32_t group_m;     /* tile rows per workgroup-order group (L2 reuse)           */
+    int32_t packed;      /* GR_PATH_TILE_PACKED: bit 0 = A copied, bit 1 = B copied     */
+    int64_t workspace;   /* bytes of the caller's workspace the path uses (else 0)     */
 } gr_plan_t;
 
 /*
@@ -118,16 +127,91 @@ int gemm_relu_f16_plan(int64_t M, int64_t N, int64_t K,
  * the planner's choice, for tests that cross-check the paths on one input.
  *   path  GR_PATH_TILE, GR_PATH_TILE_EDGE or GR_PATH_SMALL_M.
  * GR_PATH_TILE is accepted only when the planner's conditions for it hold
- * (whole tiles, 16-byte aligned rows); GR_PATH_SMALL_M only when the small-M
- * kernel's alignment conditions hold (see gemm_relu_f16_plan).  Otherwise
- * GR_ERR_INVALID_PATH and nothing is launched.  GR_PATH_TILE_EDGE accepts any
- * valid problem.
+ * (16-byte aligned rows of A and B, K a positive multiple of 32, M >= 256,
+ * pitches of at most 2^22 elements for A and 2^25 for B); GR_PATH_SMALL_M
+ * only when the small-M kernel's alignment conditions hold (see
+ * gemm_relu_f16_plan).  Otherwise GR_ERR_INVALID_PATH and nothing is
+ * launched.  GR_PATH_TILE_EDGE accepts any valid problem.
  */
 int gemm_relu_f16_forced(int64_t M, int64_t N, int64_t K,
                          const uint16_t* A, int64_t lda,
                          const uint16_t* B, int64_t ldb,
                          uint16_t* C, int64_t ldc,
                          void* stream, int path);
+
+/*
+ * ---- calls with a caller-provided workspace ---------------------------------
+ * The pipelined kernel reads A and B in whole 16-byte chunks and walks K in
+ * whole 32-deep strips.  When an operand's rows are not 16-byte aligned, or
+ * K is not a multiple of 32, the calls above fall back to the guarded
+ * register-staged kernel.  Given scratch device memory, the library instead
+ * copies the offending operand(s) into it -- rows 16-byte aligned, K padded
+ * with zeros to a multiple of 64 (the padded steps add exact zeros, the same
+ * rule as the edge guards) -- and runs the pipelined kernel on the copies:
+ * two launches on the stream, one extra read and write of the copied
+ * operands.  The result is the same up to fp32 summation order (bit-exact
+ * against the other tile paths: same MFMA steps, same k order).
+ *
+ * Workspace rules: a DEVICE pointer, 256-byte aligned, owned by the caller,
+ * not overlapping A, B or C; its contents on entry are ignored and on return
+ * are unspecified.  The work is stream-ordered: the caller may reuse or free
+ * the workspace once the call's work on `stream` is done, and two calls in
+ * flight at once (on different streams) need two workspaces.
+ */
+
+/*
+ * gemm_relu_f16_workspace_size -- bytes of workspace that let this problem
+ * take GR_PATH_TILE_PACKED; 0 when the problem never uses a workspace (it
+ * already runs on the pipelined or small-M kernel, or has fewer than 256
+ * rows, or is empty).  Validates like gemm_relu_f16; no HIP call.
+ *   bytes  host pointer receiving the size (must not be NULL)
+ */
+int gemm_relu_f16_workspace_size(int64_t M, int64_t N, int64_t K,
+                                 const uint16_t* A, int64_t lda,
+                                 const uint16_t* B, int64_t ldb,
+                                 const uint16_t* C, int64_t ldc,
+                                 int64_t* bytes);
+
+/*
+ * gemm_relu_f16_ws -- gemm_relu_f16 with a workspace.
+ *   workspace, workspace_bytes  the caller's scratch (NULL, 0 = none)
+ * Takes GR_PATH_TILE_PACKED when the workspace holds at least the size
+ * gemm_relu_f16_workspace_size reports and the problem is large enough for
+ * the copies to pay (M*N*K >= 2^30); otherwise does exactly what
+ * gemm_relu_f16 does.  Extra errors: GR_ERR_INVALID_ARG for a negative size
+ * or a workspace not 256-byte aligned, GR_ERR_NULL_PTR for NULL with a
+ * positive size, GR_ERR_ALIAS when the workspace overlaps A, B or C.
+ */
+int gemm_relu_f16_ws(int64_t M, int64_t N, int64_t K,
+                     const uint16_t* A, int64_t lda,
+                     const uint16_t* B, int64_t ldb,
+                     uint16_t* C, int64_t ldc,
+                     void* workspace, int64_t workspace_bytes,
+                     void* stream);
+
+/*
+ * gemm_relu_f16_forced_ws -- gemm_relu_f16_forced with a workspace, which
+ * also accepts GR_PATH_TILE_PACKED (whenever gemm_relu_f16_workspace_size is
+ * positive and the workspace holds that many bytes, whatever the size of the
+ * problem).  Test hook.
+ */
+int gemm_relu_f16_forced_ws(int64_t M, int64_t N, int64_t K,
+                            const uint16_t* A, int64_t lda,
+                            const uint16_t* B, int64_t ldb,
+                            uint16_t* C, int64_t ldc,
+                            void* workspace, int64_t workspace_bytes,
+                            void* stream, int path);
+
+/*
+ * gemm_relu_f16_plan_ws -- the planner's decision for gemm_relu_f16_ws with a
+ * workspace of `workspace_bytes` bytes (its address is not checked).  Pure,
+ * like gemm_relu_f16_plan.
+ */
+int gemm_relu_f16_plan_ws(int64_t M, int64_t N, int64_t K,
+                          const uint16_t* A, int64_t lda,
+                          const uint16_t* B, int64_t ldb,
+                          const uint16_t* C, int64_t ldc,
+                          int64_t workspace_bytes, gr_plan_t* out);
 
 /* Static, NUL-terminated name of a status code ("GR_OK", "GR_ERR_ALIAS", ...).
    Unknown codes give "GR_ERR_UNKNOWN". */

@@ -51,6 +51,22 @@ def call(M, N, K, dA, lda, dB, ldb, dC, ldc, path=None, stream=None, offsets=(0,
     return st
 
 
+def call_ws(M, N, K, dA, lda, dB, ldb, dC, ldc, ws, ws_bytes, path=None, offsets=(0, 0, 0)):
+    """As call(), with a device workspace (a tensor, or None) of ws_bytes bytes."""
+    t = torch()
+    a = dA.data_ptr() + 2 * offsets[0] if dA is not None else 0
+    b = dB.data_ptr() + 2 * offsets[1] if dB is not None else 0
+    c = dC.data_ptr() + 2 * offsets[2] if dC is not None else 0
+    w = ws.data_ptr() if ws is not None else 0
+    s = t.cuda.current_stream().cuda_stream
+    if path is None:
+        st = gr.gemm_relu_f16_ws(M, N, K, a, lda, b, ldb, c, ldc, w, ws_bytes, s)
+    else:
+        st = gr.gemm_relu_f16_forced_ws(M, N, K, a, lda, b, ldb, c, ldc, w, ws_bytes, s, path)
+    t.cuda.synchronize()
+    return st
+
+
 def as_f64(bits) -> np.ndarray:
     return np.asarray(bits, dtype=np.uint16).view(np.float16).astype(np.float64)
 

@@ -39,7 +39,8 @@ def header_defines():
 def test_library_exports_every_declared_symbol():
     names = header_functions()
     assert set(names) >= {"gemm_relu_f16", "gemm_relu_f16_plan", "gemm_relu_f16_forced",
-                          "gemm_relu_status_string", "gemm_relu_version"}
+                          "gemm_relu_f16_workspace_size", "gemm_relu_f16_ws", "gemm_relu_f16_forced_ws",
+                          "gemm_relu_f16_plan_ws", "gemm_relu_status_string", "gemm_relu_version"}
     lib = ctypes.CDLL(gr.LIB_PATH)
     for n in names:
         assert hasattr(lib, n), n
@@ -144,6 +145,93 @@ def test_plan_ragged_vector_widths():
     assert p["path"] == gr.GR_PATH_TILE_EDGE and p["vec_a"] == 1
 
 
+def test_plan_partial_tiles_take_the_pipelined_kernel():
+    # 16-byte rows and K % 32 == 0: partial tiles in M and N stay on the
+    # pipelined kernel, whatever C's layout
+    st, p = plan(4099, 3071, 2048, lda=2048, ldb=3072, ldc=3071)
+    assert st == gr.GR_OK and p["path"] == gr.GR_PATH_TILE and p["grid"] == 17 * 12 and p["vec_c"] == 1
+    assert plan(256, 1, 32, ldb=8)[1]["path"] == gr.GR_PATH_TILE
+    # fewer than 256 rows, K % 32 != 0, or rows not 16-byte aligned: guarded kernel
+    assert plan(255, 512, 512)[1]["path"] == gr.GR_PATH_TILE_EDGE
+    assert plan(512, 512, 48)[1]["path"] == gr.GR_PATH_TILE_EDGE
+    assert plan(512, 500, 512)[1]["path"] == gr.GR_PATH_TILE_EDGE
+    assert plan(512, 512, 512, b=BASE_B + 8)[1]["path"] == gr.GR_PATH_TILE_EDGE
+
+
+def ws_size(M, N, K, lda=None, ldb=None, ldc=None, a=BASE_A, b=BASE_B, c=BASE_C):
+    lda = max(K, 1) if lda is None else lda
+    ldb = max(N, 1) if ldb is None else ldb
+    ldc = max(N, 1) if ldc is None else ldc
+    return gr.gemm_relu_f16_workspace_size(M, N, K, a, lda, b, ldb, c, ldc)
+
+
+def plan_ws(M, N, K, ws, lda=None, ldb=None, ldc=None, a=BASE_A, b=BASE_B, c=BASE_C):
+    lda = max(K, 1) if lda is None else lda
+    ldb = max(N, 1) if ldb is None else ldb
+    ldc = max(N, 1) if ldc is None else ldc
+    return gr.gemm_relu_f16_plan_ws(M, N, K, a, lda, b, ldb, c, ldc, ws)
+
+
+def rup(x, m):
+    return -(-x // m) * m
+
+
+def test_workspace_size_and_packed_plan():
+    # the ragged workload: rows of A (4100 B) and B (6142 B) misaligned, K % 32 == 2
+    st, size = ws_size(4099, 3071, 2050)
+    kp = rup(2050, 64)
+    assert st == gr.GR_OK and size == rup(4099 * kp * 2, 256) + kp * rup(3071, 8) * 2
+    st, p = plan_ws(4099, 3071, 2050, size)
+    assert st == gr.GR_OK and p["path"] == gr.GR_PATH_TILE_PACKED and p["packed"] == 3
+    assert p["workspace"] == size and p["grid"] == 17 * 12
+    # one byte short, or no workspace: the guarded kernel
+    assert plan_ws(4099, 3071, 2050, size - 1)[1]["path"] == gr.GR_PATH_TILE_EDGE
+    assert plan(4099, 3071, 2050)[1]["path"] == gr.GR_PATH_TILE_EDGE
+    # K % 32 == 0 with only B misaligned: only B is copied, K unchanged
+    st, size = ws_size(4096, 3071, 2048)
+    assert size == 2048 * rup(3071, 8) * 2
+    assert plan_ws(4096, 3071, 2048, size)[1]["packed"] == 2
+    # only A misaligned
+    st, size = ws_size(4096, 4096, 4096, a=BASE_A + 2)
+    assert size == 4096 * 4096 * 2
+    assert plan_ws(4096, 4096, 4096, size, a=BASE_A + 2)[1]["packed"] == 1
+    # aligned K % 64 != 0 (but K % 32 != 0 too): both padded
+    st, size = ws_size(1024, 1024, 1000)
+    assert size == 1024 * 1024 * 2 + 1024 * 1024 * 2
+    # below the size threshold the planner keeps the single-launch kernel
+    st, size = ws_size(300, 300, 300)
+    assert size > 0 and plan_ws(300, 300, 300, size)[1]["path"] == gr.GR_PATH_TILE_EDGE
+
+
+def test_workspace_not_used_where_it_cannot_help():
+    assert ws_size(4096, 4096, 4096) == (gr.GR_OK, 0)       # pipelined in place
+    assert ws_size(8, 16384, 8192) == (gr.GR_OK, 0)         # small-M kernel
+    assert ws_size(200, 4096, 4100) == (gr.GR_OK, 0)        # fewer than 256 rows
+    assert ws_size(0, 4096, 4096) == (gr.GR_OK, 0)          # empty
+    assert ws_size(512, 512, 0, lda=1) == (gr.GR_OK, 0)     # K == 0
+    assert plan_ws(4096, 4096, 4096, 1 << 30)[1]["path"] == gr.GR_PATH_TILE
+    assert plan_ws(4096, 4096, 4096, 1 << 30)[1]["workspace"] == 0
+
+
+def test_workspace_argument_checks():
+    ws = 0x7F6000000000
+    args = (4099, 3071, 2050, BASE_A, 2050, BASE_B, 3071, BASE_C, 3071)
+    assert gr.gemm_relu_f16_ws(*args, ws, -1) == gr.GR_ERR_INVALID_ARG
+    assert gr.gemm_relu_f16_ws(*args, 0, 1 << 20) == gr.GR_ERR_NULL_PTR
+    assert gr.gemm_relu_f16_ws(*args, ws + 16, 1 << 20) == gr.GR_ERR_INVALID_ARG
+    assert gr.gemm_relu_f16_ws(*args, BASE_C - 256, 1 << 20) == gr.GR_ERR_ALIAS
+    assert gr.gemm_relu_f16_ws(*args, BASE_A + 4096, 256) == gr.GR_ERR_ALIAS
+    # the packed path cannot be forced without a large enough workspace
+    assert gr.gemm_relu_f16_forced(*args, None, gr.GR_PATH_TILE_PACKED) == gr.GR_ERR_INVALID_PATH
+    assert gr.gemm_relu_f16_forced_ws(*args, ws, 4096, None, gr.GR_PATH_TILE_PACKED) == gr.GR_ERR_INVALID_PATH
+    assert gr.gemm_relu_f16_forced_ws(*args, ws, 1 << 30, None, 99) == gr.GR_ERR_INVALID_PATH
+    assert gr.gemm_relu_f16_plan_ws(*args, -1)[0] == gr.GR_ERR_INVALID_ARG
+    n = ctypes.c_int64(0)
+    assert gr.lib().gemm_relu_f16_workspace_size(*args, None) == gr.GR_ERR_INVALID_ARG
+    assert gr.lib().gemm_relu_f16_workspace_size(-1, 8, 8, BASE_A, 8, BASE_B, 8, BASE_C, 8,
+                                                 ctypes.byref(n)) == gr.GR_ERR_INVALID_DIM
+
+
 def test_plan_empty_and_k_zero():
     assert plan(0, 8, 8)[1]["path"] == gr.GR_PATH_NONE
     assert plan(8, 0, 8, ldb=1, ldc=1)[1]["path"] == gr.GR_PATH_NONE
@@ -167,8 +255,13 @@ def test_calls_validate_before_touching_the_device():
     assert gr.gemm_relu_f16(-1, 8, 8, BASE_A, 8, BASE_B, 8, BASE_C, 8) == gr.GR_ERR_INVALID_DIM
     assert gr.gemm_relu_f16(8, 8, 8, BASE_A, 8, BASE_B, 8, BASE_A, 8) == gr.GR_ERR_ALIAS
     assert gr.gemm_relu_f16_forced(8, 8, 8, BASE_A, 8, BASE_B, 8, BASE_C, 8, None, 99) == gr.GR_ERR_INVALID_PATH
-    # tile path forced on a shape that does not fill whole tiles
-    assert gr.gemm_relu_f16_forced(300, 256, 64, BASE_A, 64, BASE_B, 256, BASE_C, 256, None,
+    # tile path forced where its conditions fail: K not a multiple of 32,
+    # fewer than 256 rows, misaligned B rows
+    assert gr.gemm_relu_f16_forced(300, 256, 48, BASE_A, 48, BASE_B, 256, BASE_C, 256, None,
+                                   gr.GR_PATH_TILE) == gr.GR_ERR_INVALID_PATH
+    assert gr.gemm_relu_f16_forced(255, 256, 64, BASE_A, 64, BASE_B, 256, BASE_C, 256, None,
+                                   gr.GR_PATH_TILE) == gr.GR_ERR_INVALID_PATH
+    assert gr.gemm_relu_f16_forced(300, 250, 64, BASE_A, 64, BASE_B, 250, BASE_C, 256, None,
                                    gr.GR_PATH_TILE) == gr.GR_ERR_INVALID_PATH
     # small-M forced with too many rows
     assert gr.gemm_relu_f16_forced(64, 256, 64, BASE_A, 64, BASE_B, 256, BASE_C, 256, None,
@@ -217,7 +310,8 @@ def test_no_kernel_spills_to_scratch():
     names = re.findall(r"Function Name: (\S+)", res.stderr)
     scratch = [int(x) for x in re.findall(r"ScratchSize \[bytes/lane\]: (\d+)", res.stderr)]
     assert names and len(names) == len(scratch)
-    hot = {n: s for n, s in zip(names, scratch) if "tile2" in n or "tile3" in n or "smallm" in n}
+    hot = {n: s for n, s in zip(names, scratch)
+           if any(k in n for k in ("gemm_relu_tile2_kernel", "gemm_relu_tile3_kernel", "gemm_relu_smallm_kernel"))}
     assert hot, names
     # the pipelined whole-tile kernels may spill a few bytes outside their
     # steady loop; the small-M kernel must not spill at all

@@ -12,7 +12,7 @@ import pytest
 import dense_gemm_epilogue_tiled_amd as gr
 import oracle
 import synth
-from gpu_util import (as_f64, assert_parity, call, edge_indices, from_dev, full_dev, log,
+from gpu_util import (as_f64, assert_parity, call, call_ws, edge_indices, from_dev, full_dev, log,
                       to_dev)
 
 pytestmark = [pytest.mark.gpu, pytest.mark.usefixtures("oracle_lib")]
@@ -234,6 +234,128 @@ def test_tile_pipeline_every_strip_count(K):
     C2 = run_full(A, B, M, N, K, path=gr.GR_PATH_TILE_EDGE)
     assert_parity(window(C1, M, N, N), oracle.gemm_relu_full(A, B), "tile K=%d" % K)
     assert np.array_equal(C1, C2)
+
+
+# ---- the pipelined kernels on partial tiles (16-byte rows, K % 32 == 0) -------
+
+PARTIAL_TILE_CASES = [
+    (257, 264, 64, 64, 264, 264),          # one row past a tile; N a multiple of 8
+    (300, 250, 96, 96, 256, 251),          # K % 64 == 32 (32-deep kernel); odd ldc: 2-byte stores
+    (511, 1, 128, 136, 8, 1),              # a single column; padded A rows
+    (1000, 700, 320, 320, 704, 700),       # 4 x 3 tiles, last tile row shifted by 24 rows
+    (4099, 3071, 2048, 2048, 3072, 3071),  # the ragged workload's M and N with 16-byte rows
+]
+
+
+@pytest.mark.parametrize("M,N,K,lda,ldb,ldc", PARTIAL_TILE_CASES)
+def test_pipelined_kernel_partial_tiles(M, N, K, lda, ldb, ldc):
+    """Shapes whose M and N do not fill tiles run the pipelined kernel (the
+    last tile row moved up to end at M, copies past N clamped to the last
+    chunk, guarded stores).  Full oracle check, padding of A and B poisoned,
+    C's padding columns and the rows after it must keep the sentinel, and
+    the result must equal the register-staged guarded kernel's bit for bit
+    (same MFMA steps in the same k order)."""
+    st, plan = gr.gemm_relu_f16_plan(M, N, K, 0x100000, lda, 0x200000000000, ldb, 0x400000000000, ldc)
+    assert st == gr.GR_OK and plan["path"] == gr.GR_PATH_TILE, plan
+    A, B = synth.random_operands(M, N, K, seed=M + 3 * N + 7 * K, lda=lda, ldb=ldb)
+    extra_rows = 2
+    C1 = run_full(A, B, M, N, K, lda=lda, ldb=ldb, ldc=ldc, c_rows=M + extra_rows)
+    C = C1[:M * ldc].reshape(M, ldc)
+    assert_parity(C[:, :N], oracle.gemm_relu_full(A, B, M=M, N=N, K=K, lda=lda, ldb=ldb),
+                  "pipelined partial %dx%dx%d" % (M, N, K))
+    assert np.all(C[:, N:] == SENTINEL), "a padding column of C was written"
+    assert np.all(C1[M * ldc:] == SENTINEL), "a row past M was written"
+    C2 = run_full(A, B, M, N, K, lda=lda, ldb=ldb, ldc=ldc, c_rows=M + extra_rows, path=gr.GR_PATH_TILE_EDGE)
+    assert np.array_equal(C1, C2)
+
+
+# ---- the packed path: operands copied into a workspace, then pipelined ------
+
+WS_POISON = 0x7E5A  # the workspace starts as NaN bit patterns: the copy must overwrite what it uses
+
+PACKED_CASES = [
+    # M, N, K, lda, ldb, ldc, expected `packed` bits
+    (4099, 3071, 2050, 2050, 3071, 3071, 3),  # the ragged workload: both copied, K padded to 2112
+    (300, 270, 100, 109, 275, 273, 3),        # odd pitches, padding poisoned
+    (256, 8, 33, 33, 8, 8, 3),                # one tile, K padded from 33 to 64
+    (512, 640, 1000, 1000, 640, 640, 3),      # aligned rows, K % 32 == 8: both padded
+    (1000, 3071, 2048, 2048, 3071, 3071, 2),  # only B misaligned: K unchanged
+    (777, 512, 96, 97, 512, 512, 1),          # only A misaligned, K % 64 == 32 (32-deep kernel)
+]
+
+
+@pytest.mark.parametrize("M,N,K,lda,ldb,ldc,bits", PACKED_CASES)
+def test_packed_path_parity(M, N, K, lda, ldb, ldc, bits):
+    """Forced packed path against the oracle (full), C's padding and the rows
+    after it keep the sentinel, bytes of the workspace past the size the
+    library asked for are never written, and the result equals the guarded
+    kernel's bit for bit (the padded K steps add exact zeros)."""
+    import torch as t
+    st, size = gr.gemm_relu_f16_workspace_size(M, N, K, 0x100000, lda, 0x200000000000, ldb, 0x400000000000, ldc)
+    assert st == gr.GR_OK and size > 0
+    st, plan = gr.gemm_relu_f16_plan_ws(M, N, K, 0x100000, lda, 0x200000000000, ldb, 0x400000000000, ldc, size)
+    log("packed %dx%dx%d size=%d plan=%s" % (M, N, K, size, plan))
+    A, B = synth.random_operands(M, N, K, seed=5 * M + N + K, lda=lda, ldb=ldb)
+    dA, dB = to_dev(A), to_dev(B)
+    extra_rows = 2
+    dC = full_dev(((M + extra_rows) * ldc,), SENTINEL)
+    tail = 4096
+    ws = full_dev(((size + tail) // 2,), WS_POISON).view(t.uint8)
+    assert call_ws(M, N, K, dA, lda, dB, ldb, dC, ldc, ws, size, path=gr.GR_PATH_TILE_PACKED) == gr.GR_OK
+    C1 = from_dev(dC)
+    C = C1[:M * ldc].reshape(M, ldc)
+    assert_parity(C[:, :N], oracle.gemm_relu_full(A, B, M=M, N=N, K=K, lda=lda, ldb=ldb),
+                  "packed %dx%dx%d" % (M, N, K))
+    assert np.all(C[:, N:] == SENTINEL), "a padding column of C was written"
+    assert np.all(C1[M * ldc:] == SENTINEL), "a row past M was written"
+    w = ws.view(t.int16).cpu().numpy().view(np.uint16)
+    assert np.all(w[size // 2:] == WS_POISON), "workspace written past the size the library asked for"
+    dC2 = full_dev(((M + extra_rows) * ldc,), SENTINEL)
+    assert call(M, N, K, dA, lda, dB, ldb, dC2, ldc, path=gr.GR_PATH_TILE_EDGE) == gr.GR_OK
+    assert np.array_equal(C1, from_dev(dC2))
+    # the workspace holds exactly the copies the case expects
+    kp = K if K % 32 == 0 else -(-K // 64) * 64
+    expect = (-(-(M * kp * 2) // 256) * 256 if bits & 1 else 0) + (kp * (-(-N // 8) * 8) * 2 if bits & 2 else 0)
+    assert size == expect
+    if plan["path"] == gr.GR_PATH_TILE_PACKED:
+        assert plan["packed"] == bits
+
+
+def test_packed_path_reuses_a_dirty_workspace():
+    """Two calls in a row on one workspace, the second smaller with other
+    pitches: stale copies from the first never leak into the second."""
+    import torch as t
+    shapes = [(1200, 1100, 700, 701, 1101, 1100), (520, 300, 90, 91, 301, 300)]
+    sizes = [gr.gemm_relu_f16_workspace_size(M, N, K, 0x100000, la, 0x200000000000, lb, 0x400000000000, lc)[1]
+             for M, N, K, la, lb, lc in shapes]
+    ws = full_dev((max(sizes) // 2 + 128,), WS_POISON).view(t.uint8)
+    for (M, N, K, la, lb, lc), size in zip(shapes, sizes):
+        A, B = synth.random_operands(M, N, K, seed=M + K, lda=la, ldb=lb)
+        dC = full_dev((M * lc,), SENTINEL)
+        assert call_ws(M, N, K, to_dev(A), la, to_dev(B), lb, dC, lc, ws, size,
+                       path=gr.GR_PATH_TILE_PACKED) == gr.GR_OK
+        C = from_dev(dC).reshape(M, lc)
+        assert_parity(C[:, :N], oracle.gemm_relu_full(A, B, M=M, N=N, K=K, lda=la, ldb=lb), "reuse %d" % M)
+
+
+def test_ws_call_picks_packed_path_for_the_ragged_workload():
+    """gemm_relu_f16_ws with the size the library asks for runs the packed
+    path on the ragged workload (checked through the plan) and matches the
+    call without a workspace bit for bit."""
+    w = synth.WORKLOADS["ragged4099x3071x2050"]
+    import torch as t
+    M, N, K = w.M, w.N, w.K
+    st, size = gr.gemm_relu_f16_workspace_size(M, N, K, 0x100000, K, 0x200000000000, N, 0x400000000000, N)
+    assert gr.gemm_relu_f16_plan_ws(M, N, K, 0x100000, K, 0x200000000000, N, 0x400000000000, N,
+                                    size)[1]["path"] == gr.GR_PATH_TILE_PACKED
+    A, B = synth.operands(w)
+    dA, dB = to_dev(A), to_dev(B)
+    ws = t.empty(size, dtype=t.uint8, device="cuda")
+    dC1 = full_dev((M * N,), SENTINEL)
+    dC2 = full_dev((M * N,), SENTINEL)
+    assert call_ws(M, N, K, dA, K, dB, N, dC1, N, ws, size) == gr.GR_OK
+    assert call(M, N, K, dA, K, dB, N, dC2, N) == gr.GR_OK
+    assert np.array_equal(from_dev(dC1), from_dev(dC2))
 
 
 @pytest.mark.parametrize("M,N,K", [(8, 4096, 4096), (1, 640, 96), (16, 1000, 1000), (5, 128, 8200)])
