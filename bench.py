@@ -1,17 +1,21 @@
 #!/usr/bin/env python3
 """Throughput of C = ReLU(A.B) (fp16 in, fp32 accumulate, fp16 out) on one MI355X.
 
-One "step" is one call of the library (``gemm_relu_f16`` through the C ABI) on
-the headline workload, M = N = K = 4096, with A and B already resident in HBM.
+One "step" is one call of the library through the C ABI on the headline
+workload, M = N = K = 4096, with A and B already resident in HBM
+(``gemm_relu_f16``; ``gemm_relu_f16_ws`` with a workspace allocated up front
+for a workload whose plan takes one).
 Prints ONE JSON line (rank 0) with the metric, the roofline of the dominant
 kernel measured live with HIP events on the launch stream, and the CPU oracle
 timed on a bounded sample of the same workload.
 
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
                   [--no-workloads] [--workload NAME] [--copy-probe MIB]
+                  [--vendor-reference]
 
 ``--copy-probe`` runs only a device-to-device copy of known size; it is what
-the HBM-traffic counters are calibrated against.
+the HBM-traffic counters are calibrated against.  ``--vendor-reference`` only
+times torch.mm + relu_ (the vendor BLAS) on the same workloads, for context.
 """
 from __future__ import annotations
 
@@ -66,17 +70,45 @@ def make_device_operands(torch, w, copies=1):
     return A, Bs, C
 
 
-def launcher(gr, torch, w, A, B, C, stream):
+def workspace_for(gr, torch, w, A, B, C):
+    """The device workspace the library asks for on this problem (None if
+    none), allocated once, outside any timed region, as a caller would."""
+    st, size = gr.gemm_relu_f16_workspace_size(w.M, w.N, w.K, A.data_ptr(), w.K, B.data_ptr(), w.N,
+                                               C.data_ptr(), w.N)
+    if st != 0:
+        raise gr.GemmReluError(st, "gemm_relu_f16_workspace_size")
+    return torch.empty(size, dtype=torch.uint8, device="cuda") if size else None
+
+
+def launcher(gr, torch, w, A, B, C, stream, ws=None):
+    """One library call on the workload: gemm_relu_f16, or gemm_relu_f16_ws
+    when the problem takes a workspace."""
     h = stream.cuda_stream
     a, b, c = A.data_ptr(), B.data_ptr(), C.data_ptr()
     M, N, K = w.M, w.N, w.K
-    fn = gr.lib().gemm_relu_f16
+    if ws is None:
+        fn = gr.lib().gemm_relu_f16
 
-    def run():
-        st = fn(M, N, K, a, K, b, N, c, N, h)
-        if st != 0:
-            raise gr.GemmReluError(st)
+        def run():
+            st = fn(M, N, K, a, K, b, N, c, N, h)
+            if st != 0:
+                raise gr.GemmReluError(st)
+    else:
+        fn = gr.lib().gemm_relu_f16_ws
+        wp, wb = ws.data_ptr(), ws.numel()
+
+        def run():
+            st = fn(M, N, K, a, K, b, N, c, N, wp, wb, h)
+            if st != 0:
+                raise gr.GemmReluError(st, "gemm_relu_f16_ws")
     return run
+
+
+def plan_for(gr, w, A, B, C, ws):
+    st, plan = gr.gemm_relu_f16_plan_ws(w.M, w.N, w.K, A.data_ptr(), w.K, B.data_ptr(), w.N, C.data_ptr(), w.N,
+                                        0 if ws is None else ws.numel())
+    assert st == 0
+    return plan
 
 
 def time_launches(torch, run, stream, reps):
@@ -153,7 +185,9 @@ def bench_workload(gr, torch, w, reps, cold):
     copies = 4 if cold else 1
     A, Bs, C = make_device_operands(torch, w, copies=copies)
     stream = torch.cuda.current_stream()
-    runs = [launcher(gr, torch, w, A, B, C, stream) for B in Bs]
+    ws = workspace_for(gr, torch, w, A, Bs[0], C)
+    plan = plan_for(gr, w, A, Bs[0], C, ws)
+    runs = [launcher(gr, torch, w, A, B, C, stream, ws) for B in Bs]
     for r in runs:
         for _ in range(3):
             r()
@@ -169,7 +203,7 @@ def bench_workload(gr, torch, w, reps, cold):
             times.append(t[0])
     else:
         times = time_launches(torch, runs[0], stream, reps)
-    del A, Bs, C
+    del A, Bs, C, ws, runs
     torch.cuda.empty_cache()
     times.sort()
     med = statistics.median(times)
@@ -184,6 +218,8 @@ def bench_workload(gr, torch, w, reps, cold):
         "frac_hbm": round(nbytes / (med * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
         "cache": "cold" if cold else "warm",
         "reps": reps,
+        "path": plan["path_name"],
+        "workspace_bytes": plan["workspace"],
     }
 
 
@@ -200,6 +236,30 @@ def copy_probe(torch, mib):
                       "median_us": round(med * 1e3, 2), "gbs_rw": round(4.0 * n / (med * 1e-3) / 1e9, 1)}))
 
 
+def vendor_reference(torch, reps=30):
+    """Context only: torch.mm (hipBLASLt) followed by an in-place ReLU on the
+    same workloads, timed like the per-workload table (warm, HIP events).
+    Not the product and not a target; printed as its own JSON line."""
+    out = {}
+    for name, w in synth.WORKLOADS.items():
+        A, Bs, C = make_device_operands(torch, w)
+        B = Bs[0]
+        stream = torch.cuda.current_stream()
+
+        def run():
+            torch.relu_(torch.mm(A, B, out=C))
+        for _ in range(5):
+            run()
+        torch.cuda.synchronize()
+        times = sorted(time_launches(torch, run, stream, reps if w.M * w.N * w.K < 1e12 else 10))
+        med = statistics.median(times)
+        flops, _ = algorithmic(w)
+        out[name] = {"median_us": round(med * 1e3, 2), "tflops": round(flops / (med * 1e-3) / 1e12, 1)}
+        del A, Bs, B, C
+        torch.cuda.empty_cache()
+    print(json.dumps({"vendor_reference": out, "what": "torch.mm + torch.relu_ (hipBLASLt), warm, context only"}))
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -209,6 +269,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-workloads", action="store_true", help="skip the secondary per-workload table")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB")
+    ap.add_argument("--vendor-reference", action="store_true",
+                    help="only time torch.mm + relu_ on the workloads (context, not the product)")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -231,14 +293,17 @@ def main():
     if args.copy_probe:
         copy_probe(torch, args.copy_probe)
         return
+    if args.vendor_reference:
+        vendor_reference(torch)
+        return
 
     w = synth.WORKLOADS[args.workload]
     flops, nbytes = algorithmic(w)
     A, Bs, C = make_device_operands(torch, w)
     stream = torch.cuda.current_stream()
-    run = launcher(gr, torch, w, A, Bs[0], C, stream)
-    st, plan = gr.gemm_relu_f16_plan(w.M, w.N, w.K, A.data_ptr(), w.K, Bs[0].data_ptr(), w.N, C.data_ptr(), w.N)
-    assert st == 0
+    ws = workspace_for(gr, torch, w, A, Bs[0], C)
+    run = launcher(gr, torch, w, A, Bs[0], C, stream, ws)
+    plan = plan_for(gr, w, A, Bs[0], C, ws)
 
     for _ in range(args.warmup):
         run()
@@ -271,7 +336,7 @@ def main():
     roof["kernel_avg_us"] = round(ev_ms * 1e3, 2)
     roof["algorithmic_flops"] = flops
     roof["algorithmic_bytes"] = nbytes
-    del A, Bs, C
+    del A, Bs, C, ws, run
     torch.cuda.empty_cache()
 
     out = {
@@ -290,7 +355,8 @@ def main():
         "config": {"workload": w.name, "M": w.M, "N": w.N, "K": w.K, "layout": "row-major A(MxK) B(KxN) C(MxN)",
                    "accumulate": "fp32", "path": plan["path_name"],
                    "tile": [plan["block_m"], plan["block_n"], plan["block_k"]], "grid": plan["grid"],
-                   "threads": plan["threads"], "kernel_source_hash": src_hash},
+                   "threads": plan["threads"], "workspace_bytes": plan["workspace"],
+                   "kernel_source_hash": src_hash},
         "roofline": roof,
     }
 

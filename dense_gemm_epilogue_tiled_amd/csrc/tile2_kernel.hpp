@@ -30,8 +30,10 @@
 //     direct-to-LDS copies (vmcnt) and on the transposing reads (lgkmcnt)
 //     are placed by hand: the compiler cannot see which LDS slot an
 //     in-flight copy writes and would otherwise wait for all of them.
-// Only whole tiles with 16-byte aligned rows come here (the planner checks);
-// the guarded kernel takes every other shape.
+//   * C is written through LDS once the K loop is done (epi::store_wave_tile).
+// Rows of A and B must be 16-byte aligned and K a multiple of 32 (the planner
+// checks).  EDGE=true serves M >= 256 and any N that do not fill whole tiles
+// (edge:: in common.hpp); the guarded register-staged kernel takes the rest.
 #pragma once
 
 #include <type_traits>

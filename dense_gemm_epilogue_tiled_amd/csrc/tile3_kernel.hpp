@@ -1,6 +1,7 @@
-// Pipelined MFMA tile kernel for whole tiles with K a multiple of 64.
+// Pipelined MFMA tile kernel for K a multiple of 64 (16-byte aligned rows;
+// EDGE=true for M >= 256 and N that do not fill whole tiles).
 //
-// The pipelined whole-tile kernel (see tile2_kernel.hpp) with one change in
+// The 32-deep pipelined kernel (see tile2_kernel.hpp) with one change in
 // how A is staged: A moves in 64-deep strips (128-byte row segments, one
 // full cache line per row) through a 3-slot ring, while B keeps its 32-deep
 // strips (512-byte row segments) in a 4-slot ring.  With 32-deep A strips
