@@ -117,9 +117,11 @@ __device__ __forceinline__ void store4(uint16_t* crow, bool row_owned, int64_t n
 // The MFMA accumulators hold C^T blocks: a lane owns 4 consecutive columns of
 // one row, and one store instruction of the whole wave would touch 32 rows.
 // Instead the wave first writes its ReLU'd fp16 tile to LDS (row-major, 256
-// bytes per row, the 16-byte chunk c of row r at slot c XOR (r % 16), so that
-// the read-back below is free of bank conflicts), then reads it back so that
-// consecutive lanes hold consecutive columns of C:
+// bytes per row; the 16-byte chunk c of row r sits at slot c XOR (r % 16),
+// with its two 8-byte halves swapped when (r / 16) is odd, so that both the
+// 8-byte writes of 32 rows and the read-back below are free of bank
+// conflicts), then reads it back so that consecutive lanes hold consecutive
+// columns of C:
 //   vec_c == 8: 16-byte chunks, 16 lanes per 256-byte row segment;
 //   vec_c == 4: the same chunks stored as two 8-byte halves;
 //   vec_c == 1: one element per lane, 64 consecutive columns per store.
@@ -135,6 +137,9 @@ constexpr uint32_t REGION_BYTES = WAVE_TILE * WAVE_TILE * 2;  // 32 KiB per wave
 __device__ __forceinline__ uint32_t tile_off(uint32_t row, uint32_t chunk) {
     return row * 256u + ((chunk ^ (row & 15u)) << 4);
 }
+
+// Which 8-byte half of its slot the half `h` of a chunk of row `row` uses.
+__device__ __forceinline__ uint32_t half_slot(uint32_t row, uint32_t h) { return h ^ ((row >> 4) & 1u); }
 
 template <bool EDGE>
 __device__ __forceinline__ void store_wave_tile(const f32x16 (&acc)[4][4], uint8_t* region, uint32_t lane,
@@ -152,7 +157,7 @@ __device__ __forceinline__ void store_wave_tile(const f32x16 (&acc)[4][4], uint8
                 u32x2 p;
                 p[0] = relu_pack2(acc[i][j][4 * q + 0], acc[i][j][4 * q + 1]);
                 p[1] = relu_pack2(acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]);
-                *reinterpret_cast<u32x2*>(region + tile_off(row, 4u * j + q) + 8u * half) = p;
+                *reinterpret_cast<u32x2*>(region + tile_off(row, 4u * j + q) + 8u * half_slot(row, half)) = p;
             }
         }
     }
@@ -162,17 +167,20 @@ __device__ __forceinline__ void store_wave_tile(const f32x16 (&acc)[4][4], uint8
 #pragma unroll 8
         for (uint32_t k = 0; k < 32; ++k) {
             const uint32_t row = 4u * k + (lane >> 4);
-            const u32x4 v = *reinterpret_cast<const u32x4*>(region + tile_off(row, ch));
+            u32x4 v = *reinterpret_cast<const u32x4*>(region + tile_off(row, ch));
+            if ((row >> 4) & 1u) v = u32x4{v[2], v[3], v[0], v[1]};
             const int64_t m = row0 + row;
             const int64_t n = col0 + 8 * ch;
             uint16_t* dst = C + m * ldc + n;
             if (EDGE && (m < row_min || m >= M)) continue;
             if (!EDGE || n + 8 <= N) {
+                // C is written once and never read back here: nontemporal
+                // stores keep it from displacing the A and B panels in L2.
                 if (vec_c == 8) {
-                    *reinterpret_cast<u32x4*>(dst) = v;
+                    __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(dst));
                 } else {
-                    *reinterpret_cast<u32x2*>(dst) = u32x2{v[0], v[1]};
-                    *reinterpret_cast<u32x2*>(dst + 4) = u32x2{v[2], v[3]};
+                    __builtin_nontemporal_store(u32x2{v[0], v[1]}, reinterpret_cast<u32x2*>(dst));
+                    __builtin_nontemporal_store(u32x2{v[2], v[3]}, reinterpret_cast<u32x2*>(dst + 4));
                 }
             } else {
 #pragma unroll
@@ -185,7 +193,9 @@ __device__ __forceinline__ void store_wave_tile(const f32x16 (&acc)[4][4], uint8
         for (uint32_t k = 0; k < 256; ++k) {
             const uint32_t row = k >> 1;
             const uint32_t col = 64u * (k & 1u) + lane;
-            const uint16_t h = *reinterpret_cast<const uint16_t*>(region + tile_off(row, col >> 3) + 2u * (col & 7u));
+            const uint32_t e = col & 7u;
+            const uint16_t h = *reinterpret_cast<const uint16_t*>(region + tile_off(row, col >> 3) +
+                                                                  8u * half_slot(row, e >> 2) + 2u * (e & 3u));
             const int64_t m = row0 + row;
             const int64_t n = col0 + col;
             if (EDGE && (m < row_min || m >= M || n >= N)) continue;

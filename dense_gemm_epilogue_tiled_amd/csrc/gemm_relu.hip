@@ -269,11 +269,13 @@ int launch_pack(const Pack& pk, int64_t M, int64_t N, int64_t K, const uint16_t*
     const Job none{nullptr, nullptr, 0, 8, 0, 0, 0};
     const Job ja = pk.a ? Job{A, reinterpret_cast<uint16_t*>(ws), lda, pk.lda_p, M, K, M} : none;
     const Job jb = pk.b ? Job{B, reinterpret_cast<uint16_t*>(ws + pk.off_b), ldb, pk.ldb_p, K, N, pk.kp} : none;
-    // About four 16-byte groups per thread, at most 2048 workgroups per job.
+    // UNROLL 16-byte groups per thread, at most 8192 workgroups per job
+    // (then a grid-stride loop).
     auto blocks = [](const Job& j) -> int64_t {
+        constexpr int64_t per_block = (int64_t)gr::pack::THREADS * gr::pack::UNROLL;
         const int64_t groups = j.rows_d * (j.ldd / 8);
-        const int64_t b = (groups + 4 * gr::pack::THREADS - 1) / (4 * gr::pack::THREADS);
-        return b < 2048 ? b : 2048;
+        const int64_t b = (groups + per_block - 1) / per_block;
+        return b < 8192 ? b : 8192;
     };
     const int64_t ba = blocks(ja), bb = blocks(jb);
     if (ba + bb == 0) return GR_OK;

@@ -12,8 +12,12 @@
 //
 // One launch packs up to two operands: workgroups [0, blocks_first) serve the
 // first job, the rest the second.  Every thread writes 16-byte groups of the
-// destination (8 fp16), each built from element loads of the source, so any
-// source alignment and pitch works; destination rows and pitch are 16-byte
+// destination (8 fp16), UNROLL of them at a time (all loads first, then the
+// stores), each read with 2-byte loads so that any source alignment and pitch
+// works; the eight loads of a wave together cover 1 KiB of contiguous source.
+// Only groups at a row's end test each element against the row length.
+// (Reading each group as the aligned 16-byte blocks that hold it and shifting
+// it into place was measured slower.)  Destination rows and pitch are 16-byte
 // aligned.
 #pragma once
 
@@ -37,21 +41,30 @@ struct Job {
     int64_t rows_d;  // destination rows (>= rows)
 };
 
-__device__ __forceinline__ void pack_group(const Job& j, int64_t g) {
+constexpr int UNROLL = 2;
+
+// Value of destination group g (8 fp16) and its element offset in dst.
+__device__ __forceinline__ u32x4 group_value(const Job& j, int64_t g, int64_t& off) {
     const int64_t gpr = j.ldd / 8;  // 16-byte groups per destination row
     const int64_t r = g / gpr;
     const int64_t c0 = (g - r * gpr) * 8;
+    off = r * j.ldd + c0;
     uint32_t h[8] = {0u, 0u, 0u, 0u, 0u, 0u, 0u, 0u};
     if (r < j.rows) {
-        const uint16_t* s = j.src + r * j.lds;
+        const uint16_t* s = j.src + r * j.lds + c0;
+        if (c0 + 8 <= j.cols) {
 #pragma unroll
-        for (int e = 0; e < 8; ++e)
-            if (c0 + e < j.cols) h[e] = s[c0 + e];
+            for (int e = 0; e < 8; ++e) h[e] = s[e];
+        } else {
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+                if (c0 + e < j.cols) h[e] = s[e];
+        }
     }
     u32x4 v;
 #pragma unroll
     for (int d = 0; d < 4; ++d) v[d] = h[2 * d] | (h[2 * d + 1] << 16);
-    *reinterpret_cast<u32x4*>(j.dst + r * j.ldd + c0) = v;
+    return v;
 }
 
 // Grid: blocks_first workgroups stride over the first job's groups, the
@@ -62,7 +75,20 @@ __global__ __launch_bounds__(THREADS) void pack_kernel(Job first, Job second, ui
     const int64_t blk = is_first ? blockIdx.x : blockIdx.x - blocks_first;
     const int64_t nblk = is_first ? blocks_first : gridDim.x - blocks_first;
     const int64_t groups = j.rows_d * (j.ldd / 8);
-    for (int64_t g = blk * THREADS + threadIdx.x; g < groups; g += nblk * THREADS) pack_group(j, g);
+    for (int64_t g0 = blk * THREADS * UNROLL + threadIdx.x; g0 < groups; g0 += nblk * THREADS * UNROLL) {
+        u32x4 v[UNROLL];
+        int64_t off[UNROLL];
+#pragma unroll
+        for (int u = 0; u < UNROLL; ++u) {
+            const int64_t g = g0 + (int64_t)u * THREADS;
+            if (g < groups) v[u] = group_value(j, g, off[u]);
+        }
+#pragma unroll
+        for (int u = 0; u < UNROLL; ++u) {
+            const int64_t g = g0 + (int64_t)u * THREADS;
+            if (g < groups) *reinterpret_cast<u32x4*>(j.dst + off[u]) = v[u];
+        }
+    }
 }
 
 }  // namespace pack

@@ -321,6 +321,29 @@ def test_packed_path_parity(M, N, K, lda, ldb, ldc, bits):
         assert plan["packed"] == bits
 
 
+@pytest.mark.parametrize("offs", [(1, 0, 0), (0, 3, 0), (3, 5, 7), (7, 7, 1)])
+def test_packed_path_unaligned_base_pointers(offs):
+    """Operands starting at any element offset: the copy reads each group from
+    the aligned 16-byte blocks that hold it and shifts it into place."""
+    import torch as t
+    M, N, K = 320, 296, 100
+    A, B = synth.random_operands(M, N, K, seed=sum(offs) + 50)
+    Ap = np.concatenate([np.zeros(offs[0], np.uint16), A.ravel(), np.zeros(8, np.uint16)])
+    Bp = np.concatenate([np.zeros(offs[1], np.uint16), B.ravel(), np.zeros(8, np.uint16)])
+    args = (M, N, K, 0x100000 + 2 * offs[0], K, 0x200000000000 + 2 * offs[1], N, 0x400000000000 + 2 * offs[2], N)
+    st, size = gr.gemm_relu_f16_workspace_size(*args)
+    assert st == gr.GR_OK and size > 0
+    ws = t.empty(size, dtype=t.uint8, device="cuda")
+    dC = full_dev((M * N + offs[2] + 8,), SENTINEL)
+    assert call_ws(M, N, K, to_dev(Ap), K, to_dev(Bp), N, dC, N, ws, size, path=gr.GR_PATH_TILE_PACKED,
+                   offsets=offs) == gr.GR_OK
+    Cflat = from_dev(dC)
+    C = Cflat[offs[2]:offs[2] + M * N].reshape(M, N)
+    assert_parity(C, oracle.gemm_relu_full(A, B), "packed offsets %s" % (offs,))
+    assert np.all(Cflat[:offs[2]] == SENTINEL)
+    assert np.all(Cflat[offs[2] + M * N:] == SENTINEL)
+
+
 def test_packed_path_reuses_a_dirty_workspace():
     """Two calls in a row on one workspace, the second smaller with other
     pitches: stale copies from the first never leak into the second."""
