@@ -112,63 +112,76 @@ __device__ __forceinline__ void store4(uint16_t* crow, bool row_owned, int64_t n
 
 }  // namespace edge
 
-// Write-back of one wave's 128 x 128 tile of C through LDS.
+// Write-back of one wave's tile of C (FM x FN blocks of 32 x 32) through LDS.
 //
 // The MFMA accumulators hold C^T blocks: a lane owns 4 consecutive columns of
 // one row, and one store instruction of the whole wave would touch 32 rows.
-// Instead the wave first writes its ReLU'd fp16 tile to LDS (row-major, 256
-// bytes per row; the 16-byte chunk c of row r sits at slot c XOR (r % 16),
-// with its two 8-byte halves swapped when (r / 16) is odd, so that both the
-// 8-byte writes of 32 rows and the read-back below are free of bank
-// conflicts), then reads it back so that consecutive lanes hold consecutive
-// columns of C:
-//   vec_c == 8: 16-byte chunks, 16 lanes per 256-byte row segment;
+// Instead the wave first writes its ReLU'd fp16 tile to LDS (row-major,
+// 64*FN bytes per row; the 16-byte chunk c of row r sits at slot c XOR (r mod
+// CHUNKS), CHUNKS = 4*FN chunks per row, with its two 8-byte halves swapped
+// when (r / CHUNKS) is odd, so that the 8-byte writes of 32 rows and the
+// read-back below avoid bank conflicts), then reads it back so that
+// consecutive lanes hold consecutive columns of C:
+//   vec_c == 8: 16-byte chunks, CHUNKS lanes per row segment;
 //   vec_c == 4: the same chunks stored as two 8-byte halves;
 //   vec_c == 1: one element per lane, 64 consecutive columns per store.
 // Every store instruction then covers whole row segments of C.  The caller's
 // LDS must be free: the routine starts with a workgroup barrier (all waves
-// call it), and the wave's 32 KiB region is its own.
+// call it), and the wave's region (32*FM x 32*FN fp16) is its own.
 // EDGE: only rows in [row_min, M) and columns < N are stored.
 namespace epi {
 
-constexpr int WAVE_TILE = 128;
-constexpr uint32_t REGION_BYTES = WAVE_TILE * WAVE_TILE * 2;  // 32 KiB per wave
+template <int FM, int FN>
+struct WaveTile {
+    static constexpr int ROWS = 32 * FM;
+    static constexpr int COLS = 32 * FN;
+    static constexpr uint32_t ROW_BYTES = 2 * COLS;
+    static constexpr uint32_t CHUNKS = COLS / 8;  // 16-byte chunks per row
+    static constexpr uint32_t REGION_BYTES = ROWS * ROW_BYTES;
+    static constexpr uint32_t SHIFT = CHUNKS == 16 ? 4 : (CHUNKS == 8 ? 3 : 2);
+    static_assert((1u << SHIFT) == CHUNKS, "CHUNKS is 4, 8 or 16");
 
-__device__ __forceinline__ uint32_t tile_off(uint32_t row, uint32_t chunk) {
-    return row * 256u + ((chunk ^ (row & 15u)) << 4);
-}
+    static __device__ __forceinline__ uint32_t off(uint32_t row, uint32_t chunk) {
+        return row * ROW_BYTES + ((chunk ^ (row & (CHUNKS - 1))) << 4);
+    }
+    // Which 8-byte half of its slot the half `h` of a chunk of row `row` uses.
+    static __device__ __forceinline__ uint32_t half_slot(uint32_t row, uint32_t h) {
+        return h ^ ((row >> SHIFT) & 1u);
+    }
+};
 
-// Which 8-byte half of its slot the half `h` of a chunk of row `row` uses.
-__device__ __forceinline__ uint32_t half_slot(uint32_t row, uint32_t h) { return h ^ ((row >> 4) & 1u); }
+constexpr uint32_t REGION_BYTES = WaveTile<4, 4>::REGION_BYTES;  // 32 KiB for a 128 x 128 wave tile
 
-template <bool EDGE>
-__device__ __forceinline__ void store_wave_tile(const f32x16 (&acc)[4][4], uint8_t* region, uint32_t lane,
+template <bool EDGE, int FM, int FN>
+__device__ __forceinline__ void store_wave_tile(const f32x16 (&acc)[FM][FN], uint8_t* region, uint32_t lane,
                                                 uint16_t* __restrict__ C, int64_t ldc, int64_t row0, int64_t col0,
                                                 int64_t row_min, int64_t M, int64_t N, int vec_c) {
+    using T = WaveTile<FM, FN>;
     __syncthreads();
     const uint32_t r_lane = lane & 31u, half = lane >> 5;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < FM; ++i) {
         const uint32_t row = 32u * i + r_lane;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
+        for (int j = 0; j < FN; ++j) {
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
                 u32x2 p;
                 p[0] = relu_pack2(acc[i][j][4 * q + 0], acc[i][j][4 * q + 1]);
                 p[1] = relu_pack2(acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]);
-                *reinterpret_cast<u32x2*>(region + tile_off(row, 4u * j + q) + 8u * half_slot(row, half)) = p;
+                *reinterpret_cast<u32x2*>(region + T::off(row, 4u * j + q) + 8u * T::half_slot(row, half)) = p;
             }
         }
     }
     __syncthreads();
     if (vec_c >= 4) {
-        const uint32_t ch = lane & 15u;
+        constexpr uint32_t ROWS_PER = 64u / T::CHUNKS;  // rows per wave instruction
+        const uint32_t ch = lane & (T::CHUNKS - 1);
 #pragma unroll 8
-        for (uint32_t k = 0; k < 32; ++k) {
-            const uint32_t row = 4u * k + (lane >> 4);
-            u32x4 v = *reinterpret_cast<const u32x4*>(region + tile_off(row, ch));
-            if ((row >> 4) & 1u) v = u32x4{v[2], v[3], v[0], v[1]};
+        for (uint32_t k = 0; k < T::ROWS / ROWS_PER; ++k) {
+            const uint32_t row = ROWS_PER * k + (lane >> T::SHIFT);
+            u32x4 v = *reinterpret_cast<const u32x4*>(region + T::off(row, ch));
+            if ((row >> T::SHIFT) & 1u) v = u32x4{v[2], v[3], v[0], v[1]};
             const int64_t m = row0 + row;
             const int64_t n = col0 + 8 * ch;
             uint16_t* dst = C + m * ldc + n;
@@ -190,12 +203,13 @@ __device__ __forceinline__ void store_wave_tile(const f32x16 (&acc)[4][4], uint8
         }
     } else {
 #pragma unroll 8
-        for (uint32_t k = 0; k < 256; ++k) {
-            const uint32_t row = k >> 1;
-            const uint32_t col = 64u * (k & 1u) + lane;
+        for (uint32_t k = 0; k < (uint32_t)(T::ROWS * T::COLS / 64); ++k) {
+            const uint32_t idx = 64u * k + lane;
+            const uint32_t row = idx / T::COLS;
+            const uint32_t col = idx % T::COLS;
             const uint32_t e = col & 7u;
-            const uint16_t h = *reinterpret_cast<const uint16_t*>(region + tile_off(row, col >> 3) +
-                                                                  8u * half_slot(row, e >> 2) + 2u * (e & 3u));
+            const uint16_t h = *reinterpret_cast<const uint16_t*>(region + T::off(row, col >> 3) +
+                                                                  8u * T::half_slot(row, e >> 2) + 2u * (e & 3u));
             const int64_t m = row0 + row;
             const int64_t n = col0 + col;
             if (EDGE && (m < row_min || m >= M || n >= N)) continue;

@@ -16,6 +16,7 @@
 #include "pack_kernel.hpp"
 #include "smallm_kernel.hpp"
 #include "tile2_kernel.hpp"
+#include "tile128_kernel.hpp"
 #include "tile3_kernel.hpp"
 #include "tile_kernel.hpp"
 
@@ -105,19 +106,27 @@ bool smallm_ok(int64_t M, int64_t N, int64_t K, uintptr_t A, int64_t lda, uintpt
 // Conditions of the pipelined direct-to-LDS kernels: 16-byte aligned rows of
 // A and B (every copy is a whole 16-byte chunk), K a positive multiple of the
 // 32-deep strip, pitches small enough for 32-bit per-lane copy offsets, and at
-// least one whole tile of rows (a partial last tile row is moved up to end at
+// least one whole 128-row tile (a partial last tile row is moved up to end at
 // row M).  Any N and any C layout.
 bool tile_fast_ok(int64_t M, int64_t N, int64_t K, uintptr_t A, int64_t lda, uintptr_t B, int64_t ldb) {
     using namespace gr::tile2;
-    return M >= BM && N >= 1 && K % BK == 0 && K > 0 && vec_width(A, lda) == 8 && vec_width(B, ldb) == 8 &&
-           lda <= MAX_LDA && ldb <= MAX_LDB;
+    return M >= gr::tile128::BM && N >= 1 && K % BK == 0 && K > 0 && vec_width(A, lda) == 8 &&
+           vec_width(B, ldb) == 8 && lda <= MAX_LDA && ldb <= MAX_LDB;
 }
 
-// Whole tiles: the edge-free variant of those kernels.
-bool tile_whole(int64_t M, int64_t N) {
+// 256 x 256 tiles unless they would fill less than half of one wave of
+// workgroups over the 256 CUs (or M < 256): then 128 x 128 tiles, which give
+// four times as many workgroups.
+constexpr int64_t kSmallTileMaxLargeTiles = 128;
+bool use_large_tiles(int64_t M, int64_t N) {
     using namespace gr::tile2;
-    return M % BM == 0 && N % BN == 0;
+    if (M < BM) return false;
+    const int64_t tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
+    return tiles > kSmallTileMaxLargeTiles;
 }
+
+// Whole tiles of size bm x bn: the edge-free variant of those kernels.
+bool tile_whole(int64_t M, int64_t N, int64_t bm, int64_t bn) { return M % bm == 0 && N % bn == 0; }
 
 int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
 
@@ -135,7 +144,7 @@ struct Pack {
 
 bool pack_layout(int64_t M, int64_t N, int64_t K, uintptr_t A, int64_t lda, uintptr_t B, int64_t ldb, Pack* pk) {
     using namespace gr::tile2;
-    if (M < BM || N < 1 || K < 1) return false;
+    if (M < gr::tile128::BM || N < 1 || K < 1) return false;
     Pack q;
     q.kp = K % BK == 0 ? K : round_up(K, 2 * BK);
     q.a = vec_width(A, lda) != 8 || lda > MAX_LDA || q.kp != K;
@@ -157,13 +166,15 @@ void fill_plan(int path, int64_t M, int64_t N, int64_t K, uintptr_t A, int64_t l
     std::memset(p, 0, sizeof(*p));
     p->path = path;
     if (path == GR_PATH_TILE || path == GR_PATH_TILE_PACKED) {
-        using namespace gr::tile2;
-        p->block_m = BM;
-        p->block_n = BN;
-        p->block_k = BK;
-        p->stages = STAGES;
-        p->threads = THREADS;
-        p->grid = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
+        const bool large = use_large_tiles(M, N);
+        const int64_t bm = large ? gr::tile2::BM : gr::tile128::BM;
+        const int64_t bn = large ? gr::tile2::BN : gr::tile128::BN;
+        p->block_m = (int32_t)bm;
+        p->block_n = (int32_t)bn;
+        p->block_k = gr::tile2::BK;
+        p->stages = large ? gr::tile2::STAGES : gr::tile128::STAGES;
+        p->threads = gr::tile2::THREADS;
+        p->grid = ((M + bm - 1) / bm) * ((N + bn - 1) / bn);
         p->vec_a = 8;
         p->vec_b = 8;
         p->vec_c = vec_width_c(C, ldc);
@@ -296,11 +307,20 @@ int run(const gr_plan_t& p, int64_t M, int64_t N, int64_t K, const uint16_t* A, 
             return run(q, M, N, pk.kp, Ap, pk.lda_p, Bp, pk.ldb_p, C, ldc, pk, ws, stream);
         }
         case GR_PATH_TILE: {
-            const bool whole = tile_whole(M, N);
-            const uint32_t tiles_m = (uint32_t)((M + gr::tile2::BM - 1) / gr::tile2::BM);
-            const uint32_t tiles_n = (uint32_t)((N + gr::tile2::BN - 1) / gr::tile2::BN);
+            const int64_t bm = p.block_m, bn = p.block_n;
+            const bool whole = tile_whole(M, N, bm, bn);
+            const uint32_t tiles_m = (uint32_t)((M + bm - 1) / bm);
+            const uint32_t tiles_n = (uint32_t)((N + bn - 1) / bn);
             const uint32_t gm = (uint32_t)p.group_m;
             const int vc = p.vec_c;
+            if (bm == gr::tile128::BM) {
+                using namespace gr::tile128;
+                if (whole)
+                    return launch(gemm_relu_tile128_kernel<false>, p.grid, THREADS, stream, A, B, C, M, N, K, lda,
+                                  ldb, ldc, tiles_m, tiles_n, gm, vc);
+                return launch(gemm_relu_tile128_kernel<true>, p.grid, THREADS, stream, A, B, C, M, N, K, lda, ldb,
+                              ldc, tiles_m, tiles_n, gm, vc);
+            }
             if (K % gr::tile3::BKA == 0) {
                 using namespace gr::tile3;
                 if (whole)

@@ -151,8 +151,8 @@ def test_plan_partial_tiles_take_the_pipelined_kernel():
     st, p = plan(4099, 3071, 2048, lda=2048, ldb=3072, ldc=3071)
     assert st == gr.GR_OK and p["path"] == gr.GR_PATH_TILE and p["grid"] == 17 * 12 and p["vec_c"] == 1
     assert plan(256, 1, 32, ldb=8)[1]["path"] == gr.GR_PATH_TILE
-    # fewer than 256 rows, K % 32 != 0, or rows not 16-byte aligned: guarded kernel
-    assert plan(255, 512, 512)[1]["path"] == gr.GR_PATH_TILE_EDGE
+    # fewer than 128 rows, K % 32 != 0, or rows not 16-byte aligned: guarded kernel
+    assert plan(127, 512, 512)[1]["path"] == gr.GR_PATH_TILE_EDGE
     assert plan(512, 512, 48)[1]["path"] == gr.GR_PATH_TILE_EDGE
     assert plan(512, 500, 512)[1]["path"] == gr.GR_PATH_TILE_EDGE
     assert plan(512, 512, 512, b=BASE_B + 8)[1]["path"] == gr.GR_PATH_TILE_EDGE
@@ -206,7 +206,7 @@ def test_workspace_size_and_packed_plan():
 def test_workspace_not_used_where_it_cannot_help():
     assert ws_size(4096, 4096, 4096) == (gr.GR_OK, 0)       # pipelined in place
     assert ws_size(8, 16384, 8192) == (gr.GR_OK, 0)         # small-M kernel
-    assert ws_size(200, 4096, 4100) == (gr.GR_OK, 0)        # fewer than 256 rows
+    assert ws_size(100, 4096, 4100) == (gr.GR_OK, 0)        # fewer than 128 rows
     assert ws_size(0, 4096, 4096) == (gr.GR_OK, 0)          # empty
     assert ws_size(512, 512, 0, lda=1) == (gr.GR_OK, 0)     # K == 0
     assert plan_ws(4096, 4096, 4096, 1 << 30)[1]["path"] == gr.GR_PATH_TILE
@@ -230,6 +230,17 @@ def test_workspace_argument_checks():
     assert gr.lib().gemm_relu_f16_workspace_size(*args, None) == gr.GR_ERR_INVALID_ARG
     assert gr.lib().gemm_relu_f16_workspace_size(-1, 8, 8, BASE_A, 8, BASE_B, 8, BASE_C, 8,
                                                  ctypes.byref(n)) == gr.GR_ERR_INVALID_DIM
+
+
+def test_plan_tile_size_choice():
+    # fewer than half a wave of 256 x 256 tiles (or M < 256): 128 x 128 tiles
+    for (M, N), (bm, grid) in {(1024, 1024): (128, 64), (2048, 2048): (128, 256), (128, 4096): (128, 32),
+                               (200, 304): (128, 6), (4096, 4096): (256, 256), (2816, 2816): (128, 484),
+                               (4099, 3071): (256, 204), (2048, 4096): (128, 512),
+                               (2304, 4096): (256, 144)}.items():
+        st, p = plan(M, N, 512, ldb=rup(N, 8), ldc=rup(N, 8))
+        assert st == gr.GR_OK and p["path"] == gr.GR_PATH_TILE, (M, N, p)
+        assert (p["block_m"], p["block_n"], p["grid"]) == (bm, bm, grid), (M, N, p)
 
 
 def test_plan_empty_and_k_zero():
@@ -259,7 +270,7 @@ def test_calls_validate_before_touching_the_device():
     # fewer than 256 rows, misaligned B rows
     assert gr.gemm_relu_f16_forced(300, 256, 48, BASE_A, 48, BASE_B, 256, BASE_C, 256, None,
                                    gr.GR_PATH_TILE) == gr.GR_ERR_INVALID_PATH
-    assert gr.gemm_relu_f16_forced(255, 256, 64, BASE_A, 64, BASE_B, 256, BASE_C, 256, None,
+    assert gr.gemm_relu_f16_forced(127, 256, 64, BASE_A, 64, BASE_B, 256, BASE_C, 256, None,
                                    gr.GR_PATH_TILE) == gr.GR_ERR_INVALID_PATH
     assert gr.gemm_relu_f16_forced(300, 250, 64, BASE_A, 64, BASE_B, 250, BASE_C, 256, None,
                                    gr.GR_PATH_TILE) == gr.GR_ERR_INVALID_PATH

@@ -214,32 +214,47 @@ def test_deterministic_bitwise():
     assert np.array_equal(C1, C2)
 
 
-def test_tile_and_edge_paths_bitwise_equal():
-    """The guarded variant runs the same MFMA sequence on whole tiles."""
-    M, N, K = 512, 768, 256
+@pytest.mark.parametrize("M,N,K", [(512, 768, 256), (4096, 2304, 256)])
+def test_tile_and_edge_paths_bitwise_equal(M, N, K):
+    """The guarded variant runs the same MFMA sequence on whole tiles (small
+    tiles at 512 x 768, large ones at 4096 x 2304)."""
     A, B = synth.random_operands(M, N, K, seed=63)
     C1 = run_full(A, B, M, N, K, path=gr.GR_PATH_TILE)
     C2 = run_full(A, B, M, N, K, path=gr.GR_PATH_TILE_EDGE)
     assert np.array_equal(C1, C2)
 
 
+@pytest.mark.parametrize("M,N", [(512, 256), (2304, 4096)])
 @pytest.mark.parametrize("K", [32, 64, 96, 128, 160, 192, 224, 256, 288, 320, 384, 448, 512, 1056, 1088])
-def test_tile_pipeline_every_strip_count(K):
-    """Whole tiles through the pipelined kernel, for every K-loop length up to
-    the steady state plus odd and even tails, bitwise against the guarded
-    kernel (both accumulate the same 16-deep MFMA steps in the same order)."""
-    M, N = 512, 256
+def test_tile_pipeline_every_strip_count(M, N, K):
+    """Whole tiles through the pipelined kernels (128 x 128 tiles at 512 x 256,
+    256 x 256 tiles at 2304 x 4096: the 32- and 64-deep variants), for every
+    K-loop length up to the steady state plus odd and even tails, bitwise
+    against the guarded kernel (all accumulate the same 16-deep MFMA steps in
+    the same order).  The large shape is checked against the oracle on edge
+    rows and columns, the small one in full."""
+    st, plan = gr.gemm_relu_f16_plan(M, N, K, 0x100000, K, 0x200000000000, N, 0x400000000000, N)
+    assert plan["block_m"] == (128 if M == 512 else 256), plan
     A, B = synth.random_operands(M, N, K, seed=K)
     C1 = run_full(A, B, M, N, K, path=gr.GR_PATH_TILE)
     C2 = run_full(A, B, M, N, K, path=gr.GR_PATH_TILE_EDGE)
-    assert_parity(window(C1, M, N, N), oracle.gemm_relu_full(A, B), "tile K=%d" % K)
+    C = window(C1, M, N, N)
+    if M == 512:
+        assert_parity(C, oracle.gemm_relu_full(A, B), "tile K=%d" % K)
+    else:
+        rows = edge_indices(M, plan["block_m"]) + [1000, 1024]
+        cols = edge_indices(N, plan["block_n"]) + [2000, 2048]
+        assert_parity(C[rows, :], oracle.gemm_relu_rows(A, B, rows), "tile K=%d rows" % K)
+        assert_parity(C[:, cols].T, oracle.gemm_relu_cols(A, B, cols), "tile K=%d cols" % K)
     assert np.array_equal(C1, C2)
 
 
 # ---- the pipelined kernels on partial tiles (16-byte rows, K % 32 == 0) -------
 
 PARTIAL_TILE_CASES = [
+    (128, 136, 32, 32, 136, 136),          # 128 x 128 tiles: one tile row, one partial tile column
     (257, 264, 64, 64, 264, 264),          # one row past a tile; N a multiple of 8
+    (2400, 4000, 96, 96, 4000, 4001),      # 256 x 256 tiles, K % 64 == 32 (32-deep kernel), odd ldc
     (300, 250, 96, 96, 256, 251),          # K % 64 == 32 (32-deep kernel); odd ldc: 2-byte stores
     (511, 1, 128, 136, 8, 1),              # a single column; padded A rows
     (1000, 700, 320, 320, 704, 700),       # 4 x 3 tiles, last tile row shifted by 24 rows
@@ -257,6 +272,7 @@ def test_pipelined_kernel_partial_tiles(M, N, K, lda, ldb, ldc):
     (same MFMA steps in the same k order)."""
     st, plan = gr.gemm_relu_f16_plan(M, N, K, 0x100000, lda, 0x200000000000, ldb, 0x400000000000, ldc)
     assert st == gr.GR_OK and plan["path"] == gr.GR_PATH_TILE, plan
+    log("partial %dx%dx%d tile %d" % (M, N, K, plan["block_m"]))
     A, B = synth.random_operands(M, N, K, seed=M + 3 * N + 7 * K, lda=lda, ldb=ldb)
     extra_rows = 2
     C1 = run_full(A, B, M, N, K, lda=lda, ldb=ldb, ldc=ldc, c_rows=M + extra_rows)
