@@ -31,9 +31,11 @@ GR_PATH_TILE = 1
 GR_PATH_TILE_EDGE = 2
 GR_PATH_SMALL_M = 3
 GR_PATH_TILE_PACKED = 4
+GR_PATH_SMALL_M_SPLIT = 5
 
 PATH_NAMES = {GR_PATH_NONE: "none", GR_PATH_TILE: "tile", GR_PATH_TILE_EDGE: "tile_edge",
-              GR_PATH_SMALL_M: "small_m", GR_PATH_TILE_PACKED: "tile_packed"}
+              GR_PATH_SMALL_M: "small_m", GR_PATH_TILE_PACKED: "tile_packed",
+              GR_PATH_SMALL_M_SPLIT: "small_m_split"}
 
 
 class gr_plan_t(ctypes.Structure):
@@ -51,6 +53,7 @@ class gr_plan_t(ctypes.Structure):
         ("group_m", ctypes.c_int32),
         ("packed", ctypes.c_int32),
         ("workspace", ctypes.c_int64),
+        ("split_k", ctypes.c_int32),
     ]
 
 

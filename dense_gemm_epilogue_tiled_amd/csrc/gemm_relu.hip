@@ -103,6 +103,37 @@ bool smallm_ok(int64_t M, int64_t N, int64_t K, uintptr_t A, int64_t lda, uintpt
     return M >= 1 && M <= kSmallMThreshold && A % 16 == 0 && lda % 8 == 0 && B % 8 == 0 && ldb % 4 == 0;
 }
 
+// Split-K layout of the small-M path: S splits of k_per_split (a multiple of
+// 32, at least two 32-deep steps) over ceil(N / 256) column blocks, about 256
+// workgroups in all, and the fp32 partial sums S x M x N in the workspace.
+// Needs 16-byte rows of B.
+struct SmallMSplit {
+    int64_t splits = 0, k_per_split = 0, n_blocks = 0, bytes = 0;
+};
+constexpr int64_t kSmallMMaxSplits = 64;
+
+// The split pays only where the single-pass kernel (one workgroup per
+// 64-column strip) leaves CUs idle: measured at N = 16384 (256 strips) the
+// split's first pass is 4% faster, and its second pass costs more than that.
+bool smallm_split_pays(int64_t N) { return (N + gr::smallm::NB - 1) / gr::smallm::NB < 256; }
+
+bool smallm_split_layout(int64_t M, int64_t N, int64_t K, uintptr_t A, int64_t lda, uintptr_t B, int64_t ldb,
+                         SmallMSplit* sp) {
+    using namespace gr::smallm;
+    if (K < 1 || N < 1 || !smallm_ok(M, N, K, A, lda, B, ldb) || B % 16 != 0 || ldb % 8 != 0) return false;
+    SmallMSplit q;
+    q.n_blocks = (N + SPLIT_NB - 1) / SPLIT_NB;
+    int64_t S = 256 / q.n_blocks;
+    S = S < 1 ? 1 : (S > kSmallMMaxSplits ? kSmallMMaxSplits : S);
+    const int64_t ksteps = (K + KSTEP - 1) / KSTEP;
+    if (S > ksteps / 2) S = ksteps / 2 > 0 ? ksteps / 2 : 1;
+    q.k_per_split = (ksteps + S - 1) / S * KSTEP;
+    q.splits = (K + q.k_per_split - 1) / q.k_per_split;  // no empty split
+    q.bytes = (q.splits * M * N * 4 + kWorkspaceAlign - 1) / kWorkspaceAlign * kWorkspaceAlign;
+    *sp = q;
+    return true;
+}
+
 // Conditions of the pipelined direct-to-LDS kernels: 16-byte aligned rows of
 // A and B (every copy is a whole 16-byte chunk), K a positive multiple of the
 // 32-deep strip, pitches small enough for 32-bit per-lane copy offsets, and at
@@ -162,7 +193,7 @@ bool pack_layout(int64_t M, int64_t N, int64_t K, uintptr_t A, int64_t lda, uint
 }
 
 void fill_plan(int path, int64_t M, int64_t N, int64_t K, uintptr_t A, int64_t lda, uintptr_t B,
-               int64_t ldb, uintptr_t C, int64_t ldc, const Pack& pk, gr_plan_t* p) {
+               int64_t ldb, uintptr_t C, int64_t ldc, const Pack& pk, const SmallMSplit& sp, gr_plan_t* p) {
     std::memset(p, 0, sizeof(*p));
     p->path = path;
     if (path == GR_PATH_TILE || path == GR_PATH_TILE_PACKED) {
@@ -195,6 +226,20 @@ void fill_plan(int path, int64_t M, int64_t N, int64_t K, uintptr_t A, int64_t l
         p->vec_b = vec_width(B, ldb);
         p->vec_c = vec_width_c(C, ldc);
         p->group_m = kGroupM;
+    } else if (path == GR_PATH_SMALL_M_SPLIT) {
+        using namespace gr::smallm;
+        p->block_m = MAX_M;
+        p->block_n = SPLIT_NB;
+        p->block_k = KSTEP;
+        p->stages = SPLIT_U;
+        p->threads = SPLIT_THREADS;
+        p->grid = sp.n_blocks * sp.splits;
+        p->vec_a = 8;
+        p->vec_b = 8;
+        p->vec_c = 1;
+        p->group_m = 1;
+        p->workspace = sp.bytes;
+        p->split_k = (int32_t)sp.splits;
     } else if (path == GR_PATH_SMALL_M) {
         using namespace gr::smallm;
         p->block_m = MAX_M;
@@ -207,15 +252,21 @@ void fill_plan(int path, int64_t M, int64_t N, int64_t K, uintptr_t A, int64_t l
         p->vec_b = 4;
         p->vec_c = 1;
         p->group_m = 1;
+        p->split_k = 1;
     }
 }
 
 int choose_path(int64_t M, int64_t N, int64_t K, uintptr_t A, int64_t lda, uintptr_t B, int64_t ldb,
-                uintptr_t C, int64_t ldc, int64_t ws_bytes, Pack* pk) {
+                uintptr_t C, int64_t ldc, int64_t ws_bytes, Pack* pk, SmallMSplit* sp) {
     (void)C;
     (void)ldc;
     if (M == 0 || N == 0) return GR_PATH_NONE;
-    if (K > 0 && smallm_ok(M, N, K, A, lda, B, ldb)) return GR_PATH_SMALL_M;
+    if (K > 0 && smallm_ok(M, N, K, A, lda, B, ldb)) {
+        if (ws_bytes > 0 && smallm_split_pays(N) && smallm_split_layout(M, N, K, A, lda, B, ldb, sp) &&
+            sp->splits >= 2 && sp->bytes <= ws_bytes)
+            return GR_PATH_SMALL_M_SPLIT;
+        return GR_PATH_SMALL_M;
+    }
     if (tile_fast_ok(M, N, K, A, lda, B, ldb)) return GR_PATH_TILE;
     if (ws_bytes > 0 && pack_layout(M, N, K, A, lda, B, ldb, pk) && pk->bytes <= ws_bytes &&
         (double)M * (double)N * (double)K >= (double)kPackMinMacs)
@@ -294,9 +345,25 @@ int launch_pack(const Pack& pk, int64_t M, int64_t N, int64_t K, const uint16_t*
 }
 
 int run(const gr_plan_t& p, int64_t M, int64_t N, int64_t K, const uint16_t* A, int64_t lda, const uint16_t* B,
-        int64_t ldb, uint16_t* C, int64_t ldc, const Pack& pk, uint8_t* ws, hipStream_t stream) {
+        int64_t ldb, uint16_t* C, int64_t ldc, const Pack& pk, const SmallMSplit& sp, uint8_t* ws,
+        hipStream_t stream) {
     switch (p.path) {
         case GR_PATH_NONE: return GR_OK;
+        case GR_PATH_SMALL_M_SPLIT: {
+            using namespace gr::smallm;
+            float* part = reinterpret_cast<float*>(ws);
+            const bool whole = N % SPLIT_NB == 0 && K % KSTEP == 0;
+            const uint32_t nb = (uint32_t)sp.n_blocks;
+            int st = whole ? launch(gemm_relu_smallm_split_kernel<false>, p.grid, SPLIT_THREADS, stream, A, B, part,
+                                    M, N, K, lda, ldb, sp.k_per_split, nb)
+                           : launch(gemm_relu_smallm_split_kernel<true>, p.grid, SPLIT_THREADS, stream, A, B, part, M,
+                                    N, K, lda, ldb, sp.k_per_split, nb);
+            if (st != GR_OK) return st;
+            int64_t rblocks = (M * N + 255) / 256;
+            if (rblocks > 2048) rblocks = 2048;
+            return launch(gemm_relu_smallm_reduce_kernel, rblocks, 256, stream, (const float*)part, C, M, N, ldc,
+                          (int)sp.splits);
+        }
         case GR_PATH_TILE_PACKED: {
             const int st = launch_pack(pk, M, N, K, A, lda, B, ldb, ws, stream);
             if (st != GR_OK) return st;
@@ -304,7 +371,7 @@ int run(const gr_plan_t& p, int64_t M, int64_t N, int64_t K, const uint16_t* A, 
             q.path = GR_PATH_TILE;
             const uint16_t* Ap = pk.a ? reinterpret_cast<const uint16_t*>(ws) : A;
             const uint16_t* Bp = pk.b ? reinterpret_cast<const uint16_t*>(ws + pk.off_b) : B;
-            return run(q, M, N, pk.kp, Ap, pk.lda_p, Bp, pk.ldb_p, C, ldc, pk, ws, stream);
+            return run(q, M, N, pk.kp, Ap, pk.lda_p, Bp, pk.ldb_p, C, ldc, pk, sp, ws, stream);
         }
         case GR_PATH_TILE: {
             const int64_t bm = p.block_m, bn = p.block_n;
@@ -359,12 +426,13 @@ int run(const gr_plan_t& p, int64_t M, int64_t N, int64_t K, const uint16_t* A, 
 // ws_known: the workspace pointer is real and is checked (a plan made from
 // a size alone skips the pointer checks).
 int plan_call(int64_t M, int64_t N, int64_t K, uintptr_t a, int64_t lda, uintptr_t b, int64_t ldb, uintptr_t c,
-              int64_t ldc, uintptr_t ws, int64_t ws_bytes, bool ws_known, int forced, Pack* pk, gr_plan_t* p) {
+              int64_t ldc, uintptr_t ws, int64_t ws_bytes, bool ws_known, int forced, Pack* pk, SmallMSplit* sp,
+              gr_plan_t* p) {
     if (ws_bytes < 0) return GR_ERR_INVALID_ARG;
     int st = ws_known ? validate(M, N, K, a, lda, b, ldb, c, ldc, ws, ws_bytes)
                       : validate(M, N, K, a, lda, b, ldb, c, ldc);
     if (st != GR_OK) return st;
-    int path = choose_path(M, N, K, a, lda, b, ldb, c, ldc, ws_bytes, pk);
+    int path = choose_path(M, N, K, a, lda, b, ldb, c, ldc, ws_bytes, pk, sp);
     if (forced >= 0 && path != GR_PATH_NONE) {
         if (forced == GR_PATH_TILE) {
             if (!tile_fast_ok(M, N, K, a, lda, b, ldb)) return GR_ERR_INVALID_PATH;
@@ -372,32 +440,38 @@ int plan_call(int64_t M, int64_t N, int64_t K, uintptr_t a, int64_t lda, uintptr
             if (K == 0 || !smallm_ok(M, N, K, a, lda, b, ldb)) return GR_ERR_INVALID_PATH;
         } else if (forced == GR_PATH_TILE_PACKED) {
             if (!pack_layout(M, N, K, a, lda, b, ldb, pk) || pk->bytes > ws_bytes) return GR_ERR_INVALID_PATH;
+        } else if (forced == GR_PATH_SMALL_M_SPLIT) {
+            if (!smallm_split_layout(M, N, K, a, lda, b, ldb, sp) || sp->bytes > ws_bytes) return GR_ERR_INVALID_PATH;
         } else if (forced != GR_PATH_TILE_EDGE) {
             return GR_ERR_INVALID_PATH;
         }
         path = forced;
     }
-    fill_plan(path, M, N, K, a, lda, b, ldb, c, ldc, *pk, p);
+    fill_plan(path, M, N, K, a, lda, b, ldb, c, ldc, *pk, *sp, p);
     return GR_OK;
 }
 
 int entry(int64_t M, int64_t N, int64_t K, const uint16_t* A, int64_t lda, const uint16_t* B, int64_t ldb,
           uint16_t* C, int64_t ldc, void* ws, int64_t ws_bytes, void* stream, int forced) {
     Pack pk;
+    SmallMSplit sp;
     gr_plan_t p;
     int st = plan_call(M, N, K, (uintptr_t)A, lda, (uintptr_t)B, ldb, (uintptr_t)C, ldc, (uintptr_t)ws, ws_bytes,
-                       true, forced, &pk, &p);
+                       true, forced, &pk, &sp, &p);
     if (st != GR_OK) return st;
     if (p.path == GR_PATH_NONE) return GR_OK;
     st = check_device();
     if (st != GR_OK) return st;
-    return run(p, M, N, K, A, lda, B, ldb, C, ldc, pk, static_cast<uint8_t*>(ws), static_cast<hipStream_t>(stream));
+    return run(p, M, N, K, A, lda, B, ldb, C, ldc, pk, sp, static_cast<uint8_t*>(ws),
+               static_cast<hipStream_t>(stream));
 }
 
 bool known_path(int path) {
     return path == GR_PATH_TILE || path == GR_PATH_TILE_EDGE || path == GR_PATH_SMALL_M ||
-           path == GR_PATH_TILE_PACKED;
+           path == GR_PATH_TILE_PACKED || path == GR_PATH_SMALL_M_SPLIT;
 }
+
+bool needs_workspace(int path) { return path == GR_PATH_TILE_PACKED || path == GR_PATH_SMALL_M_SPLIT; }
 
 }  // namespace
 
@@ -410,7 +484,7 @@ int gemm_relu_f16(int64_t M, int64_t N, int64_t K, const uint16_t* A, int64_t ld
 
 int gemm_relu_f16_forced(int64_t M, int64_t N, int64_t K, const uint16_t* A, int64_t lda, const uint16_t* B,
                          int64_t ldb, uint16_t* C, int64_t ldc, void* stream, int path) {
-    if (!known_path(path) || path == GR_PATH_TILE_PACKED) return GR_ERR_INVALID_PATH;
+    if (!known_path(path) || needs_workspace(path)) return GR_ERR_INVALID_PATH;
     return entry(M, N, K, A, lda, B, ldb, C, ldc, nullptr, 0, stream, path);
 }
 
@@ -426,10 +500,15 @@ int gemm_relu_f16_workspace_size(int64_t M, int64_t N, int64_t K, const uint16_t
     int st = validate(M, N, K, a, lda, b, ldb, c, ldc);
     if (st != GR_OK) return st;
     *bytes = 0;
+    if (M == 0 || N == 0) return GR_OK;
     Pack pk;
-    if (M > 0 && N > 0 && !smallm_ok(M, N, K, a, lda, b, ldb) && !tile_fast_ok(M, N, K, a, lda, b, ldb) &&
-        pack_layout(M, N, K, a, lda, b, ldb, &pk))
+    SmallMSplit sp;
+    if (smallm_ok(M, N, K, a, lda, b, ldb)) {
+        if (smallm_split_pays(N) && smallm_split_layout(M, N, K, a, lda, b, ldb, &sp) && sp.splits >= 2)
+            *bytes = sp.bytes;
+    } else if (!tile_fast_ok(M, N, K, a, lda, b, ldb) && pack_layout(M, N, K, a, lda, b, ldb, &pk)) {
         *bytes = pk.bytes;
+    }
     return GR_OK;
 }
 
@@ -449,8 +528,9 @@ int gemm_relu_f16_plan_ws(int64_t M, int64_t N, int64_t K, const uint16_t* A, in
                           int64_t ldb, const uint16_t* C, int64_t ldc, int64_t workspace_bytes, gr_plan_t* out) {
     if (!out) return GR_ERR_INVALID_ARG;
     Pack pk;
+    SmallMSplit sp;
     return plan_call(M, N, K, (uintptr_t)A, lda, (uintptr_t)B, ldb, (uintptr_t)C, ldc, 0, workspace_bytes, false,
-                     -1, &pk, out);
+                     -1, &pk, &sp, out);
 }
 
 const char* gemm_relu_status_string(int status) {

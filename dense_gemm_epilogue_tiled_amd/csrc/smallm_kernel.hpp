@@ -181,5 +181,154 @@ __global__ __launch_bounds__(64 * W, 1) void gemm_relu_smallm_kernel(
     }
 }
 
+// ---- split-K variant (needs a workspace) -------------------------------------
+//
+// A 64-column strip over all of K reads each row of B as one 128-byte piece,
+// 32 KiB away from the next: measured on this part, that pattern streams at
+// about 5.5 TB/s, while blocks of 256 columns over a quarter of K (512-byte
+// pieces) reach about 6.2 TB/s.  With scratch memory the small-M product is
+// therefore split in K, the split-K of the TileLang tutorial's chapter on
+// performance forensics (work for idle CUs when M x N is small), here with a
+// second pass because ReLU must see the complete sum:
+//   pass 1: workgroup (cb, s) owns columns [256 cb, 256 cb + 256) and the K
+//           range of split s; its 4 waves are 2 column halves x 2 interleaved
+//           32-deep K phases; 16-byte nontemporal loads of B (8 columns per
+//           lane, an 8 x 8 block per step transposed in registers into 8
+//           operands of v_mfma_f32_16x16x32_f16); the two K phases are summed
+//           in LDS and the fp32 partial sums of rows m < M written to
+//           part[s][m][n].
+//   pass 2: every output sums its S partials in split order, then ReLU and
+//           the fp16 rounding, then the store.
+// Both passes are deterministic; the result differs from the single-pass
+// kernel only by fp32 summation order.
+constexpr int SPLIT_NB = 256;
+constexpr int SPLIT_THREADS = 256;
+constexpr int SPLIT_U = 2;  // 32-deep steps per load group
+
+// Eight consecutive fp16 of row k from column n; zero outside [0,kend) x [0,N).
+template <bool GUARD>
+__device__ __forceinline__ u32x4 load_b8(const uint16_t* B, int64_t ldb, int64_t k, int64_t n, int64_t kend,
+                                         int64_t N) {
+    if constexpr (!GUARD) {
+        return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(B + k * ldb + n));
+    } else {
+        u32x4 v = u32x4{0u, 0u, 0u, 0u};
+        if (k < kend) {
+            const uint16_t* p = B + k * ldb + n;
+            if (n + 8 <= N) {
+                v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+            } else {
+                uint32_t h[8] = {0u, 0u, 0u, 0u, 0u, 0u, 0u, 0u};
+#pragma unroll
+                for (int e = 0; e < 8; ++e)
+                    if (n + e < N) h[e] = p[e];
+#pragma unroll
+                for (int d = 0; d < 4; ++d) v[d] = h[2 * d] | (h[2 * d + 1] << 16);
+            }
+        }
+        return v;
+    }
+}
+
+template <bool GUARD>
+__global__ __launch_bounds__(SPLIT_THREADS, 1) void gemm_relu_smallm_split_kernel(
+    const uint16_t* __restrict__ A, const uint16_t* __restrict__ B, float* __restrict__ part, int64_t M, int64_t N,
+    int64_t K, int64_t lda, int64_t ldb, int64_t k_per_split, uint32_t n_blocks) {
+    __shared__ __attribute__((aligned(16))) float red[2][MAX_M][SPLIT_NB];
+
+    const uint32_t tid = threadIdx.x;
+    const uint32_t lane = tid & 63u;
+    const uint32_t wave = tid >> 6;
+    const uint32_t ch = wave & 1u;   // column half (128 columns)
+    const uint32_t kp = wave >> 1;   // K phase: steps kp, kp + 2, ...
+    const uint32_t li = lane & 15u;  // 8 columns of B / row of A
+    const uint32_t lg = lane >> 4;   // 8-deep k group of the 32-deep step
+
+    const uint32_t cb = blockIdx.x % n_blocks;
+    const int64_t s = blockIdx.x / n_blocks;
+    const int64_t n_base = (int64_t)cb * SPLIT_NB + 128 * ch;
+    const int64_t n_lane = n_base + 8 * li;
+    const int64_t k_begin = s * k_per_split;
+    const int64_t k_end = k_begin + k_per_split < K ? k_begin + k_per_split : K;
+    const int64_t steps = k_end > k_begin ? (k_end - k_begin + KSTEP - 1) / KSTEP : 0;
+
+    f32x4 acc[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) acc[j] = f32x4{};
+
+    auto load_group = [&](int64_t t0, u32x4 (&rb)[SPLIT_U][8], u32x4 (&ra)[SPLIT_U]) {
+#pragma unroll
+        for (int u = 0; u < SPLIT_U; ++u) {
+            const int64_t t = t0 + 2 * u;
+            const int64_t k = k_begin + t * KSTEP + 8 * lg;
+            if (t < steps) {
+#pragma unroll
+                for (int r = 0; r < 8; ++r) rb[u][r] = load_b8<GUARD>(B, ldb, k + r, n_lane, k_end, N);
+                ra[u] = load_a8<true>(A, lda, li, k, M, k_end);
+            } else {
+#pragma unroll
+                for (int r = 0; r < 8; ++r) rb[u][r] = u32x4{0u, 0u, 0u, 0u};
+                ra[u] = u32x4{0u, 0u, 0u, 0u};
+            }
+        }
+    };
+    auto compute_group = [&](const u32x4 (&rb)[SPLIT_U][8], const u32x4 (&ra)[SPLIT_U]) {
+#pragma unroll
+        for (int u = 0; u < SPLIT_U; ++u) {
+            const f16x8 a = __builtin_bit_cast(f16x8, ra[u]);
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                u32x4 o;
+#pragma unroll
+                for (int d = 0; d < 4; ++d) o[d] = pair_halves(rb[u][2 * d][j >> 1], rb[u][2 * d + 1][j >> 1], j & 1);
+                acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, o), a, acc[j], 0, 0, 0);
+            }
+        }
+    };
+
+    // Two register sets: the loads of group g+1 are in flight while group g
+    // is transposed and multiplied.
+    const int64_t stride = 2 * SPLIT_U;
+    u32x4 rb0[SPLIT_U][8], rb1[SPLIT_U][8];
+    u32x4 ra0[SPLIT_U], ra1[SPLIT_U];
+    int64_t t0 = kp;
+    if (t0 < steps) load_group(t0, rb0, ra0);
+    for (; t0 < steps; t0 += 2 * stride) {
+        if (t0 + stride < steps) load_group(t0 + stride, rb1, ra1);
+        compute_group(rb0, ra0);
+        if (t0 + stride >= steps) break;
+        if (t0 + 2 * stride < steps) load_group(t0 + 2 * stride, rb0, ra0);
+        compute_group(rb1, ra1);
+    }
+
+    // acc[j] holds C^T: lane l, register r is the partial sum for row
+    // m = l%16 and column n = n_base + 8(4(l/16) + r) + j.
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) red[kp][li][128 * ch + 8 * (4 * lg + r) + j] = acc[j][r];
+    __syncthreads();
+
+    const int64_t n0 = (int64_t)cb * SPLIT_NB;
+    for (uint32_t o = tid; o < (uint32_t)(MAX_M * SPLIT_NB); o += SPLIT_THREADS) {
+        const uint32_t m = o / SPLIT_NB, nl = o % SPLIT_NB;
+        const int64_t n = n0 + nl;
+        if ((int64_t)m < M && n < N) part[(s * M + m) * N + n] = red[0][m][nl] + red[1][m][nl];
+    }
+}
+
+// Pass 2: C[m][n] = ReLU(sum over s of part[s][m][n]), rounded to fp16.
+__global__ __launch_bounds__(256) void gemm_relu_smallm_reduce_kernel(const float* __restrict__ part,
+                                                                      uint16_t* __restrict__ C, int64_t M,
+                                                                      int64_t N, int64_t ldc, int splits) {
+    const int64_t total = M * N;
+    for (int64_t o = (int64_t)blockIdx.x * 256 + threadIdx.x; o < total; o += (int64_t)gridDim.x * 256) {
+        float sum = 0.0f;
+        for (int s = 0; s < splits; ++s) sum += part[(int64_t)s * total + o];
+        const int64_t m = o / N, n = o - m * N;
+        C[m * ldc + n] = relu_to_f16(sum);
+    }
+}
+
 }  // namespace smallm
 }  // namespace gr

@@ -72,6 +72,8 @@ extern "C" {
 #define GR_PATH_SMALL_M    3 /* bandwidth kernel for GEMV-like shapes (few rows of A)       */
 #define GR_PATH_TILE_PACKED 4 /* copy A and/or B into the caller's workspace (aligned rows, */
                               /* K zero-padded), then the pipelined kernel; needs workspace */
+#define GR_PATH_SMALL_M_SPLIT 5 /* small-M split over K: fp32 partial sums in the caller's   */
+                                /* workspace, then a pass that sums them and applies ReLU  */
 
 /* What the planner decided for one problem.  Filled by gemm_relu_f16_plan. */
 typedef struct gr_plan_t {
@@ -88,6 +90,7 @@ typedef struct gr_plan_t {
     int32_t group_m;     /* tile rows per workgroup-order group (L2 reuse)           */
     int32_t packed;      /* GR_PATH_TILE_PACKED: bit 0 = A copied, bit 1 = B copied     */
     int64_t workspace;   /* bytes of the caller's workspace the path uses (else 0)     */
+    int32_t split_k;     /* K splits (GR_PATH_SMALL_M_SPLIT), 1 for the small-M path   */
 } gr_plan_t;
 
 /*
@@ -142,16 +145,22 @@ int gemm_relu_f16_forced(int64_t M, int64_t N, int64_t K,
 
 /*
  * ---- calls with a caller-provided workspace ---------------------------------
- * The pipelined kernel reads A and B in whole 16-byte chunks and walks K in
- * whole 32-deep strips.  When an operand's rows are not 16-byte aligned, or
- * K is not a multiple of 32, the calls above fall back to the guarded
- * register-staged kernel.  Given scratch device memory, the library instead
- * copies the offending operand(s) into it -- rows 16-byte aligned, K padded
- * with zeros to a multiple of 64 (the padded steps add exact zeros, the same
- * rule as the edge guards) -- and runs the pipelined kernel on the copies:
- * two launches on the stream, one extra read and write of the copied
- * operands.  The result is the same up to fp32 summation order (bit-exact
- * against the other tile paths: same MFMA steps, same k order).
+ * Two paths use scratch device memory when the caller provides it:
+ *   - GR_PATH_TILE_PACKED.  The pipelined kernel reads A and B in whole
+ *     16-byte chunks and walks K in whole 32-deep strips.  When an operand's
+ *     rows are not 16-byte aligned, or K is not a multiple of 32, the calls
+ *     above fall back to the guarded register-staged kernel.  With a
+ *     workspace the library instead copies the offending operand(s) into it
+ *     -- rows 16-byte aligned, K padded with zeros to a multiple of 64 (the
+ *     padded steps add exact zeros, the same rule as the edge guards) -- and
+ *     runs the pipelined kernel on the copies: two launches on the stream,
+ *     one extra read and write of the copied operands.  Bit-exact against
+ *     the other tile paths (same MFMA steps, same k order).
+ *   - GR_PATH_SMALL_M_SPLIT.  For M <= 16 (with 16-byte rows of B) the K
+ *     range is split so that each workgroup streams 256 columns of B over a
+ *     part of K; the fp32 partial sums (splits x M x N) go to the workspace
+ *     and a second launch adds them in split order, applies ReLU and rounds.
+ *     Same result as GR_PATH_SMALL_M up to fp32 summation order.
  *
  * Workspace rules: a DEVICE pointer, 256-byte aligned, owned by the caller,
  * not overlapping A, B or C; its contents on entry are ignored and on return
@@ -162,9 +171,10 @@ int gemm_relu_f16_forced(int64_t M, int64_t N, int64_t K,
 
 /*
  * gemm_relu_f16_workspace_size -- bytes of workspace that let this problem
- * take GR_PATH_TILE_PACKED; 0 when the problem never uses a workspace (it
- * already runs on the pipelined or small-M kernel, or has fewer than 128
- * rows, or is empty).  Validates like gemm_relu_f16; no HIP call.
+ * take GR_PATH_TILE_PACKED or GR_PATH_SMALL_M_SPLIT; 0 when the problem never
+ * uses a workspace (it already runs on the pipelined kernel in place, has
+ * between 17 and 127 rows, a K too short to split, or is empty).  Validates
+ * like gemm_relu_f16; no HIP call.
  *   bytes  host pointer receiving the size (must not be NULL)
  */
 int gemm_relu_f16_workspace_size(int64_t M, int64_t N, int64_t K,
@@ -176,10 +186,10 @@ int gemm_relu_f16_workspace_size(int64_t M, int64_t N, int64_t K,
 /*
  * gemm_relu_f16_ws -- gemm_relu_f16 with a workspace.
  *   workspace, workspace_bytes  the caller's scratch (NULL, 0 = none)
- * Takes GR_PATH_TILE_PACKED when the workspace holds at least the size
- * gemm_relu_f16_workspace_size reports and the problem is large enough for
- * the copies to pay (M*N*K >= 2^30); otherwise does exactly what
- * gemm_relu_f16 does.  Extra errors: GR_ERR_INVALID_ARG for a negative size
+ * Takes GR_PATH_TILE_PACKED or GR_PATH_SMALL_M_SPLIT when the workspace
+ * holds at least the size gemm_relu_f16_workspace_size reports (the packed
+ * path only when the problem is large enough for the copies to pay, M*N*K >=
+ * 2^30); otherwise does exactly what gemm_relu_f16 does.  Extra errors: GR_ERR_INVALID_ARG for a negative size
  * or a workspace not 256-byte aligned, GR_ERR_NULL_PTR for NULL with a
  * positive size, GR_ERR_ALIAS when the workspace overlaps A, B or C.
  */
@@ -192,9 +202,9 @@ int gemm_relu_f16_ws(int64_t M, int64_t N, int64_t K,
 
 /*
  * gemm_relu_f16_forced_ws -- gemm_relu_f16_forced with a workspace, which
- * also accepts GR_PATH_TILE_PACKED (whenever gemm_relu_f16_workspace_size is
- * positive and the workspace holds that many bytes, whatever the size of the
- * problem).  Test hook.
+ * also accepts GR_PATH_TILE_PACKED and GR_PATH_SMALL_M_SPLIT when the problem
+ * qualifies and the workspace holds the bytes that path needs, whatever the
+ * size of the problem (a split path may then use a single split).  Test hook.
  */
 int gemm_relu_f16_forced_ws(int64_t M, int64_t N, int64_t K,
                             const uint16_t* A, int64_t lda,

@@ -205,12 +205,41 @@ def test_workspace_size_and_packed_plan():
 
 def test_workspace_not_used_where_it_cannot_help():
     assert ws_size(4096, 4096, 4096) == (gr.GR_OK, 0)       # pipelined in place
-    assert ws_size(8, 16384, 8192) == (gr.GR_OK, 0)         # small-M kernel
     assert ws_size(100, 4096, 4100) == (gr.GR_OK, 0)        # fewer than 128 rows
     assert ws_size(0, 4096, 4096) == (gr.GR_OK, 0)          # empty
     assert ws_size(512, 512, 0, lda=1) == (gr.GR_OK, 0)     # K == 0
     assert plan_ws(4096, 4096, 4096, 1 << 30)[1]["path"] == gr.GR_PATH_TILE
     assert plan_ws(4096, 4096, 4096, 1 << 30)[1]["workspace"] == 0
+
+
+def test_small_m_split_plan():
+    # N = 4096: the single-pass kernel would run 64 workgroups; the split runs
+    # 16 column blocks of 256 x 16 splits of 512 = 256 workgroups
+    st, size = ws_size(8, 4096, 8192)
+    assert st == gr.GR_OK and size == 16 * 8 * 4096 * 4
+    st, p = plan_ws(8, 4096, 8192, size)
+    assert p["path"] == gr.GR_PATH_SMALL_M_SPLIT and p["split_k"] == 16 and p["grid"] == 256
+    assert p["workspace"] == size and p["block_n"] == 256
+    # too small a workspace, or none: the single-pass small-M kernel
+    assert plan_ws(8, 4096, 8192, size - 1)[1]["path"] == gr.GR_PATH_SMALL_M
+    assert plan(8, 4096, 8192)[1]["path"] == gr.GR_PATH_SMALL_M
+    # 256 strips or more already fill the chip: no workspace asked for
+    assert ws_size(8, 16384, 8192) == (gr.GR_OK, 0)
+    assert plan_ws(8, 16384, 8192, 1 << 30)[1]["path"] == gr.GR_PATH_SMALL_M
+    # B rows only 8-byte aligned: no split
+    assert ws_size(8, 4096, 8192, b=BASE_B + 8) == (gr.GR_OK, 0)
+    assert ws_size(8, 4096, 8192, ldb=4100) == (gr.GR_OK, 0)
+    # K of fewer than four 32-deep steps is not split
+    assert ws_size(8, 4096, 96) == (gr.GR_OK, 0)
+    # one column block: up to 64 splits, each at least two steps deep
+    st, p = plan_ws(4, 256, 4096, 1 << 24)
+    assert p["path"] == gr.GR_PATH_SMALL_M_SPLIT and p["split_k"] == 64 and p["grid"] == 64
+    assert p["workspace"] == 64 * 4 * 256 * 4
+    st, p = plan_ws(4, 256, 1024, 1 << 24)
+    assert p["split_k"] == 16
+    # forced without a workspace is refused
+    assert gr.gemm_relu_f16_forced(8, 16384, 8192, BASE_A, 8192, BASE_B, 16384, BASE_C, 16384, None,
+                                   gr.GR_PATH_SMALL_M_SPLIT) == gr.GR_ERR_INVALID_PATH
 
 
 def test_workspace_argument_checks():
@@ -322,10 +351,11 @@ def test_no_kernel_spills_to_scratch():
     scratch = [int(x) for x in re.findall(r"ScratchSize \[bytes/lane\]: (\d+)", res.stderr)]
     assert names and len(names) == len(scratch)
     hot = {n: s for n, s in zip(names, scratch)
-           if any(k in n for k in ("gemm_relu_tile2_kernel", "gemm_relu_tile3_kernel", "gemm_relu_smallm_kernel"))}
+           if any(k in n for k in ("gemm_relu_tile2_kernel", "gemm_relu_tile3_kernel", "gemm_relu_tile128_kernel",
+                                   "gemm_relu_smallm_kernel", "gemm_relu_smallm_split_kernel"))}
     assert hot, names
     # the pipelined whole-tile kernels may spill a few bytes outside their
     # steady loop; the small-M kernel must not spill at all
     for n, s in hot.items():
-        limit = 0 if "smallm" in n else 16
+        limit = 0 if ("smallm" in n or "tile128" in n) else 16
         assert s <= limit, (n, s)

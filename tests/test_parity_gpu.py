@@ -408,6 +408,72 @@ def test_small_m_and_tile_paths_agree(M, N, K):
     assert_parity(Cs, Ct, "small-M vs tile")
 
 
+# ---- the small-M split-K path (fp32 partial sums in a workspace) -------------
+
+SPLIT_CASES = [
+    # M, N, K, lda, ldb, ldc
+    (8, 16384, 8192, 8192, 16384, 16384),  # the small-M workload's shape (forced: 4 splits)
+    (8, 2048, 8192, 8192, 2048, 2048),     # 8 column blocks x 32 splits
+    (16, 1000, 1000, 1000, 1000, 1000),    # partial column block, K % 32 == 8
+    (5, 128, 8200, 8200, 128, 128),        # one column block, 8 splits
+    (1, 640, 96, 96, 640, 640),            # one row, 3 splits of one step
+    (3, 4096, 4096, 4104, 4104, 4097),     # padded A and B (poisoned), odd ldc
+]
+
+
+@pytest.mark.parametrize("M,N,K,lda,ldb,ldc", SPLIT_CASES)
+def test_small_m_split_parity(M, N, K, lda, ldb, ldc):
+    """Forced split-K small-M path against the oracle (full), C's padding and
+    the rows after it keep the sentinel, the workspace is not written past the
+    size asked for, and the single-pass small-M kernel agrees within the
+    tolerance (the two differ in fp32 summation order only)."""
+    import torch as t
+    st, size = gr.gemm_relu_f16_workspace_size(M, N, K, 0x100000, lda, 0x200000000000, ldb, 0x400000000000, ldc)
+    st2, plan = gr.gemm_relu_f16_plan_ws(M, N, K, 0x100000, lda, 0x200000000000, ldb, 0x400000000000, ldc, size)
+    log("split %dx%dx%d size=%d plan=%s" % (M, N, K, size, plan))
+    if size == 0:  # the planner would not split (the single pass fills the chip): force it
+        size = 64 * 4 * M * N + 256
+    assert st == gr.GR_OK and st2 == gr.GR_OK
+    A, B = synth.random_operands(M, N, K, seed=M * 31 + N + K, lda=lda, ldb=ldb, b_scale=K ** -0.5)
+    dA, dB = to_dev(A), to_dev(B)
+    extra_rows = 2
+    dC = full_dev(((M + extra_rows) * ldc,), SENTINEL)
+    tail = 4096
+    ws = full_dev(((size + tail) // 2,), WS_POISON).view(t.uint8)
+    assert call_ws(M, N, K, dA, lda, dB, ldb, dC, ldc, ws, size, path=gr.GR_PATH_SMALL_M_SPLIT) == gr.GR_OK
+    C1 = from_dev(dC)
+    C = C1[:M * ldc].reshape(M, ldc)
+    ref = oracle.gemm_relu_full(A, B, M=M, N=N, K=K, lda=lda, ldb=ldb)
+    assert_parity(C[:, :N], ref, "split %dx%dx%d" % (M, N, K))
+    assert np.all(C[:, N:] == SENTINEL), "a padding column of C was written"
+    assert np.all(C1[M * ldc:] == SENTINEL), "a row past M was written"
+    w = ws.view(t.int16).cpu().numpy().view(np.uint16)
+    assert np.all(w[size // 2:] == WS_POISON), "workspace written past the size the library asked for"
+    dC2 = full_dev((M * ldc,), SENTINEL)
+    assert call(M, N, K, dA, lda, dB, ldb, dC2, ldc, path=gr.GR_PATH_SMALL_M) == gr.GR_OK
+    C2 = from_dev(dC2).reshape(M, ldc)
+    assert_parity(C[:, :N], C2[:, :N], "split vs single pass")
+    # deterministic: a second call on the dirty workspace gives the same bits
+    dC3 = full_dev(((M + extra_rows) * ldc,), SENTINEL)
+    assert call_ws(M, N, K, dA, lda, dB, ldb, dC3, ldc, ws, size, path=gr.GR_PATH_SMALL_M_SPLIT) == gr.GR_OK
+    assert np.array_equal(C1, from_dev(dC3))
+
+
+def test_ws_call_picks_split_path_for_narrow_small_m():
+    """gemm_relu_f16_ws with the size the library asks for splits K when the
+    single-pass kernel would leave CUs idle (8 x 2048 x 8192: 32 strips)."""
+    import torch as t
+    M, N, K = 8, 2048, 8192
+    st, size = gr.gemm_relu_f16_workspace_size(M, N, K, 0x100000, K, 0x200000000000, N, 0x400000000000, N)
+    assert gr.gemm_relu_f16_plan_ws(M, N, K, 0x100000, K, 0x200000000000, N, 0x400000000000, N,
+                                    size)[1]["path"] == gr.GR_PATH_SMALL_M_SPLIT
+    A, B = synth.random_operands(M, N, K, seed=77, b_scale=K ** -0.5)
+    ws = t.empty(size, dtype=t.uint8, device="cuda")
+    dC = full_dev((M * N,), SENTINEL)
+    assert call_ws(M, N, K, to_dev(A), K, to_dev(B), N, dC, N, ws, size) == gr.GR_OK
+    assert_parity(from_dev(dC).reshape(M, N), oracle.gemm_relu_full(A, B), "narrow small-M, split")
+
+
 def test_runs_on_a_side_stream():
     t = pytest.importorskip("torch")
     M, N, K = 512, 512, 256
