@@ -32,10 +32,11 @@ GR_PATH_TILE_EDGE = 2
 GR_PATH_SMALL_M = 3
 GR_PATH_TILE_PACKED = 4
 GR_PATH_SMALL_M_SPLIT = 5
+GR_PATH_TILE_SPLIT = 6
 
 PATH_NAMES = {GR_PATH_NONE: "none", GR_PATH_TILE: "tile", GR_PATH_TILE_EDGE: "tile_edge",
               GR_PATH_SMALL_M: "small_m", GR_PATH_TILE_PACKED: "tile_packed",
-              GR_PATH_SMALL_M_SPLIT: "small_m_split"}
+              GR_PATH_SMALL_M_SPLIT: "small_m_split", GR_PATH_TILE_SPLIT: "tile_split"}
 
 
 class gr_plan_t(ctypes.Structure):

@@ -156,6 +156,38 @@ bool use_large_tiles(int64_t M, int64_t N) {
     return tiles > kSmallTileMaxLargeTiles;
 }
 
+// Split-K of the 128 x 128 tile path (workspace): when the small tiles do not
+// fill the chip (two workgroups per CU, 512 in all) and K is long, each tile's
+// K range is split S ways (S x tiles <= 512, at least 8 strips per split,
+// S <= 16); fp32 partial sums S x M x N go to the workspace and a second pass
+// adds them in order and applies ReLU.  The planner splits only when that
+// saves each workgroup at least 96 strips (measured: the second pass and the
+// partial sums cost about as much as 60-70 strips; 1024^3 and 2048^3 run
+// slower split, 1024 x 1024 x 4096 and up faster).
+constexpr int64_t kTileSplitMinSavedStrips = 96;
+struct TileSplit {
+    int64_t splits = 0, k_per_split = 0, bytes = 0;
+};
+constexpr int64_t kTileMaxSplits = 16;
+constexpr int64_t kTileMinSplitK = 256;
+
+bool tile_split_layout(int64_t M, int64_t N, int64_t K, bool allow_one, TileSplit* ts) {
+    using namespace gr::tile128;
+    const int64_t tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
+    int64_t S = 512 / tiles;
+    if (S > K / kTileMinSplitK) S = K / kTileMinSplitK;
+    if (S > kTileMaxSplits) S = kTileMaxSplits;
+    if (S < 1) S = 1;
+    const int64_t strips = K / BK;
+    if (!allow_one && (S < 2 || strips * (S - 1) < kTileSplitMinSavedStrips * S)) return false;
+    TileSplit q;
+    q.k_per_split = (strips + S - 1) / S * BK;
+    q.splits = (K + q.k_per_split - 1) / q.k_per_split;  // no empty split
+    q.bytes = (q.splits * M * N * 4 + kWorkspaceAlign - 1) / kWorkspaceAlign * kWorkspaceAlign;
+    *ts = q;
+    return true;
+}
+
 // Whole tiles of size bm x bn: the edge-free variant of those kernels.
 bool tile_whole(int64_t M, int64_t N, int64_t bm, int64_t bn) { return M % bm == 0 && N % bn == 0; }
 
@@ -193,11 +225,12 @@ bool pack_layout(int64_t M, int64_t N, int64_t K, uintptr_t A, int64_t lda, uint
 }
 
 void fill_plan(int path, int64_t M, int64_t N, int64_t K, uintptr_t A, int64_t lda, uintptr_t B,
-               int64_t ldb, uintptr_t C, int64_t ldc, const Pack& pk, const SmallMSplit& sp, gr_plan_t* p) {
+               int64_t ldb, uintptr_t C, int64_t ldc, const Pack& pk, const SmallMSplit& sp, const TileSplit& ts,
+               gr_plan_t* p) {
     std::memset(p, 0, sizeof(*p));
     p->path = path;
-    if (path == GR_PATH_TILE || path == GR_PATH_TILE_PACKED) {
-        const bool large = use_large_tiles(M, N);
+    if (path == GR_PATH_TILE || path == GR_PATH_TILE_PACKED || path == GR_PATH_TILE_SPLIT) {
+        const bool large = path != GR_PATH_TILE_SPLIT && use_large_tiles(M, N);
         const int64_t bm = large ? gr::tile2::BM : gr::tile128::BM;
         const int64_t bn = large ? gr::tile2::BN : gr::tile128::BN;
         p->block_m = (int32_t)bm;
@@ -210,9 +243,14 @@ void fill_plan(int path, int64_t M, int64_t N, int64_t K, uintptr_t A, int64_t l
         p->vec_b = 8;
         p->vec_c = vec_width_c(C, ldc);
         p->group_m = kGroupM;
+        p->split_k = 1;
         if (path == GR_PATH_TILE_PACKED) {
             p->packed = (pk.a ? 1 : 0) | (pk.b ? 2 : 0);
             p->workspace = pk.bytes;
+        } else if (path == GR_PATH_TILE_SPLIT) {
+            p->grid *= ts.splits;
+            p->split_k = (int32_t)ts.splits;
+            p->workspace = ts.bytes;
         }
     } else if (path == GR_PATH_TILE_EDGE) {
         using namespace gr::tile;
@@ -257,7 +295,7 @@ void fill_plan(int path, int64_t M, int64_t N, int64_t K, uintptr_t A, int64_t l
 }
 
 int choose_path(int64_t M, int64_t N, int64_t K, uintptr_t A, int64_t lda, uintptr_t B, int64_t ldb,
-                uintptr_t C, int64_t ldc, int64_t ws_bytes, Pack* pk, SmallMSplit* sp) {
+                uintptr_t C, int64_t ldc, int64_t ws_bytes, Pack* pk, SmallMSplit* sp, TileSplit* ts) {
     (void)C;
     (void)ldc;
     if (M == 0 || N == 0) return GR_PATH_NONE;
@@ -267,7 +305,12 @@ int choose_path(int64_t M, int64_t N, int64_t K, uintptr_t A, int64_t lda, uintp
             return GR_PATH_SMALL_M_SPLIT;
         return GR_PATH_SMALL_M;
     }
-    if (tile_fast_ok(M, N, K, A, lda, B, ldb)) return GR_PATH_TILE;
+    if (tile_fast_ok(M, N, K, A, lda, B, ldb)) {
+        if (ws_bytes > 0 && !use_large_tiles(M, N) && tile_split_layout(M, N, K, false, ts) &&
+            ts->bytes <= ws_bytes)
+            return GR_PATH_TILE_SPLIT;
+        return GR_PATH_TILE;
+    }
     if (ws_bytes > 0 && pack_layout(M, N, K, A, lda, B, ldb, pk) && pk->bytes <= ws_bytes &&
         (double)M * (double)N * (double)K >= (double)kPackMinMacs)
         return GR_PATH_TILE_PACKED;
@@ -345,8 +388,8 @@ int launch_pack(const Pack& pk, int64_t M, int64_t N, int64_t K, const uint16_t*
 }
 
 int run(const gr_plan_t& p, int64_t M, int64_t N, int64_t K, const uint16_t* A, int64_t lda, const uint16_t* B,
-        int64_t ldb, uint16_t* C, int64_t ldc, const Pack& pk, const SmallMSplit& sp, uint8_t* ws,
-        hipStream_t stream) {
+        int64_t ldb, uint16_t* C, int64_t ldc, const Pack& pk, const SmallMSplit& sp, const TileSplit& ts,
+        uint8_t* ws, hipStream_t stream) {
     switch (p.path) {
         case GR_PATH_NONE: return GR_OK;
         case GR_PATH_SMALL_M_SPLIT: {
@@ -364,6 +407,25 @@ int run(const gr_plan_t& p, int64_t M, int64_t N, int64_t K, const uint16_t* A, 
             return launch(gemm_relu_smallm_reduce_kernel, rblocks, 256, stream, (const float*)part, C, M, N, ldc,
                           (int)sp.splits);
         }
+        case GR_PATH_TILE_SPLIT: {
+            using namespace gr::tile128;
+            float* part = reinterpret_cast<float*>(ws);
+            const bool whole = tile_whole(M, N, BM, BN);
+            const uint32_t tiles_m = (uint32_t)((M + BM - 1) / BM);
+            const uint32_t tiles_n = (uint32_t)((N + BN - 1) / BN);
+            const uint32_t gm = (uint32_t)p.group_m;
+            const int vc = p.vec_c;
+            const int64_t kps = ts.k_per_split;
+            int st = whole ? launch(gemm_relu_tile128_kernel<false, true>, p.grid, THREADS, stream, A, B, C, M, N, K,
+                                    lda, ldb, ldc, tiles_m, tiles_n, gm, vc, part, kps)
+                           : launch(gemm_relu_tile128_kernel<true, true>, p.grid, THREADS, stream, A, B, C, M, N, K,
+                                    lda, ldb, ldc, tiles_m, tiles_n, gm, vc, part, kps);
+            if (st != GR_OK) return st;
+            int64_t rblocks = (M * N + 255) / 256;
+            if (rblocks > 2048) rblocks = 2048;
+            return launch(gr::smallm::gemm_relu_smallm_reduce_kernel, rblocks, 256, stream, (const float*)part, C, M,
+                          N, ldc, (int)ts.splits);
+        }
         case GR_PATH_TILE_PACKED: {
             const int st = launch_pack(pk, M, N, K, A, lda, B, ldb, ws, stream);
             if (st != GR_OK) return st;
@@ -371,7 +433,7 @@ int run(const gr_plan_t& p, int64_t M, int64_t N, int64_t K, const uint16_t* A, 
             q.path = GR_PATH_TILE;
             const uint16_t* Ap = pk.a ? reinterpret_cast<const uint16_t*>(ws) : A;
             const uint16_t* Bp = pk.b ? reinterpret_cast<const uint16_t*>(ws + pk.off_b) : B;
-            return run(q, M, N, pk.kp, Ap, pk.lda_p, Bp, pk.ldb_p, C, ldc, pk, sp, ws, stream);
+            return run(q, M, N, pk.kp, Ap, pk.lda_p, Bp, pk.ldb_p, C, ldc, pk, sp, ts, ws, stream);
         }
         case GR_PATH_TILE: {
             const int64_t bm = p.block_m, bn = p.block_n;
@@ -382,11 +444,13 @@ int run(const gr_plan_t& p, int64_t M, int64_t N, int64_t K, const uint16_t* A, 
             const int vc = p.vec_c;
             if (bm == gr::tile128::BM) {
                 using namespace gr::tile128;
+                float* no_part = nullptr;
+                const int64_t no_split = 0;
                 if (whole)
-                    return launch(gemm_relu_tile128_kernel<false>, p.grid, THREADS, stream, A, B, C, M, N, K, lda,
-                                  ldb, ldc, tiles_m, tiles_n, gm, vc);
-                return launch(gemm_relu_tile128_kernel<true>, p.grid, THREADS, stream, A, B, C, M, N, K, lda, ldb,
-                              ldc, tiles_m, tiles_n, gm, vc);
+                    return launch(gemm_relu_tile128_kernel<false, false>, p.grid, THREADS, stream, A, B, C, M, N, K,
+                                  lda, ldb, ldc, tiles_m, tiles_n, gm, vc, no_part, no_split);
+                return launch(gemm_relu_tile128_kernel<true, false>, p.grid, THREADS, stream, A, B, C, M, N, K, lda,
+                              ldb, ldc, tiles_m, tiles_n, gm, vc, no_part, no_split);
             }
             if (K % gr::tile3::BKA == 0) {
                 using namespace gr::tile3;
@@ -427,12 +491,12 @@ int run(const gr_plan_t& p, int64_t M, int64_t N, int64_t K, const uint16_t* A, 
 // a size alone skips the pointer checks).
 int plan_call(int64_t M, int64_t N, int64_t K, uintptr_t a, int64_t lda, uintptr_t b, int64_t ldb, uintptr_t c,
               int64_t ldc, uintptr_t ws, int64_t ws_bytes, bool ws_known, int forced, Pack* pk, SmallMSplit* sp,
-              gr_plan_t* p) {
+              TileSplit* ts, gr_plan_t* p) {
     if (ws_bytes < 0) return GR_ERR_INVALID_ARG;
     int st = ws_known ? validate(M, N, K, a, lda, b, ldb, c, ldc, ws, ws_bytes)
                       : validate(M, N, K, a, lda, b, ldb, c, ldc);
     if (st != GR_OK) return st;
-    int path = choose_path(M, N, K, a, lda, b, ldb, c, ldc, ws_bytes, pk, sp);
+    int path = choose_path(M, N, K, a, lda, b, ldb, c, ldc, ws_bytes, pk, sp, ts);
     if (forced >= 0 && path != GR_PATH_NONE) {
         if (forced == GR_PATH_TILE) {
             if (!tile_fast_ok(M, N, K, a, lda, b, ldb)) return GR_ERR_INVALID_PATH;
@@ -440,6 +504,10 @@ int plan_call(int64_t M, int64_t N, int64_t K, uintptr_t a, int64_t lda, uintptr
             if (K == 0 || !smallm_ok(M, N, K, a, lda, b, ldb)) return GR_ERR_INVALID_PATH;
         } else if (forced == GR_PATH_TILE_PACKED) {
             if (!pack_layout(M, N, K, a, lda, b, ldb, pk) || pk->bytes > ws_bytes) return GR_ERR_INVALID_PATH;
+        } else if (forced == GR_PATH_TILE_SPLIT) {
+            if (!tile_fast_ok(M, N, K, a, lda, b, ldb) || !tile_split_layout(M, N, K, true, ts) ||
+                ts->bytes > ws_bytes)
+                return GR_ERR_INVALID_PATH;
         } else if (forced == GR_PATH_SMALL_M_SPLIT) {
             if (!smallm_split_layout(M, N, K, a, lda, b, ldb, sp) || sp->bytes > ws_bytes) return GR_ERR_INVALID_PATH;
         } else if (forced != GR_PATH_TILE_EDGE) {
@@ -447,7 +515,7 @@ int plan_call(int64_t M, int64_t N, int64_t K, uintptr_t a, int64_t lda, uintptr
         }
         path = forced;
     }
-    fill_plan(path, M, N, K, a, lda, b, ldb, c, ldc, *pk, *sp, p);
+    fill_plan(path, M, N, K, a, lda, b, ldb, c, ldc, *pk, *sp, *ts, p);
     return GR_OK;
 }
 
@@ -455,23 +523,26 @@ int entry(int64_t M, int64_t N, int64_t K, const uint16_t* A, int64_t lda, const
           uint16_t* C, int64_t ldc, void* ws, int64_t ws_bytes, void* stream, int forced) {
     Pack pk;
     SmallMSplit sp;
+    TileSplit ts;
     gr_plan_t p;
     int st = plan_call(M, N, K, (uintptr_t)A, lda, (uintptr_t)B, ldb, (uintptr_t)C, ldc, (uintptr_t)ws, ws_bytes,
-                       true, forced, &pk, &sp, &p);
+                       true, forced, &pk, &sp, &ts, &p);
     if (st != GR_OK) return st;
     if (p.path == GR_PATH_NONE) return GR_OK;
     st = check_device();
     if (st != GR_OK) return st;
-    return run(p, M, N, K, A, lda, B, ldb, C, ldc, pk, sp, static_cast<uint8_t*>(ws),
+    return run(p, M, N, K, A, lda, B, ldb, C, ldc, pk, sp, ts, static_cast<uint8_t*>(ws),
                static_cast<hipStream_t>(stream));
 }
 
 bool known_path(int path) {
     return path == GR_PATH_TILE || path == GR_PATH_TILE_EDGE || path == GR_PATH_SMALL_M ||
-           path == GR_PATH_TILE_PACKED || path == GR_PATH_SMALL_M_SPLIT;
+           path == GR_PATH_TILE_PACKED || path == GR_PATH_SMALL_M_SPLIT || path == GR_PATH_TILE_SPLIT;
 }
 
-bool needs_workspace(int path) { return path == GR_PATH_TILE_PACKED || path == GR_PATH_SMALL_M_SPLIT; }
+bool needs_workspace(int path) {
+    return path == GR_PATH_TILE_PACKED || path == GR_PATH_SMALL_M_SPLIT || path == GR_PATH_TILE_SPLIT;
+}
 
 }  // namespace
 
@@ -503,10 +574,13 @@ int gemm_relu_f16_workspace_size(int64_t M, int64_t N, int64_t K, const uint16_t
     if (M == 0 || N == 0) return GR_OK;
     Pack pk;
     SmallMSplit sp;
+    TileSplit ts;
     if (smallm_ok(M, N, K, a, lda, b, ldb)) {
         if (smallm_split_pays(N) && smallm_split_layout(M, N, K, a, lda, b, ldb, &sp) && sp.splits >= 2)
             *bytes = sp.bytes;
-    } else if (!tile_fast_ok(M, N, K, a, lda, b, ldb) && pack_layout(M, N, K, a, lda, b, ldb, &pk)) {
+    } else if (tile_fast_ok(M, N, K, a, lda, b, ldb)) {
+        if (!use_large_tiles(M, N) && tile_split_layout(M, N, K, false, &ts)) *bytes = ts.bytes;
+    } else if (pack_layout(M, N, K, a, lda, b, ldb, &pk)) {
         *bytes = pk.bytes;
     }
     return GR_OK;
@@ -529,8 +603,9 @@ int gemm_relu_f16_plan_ws(int64_t M, int64_t N, int64_t K, const uint16_t* A, in
     if (!out) return GR_ERR_INVALID_ARG;
     Pack pk;
     SmallMSplit sp;
+    TileSplit ts;
     return plan_call(M, N, K, (uintptr_t)A, lda, (uintptr_t)B, ldb, (uintptr_t)C, ldc, 0, workspace_bytes, false,
-                     -1, &pk, &sp, out);
+                     -1, &pk, &sp, &ts, out);
 }
 
 const char* gemm_relu_status_string(int status) {

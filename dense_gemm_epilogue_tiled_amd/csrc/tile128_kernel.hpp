@@ -19,6 +19,11 @@
 //   * Edges as in the large-tile kernels (edge:: in common.hpp): the last
 //     tile row is moved up to end at row M (M >= 128), B copies past N read
 //     the last chunk, and the LDS-staged store of C is guarded.
+//   * SPLIT=true (split-K, with a workspace): workgroup g covers tile
+//     g % tiles of the K range of split g / tiles, and writes its fp32 sums
+//     for the outputs it owns to part[split][m][n]; a second pass
+//     (smallm::gemm_relu_smallm_reduce_kernel) adds the splits in order and
+//     applies ReLU, so ReLU still sees the complete sum.
 // Rows of A and B must be 16-byte aligned and K a positive multiple of 32.
 #pragma once
 
@@ -62,11 +67,11 @@ __device__ __forceinline__ f16x8 read_b_operand(const GR_LDS uint8_t* p) {
     return __builtin_bit_cast(f16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
 }
 
-template <bool EDGE>
+template <bool EDGE, bool SPLIT>
 __global__ __launch_bounds__(THREADS, 2) void gemm_relu_tile128_kernel(
     const uint16_t* __restrict__ A, const uint16_t* __restrict__ B, uint16_t* __restrict__ C, int64_t M, int64_t N,
     int64_t K, int64_t lda, int64_t ldb, int64_t ldc, uint32_t tiles_m, uint32_t tiles_n, uint32_t group_m,
-    int vec_c) {
+    int vec_c, float* __restrict__ part, int64_t k_per_split) {
     using tile2::barrier;
     using tile2::dma16;
     using tile2::read_a_operand;
@@ -80,17 +85,24 @@ __global__ __launch_bounds__(THREADS, 2) void gemm_relu_tile128_kernel(
     const uint32_t wm = wave >> 1;
     const uint32_t wn = wave & 1u;
 
+    const uint32_t tiles = tiles_m * tiles_n;
+    const uint32_t wg = SPLIT ? blockIdx.x % tiles : blockIdx.x;
+    const int64_t split = SPLIT ? blockIdx.x / tiles : 0;
     uint32_t tm, tn;
-    tile_of_workgroup(blockIdx.x, gridDim.x, tiles_m, tiles_n, group_m, tm, tn);
+    tile_of_workgroup(wg, SPLIT ? tiles : gridDim.x, tiles_m, tiles_n, group_m, tm, tn);
     const int64_t m_tile = (int64_t)tm * BM;
     const int64_t m0 = EDGE ? edge::shifted_row0(m_tile, M, BM) : m_tile;
     const int64_t n0 = (int64_t)tn * BN;
+    // K range of this workgroup (all of K unless split).
+    const int64_t k_begin = SPLIT ? split * k_per_split : 0;
+    const int64_t k_rest = K - k_begin > 0 ? K - k_begin : 0;
+    const int64_t k_len = SPLIT ? (k_rest < k_per_split ? k_rest : k_per_split) : K;
 
     // ---- copies: copy i of this wave fills LDS block 2*wave + i of a slot ---
     // A block = 16 rows x 64 bytes; lane -> row lane/4, slot lane%4.
     // B block = 4 rows x 256 bytes; lane -> row lane/16, slot lane%16.
-    const uint8_t* base_a = reinterpret_cast<const uint8_t*>(A + m0 * lda);
-    const uint8_t* base_b = reinterpret_cast<const uint8_t*>(B + n0);
+    const uint8_t* base_a = reinterpret_cast<const uint8_t*>(A + m0 * lda + k_begin);
+    const uint8_t* base_b = reinterpret_cast<const uint8_t*>(B + k_begin * ldb + n0);
     const int64_t step_a = BK * 2;
     const int64_t step_b = (int64_t)BK * ldb * 2;
     uint32_t off_a[COPIES], off_b[COPIES];
@@ -140,8 +152,8 @@ __global__ __launch_bounds__(THREADS, 2) void gemm_relu_tile128_kernel(
 #pragma unroll
         for (int j = 0; j < FN; ++j) acc[i][j] = f32x16{};
 
-    const uint32_t KT = (uint32_t)(K / BK);  // >= 1, whole strips only
-    issue(0);
+    const uint32_t KT = (uint32_t)(k_len / BK);  // whole strips only (>= 1 unless an empty split)
+    if (KT > 0) issue(0);
     if (KT > 1) issue(1);
     if (KT > 2) issue(2);
 
@@ -171,9 +183,41 @@ __global__ __launch_bounds__(THREADS, 2) void gemm_relu_tile128_kernel(
                     acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(fb[s][j], fa[s][i], acc[i][j], 0, 0, 0);
     }
 
-    // Epilogue: ReLU, fp16 and the store of C, staged through LDS.
-    epi::store_wave_tile<EDGE>(acc, lds + wave * epi::WaveTile<FM, FN>::REGION_BYTES, lane, C, ldc,
-                               m0 + wm * WAVE_TM, n0 + wn * WAVE_TN, m_tile, M, N, vec_c);
+    if constexpr (SPLIT) {
+        // fp32 partial sums of the outputs this tile owns: block (i, j) holds
+        // C^T, lane l register r is row 32i + l%32, column 32j + 8(r/4) +
+        // 4(l/32) + r%4 of the wave's tile.
+        float* pbase = part + split * M * N;
+#pragma unroll
+        for (int i = 0; i < FM; ++i) {
+            const int64_t m = m0 + wm * WAVE_TM + 32 * i + (lane & 31u);
+            const bool row_ok = !EDGE || m >= m_tile;
+#pragma unroll
+            for (int j = 0; j < FN; ++j) {
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const int64_t n = n0 + wn * WAVE_TN + 32 * j + 8 * q + 4 * (lane >> 5);
+                    float* dst = pbase + m * N + n;
+                    if (!EDGE || (row_ok && n + 4 <= N && (N & 3) == 0)) {
+                        *reinterpret_cast<f32x4*>(dst) = f32x4{acc[i][j][4 * q], acc[i][j][4 * q + 1],
+                                                               acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
+                    } else if (row_ok) {
+#pragma unroll
+                        for (int e = 0; e < 4; ++e)
+                            if (n + e < N) dst[e] = acc[i][j][4 * q + e];
+                    }
+                }
+            }
+        }
+        (void)C;
+        (void)ldc;
+        (void)vec_c;
+    } else {
+        // Epilogue: ReLU, fp16 and the store of C, staged through LDS.
+        epi::store_wave_tile<EDGE>(acc, lds + wave * epi::WaveTile<FM, FN>::REGION_BYTES, lane, C, ldc,
+                                   m0 + wm * WAVE_TM, n0 + wn * WAVE_TN, m_tile, M, N, vec_c);
+        (void)part;
+    }
 }
 
 #undef GR_LDS

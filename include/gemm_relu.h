@@ -74,6 +74,8 @@ extern "C" {
                               /* K zero-padded), then the pipelined kernel; needs workspace */
 #define GR_PATH_SMALL_M_SPLIT 5 /* small-M split over K: fp32 partial sums in the caller's   */
                                 /* workspace, then a pass that sums them and applies ReLU  */
+#define GR_PATH_TILE_SPLIT    6 /* 128x128-tile kernel split over K (few tiles, long K):     */
+                                /* fp32 partial sums in the workspace, then the same pass  */
 
 /* What the planner decided for one problem.  Filled by gemm_relu_f16_plan. */
 typedef struct gr_plan_t {
@@ -90,7 +92,8 @@ typedef struct gr_plan_t {
     int32_t group_m;     /* tile rows per workgroup-order group (L2 reuse)           */
     int32_t packed;      /* GR_PATH_TILE_PACKED: bit 0 = A copied, bit 1 = B copied     */
     int64_t workspace;   /* bytes of the caller's workspace the path uses (else 0)     */
-    int32_t split_k;     /* K splits (GR_PATH_SMALL_M_SPLIT), 1 for the small-M path   */
+    int32_t split_k;     /* K splits (the *_SPLIT paths); 1 for the tile and small-M  */
+                         /* paths                                                       */
 } gr_plan_t;
 
 /*
@@ -161,6 +164,11 @@ int gemm_relu_f16_forced(int64_t M, int64_t N, int64_t K,
  *     part of K; the fp32 partial sums (splits x M x N) go to the workspace
  *     and a second launch adds them in split order, applies ReLU and rounds.
  *     Same result as GR_PATH_SMALL_M up to fp32 summation order.
+ *   - GR_PATH_TILE_SPLIT.  For pipelined-path problems with too few 128x128
+ *     tiles to fill the chip and a long K, each tile's K range is split; the
+ *     fp32 partial sums go to the workspace and the same second launch sums
+ *     them in order and applies ReLU.  Same result as GR_PATH_TILE up to fp32
+ *     summation order.
  *
  * Workspace rules: a DEVICE pointer, 256-byte aligned, owned by the caller,
  * not overlapping A, B or C; its contents on entry are ignored and on return
@@ -171,10 +179,10 @@ int gemm_relu_f16_forced(int64_t M, int64_t N, int64_t K,
 
 /*
  * gemm_relu_f16_workspace_size -- bytes of workspace that let this problem
- * take GR_PATH_TILE_PACKED or GR_PATH_SMALL_M_SPLIT; 0 when the problem never
- * uses a workspace (it already runs on the pipelined kernel in place, has
- * between 17 and 127 rows, a K too short to split, or is empty).  Validates
- * like gemm_relu_f16; no HIP call.
+ * take GR_PATH_TILE_PACKED, GR_PATH_SMALL_M_SPLIT or GR_PATH_TILE_SPLIT; 0
+ * when the problem never uses a workspace (it fills the chip on the pipelined
+ * or small-M kernel as it is, has between 17 and 127 rows, a K too short to
+ * split, or is empty).  Validates like gemm_relu_f16; no HIP call.
  *   bytes  host pointer receiving the size (must not be NULL)
  */
 int gemm_relu_f16_workspace_size(int64_t M, int64_t N, int64_t K,
@@ -186,10 +194,11 @@ int gemm_relu_f16_workspace_size(int64_t M, int64_t N, int64_t K,
 /*
  * gemm_relu_f16_ws -- gemm_relu_f16 with a workspace.
  *   workspace, workspace_bytes  the caller's scratch (NULL, 0 = none)
- * Takes GR_PATH_TILE_PACKED or GR_PATH_SMALL_M_SPLIT when the workspace
- * holds at least the size gemm_relu_f16_workspace_size reports (the packed
- * path only when the problem is large enough for the copies to pay, M*N*K >=
- * 2^30); otherwise does exactly what gemm_relu_f16 does.  Extra errors: GR_ERR_INVALID_ARG for a negative size
+ * Takes GR_PATH_TILE_PACKED, GR_PATH_SMALL_M_SPLIT or GR_PATH_TILE_SPLIT
+ * when the workspace holds at least the size gemm_relu_f16_workspace_size
+ * reports (the packed path only when the problem is large enough for the
+ * copies to pay, M*N*K >= 2^30); otherwise does exactly what gemm_relu_f16
+ * does.  Extra errors: GR_ERR_INVALID_ARG for a negative size
  * or a workspace not 256-byte aligned, GR_ERR_NULL_PTR for NULL with a
  * positive size, GR_ERR_ALIAS when the workspace overlaps A, B or C.
  */
@@ -202,9 +211,10 @@ int gemm_relu_f16_ws(int64_t M, int64_t N, int64_t K,
 
 /*
  * gemm_relu_f16_forced_ws -- gemm_relu_f16_forced with a workspace, which
- * also accepts GR_PATH_TILE_PACKED and GR_PATH_SMALL_M_SPLIT when the problem
- * qualifies and the workspace holds the bytes that path needs, whatever the
- * size of the problem (a split path may then use a single split).  Test hook.
+ * also accepts GR_PATH_TILE_PACKED, GR_PATH_SMALL_M_SPLIT and
+ * GR_PATH_TILE_SPLIT when the problem qualifies and the workspace holds the
+ * bytes that path needs, whatever the size of the problem (a split path may
+ * then use a single split).  Test hook.
  */
 int gemm_relu_f16_forced_ws(int64_t M, int64_t N, int64_t K,
                             const uint16_t* A, int64_t lda,

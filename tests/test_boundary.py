@@ -204,7 +204,7 @@ def test_workspace_size_and_packed_plan():
 
 
 def test_workspace_not_used_where_it_cannot_help():
-    assert ws_size(4096, 4096, 4096) == (gr.GR_OK, 0)       # pipelined in place
+    assert ws_size(4096, 4096, 4096) == (gr.GR_OK, 0)       # pipelined in place, fills the chip
     assert ws_size(100, 4096, 4100) == (gr.GR_OK, 0)        # fewer than 128 rows
     assert ws_size(0, 4096, 4096) == (gr.GR_OK, 0)          # empty
     assert ws_size(512, 512, 0, lda=1) == (gr.GR_OK, 0)     # K == 0
@@ -240,6 +240,30 @@ def test_small_m_split_plan():
     # forced without a workspace is refused
     assert gr.gemm_relu_f16_forced(8, 16384, 8192, BASE_A, 8192, BASE_B, 16384, BASE_C, 16384, None,
                                    gr.GR_PATH_SMALL_M_SPLIT) == gr.GR_ERR_INVALID_PATH
+
+
+def test_tile_split_plan():
+    # 1024 x 1024: 64 tiles of 128 x 128; K = 16384 -> 8 splits (512 workgroups)
+    st, size = ws_size(1024, 1024, 16384)
+    assert st == gr.GR_OK and size == 8 * 1024 * 1024 * 4
+    st, p = plan_ws(1024, 1024, 16384, size)
+    assert p["path"] == gr.GR_PATH_TILE_SPLIT and p["split_k"] == 8 and p["grid"] == 512
+    assert p["block_m"] == 128 and p["workspace"] == size
+    # K = 4096: 8 splits of 512 save 112 of 128 strips per workgroup
+    assert plan_ws(1024, 1024, 4096, 1 << 30)[1]["split_k"] == 8
+    # a split must save at least 96 strips: not at 1024^3 (4 splits save 24)
+    # nor 2048^3 (2 splits save 32); large tiles that fill the chip never split
+    assert ws_size(1024, 1024, 1024) == (gr.GR_OK, 0)
+    assert ws_size(2048, 2048, 2048) == (gr.GR_OK, 0)
+    assert ws_size(1024, 1024, 256) == (gr.GR_OK, 0)
+    assert ws_size(4096, 4096, 4096) == (gr.GR_OK, 0)
+    assert plan_ws(2048, 2048, 2048, 1 << 30)[1]["path"] == gr.GR_PATH_TILE
+    # without a workspace, or one too small: the unsplit kernel
+    assert plan(1024, 1024, 16384)[1]["path"] == gr.GR_PATH_TILE
+    assert plan_ws(1024, 1024, 16384, size - 1)[1]["path"] == gr.GR_PATH_TILE
+    # forced without a workspace is refused
+    assert gr.gemm_relu_f16_forced(1024, 1024, 1024, BASE_A, 1024, BASE_B, 1024, BASE_C, 1024, None,
+                                   gr.GR_PATH_TILE_SPLIT) == gr.GR_ERR_INVALID_PATH
 
 
 def test_workspace_argument_checks():

@@ -474,6 +474,53 @@ def test_ws_call_picks_split_path_for_narrow_small_m():
     assert_parity(from_dev(dC).reshape(M, N), oracle.gemm_relu_full(A, B), "narrow small-M, split")
 
 
+# ---- split-K on the 128 x 128 tile path --------------------------------------
+
+TILE_SPLIT_CASES = [
+    # M, N, K, lda, ldb, ldc
+    (1024, 1024, 16384, 16384, 1024, 1024),  # 64 tiles x 8 splits
+    (128, 128, 1024, 1024, 128, 128),        # one tile, 4 splits
+    (300, 520, 4096, 4104, 520, 521),        # partial tiles, padded A, odd ldc
+    (640, 1000, 2080, 2080, 1000, 1000),     # 40 tiles x 8 splits, last split 2 strips deep
+]
+
+
+@pytest.mark.parametrize("M,N,K,lda,ldb,ldc", TILE_SPLIT_CASES)
+def test_tile_split_parity(M, N, K, lda, ldb, ldc):
+    """Forced split-K tile path against the oracle (full), padding of C and
+    the rows after it untouched, workspace not written past its size, the
+    unsplit kernel agrees within tolerance, and a repeat on the dirty
+    workspace gives the same bits."""
+    import torch as t
+    st, size = gr.gemm_relu_f16_workspace_size(M, N, K, 0x100000, lda, 0x200000000000, ldb, 0x400000000000, ldc)
+    st2, plan = gr.gemm_relu_f16_plan_ws(M, N, K, 0x100000, lda, 0x200000000000, ldb, 0x400000000000, ldc, size)
+    log("tile split %dx%dx%d size=%d plan=%s" % (M, N, K, size, plan))
+    if size == 0:  # the planner would not split this one: force it
+        size = 16 * M * N * 4 + 256
+    assert st == gr.GR_OK and st2 == gr.GR_OK
+    A, B = synth.random_operands(M, N, K, seed=M + N + K + 9, lda=lda, ldb=ldb, b_scale=K ** -0.5)
+    dA, dB = to_dev(A), to_dev(B)
+    extra_rows = 2
+    dC = full_dev(((M + extra_rows) * ldc,), SENTINEL)
+    tail = 4096
+    ws = full_dev(((size + tail) // 2,), WS_POISON).view(t.uint8)
+    assert call_ws(M, N, K, dA, lda, dB, ldb, dC, ldc, ws, size, path=gr.GR_PATH_TILE_SPLIT) == gr.GR_OK
+    C1 = from_dev(dC)
+    C = C1[:M * ldc].reshape(M, ldc)
+    assert_parity(C[:, :N], oracle.gemm_relu_full(A, B, M=M, N=N, K=K, lda=lda, ldb=ldb),
+                  "tile split %dx%dx%d" % (M, N, K))
+    assert np.all(C[:, N:] == SENTINEL), "a padding column of C was written"
+    assert np.all(C1[M * ldc:] == SENTINEL), "a row past M was written"
+    w = ws.view(t.int16).cpu().numpy().view(np.uint16)
+    assert np.all(w[size // 2:] == WS_POISON), "workspace written past the size the library asked for"
+    dC2 = full_dev((M * ldc,), SENTINEL)
+    assert call(M, N, K, dA, lda, dB, ldb, dC2, ldc, path=gr.GR_PATH_TILE) == gr.GR_OK
+    assert_parity(C[:, :N], from_dev(dC2).reshape(M, ldc)[:, :N], "split vs unsplit")
+    dC3 = full_dev(((M + extra_rows) * ldc,), SENTINEL)
+    assert call_ws(M, N, K, dA, lda, dB, ldb, dC3, ldc, ws, size, path=gr.GR_PATH_TILE_SPLIT) == gr.GR_OK
+    assert np.array_equal(C1, from_dev(dC3))
+
+
 def test_runs_on_a_side_stream():
     t = pytest.importorskip("torch")
     M, N, K = 512, 512, 256
