@@ -136,13 +136,14 @@ bool smallm_split_layout(int64_t M, int64_t N, int64_t K, uintptr_t A, int64_t l
 
 // Conditions of the pipelined direct-to-LDS kernels: 16-byte aligned rows of
 // A and B (every copy is a whole 16-byte chunk), K a positive multiple of the
-// 32-deep strip, pitches small enough for 32-bit per-lane copy offsets, and at
-// least one whole 128-row tile (a partial last tile row is moved up to end at
-// row M).  Any N and any C layout.
+// 32-deep strip and pitches small enough for 32-bit per-lane copy offsets.
+// Any M, N and C layout (the 256 x 256 kernels, used only for M >= 256, move
+// a partial last tile row up to end at row M; the 128 x 128 kernel clamps
+// rows past M).
 bool tile_fast_ok(int64_t M, int64_t N, int64_t K, uintptr_t A, int64_t lda, uintptr_t B, int64_t ldb) {
     using namespace gr::tile2;
-    return M >= gr::tile128::BM && N >= 1 && K % BK == 0 && K > 0 && vec_width(A, lda) == 8 &&
-           vec_width(B, ldb) == 8 && lda <= MAX_LDA && ldb <= MAX_LDB;
+    return M >= 1 && N >= 1 && K % BK == 0 && K > 0 && vec_width(A, lda) == 8 && vec_width(B, ldb) == 8 &&
+           lda <= MAX_LDA && ldb <= MAX_LDB;
 }
 
 // 256 x 256 tiles unless they would fill less than half of one wave of
@@ -207,7 +208,7 @@ struct Pack {
 
 bool pack_layout(int64_t M, int64_t N, int64_t K, uintptr_t A, int64_t lda, uintptr_t B, int64_t ldb, Pack* pk) {
     using namespace gr::tile2;
-    if (M < gr::tile128::BM || N < 1 || K < 1) return false;
+    if (M < 1 || N < 1 || K < 1) return false;
     Pack q;
     q.kp = K % BK == 0 ? K : round_up(K, 2 * BK);
     q.a = vec_width(A, lda) != 8 || lda > MAX_LDA || q.kp != K;

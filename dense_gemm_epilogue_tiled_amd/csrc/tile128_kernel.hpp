@@ -16,9 +16,10 @@
 //     landed, every wave done with the slot about to be refilled), issue the
 //     copies of strip kt+3, read the strip's fragments (ds_read_b128 for A,
 //     ds_read_b64_tr_b16 for B), 8 MFMAs.
-//   * Edges as in the large-tile kernels (edge:: in common.hpp): the last
-//     tile row is moved up to end at row M (M >= 128), B copies past N read
-//     the last chunk, and the LDS-staged store of C is guarded.
+//   * Edges (EDGE=true): a copy of a row past M reads row M-1 instead (the
+//     per-lane copy offsets are clamped once), so any M >= 1 works; B copies
+//     past N read the last chunk (edge:: in common.hpp); the rows and columns
+//     they feed are never stored, and the LDS-staged store of C is guarded.
 //   * SPLIT=true (split-K, with a workspace): workgroup g covers tile
 //     g % tiles of the K range of split g / tiles, and writes its fp32 sums
 //     for the outputs it owns to part[split][m][n]; a second pass
@@ -90,8 +91,7 @@ __global__ __launch_bounds__(THREADS, 2) void gemm_relu_tile128_kernel(
     const int64_t split = SPLIT ? blockIdx.x / tiles : 0;
     uint32_t tm, tn;
     tile_of_workgroup(wg, SPLIT ? tiles : gridDim.x, tiles_m, tiles_n, group_m, tm, tn);
-    const int64_t m_tile = (int64_t)tm * BM;
-    const int64_t m0 = EDGE ? edge::shifted_row0(m_tile, M, BM) : m_tile;
+    const int64_t m0 = (int64_t)tm * BM;
     const int64_t n0 = (int64_t)tn * BN;
     // K range of this workgroup (all of K unless split).
     const int64_t k_begin = SPLIT ? split * k_per_split : 0;
@@ -111,7 +111,9 @@ __global__ __launch_bounds__(THREADS, 2) void gemm_relu_tile128_kernel(
         const uint32_t blk = 2u * wave + (uint32_t)i;
         const uint32_t ra = 16u * blk + (lane >> 2);
         const uint32_t ca = (lane & 3u) ^ ((ra >> 2) & 3u);
-        off_a[i] = (uint32_t)((ra * lda + 8u * ca) * 2);
+        uint32_t ra_src = ra;  // row of A this lane copies into LDS row ra
+        if constexpr (EDGE) ra_src = m0 + ra < M ? ra : (uint32_t)(M - 1 - m0);
+        off_a[i] = (uint32_t)((ra_src * lda + 8u * ca) * 2);
         const uint32_t rb = 4u * blk + (lane >> 4);
         uint32_t cb = (lane & 15u) ^ ((rb & 3u) << 2);
         if constexpr (EDGE) cb = edge::clamp_chunk(cb, n0, N);
@@ -191,7 +193,7 @@ __global__ __launch_bounds__(THREADS, 2) void gemm_relu_tile128_kernel(
 #pragma unroll
         for (int i = 0; i < FM; ++i) {
             const int64_t m = m0 + wm * WAVE_TM + 32 * i + (lane & 31u);
-            const bool row_ok = !EDGE || m >= m_tile;
+            const bool row_ok = !EDGE || m < M;
 #pragma unroll
             for (int j = 0; j < FN; ++j) {
 #pragma unroll
@@ -215,7 +217,7 @@ __global__ __launch_bounds__(THREADS, 2) void gemm_relu_tile128_kernel(
     } else {
         // Epilogue: ReLU, fp16 and the store of C, staged through LDS.
         epi::store_wave_tile<EDGE>(acc, lds + wave * epi::WaveTile<FM, FN>::REGION_BYTES, lane, C, ldc,
-                                   m0 + wm * WAVE_TM, n0 + wn * WAVE_TN, m_tile, M, N, vec_c);
+                                   m0 + wm * WAVE_TM, n0 + wn * WAVE_TN, m0, M, N, vec_c);
         (void)part;
     }
 }

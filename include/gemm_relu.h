@@ -66,8 +66,8 @@ extern "C" {
 /* ---- execution paths chosen by the planner --------------------------------- */
 #define GR_PATH_NONE       0 /* empty output: nothing to launch                            */
 #define GR_PATH_TILE       1 /* pipelined MFMA tile kernel, direct-to-LDS copies: 16-B rows  */
-                             /* of A and B, K % 32 == 0, M >= 128; any N and C layout;     */
-                             /* 256x256 tiles, or 128x128 when fewer than 129 large tiles  */
+                             /* of A and B, K % 32 == 0; any M, N and C layout; 256x256    */
+                             /* tiles, or 128x128 when M < 256 or fewer than 129 large ones */
 #define GR_PATH_TILE_EDGE  2 /* MFMA tile kernel with edge guards and narrow loads          */
 #define GR_PATH_SMALL_M    3 /* bandwidth kernel for GEMV-like shapes (few rows of A)       */
 #define GR_PATH_TILE_PACKED 4 /* copy A and/or B into the caller's workspace (aligned rows, */
@@ -134,8 +134,8 @@ int gemm_relu_f16_plan(int64_t M, int64_t N, int64_t K,
  * the planner's choice, for tests that cross-check the paths on one input.
  *   path  GR_PATH_TILE, GR_PATH_TILE_EDGE or GR_PATH_SMALL_M.
  * GR_PATH_TILE is accepted only when the planner's conditions for it hold
- * (16-byte aligned rows of A and B, K a positive multiple of 32, M >= 128,
- * pitches of at most 2^22 elements for A and 2^25 for B); GR_PATH_SMALL_M
+ * (16-byte aligned rows of A and B, K a positive multiple of 32, pitches of
+ * at most 2^22 elements for A and 2^25 for B); GR_PATH_SMALL_M
  * only when the small-M kernel's alignment conditions hold (see
  * gemm_relu_f16_plan).  Otherwise GR_ERR_INVALID_PATH and nothing is
  * launched.  GR_PATH_TILE_EDGE accepts any valid problem.
@@ -181,8 +181,8 @@ int gemm_relu_f16_forced(int64_t M, int64_t N, int64_t K,
  * gemm_relu_f16_workspace_size -- bytes of workspace that let this problem
  * take GR_PATH_TILE_PACKED, GR_PATH_SMALL_M_SPLIT or GR_PATH_TILE_SPLIT; 0
  * when the problem never uses a workspace (it fills the chip on the pipelined
- * or small-M kernel as it is, has between 17 and 127 rows, a K too short to
- * split, or is empty).  Validates like gemm_relu_f16; no HIP call.
+ * or small-M kernel as it is, has a K too short to split, or is empty).
+ * Validates like gemm_relu_f16; no HIP call.
  *   bytes  host pointer receiving the size (must not be NULL)
  */
 int gemm_relu_f16_workspace_size(int64_t M, int64_t N, int64_t K,

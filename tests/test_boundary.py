@@ -151,8 +151,10 @@ def test_plan_partial_tiles_take_the_pipelined_kernel():
     st, p = plan(4099, 3071, 2048, lda=2048, ldb=3072, ldc=3071)
     assert st == gr.GR_OK and p["path"] == gr.GR_PATH_TILE and p["grid"] == 17 * 12 and p["vec_c"] == 1
     assert plan(256, 1, 32, ldb=8)[1]["path"] == gr.GR_PATH_TILE
-    # fewer than 128 rows, K % 32 != 0, or rows not 16-byte aligned: guarded kernel
-    assert plan(127, 512, 512)[1]["path"] == gr.GR_PATH_TILE_EDGE
+    # any M above the small-M threshold takes the pipelined kernel (rows past M
+    # clamped); K % 32 != 0 or rows not 16-byte aligned: guarded kernel
+    st, p = plan(17, 512, 512)
+    assert p["path"] == gr.GR_PATH_TILE and (p["block_m"], p["grid"]) == (128, 4)
     assert plan(512, 512, 48)[1]["path"] == gr.GR_PATH_TILE_EDGE
     assert plan(512, 500, 512)[1]["path"] == gr.GR_PATH_TILE_EDGE
     assert plan(512, 512, 512, b=BASE_B + 8)[1]["path"] == gr.GR_PATH_TILE_EDGE
@@ -205,7 +207,6 @@ def test_workspace_size_and_packed_plan():
 
 def test_workspace_not_used_where_it_cannot_help():
     assert ws_size(4096, 4096, 4096) == (gr.GR_OK, 0)       # pipelined in place, fills the chip
-    assert ws_size(100, 4096, 4100) == (gr.GR_OK, 0)        # fewer than 128 rows
     assert ws_size(0, 4096, 4096) == (gr.GR_OK, 0)          # empty
     assert ws_size(512, 512, 0, lda=1) == (gr.GR_OK, 0)     # K == 0
     assert plan_ws(4096, 4096, 4096, 1 << 30)[1]["path"] == gr.GR_PATH_TILE
@@ -305,7 +306,7 @@ def test_plan_empty_and_k_zero():
 
 def test_plan_small_m_threshold():
     assert plan(16, 4096, 4096)[1]["path"] == gr.GR_PATH_SMALL_M
-    assert plan(17, 4096, 4096)[1]["path"] == gr.GR_PATH_TILE_EDGE
+    assert plan(17, 4096, 4096)[1]["path"] == gr.GR_PATH_TILE
     assert plan(1, 1, 1)[1]["path"] == gr.GR_PATH_TILE_EDGE  # B row pitch 1: not 8-byte aligned
 
 
@@ -323,7 +324,7 @@ def test_calls_validate_before_touching_the_device():
     # fewer than 256 rows, misaligned B rows
     assert gr.gemm_relu_f16_forced(300, 256, 48, BASE_A, 48, BASE_B, 256, BASE_C, 256, None,
                                    gr.GR_PATH_TILE) == gr.GR_ERR_INVALID_PATH
-    assert gr.gemm_relu_f16_forced(127, 256, 64, BASE_A, 64, BASE_B, 256, BASE_C, 256, None,
+    assert gr.gemm_relu_f16_forced(300, 256, 64, BASE_A, 65, BASE_B, 256, BASE_C, 256, None,
                                    gr.GR_PATH_TILE) == gr.GR_ERR_INVALID_PATH
     assert gr.gemm_relu_f16_forced(300, 250, 64, BASE_A, 64, BASE_B, 250, BASE_C, 256, None,
                                    gr.GR_PATH_TILE) == gr.GR_ERR_INVALID_PATH

@@ -252,6 +252,8 @@ def test_tile_pipeline_every_strip_count(M, N, K):
 # ---- the pipelined kernels on partial tiles (16-byte rows, K % 32 == 0) -------
 
 PARTIAL_TILE_CASES = [
+    (17, 264, 64, 72, 264, 265),           # 17 rows: rows past M clamped, padded A, odd ldc
+    (100, 304, 96, 96, 304, 300 + 4),      # fewer rows than one tile, K % 64 == 32
     (128, 136, 32, 32, 136, 136),          # 128 x 128 tiles: one tile row, one partial tile column
     (257, 264, 64, 64, 264, 264),          # one row past a tile; N a multiple of 8
     (2400, 4000, 96, 96, 4000, 4001),      # 256 x 256 tiles, K % 64 == 32 (32-deep kernel), odd ldc
