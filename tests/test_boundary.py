@@ -310,6 +310,58 @@ def test_plan_small_m_threshold():
     assert plan(1, 1, 1)[1]["path"] == gr.GR_PATH_TILE_EDGE  # B row pitch 1: not 8-byte aligned
 
 
+def test_planner_invariants_on_random_problems():
+    """Seeded random shapes, pitches and alignments: the planner's choice
+    respects every kernel's preconditions, the grid matches the tile count,
+    and a workspace changes the path only when the library asked for one."""
+    import numpy as np
+    rng = np.random.default_rng(7)
+    for _ in range(3000):
+        M = int(rng.choice([rng.integers(0, 17), rng.integers(17, 5000)]))
+        N = int(rng.integers(0, 30000))
+        K = int(rng.choice([0, rng.integers(1, 9000), 32 * rng.integers(1, 300)]))
+        lda = max(K, 1) + int(rng.choice([0, 0, rng.integers(1, 17)]))
+        ldb = max(N, 1) + int(rng.choice([0, 0, rng.integers(1, 17)]))
+        ldc = max(N, 1) + int(rng.choice([0, 0, rng.integers(1, 17)]))
+        a = BASE_A + 2 * int(rng.choice([0, 0, rng.integers(1, 8)]))
+        b = BASE_B + 2 * int(rng.choice([0, 0, rng.integers(1, 8)]))
+        c = BASE_C + 2 * int(rng.choice([0, 0, rng.integers(1, 8)]))
+        st, p = gr.gemm_relu_f16_plan(M, N, K, a, lda, b, ldb, c, ldc)
+        assert st == gr.GR_OK, (M, N, K)
+        st, size = gr.gemm_relu_f16_workspace_size(M, N, K, a, lda, b, ldb, c, ldc)
+        assert st == gr.GR_OK and size >= 0 and size % 256 == 0
+        st, pw = gr.gemm_relu_f16_plan_ws(M, N, K, a, lda, b, ldb, c, ldc, size)
+        assert st == gr.GR_OK
+        key = (M, N, K, lda, ldb, ldc, a % 16, b % 16, c % 16)
+        if M == 0 or N == 0:
+            assert p["path"] == gr.GR_PATH_NONE and size == 0
+            continue
+        aligned = a % 16 == 0 and lda % 8 == 0 and b % 16 == 0 and ldb % 8 == 0
+        if p["path"] == gr.GR_PATH_TILE:
+            assert aligned and K % 32 == 0 and K > 0, key
+            bm = p["block_m"]
+            assert bm in (128, 256) and (bm == 128 or M >= 256), key
+            assert p["grid"] == -(-M // bm) * -(-N // bm), key
+        elif p["path"] == gr.GR_PATH_SMALL_M:
+            assert 1 <= M <= 16 and K > 0 and p["grid"] == -(-N // 64), key
+        else:
+            assert p["path"] == gr.GR_PATH_TILE_EDGE, key
+            assert not (aligned and K % 32 == 0 and K > 0), key
+        # the workspace plan differs from the plain one only where a workspace was asked for
+        if size == 0:
+            assert pw["path"] == p["path"] and pw["workspace"] == 0, key
+        else:
+            assert pw["workspace"] <= size, key
+            if pw["path"] != p["path"]:
+                assert pw["path"] in (gr.GR_PATH_TILE_PACKED, gr.GR_PATH_SMALL_M_SPLIT, gr.GR_PATH_TILE_SPLIT), key
+                assert pw["workspace"] == size, key
+            if pw["path"] == gr.GR_PATH_SMALL_M_SPLIT:
+                assert pw["grid"] == -(-N // 256) * pw["split_k"] and pw["workspace"] >= 4 * M * N * pw["split_k"]
+            if pw["path"] == gr.GR_PATH_TILE_SPLIT:
+                assert pw["block_m"] == 128 and pw["grid"] == -(-M // 128) * -(-N // 128) * pw["split_k"]
+                assert pw["workspace"] >= 4 * M * N * pw["split_k"], key
+
+
 def test_plan_null_output_struct():
     lib = gr.lib()
     assert lib.gemm_relu_f16_plan(8, 8, 8, BASE_A, 8, BASE_B, 8, BASE_C, 8, None) == gr.GR_ERR_INVALID_ARG

@@ -523,6 +523,72 @@ def test_tile_split_parity(M, N, K, lda, ldb, ldc):
     assert np.array_equal(C1, from_dev(dC3))
 
 
+# ---- seeded random problems across every planner decision --------------------
+
+def _fuzz_cases(count, seed):
+    """Half the cases have 16-byte rows and K % 32 == 0 (pipelined, small-M and
+    split paths; some with K of 3200-6400 so that the tile path splits K),
+    the others arbitrary pitches and offsets (guarded kernel, or packed with a
+    workspace), some of them large enough (>= 2^30 MAC) for the planner to
+    pack."""
+    rng = np.random.default_rng(seed)
+    cases = []
+    for i in range(count):
+        mode = ["aligned", "aligned", "aligned", "any", "any", "big", "long", "any"][i % 8]
+        M = int(rng.choice([rng.integers(1, 17), rng.integers(17, 300), rng.integers(300, 700)]))
+        N = int(rng.integers(1, 700))
+        if mode in ("aligned", "long"):
+            K = int(32 * (rng.integers(100, 200) if mode == "long" else rng.integers(1, 40)))
+            pads = [(-K) % 8 + 8 * int(rng.integers(0, 2)), (-N) % 8 + 8 * int(rng.integers(0, 2)),
+                    int(rng.integers(0, 9))]
+            offs = [0, 0, int(rng.choice([0, 0, rng.integers(1, 8)]))]
+        else:
+            K = int(rng.choice([0, rng.integers(1, 64), rng.integers(64, 700), 32 * rng.integers(1, 22)]))
+            pads = [int(rng.choice([0, 0, rng.integers(1, 9), 8])) for _ in range(3)]
+            offs = [int(rng.choice([0, 0, 0, rng.integers(1, 8)])) for _ in range(3)]
+            if mode == "big":
+                M, N, K = int(rng.integers(1000, 1300)), int(rng.integers(1000, 1300)), int(rng.integers(900, 1100))
+        use_ws = bool(rng.integers(0, 2)) or mode == "big"
+        cases.append((i, M, N, K, pads, offs, use_ws))
+    return cases
+
+
+@pytest.mark.parametrize("case", _fuzz_cases(48, 2024), ids=lambda c: "fuzz%d" % c[0])
+def test_random_problems_against_oracle(case):
+    """Random shapes, pitches and pointer offsets, with and without the
+    workspace the library asks for: whatever path the planner picks, the
+    result matches the oracle, padding of C and the bytes around it keep the
+    sentinel."""
+    import torch as t
+    i, M, N, K, pads, offs, use_ws = case
+    lda, ldb, ldc = max(K, 1) + pads[0], max(N, 1) + pads[1], N + pads[2]
+    A, B = synth.random_operands(M, N, K, seed=1000 + i, lda=lda, ldb=ldb)
+    Ap = np.concatenate([np.zeros(offs[0], np.uint16), A.ravel(), np.zeros(8, np.uint16)])
+    Bp = np.concatenate([np.zeros(offs[1], np.uint16), B.ravel(), np.zeros(8, np.uint16)])
+    dA, dB = to_dev(Ap), to_dev(Bp)
+    c_elems = M * ldc + offs[2] + 8
+    dC = full_dev((c_elems,), SENTINEL)
+    a = dA.data_ptr() + 2 * offs[0]
+    b = dB.data_ptr() + 2 * offs[1]
+    c = dC.data_ptr() + 2 * offs[2]
+    st, size = gr.gemm_relu_f16_workspace_size(M, N, K, a, lda, b, ldb, c, ldc)
+    assert st == gr.GR_OK
+    ws = t.empty(max(size, 256), dtype=t.uint8, device="cuda") if (use_ws and size) else None
+    wbytes = size if ws is not None else 0
+    st, plan = gr.gemm_relu_f16_plan_ws(M, N, K, a, lda, b, ldb, c, ldc, wbytes)
+    log("fuzz%d M=%d N=%d K=%d ld=%d,%d,%d offs=%s ws=%d path=%s" % (i, M, N, K, lda, ldb, ldc, offs, wbytes,
+                                                                    plan["path_name"]))
+    assert call_ws(M, N, K, dA, lda, dB, ldb, dC, ldc, ws, wbytes, offsets=tuple(offs)) == gr.GR_OK
+    Cflat = from_dev(dC)
+    assert np.all(Cflat[:offs[2]] == SENTINEL)
+    Cw = Cflat[offs[2]:offs[2] + M * ldc].reshape(M, ldc) if M else np.zeros((0, ldc), np.uint16)
+    assert np.all(Cflat[offs[2] + M * ldc:] == SENTINEL)
+    if M and N:
+        ref = oracle.gemm_relu_full(A, B, M=M, N=N, K=K, lda=lda, ldb=ldb)
+        assert_parity(Cw[:, :N], ref, "fuzz%d %s" % (i, plan["path_name"]))
+    assert np.all(Cw[:, N:] == SENTINEL)
+
+
 def test_runs_on_a_side_stream():
     t = pytest.importorskip("torch")
     M, N, K = 512, 512, 256
