@@ -95,6 +95,12 @@ def lib() -> ctypes.CDLL:
             l.gemm_relu_f16_plan_ws.argtypes = [i64, i64, i64, p, i64, p, i64, p, i64, i64,
                                                 ctypes.POINTER(gr_plan_t)]
             l.gemm_relu_f16_plan_ws.restype = i32
+            l.gemm_relu_f16_bt.argtypes = [i64, i64, i64, p, i64, p, i64, p, i64, p]
+            l.gemm_relu_f16_bt.restype = i32
+            l.gemm_relu_f16_bt_forced.argtypes = [i64, i64, i64, p, i64, p, i64, p, i64, p, i32]
+            l.gemm_relu_f16_bt_forced.restype = i32
+            l.gemm_relu_f16_bt_plan.argtypes = [i64, i64, i64, p, i64, p, i64, p, i64, ctypes.POINTER(gr_plan_t)]
+            l.gemm_relu_f16_bt_plan.restype = i32
             l.gemm_relu_status_string.argtypes = [i32]
             l.gemm_relu_status_string.restype = ctypes.c_char_p
             l.gemm_relu_version.argtypes = []
@@ -158,6 +164,21 @@ def gemm_relu_f16_forced_ws(M, N, K, A, lda, B, ldb, C, ldc, workspace, workspac
                                          int(workspace_bytes), _ptr(stream), path)
 
 
+def gemm_relu_f16_bt(M, N, K, A, lda, Bt, ldbt, C, ldc, stream=None) -> int:
+    """C := ReLU(A.Bt^T) with B given transposed (Bt is N x K); returns the status code."""
+    return lib().gemm_relu_f16_bt(M, N, K, _ptr(A), lda, _ptr(Bt), ldbt, _ptr(C), ldc, _ptr(stream))
+
+
+def gemm_relu_f16_bt_forced(M, N, K, A, lda, Bt, ldbt, C, ldc, stream=None, path=GR_PATH_TILE_EDGE) -> int:
+    return lib().gemm_relu_f16_bt_forced(M, N, K, _ptr(A), lda, _ptr(Bt), ldbt, _ptr(C), ldc, _ptr(stream), path)
+
+
+def gemm_relu_f16_bt_plan(M, N, K, A, lda, Bt, ldbt, C, ldc):
+    plan = gr_plan_t()
+    st = lib().gemm_relu_f16_bt_plan(M, N, K, _ptr(A), lda, _ptr(Bt), ldbt, _ptr(C), ldc, ctypes.byref(plan))
+    return st, _plan_dict(plan)
+
+
 def gemm_relu_status_string(status: int) -> str:
     return lib().gemm_relu_status_string(int(status)).decode()
 
@@ -173,6 +194,33 @@ def _stream_handle(stream):
     if isinstance(stream, int):
         return stream
     return stream.cuda_stream
+
+
+def gemm_relu_bt(a, bt, out=None, stream=None, path=None):
+    """Tensor convenience: ``out = ReLU(a @ bt.T)`` with the second operand
+    given transposed (``bt`` is N x K, as a linear layer's weight), 2-D fp16
+    tensors on the GPU with unit column stride."""
+    import torch
+    if a.dtype != torch.float16 or bt.dtype != torch.float16:
+        raise TypeError("a and bt must be float16")
+    if a.dim() != 2 or bt.dim() != 2 or a.shape[1] != bt.shape[1]:
+        raise ValueError("shapes do not form a matrix product: %s x %s^T" % (tuple(a.shape), tuple(bt.shape)))
+    M, K = a.shape
+    N = bt.shape[0]
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.float16, device=a.device)
+    for t in (a, bt, out):
+        if t.numel() and t.stride(1) != 1:
+            raise ValueError("tensors need unit column stride")
+    lda = max(a.stride(0), 1) if M > 1 else max(K, 1)
+    ldbt = max(bt.stride(0), 1) if N > 1 else max(K, 1)
+    ldc = max(out.stride(0), 1) if M > 1 else max(N, 1)
+    h = _stream_handle(stream)
+    args = (M, N, K, a.data_ptr(), lda, bt.data_ptr(), ldbt, out.data_ptr(), ldc, h)
+    st = gemm_relu_f16_bt(*args) if path is None else gemm_relu_f16_bt_forced(*args, path)
+    if st != GR_OK:
+        raise GemmReluError(st, "gemm_relu_f16_bt")
+    return out
 
 
 def gemm_relu(a, b, out=None, stream=None, path=None, workspace="auto"):

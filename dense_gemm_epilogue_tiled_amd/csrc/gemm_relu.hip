@@ -545,9 +545,203 @@ bool needs_workspace(int path) {
     return path == GR_PATH_TILE_PACKED || path == GR_PATH_SMALL_M_SPLIT || path == GR_PATH_TILE_SPLIT;
 }
 
+// ---- B given transposed (Bt, N x K) -------------------------------------------
+
+// Argument checks for the transposed-B calls: Bt is N x K with pitch ldbt >=
+// max(1, K); otherwise as validate().
+int validate_bt(int64_t M, int64_t N, int64_t K, uintptr_t A, int64_t lda, uintptr_t Bt, int64_t ldbt,
+                uintptr_t C, int64_t ldc) {
+    if (M < 0 || N < 0 || K < 0) return GR_ERR_INVALID_DIM;
+    if (M > kMaxDim || N > kMaxDim || K > kMaxDim) return GR_ERR_TOO_LARGE;
+    const int64_t kmin = K > 1 ? K : 1, nmin = N > 1 ? N : 1;
+    if (lda < kmin || ldbt < kmin || ldc < nmin) return GR_ERR_INVALID_LD;
+    const bool used = M > 0 && N > 0 && K > 0;
+    const bool c_used = M > 0 && N > 0;
+    if ((used && (!A || !Bt)) || (c_used && !C)) return GR_ERR_NULL_PTR;
+    const int64_t sa = used ? span_bytes(M, K, lda) : 0;
+    const int64_t sb = used ? span_bytes(N, K, ldbt) : 0;
+    const int64_t sc = c_used ? span_bytes(M, N, ldc) : 0;
+    if (sa < 0 || sb < 0 || sc < 0) return GR_ERR_TOO_LARGE;
+    if (overlaps(C, sc, A, sa) || overlaps(C, sc, Bt, sb)) return GR_ERR_ALIAS;
+    return GR_OK;
+}
+
+// Largest pitch for which the direct-to-LDS small-M Bt kernel's per-lane copy
+// offsets (64 rows of Bt) fit in 32 bits.
+constexpr int64_t kBtLdsMaxPitch = (int64_t(1) << 32) / (64 * 2) - 512;
+
+// Small-M kernel for Bt: 16-byte rows of A and of Bt.
+bool smallm_bt_ok(int64_t M, int64_t K, uintptr_t A, int64_t lda, uintptr_t Bt, int64_t ldbt) {
+    return M >= 1 && M <= kSmallMThreshold && K > 0 && A % 16 == 0 && lda % 8 == 0 && Bt % 16 == 0 &&
+           ldbt % 8 == 0;
+}
+
+// Pipelined kernels for Bt: 16-byte rows of A and Bt, K % 32 == 0; Bt is
+// staged like A, so its pitch has A's limit.
+bool tile_bt_ok(int64_t M, int64_t N, int64_t K, uintptr_t A, int64_t lda, uintptr_t Bt, int64_t ldbt) {
+    using namespace gr::tile2;
+    return M >= 1 && N >= 1 && K > 0 && K % BK == 0 && vec_width(A, lda) == 8 && vec_width(Bt, ldbt) == 8 &&
+           lda <= MAX_LDA && ldbt <= MAX_LDA;
+}
+
+int choose_path_bt(int64_t M, int64_t N, int64_t K, uintptr_t A, int64_t lda, uintptr_t Bt, int64_t ldbt) {
+    if (M == 0 || N == 0) return GR_PATH_NONE;
+    if (smallm_bt_ok(M, K, A, lda, Bt, ldbt)) return GR_PATH_SMALL_M;
+    if (tile_bt_ok(M, N, K, A, lda, Bt, ldbt)) return GR_PATH_TILE;
+    return GR_PATH_TILE_EDGE;
+}
+
+void fill_plan_bt(int path, int64_t M, int64_t N, int64_t K, uintptr_t A, int64_t lda, uintptr_t Bt, int64_t ldbt,
+                  uintptr_t C, int64_t ldc, gr_plan_t* p) {
+    Pack pk;
+    SmallMSplit sp;
+    TileSplit ts;
+    fill_plan(path == GR_PATH_SMALL_M ? GR_PATH_NONE : path, M, N, K, A, lda, Bt, ldbt, C, ldc, pk, sp, ts, p);
+    p->path = path;
+    if (path == GR_PATH_TILE) {
+        p->block_k = gr::tile2::BK;
+        p->stages = gr::tile2::STAGES;
+    } else if (path == GR_PATH_TILE_EDGE) {
+        p->vec_b = vec_width(Bt, ldbt);
+    } else if (path == GR_PATH_SMALL_M) {
+        using namespace gr::smallm;
+        p->block_m = MAX_M;
+        p->block_n = BT_NB;
+        p->block_k = KSTEP;
+        p->stages = BT_U;
+        p->threads = 64 * BT_WAVES;
+        p->grid = (N + BT_NB - 1) / BT_NB;
+        p->vec_a = 8;
+        p->vec_b = 8;
+        p->vec_c = 1;
+        p->group_m = 1;
+        p->split_k = 1;
+    }
+}
+
+template <int VA, int VB>
+int launch_tile_bt(const gr_plan_t& p, int64_t M, int64_t N, int64_t K, const uint16_t* A, int64_t lda,
+                   const uint16_t* Bt, int64_t ldbt, uint16_t* C, int64_t ldc, hipStream_t stream) {
+    using namespace gr::tile;
+    const uint32_t tiles_m = (uint32_t)((M + BM - 1) / BM);
+    const uint32_t tiles_n = (uint32_t)((N + BN - 1) / BN);
+    return launch(gemm_relu_tile_kernel<true, VA, VB, true>, p.grid, THREADS, stream, A, Bt, C, M, N, K, lda, ldbt,
+                  ldc, tiles_m, tiles_n, (uint32_t)p.group_m, (int)p.vec_c);
+}
+
+int run_bt(const gr_plan_t& p, int64_t M, int64_t N, int64_t K, const uint16_t* A, int64_t lda, const uint16_t* Bt,
+           int64_t ldbt, uint16_t* C, int64_t ldc, hipStream_t stream) {
+    switch (p.path) {
+        case GR_PATH_NONE: return GR_OK;
+        case GR_PATH_SMALL_M: {
+            using namespace gr::smallm;
+            if (K % BTL_KC == 0 && ldbt <= kBtLdsMaxPitch && lda <= kBtLdsMaxPitch) {
+                // K in whole 256-deep chunks: the direct-to-LDS variant
+                const int64_t grid = (N + BTL_NB - 1) / BTL_NB;
+                if (N % BTL_NB == 0)
+                    return launch(gemm_relu_smallm_bt_lds_kernel<false>, grid, 256, stream, A, Bt, C, M, N, K, lda,
+                                  ldbt, ldc);
+                return launch(gemm_relu_smallm_bt_lds_kernel<true>, grid, 256, stream, A, Bt, C, M, N, K, lda, ldbt,
+                              ldc);
+            }
+            const bool whole = N % BT_NB == 0 && K % KSTEP == 0;
+            if (whole)
+                return launch(gemm_relu_smallm_bt_kernel<false>, p.grid, p.threads, stream, A, Bt, C, M, N, K, lda,
+                              ldbt, ldc);
+            return launch(gemm_relu_smallm_bt_kernel<true>, p.grid, p.threads, stream, A, Bt, C, M, N, K, lda, ldbt,
+                          ldc);
+        }
+        case GR_PATH_TILE: {
+            const int64_t bm = p.block_m, bn = p.block_n;
+            const bool whole = tile_whole(M, N, bm, bn);
+            const uint32_t tiles_m = (uint32_t)((M + bm - 1) / bm);
+            const uint32_t tiles_n = (uint32_t)((N + bn - 1) / bn);
+            const uint32_t gm = (uint32_t)p.group_m;
+            const int vc = p.vec_c;
+            if (bm == gr::tile128::BM) {
+                using namespace gr::tile128;
+                float* no_part = nullptr;
+                const int64_t no_split = 0;
+                if (whole)
+                    return launch(gemm_relu_tile128_kernel<false, false, true>, p.grid, THREADS, stream, A, Bt, C, M,
+                                  N, K, lda, ldbt, ldc, tiles_m, tiles_n, gm, vc, no_part, no_split);
+                return launch(gemm_relu_tile128_kernel<true, false, true>, p.grid, THREADS, stream, A, Bt, C, M, N,
+                              K, lda, ldbt, ldc, tiles_m, tiles_n, gm, vc, no_part, no_split);
+            }
+            using namespace gr::tile2;
+            if (whole)
+                return launch(gemm_relu_tile2_kernel<false, true>, p.grid, THREADS, stream, A, Bt, C, M, N, K, lda,
+                              ldbt, ldc, tiles_m, tiles_n, gm, vc);
+            return launch(gemm_relu_tile2_kernel<true, true>, p.grid, THREADS, stream, A, Bt, C, M, N, K, lda, ldbt,
+                          ldc, tiles_m, tiles_n, gm, vc);
+        }
+        case GR_PATH_TILE_EDGE: {
+            const int va = p.vec_a, vb = p.vec_b;
+            if (va == 8 && vb == 8) return launch_tile_bt<8, 8>(p, M, N, K, A, lda, Bt, ldbt, C, ldc, stream);
+            if (va == 8 && vb == 2) return launch_tile_bt<8, 2>(p, M, N, K, A, lda, Bt, ldbt, C, ldc, stream);
+            if (va == 8) return launch_tile_bt<8, 1>(p, M, N, K, A, lda, Bt, ldbt, C, ldc, stream);
+            if (va == 2 && vb == 8) return launch_tile_bt<2, 8>(p, M, N, K, A, lda, Bt, ldbt, C, ldc, stream);
+            if (va == 2 && vb == 2) return launch_tile_bt<2, 2>(p, M, N, K, A, lda, Bt, ldbt, C, ldc, stream);
+            if (va == 2) return launch_tile_bt<2, 1>(p, M, N, K, A, lda, Bt, ldbt, C, ldc, stream);
+            if (vb == 8) return launch_tile_bt<1, 8>(p, M, N, K, A, lda, Bt, ldbt, C, ldc, stream);
+            if (vb == 2) return launch_tile_bt<1, 2>(p, M, N, K, A, lda, Bt, ldbt, C, ldc, stream);
+            return launch_tile_bt<1, 1>(p, M, N, K, A, lda, Bt, ldbt, C, ldc, stream);
+        }
+        default: return GR_ERR_INVALID_PATH;
+    }
+}
+
+int plan_call_bt(int64_t M, int64_t N, int64_t K, uintptr_t a, int64_t lda, uintptr_t bt, int64_t ldbt, uintptr_t c,
+                 int64_t ldc, int forced, gr_plan_t* p) {
+    int st = validate_bt(M, N, K, a, lda, bt, ldbt, c, ldc);
+    if (st != GR_OK) return st;
+    int path = choose_path_bt(M, N, K, a, lda, bt, ldbt);
+    if (forced >= 0 && path != GR_PATH_NONE) {
+        if (forced == GR_PATH_TILE) {
+            if (!tile_bt_ok(M, N, K, a, lda, bt, ldbt)) return GR_ERR_INVALID_PATH;
+        } else if (forced == GR_PATH_SMALL_M) {
+            if (!smallm_bt_ok(M, K, a, lda, bt, ldbt)) return GR_ERR_INVALID_PATH;
+        } else if (forced != GR_PATH_TILE_EDGE) {
+            return GR_ERR_INVALID_PATH;
+        }
+        path = forced;
+    }
+    fill_plan_bt(path, M, N, K, a, lda, bt, ldbt, c, ldc, p);
+    return GR_OK;
+}
+
+int entry_bt(int64_t M, int64_t N, int64_t K, const uint16_t* A, int64_t lda, const uint16_t* Bt, int64_t ldbt,
+             uint16_t* C, int64_t ldc, void* stream, int forced) {
+    gr_plan_t p;
+    int st = plan_call_bt(M, N, K, (uintptr_t)A, lda, (uintptr_t)Bt, ldbt, (uintptr_t)C, ldc, forced, &p);
+    if (st != GR_OK) return st;
+    if (p.path == GR_PATH_NONE) return GR_OK;
+    st = check_device();
+    if (st != GR_OK) return st;
+    return run_bt(p, M, N, K, A, lda, Bt, ldbt, C, ldc, static_cast<hipStream_t>(stream));
+}
+
 }  // namespace
 
 extern "C" {
+
+int gemm_relu_f16_bt(int64_t M, int64_t N, int64_t K, const uint16_t* A, int64_t lda, const uint16_t* Bt,
+                     int64_t ldbt, uint16_t* C, int64_t ldc, void* stream) {
+    return entry_bt(M, N, K, A, lda, Bt, ldbt, C, ldc, stream, -1);
+}
+
+int gemm_relu_f16_bt_forced(int64_t M, int64_t N, int64_t K, const uint16_t* A, int64_t lda, const uint16_t* Bt,
+                            int64_t ldbt, uint16_t* C, int64_t ldc, void* stream, int path) {
+    if (path != GR_PATH_TILE && path != GR_PATH_TILE_EDGE && path != GR_PATH_SMALL_M) return GR_ERR_INVALID_PATH;
+    return entry_bt(M, N, K, A, lda, Bt, ldbt, C, ldc, stream, path);
+}
+
+int gemm_relu_f16_bt_plan(int64_t M, int64_t N, int64_t K, const uint16_t* A, int64_t lda, const uint16_t* Bt,
+                          int64_t ldbt, const uint16_t* C, int64_t ldc, gr_plan_t* out) {
+    if (!out) return GR_ERR_INVALID_ARG;
+    return plan_call_bt(M, N, K, (uintptr_t)A, lda, (uintptr_t)Bt, ldbt, (uintptr_t)C, ldc, -1, out);
+}
+
 
 int gemm_relu_f16(int64_t M, int64_t N, int64_t K, const uint16_t* A, int64_t lda, const uint16_t* B, int64_t ldb,
                   uint16_t* C, int64_t ldc, void* stream) {

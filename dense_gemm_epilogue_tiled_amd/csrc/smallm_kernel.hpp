@@ -24,6 +24,7 @@
 #pragma once
 
 #include "common.hpp"
+#include "tile2_kernel.hpp"
 
 namespace gr {
 
@@ -327,6 +328,220 @@ __global__ __launch_bounds__(256) void gemm_relu_smallm_reduce_kernel(const floa
         for (int s = 0; s < splits; ++s) sum += part[(int64_t)s * total + o];
         const int64_t m = o / N, n = o - m * N;
         C[m * ldc + n] = relu_to_f16(sum);
+    }
+}
+
+// ---- B given transposed (Bt, N x K row-major): the GEMV pattern proper ------
+//
+// With B stored as N x K (a weight matrix in the layout of the GEMV pattern of
+// "Tilelang Cuda Patterns", section 4), every column of C is a dot product of
+// two contiguous rows.  A workgroup owns 64 columns (64 rows of Bt): its 8
+// waves are 4 column groups of 16 x 2 interleaved K phases (groups of BT_U
+// 32-deep steps alternate between the phases), so that 8 waves per CU keep
+// loads in flight.  Per step a lane loads 16 bytes of one Bt row (row l%16,
+// k group l/16) and 16 bytes of one row of A, and both are
+// v_mfma_f32_16x16x32_f16 operands as they stand -- no transpose.  Two
+// register sets of BT_U steps; at the end the two K phases are added in LDS,
+// then ReLU, fp16 and the store.
+constexpr int BT_COLS = 16;    // columns of C per column group
+constexpr int BT_GROUPS = 4;   // column groups per workgroup
+constexpr int BT_PHASES = 2;   // interleaved K phases per column group
+constexpr int BT_WAVES = BT_GROUPS * BT_PHASES;
+constexpr int BT_NB = BT_COLS * BT_GROUPS;  // columns per workgroup
+constexpr int BT_U = 8;
+
+// Eight consecutive fp16 of Bt row n from column k; zero outside [0,N) x [0,K).
+template <bool GUARD>
+__device__ __forceinline__ u32x4 load_bt8(const uint16_t* Bt, int64_t ldbt, int64_t n, int64_t k, int64_t N,
+                                          int64_t K) {
+    if constexpr (!GUARD) {
+        return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(Bt + n * ldbt + k));
+    } else {
+        u32x4 v = u32x4{0u, 0u, 0u, 0u};
+        if (n < N && k < K) {
+            const uint16_t* p = Bt + n * ldbt + k;
+            if (k + 8 <= K) {
+                v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+            } else {
+                uint32_t h[8] = {0u, 0u, 0u, 0u, 0u, 0u, 0u, 0u};
+#pragma unroll
+                for (int e = 0; e < 8; ++e)
+                    if (k + e < K) h[e] = p[e];
+#pragma unroll
+                for (int d = 0; d < 4; ++d) v[d] = h[2 * d] | (h[2 * d + 1] << 16);
+            }
+        }
+        return v;
+    }
+}
+
+template <bool GUARD>
+__global__ __launch_bounds__(64 * BT_WAVES) void gemm_relu_smallm_bt_kernel(
+    const uint16_t* __restrict__ A, const uint16_t* __restrict__ Bt, uint16_t* __restrict__ C, int64_t M, int64_t N,
+    int64_t K, int64_t lda, int64_t ldbt, int64_t ldc) {
+    __shared__ __attribute__((aligned(16))) float red[BT_PHASES][MAX_M][BT_NB];
+
+    const uint32_t tid = threadIdx.x;
+    const uint32_t lane = tid & 63u;
+    const uint32_t wave = tid >> 6;
+    const uint32_t cg = wave % BT_GROUPS;  // column group
+    const uint32_t kp = wave / BT_GROUPS;  // K phase
+    const uint32_t li = lane & 15u;        // row of Bt (column of C) / row of A
+    const uint32_t lg = lane >> 4;         // 8-deep k group of the 32-deep step
+
+    const int64_t n_wg = (int64_t)blockIdx.x * BT_NB;
+    const int64_t n_base = n_wg + BT_COLS * cg;
+    const int64_t n_row = n_base + li;
+    const int64_t steps = (K + KSTEP - 1) / KSTEP;
+
+    f32x4 acc = f32x4{};
+    auto load_group = [&](int64_t t0, u32x4 (&rb)[BT_U], u32x4 (&ra)[BT_U]) {
+#pragma unroll
+        for (int u = 0; u < BT_U; ++u) {
+            const int64_t t = t0 + u;
+            const int64_t k = t * KSTEP + 8 * lg;
+            if (t < steps) {
+                rb[u] = load_bt8<GUARD>(Bt, ldbt, n_row, k, N, K);
+                ra[u] = load_a8<true>(A, lda, li, k, M, K);
+            } else {
+                rb[u] = u32x4{0u, 0u, 0u, 0u};
+                ra[u] = u32x4{0u, 0u, 0u, 0u};
+            }
+        }
+    };
+    auto compute_group = [&](const u32x4 (&rb)[BT_U], const u32x4 (&ra)[BT_U]) {
+#pragma unroll
+        for (int u = 0; u < BT_U; ++u)
+            acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, rb[u]),
+                                                         __builtin_bit_cast(f16x8, ra[u]), acc, 0, 0, 0);
+    };
+
+    // Phase kp takes the step groups kp, kp + 2, kp + 4, ... (BT_U steps each).
+    const int64_t stride = (int64_t)BT_PHASES * BT_U;
+    u32x4 rb0[BT_U], rb1[BT_U], ra0[BT_U], ra1[BT_U];
+    int64_t t0 = (int64_t)kp * BT_U;
+    if (t0 < steps) load_group(t0, rb0, ra0);
+    for (; t0 < steps; t0 += 2 * stride) {
+        if (t0 + stride < steps) load_group(t0 + stride, rb1, ra1);
+        compute_group(rb0, ra0);
+        if (t0 + stride >= steps) break;
+        if (t0 + 2 * stride < steps) load_group(t0 + 2 * stride, rb0, ra0);
+        compute_group(rb1, ra1);
+    }
+
+    // acc holds C^T: lane l, register r is the partial sum of C[m][n] with
+    // m = l%16 and n = n_base + 4(l/16) + r.
+#pragma unroll
+    for (int r = 0; r < 4; ++r) red[kp][li][BT_COLS * cg + 4 * lg + r] = acc[r];
+    __syncthreads();
+    for (uint32_t o = tid; o < (uint32_t)(MAX_M * BT_NB); o += 64 * BT_WAVES) {
+        const uint32_t m = o / BT_NB, nl = o % BT_NB;
+        const int64_t n = n_wg + nl;
+        if ((int64_t)m < M && n < N) C[(int64_t)m * ldc + n] = relu_to_f16(red[0][m][nl] + red[1][m][nl]);
+    }
+}
+
+// Bt version with direct-to-LDS copies, for K a multiple of 256: loading MFMA
+// operands straight from global memory (above) reads every Bt row in 64-byte
+// pieces and re-reads A for every column group.  Here a workgroup of 4 waves
+// owns 64 columns; K moves in 256-deep chunks (512 bytes of each Bt row)
+// through a 4-slot LDS ring (all 160 KiB), three chunks ahead:
+//   * each wave copies its own 16 Bt rows (8 global_load_lds_dwordx4 per
+//     chunk, 2 rows x 512 contiguous bytes each) and 4 of the 16 rows of the
+//     A chunk (rows past M read row M-1: they only feed columns of C^T that
+//     are never stored);
+//   * LDS rows are 512 bytes; the 16-byte chunk c of row r sits at slot
+//     c XOR (r % 16) (the permutation is applied on the global side, inside
+//     the row), so the 16 rows a fragment read touches hit 16 bank groups;
+//   * per chunk each wave runs 8 v_mfma_f32_16x16x32_f16 on fragments read
+//     with ds_read_b128, then ReLU, fp16 and the store at the end.
+constexpr int BTL_KC = 256;                    // K per chunk
+constexpr int BTL_ROW_BYTES = BTL_KC * 2;      // 512
+constexpr int BTL_NB = 64;                     // columns (Bt rows) per workgroup
+constexpr int BTL_BT_BYTES = BTL_NB * BTL_ROW_BYTES;  // 32 KiB
+constexpr int BTL_A_BYTES = MAX_M * BTL_ROW_BYTES;    // 8 KiB
+constexpr int BTL_SLOT = BTL_BT_BYTES + BTL_A_BYTES;
+constexpr int BTL_SLOTS = 4;
+constexpr int BTL_COPIES = 10;  // copies per wave per chunk: 8 (Bt) + 2 (A)
+
+template <bool GUARD>
+__global__ __launch_bounds__(256, 1) void gemm_relu_smallm_bt_lds_kernel(
+    const uint16_t* __restrict__ A, const uint16_t* __restrict__ Bt, uint16_t* __restrict__ C, int64_t M, int64_t N,
+    int64_t K, int64_t lda, int64_t ldbt, int64_t ldc) {
+    __shared__ __attribute__((aligned(1024))) uint8_t lds[BTL_SLOTS * BTL_SLOT];
+
+    const uint32_t lane = threadIdx.x & 63u;
+    const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int64_t n_wg = (int64_t)blockIdx.x * BTL_NB;
+
+    // Copy i of a chunk: LDS rows 2i, 2i+1 of the Bt block (this wave: rows
+    // 16w .. 16w+15) or of the A block (rows 4w .. 4w+3); lane -> row
+    // 2i + lane/32, slot lane%32, which holds global chunk slot ^ (row % 16).
+    uint32_t off_bt[8], off_a[2];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const uint32_t row = 16u * wave + 2u * i + (lane >> 5);
+        const uint32_t chunk = (lane & 31u) ^ (row & 15u);
+        int64_t n = n_wg + row;
+        if (GUARD && n >= N) n = N - 1;
+        off_bt[i] = (uint32_t)((n - n_wg) * ldbt * 2 + chunk * 16);
+    }
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        const uint32_t row = 4u * wave + 2u * i + (lane >> 5);
+        const uint32_t chunk = (lane & 31u) ^ (row & 15u);
+        const int64_t m = (int64_t)row < M ? (int64_t)row : M - 1;
+        off_a[i] = (uint32_t)(m * lda * 2 + chunk * 16);
+    }
+    const uint8_t* base_bt = reinterpret_cast<const uint8_t*>(Bt + n_wg * ldbt);
+    const uint8_t* base_a = reinterpret_cast<const uint8_t*>(A);
+    const uint32_t lds_base = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t*)lds);
+    auto issue = [&](int64_t kc) {
+        const uint32_t slot = lds_base + (uint32_t)(kc % BTL_SLOTS) * BTL_SLOT;
+        const int64_t kb = kc * BTL_ROW_BYTES;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) tile2::dma16(base_bt + kb, off_bt[i], slot + (16u * wave + 2u * i) * 512u);
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+            tile2::dma16(base_a + kb, off_a[i], slot + BTL_BT_BYTES + (4u * wave + 2u * i) * 512u);
+    };
+
+    // Fragment addresses: Bt operand of step s = row 16w + l%16, chunk
+    // 4s + l/16; A operand = row l%16, same chunk.
+    const uint32_t li = lane & 15u, lg = lane >> 4;
+    const uint32_t bt_row = 16u * wave + li;
+    f32x4 acc0 = f32x4{}, acc1 = f32x4{};
+
+    const int64_t chunks = K / BTL_KC;
+    for (int64_t c = 0; c < BTL_SLOTS - 1 && c < chunks; ++c) issue(c);
+    for (int64_t kc = 0; kc < chunks; ++kc) {
+        // chunk kc landed; the (up to BTL_SLOTS - 2) chunks after it may still be in flight
+        const int64_t ahead = chunks - 1 - kc < BTL_SLOTS - 2 ? chunks - 1 - kc : BTL_SLOTS - 2;
+        if (ahead >= 2) tile2::wait_vmcnt<2 * BTL_COPIES>();
+        else if (ahead == 1) tile2::wait_vmcnt<BTL_COPIES>();
+        else tile2::wait_vmcnt<0>();
+        tile2::barrier();
+        if (kc + BTL_SLOTS - 1 < chunks) issue(kc + BTL_SLOTS - 1);
+        const uint8_t* slot = lds + (kc % BTL_SLOTS) * BTL_SLOT;
+#pragma unroll
+        for (int st = 0; st < BTL_KC / KSTEP; ++st) {
+            const uint32_t chunk = 4u * st + lg;
+            const f16x8 b = *reinterpret_cast<const f16x8*>(slot + bt_row * 512u + ((chunk ^ (bt_row & 15u)) << 4));
+            const f16x8 a = *reinterpret_cast<const f16x8*>(slot + BTL_BT_BYTES + li * 512u + ((chunk ^ li) << 4));
+            if (st & 1) acc1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(b, a, acc1, 0, 0, 0);
+            else acc0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(b, a, acc0, 0, 0, 0);
+        }
+    }
+
+    // acc holds C^T: lane l, register r is C[m][n] with m = l%16 and
+    // n = n_wg + 16w + 4(l/16) + r.
+    const int64_t m = li;
+    if (m < M) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int64_t n = n_wg + 16 * wave + 4 * lg + r;
+            if (!GUARD || n < N) C[m * ldc + n] = relu_to_f16(acc0[r] + acc1[r]);
+        }
     }
 }
 

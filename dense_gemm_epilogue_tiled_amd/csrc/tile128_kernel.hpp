@@ -68,7 +68,9 @@ __device__ __forceinline__ f16x8 read_b_operand(const GR_LDS uint8_t* p) {
     return __builtin_bit_cast(f16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
 }
 
-template <bool EDGE, bool SPLIT>
+// BT=true: B given transposed (Bt, N x K row-major, pitch ldb), staged and
+// read like A (rows of Bt past N clamped to row N-1).
+template <bool EDGE, bool SPLIT, bool BT = false>
 __global__ __launch_bounds__(THREADS, 2) void gemm_relu_tile128_kernel(
     const uint16_t* __restrict__ A, const uint16_t* __restrict__ B, uint16_t* __restrict__ C, int64_t M, int64_t N,
     int64_t K, int64_t lda, int64_t ldb, int64_t ldc, uint32_t tiles_m, uint32_t tiles_n, uint32_t group_m,
@@ -102,9 +104,9 @@ __global__ __launch_bounds__(THREADS, 2) void gemm_relu_tile128_kernel(
     // A block = 16 rows x 64 bytes; lane -> row lane/4, slot lane%4.
     // B block = 4 rows x 256 bytes; lane -> row lane/16, slot lane%16.
     const uint8_t* base_a = reinterpret_cast<const uint8_t*>(A + m0 * lda + k_begin);
-    const uint8_t* base_b = reinterpret_cast<const uint8_t*>(B + k_begin * ldb + n0);
+    const uint8_t* base_b = reinterpret_cast<const uint8_t*>(BT ? B + n0 * ldb + k_begin : B + k_begin * ldb + n0);
     const int64_t step_a = BK * 2;
-    const int64_t step_b = (int64_t)BK * ldb * 2;
+    const int64_t step_b = BT ? (int64_t)BK * 2 : (int64_t)BK * ldb * 2;
     uint32_t off_a[COPIES], off_b[COPIES];
 #pragma unroll
     for (int i = 0; i < COPIES; ++i) {
@@ -114,10 +116,16 @@ __global__ __launch_bounds__(THREADS, 2) void gemm_relu_tile128_kernel(
         uint32_t ra_src = ra;  // row of A this lane copies into LDS row ra
         if constexpr (EDGE) ra_src = m0 + ra < M ? ra : (uint32_t)(M - 1 - m0);
         off_a[i] = (uint32_t)((ra_src * lda + 8u * ca) * 2);
-        const uint32_t rb = 4u * blk + (lane >> 4);
-        uint32_t cb = (lane & 15u) ^ ((rb & 3u) << 2);
-        if constexpr (EDGE) cb = edge::clamp_chunk(cb, n0, N);
-        off_b[i] = (uint32_t)((rb * ldb + 8u * cb) * 2);
+        if constexpr (BT) {
+            uint32_t rb_src = ra;  // row n0 + ra of Bt, clamped to N-1
+            if constexpr (EDGE) rb_src = n0 + ra < N ? ra : (uint32_t)(N - 1 - n0);
+            off_b[i] = (uint32_t)((rb_src * ldb + 8u * ca) * 2);
+        } else {
+            const uint32_t rb = 4u * blk + (lane >> 4);
+            uint32_t cb = (lane & 15u) ^ ((rb & 3u) << 2);
+            if constexpr (EDGE) cb = edge::clamp_chunk(cb, n0, N);
+            off_b[i] = (uint32_t)((rb * ldb + 8u * cb) * 2);
+        }
     }
     const uint32_t lds_base = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(GR_LDS uint8_t*)lds);
     auto issue = [&](uint32_t kt) {
@@ -147,6 +155,12 @@ __global__ __launch_bounds__(THREADS, 2) void gemm_relu_tile128_kernel(
         const uint32_t n = wn * WAVE_TN + 32u * j + 16u * ((lane >> 4) & 1u) + 4u * (lane & 3u);
         b_ptr[j] = lds_p + A_BYTES + b_off(bk, n >> 3) + 2u * (n & 7u);
     }
+    // BT: B operand of step s, block j: row wn*64 + 32j + lane%32 of the Bt
+    // strip, chunk 2s + lane/32 (A's layout; block j is 2 KiB further on).
+    const uint32_t br = wn * WAVE_TN + (lane & 31u);
+    const GR_LDS uint8_t* bt_ptr[KSUB];
+#pragma unroll
+    for (int s = 0; s < KSUB; ++s) bt_ptr[s] = lds_p + A_BYTES + a_off(br, 2u * s + (lane >> 5));
 
     f32x16 acc[FM][FN];
 #pragma unroll
@@ -174,7 +188,10 @@ __global__ __launch_bounds__(THREADS, 2) void gemm_relu_tile128_kernel(
 #pragma unroll
             for (int i = 0; i < FM; ++i) fa[s][i] = read_a_operand(a_ptr[s] + so + 2048u * i);
 #pragma unroll
-            for (int j = 0; j < FN; ++j) fb[s][j] = read_b_operand(b_ptr[j] + so + 16u * 256u * s);
+            for (int j = 0; j < FN; ++j) {
+                if constexpr (BT) fb[s][j] = read_a_operand(bt_ptr[s] + so + 2048u * j);
+                else fb[s][j] = read_b_operand(b_ptr[j] + so + 16u * 256u * s);
+            }
         }
 #pragma unroll
         for (int s = 0; s < KSUB; ++s)

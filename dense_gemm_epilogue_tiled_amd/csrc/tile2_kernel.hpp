@@ -118,7 +118,11 @@ __device__ __forceinline__ void pin() { __builtin_amdgcn_sched_barrier(0); }
 constexpr int64_t MAX_LDA = (int64_t(1) << 31) / (BM * 2);
 constexpr int64_t MAX_LDB = (int64_t(1) << 31) / (BK * 2);
 
-template <bool EDGE>
+// BT=true: B is given transposed (Bt, N x K row-major, pitch ldb): its strips
+// [256 n][32 k] are staged exactly like A's (64-byte rows, chunk XOR (n/4)%4)
+// and its fragments are read like A's (ds_read_b128); rows of Bt past N are
+// clamped to row N-1 (their columns are never stored).
+template <bool EDGE, bool BT = false>
 __global__ __launch_bounds__(THREADS, 1) void gemm_relu_tile2_kernel(
     const uint16_t* __restrict__ A, const uint16_t* __restrict__ B, uint16_t* __restrict__ C, int64_t M, int64_t N,
     int64_t K, int64_t lda, int64_t ldb, int64_t ldc, uint32_t tiles_m, uint32_t tiles_n, uint32_t group_m,
@@ -142,9 +146,9 @@ __global__ __launch_bounds__(THREADS, 1) void gemm_relu_tile2_kernel(
     // B block = 2 rows x 512 bytes; lane -> row lane/32, slot lane%32.
     // Wave-uniform bases (advanced one strip per step) + per-lane offsets.
     const uint8_t* base_a = reinterpret_cast<const uint8_t*>(A + m0 * lda);
-    const uint8_t* base_b = reinterpret_cast<const uint8_t*>(B + n0);
+    const uint8_t* base_b = reinterpret_cast<const uint8_t*>(BT ? B + n0 * ldb : B + n0);
     const int64_t step_a = BK * 2;
-    const int64_t step_b = (int64_t)BK * ldb * 2;
+    const int64_t step_b = BT ? (int64_t)BK * 2 : (int64_t)BK * ldb * 2;
     uint32_t off_a[COPIES], off_b[COPIES];
 #pragma unroll
     for (int i = 0; i < COPIES; ++i) {
@@ -152,10 +156,16 @@ __global__ __launch_bounds__(THREADS, 1) void gemm_relu_tile2_kernel(
         const uint32_t ra = 16u * blk + (lane >> 2);
         const uint32_t ca = (lane & 3u) ^ ((ra >> 2) & 3u);
         off_a[i] = (uint32_t)((ra * lda + 8u * ca) * 2);
-        const uint32_t rb = 2u * blk + (lane >> 5);
-        uint32_t cb = (lane & 31u) ^ ((rb & 3u) << 2);
-        if constexpr (EDGE) cb = edge::clamp_chunk(cb, n0, N);
-        off_b[i] = (uint32_t)((rb * ldb + 8u * cb) * 2);
+        if constexpr (BT) {
+            uint32_t rb_src = ra;  // row n0 + ra of Bt, clamped to N-1
+            if constexpr (EDGE) rb_src = n0 + ra < N ? ra : (uint32_t)(N - 1 - n0);
+            off_b[i] = (uint32_t)((rb_src * ldb + 8u * ca) * 2);
+        } else {
+            const uint32_t rb = 2u * blk + (lane >> 5);
+            uint32_t cb = (lane & 31u) ^ ((rb & 3u) << 2);
+            if constexpr (EDGE) cb = edge::clamp_chunk(cb, n0, N);
+            off_b[i] = (uint32_t)((rb * ldb + 8u * cb) * 2);
+        }
     }
     const uint32_t lds_base = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(GR_LDS uint8_t*)lds);
 
@@ -193,6 +203,12 @@ __global__ __launch_bounds__(THREADS, 1) void gemm_relu_tile2_kernel(
         const uint32_t n = wn * WAVE_TN + 32u * j + 16u * ((lane >> 4) & 1u) + 4u * (lane & 3u);
         b_ptr[j] = lds_p + A_BYTES + b_off(bk, n >> 3) + 2u * (n & 7u);
     }
+    // BT: B operand of step s, block j is row wn*128 + 32j + lane%32 of the
+    // Bt strip, chunk 2s + lane/32 (block j is 2 KiB further on).
+    const uint32_t br = wn * WAVE_TN + (lane & 31u);
+    const GR_LDS uint8_t* bt_ptr[KSUB];
+#pragma unroll
+    for (int s = 0; s < KSUB; ++s) bt_ptr[s] = lds_p + A_BYTES + a_off(br, 2u * s + (lane >> 5));
 
     f32x16 acc[FM][FN];
 #pragma unroll
@@ -210,7 +226,8 @@ __global__ __launch_bounds__(THREADS, 1) void gemm_relu_tile2_kernel(
             f.a[s][0] = read_a_operand(a_ptr[s] + so);
         } else if (q <= 4) {
             const int j = q - 1;
-            f.b[s][j] = read_b_operand(b_ptr[j] + so + 8192u * s);
+            if constexpr (BT) f.b[s][j] = read_a_operand(bt_ptr[s] + so + 2048u * j);
+            else f.b[s][j] = read_b_operand(b_ptr[j] + so + 8192u * s);
         } else {
             const int i = q - 4;
             f.a[s][i] = read_a_operand(a_ptr[s] + so + 2048u * i);

@@ -109,7 +109,10 @@ __device__ __forceinline__ u32x4 load8(const uint16_t* base, int64_t ld, int64_t
     }
 }
 
-template <bool GUARD, int VA, int VB>
+// BT=true: B is given transposed (Bt, N x K row-major, pitch ldb); its
+// chunks are loaded like A's (rows n, 8 consecutive k) and stored as they
+// are, since the LDS B tile is k-contiguous already.
+template <bool GUARD, int VA, int VB, bool BT = false>
 __global__ __launch_bounds__(THREADS, 1) void gemm_relu_tile_kernel(
     const uint16_t* __restrict__ A, const uint16_t* __restrict__ B, uint16_t* __restrict__ C,
     int64_t M, int64_t N, int64_t K, int64_t lda, int64_t ldb, int64_t ldc,
@@ -143,8 +146,10 @@ __global__ __launch_bounds__(THREADS, 1) void gemm_relu_tile_kernel(
         for (int j = 0; j < 8; ++j)
             ra[j] = load8<GUARD, VA>(A, lda, m0 + a_row + 32 * j, k0 + 8 * a_chunk, M, K);
 #pragma unroll
-        for (int r = 0; r < 8; ++r)
-            rb[r] = load8<GUARD, VB>(B, ldb, k0 + 8 * b_kb + r, n0 + 8 * b_ng, K, N);
+        for (int r = 0; r < 8; ++r) {
+            if constexpr (BT) rb[r] = load8<GUARD, VB>(B, ldb, n0 + a_row + 32 * r, k0 + 8 * a_chunk, N, K);
+            else rb[r] = load8<GUARD, VB>(B, ldb, k0 + 8 * b_kb + r, n0 + 8 * b_ng, K, N);
+        }
     };
 
     auto store_tiles = [&](uint32_t stage) {
@@ -153,13 +158,19 @@ __global__ __launch_bounds__(THREADS, 1) void gemm_relu_tile_kernel(
 #pragma unroll
         for (int j = 0; j < 8; ++j)
             *reinterpret_cast<u32x4*>(sa + lds_chunk(a_row + 32 * j, a_chunk)) = ra[j];
-        // Transpose the 8 (k) x 8 (n) block: column c becomes one k-chunk.
+        if constexpr (BT) {
 #pragma unroll
-        for (int c = 0; c < 8; ++c) {
-            u32x4 o;
+            for (int j = 0; j < 8; ++j)
+                *reinterpret_cast<u32x4*>(sb + lds_chunk(a_row + 32 * j, a_chunk)) = rb[j];
+        } else {
+            // Transpose the 8 (k) x 8 (n) block: column c becomes one k-chunk.
 #pragma unroll
-            for (int d = 0; d < 4; ++d) o[d] = pair_halves(rb[2 * d][c >> 1], rb[2 * d + 1][c >> 1], c & 1);
-            *reinterpret_cast<u32x4*>(sb + lds_chunk(8 * b_ng + c, b_kb)) = o;
+            for (int c = 0; c < 8; ++c) {
+                u32x4 o;
+#pragma unroll
+                for (int d = 0; d < 4; ++d) o[d] = pair_halves(rb[2 * d][c >> 1], rb[2 * d + 1][c >> 1], c & 1);
+                *reinterpret_cast<u32x4*>(sb + lds_chunk(8 * b_ng + c, b_kb)) = o;
+            }
         }
     };
 

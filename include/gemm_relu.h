@@ -234,6 +234,45 @@ int gemm_relu_f16_plan_ws(int64_t M, int64_t N, int64_t K,
                           const uint16_t* C, int64_t ldc,
                           int64_t workspace_bytes, gr_plan_t* out);
 
+/*
+ * ---- B given transposed -----------------------------------------------------
+ * The same operation with B stored as its transpose Bt (N x K row-major,
+ * element (n, k) at Bt[n*ldbt + k], pitch ldbt >= max(1, K)): C := ReLU(A *
+ * Bt^T).  This is the layout of a weight matrix in the GEMV pattern of "Tilelang
+ * Cuda Patterns", section 4 (B as N x K, each output a dot product of two
+ * contiguous rows) and of the B_T option of the tutorial's GEMM.  Every
+ * convention above holds, with Bt in the place of B; the paths are:
+ *   GR_PATH_SMALL_M   M <= 16, 16-byte rows of A and Bt: each wave streams 16
+ *                     rows of Bt, whose 16-byte pieces are MFMA operands as
+ *                     they stand;
+ *   GR_PATH_TILE      16-byte rows of A and Bt, K % 32 == 0, pitches of at
+ *                     most 2^22 elements: the pipelined kernel with Bt staged
+ *                     like A;
+ *   GR_PATH_TILE_EDGE everything else (guarded register-staged kernel).
+ * There is no workspace variant.
+ */
+int gemm_relu_f16_bt(int64_t M, int64_t N, int64_t K,
+                     const uint16_t* A, int64_t lda,
+                     const uint16_t* Bt, int64_t ldbt,
+                     uint16_t* C, int64_t ldc,
+                     void* stream);
+
+/* Pure planner for gemm_relu_f16_bt (no GPU needed); see gemm_relu_f16_plan. */
+int gemm_relu_f16_bt_plan(int64_t M, int64_t N, int64_t K,
+                          const uint16_t* A, int64_t lda,
+                          const uint16_t* Bt, int64_t ldbt,
+                          const uint16_t* C, int64_t ldc,
+                          gr_plan_t* out);
+
+/* gemm_relu_f16_bt on a given path (GR_PATH_TILE, GR_PATH_TILE_EDGE or
+   GR_PATH_SMALL_M; GR_ERR_INVALID_PATH when the path's conditions do not
+   hold).  Test hook. */
+int gemm_relu_f16_bt_forced(int64_t M, int64_t N, int64_t K,
+                            const uint16_t* A, int64_t lda,
+                            const uint16_t* Bt, int64_t ldbt,
+                            uint16_t* C, int64_t ldc,
+                            void* stream, int path);
+
 /* Static, NUL-terminated name of a status code ("GR_OK", "GR_ERR_ALIAS", ...).
    Unknown codes give "GR_ERR_UNKNOWN". */
 const char* gemm_relu_status_string(int status);

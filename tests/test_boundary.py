@@ -362,6 +362,40 @@ def test_planner_invariants_on_random_problems():
                 assert pw["workspace"] >= 4 * M * N * pw["split_k"], key
 
 
+def plan_bt(M, N, K, lda=None, ldbt=None, ldc=None, a=BASE_A, b=BASE_B, c=BASE_C):
+    lda = max(K, 1) if lda is None else lda
+    ldbt = max(K, 1) if ldbt is None else ldbt
+    ldc = max(N, 1) if ldc is None else ldc
+    return gr.gemm_relu_f16_bt_plan(M, N, K, a, lda, b, ldbt, c, ldc)
+
+
+def test_transposed_b_planner_and_checks():
+    # Bt is N x K: its pitch is checked against K, its span is N rows
+    assert plan_bt(8, 8, 8, ldbt=7)[0] == gr.GR_ERR_INVALID_LD
+    assert plan_bt(8, 100, 8, ldbt=8)[0] == gr.GR_OK
+    assert plan_bt(8, 8, 8, b=0)[0] == gr.GR_ERR_NULL_PTR
+    assert plan_bt(8, 8, 8, c=BASE_B + 2 * 8 * 7)[0] == gr.GR_ERR_ALIAS
+    assert plan_bt(8, 8, 8, c=BASE_B + 2 * 8 * 8)[0] == gr.GR_OK
+    # paths
+    st, p = plan_bt(8, 16384, 8192)
+    assert p["path"] == gr.GR_PATH_SMALL_M and p["grid"] == 16384 // 64
+    st, p = plan_bt(4096, 4096, 4096)
+    assert p["path"] == gr.GR_PATH_TILE and p["block_m"] == 256 and p["grid"] == 256
+    st, p = plan_bt(1024, 1024, 1024)
+    assert p["path"] == gr.GR_PATH_TILE and p["block_m"] == 128
+    assert plan_bt(4096, 4096, 4100)[1]["path"] == gr.GR_PATH_TILE_EDGE          # K % 32 != 0
+    assert plan_bt(4096, 4096, 4096, ldbt=4100)[1]["path"] == gr.GR_PATH_TILE_EDGE  # Bt rows not 16-B
+    assert plan_bt(8, 4096, 4096, b=BASE_B + 8)[1]["path"] == gr.GR_PATH_TILE_EDGE  # Bt rows not 16-B
+    assert plan_bt(0, 4096, 4096)[1]["path"] == gr.GR_PATH_NONE
+    # forced paths are checked
+    assert gr.gemm_relu_f16_bt_forced(300, 256, 48, BASE_A, 48, BASE_B, 48, BASE_C, 256, None,
+                                      gr.GR_PATH_TILE) == gr.GR_ERR_INVALID_PATH
+    assert gr.gemm_relu_f16_bt_forced(64, 256, 64, BASE_A, 64, BASE_B, 64, BASE_C, 256, None,
+                                      gr.GR_PATH_SMALL_M) == gr.GR_ERR_INVALID_PATH
+    assert gr.gemm_relu_f16_bt_forced(8, 256, 64, BASE_A, 64, BASE_B, 64, BASE_C, 256, None,
+                                      gr.GR_PATH_TILE_PACKED) == gr.GR_ERR_INVALID_PATH
+
+
 def test_plan_null_output_struct():
     lib = gr.lib()
     assert lib.gemm_relu_f16_plan(8, 8, 8, BASE_A, 8, BASE_B, 8, BASE_C, 8, None) == gr.GR_ERR_INVALID_ARG

@@ -589,6 +589,105 @@ def test_random_problems_against_oracle(case):
     assert np.all(Cw[:, N:] == SENTINEL)
 
 
+# ---- B given transposed (Bt, N x K) --------------------------------------------
+
+def run_bt(A, Bt, M, N, K, lda, ldbt, ldc, path=None, c_rows=None, offsets=(0, 0, 0)):
+    import torch as t
+    dA, dBt = to_dev(A), to_dev(Bt)
+    rows = M if c_rows is None else c_rows
+    dC = full_dev((rows * ldc + offsets[2] + 8,), SENTINEL)
+    a = dA.data_ptr() + 2 * offsets[0]
+    b = dBt.data_ptr() + 2 * offsets[1]
+    c = dC.data_ptr() + 2 * offsets[2]
+    s = t.cuda.current_stream().cuda_stream
+    log("bt M=%d N=%d K=%d lda=%d ldbt=%d ldc=%d path=%s offsets=%s" % (M, N, K, lda, ldbt, ldc, path, offsets))
+    if path is None:
+        st = gr.gemm_relu_f16_bt(M, N, K, a, lda, b, ldbt, c, ldc, s)
+    else:
+        st = gr.gemm_relu_f16_bt_forced(M, N, K, a, lda, b, ldbt, c, ldc, s, path)
+    t.cuda.synchronize()
+    assert st == gr.GR_OK, gr.gemm_relu_status_string(st)
+    return from_dev(dC)
+
+
+def bt_operands(M, N, K, seed, lda, ldbt, b_scale=None):
+    """A (M x lda) and Bt (N x ldbt), padding poisoned, plus the K x N B the
+    oracle takes (the transpose of Bt's first K columns)."""
+    A, B = synth.random_operands(M, N, K, seed=seed, lda=lda, b_scale=b_scale)
+    Bt = np.full((N, max(ldbt, 1)), 0x7BFF, dtype=np.uint16)
+    Bt[:, :K] = B[:, :N].T
+    return A, Bt, np.ascontiguousarray(Bt[:, :K].T)
+
+
+BT_CASES = [
+    # M, N, K, lda, ldbt, ldc, expected path
+    (8, 16384, 8192, 8192, 8192, 16384, gr.GR_PATH_SMALL_M),   # the small-M workload's shape
+    (16, 1000, 1000, 1000, 1000, 1000, gr.GR_PATH_SMALL_M),    # K % 32 != 0: guarded loads
+    (16, 1000, 1024, 1032, 1032, 1001, gr.GR_PATH_SMALL_M),    # partial wave of columns, padding
+    (1, 100, 96, 96, 96, 100, gr.GR_PATH_SMALL_M),
+    (5, 4096, 256, 256, 264, 4096, gr.GR_PATH_SMALL_M),        # one 256-deep chunk, padded Bt
+    (3, 64, 512, 520, 512, 65, gr.GR_PATH_SMALL_M),            # one workgroup, two chunks, odd ldc
+    (512, 768, 256, 256, 256, 768, gr.GR_PATH_TILE),           # 128 x 128 tiles
+    (4096, 2304, 512, 512, 520, 2304, gr.GR_PATH_TILE),        # 256 x 256 tiles, padded Bt
+    (300, 250, 96, 104, 96, 251, gr.GR_PATH_TILE),             # partial tiles, rows of Bt clamped
+    (2400, 4000, 96, 96, 96, 4001, gr.GR_PATH_TILE),           # large partial tiles
+    (17, 264, 64, 72, 64, 265, gr.GR_PATH_TILE),
+    (300, 270, 100, 109, 105, 273, gr.GR_PATH_TILE_EDGE),      # odd pitches
+]
+
+
+@pytest.mark.parametrize("M,N,K,lda,ldbt,ldc,path", BT_CASES)
+def test_transposed_b_parity(M, N, K, lda, ldbt, ldc, path):
+    """gemm_relu_f16_bt against the oracle on the transposed operand (full),
+    with poisoned padding and C canaries; the guarded kernel on the same
+    input gives the same bits as the pipelined one (same k order)."""
+    st, plan = gr.gemm_relu_f16_bt_plan(M, N, K, 0x100000, lda, 0x200000000000, ldbt, 0x400000000000, ldc)
+    assert st == gr.GR_OK and plan["path"] == path, plan
+    A, Bt, B = bt_operands(M, N, K, seed=M + N + K + 5, lda=lda, ldbt=ldbt, b_scale=K ** -0.5)
+    extra = 2
+    C1 = run_bt(A, Bt, M, N, K, lda, ldbt, ldc, c_rows=M + extra)
+    C = C1[:M * ldc].reshape(M, ldc)
+    assert_parity(C[:, :N], oracle.gemm_relu_full(A, B, M=M, N=N, K=K, lda=lda, ldb=N),
+                  "bt %dx%dx%d" % (M, N, K))
+    assert np.all(C[:, N:] == SENTINEL) and np.all(C1[M * ldc:] == SENTINEL)
+    if path == gr.GR_PATH_TILE:
+        C2 = run_bt(A, Bt, M, N, K, lda, ldbt, ldc, c_rows=M + extra, path=gr.GR_PATH_TILE_EDGE)
+        assert np.array_equal(C1, C2)
+
+
+@pytest.mark.parametrize("M,N,K", [(512, 768, 256), (4096, 2304, 256), (300, 250, 96)])
+def test_transposed_b_matches_plain_layout_bitwise(M, N, K):
+    """The same product through B (K x N) and through Bt (N x K) gives the same
+    bits: both layouts feed the same MFMA sequence."""
+    A, Bt, B = bt_operands(M, N, K, seed=K + 3, lda=K, ldbt=K)
+    Cbt = run_bt(A, Bt, M, N, K, K, K, N)
+    Cnn = run_full(A, B, M, N, K)
+    assert np.array_equal(Cbt[:M * N], Cnn[:M * N])
+
+
+@pytest.mark.parametrize("offs", [(1, 0, 0), (0, 3, 0), (5, 7, 1)])
+def test_transposed_b_unaligned_base_pointers(offs):
+    M, N, K = 320, 288, 96
+    A, Bt, B = bt_operands(M, N, K, seed=sum(offs), lda=K, ldbt=K)
+    Ap = np.concatenate([np.zeros(offs[0], np.uint16), A.ravel(), np.zeros(8, np.uint16)])
+    Btp = np.concatenate([np.zeros(offs[1], np.uint16), Bt.ravel(), np.zeros(8, np.uint16)])
+    Cflat = run_bt(Ap, Btp, M, N, K, K, K, N, offsets=offs)
+    C = Cflat[offs[2]:offs[2] + M * N].reshape(M, N)
+    assert_parity(C, oracle.gemm_relu_full(A, B), "bt offsets %s" % (offs,))
+    assert np.all(Cflat[:offs[2]] == SENTINEL) and np.all(Cflat[offs[2] + M * N:] == SENTINEL)
+
+
+def test_transposed_b_tensor_wrapper():
+    t = pytest.importorskip("torch")
+    M, N, K = 300, 200, 128
+    A, Bt, B = bt_operands(M, N, K, seed=91, lda=K, ldbt=K)
+    a = to_dev(A).view(t.float16).reshape(M, K)
+    bt = to_dev(Bt).view(t.float16).reshape(N, K)
+    c = gr.gemm_relu_bt(a, bt)
+    t.cuda.synchronize()
+    assert_parity(c.view(t.int16).cpu().numpy().view(np.uint16), oracle.gemm_relu_full(A, B), "bt wrapper")
+
+
 def test_runs_on_a_side_stream():
     t = pytest.importorskip("torch")
     M, N, K = 512, 512, 256
