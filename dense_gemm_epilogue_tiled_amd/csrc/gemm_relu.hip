@@ -668,6 +668,14 @@ int run_bt(const gr_plan_t& p, int64_t M, int64_t N, int64_t K, const uint16_t* 
                 return launch(gemm_relu_tile128_kernel<true, false, true>, p.grid, THREADS, stream, A, Bt, C, M, N,
                               K, lda, ldbt, ldc, tiles_m, tiles_n, gm, vc, no_part, no_split);
             }
+            if (K % gr::tile3::BKA == 0) {
+                using namespace gr::tile3;
+                if (whole)
+                    return launch(gemm_relu_tile3_kernel<false, true>, p.grid, THREADS, stream, A, Bt, C, M, N, K,
+                                  lda, ldbt, ldc, tiles_m, tiles_n, gm, vc);
+                return launch(gemm_relu_tile3_kernel<true, true>, p.grid, THREADS, stream, A, Bt, C, M, N, K, lda,
+                              ldbt, ldc, tiles_m, tiles_n, gm, vc);
+            }
             using namespace gr::tile2;
             if (whole)
                 return launch(gemm_relu_tile2_kernel<false, true>, p.grid, THREADS, stream, A, Bt, C, M, N, K, lda,

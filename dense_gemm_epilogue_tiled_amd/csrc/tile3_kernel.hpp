@@ -60,7 +60,11 @@ struct Frags {
     f16x8 b[KSUB][FN];
 };
 
-template <bool EDGE>
+// BT=true: B given transposed (Bt, N x K row-major, pitch ldb); its 32-deep
+// strips [256 n][32 k] are staged like the 32-deep kernel's A strips (64-byte
+// rows, chunk XOR (n/4)%4, same 16 KiB slots) and its fragments are read with
+// ds_read_b128; rows of Bt past N are clamped to row N-1.
+template <bool EDGE, bool BT = false>
 __global__ __launch_bounds__(THREADS, 1) void gemm_relu_tile3_kernel(
     const uint16_t* __restrict__ A, const uint16_t* __restrict__ B, uint16_t* __restrict__ C, int64_t M, int64_t N,
     int64_t K, int64_t lda, int64_t ldb, int64_t ldc, uint32_t tiles_m, uint32_t tiles_n, uint32_t group_m,
@@ -94,9 +98,9 @@ __global__ __launch_bounds__(THREADS, 1) void gemm_relu_tile3_kernel(
     // B strip (16 KiB) = 16 blocks of 2 rows x 512 bytes; this wave fills
     // blocks 4w .. 4w+3.  lane -> row lane/32, slot lane%32.
     const uint8_t* base_a = reinterpret_cast<const uint8_t*>(A + m0 * lda);
-    const uint8_t* base_b = reinterpret_cast<const uint8_t*>(B + n0);
+    const uint8_t* base_b = reinterpret_cast<const uint8_t*>(BT ? B + n0 * ldb : B + n0);
     const int64_t step_a = BKA * 2;
-    const int64_t step_b = (int64_t)BK * ldb * 2;
+    const int64_t step_b = BT ? (int64_t)BK * 2 : (int64_t)BK * ldb * 2;
     // The odd-step half (blocks +4, rows +32) only adds a wave-uniform
     // 32-row offset: the chunk XOR term, (row/2)%8, is unchanged by it.
     uint32_t off_a[4], off_b[4];
@@ -111,10 +115,19 @@ __global__ __launch_bounds__(THREADS, 1) void gemm_relu_tile3_kernel(
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         const uint32_t blk = 4u * wave + (uint32_t)i;
-        const uint32_t rb = 2u * blk + (lane >> 5);
-        uint32_t cb = (lane & 31u) ^ ((rb & 3u) << 2);
-        if constexpr (EDGE) cb = edge::clamp_chunk(cb, n0, N);
-        off_b[i] = (uint32_t)((rb * ldb + 8u * cb) * 2);
+        if constexpr (BT) {
+            // block = 16 rows of Bt x 64 bytes; lane -> row lane/4, slot lane%4
+            const uint32_t rn = 16u * blk + (lane >> 2);
+            const uint32_t cn = (lane & 3u) ^ ((rn >> 2) & 3u);
+            uint32_t rn_src = rn;
+            if constexpr (EDGE) rn_src = n0 + rn < N ? rn : (uint32_t)(N - 1 - n0);
+            off_b[i] = (uint32_t)((rn_src * ldb + 8u * cn) * 2);
+        } else {
+            const uint32_t rb = 2u * blk + (lane >> 5);
+            uint32_t cb = (lane & 31u) ^ ((rb & 3u) << 2);
+            if constexpr (EDGE) cb = edge::clamp_chunk(cb, n0, N);
+            off_b[i] = (uint32_t)((rb * ldb + 8u * cb) * 2);
+        }
     }
     const uint32_t lds_base = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(GR_LDS uint8_t*)lds);
 
@@ -149,6 +162,12 @@ __global__ __launch_bounds__(THREADS, 1) void gemm_relu_tile3_kernel(
         const uint32_t n = wn * WAVE_TN + 32u * j + 16u * ((lane >> 4) & 1u) + 4u * (lane & 3u);
         b_ptr[j] = lds_p + b_off(bk, n >> 3) + 2u * (n & 7u);
     }
+    // BT: B operand of step s, block j is row wn*128 + 32j + lane%32 of the
+    // Bt strip, chunk 2s + lane/32 (block j is 2 KiB further on).
+    const uint32_t br = wn * WAVE_TN + (lane & 31u);
+    const GR_LDS uint8_t* bt_ptr[KSUB];
+#pragma unroll
+    for (int s = 0; s < KSUB; ++s) bt_ptr[s] = lds_p + tile2::a_off(br, 2u * s + (lane >> 5));
 
     f32x16 acc[FM][FN];
 #pragma unroll
@@ -168,7 +187,8 @@ __global__ __launch_bounds__(THREADS, 1) void gemm_relu_tile3_kernel(
             f.a[s][i] = read_a_operand((const GR_LDS uint8_t*)(uintptr_t)addr);
         } else {
             const int j = q - 1;
-            f.b[s][j] = read_b_operand(b_ptr[j] + bo + 8192u * s);
+            if constexpr (BT) f.b[s][j] = read_a_operand(bt_ptr[s] + bo + 2048u * j);
+            else f.b[s][j] = read_b_operand(b_ptr[j] + bo + 8192u * s);
         }
     };
     auto a_slot = [&](uint32_t kt) { return ((kt >> 1) % A_SLOTS) * A_SLOT_BYTES; };
