@@ -11,11 +11,13 @@ timed on a bounded sample of the same workload.
 
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
                   [--no-workloads] [--workload NAME] [--copy-probe MIB]
-                  [--vendor-reference]
+                  [--vendor-reference] [--extra-shapes]
 
 ``--copy-probe`` runs only a device-to-device copy of known size; it is what
 the HBM-traffic counters are calibrated against.  ``--vendor-reference`` only
-times torch.mm + relu_ (the vendor BLAS) on the same workloads, for context.
+times torch.mm + relu_ (the vendor BLAS) on the same workloads, for context;
+``--extra-shapes`` times the library (and torch.mm + relu_) on shapes beyond
+the workloads: mid-M, narrow small-M, long K, B given transposed.
 """
 from __future__ import annotations
 
@@ -260,6 +262,54 @@ def vendor_reference(torch, reps=30):
     print(json.dumps({"vendor_reference": out, "what": "torch.mm + torch.relu_ (hipBLASLt), warm, context only"}))
 
 
+EXTRA_SHAPES = [
+    # (label, M, N, K, layout) -- shapes beyond the workloads, for the paths they exercise
+    ("mid-M", 64, 4096, 4096, "nn"),
+    ("narrow small-M", 8, 4096, 8192, "nn"),
+    ("long K, few tiles", 1024, 1024, 16384, "nn"),
+    ("B transposed, square", 4096, 4096, 4096, "bt"),
+    ("B transposed, small-M", 8, 16384, 8192, "bt"),
+    ("B transposed, narrow small-M", 16, 4096, 4096, "bt"),
+]
+
+
+def extra_shapes(gr, torch, reps=30):
+    """Context only: library calls on shapes beyond the workloads (without and
+    with the workspace the library asks for; B given transposed through the
+    _bt calls) next to torch.mm + relu_. Warm, HIP events per launch."""
+    out = []
+    stream = torch.cuda.current_stream()
+    for label, M, N, K, layout in EXTRA_SHAPES:
+        g = torch.Generator(device="cuda").manual_seed(M + N + K)
+        A = torch.randn(M, K, generator=g, device="cuda").half()
+        B = (torch.randn(K, N, generator=g, device="cuda") * K ** -0.5).half()
+        C = torch.empty(M, N, device="cuda", dtype=torch.float16)
+        row = {"shape": "%dx%dx%d" % (M, N, K), "what": label, "layout": layout}
+        runs = {}
+        if layout == "bt":
+            Bt = B.t().contiguous()
+            runs["ours"] = lambda: gr.gemm_relu_bt(A, Bt, C, stream)
+            runs["vendor"] = lambda: torch.relu_(torch.mm(A, Bt.t(), out=C))
+        else:
+            st, size = gr.gemm_relu_f16_workspace_size(M, N, K, A.data_ptr(), K, B.data_ptr(), N, C.data_ptr(), N)
+            ws = torch.empty(size, dtype=torch.uint8, device="cuda") if size else None
+            runs["ours"] = lambda: gr.gemm_relu(A, B, C, stream, workspace=None)
+            if ws is not None:
+                runs["ours_ws"] = lambda: gr.gemm_relu(A, B, C, stream, workspace=ws)
+                row["workspace_bytes"] = size
+            runs["vendor"] = lambda: torch.relu_(torch.mm(A, B, out=C))
+        for name, run in runs.items():
+            for _ in range(5):
+                run()
+            torch.cuda.synchronize()
+            row[name + "_us"] = round(statistics.median(time_launches(torch, run, stream, reps)) * 1e3, 2)
+        out.append(row)
+        print("[extra] %s" % row, file=sys.stderr, flush=True)
+        del A, B, C
+        torch.cuda.empty_cache()
+    print(json.dumps({"extra_shapes": out, "what": "library calls vs torch.mm + relu_, warm, context only"}))
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -271,6 +321,8 @@ def main():
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB")
     ap.add_argument("--vendor-reference", action="store_true",
                     help="only time torch.mm + relu_ on the workloads (context, not the product)")
+    ap.add_argument("--extra-shapes", action="store_true",
+                    help="only time the library and torch.mm + relu_ on shapes beyond the workloads")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -295,6 +347,9 @@ def main():
         return
     if args.vendor_reference:
         vendor_reference(torch)
+        return
+    if args.extra_shapes:
+        extra_shapes(gr, torch)
         return
 
     w = synth.WORKLOADS[args.workload]
