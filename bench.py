@@ -270,6 +270,10 @@ EXTRA_SHAPES = [
     ("B transposed, square", 4096, 4096, 4096, "bt"),
     ("B transposed, small-M", 8, 16384, 8192, "bt"),
     ("B transposed, narrow small-M", 16, 4096, 4096, "bt"),
+    ("bfloat16, square", 4096, 4096, 4096, "bf16"),
+    ("bfloat16, square 1024", 1024, 1024, 1024, "bf16"),
+    ("bfloat16, MLP projection", 8192, 28672, 8192, "bf16"),
+    ("bfloat16, small-M", 8, 16384, 8192, "bf16"),
 ]
 
 
@@ -281,12 +285,16 @@ def extra_shapes(gr, torch, reps=30):
     stream = torch.cuda.current_stream()
     for label, M, N, K, layout in EXTRA_SHAPES:
         g = torch.Generator(device="cuda").manual_seed(M + N + K)
-        A = torch.randn(M, K, generator=g, device="cuda").half()
-        B = (torch.randn(K, N, generator=g, device="cuda") * K ** -0.5).half()
-        C = torch.empty(M, N, device="cuda", dtype=torch.float16)
+        dt = torch.bfloat16 if layout == "bf16" else torch.float16
+        A = torch.randn(M, K, generator=g, device="cuda").to(dt)
+        B = (torch.randn(K, N, generator=g, device="cuda") * K ** -0.5).to(dt)
+        C = torch.empty(M, N, device="cuda", dtype=dt)
         row = {"shape": "%dx%dx%d" % (M, N, K), "what": label, "layout": layout}
         runs = {}
-        if layout == "bt":
+        if layout == "bf16":
+            runs["ours"] = lambda: gr.gemm_relu(A, B, C, stream, workspace=None)
+            runs["vendor"] = lambda: torch.relu_(torch.mm(A, B, out=C))
+        elif layout == "bt":
             Bt = B.t().contiguous()
             runs["ours"] = lambda: gr.gemm_relu_bt(A, Bt, C, stream)
             runs["vendor"] = lambda: torch.relu_(torch.mm(A, Bt.t(), out=C))
@@ -302,7 +310,9 @@ def extra_shapes(gr, torch, reps=30):
             for _ in range(5):
                 run()
             torch.cuda.synchronize()
-            row[name + "_us"] = round(statistics.median(time_launches(torch, run, stream, reps)) * 1e3, 2)
+            med_ms = statistics.median(time_launches(torch, run, stream, reps))
+            row[name + "_us"] = round(med_ms * 1e3, 2)
+            row[name + "_tflops"] = round(2.0 * M * N * K / (med_ms * 1e-3) / 1e12, 1)
         out.append(row)
         print("[extra] %s" % row, file=sys.stderr, flush=True)
         del A, B, C

@@ -101,6 +101,10 @@ def lib() -> ctypes.CDLL:
             l.gemm_relu_f16_bt_forced.restype = i32
             l.gemm_relu_f16_bt_plan.argtypes = [i64, i64, i64, p, i64, p, i64, p, i64, ctypes.POINTER(gr_plan_t)]
             l.gemm_relu_f16_bt_plan.restype = i32
+            l.gemm_relu_bf16.argtypes = [i64, i64, i64, p, i64, p, i64, p, i64, p]
+            l.gemm_relu_bf16.restype = i32
+            l.gemm_relu_bf16_forced.argtypes = [i64, i64, i64, p, i64, p, i64, p, i64, p, i32]
+            l.gemm_relu_bf16_forced.restype = i32
             l.gemm_relu_status_string.argtypes = [i32]
             l.gemm_relu_status_string.restype = ctypes.c_char_p
             l.gemm_relu_version.argtypes = []
@@ -179,6 +183,16 @@ def gemm_relu_f16_bt_plan(M, N, K, A, lda, Bt, ldbt, C, ldc):
     return st, _plan_dict(plan)
 
 
+def gemm_relu_bf16(M, N, K, A, lda, B, ldb, C, ldc, stream=None) -> int:
+    """C := ReLU(A.B) with bfloat16 operands and result (device pointers as ints)."""
+    return lib().gemm_relu_bf16(M, N, K, _ptr(A), lda, _ptr(B), ldb, _ptr(C), ldc, _ptr(stream))
+
+
+def gemm_relu_bf16_forced(M, N, K, A, lda, B, ldb, C, ldc, stream=None, path=GR_PATH_TILE_EDGE) -> int:
+    """As gemm_relu_bf16 but on the given path (GR_PATH_TILE, _TILE_EDGE or _SMALL_M)."""
+    return lib().gemm_relu_bf16_forced(M, N, K, _ptr(A), lda, _ptr(B), ldb, _ptr(C), ldc, _ptr(stream), path)
+
+
 def gemm_relu_status_string(status: int) -> str:
     return lib().gemm_relu_status_string(int(status)).decode()
 
@@ -224,23 +238,26 @@ def gemm_relu_bt(a, bt, out=None, stream=None, path=None):
 
 
 def gemm_relu(a, b, out=None, stream=None, path=None, workspace="auto"):
-    """Tensor convenience: ``out = ReLU(a @ b)`` for 2-D fp16 tensors on the GPU.
+    """Tensor convenience: ``out = ReLU(a @ b)`` for 2-D fp16 (or bfloat16)
+    tensors on the GPU.
 
     Row pitches are taken from the tensors' strides (unit column stride
-    required). ``workspace``: "auto" allocates (from torch's caching
-    allocator) the scratch the library asks for, if any; a uint8 device
-    tensor is used as given; None means no workspace. Raises GemmReluError on
-    a non-zero status.
+    required). ``workspace`` (fp16 only): "auto" allocates (from torch's
+    caching allocator) the scratch the library asks for, if any; a uint8
+    device tensor is used as given; None means no workspace. Raises
+    GemmReluError on a non-zero status.
     """
     import torch
-    if a.dtype != torch.float16 or b.dtype != torch.float16:
-        raise TypeError("a and b must be float16")
+    if a.dtype not in (torch.float16, torch.bfloat16) or b.dtype != a.dtype:
+        raise TypeError("a and b must both be float16 or both bfloat16")
     if a.dim() != 2 or b.dim() != 2 or a.shape[1] != b.shape[0]:
         raise ValueError("shapes do not form a matrix product: %s x %s" % (tuple(a.shape), tuple(b.shape)))
     M, K = a.shape
     N = b.shape[1]
     if out is None:
-        out = torch.empty((M, N), dtype=torch.float16, device=a.device)
+        out = torch.empty((M, N), dtype=a.dtype, device=a.device)
+    elif out.dtype != a.dtype:
+        raise TypeError("out must have the operands' dtype")
     for t in (a, b, out):
         if t.numel() and t.stride(1) != 1:
             raise ValueError("tensors need unit column stride")
@@ -248,6 +265,14 @@ def gemm_relu(a, b, out=None, stream=None, path=None, workspace="auto"):
     ldb = max(b.stride(0), 1) if K > 1 else max(N, 1)
     ldc = max(out.stride(0), 1) if M > 1 else max(N, 1)
     args = (M, N, K, a.data_ptr(), lda, b.data_ptr(), ldb, out.data_ptr(), ldc)
+    if a.dtype == torch.bfloat16:
+        if workspace is not None and not (isinstance(workspace, str) and workspace == "auto"):
+            raise ValueError("the bfloat16 paths take no workspace")
+        h = _stream_handle(stream)
+        st = gemm_relu_bf16(*args, h) if path is None else gemm_relu_bf16_forced(*args, h, path)
+        if st != GR_OK:
+            raise GemmReluError(st, "gemm_relu_bf16")
+        return out
     if isinstance(workspace, str):
         if workspace != "auto":
             raise ValueError("workspace must be 'auto', None or a uint8 tensor")

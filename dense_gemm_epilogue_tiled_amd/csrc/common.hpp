@@ -38,6 +38,50 @@ __device__ __forceinline__ uint32_t relu_pack2(float x0, float x1) {
     return (uint32_t)relu_to_f16(x0) | ((uint32_t)relu_to_f16(x1) << 16);
 }
 
+// The same epilogue for bfloat16 output: ReLU, then round to nearest even
+// bf16 (the upper 16 bits of the fp32 pattern after adding 0x7FFF plus the
+// lowest kept bit; exact for every non-negative fp32, +Inf included, and
+// values above the largest bf16 round to +Inf).
+__device__ __forceinline__ uint16_t relu_to_bf16(float x) {
+    const float r = (x > 0.0f) ? x : 0.0f;
+    const uint32_t u = __builtin_bit_cast(uint32_t, r);
+    return (uint16_t)((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16);
+}
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+
+// Element types of A, B and C.  Operands travel as 16-bit patterns (f16x8
+// registers); only the matrix-core instruction and the output rounding
+// depend on the type.  Accumulation is fp32 for both.
+struct ElemF16 {
+    static constexpr bool kIsF16 = true;
+    static __device__ __forceinline__ f32x16 mfma32(f16x8 b, f16x8 a, f32x16 c) {
+        return __builtin_amdgcn_mfma_f32_32x32x16_f16(b, a, c, 0, 0, 0);
+    }
+    static __device__ __forceinline__ f32x4 mfma16(f16x8 b, f16x8 a, f32x4 c) {
+        return __builtin_amdgcn_mfma_f32_16x16x32_f16(b, a, c, 0, 0, 0);
+    }
+    static __device__ __forceinline__ uint16_t relu_round(float x) { return relu_to_f16(x); }
+};
+
+struct ElemBF16 {
+    static constexpr bool kIsF16 = false;
+    static __device__ __forceinline__ f32x16 mfma32(f16x8 b, f16x8 a, f32x16 c) {
+        return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, b), __builtin_bit_cast(bf16x8, a),
+                                                        c, 0, 0, 0);
+    }
+    static __device__ __forceinline__ f32x4 mfma16(f16x8 b, f16x8 a, f32x4 c) {
+        return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, b), __builtin_bit_cast(bf16x8, a),
+                                                        c, 0, 0, 0);
+    }
+    static __device__ __forceinline__ uint16_t relu_round(float x) { return relu_to_bf16(x); }
+};
+
+template <typename E>
+__device__ __forceinline__ uint32_t relu_pack2_e(float x0, float x1) {
+    return (uint32_t)E::relu_round(x0) | ((uint32_t)E::relu_round(x1) << 16);
+}
+
 // Map a 1-D workgroup id to a tile (tm, tn).
 //  1. Workgroups are handed to the 8 XCDs round-robin (id % 8), each XCD
 //     with its own L2.  Renumber so that each XCD receives a contiguous range
@@ -77,7 +121,7 @@ __device__ __forceinline__ void tile_of_workgroup(uint32_t wg, uint32_t n_wg, ui
 //     16-byte block of element N-1); the columns >= N it brings in only
 //     reach outputs that are never stored.
 //   * stores: an output is written only if its row is owned by the tile and
-//     its column is < N; 8-byte stores where C allows them, else 2-byte ones.
+//     its column is < N (epi::store_wave_tile below).
 namespace edge {
 
 __device__ __forceinline__ int64_t shifted_row0(int64_t m_tile, int64_t M, int64_t bm) {
@@ -89,25 +133,6 @@ __device__ __forceinline__ int64_t shifted_row0(int64_t m_tile, int64_t M, int64
 __device__ __forceinline__ uint32_t clamp_chunk(uint32_t c, int64_t n0, int64_t N) {
     const uint32_t last = (uint32_t)((N - 1) / 8 - n0 / 8);
     return c < last ? c : last;
-}
-
-// Outputs (row, n .. n+3) of one lane, ReLU'd and rounded, where they fall
-// inside the tile's part of C.  vec_c == 4: C and its pitch allow 8-byte
-// stores.
-__device__ __forceinline__ void store4(uint16_t* crow, bool row_owned, int64_t n, int64_t N, int vec_c, float a0,
-                                       float a1, float a2, float a3) {
-    if (!row_owned) return;
-    if (vec_c == 4 && n + 4 <= N) {
-        u32x2 p;
-        p[0] = relu_pack2(a0, a1);
-        p[1] = relu_pack2(a2, a3);
-        *reinterpret_cast<u32x2*>(crow + n) = p;
-        return;
-    }
-    if (n < N) crow[n] = relu_to_f16(a0);
-    if (n + 1 < N) crow[n + 1] = relu_to_f16(a1);
-    if (n + 2 < N) crow[n + 2] = relu_to_f16(a2);
-    if (n + 3 < N) crow[n + 3] = relu_to_f16(a3);
 }
 
 }  // namespace edge
@@ -152,7 +177,7 @@ struct WaveTile {
 
 constexpr uint32_t REGION_BYTES = WaveTile<4, 4>::REGION_BYTES;  // 32 KiB for a 128 x 128 wave tile
 
-template <bool EDGE, int FM, int FN>
+template <bool EDGE, typename E = ElemF16, int FM, int FN>
 __device__ __forceinline__ void store_wave_tile(const f32x16 (&acc)[FM][FN], uint8_t* region, uint32_t lane,
                                                 uint16_t* __restrict__ C, int64_t ldc, int64_t row0, int64_t col0,
                                                 int64_t row_min, int64_t M, int64_t N, int vec_c) {
@@ -167,8 +192,8 @@ __device__ __forceinline__ void store_wave_tile(const f32x16 (&acc)[FM][FN], uin
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
                 u32x2 p;
-                p[0] = relu_pack2(acc[i][j][4 * q + 0], acc[i][j][4 * q + 1]);
-                p[1] = relu_pack2(acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]);
+                p[0] = relu_pack2_e<E>(acc[i][j][4 * q + 0], acc[i][j][4 * q + 1]);
+                p[1] = relu_pack2_e<E>(acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]);
                 *reinterpret_cast<u32x2*>(region + T::off(row, 4u * j + q) + 8u * T::half_slot(row, half)) = p;
             }
         }

@@ -348,23 +348,23 @@ int launch(void (*kernel)(Args...), int64_t grid, int threads, hipStream_t strea
     return e == hipSuccess ? GR_OK : GR_ERR_LAUNCH;
 }
 
-template <bool GUARD, int VA, int VB>
+template <bool GUARD, int VA, int VB, typename E>
 int launch_tile(const gr_plan_t& p, int64_t M, int64_t N, int64_t K, const uint16_t* A, int64_t lda,
                 const uint16_t* B, int64_t ldb, uint16_t* C, int64_t ldc, hipStream_t stream) {
     using namespace gr::tile;
     const uint32_t tiles_m = (uint32_t)((M + BM - 1) / BM);
     const uint32_t tiles_n = (uint32_t)((N + BN - 1) / BN);
-    return launch(gemm_relu_tile_kernel<GUARD, VA, VB>, p.grid, THREADS, stream, A, B, C, M, N, K, lda, ldb, ldc,
-                  tiles_m, tiles_n, (uint32_t)p.group_m, (int)p.vec_c);
+    return launch(gemm_relu_tile_kernel<GUARD, VA, VB, false, E>, p.grid, THREADS, stream, A, B, C, M, N, K, lda,
+                  ldb, ldc, tiles_m, tiles_n, (uint32_t)p.group_m, (int)p.vec_c);
 }
 
-template <bool GUARD, int VA>
+template <bool GUARD, int VA, typename E>
 int launch_tile_vb(const gr_plan_t& p, int64_t M, int64_t N, int64_t K, const uint16_t* A, int64_t lda,
                    const uint16_t* B, int64_t ldb, uint16_t* C, int64_t ldc, hipStream_t stream) {
     switch (p.vec_b) {
-        case 8: return launch_tile<GUARD, VA, 8>(p, M, N, K, A, lda, B, ldb, C, ldc, stream);
-        case 2: return launch_tile<GUARD, VA, 2>(p, M, N, K, A, lda, B, ldb, C, ldc, stream);
-        default: return launch_tile<GUARD, VA, 1>(p, M, N, K, A, lda, B, ldb, C, ldc, stream);
+        case 8: return launch_tile<GUARD, VA, 8, E>(p, M, N, K, A, lda, B, ldb, C, ldc, stream);
+        case 2: return launch_tile<GUARD, VA, 2, E>(p, M, N, K, A, lda, B, ldb, C, ldc, stream);
+        default: return launch_tile<GUARD, VA, 1, E>(p, M, N, K, A, lda, B, ldb, C, ldc, stream);
     }
 }
 
@@ -388,9 +388,15 @@ int launch_pack(const Pack& pk, int64_t M, int64_t N, int64_t K, const uint16_t*
     return launch(gr::pack::pack_kernel, ba + bb, gr::pack::THREADS, stream, ja, jb, (uint32_t)ba);
 }
 
+// E: element type of A, B and C (the workspace paths exist for fp16 only).
+template <typename E>
 int run(const gr_plan_t& p, int64_t M, int64_t N, int64_t K, const uint16_t* A, int64_t lda, const uint16_t* B,
         int64_t ldb, uint16_t* C, int64_t ldc, const Pack& pk, const SmallMSplit& sp, const TileSplit& ts,
         uint8_t* ws, hipStream_t stream) {
+    if constexpr (!E::kIsF16) {
+        if (p.path == GR_PATH_SMALL_M_SPLIT || p.path == GR_PATH_TILE_SPLIT || p.path == GR_PATH_TILE_PACKED)
+            return GR_ERR_INVALID_PATH;
+    }
     switch (p.path) {
         case GR_PATH_NONE: return GR_OK;
         case GR_PATH_SMALL_M_SPLIT: {
@@ -434,7 +440,7 @@ int run(const gr_plan_t& p, int64_t M, int64_t N, int64_t K, const uint16_t* A, 
             q.path = GR_PATH_TILE;
             const uint16_t* Ap = pk.a ? reinterpret_cast<const uint16_t*>(ws) : A;
             const uint16_t* Bp = pk.b ? reinterpret_cast<const uint16_t*>(ws + pk.off_b) : B;
-            return run(q, M, N, pk.kp, Ap, pk.lda_p, Bp, pk.ldb_p, C, ldc, pk, sp, ts, ws, stream);
+            return run<E>(q, M, N, pk.kp, Ap, pk.lda_p, Bp, pk.ldb_p, C, ldc, pk, sp, ts, ws, stream);
         }
         case GR_PATH_TILE: {
             const int64_t bm = p.block_m, bn = p.block_n;
@@ -448,40 +454,40 @@ int run(const gr_plan_t& p, int64_t M, int64_t N, int64_t K, const uint16_t* A, 
                 float* no_part = nullptr;
                 const int64_t no_split = 0;
                 if (whole)
-                    return launch(gemm_relu_tile128_kernel<false, false>, p.grid, THREADS, stream, A, B, C, M, N, K,
-                                  lda, ldb, ldc, tiles_m, tiles_n, gm, vc, no_part, no_split);
-                return launch(gemm_relu_tile128_kernel<true, false>, p.grid, THREADS, stream, A, B, C, M, N, K, lda,
-                              ldb, ldc, tiles_m, tiles_n, gm, vc, no_part, no_split);
+                    return launch(gemm_relu_tile128_kernel<false, false, false, E>, p.grid, THREADS, stream, A, B, C,
+                                  M, N, K, lda, ldb, ldc, tiles_m, tiles_n, gm, vc, no_part, no_split);
+                return launch(gemm_relu_tile128_kernel<true, false, false, E>, p.grid, THREADS, stream, A, B, C, M,
+                              N, K, lda, ldb, ldc, tiles_m, tiles_n, gm, vc, no_part, no_split);
             }
             if (K % gr::tile3::BKA == 0) {
                 using namespace gr::tile3;
                 if (whole)
-                    return launch(gemm_relu_tile3_kernel<false>, p.grid, THREADS, stream, A, B, C, M, N, K, lda, ldb,
-                                  ldc, tiles_m, tiles_n, gm, vc);
-                return launch(gemm_relu_tile3_kernel<true>, p.grid, THREADS, stream, A, B, C, M, N, K, lda, ldb, ldc,
-                              tiles_m, tiles_n, gm, vc);
+                    return launch(gemm_relu_tile3_kernel<false, false, E>, p.grid, THREADS, stream, A, B, C, M, N, K,
+                                  lda, ldb, ldc, tiles_m, tiles_n, gm, vc);
+                return launch(gemm_relu_tile3_kernel<true, false, E>, p.grid, THREADS, stream, A, B, C, M, N, K, lda,
+                              ldb, ldc, tiles_m, tiles_n, gm, vc);
             }
             using namespace gr::tile2;
             if (whole)
-                return launch(gemm_relu_tile2_kernel<false>, p.grid, THREADS, stream, A, B, C, M, N, K, lda, ldb, ldc,
-                              tiles_m, tiles_n, gm, vc);
-            return launch(gemm_relu_tile2_kernel<true>, p.grid, THREADS, stream, A, B, C, M, N, K, lda, ldb, ldc,
-                          tiles_m, tiles_n, gm, vc);
+                return launch(gemm_relu_tile2_kernel<false, false, E>, p.grid, THREADS, stream, A, B, C, M, N, K, lda,
+                              ldb, ldc, tiles_m, tiles_n, gm, vc);
+            return launch(gemm_relu_tile2_kernel<true, false, E>, p.grid, THREADS, stream, A, B, C, M, N, K, lda, ldb,
+                          ldc, tiles_m, tiles_n, gm, vc);
         }
         case GR_PATH_TILE_EDGE:
             switch (p.vec_a) {
-                case 8: return launch_tile_vb<true, 8>(p, M, N, K, A, lda, B, ldb, C, ldc, stream);
-                case 2: return launch_tile_vb<true, 2>(p, M, N, K, A, lda, B, ldb, C, ldc, stream);
-                default: return launch_tile_vb<true, 1>(p, M, N, K, A, lda, B, ldb, C, ldc, stream);
+                case 8: return launch_tile_vb<true, 8, E>(p, M, N, K, A, lda, B, ldb, C, ldc, stream);
+                case 2: return launch_tile_vb<true, 2, E>(p, M, N, K, A, lda, B, ldb, C, ldc, stream);
+                default: return launch_tile_vb<true, 1, E>(p, M, N, K, A, lda, B, ldb, C, ldc, stream);
             }
         case GR_PATH_SMALL_M: {
             using namespace gr::smallm;
             const bool whole = N % NB == 0 && K % KSTEP == 0;
             if (whole)
-                return launch(gemm_relu_smallm_kernel<kSmallMWaves, kSmallMUnroll, false>, p.grid, p.threads,
+                return launch(gemm_relu_smallm_kernel<kSmallMWaves, kSmallMUnroll, false, E>, p.grid, p.threads,
                               stream, A, B, C, M, N, K, lda, ldb, ldc);
-            return launch(gemm_relu_smallm_kernel<kSmallMWaves, kSmallMUnroll, true>, p.grid, p.threads, stream, A,
-                          B, C, M, N, K, lda, ldb, ldc);
+            return launch(gemm_relu_smallm_kernel<kSmallMWaves, kSmallMUnroll, true, E>, p.grid, p.threads, stream,
+                          A, B, C, M, N, K, lda, ldb, ldc);
         }
         default: return GR_ERR_INVALID_PATH;
     }
@@ -532,8 +538,25 @@ int entry(int64_t M, int64_t N, int64_t K, const uint16_t* A, int64_t lda, const
     if (p.path == GR_PATH_NONE) return GR_OK;
     st = check_device();
     if (st != GR_OK) return st;
-    return run(p, M, N, K, A, lda, B, ldb, C, ldc, pk, sp, ts, static_cast<uint8_t*>(ws),
-               static_cast<hipStream_t>(stream));
+    return run<gr::ElemF16>(p, M, N, K, A, lda, B, ldb, C, ldc, pk, sp, ts, static_cast<uint8_t*>(ws),
+                            static_cast<hipStream_t>(stream));
+}
+
+// bfloat16 operands and output: the planner's paths without a workspace.
+int entry_bf16(int64_t M, int64_t N, int64_t K, const uint16_t* A, int64_t lda, const uint16_t* B, int64_t ldb,
+               uint16_t* C, int64_t ldc, void* stream, int forced) {
+    Pack pk;
+    SmallMSplit sp;
+    TileSplit ts;
+    gr_plan_t p;
+    int st = plan_call(M, N, K, (uintptr_t)A, lda, (uintptr_t)B, ldb, (uintptr_t)C, ldc, 0, 0, true, forced, &pk, &sp,
+                       &ts, &p);
+    if (st != GR_OK) return st;
+    if (p.path == GR_PATH_NONE) return GR_OK;
+    st = check_device();
+    if (st != GR_OK) return st;
+    return run<gr::ElemBF16>(p, M, N, K, A, lda, B, ldb, C, ldc, pk, sp, ts, nullptr,
+                             static_cast<hipStream_t>(stream));
 }
 
 bool known_path(int path) {
@@ -732,6 +755,17 @@ int entry_bt(int64_t M, int64_t N, int64_t K, const uint16_t* A, int64_t lda, co
 }  // namespace
 
 extern "C" {
+
+int gemm_relu_bf16(int64_t M, int64_t N, int64_t K, const uint16_t* A, int64_t lda, const uint16_t* B, int64_t ldb,
+                   uint16_t* C, int64_t ldc, void* stream) {
+    return entry_bf16(M, N, K, A, lda, B, ldb, C, ldc, stream, -1);
+}
+
+int gemm_relu_bf16_forced(int64_t M, int64_t N, int64_t K, const uint16_t* A, int64_t lda, const uint16_t* B,
+                          int64_t ldb, uint16_t* C, int64_t ldc, void* stream, int path) {
+    if (path != GR_PATH_TILE && path != GR_PATH_TILE_EDGE && path != GR_PATH_SMALL_M) return GR_ERR_INVALID_PATH;
+    return entry_bf16(M, N, K, A, lda, B, ldb, C, ldc, stream, path);
+}
 
 int gemm_relu_f16_bt(int64_t M, int64_t N, int64_t K, const uint16_t* A, int64_t lda, const uint16_t* Bt,
                      int64_t ldbt, uint16_t* C, int64_t ldc, void* stream) {

@@ -96,7 +96,8 @@ __device__ __forceinline__ u32x4 load_a8(const uint16_t* A, int64_t lda, int64_t
     return v;
 }
 
-template <int W, int U, bool GUARD>
+// E: element type (ElemF16 or ElemBF16; only the MFMA and the rounding differ).
+template <int W, int U, bool GUARD, typename E = ElemF16>
 __global__ __launch_bounds__(64 * W, 1) void gemm_relu_smallm_kernel(
     const uint16_t* __restrict__ A, const uint16_t* __restrict__ B, uint16_t* __restrict__ C,
     int64_t M, int64_t N, int64_t K, int64_t lda, int64_t ldb, int64_t ldc) {
@@ -142,7 +143,7 @@ __global__ __launch_bounds__(64 * W, 1) void gemm_relu_smallm_kernel(
                 u32x4 o;
 #pragma unroll
                 for (int d = 0; d < 4; ++d) o[d] = pair_halves(rb[u][2 * d][c >> 1], rb[u][2 * d + 1][c >> 1], c & 1);
-                acc[c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, o), a, acc[c], 0, 0, 0);
+                acc[c] = E::mfma16(__builtin_bit_cast(f16x8, o), a, acc[c]);
             }
         }
     };
@@ -177,7 +178,7 @@ __global__ __launch_bounds__(64 * W, 1) void gemm_relu_smallm_kernel(
             float sum = 0.0f;
 #pragma unroll
             for (int w = 0; w < W; ++w) sum += red[w][m][nl];
-            C[(int64_t)m * ldc + n] = relu_to_f16(sum);
+            C[(int64_t)m * ldc + n] = E::relu_round(sum);
         }
     }
 }

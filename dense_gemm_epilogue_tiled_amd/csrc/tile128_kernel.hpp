@@ -70,7 +70,8 @@ __device__ __forceinline__ f16x8 read_b_operand(const GR_LDS uint8_t* p) {
 
 // BT=true: B given transposed (Bt, N x K row-major, pitch ldb), staged and
 // read like A (rows of Bt past N clamped to row N-1).
-template <bool EDGE, bool SPLIT, bool BT = false>
+// E: element type (ElemF16 or ElemBF16; only the MFMA and the rounding differ).
+template <bool EDGE, bool SPLIT, bool BT = false, typename E = ElemF16>
 __global__ __launch_bounds__(THREADS, 2) void gemm_relu_tile128_kernel(
     const uint16_t* __restrict__ A, const uint16_t* __restrict__ B, uint16_t* __restrict__ C, int64_t M, int64_t N,
     int64_t K, int64_t lda, int64_t ldb, int64_t ldc, uint32_t tiles_m, uint32_t tiles_n, uint32_t group_m,
@@ -199,7 +200,7 @@ __global__ __launch_bounds__(THREADS, 2) void gemm_relu_tile128_kernel(
             for (int i = 0; i < FM; ++i)
 #pragma unroll
                 for (int j = 0; j < FN; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(fb[s][j], fa[s][i], acc[i][j], 0, 0, 0);
+                    acc[i][j] = E::mfma32(fb[s][j], fa[s][i], acc[i][j]);
     }
 
     if constexpr (SPLIT) {
@@ -233,7 +234,7 @@ __global__ __launch_bounds__(THREADS, 2) void gemm_relu_tile128_kernel(
         (void)vec_c;
     } else {
         // Epilogue: ReLU, fp16 and the store of C, staged through LDS.
-        epi::store_wave_tile<EDGE>(acc, lds + wave * epi::WaveTile<FM, FN>::REGION_BYTES, lane, C, ldc,
+        epi::store_wave_tile<EDGE, E>(acc, lds + wave * epi::WaveTile<FM, FN>::REGION_BYTES, lane, C, ldc,
                                    m0 + wm * WAVE_TM, n0 + wn * WAVE_TN, m0, M, N, vec_c);
         (void)part;
     }

@@ -122,7 +122,8 @@ constexpr int64_t MAX_LDB = (int64_t(1) << 31) / (BK * 2);
 // [256 n][32 k] are staged exactly like A's (64-byte rows, chunk XOR (n/4)%4)
 // and its fragments are read like A's (ds_read_b128); rows of Bt past N are
 // clamped to row N-1 (their columns are never stored).
-template <bool EDGE, bool BT = false>
+// E: element type (ElemF16 or ElemBF16; only the MFMA and the rounding differ).
+template <bool EDGE, bool BT = false, typename E = ElemF16>
 __global__ __launch_bounds__(THREADS, 1) void gemm_relu_tile2_kernel(
     const uint16_t* __restrict__ A, const uint16_t* __restrict__ B, uint16_t* __restrict__ C, int64_t M, int64_t N,
     int64_t K, int64_t lda, int64_t ldb, int64_t ldc, uint32_t tiles_m, uint32_t tiles_n, uint32_t group_m,
@@ -237,7 +238,7 @@ __global__ __launch_bounds__(THREADS, 1) void gemm_relu_tile2_kernel(
     // MFMA t of a step: s = t/16, i = (t/4)%4, j = t%4.
     auto mfma_one = [&](const Frags& f, int t) {
         const int s = t >> 4, i = (t >> 2) & 3, j = t & 3;
-        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(f.b[s][j], f.a[s][i], acc[i][j], 0, 0, 0);
+        acc[i][j] = E::mfma32(f.b[s][j], f.a[s][i], acc[i][j]);
     };
 
     const uint32_t KT = (uint32_t)(K / BK);  // >= 1, whole strips only
@@ -341,7 +342,7 @@ __global__ __launch_bounds__(THREADS, 1) void gemm_relu_tile2_kernel(
 
     // Epilogue: ReLU, fp16 and the store of C, staged through LDS (the
     // operand ring is no longer needed).
-    epi::store_wave_tile<EDGE>(acc, lds + wave * epi::REGION_BYTES, lane, C, ldc, m0 + wm * WAVE_TM,
+    epi::store_wave_tile<EDGE, E>(acc, lds + wave * epi::REGION_BYTES, lane, C, ldc, m0 + wm * WAVE_TM,
                                n0 + wn * WAVE_TN, m_tile, M, N, vec_c);
 }
 

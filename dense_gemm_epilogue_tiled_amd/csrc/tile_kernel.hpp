@@ -112,7 +112,8 @@ __device__ __forceinline__ u32x4 load8(const uint16_t* base, int64_t ld, int64_t
 // BT=true: B is given transposed (Bt, N x K row-major, pitch ldb); its
 // chunks are loaded like A's (rows n, 8 consecutive k) and stored as they
 // are, since the LDS B tile is k-contiguous already.
-template <bool GUARD, int VA, int VB, bool BT = false>
+// E: element type (ElemF16 or ElemBF16; only the MFMA and the rounding differ).
+template <bool GUARD, int VA, int VB, bool BT = false, typename E = ElemF16>
 __global__ __launch_bounds__(THREADS, 1) void gemm_relu_tile_kernel(
     const uint16_t* __restrict__ A, const uint16_t* __restrict__ B, uint16_t* __restrict__ C,
     int64_t M, int64_t N, int64_t K, int64_t lda, int64_t ldb, int64_t ldc,
@@ -209,7 +210,7 @@ __global__ __launch_bounds__(THREADS, 1) void gemm_relu_tile_kernel(
             for (int i = 0; i < FM; ++i)
 #pragma unroll
                 for (int j = 0; j < FN; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(bf[j], af[i], acc[i][j], 0, 0, 0);
+                    acc[i][j] = E::mfma32(bf[j], af[i], acc[i][j]);
         }
 
         if (kt + 1 < KT) store_tiles(stage ^ 1u);
@@ -232,13 +233,13 @@ __global__ __launch_bounds__(THREADS, 1) void gemm_relu_tile_kernel(
                                     acc[i][j][4 * q + 3]};
                 if (!GUARD || (vec_c >= 4 && n + 4 <= N)) {
                     u32x2 p;
-                    p[0] = relu_pack2(v[0], v[1]);
-                    p[1] = relu_pack2(v[2], v[3]);
+                    p[0] = relu_pack2_e<E>(v[0], v[1]);
+                    p[1] = relu_pack2_e<E>(v[2], v[3]);
                     *reinterpret_cast<u32x2*>(crow + n) = p;
                 } else {
 #pragma unroll
                     for (int e = 0; e < 4; ++e)
-                        if (n + e < N) crow[n + e] = relu_to_f16(v[e]);
+                        if (n + e < N) crow[n + e] = E::relu_round(v[e]);
                 }
             }
         }

@@ -1,5 +1,6 @@
 /*
- * gemm_relu.h -- C ABI of the MI355X (gfx950) fused fp16 GEMM + ReLU library.
+ * gemm_relu.h -- C ABI of the MI355X (gfx950) fused fp16 GEMM + ReLU library
+ * (with bfloat16 and transposed-B variants further down).
  *
  * The one operation:  C := ReLU(A * B)
  *   A  M x K, B  K x N, C  M x N, all IEEE binary16, row-major with a row
@@ -272,6 +273,38 @@ int gemm_relu_f16_bt_forced(int64_t M, int64_t N, int64_t K,
                             const uint16_t* Bt, int64_t ldbt,
                             uint16_t* C, int64_t ldc,
                             void* stream, int path);
+
+/*
+ * ---- bfloat16 operands and result ---------------------------------------------
+ * The same operation with A, B and C in bfloat16 (1 sign, 8 exponent, 7
+ * fraction bits: the upper half of a binary32): products accumulate in fp32,
+ * ReLU acts on the fp32 sum, and the result is rounded to bfloat16 (nearest,
+ * ties to even) when it is written.  The TileLang tutorial, section "张量核与
+ * CUDA core", names fp16 and bf16 as the inputs a GEMM feeds to the matrix
+ * engines; the epilogue is the one defined above.  Every convention above
+ * holds (layouts, pitches, edges, errors, streams); the paths are those of
+ * gemm_relu_f16 without a workspace:
+ *   GR_PATH_SMALL_M   M <= 16, 16-byte rows of A and B;
+ *   GR_PATH_TILE      16-byte rows of A and B, K % 32 == 0 (256x256 or
+ *                     128x128 tiles, as for fp16);
+ *   GR_PATH_TILE_EDGE everything else (guarded register-staged kernel).
+ * gemm_relu_f16_plan describes the plan these calls follow (the path does not
+ * depend on the element format).  There is no workspace variant.
+ */
+int gemm_relu_bf16(int64_t M, int64_t N, int64_t K,
+                   const uint16_t* A, int64_t lda,
+                   const uint16_t* B, int64_t ldb,
+                   uint16_t* C, int64_t ldc,
+                   void* stream);
+
+/* gemm_relu_bf16 on a given path (GR_PATH_TILE, GR_PATH_TILE_EDGE or
+   GR_PATH_SMALL_M; GR_ERR_INVALID_PATH for any other path, or when the path's
+   conditions do not hold).  Test hook. */
+int gemm_relu_bf16_forced(int64_t M, int64_t N, int64_t K,
+                          const uint16_t* A, int64_t lda,
+                          const uint16_t* B, int64_t ldb,
+                          uint16_t* C, int64_t ldc,
+                          void* stream, int path);
 
 /* Static, NUL-terminated name of a status code ("GR_OK", "GR_ERR_ALIAS", ...).
    Unknown codes give "GR_ERR_UNKNOWN". */

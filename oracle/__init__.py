@@ -1,4 +1,5 @@
-"""CPU oracle for C = ReLU(A.B), fp16 in, fp32 accumulate, fp16 out.
+"""CPU oracle for C = ReLU(A.B), fp16 in, fp32 accumulate, fp16 out (and the
+same with bfloat16 operands and result, ``fmt="bf16"``).
 
 TEST INFRASTRUCTURE. Only the test suite, ``__graft_entry__.smoke()`` and the
 ``cpu_baseline`` leg of ``bench.py`` may import this package. The product
@@ -30,6 +31,8 @@ LIB_PATH = os.path.join(_HERE, "liboracle_gemm_relu.so")
 _CFLAGS = ["-O2", "-std=c11", "-fno-fast-math", "-ffp-contract=off", "-fopenmp",
            "-fPIC", "-shared", "-Wall", "-Wextra"]
 
+_FMTS = ("f16", "bf16")
+
 _lock = threading.Lock()
 _lib = None
 
@@ -59,16 +62,22 @@ def _load():
             lib.oracle_f16_to_f32_array.restype = None
             lib.oracle_f32_to_f16_array.argtypes = [p, p, i64]
             lib.oracle_f32_to_f16_array.restype = None
+            lib.oracle_bf16_to_f32_array.argtypes = [p, p, i64]
+            lib.oracle_bf16_to_f32_array.restype = None
+            lib.oracle_f32_to_bf16_array.argtypes = [p, p, i64]
+            lib.oracle_f32_to_bf16_array.restype = None
             lib.oracle_set_threads.argtypes = [ctypes.c_int]
             lib.oracle_set_threads.restype = None
             lib.oracle_max_threads.argtypes = []
             lib.oracle_max_threads.restype = ctypes.c_int
-            lib.oracle_gemm_relu_f16_full.argtypes = [i64, i64, i64, p, i64, p, i64, p, i64]
-            lib.oracle_gemm_relu_f16_rows.argtypes = [i64, i64, i64, p, i64, p, i64, p, i64, p]
-            lib.oracle_gemm_relu_f16_cols.argtypes = [i64, i64, i64, p, i64, p, i64, p, i64, p]
-            lib.oracle_gemm_relu_f16_elems.argtypes = [i64, i64, i64, p, i64, p, i64, p, p, i64, p]
-            for name in ("full", "rows", "cols", "elems"):
-                getattr(lib, "oracle_gemm_relu_f16_" + name).restype = ctypes.c_int
+            for fmt in _FMTS:
+                getattr(lib, "oracle_gemm_relu_%s_full" % fmt).argtypes = [i64, i64, i64, p, i64, p, i64, p, i64]
+                getattr(lib, "oracle_gemm_relu_%s_rows" % fmt).argtypes = [i64, i64, i64, p, i64, p, i64, p, i64, p]
+                getattr(lib, "oracle_gemm_relu_%s_cols" % fmt).argtypes = [i64, i64, i64, p, i64, p, i64, p, i64, p]
+                getattr(lib, "oracle_gemm_relu_%s_elems" % fmt).argtypes = [
+                    i64, i64, i64, p, i64, p, i64, p, p, i64, p]
+                for name in ("full", "rows", "cols", "elems"):
+                    getattr(lib, "oracle_gemm_relu_%s_%s" % (fmt, name)).restype = ctypes.c_int
             _lib = lib
     return _lib
 
@@ -79,7 +88,7 @@ def _ptr(a: np.ndarray) -> int:
 
 def _check_operands(A, B, M, N, K, lda, ldb):
     if A.dtype != np.uint16 or B.dtype != np.uint16:
-        raise TypeError("operands must be uint16 arrays of fp16 bit patterns")
+        raise TypeError("operands must be uint16 arrays of fp16 / bf16 bit patterns")
     if not (A.flags.c_contiguous and B.flags.c_contiguous):
         raise ValueError("operands must be C-contiguous")
     if M > 0 and K > 0 and A.size < (M - 1) * lda + K:
@@ -116,8 +125,32 @@ def f32_to_f16(vals: np.ndarray) -> np.ndarray:
     return out.reshape(np.shape(vals))
 
 
-def gemm_relu_full(A, B, M=None, N=None, K=None, lda=None, ldb=None, threads=None):
-    """The whole M x N result as fp16 bits (packed, ldc = N)."""
+def bf16_to_f32(bits: np.ndarray) -> np.ndarray:
+    """Element-wise bfloat16 -> binary32 through the oracle's own conversion."""
+    lib = _load()
+    flat = np.ascontiguousarray(bits, dtype=np.uint16).ravel()
+    out = np.empty(flat.size, dtype=np.float32)
+    lib.oracle_bf16_to_f32_array(_ptr(flat), _ptr(out), flat.size)
+    return out.reshape(np.shape(bits))
+
+
+def f32_to_bf16(vals: np.ndarray) -> np.ndarray:
+    """Element-wise binary32 -> bfloat16 (RNE) through the oracle's own conversion."""
+    lib = _load()
+    flat = np.ascontiguousarray(vals, dtype=np.float32).ravel()
+    out = np.empty(flat.size, dtype=np.uint16)
+    lib.oracle_f32_to_bf16_array(_ptr(flat), _ptr(out), flat.size)
+    return out.reshape(np.shape(vals))
+
+
+def _entry(lib, fmt, name):
+    if fmt not in _FMTS:
+        raise ValueError("fmt must be one of %s" % (_FMTS,))
+    return getattr(lib, "oracle_gemm_relu_%s_%s" % (fmt, name))
+
+
+def gemm_relu_full(A, B, M=None, N=None, K=None, lda=None, ldb=None, threads=None, fmt="f16"):
+    """The whole M x N result as fp16 (or bf16, fmt="bf16") bits (packed, ldc = N)."""
     M, N, K, lda, ldb = _dims(A, B, M, N, K, lda, ldb)
     _check_operands(A, B, M, N, K, lda, ldb)
     lib = _load()
@@ -125,14 +158,14 @@ def gemm_relu_full(A, B, M=None, N=None, K=None, lda=None, ldb=None, threads=Non
         lib.oracle_set_threads(int(threads))
     C = np.zeros((M, N), dtype=np.uint16)
     if M > 0 and N > 0:
-        rc = lib.oracle_gemm_relu_f16_full(M, N, K, _ptr(A), lda, _ptr(B), ldb, _ptr(C), N)
+        rc = _entry(lib, fmt, "full")(M, N, K, _ptr(A), lda, _ptr(B), ldb, _ptr(C), N)
         if rc != 0:
             raise MemoryError("oracle allocation failed")
     return C
 
 
-def gemm_relu_rows(A, B, rows, M=None, N=None, K=None, lda=None, ldb=None, threads=None):
-    """Full rows ``rows`` of the result: array (len(rows), N) of fp16 bits."""
+def gemm_relu_rows(A, B, rows, M=None, N=None, K=None, lda=None, ldb=None, threads=None, fmt="f16"):
+    """Full rows ``rows`` of the result: array (len(rows), N) of fp16 / bf16 bits."""
     M, N, K, lda, ldb = _dims(A, B, M, N, K, lda, ldb)
     _check_operands(A, B, M, N, K, lda, ldb)
     r = np.ascontiguousarray(rows, dtype=np.int64)
@@ -143,14 +176,14 @@ def gemm_relu_rows(A, B, rows, M=None, N=None, K=None, lda=None, ldb=None, threa
         lib.oracle_set_threads(int(threads))
     out = np.zeros((r.size, N), dtype=np.uint16)
     if r.size and N > 0:
-        rc = lib.oracle_gemm_relu_f16_rows(M, N, K, _ptr(A), lda, _ptr(B), ldb, _ptr(r), r.size, _ptr(out))
+        rc = _entry(lib, fmt, "rows")(M, N, K, _ptr(A), lda, _ptr(B), ldb, _ptr(r), r.size, _ptr(out))
         if rc != 0:
             raise MemoryError("oracle allocation failed")
     return out
 
 
-def gemm_relu_cols(A, B, cols, M=None, N=None, K=None, lda=None, ldb=None, threads=None):
-    """Full columns ``cols`` of the result: array (len(cols), M) of fp16 bits."""
+def gemm_relu_cols(A, B, cols, M=None, N=None, K=None, lda=None, ldb=None, threads=None, fmt="f16"):
+    """Full columns ``cols`` of the result: array (len(cols), M) of fp16 / bf16 bits."""
     M, N, K, lda, ldb = _dims(A, B, M, N, K, lda, ldb)
     _check_operands(A, B, M, N, K, lda, ldb)
     c = np.ascontiguousarray(cols, dtype=np.int64)
@@ -161,14 +194,14 @@ def gemm_relu_cols(A, B, cols, M=None, N=None, K=None, lda=None, ldb=None, threa
         lib.oracle_set_threads(int(threads))
     out = np.zeros((c.size, M), dtype=np.uint16)
     if c.size and M > 0:
-        rc = lib.oracle_gemm_relu_f16_cols(M, N, K, _ptr(A), lda, _ptr(B), ldb, _ptr(c), c.size, _ptr(out))
+        rc = _entry(lib, fmt, "cols")(M, N, K, _ptr(A), lda, _ptr(B), ldb, _ptr(c), c.size, _ptr(out))
         if rc != 0:
             raise MemoryError("oracle allocation failed")
     return out
 
 
-def gemm_relu_elems(A, B, ii, jj, M=None, N=None, K=None, lda=None, ldb=None, threads=None):
-    """Single elements C[ii[e], jj[e]] as fp16 bits."""
+def gemm_relu_elems(A, B, ii, jj, M=None, N=None, K=None, lda=None, ldb=None, threads=None, fmt="f16"):
+    """Single elements C[ii[e], jj[e]] as fp16 / bf16 bits."""
     M, N, K, lda, ldb = _dims(A, B, M, N, K, lda, ldb)
     _check_operands(A, B, M, N, K, lda, ldb)
     i = np.ascontiguousarray(ii, dtype=np.int64)
@@ -182,7 +215,7 @@ def gemm_relu_elems(A, B, ii, jj, M=None, N=None, K=None, lda=None, ldb=None, th
         lib.oracle_set_threads(int(threads))
     out = np.zeros(i.size, dtype=np.uint16)
     if i.size:
-        lib.oracle_gemm_relu_f16_elems(M, N, K, _ptr(A), lda, _ptr(B), ldb, _ptr(i), _ptr(j), i.size, _ptr(out))
+        _entry(lib, fmt, "elems")(M, N, K, _ptr(A), lda, _ptr(B), ldb, _ptr(i), _ptr(j), i.size, _ptr(out))
     return out
 
 

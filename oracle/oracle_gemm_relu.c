@@ -35,6 +35,14 @@
  *
  * The fp16 <-> fp32 conversions below are written from the IEEE 754 binary16
  * and binary32 encodings, not taken from any library.
+ *
+ * The same computation is offered for bfloat16 operands and result (the
+ * *_bf16_* entry points): bfloat16 is the upper half of a binary32 pattern (8
+ * exponent bits, 7 fraction bits), so widening is exact and only step 4
+ * changes: round r to bfloat16, nearest with ties to even.  The product of two
+ * bfloat16 numbers needs at most 16 significand bits and stays in the fp32
+ * range only if the exponents allow; the tests use magnitudes where it is
+ * exact, as for fp16.
  */
 #include <stdint.h>
 #include <stdlib.h>
@@ -113,7 +121,33 @@ uint16_t oracle_f32_to_f16_rne(float f) {
     return (uint16_t)(sign | q);
 }
 
-/* Array forms of the two conversions (used by the conversion pins). */
+/* bfloat16: the upper 16 bits of a binary32 pattern. */
+float oracle_bf16_to_f32(uint16_t h) { return bits_to_f32((uint32_t)h << 16); }
+
+/* Round a binary32 value to bfloat16, nearest, ties to even.  The kept part is
+   the upper 16 bits; the discarded lower 16 bits decide the rounding.  A carry
+   out of the fraction increments the exponent, which is the correct result,
+   up to +-Inf for the largest finite values. */
+uint16_t oracle_f32_to_bf16_rne(float f) {
+    uint32_t u = f32_to_bits(f);
+    uint32_t exp = (u >> 23) & 0xFFu;
+    uint32_t frac = u & 0x7FFFFFu;
+    if (exp == 0xFFu && frac != 0) return (uint16_t)((u >> 16) | 0x0040u); /* quiet NaN */
+    uint32_t keep = u >> 16;
+    uint32_t rem = u & 0xFFFFu;
+    if (rem > 0x8000u || (rem == 0x8000u && (keep & 1u))) keep += 1u;
+    return (uint16_t)keep;
+}
+
+/* Array forms of the conversions (used by the conversion pins). */
+void oracle_bf16_to_f32_array(const uint16_t* in, float* out, int64_t n) {
+    for (int64_t e = 0; e < n; ++e) out[e] = oracle_bf16_to_f32(in[e]);
+}
+
+void oracle_f32_to_bf16_array(const float* in, uint16_t* out, int64_t n) {
+    for (int64_t e = 0; e < n; ++e) out[e] = oracle_f32_to_bf16_rne(in[e]);
+}
+
 void oracle_f16_to_f32_array(const uint16_t* in, float* out, int64_t n) {
     for (int64_t e = 0; e < n; ++e) out[e] = oracle_f16_to_f32(in[e]);
 }
@@ -122,10 +156,15 @@ void oracle_f32_to_f16_array(const float* in, uint16_t* out, int64_t n) {
     for (int64_t e = 0; e < n; ++e) out[e] = oracle_f32_to_f16_rne(in[e]);
 }
 
-/* ReLU on the fp32 accumulator followed by the fp16 write-back rounding. */
-static uint16_t epilogue(float acc) {
+/* Element formats of A, B and C. */
+enum { FMT_F16 = 0, FMT_BF16 = 1 };
+
+static float widen(int fmt, uint16_t h) { return fmt == FMT_BF16 ? oracle_bf16_to_f32(h) : oracle_f16_to_f32(h); }
+
+/* ReLU on the fp32 accumulator followed by the write-back rounding. */
+static uint16_t epilogue(int fmt, float acc) {
     float r = (acc > 0.0f) ? acc : 0.0f; /* NaN compares false -> +0 */
-    return oracle_f32_to_f16_rne(r);
+    return fmt == FMT_BF16 ? oracle_f32_to_bf16_rne(r) : oracle_f32_to_f16_rne(r);
 }
 
 /* ---- thread control (used only to time the oracle) ----------------------- */
@@ -146,36 +185,34 @@ int oracle_max_threads(void) {
 #endif
 }
 
-/* ---- the four entry points ----------------------------------------------- */
+/* ---- the four entry points (fp16 and bf16) -------------------------------- */
 
 /* One full output row i.  bf holds B widened to fp32, packed K x N. */
-static void one_row(int64_t i, int64_t N, int64_t K, const uint16_t* A, int64_t lda,
+static void one_row(int fmt, int64_t i, int64_t N, int64_t K, const uint16_t* A, int64_t lda,
                     const float* bf, float* acc, uint16_t* out) {
     for (int64_t j = 0; j < N; ++j) acc[j] = 0.0f;
     for (int64_t k = 0; k < K; ++k) {
-        float a = oracle_f16_to_f32(A[i * lda + k]);
+        float a = widen(fmt, A[i * lda + k]);
         const float* brow = bf + k * N;
         for (int64_t j = 0; j < N; ++j) acc[j] = acc[j] + a * brow[j];
     }
-    for (int64_t j = 0; j < N; ++j) out[j] = epilogue(acc[j]);
+    for (int64_t j = 0; j < N; ++j) out[j] = epilogue(fmt, acc[j]);
 }
 
-static float* widen_b(int64_t N, int64_t K, const uint16_t* B, int64_t ldb) {
+static float* widen_b(int fmt, int64_t N, int64_t K, const uint16_t* B, int64_t ldb) {
     float* bf = (float*)malloc((size_t)(K > 0 ? K : 1) * (size_t)(N > 0 ? N : 1) * sizeof(float));
     if (!bf) return NULL;
     for (int64_t k = 0; k < K; ++k)
-        for (int64_t j = 0; j < N; ++j) bf[k * N + j] = oracle_f16_to_f32(B[k * ldb + j]);
+        for (int64_t j = 0; j < N; ++j) bf[k * N + j] = widen(fmt, B[k * ldb + j]);
     return bf;
 }
 
 /* C[i*ldc + j] for all 0 <= i < M, 0 <= j < N.  Returns 0, or -1 on allocation
    failure.  Columns j >= N of C are not touched. */
-int oracle_gemm_relu_f16_full(int64_t M, int64_t N, int64_t K,
-                              const uint16_t* A, int64_t lda,
-                              const uint16_t* B, int64_t ldb,
-                              uint16_t* C, int64_t ldc) {
+static int gemm_full(int fmt, int64_t M, int64_t N, int64_t K, const uint16_t* A, int64_t lda,
+                     const uint16_t* B, int64_t ldb, uint16_t* C, int64_t ldc) {
     if (M <= 0 || N <= 0) return 0;
-    float* bf = widen_b(N, K, B, ldb);
+    float* bf = widen_b(fmt, N, K, B, ldb);
     if (!bf) return -1;
     int failed = 0;
 #pragma omp parallel
@@ -186,7 +223,7 @@ int oracle_gemm_relu_f16_full(int64_t M, int64_t N, int64_t K,
             failed = 1;
         } else {
 #pragma omp for schedule(dynamic, 1)
-            for (int64_t i = 0; i < M; ++i) one_row(i, N, K, A, lda, bf, acc, C + i * ldc);
+            for (int64_t i = 0; i < M; ++i) one_row(fmt, i, N, K, A, lda, bf, acc, C + i * ldc);
             free(acc);
         }
     }
@@ -195,13 +232,10 @@ int oracle_gemm_relu_f16_full(int64_t M, int64_t N, int64_t K,
 }
 
 /* Full rows: out[r*N + j] = C[rows[r]][j] for r < nrows. */
-int oracle_gemm_relu_f16_rows(int64_t M, int64_t N, int64_t K,
-                              const uint16_t* A, int64_t lda,
-                              const uint16_t* B, int64_t ldb,
-                              const int64_t* rows, int64_t nrows, uint16_t* out) {
-    (void)M;
+static int gemm_rows(int fmt, int64_t N, int64_t K, const uint16_t* A, int64_t lda, const uint16_t* B,
+                     int64_t ldb, const int64_t* rows, int64_t nrows, uint16_t* out) {
     if (nrows <= 0 || N <= 0) return 0;
-    float* bf = widen_b(N, K, B, ldb);
+    float* bf = widen_b(fmt, N, K, B, ldb);
     if (!bf) return -1;
     int failed = 0;
 #pragma omp parallel
@@ -212,7 +246,7 @@ int oracle_gemm_relu_f16_rows(int64_t M, int64_t N, int64_t K,
             failed = 1;
         } else {
 #pragma omp for schedule(dynamic, 1)
-            for (int64_t r = 0; r < nrows; ++r) one_row(rows[r], N, K, A, lda, bf, acc, out + r * N);
+            for (int64_t r = 0; r < nrows; ++r) one_row(fmt, rows[r], N, K, A, lda, bf, acc, out + r * N);
             free(acc);
         }
     }
@@ -221,11 +255,8 @@ int oracle_gemm_relu_f16_rows(int64_t M, int64_t N, int64_t K,
 }
 
 /* Full columns: out[c*M + i] = C[i][cols[c]] for c < ncols. */
-int oracle_gemm_relu_f16_cols(int64_t M, int64_t N, int64_t K,
-                              const uint16_t* A, int64_t lda,
-                              const uint16_t* B, int64_t ldb,
-                              const int64_t* cols, int64_t ncols, uint16_t* out) {
-    (void)N;
+static int gemm_cols(int fmt, int64_t M, int64_t K, const uint16_t* A, int64_t lda, const uint16_t* B,
+                     int64_t ldb, const int64_t* cols, int64_t ncols, uint16_t* out) {
     if (ncols <= 0 || M <= 0) return 0;
     int failed = 0;
 #pragma omp parallel
@@ -238,11 +269,11 @@ int oracle_gemm_relu_f16_cols(int64_t M, int64_t N, int64_t K,
 #pragma omp for schedule(dynamic, 1)
             for (int64_t c = 0; c < ncols; ++c) {
                 int64_t j = cols[c];
-                for (int64_t k = 0; k < K; ++k) bcol[k] = oracle_f16_to_f32(B[k * ldb + j]);
+                for (int64_t k = 0; k < K; ++k) bcol[k] = widen(fmt, B[k * ldb + j]);
                 for (int64_t i = 0; i < M; ++i) {
                     float acc = 0.0f;
-                    for (int64_t k = 0; k < K; ++k) acc = acc + oracle_f16_to_f32(A[i * lda + k]) * bcol[k];
-                    out[c * M + i] = epilogue(acc);
+                    for (int64_t k = 0; k < K; ++k) acc = acc + widen(fmt, A[i * lda + k]) * bcol[k];
+                    out[c * M + i] = epilogue(fmt, acc);
                 }
             }
             free(bcol);
@@ -252,18 +283,64 @@ int oracle_gemm_relu_f16_cols(int64_t M, int64_t N, int64_t K,
 }
 
 /* Single elements: out[e] = C[ii[e]][jj[e]] for e < n. */
-int oracle_gemm_relu_f16_elems(int64_t M, int64_t N, int64_t K,
-                               const uint16_t* A, int64_t lda,
-                               const uint16_t* B, int64_t ldb,
-                               const int64_t* ii, const int64_t* jj, int64_t n, uint16_t* out) {
-    (void)M;
-    (void)N;
+static int gemm_elems(int fmt, int64_t K, const uint16_t* A, int64_t lda, const uint16_t* B, int64_t ldb,
+                      const int64_t* ii, const int64_t* jj, int64_t n, uint16_t* out) {
 #pragma omp parallel for schedule(static)
     for (int64_t e = 0; e < n; ++e) {
         float acc = 0.0f;
         for (int64_t k = 0; k < K; ++k)
-            acc = acc + oracle_f16_to_f32(A[ii[e] * lda + k]) * oracle_f16_to_f32(B[k * ldb + jj[e]]);
-        out[e] = epilogue(acc);
+            acc = acc + widen(fmt, A[ii[e] * lda + k]) * widen(fmt, B[k * ldb + jj[e]]);
+        out[e] = epilogue(fmt, acc);
     }
     return 0;
+}
+
+int oracle_gemm_relu_f16_full(int64_t M, int64_t N, int64_t K, const uint16_t* A, int64_t lda,
+                              const uint16_t* B, int64_t ldb, uint16_t* C, int64_t ldc) {
+    return gemm_full(FMT_F16, M, N, K, A, lda, B, ldb, C, ldc);
+}
+
+int oracle_gemm_relu_f16_rows(int64_t M, int64_t N, int64_t K, const uint16_t* A, int64_t lda,
+                              const uint16_t* B, int64_t ldb, const int64_t* rows, int64_t nrows, uint16_t* out) {
+    (void)M;
+    return gemm_rows(FMT_F16, N, K, A, lda, B, ldb, rows, nrows, out);
+}
+
+int oracle_gemm_relu_f16_cols(int64_t M, int64_t N, int64_t K, const uint16_t* A, int64_t lda,
+                              const uint16_t* B, int64_t ldb, const int64_t* cols, int64_t ncols, uint16_t* out) {
+    (void)N;
+    return gemm_cols(FMT_F16, M, K, A, lda, B, ldb, cols, ncols, out);
+}
+
+int oracle_gemm_relu_f16_elems(int64_t M, int64_t N, int64_t K, const uint16_t* A, int64_t lda,
+                               const uint16_t* B, int64_t ldb, const int64_t* ii, const int64_t* jj, int64_t n,
+                               uint16_t* out) {
+    (void)M;
+    (void)N;
+    return gemm_elems(FMT_F16, K, A, lda, B, ldb, ii, jj, n, out);
+}
+
+int oracle_gemm_relu_bf16_full(int64_t M, int64_t N, int64_t K, const uint16_t* A, int64_t lda,
+                               const uint16_t* B, int64_t ldb, uint16_t* C, int64_t ldc) {
+    return gemm_full(FMT_BF16, M, N, K, A, lda, B, ldb, C, ldc);
+}
+
+int oracle_gemm_relu_bf16_rows(int64_t M, int64_t N, int64_t K, const uint16_t* A, int64_t lda,
+                               const uint16_t* B, int64_t ldb, const int64_t* rows, int64_t nrows, uint16_t* out) {
+    (void)M;
+    return gemm_rows(FMT_BF16, N, K, A, lda, B, ldb, rows, nrows, out);
+}
+
+int oracle_gemm_relu_bf16_cols(int64_t M, int64_t N, int64_t K, const uint16_t* A, int64_t lda,
+                               const uint16_t* B, int64_t ldb, const int64_t* cols, int64_t ncols, uint16_t* out) {
+    (void)N;
+    return gemm_cols(FMT_BF16, M, K, A, lda, B, ldb, cols, ncols, out);
+}
+
+int oracle_gemm_relu_bf16_elems(int64_t M, int64_t N, int64_t K, const uint16_t* A, int64_t lda,
+                                const uint16_t* B, int64_t ldb, const int64_t* ii, const int64_t* jj, int64_t n,
+                                uint16_t* out) {
+    (void)M;
+    (void)N;
+    return gemm_elems(FMT_BF16, K, A, lda, B, ldb, ii, jj, n, out);
 }

@@ -10,7 +10,8 @@ Recipe (one CPU ``torch.Generator`` per workload, A drawn first, then B):
     programming basics", section 2; "Writing high-performance kernels in
     TileLang", section "Writing a GEMM");
   * for the MLP-projection and small-M shapes B is scaled by K^-1/2 in fp32;
-  * each fp32 value is rounded to fp16 (round to nearest even) by torch.
+  * each fp32 value is rounded to fp16 (round to nearest even) by torch; the
+    bfloat16 variants (``fmt="bf16"``) round the same fp32 draws to bfloat16.
 """
 from __future__ import annotations
 
@@ -47,44 +48,54 @@ def _torch():
     return torch
 
 
-def normal_f16(shape, gen, scale: float | None = None) -> np.ndarray:
-    """N(0,1) (times ``scale``) drawn in fp32, rounded to fp16; returns uint16 bits."""
+FORMATS = ("f16", "bf16")
+
+# Largest finite value of each format, as bits: the default padding pattern.
+LARGEST_FINITE = {"f16": 0x7BFF, "bf16": 0x7F7F}
+
+
+def normal_f16(shape, gen, scale: float | None = None, fmt: str = "f16") -> np.ndarray:
+    """N(0,1) (times ``scale``) drawn in fp32, rounded to fp16 (or bfloat16 with
+    ``fmt="bf16"``); returns uint16 bits."""
     torch = _torch()
+    if fmt not in FORMATS:
+        raise ValueError("fmt must be one of %s" % (FORMATS,))
     x = torch.randn(*shape, generator=gen, dtype=torch.float32)
     if scale is not None:
         x.mul_(scale)
-    return x.to(torch.float16).view(torch.int16).numpy().view(np.uint16)
+    dt = torch.bfloat16 if fmt == "bf16" else torch.float16
+    return x.to(dt).view(torch.int16).numpy().view(np.uint16)
 
 
-def operands(w: Workload):
+def operands(w: Workload, fmt: str = "f16"):
     """(A, B) as packed row-major uint16 arrays for workload ``w``."""
     torch = _torch()
     gen = torch.Generator().manual_seed(w.seed)
-    A = normal_f16((w.M, w.K), gen)
-    B = normal_f16((w.K, w.N), gen, scale=(w.K ** -0.5) if w.b_scaled else None)
+    A = normal_f16((w.M, w.K), gen, fmt=fmt)
+    B = normal_f16((w.K, w.N), gen, scale=(w.K ** -0.5) if w.b_scaled else None, fmt=fmt)
     return A, B
 
 
 def random_operands(M: int, N: int, K: int, seed: int, lda: int | None = None,
                     ldb: int | None = None, pad_value: int | None = None,
-                    b_scale: float | None = None):
+                    b_scale: float | None = None, fmt: str = "f16"):
     """Random N(0,1) operands with optional row pitches.
 
-    With ``lda > K`` (``ldb > N``) the padding columns are filled with the fp16
-    bit pattern ``pad_value`` (default: 65504, the largest finite fp16), so a
-    kernel that reads padding produces visibly wrong results.
+    With ``lda > K`` (``ldb > N``) the padding columns are filled with the bit
+    pattern ``pad_value`` (default: the format's largest finite value, 65504
+    for fp16), so a kernel that reads padding produces visibly wrong results.
     """
     torch = _torch()
     gen = torch.Generator().manual_seed(seed)
     lda = K if lda is None else lda
     ldb = N if ldb is None else ldb
-    pad = 0x7BFF if pad_value is None else pad_value
+    pad = LARGEST_FINITE[fmt] if pad_value is None else pad_value
     A = np.full((M, max(lda, 1)), pad, dtype=np.uint16)
     B = np.full((K, max(ldb, 1)), pad, dtype=np.uint16)
     if M and K:
-        A[:, :K] = normal_f16((M, K), gen)
+        A[:, :K] = normal_f16((M, K), gen, fmt=fmt)
     if K and N:
-        B[:, :N] = normal_f16((K, N), gen, scale=b_scale)
+        B[:, :N] = normal_f16((K, N), gen, scale=b_scale, fmt=fmt)
     return A, B
 
 

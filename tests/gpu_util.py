@@ -67,13 +67,16 @@ def call_ws(M, N, K, dA, lda, dB, ldb, dC, ldc, ws, ws_bytes, path=None, offsets
     return st
 
 
-def as_f64(bits) -> np.ndarray:
-    return np.asarray(bits, dtype=np.uint16).view(np.float16).astype(np.float64)
+def as_f64(bits, fmt: str = "f16") -> np.ndarray:
+    b = np.asarray(bits, dtype=np.uint16)
+    if fmt == "bf16":  # the upper half of a binary32
+        return (b.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    return b.view(np.float16).astype(np.float64)
 
 
-def parity_report(got_bits, ref_bits):
-    g = as_f64(got_bits)
-    o = as_f64(ref_bits)
+def parity_report(got_bits, ref_bits, fmt: str = "f16"):
+    g = as_f64(got_bits, fmt)
+    o = as_f64(ref_bits, fmt)
     err = np.abs(g - o)
     bound = ATOL + RTOL * np.abs(o)
     bad = ~(err <= bound) | ~np.isfinite(g)
@@ -92,8 +95,8 @@ def parity_report(got_bits, ref_bits):
     return rep
 
 
-def assert_parity(got_bits, ref_bits, label=""):
-    rep = parity_report(got_bits, ref_bits)
+def assert_parity(got_bits, ref_bits, label="", fmt: str = "f16"):
+    rep = parity_report(got_bits, ref_bits, fmt)
     assert rep["violations"] == 0, "%s: %s" % (label, rep)
     return rep
 

@@ -396,6 +396,22 @@ def test_transposed_b_planner_and_checks():
                                       gr.GR_PATH_TILE_PACKED) == gr.GR_ERR_INVALID_PATH
 
 
+def test_bf16_argument_checks_need_no_gpu():
+    """The bfloat16 entry points share the fp16 argument checks, which run
+    before any HIP call; paths that need a workspace are refused."""
+    f = gr.gemm_relu_bf16
+    assert f(-1, 8, 8, BASE_A, 8, BASE_B, 8, BASE_C, 8) == gr.GR_ERR_INVALID_DIM
+    assert f(8, 8, 8, BASE_A, 7, BASE_B, 8, BASE_C, 8) == gr.GR_ERR_INVALID_LD
+    assert f(8, 8, 8, 0, 8, BASE_B, 8, BASE_C, 8) == gr.GR_ERR_NULL_PTR
+    assert f(8, 8, 8, BASE_A, 8, BASE_B, 8, BASE_A + 64, 8) == gr.GR_ERR_ALIAS
+    assert f(0, 8, 8, 0, 8, BASE_B, 8, 0, 8) == gr.GR_OK  # empty: nothing launched
+    g = gr.gemm_relu_bf16_forced
+    for path in (gr.GR_PATH_TILE_PACKED, gr.GR_PATH_SMALL_M_SPLIT, gr.GR_PATH_TILE_SPLIT, 99):
+        assert g(8, 256, 64, BASE_A, 64, BASE_B, 256, BASE_C, 256, None, path) == gr.GR_ERR_INVALID_PATH
+    assert g(300, 256, 48, BASE_A, 48, BASE_B, 256, BASE_C, 256, None, gr.GR_PATH_TILE) == gr.GR_ERR_INVALID_PATH
+    assert g(64, 256, 64, BASE_A, 64, BASE_B, 256, BASE_C, 256, None, gr.GR_PATH_SMALL_M) == gr.GR_ERR_INVALID_PATH
+
+
 def test_plan_null_output_struct():
     lib = gr.lib()
     assert lib.gemm_relu_f16_plan(8, 8, 8, BASE_A, 8, BASE_B, 8, BASE_C, 8, None) == gr.GR_ERR_INVALID_ARG
