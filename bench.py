@@ -274,6 +274,10 @@ EXTRA_SHAPES = [
     ("bfloat16, square 1024", 1024, 1024, 1024, "bf16"),
     ("bfloat16, MLP projection", 8192, 28672, 8192, "bf16"),
     ("bfloat16, small-M", 8, 16384, 8192, "bf16"),
+    ("bias + GELU, square", 4096, 4096, 4096, "epi:f16:gelu"),
+    ("bias + GELU (tanh), MLP projection", 8192, 28672, 8192, "epi:f16:gelu_tanh"),
+    ("bias + SiLU, bfloat16, MLP projection", 8192, 28672, 8192, "epi:bf16:silu"),
+    ("bias + SiLU, small-M", 8, 16384, 8192, "epi:f16:silu"),
 ]
 
 
@@ -285,13 +289,20 @@ def extra_shapes(gr, torch, reps=30):
     stream = torch.cuda.current_stream()
     for label, M, N, K, layout in EXTRA_SHAPES:
         g = torch.Generator(device="cuda").manual_seed(M + N + K)
-        dt = torch.bfloat16 if layout == "bf16" else torch.float16
+        dt = torch.bfloat16 if "bf16" in layout else torch.float16
         A = torch.randn(M, K, generator=g, device="cuda").to(dt)
         B = (torch.randn(K, N, generator=g, device="cuda") * K ** -0.5).to(dt)
         C = torch.empty(M, N, device="cuda", dtype=dt)
         row = {"shape": "%dx%dx%d" % (M, N, K), "what": label, "layout": layout}
         runs = {}
-        if layout == "bf16":
+        if layout.startswith("epi:"):
+            act = layout.split(":")[2]
+            bias = torch.randn(N, generator=g, device="cuda").to(dt)
+            fn = {"gelu": torch.nn.functional.gelu, "silu": torch.nn.functional.silu,
+                  "gelu_tanh": lambda x: torch.nn.functional.gelu(x, approximate="tanh")}[act]
+            runs["ours"] = lambda: gr.gemm_bias_act(A, B, bias, act, C, stream)
+            runs["vendor"] = lambda: fn(torch.addmm(bias, A, B, out=C))
+        elif layout == "bf16":
             runs["ours"] = lambda: gr.gemm_relu(A, B, C, stream, workspace=None)
             runs["vendor"] = lambda: torch.relu_(torch.mm(A, B, out=C))
         elif layout == "bt":

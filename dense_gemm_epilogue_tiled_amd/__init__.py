@@ -34,6 +34,17 @@ GR_PATH_TILE_PACKED = 4
 GR_PATH_SMALL_M_SPLIT = 5
 GR_PATH_TILE_SPLIT = 6
 
+GR_ACT_NONE = 0
+GR_ACT_RELU = 1
+GR_ACT_GELU = 2
+GR_ACT_GELU_TANH = 3
+GR_ACT_SILU = 4
+GR_ACT_SIGMOID = 5
+GR_ACT_TANH = 6
+
+ACT_CODES = {"none": GR_ACT_NONE, "relu": GR_ACT_RELU, "gelu": GR_ACT_GELU, "gelu_tanh": GR_ACT_GELU_TANH,
+             "silu": GR_ACT_SILU, "sigmoid": GR_ACT_SIGMOID, "tanh": GR_ACT_TANH}
+
 PATH_NAMES = {GR_PATH_NONE: "none", GR_PATH_TILE: "tile", GR_PATH_TILE_EDGE: "tile_edge",
               GR_PATH_SMALL_M: "small_m", GR_PATH_TILE_PACKED: "tile_packed",
               GR_PATH_SMALL_M_SPLIT: "small_m_split", GR_PATH_TILE_SPLIT: "tile_split"}
@@ -77,6 +88,15 @@ def lib() -> ctypes.CDLL:
                 raise RuntimeError(
                     "libgemm_relu.so is not built (%s); run `python -m dense_gemm_epilogue_tiled_amd.build` "
                     "or __graft_entry__.build()" % LIB_PATH)
+            # torch carries its own copy of the HIP and HSA runtimes.  When
+            # torch is loaded first, this library binds to that copy (same
+            # soname), so both share devices, streams and memory; loaded
+            # first, the library would pull in the system copy as a second
+            # runtime, which cannot use torch's streams or see its device.
+            try:
+                import torch  # noqa: F401
+            except ImportError:
+                pass
             l = ctypes.CDLL(LIB_PATH)
             i64, p, i32 = ctypes.c_int64, ctypes.c_void_p, ctypes.c_int
             l.gemm_relu_f16.argtypes = [i64, i64, i64, p, i64, p, i64, p, i64, p]
@@ -105,6 +125,11 @@ def lib() -> ctypes.CDLL:
             l.gemm_relu_bf16.restype = i32
             l.gemm_relu_bf16_forced.argtypes = [i64, i64, i64, p, i64, p, i64, p, i64, p, i32]
             l.gemm_relu_bf16_forced.restype = i32
+            for nm in ("gemm_bias_act_f16", "gemm_bias_act_bf16"):
+                getattr(l, nm).argtypes = [i64, i64, i64, p, i64, p, i64, p, i32, p, i64, p]
+                getattr(l, nm).restype = i32
+                getattr(l, nm + "_forced").argtypes = [i64, i64, i64, p, i64, p, i64, p, i32, p, i64, p, i32]
+                getattr(l, nm + "_forced").restype = i32
             l.gemm_relu_status_string.argtypes = [i32]
             l.gemm_relu_status_string.restype = ctypes.c_char_p
             l.gemm_relu_version.argtypes = []
@@ -191,6 +216,26 @@ def gemm_relu_bf16(M, N, K, A, lda, B, ldb, C, ldc, stream=None) -> int:
 def gemm_relu_bf16_forced(M, N, K, A, lda, B, ldb, C, ldc, stream=None, path=GR_PATH_TILE_EDGE) -> int:
     """As gemm_relu_bf16 but on the given path (GR_PATH_TILE, _TILE_EDGE or _SMALL_M)."""
     return lib().gemm_relu_bf16_forced(M, N, K, _ptr(A), lda, _ptr(B), ldb, _ptr(C), ldc, _ptr(stream), path)
+
+
+def gemm_bias_act_f16(M, N, K, A, lda, B, ldb, bias, act, C, ldc, stream=None) -> int:
+    """C := act(A.B + bias) with fp16 operands, bias (N values or None) and result."""
+    return lib().gemm_bias_act_f16(M, N, K, _ptr(A), lda, _ptr(B), ldb, _ptr(bias), act, _ptr(C), ldc, _ptr(stream))
+
+
+def gemm_bias_act_bf16(M, N, K, A, lda, B, ldb, bias, act, C, ldc, stream=None) -> int:
+    """C := act(A.B + bias) with bfloat16 operands, bias (N values or None) and result."""
+    return lib().gemm_bias_act_bf16(M, N, K, _ptr(A), lda, _ptr(B), ldb, _ptr(bias), act, _ptr(C), ldc, _ptr(stream))
+
+
+def gemm_bias_act_f16_forced(M, N, K, A, lda, B, ldb, bias, act, C, ldc, stream=None, path=GR_PATH_TILE_EDGE) -> int:
+    return lib().gemm_bias_act_f16_forced(M, N, K, _ptr(A), lda, _ptr(B), ldb, _ptr(bias), act, _ptr(C), ldc,
+                                          _ptr(stream), path)
+
+
+def gemm_bias_act_bf16_forced(M, N, K, A, lda, B, ldb, bias, act, C, ldc, stream=None, path=GR_PATH_TILE_EDGE) -> int:
+    return lib().gemm_bias_act_bf16_forced(M, N, K, _ptr(A), lda, _ptr(B), ldb, _ptr(bias), act, _ptr(C), ldc,
+                                           _ptr(stream), path)
 
 
 def gemm_relu_status_string(status: int) -> str:
@@ -291,4 +336,42 @@ def gemm_relu(a, b, out=None, stream=None, path=None, workspace="auto"):
         st = gemm_relu_f16_forced_ws(*args, ws_ptr, ws_bytes, h, path)
     if st != GR_OK:
         raise GemmReluError(st)
+    return out
+
+
+def gemm_bias_act(a, b, bias=None, act="gelu", out=None, stream=None, path=None):
+    """Tensor convenience: ``out = act(a @ b + bias)`` for 2-D fp16 or bfloat16
+    tensors on the GPU; ``bias`` is None or a 1-D tensor of N values of the
+    same dtype, ``act`` a key of ACT_CODES or a GR_ACT_* code."""
+    import torch
+    if a.dtype not in (torch.float16, torch.bfloat16) or b.dtype != a.dtype:
+        raise TypeError("a and b must both be float16 or both bfloat16")
+    if a.dim() != 2 or b.dim() != 2 or a.shape[1] != b.shape[0]:
+        raise ValueError("shapes do not form a matrix product: %s x %s" % (tuple(a.shape), tuple(b.shape)))
+    M, K = a.shape
+    N = b.shape[1]
+    code = ACT_CODES[act] if isinstance(act, str) else int(act)
+    if bias is not None:
+        if bias.dtype != a.dtype or bias.dim() != 1 or bias.shape[0] != N or (N > 1 and bias.stride(0) != 1):
+            raise ValueError("bias must be a contiguous 1-D tensor of N values of the operands' dtype")
+    if out is None:
+        out = torch.empty((M, N), dtype=a.dtype, device=a.device)
+    elif out.dtype != a.dtype:
+        raise TypeError("out must have the operands' dtype")
+    for t in (a, b, out):
+        if t.numel() and t.stride(1) != 1:
+            raise ValueError("tensors need unit column stride")
+    lda = max(a.stride(0), 1) if M > 1 else max(K, 1)
+    ldb = max(b.stride(0), 1) if K > 1 else max(N, 1)
+    ldc = max(out.stride(0), 1) if M > 1 else max(N, 1)
+    bptr = bias.data_ptr() if bias is not None and bias.numel() else None
+    h = _stream_handle(stream)
+    args = (M, N, K, a.data_ptr(), lda, b.data_ptr(), ldb, bptr, code, out.data_ptr(), ldc, h)
+    bf = a.dtype == torch.bfloat16
+    if path is None:
+        st = (gemm_bias_act_bf16 if bf else gemm_bias_act_f16)(*args)
+    else:
+        st = (gemm_bias_act_bf16_forced if bf else gemm_bias_act_f16_forced)(*args, path)
+    if st != GR_OK:
+        raise GemmReluError(st, "gemm_bias_act_bf16" if bf else "gemm_bias_act_f16")
     return out

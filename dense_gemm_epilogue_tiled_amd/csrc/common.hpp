@@ -48,13 +48,31 @@ __device__ __forceinline__ uint16_t relu_to_bf16(float x) {
     return (uint16_t)((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16);
 }
 
+// Round to nearest even bfloat16 with no ReLU (NaN stays a quiet NaN; the
+// carry of the rounding bias moves into the exponent, so the largest values
+// round to +-Inf).
+__device__ __forceinline__ uint16_t to_bf16(float x) {
+    const uint32_t u = __builtin_bit_cast(uint32_t, x);
+    if ((u & 0x7FFFFFFFu) > 0x7F800000u) return (uint16_t)((u >> 16) | 0x0040u);
+    return (uint16_t)((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16);
+}
+
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 
 // Element types of A, B and C.  Operands travel as 16-bit patterns (f16x8
 // registers); only the matrix-core instruction and the output rounding
-// depend on the type.  Accumulation is fp32 for both.
+// depend on the type.  Accumulation is fp32 for both.  kGeneral selects the
+// epilogue: false is the fused ReLU; true (the Epi<> wrapper below) is bias
+// plus a run-time activation.
 struct ElemF16 {
     static constexpr bool kIsF16 = true;
+    static constexpr bool kGeneral = false;
+    static __device__ __forceinline__ float widen(uint16_t h) {
+        return (float)__builtin_bit_cast(_Float16, h);
+    }
+    static __device__ __forceinline__ uint16_t round(float x) {
+        return __builtin_bit_cast(uint16_t, (_Float16)x);
+    }
     static __device__ __forceinline__ f32x16 mfma32(f16x8 b, f16x8 a, f32x16 c) {
         return __builtin_amdgcn_mfma_f32_32x32x16_f16(b, a, c, 0, 0, 0);
     }
@@ -66,6 +84,11 @@ struct ElemF16 {
 
 struct ElemBF16 {
     static constexpr bool kIsF16 = false;
+    static constexpr bool kGeneral = false;
+    static __device__ __forceinline__ float widen(uint16_t h) {
+        return __builtin_bit_cast(float, (uint32_t)h << 16);
+    }
+    static __device__ __forceinline__ uint16_t round(float x) { return to_bf16(x); }
     static __device__ __forceinline__ f32x16 mfma32(f16x8 b, f16x8 a, f32x16 c) {
         return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, b), __builtin_bit_cast(bf16x8, a),
                                                         c, 0, 0, 0);
@@ -80,6 +103,137 @@ struct ElemBF16 {
 template <typename E>
 __device__ __forceinline__ uint32_t relu_pack2_e(float x0, float x1) {
     return (uint32_t)E::relu_round(x0) | ((uint32_t)E::relu_round(x1) << 16);
+}
+
+// ---- epilogues beyond ReLU ------------------------------------------------------
+//
+// out[m][n] = round(act(acc[m][n] + bias[n])): a bias broadcast along the
+// rows and one of the activations the elementwise pattern lists (relu,
+// sigmoid, tanh, gelu; "Tilelang Cuda Patterns", section 1), plus SiLU and
+// the tanh form of GELU.  The activation is evaluated in fp32 on the biased
+// accumulator, then rounded once to the output type.
+
+// Activation codes (equal to the GR_ACT_* values of the C ABI).
+enum : int {
+    kActNone = 0,
+    kActRelu = 1,
+    kActGelu = 2,      // x * Phi(x) = x/2 * (1 + erf(x / sqrt 2))
+    kActGeluTanh = 3,  // x/2 * (1 + tanh(sqrt(2/pi) * (x + 0.044715 x^3)))
+    kActSilu = 4,      // x / (1 + e^-x)
+    kActSigmoid = 5,   // 1 / (1 + e^-x)
+    kActTanh = 6,
+    kActCount = 7
+};
+
+// Run-time arguments of the general epilogue, passed by value to every
+// kernel (ignored by the ReLU instantiations).
+struct EpiArgs {
+    const uint16_t* bias;  // N values of C's element type, or nullptr for none
+    int act;               // kAct*
+};
+
+// The activations in fp32, in forms built from the hardware exp2 and
+// reciprocal (v_exp_f32, v_rcp_f32: about 1 ulp each) and a few FMAs, so
+// the epilogue's vector work stays small next to the tile's matrix work:
+//   sigmoid(x) = 1 / (1 + e^-x), SiLU(x) = x sigmoid(x);
+//   tanh form of GELU: x/2 (1 + tanh u) = x / (1 + e^(-2u)) (exact identity,
+//     no cancellation for x << 0);
+//   GELU = x Phi(x) with Phi(-|x|) = erfc(|x|/sqrt 2) / 2 from the rational
+//     approximation of Abramowitz and Stegun, formula 7.1.26 (erfc(z) =
+//     t P(t) e^(-z^2), t = 1/(1 + p z), |error in erf| <= 1.5e-7), and
+//     Phi(|x|) = 1 - Phi(-|x|);
+//   tanh(a) = (1 - e^(-2a)) / (1 + e^(-2a)) for a = |x| >= 1/16, and its
+//     odd Taylor polynomial to a^5 below (relative error < 4e-9), sign
+//     restored.
+// Each is within about 2e-7 * max(1, |x|) of the exact function in absolute
+// terms, far below half an ulp of the fp16 or bfloat16 result at the sizes
+// that matter.
+namespace act {
+
+__device__ __forceinline__ float ex(float x) { return __builtin_amdgcn_exp2f(x * 1.44269504088896341f); }
+__device__ __forceinline__ float rcp(float x) { return __builtin_amdgcn_rcpf(x); }
+
+template <int A>
+__device__ __forceinline__ float apply(float x) {
+    if constexpr (A == kActRelu) {
+        return x > 0.0f ? x : 0.0f;
+    } else if constexpr (A == kActGelu) {
+        const float z = __builtin_fabsf(x) * 0.70710678118654752f;
+        const float t = rcp(1.0f + 0.3275911f * z);
+        const float poly =
+            t * (0.254829592f + t * (-0.284496736f + t * (1.421413741f + t * (-1.453152027f + t * 1.061405429f))));
+        const float q = 0.5f * poly * ex(-z * z);  // Phi(-|x|)
+        return x * (x >= 0.0f ? 1.0f - q : q);
+    } else if constexpr (A == kActGeluTanh) {
+        const float u = 0.79788456080286536f * x * (1.0f + 0.044715f * x * x);
+        return x * rcp(1.0f + ex(-2.0f * u));
+    } else if constexpr (A == kActSilu) {
+        return x * rcp(1.0f + ex(-x));
+    } else if constexpr (A == kActSigmoid) {
+        return rcp(1.0f + ex(-x));
+    } else if constexpr (A == kActTanh) {
+        const float a = __builtin_fabsf(x);
+        const float e = ex(-2.0f * a);
+        const float big = (1.0f - e) * rcp(1.0f + e);
+        const float a2 = a * a;
+        const float small = a * (1.0f + a2 * (-0.333333333f + a2 * 0.133333333f));
+        return __builtin_copysignf(a < 0.0625f ? small : big, x);
+    } else {
+        return x;
+    }
+}
+
+template <int A>
+struct Tag {
+    static constexpr int value = A;
+};
+
+// Call f(Tag<act>{}) with the activation as a compile-time constant, so the
+// per-element code has no branch on it.
+template <typename F>
+__device__ __forceinline__ void dispatch(int a, F&& f) {
+    switch (a) {
+        case kActRelu: f(Tag<kActRelu>{}); break;
+        case kActGelu: f(Tag<kActGelu>{}); break;
+        case kActGeluTanh: f(Tag<kActGeluTanh>{}); break;
+        case kActSilu: f(Tag<kActSilu>{}); break;
+        case kActSigmoid: f(Tag<kActSigmoid>{}); break;
+        case kActTanh: f(Tag<kActTanh>{}); break;
+        default: f(Tag<kActNone>{}); break;
+    }
+}
+
+}  // namespace act
+
+__device__ __forceinline__ float activate(float x, int a) {
+    switch (a) {
+        case kActRelu: return act::apply<kActRelu>(x);
+        case kActGelu: return act::apply<kActGelu>(x);
+        case kActGeluTanh: return act::apply<kActGeluTanh>(x);
+        case kActSilu: return act::apply<kActSilu>(x);
+        case kActSigmoid: return act::apply<kActSigmoid>(x);
+        case kActTanh: return act::apply<kActTanh>(x);
+        default: return x;
+    }
+}
+
+// The general-epilogue form of an element type.
+template <typename Base>
+struct Epi : Base {
+    static constexpr bool kGeneral = true;
+};
+
+// One output value: the fused ReLU, or bias + activation.  n is the output
+// column; a bias is read only for n < N.
+template <typename E>
+__device__ __forceinline__ uint16_t epi_value(float acc, int64_t n, int64_t N, const EpiArgs& ep) {
+    if constexpr (E::kGeneral) {
+        float x = acc;
+        if (ep.bias != nullptr && n < N) x += E::widen(ep.bias[n]);
+        return E::round(activate(x, ep.act));
+    } else {
+        return E::relu_round(acc);
+    }
 }
 
 // Map a 1-D workgroup id to a tile (tm, tn).
@@ -177,11 +331,94 @@ struct WaveTile {
 
 constexpr uint32_t REGION_BYTES = WaveTile<4, 4>::REGION_BYTES;  // 32 KiB for a 128 x 128 wave tile
 
+// General epilogue (bias + activation) for one wave's tile, one 32-row block
+// at a time: the wave writes the block's fp32 accumulators to its LDS region
+// (32 rows x 32*FN columns, 16-byte chunk c of row r at slot c XOR (r mod
+// chunks per row)), then reads it back with each lane on 4 consecutive
+// columns, so the bias is loaded once per lane and every store covers whole
+// row segments (8-byte stores when C's rows allow, else 2-byte ones).  Needs
+// 16 KiB (FN = 4) or 8 KiB (FN = 2) of LDS per wave; all waves call it.
+template <bool EDGE, typename E, int FM, int FN>
+__device__ __forceinline__ void store_wave_tile_general(const f32x16 (&acc)[FM][FN], uint8_t* region, uint32_t lane,
+                                                        uint16_t* __restrict__ C, int64_t ldc, int64_t row0,
+                                                        int64_t col0, int64_t row_min, int64_t M, int64_t N,
+                                                        int vec_c, const EpiArgs& ep) {
+    constexpr uint32_t COLS = 32 * FN;
+    constexpr uint32_t CHUNKS = COLS / 4;  // 16-byte fp32 chunks per row, also lanes per row on the way back
+    constexpr uint32_t ROW_BYTES = 4 * COLS;
+    constexpr uint32_t RPI = 64 / CHUNKS;  // rows per read-back instruction
+    auto off = [](uint32_t row, uint32_t chunk) -> uint32_t {
+        return row * ROW_BYTES + ((chunk ^ (row & (CHUNKS - 1))) << 4);
+    };
+    const uint32_t r_lane = lane & 31u, half = lane >> 5;
+    const uint32_t ch = lane & (CHUNKS - 1);  // this lane's chunk on the way back
+    const int64_t n = col0 + 4 * ch;
+    const bool has_bias = ep.bias != nullptr;
+    float b[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+    if (has_bias) {
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+            if (n + t < N) b[t] = E::widen(ep.bias[n + t]);
+    }
+    const bool wide = vec_c >= 4;
+    // The block loop and the read-back loop stay rolled, so the activation
+    // code exists once per kernel; only the register-indexed write of block
+    // i is unrolled (one branch per block).
+#pragma unroll 1
+    for (int i = 0; i < FM; ++i) {
+        __syncthreads();
+        // Block (i, j) holds C^T: lane l, register 4q + t is row l%32,
+        // column 32j + 8q + 4(l/32) + t, i.e. fp32 chunk 8j + 2q + l/32.
+#pragma unroll
+        for (int ii = 0; ii < FM; ++ii) {
+            if (ii != i) continue;
+#pragma unroll
+            for (int j = 0; j < FN; ++j)
+#pragma unroll
+                for (int q = 0; q < 4; ++q)
+                    *reinterpret_cast<f32x4*>(region + off(r_lane, 8u * j + 2u * q + half)) =
+                        f32x4{acc[ii][j][4 * q + 0], acc[ii][j][4 * q + 1], acc[ii][j][4 * q + 2],
+                              acc[ii][j][4 * q + 3]};
+        }
+        __syncthreads();
+        // One copy of the read-back per activation; two rows in flight.
+        act::dispatch(ep.act, [&](auto tag) {
+            constexpr int A = decltype(tag)::value;
+#pragma unroll 2
+            for (uint32_t k = 0; k < 32u / RPI; ++k) {
+                const uint32_t row = RPI * k + lane / CHUNKS;
+                const int64_t m = row0 + 32 * i + row;
+                const f32x4 v = *reinterpret_cast<const f32x4*>(region + off(row, ch));
+                if (EDGE && (m < row_min || m >= M)) continue;
+                uint16_t o[4];
+#pragma unroll
+                for (int t = 0; t < 4; ++t) o[t] = E::round(act::apply<A>(has_bias ? v[t] + b[t] : v[t]));
+                uint16_t* dst = C + m * ldc + n;
+                if (wide && (!EDGE || n + 4 <= N)) {
+                    __builtin_nontemporal_store(u32x2{(uint32_t)o[0] | ((uint32_t)o[1] << 16),
+                                                      (uint32_t)o[2] | ((uint32_t)o[3] << 16)},
+                                                reinterpret_cast<u32x2*>(dst));
+                } else {
+#pragma unroll
+                    for (int t = 0; t < 4; ++t)
+                        if (!EDGE || n + t < N) dst[t] = o[t];
+                }
+            }
+        });
+    }
+}
+
 template <bool EDGE, typename E = ElemF16, int FM, int FN>
 __device__ __forceinline__ void store_wave_tile(const f32x16 (&acc)[FM][FN], uint8_t* region, uint32_t lane,
                                                 uint16_t* __restrict__ C, int64_t ldc, int64_t row0, int64_t col0,
-                                                int64_t row_min, int64_t M, int64_t N, int vec_c) {
+                                                int64_t row_min, int64_t M, int64_t N, int vec_c,
+                                                const EpiArgs& ep) {
     using T = WaveTile<FM, FN>;
+    if constexpr (E::kGeneral) {
+        static_assert(32 * 32 * FN * 4 <= T::REGION_BYTES, "the fp32 block fits the wave's region");
+        store_wave_tile_general<EDGE, E>(acc, region, lane, C, ldc, row0, col0, row_min, M, N, vec_c, ep);
+        return;
+    }
     __syncthreads();
     const uint32_t r_lane = lane & 31u, half = lane >> 5;
 #pragma unroll

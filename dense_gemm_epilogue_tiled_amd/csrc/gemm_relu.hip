@@ -350,21 +350,22 @@ int launch(void (*kernel)(Args...), int64_t grid, int threads, hipStream_t strea
 
 template <bool GUARD, int VA, int VB, typename E>
 int launch_tile(const gr_plan_t& p, int64_t M, int64_t N, int64_t K, const uint16_t* A, int64_t lda,
-                const uint16_t* B, int64_t ldb, uint16_t* C, int64_t ldc, hipStream_t stream) {
+                const uint16_t* B, int64_t ldb, uint16_t* C, int64_t ldc, const gr::EpiArgs& ep, hipStream_t stream) {
     using namespace gr::tile;
     const uint32_t tiles_m = (uint32_t)((M + BM - 1) / BM);
     const uint32_t tiles_n = (uint32_t)((N + BN - 1) / BN);
     return launch(gemm_relu_tile_kernel<GUARD, VA, VB, false, E>, p.grid, THREADS, stream, A, B, C, M, N, K, lda,
-                  ldb, ldc, tiles_m, tiles_n, (uint32_t)p.group_m, (int)p.vec_c);
+                  ldb, ldc, tiles_m, tiles_n, (uint32_t)p.group_m, (int)p.vec_c, ep);
 }
 
 template <bool GUARD, int VA, typename E>
 int launch_tile_vb(const gr_plan_t& p, int64_t M, int64_t N, int64_t K, const uint16_t* A, int64_t lda,
-                   const uint16_t* B, int64_t ldb, uint16_t* C, int64_t ldc, hipStream_t stream) {
+                   const uint16_t* B, int64_t ldb, uint16_t* C, int64_t ldc, const gr::EpiArgs& ep,
+                   hipStream_t stream) {
     switch (p.vec_b) {
-        case 8: return launch_tile<GUARD, VA, 8, E>(p, M, N, K, A, lda, B, ldb, C, ldc, stream);
-        case 2: return launch_tile<GUARD, VA, 2, E>(p, M, N, K, A, lda, B, ldb, C, ldc, stream);
-        default: return launch_tile<GUARD, VA, 1, E>(p, M, N, K, A, lda, B, ldb, C, ldc, stream);
+        case 8: return launch_tile<GUARD, VA, 8, E>(p, M, N, K, A, lda, B, ldb, C, ldc, ep, stream);
+        case 2: return launch_tile<GUARD, VA, 2, E>(p, M, N, K, A, lda, B, ldb, C, ldc, ep, stream);
+        default: return launch_tile<GUARD, VA, 1, E>(p, M, N, K, A, lda, B, ldb, C, ldc, ep, stream);
     }
 }
 
@@ -388,12 +389,13 @@ int launch_pack(const Pack& pk, int64_t M, int64_t N, int64_t K, const uint16_t*
     return launch(gr::pack::pack_kernel, ba + bb, gr::pack::THREADS, stream, ja, jb, (uint32_t)ba);
 }
 
-// E: element type of A, B and C (the workspace paths exist for fp16 only).
+// E: element type of A, B and C and the epilogue (the workspace paths exist
+// for the fp16 ReLU only); ep: bias and activation of the general epilogue.
 template <typename E>
 int run(const gr_plan_t& p, int64_t M, int64_t N, int64_t K, const uint16_t* A, int64_t lda, const uint16_t* B,
         int64_t ldb, uint16_t* C, int64_t ldc, const Pack& pk, const SmallMSplit& sp, const TileSplit& ts,
-        uint8_t* ws, hipStream_t stream) {
-    if constexpr (!E::kIsF16) {
+        uint8_t* ws, const gr::EpiArgs& ep, hipStream_t stream) {
+    if constexpr (!E::kIsF16 || E::kGeneral) {
         if (p.path == GR_PATH_SMALL_M_SPLIT || p.path == GR_PATH_TILE_SPLIT || p.path == GR_PATH_TILE_PACKED)
             return GR_ERR_INVALID_PATH;
     }
@@ -424,9 +426,9 @@ int run(const gr_plan_t& p, int64_t M, int64_t N, int64_t K, const uint16_t* A, 
             const int vc = p.vec_c;
             const int64_t kps = ts.k_per_split;
             int st = whole ? launch(gemm_relu_tile128_kernel<false, true>, p.grid, THREADS, stream, A, B, C, M, N, K,
-                                    lda, ldb, ldc, tiles_m, tiles_n, gm, vc, part, kps)
+                                    lda, ldb, ldc, tiles_m, tiles_n, gm, vc, part, kps, ep)
                            : launch(gemm_relu_tile128_kernel<true, true>, p.grid, THREADS, stream, A, B, C, M, N, K,
-                                    lda, ldb, ldc, tiles_m, tiles_n, gm, vc, part, kps);
+                                    lda, ldb, ldc, tiles_m, tiles_n, gm, vc, part, kps, ep);
             if (st != GR_OK) return st;
             int64_t rblocks = (M * N + 255) / 256;
             if (rblocks > 2048) rblocks = 2048;
@@ -440,7 +442,7 @@ int run(const gr_plan_t& p, int64_t M, int64_t N, int64_t K, const uint16_t* A, 
             q.path = GR_PATH_TILE;
             const uint16_t* Ap = pk.a ? reinterpret_cast<const uint16_t*>(ws) : A;
             const uint16_t* Bp = pk.b ? reinterpret_cast<const uint16_t*>(ws + pk.off_b) : B;
-            return run<E>(q, M, N, pk.kp, Ap, pk.lda_p, Bp, pk.ldb_p, C, ldc, pk, sp, ts, ws, stream);
+            return run<E>(q, M, N, pk.kp, Ap, pk.lda_p, Bp, pk.ldb_p, C, ldc, pk, sp, ts, ws, ep, stream);
         }
         case GR_PATH_TILE: {
             const int64_t bm = p.block_m, bn = p.block_n;
@@ -455,39 +457,39 @@ int run(const gr_plan_t& p, int64_t M, int64_t N, int64_t K, const uint16_t* A, 
                 const int64_t no_split = 0;
                 if (whole)
                     return launch(gemm_relu_tile128_kernel<false, false, false, E>, p.grid, THREADS, stream, A, B, C,
-                                  M, N, K, lda, ldb, ldc, tiles_m, tiles_n, gm, vc, no_part, no_split);
+                                  M, N, K, lda, ldb, ldc, tiles_m, tiles_n, gm, vc, no_part, no_split, ep);
                 return launch(gemm_relu_tile128_kernel<true, false, false, E>, p.grid, THREADS, stream, A, B, C, M,
-                              N, K, lda, ldb, ldc, tiles_m, tiles_n, gm, vc, no_part, no_split);
+                              N, K, lda, ldb, ldc, tiles_m, tiles_n, gm, vc, no_part, no_split, ep);
             }
             if (K % gr::tile3::BKA == 0) {
                 using namespace gr::tile3;
                 if (whole)
                     return launch(gemm_relu_tile3_kernel<false, false, E>, p.grid, THREADS, stream, A, B, C, M, N, K,
-                                  lda, ldb, ldc, tiles_m, tiles_n, gm, vc);
+                                  lda, ldb, ldc, tiles_m, tiles_n, gm, vc, ep);
                 return launch(gemm_relu_tile3_kernel<true, false, E>, p.grid, THREADS, stream, A, B, C, M, N, K, lda,
-                              ldb, ldc, tiles_m, tiles_n, gm, vc);
+                              ldb, ldc, tiles_m, tiles_n, gm, vc, ep);
             }
             using namespace gr::tile2;
             if (whole)
                 return launch(gemm_relu_tile2_kernel<false, false, E>, p.grid, THREADS, stream, A, B, C, M, N, K, lda,
-                              ldb, ldc, tiles_m, tiles_n, gm, vc);
+                              ldb, ldc, tiles_m, tiles_n, gm, vc, ep);
             return launch(gemm_relu_tile2_kernel<true, false, E>, p.grid, THREADS, stream, A, B, C, M, N, K, lda, ldb,
-                          ldc, tiles_m, tiles_n, gm, vc);
+                          ldc, tiles_m, tiles_n, gm, vc, ep);
         }
         case GR_PATH_TILE_EDGE:
             switch (p.vec_a) {
-                case 8: return launch_tile_vb<true, 8, E>(p, M, N, K, A, lda, B, ldb, C, ldc, stream);
-                case 2: return launch_tile_vb<true, 2, E>(p, M, N, K, A, lda, B, ldb, C, ldc, stream);
-                default: return launch_tile_vb<true, 1, E>(p, M, N, K, A, lda, B, ldb, C, ldc, stream);
+                case 8: return launch_tile_vb<true, 8, E>(p, M, N, K, A, lda, B, ldb, C, ldc, ep, stream);
+                case 2: return launch_tile_vb<true, 2, E>(p, M, N, K, A, lda, B, ldb, C, ldc, ep, stream);
+                default: return launch_tile_vb<true, 1, E>(p, M, N, K, A, lda, B, ldb, C, ldc, ep, stream);
             }
         case GR_PATH_SMALL_M: {
             using namespace gr::smallm;
             const bool whole = N % NB == 0 && K % KSTEP == 0;
             if (whole)
                 return launch(gemm_relu_smallm_kernel<kSmallMWaves, kSmallMUnroll, false, E>, p.grid, p.threads,
-                              stream, A, B, C, M, N, K, lda, ldb, ldc);
+                              stream, A, B, C, M, N, K, lda, ldb, ldc, ep);
             return launch(gemm_relu_smallm_kernel<kSmallMWaves, kSmallMUnroll, true, E>, p.grid, p.threads, stream,
-                          A, B, C, M, N, K, lda, ldb, ldc);
+                          A, B, C, M, N, K, lda, ldb, ldc, ep);
         }
         default: return GR_ERR_INVALID_PATH;
     }
@@ -526,6 +528,14 @@ int plan_call(int64_t M, int64_t N, int64_t K, uintptr_t a, int64_t lda, uintptr
     return GR_OK;
 }
 
+static_assert(GR_ACT_NONE == gr::kActNone && GR_ACT_RELU == gr::kActRelu && GR_ACT_GELU == gr::kActGelu &&
+                  GR_ACT_GELU_TANH == gr::kActGeluTanh && GR_ACT_SILU == gr::kActSilu &&
+                  GR_ACT_SIGMOID == gr::kActSigmoid && GR_ACT_TANH == gr::kActTanh && gr::kActCount == 7,
+              "activation codes of the C ABI and the kernels agree");
+
+// Epilogue arguments of the fused-ReLU calls (their kernels ignore them).
+const gr::EpiArgs kReluOnly{nullptr, gr::kActRelu};
+
 int entry(int64_t M, int64_t N, int64_t K, const uint16_t* A, int64_t lda, const uint16_t* B, int64_t ldb,
           uint16_t* C, int64_t ldc, void* ws, int64_t ws_bytes, void* stream, int forced) {
     Pack pk;
@@ -538,7 +548,7 @@ int entry(int64_t M, int64_t N, int64_t K, const uint16_t* A, int64_t lda, const
     if (p.path == GR_PATH_NONE) return GR_OK;
     st = check_device();
     if (st != GR_OK) return st;
-    return run<gr::ElemF16>(p, M, N, K, A, lda, B, ldb, C, ldc, pk, sp, ts, static_cast<uint8_t*>(ws),
+    return run<gr::ElemF16>(p, M, N, K, A, lda, B, ldb, C, ldc, pk, sp, ts, static_cast<uint8_t*>(ws), kReluOnly,
                             static_cast<hipStream_t>(stream));
 }
 
@@ -555,8 +565,31 @@ int entry_bf16(int64_t M, int64_t N, int64_t K, const uint16_t* A, int64_t lda, 
     if (p.path == GR_PATH_NONE) return GR_OK;
     st = check_device();
     if (st != GR_OK) return st;
-    return run<gr::ElemBF16>(p, M, N, K, A, lda, B, ldb, C, ldc, pk, sp, ts, nullptr,
+    return run<gr::ElemBF16>(p, M, N, K, A, lda, B, ldb, C, ldc, pk, sp, ts, nullptr, kReluOnly,
                              static_cast<hipStream_t>(stream));
+}
+
+// Bias + activation epilogue (Base: element type), on the planner's paths
+// without a workspace.  The bias (N values, or none) must not overlap C.
+template <typename Base>
+int entry_epi(int64_t M, int64_t N, int64_t K, const uint16_t* A, int64_t lda, const uint16_t* B, int64_t ldb,
+              const uint16_t* bias, int act, uint16_t* C, int64_t ldc, void* stream, int forced) {
+    if (act < 0 || act >= gr::kActCount) return GR_ERR_INVALID_ARG;
+    Pack pk;
+    SmallMSplit sp;
+    TileSplit ts;
+    gr_plan_t p;
+    int st = plan_call(M, N, K, (uintptr_t)A, lda, (uintptr_t)B, ldb, (uintptr_t)C, ldc, 0, 0, true, forced, &pk, &sp,
+                       &ts, &p);
+    if (st != GR_OK) return st;
+    if (bias != nullptr && M > 0 && N > 0 &&
+        overlaps((uintptr_t)C, span_bytes(M, N, ldc), (uintptr_t)bias, 2 * N))
+        return GR_ERR_ALIAS;
+    if (p.path == GR_PATH_NONE) return GR_OK;
+    st = check_device();
+    if (st != GR_OK) return st;
+    return run<gr::Epi<Base>>(p, M, N, K, A, lda, B, ldb, C, ldc, pk, sp, ts, nullptr, gr::EpiArgs{bias, act},
+                              static_cast<hipStream_t>(stream));
 }
 
 bool known_path(int path) {
@@ -644,16 +677,18 @@ void fill_plan_bt(int path, int64_t M, int64_t N, int64_t K, uintptr_t A, int64_
 
 template <int VA, int VB>
 int launch_tile_bt(const gr_plan_t& p, int64_t M, int64_t N, int64_t K, const uint16_t* A, int64_t lda,
-                   const uint16_t* Bt, int64_t ldbt, uint16_t* C, int64_t ldc, hipStream_t stream) {
+                   const uint16_t* Bt, int64_t ldbt, uint16_t* C, int64_t ldc, const gr::EpiArgs& ep,
+                   hipStream_t stream) {
     using namespace gr::tile;
     const uint32_t tiles_m = (uint32_t)((M + BM - 1) / BM);
     const uint32_t tiles_n = (uint32_t)((N + BN - 1) / BN);
     return launch(gemm_relu_tile_kernel<true, VA, VB, true>, p.grid, THREADS, stream, A, Bt, C, M, N, K, lda, ldbt,
-                  ldc, tiles_m, tiles_n, (uint32_t)p.group_m, (int)p.vec_c);
+                  ldc, tiles_m, tiles_n, (uint32_t)p.group_m, (int)p.vec_c, ep);
 }
 
 int run_bt(const gr_plan_t& p, int64_t M, int64_t N, int64_t K, const uint16_t* A, int64_t lda, const uint16_t* Bt,
            int64_t ldbt, uint16_t* C, int64_t ldc, hipStream_t stream) {
+    const gr::EpiArgs ep{nullptr, gr::kActRelu};  // the fused ReLU kernels ignore it
     switch (p.path) {
         case GR_PATH_NONE: return GR_OK;
         case GR_PATH_SMALL_M: {
@@ -687,36 +722,36 @@ int run_bt(const gr_plan_t& p, int64_t M, int64_t N, int64_t K, const uint16_t* 
                 const int64_t no_split = 0;
                 if (whole)
                     return launch(gemm_relu_tile128_kernel<false, false, true>, p.grid, THREADS, stream, A, Bt, C, M,
-                                  N, K, lda, ldbt, ldc, tiles_m, tiles_n, gm, vc, no_part, no_split);
+                                  N, K, lda, ldbt, ldc, tiles_m, tiles_n, gm, vc, no_part, no_split, ep);
                 return launch(gemm_relu_tile128_kernel<true, false, true>, p.grid, THREADS, stream, A, Bt, C, M, N,
-                              K, lda, ldbt, ldc, tiles_m, tiles_n, gm, vc, no_part, no_split);
+                              K, lda, ldbt, ldc, tiles_m, tiles_n, gm, vc, no_part, no_split, ep);
             }
             if (K % gr::tile3::BKA == 0) {
                 using namespace gr::tile3;
                 if (whole)
                     return launch(gemm_relu_tile3_kernel<false, true>, p.grid, THREADS, stream, A, Bt, C, M, N, K,
-                                  lda, ldbt, ldc, tiles_m, tiles_n, gm, vc);
+                                  lda, ldbt, ldc, tiles_m, tiles_n, gm, vc, ep);
                 return launch(gemm_relu_tile3_kernel<true, true>, p.grid, THREADS, stream, A, Bt, C, M, N, K, lda,
-                              ldbt, ldc, tiles_m, tiles_n, gm, vc);
+                              ldbt, ldc, tiles_m, tiles_n, gm, vc, ep);
             }
             using namespace gr::tile2;
             if (whole)
                 return launch(gemm_relu_tile2_kernel<false, true>, p.grid, THREADS, stream, A, Bt, C, M, N, K, lda,
-                              ldbt, ldc, tiles_m, tiles_n, gm, vc);
+                              ldbt, ldc, tiles_m, tiles_n, gm, vc, ep);
             return launch(gemm_relu_tile2_kernel<true, true>, p.grid, THREADS, stream, A, Bt, C, M, N, K, lda, ldbt,
-                          ldc, tiles_m, tiles_n, gm, vc);
+                          ldc, tiles_m, tiles_n, gm, vc, ep);
         }
         case GR_PATH_TILE_EDGE: {
             const int va = p.vec_a, vb = p.vec_b;
-            if (va == 8 && vb == 8) return launch_tile_bt<8, 8>(p, M, N, K, A, lda, Bt, ldbt, C, ldc, stream);
-            if (va == 8 && vb == 2) return launch_tile_bt<8, 2>(p, M, N, K, A, lda, Bt, ldbt, C, ldc, stream);
-            if (va == 8) return launch_tile_bt<8, 1>(p, M, N, K, A, lda, Bt, ldbt, C, ldc, stream);
-            if (va == 2 && vb == 8) return launch_tile_bt<2, 8>(p, M, N, K, A, lda, Bt, ldbt, C, ldc, stream);
-            if (va == 2 && vb == 2) return launch_tile_bt<2, 2>(p, M, N, K, A, lda, Bt, ldbt, C, ldc, stream);
-            if (va == 2) return launch_tile_bt<2, 1>(p, M, N, K, A, lda, Bt, ldbt, C, ldc, stream);
-            if (vb == 8) return launch_tile_bt<1, 8>(p, M, N, K, A, lda, Bt, ldbt, C, ldc, stream);
-            if (vb == 2) return launch_tile_bt<1, 2>(p, M, N, K, A, lda, Bt, ldbt, C, ldc, stream);
-            return launch_tile_bt<1, 1>(p, M, N, K, A, lda, Bt, ldbt, C, ldc, stream);
+            if (va == 8 && vb == 8) return launch_tile_bt<8, 8>(p, M, N, K, A, lda, Bt, ldbt, C, ldc, ep, stream);
+            if (va == 8 && vb == 2) return launch_tile_bt<8, 2>(p, M, N, K, A, lda, Bt, ldbt, C, ldc, ep, stream);
+            if (va == 8) return launch_tile_bt<8, 1>(p, M, N, K, A, lda, Bt, ldbt, C, ldc, ep, stream);
+            if (va == 2 && vb == 8) return launch_tile_bt<2, 8>(p, M, N, K, A, lda, Bt, ldbt, C, ldc, ep, stream);
+            if (va == 2 && vb == 2) return launch_tile_bt<2, 2>(p, M, N, K, A, lda, Bt, ldbt, C, ldc, ep, stream);
+            if (va == 2) return launch_tile_bt<2, 1>(p, M, N, K, A, lda, Bt, ldbt, C, ldc, ep, stream);
+            if (vb == 8) return launch_tile_bt<1, 8>(p, M, N, K, A, lda, Bt, ldbt, C, ldc, ep, stream);
+            if (vb == 2) return launch_tile_bt<1, 2>(p, M, N, K, A, lda, Bt, ldbt, C, ldc, ep, stream);
+            return launch_tile_bt<1, 1>(p, M, N, K, A, lda, Bt, ldbt, C, ldc, ep, stream);
         }
         default: return GR_ERR_INVALID_PATH;
     }
@@ -765,6 +800,30 @@ int gemm_relu_bf16_forced(int64_t M, int64_t N, int64_t K, const uint16_t* A, in
                           int64_t ldb, uint16_t* C, int64_t ldc, void* stream, int path) {
     if (path != GR_PATH_TILE && path != GR_PATH_TILE_EDGE && path != GR_PATH_SMALL_M) return GR_ERR_INVALID_PATH;
     return entry_bf16(M, N, K, A, lda, B, ldb, C, ldc, stream, path);
+}
+
+int gemm_bias_act_f16(int64_t M, int64_t N, int64_t K, const uint16_t* A, int64_t lda, const uint16_t* B,
+                      int64_t ldb, const uint16_t* bias, int act, uint16_t* C, int64_t ldc, void* stream) {
+    return entry_epi<gr::ElemF16>(M, N, K, A, lda, B, ldb, bias, act, C, ldc, stream, -1);
+}
+
+int gemm_bias_act_f16_forced(int64_t M, int64_t N, int64_t K, const uint16_t* A, int64_t lda, const uint16_t* B,
+                             int64_t ldb, const uint16_t* bias, int act, uint16_t* C, int64_t ldc, void* stream,
+                             int path) {
+    if (path != GR_PATH_TILE && path != GR_PATH_TILE_EDGE && path != GR_PATH_SMALL_M) return GR_ERR_INVALID_PATH;
+    return entry_epi<gr::ElemF16>(M, N, K, A, lda, B, ldb, bias, act, C, ldc, stream, path);
+}
+
+int gemm_bias_act_bf16(int64_t M, int64_t N, int64_t K, const uint16_t* A, int64_t lda, const uint16_t* B,
+                       int64_t ldb, const uint16_t* bias, int act, uint16_t* C, int64_t ldc, void* stream) {
+    return entry_epi<gr::ElemBF16>(M, N, K, A, lda, B, ldb, bias, act, C, ldc, stream, -1);
+}
+
+int gemm_bias_act_bf16_forced(int64_t M, int64_t N, int64_t K, const uint16_t* A, int64_t lda, const uint16_t* B,
+                              int64_t ldb, const uint16_t* bias, int act, uint16_t* C, int64_t ldc, void* stream,
+                              int path) {
+    if (path != GR_PATH_TILE && path != GR_PATH_TILE_EDGE && path != GR_PATH_SMALL_M) return GR_ERR_INVALID_PATH;
+    return entry_epi<gr::ElemBF16>(M, N, K, A, lda, B, ldb, bias, act, C, ldc, stream, path);
 }
 
 int gemm_relu_f16_bt(int64_t M, int64_t N, int64_t K, const uint16_t* A, int64_t lda, const uint16_t* Bt,

@@ -100,7 +100,7 @@ __device__ __forceinline__ u32x4 load_a8(const uint16_t* A, int64_t lda, int64_t
 template <int W, int U, bool GUARD, typename E = ElemF16>
 __global__ __launch_bounds__(64 * W, 1) void gemm_relu_smallm_kernel(
     const uint16_t* __restrict__ A, const uint16_t* __restrict__ B, uint16_t* __restrict__ C,
-    int64_t M, int64_t N, int64_t K, int64_t lda, int64_t ldb, int64_t ldc) {
+    int64_t M, int64_t N, int64_t K, int64_t lda, int64_t ldb, int64_t ldc, EpiArgs ep) {
     __shared__ __attribute__((aligned(16))) float red[W][MAX_M][NB];
 
     const uint32_t tid = threadIdx.x;
@@ -178,7 +178,7 @@ __global__ __launch_bounds__(64 * W, 1) void gemm_relu_smallm_kernel(
             float sum = 0.0f;
 #pragma unroll
             for (int w = 0; w < W; ++w) sum += red[w][m][nl];
-            C[(int64_t)m * ldc + n] = E::relu_round(sum);
+            C[(int64_t)m * ldc + n] = epi_value<E>(sum, n, N, ep);
         }
     }
 }

@@ -75,7 +75,7 @@ template <bool EDGE, bool SPLIT, bool BT = false, typename E = ElemF16>
 __global__ __launch_bounds__(THREADS, 2) void gemm_relu_tile128_kernel(
     const uint16_t* __restrict__ A, const uint16_t* __restrict__ B, uint16_t* __restrict__ C, int64_t M, int64_t N,
     int64_t K, int64_t lda, int64_t ldb, int64_t ldc, uint32_t tiles_m, uint32_t tiles_n, uint32_t group_m,
-    int vec_c, float* __restrict__ part, int64_t k_per_split) {
+    int vec_c, float* __restrict__ part, int64_t k_per_split, EpiArgs ep) {
     using tile2::barrier;
     using tile2::dma16;
     using tile2::read_a_operand;
@@ -235,7 +235,7 @@ __global__ __launch_bounds__(THREADS, 2) void gemm_relu_tile128_kernel(
     } else {
         // Epilogue: ReLU, fp16 and the store of C, staged through LDS.
         epi::store_wave_tile<EDGE, E>(acc, lds + wave * epi::WaveTile<FM, FN>::REGION_BYTES, lane, C, ldc,
-                                   m0 + wm * WAVE_TM, n0 + wn * WAVE_TN, m0, M, N, vec_c);
+                                   m0 + wm * WAVE_TM, n0 + wn * WAVE_TN, m0, M, N, vec_c, ep);
         (void)part;
     }
 }

@@ -127,7 +127,7 @@ template <bool EDGE, bool BT = false, typename E = ElemF16>
 __global__ __launch_bounds__(THREADS, 1) void gemm_relu_tile2_kernel(
     const uint16_t* __restrict__ A, const uint16_t* __restrict__ B, uint16_t* __restrict__ C, int64_t M, int64_t N,
     int64_t K, int64_t lda, int64_t ldb, int64_t ldc, uint32_t tiles_m, uint32_t tiles_n, uint32_t group_m,
-    int vec_c) {
+    int vec_c, EpiArgs ep) {
     __shared__ __attribute__((aligned(1024))) uint8_t lds[LDS_BYTES];
 
     const uint32_t tid = threadIdx.x;
@@ -343,7 +343,7 @@ __global__ __launch_bounds__(THREADS, 1) void gemm_relu_tile2_kernel(
     // Epilogue: ReLU, fp16 and the store of C, staged through LDS (the
     // operand ring is no longer needed).
     epi::store_wave_tile<EDGE, E>(acc, lds + wave * epi::REGION_BYTES, lane, C, ldc, m0 + wm * WAVE_TM,
-                               n0 + wn * WAVE_TN, m_tile, M, N, vec_c);
+                               n0 + wn * WAVE_TN, m_tile, M, N, vec_c, ep);
 }
 
 #undef GR_LDS

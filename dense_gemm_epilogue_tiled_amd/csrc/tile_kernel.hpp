@@ -117,7 +117,7 @@ template <bool GUARD, int VA, int VB, bool BT = false, typename E = ElemF16>
 __global__ __launch_bounds__(THREADS, 1) void gemm_relu_tile_kernel(
     const uint16_t* __restrict__ A, const uint16_t* __restrict__ B, uint16_t* __restrict__ C,
     int64_t M, int64_t N, int64_t K, int64_t lda, int64_t ldb, int64_t ldc,
-    uint32_t tiles_m, uint32_t tiles_n, uint32_t group_m, int vec_c) {
+    uint32_t tiles_m, uint32_t tiles_n, uint32_t group_m, int vec_c, EpiArgs ep) {
     __shared__ __attribute__((aligned(1024))) uint8_t lds[LDS_BYTES];
 
     const uint32_t tid = threadIdx.x;
@@ -215,6 +215,15 @@ __global__ __launch_bounds__(THREADS, 1) void gemm_relu_tile_kernel(
 
         if (kt + 1 < KT) store_tiles(stage ^ 1u);
         __syncthreads();
+    }
+
+    if constexpr (E::kGeneral) {
+        // Bias + activation through LDS (the operand stages are free now:
+        // the K loop ends with a barrier).
+        static_assert(4 * 16384 <= LDS_BYTES, "four 16 KiB wave regions");
+        epi::store_wave_tile_general<GUARD, E>(acc, lds + wave * 16384u, lane, C, ldc, m0 + wm * WAVE_TM,
+                                               n0 + wn * WAVE_TN, 0, M, N, vec_c, ep);
+        return;
     }
 
     // Epilogue.  Block (i, j) holds C^T: lane l, register r is

@@ -1,6 +1,6 @@
 /*
  * gemm_relu.h -- C ABI of the MI355X (gfx950) fused fp16 GEMM + ReLU library
- * (with bfloat16 and transposed-B variants further down).
+ * (with bfloat16, transposed-B and bias + activation variants further down).
  *
  * The one operation:  C := ReLU(A * B)
  *   A  M x K, B  K x N, C  M x N, all IEEE binary16, row-major with a row
@@ -305,6 +305,72 @@ int gemm_relu_bf16_forced(int64_t M, int64_t N, int64_t K,
                           const uint16_t* B, int64_t ldb,
                           uint16_t* C, int64_t ldc,
                           void* stream, int path);
+
+/*
+ * ---- bias and other activations -------------------------------------------------
+ * C := act(A * B + bias), the same tiled GEMM with a wider epilogue: bias is
+ * a row vector of N values broadcast down the columns (bias[n] is added to
+ * every element of column n; NULL for none), and act is one of the GR_ACT_*
+ * codes below, applied to the fp32 sum.  The result is rounded once to the
+ * output type (nearest, ties to even).  The elementwise pattern of "Tilelang
+ * Cuda Patterns", section 1, lists relu, sigmoid, tanh and gelu among the
+ * activations and a broadcast among the operations; the tutorial's GEMM
+ * chapters fuse such elementwise work into the write-back of the fp32
+ * fragment.  The activations, on x = acc + bias[n] in fp32:
+ *   GR_ACT_NONE       x (a plain GEMM; negative values are kept)
+ *   GR_ACT_RELU       x > 0 ? x : +0 (with bias NULL: bit for bit gemm_relu_*)
+ *   GR_ACT_GELU       x * Phi(x) = x/2 * (1 + erf(x / sqrt(2)))
+ *   GR_ACT_GELU_TANH  x/2 * (1 + tanh(sqrt(2/pi) * (x + 0.044715 x^3)))
+ *   GR_ACT_SILU       x / (1 + exp(-x))
+ *   GR_ACT_SIGMOID    1 / (1 + exp(-x))
+ *   GR_ACT_TANH       tanh(x)
+ * The transcendental functions are the device library's fp32 ones (a few
+ * ulp of fp32, far below the output's rounding).  A, B, bias and C share the
+ * element type: fp16 for gemm_bias_act_f16, bfloat16 for gemm_bias_act_bf16.
+ * Every convention of gemm_relu_f16 holds; in addition GR_ERR_INVALID_ARG
+ * for an unknown act and GR_ERR_ALIAS when the bias overlaps C.  K == 0
+ * gives C = act(bias) (act(0) without a bias).  Paths: GR_PATH_SMALL_M,
+ * GR_PATH_TILE, GR_PATH_TILE_EDGE, chosen as gemm_relu_f16_plan says; no
+ * workspace variant.
+ */
+#define GR_ACT_NONE        0
+#define GR_ACT_RELU        1
+#define GR_ACT_GELU        2
+#define GR_ACT_GELU_TANH   3
+#define GR_ACT_SILU        4
+#define GR_ACT_SIGMOID     5
+#define GR_ACT_TANH        6
+
+int gemm_bias_act_f16(int64_t M, int64_t N, int64_t K,
+                      const uint16_t* A, int64_t lda,
+                      const uint16_t* B, int64_t ldb,
+                      const uint16_t* bias, int act,
+                      uint16_t* C, int64_t ldc,
+                      void* stream);
+
+int gemm_bias_act_bf16(int64_t M, int64_t N, int64_t K,
+                       const uint16_t* A, int64_t lda,
+                       const uint16_t* B, int64_t ldb,
+                       const uint16_t* bias, int act,
+                       uint16_t* C, int64_t ldc,
+                       void* stream);
+
+/* The two calls above on a given path (GR_PATH_TILE, GR_PATH_TILE_EDGE or
+   GR_PATH_SMALL_M; GR_ERR_INVALID_PATH otherwise or when the path's
+   conditions do not hold).  Test hooks. */
+int gemm_bias_act_f16_forced(int64_t M, int64_t N, int64_t K,
+                             const uint16_t* A, int64_t lda,
+                             const uint16_t* B, int64_t ldb,
+                             const uint16_t* bias, int act,
+                             uint16_t* C, int64_t ldc,
+                             void* stream, int path);
+
+int gemm_bias_act_bf16_forced(int64_t M, int64_t N, int64_t K,
+                              const uint16_t* A, int64_t lda,
+                              const uint16_t* B, int64_t ldb,
+                              const uint16_t* bias, int act,
+                              uint16_t* C, int64_t ldc,
+                              void* stream, int path);
 
 /* Static, NUL-terminated name of a status code ("GR_OK", "GR_ERR_ALIAS", ...).
    Unknown codes give "GR_ERR_UNKNOWN". */

@@ -33,6 +33,9 @@ _CFLAGS = ["-O2", "-std=c11", "-fno-fast-math", "-ffp-contract=off", "-fopenmp",
 
 _FMTS = ("f16", "bf16")
 
+# Activation names and their codes (the library's GR_ACT_* values).
+ACTS = {"none": 0, "relu": 1, "gelu": 2, "gelu_tanh": 3, "silu": 4, "sigmoid": 5, "tanh": 6}
+
 _lock = threading.Lock()
 _lib = None
 
@@ -78,6 +81,15 @@ def _load():
                     i64, i64, i64, p, i64, p, i64, p, p, i64, p]
                 for name in ("full", "rows", "cols", "elems"):
                     getattr(lib, "oracle_gemm_relu_%s_%s" % (fmt, name)).restype = ctypes.c_int
+            lib.oracle_gemm_epi_full.argtypes = [ctypes.c_int, p, ctypes.c_int, i64, i64, i64, p, i64, p, i64, p, i64]
+            lib.oracle_gemm_epi_rows.argtypes = [ctypes.c_int, p, ctypes.c_int, i64, i64, i64, p, i64, p, i64, p,
+                                                 i64, p]
+            lib.oracle_gemm_epi_cols.argtypes = [ctypes.c_int, p, ctypes.c_int, i64, i64, i64, p, i64, p, i64, p,
+                                                 i64, p]
+            lib.oracle_gemm_epi_elems.argtypes = [ctypes.c_int, p, ctypes.c_int, i64, i64, i64, p, i64, p, i64, p, p,
+                                                  i64, p]
+            for name in ("full", "rows", "cols", "elems"):
+                getattr(lib, "oracle_gemm_epi_" + name).restype = ctypes.c_int
             _lib = lib
     return _lib
 
@@ -143,14 +155,40 @@ def f32_to_bf16(vals: np.ndarray) -> np.ndarray:
     return out.reshape(np.shape(vals))
 
 
-def _entry(lib, fmt, name):
+def _entry(lib, fmt, name, bias=None, act="relu", N=None):
+    """The C routine for (fmt, name): the fused-ReLU entry points, or, with a
+    bias or another activation, the general epilogue with its first three
+    arguments (format, bias pointer, activation code) bound."""
     if fmt not in _FMTS:
         raise ValueError("fmt must be one of %s" % (_FMTS,))
-    return getattr(lib, "oracle_gemm_relu_%s_%s" % (fmt, name))
+    if act not in ACTS:
+        raise ValueError("act must be one of %s" % (sorted(ACTS),))
+    if bias is None and act == "relu":
+        return getattr(lib, "oracle_gemm_relu_%s_%s" % (fmt, name))
+    bptr = 0
+    if bias is not None:
+        if bias.dtype != np.uint16 or not bias.flags.c_contiguous or bias.ndim != 1:
+            raise TypeError("bias must be a contiguous 1-D uint16 array of bit patterns")
+        if N is not None and bias.size < N:
+            raise ValueError("bias needs N values")
+        bptr = _ptr(bias)
+    fn = getattr(lib, "oracle_gemm_epi_" + name)
+    code = _FMTS.index(fmt)
+
+    def call(*args):
+        rc = fn(code, bptr, ACTS[act], *args)
+        if rc == -2:
+            raise ValueError("bad format or activation")
+        return rc
+    return call
 
 
-def gemm_relu_full(A, B, M=None, N=None, K=None, lda=None, ldb=None, threads=None, fmt="f16"):
-    """The whole M x N result as fp16 (or bf16, fmt="bf16") bits (packed, ldc = N)."""
+def gemm_relu_full(A, B, M=None, N=None, K=None, lda=None, ldb=None, threads=None, fmt="f16", bias=None, act="relu"):
+    """The whole M x N result as fp16 (or bf16, fmt="bf16") bits (packed, ldc = N).
+
+    With ``bias`` (N values, same format) and/or ``act`` (a key of ACTS) the
+    result is act(A.B + bias) instead of ReLU(A.B); the same holds for the
+    rows, cols and elems variants."""
     M, N, K, lda, ldb = _dims(A, B, M, N, K, lda, ldb)
     _check_operands(A, B, M, N, K, lda, ldb)
     lib = _load()
@@ -158,13 +196,13 @@ def gemm_relu_full(A, B, M=None, N=None, K=None, lda=None, ldb=None, threads=Non
         lib.oracle_set_threads(int(threads))
     C = np.zeros((M, N), dtype=np.uint16)
     if M > 0 and N > 0:
-        rc = _entry(lib, fmt, "full")(M, N, K, _ptr(A), lda, _ptr(B), ldb, _ptr(C), N)
+        rc = _entry(lib, fmt, "full", bias, act, N)(M, N, K, _ptr(A), lda, _ptr(B), ldb, _ptr(C), N)
         if rc != 0:
             raise MemoryError("oracle allocation failed")
     return C
 
 
-def gemm_relu_rows(A, B, rows, M=None, N=None, K=None, lda=None, ldb=None, threads=None, fmt="f16"):
+def gemm_relu_rows(A, B, rows, M=None, N=None, K=None, lda=None, ldb=None, threads=None, fmt="f16", bias=None, act="relu"):
     """Full rows ``rows`` of the result: array (len(rows), N) of fp16 / bf16 bits."""
     M, N, K, lda, ldb = _dims(A, B, M, N, K, lda, ldb)
     _check_operands(A, B, M, N, K, lda, ldb)
@@ -176,13 +214,13 @@ def gemm_relu_rows(A, B, rows, M=None, N=None, K=None, lda=None, ldb=None, threa
         lib.oracle_set_threads(int(threads))
     out = np.zeros((r.size, N), dtype=np.uint16)
     if r.size and N > 0:
-        rc = _entry(lib, fmt, "rows")(M, N, K, _ptr(A), lda, _ptr(B), ldb, _ptr(r), r.size, _ptr(out))
+        rc = _entry(lib, fmt, "rows", bias, act, N)(M, N, K, _ptr(A), lda, _ptr(B), ldb, _ptr(r), r.size, _ptr(out))
         if rc != 0:
             raise MemoryError("oracle allocation failed")
     return out
 
 
-def gemm_relu_cols(A, B, cols, M=None, N=None, K=None, lda=None, ldb=None, threads=None, fmt="f16"):
+def gemm_relu_cols(A, B, cols, M=None, N=None, K=None, lda=None, ldb=None, threads=None, fmt="f16", bias=None, act="relu"):
     """Full columns ``cols`` of the result: array (len(cols), M) of fp16 / bf16 bits."""
     M, N, K, lda, ldb = _dims(A, B, M, N, K, lda, ldb)
     _check_operands(A, B, M, N, K, lda, ldb)
@@ -194,13 +232,13 @@ def gemm_relu_cols(A, B, cols, M=None, N=None, K=None, lda=None, ldb=None, threa
         lib.oracle_set_threads(int(threads))
     out = np.zeros((c.size, M), dtype=np.uint16)
     if c.size and M > 0:
-        rc = _entry(lib, fmt, "cols")(M, N, K, _ptr(A), lda, _ptr(B), ldb, _ptr(c), c.size, _ptr(out))
+        rc = _entry(lib, fmt, "cols", bias, act, N)(M, N, K, _ptr(A), lda, _ptr(B), ldb, _ptr(c), c.size, _ptr(out))
         if rc != 0:
             raise MemoryError("oracle allocation failed")
     return out
 
 
-def gemm_relu_elems(A, B, ii, jj, M=None, N=None, K=None, lda=None, ldb=None, threads=None, fmt="f16"):
+def gemm_relu_elems(A, B, ii, jj, M=None, N=None, K=None, lda=None, ldb=None, threads=None, fmt="f16", bias=None, act="relu"):
     """Single elements C[ii[e], jj[e]] as fp16 / bf16 bits."""
     M, N, K, lda, ldb = _dims(A, B, M, N, K, lda, ldb)
     _check_operands(A, B, M, N, K, lda, ldb)
@@ -215,7 +253,7 @@ def gemm_relu_elems(A, B, ii, jj, M=None, N=None, K=None, lda=None, ldb=None, th
         lib.oracle_set_threads(int(threads))
     out = np.zeros(i.size, dtype=np.uint16)
     if i.size:
-        _entry(lib, fmt, "elems")(M, N, K, _ptr(A), lda, _ptr(B), ldb, _ptr(i), _ptr(j), i.size, _ptr(out))
+        _entry(lib, fmt, "elems", bias, act, N)(M, N, K, _ptr(A), lda, _ptr(B), ldb, _ptr(i), _ptr(j), i.size, _ptr(out))
     return out
 
 

@@ -43,7 +43,24 @@
  * bfloat16 numbers needs at most 16 significand bits and stays in the fp32
  * range only if the exponents allow; the tests use magnitudes where it is
  * exact, as for fp16.
+ *
+ * The *_epi_* entry points generalise steps 3 and 4 to C = act(A*B + bias):
+ *   3'. x = acc, plus fl32(acc + bias[j]) when a bias (one value per output
+ *       column, in the operands' format) is given: the bias is broadcast down
+ *       the columns, one of the elementwise operations of "Tilelang Cuda
+ *       Patterns", section 1.
+ *   4'. y = act(x) for one of the activations that section lists (relu,
+ *       sigmoid, tanh, gelu), plus SiLU and the tanh form of GELU, evaluated
+ *       in double precision with the C library (erf, tanh, exp); then y is
+ *       rounded once to the output format, nearest with ties to even.  ReLU
+ *       and the identity stay in fp32 (they are exact) and round as in step 4.
+ * The single rounding from double goes through fp32 with round-to-odd (the
+ * nearest fp32 toward zero with its last bit forced to 1 when inexact), which
+ * keeps two or more spare bits over the fp16 and bfloat16 significands, so
+ * the final round-to-nearest-even sees the same side of every midpoint as the
+ * exact double would.
  */
+#include <math.h>
 #include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
@@ -159,12 +176,59 @@ void oracle_f32_to_f16_array(const float* in, uint16_t* out, int64_t n) {
 /* Element formats of A, B and C. */
 enum { FMT_F16 = 0, FMT_BF16 = 1 };
 
+/* Activations (the same codes as the library's GR_ACT_*). */
+enum { ACT_NONE = 0, ACT_RELU = 1, ACT_GELU = 2, ACT_GELU_TANH = 3, ACT_SILU = 4, ACT_SIGMOID = 5, ACT_TANH = 6,
+       ACT_COUNT = 7 };
+
+/* The epilogue of one call: bias (N values, or NULL) and activation. */
+typedef struct {
+    const uint16_t* bias;
+    int act;
+} Epi;
+
+static const Epi kRelu = {NULL, ACT_RELU};
+
 static float widen(int fmt, uint16_t h) { return fmt == FMT_BF16 ? oracle_bf16_to_f32(h) : oracle_f16_to_f32(h); }
 
-/* ReLU on the fp32 accumulator followed by the write-back rounding. */
-static uint16_t epilogue(int fmt, float acc) {
-    float r = (acc > 0.0f) ? acc : 0.0f; /* NaN compares false -> +0 */
+static uint16_t round_to(int fmt, float r) {
     return fmt == FMT_BF16 ? oracle_f32_to_bf16_rne(r) : oracle_f32_to_f16_rne(r);
+}
+
+/* Nearest fp32 toward zero, last bit forced to 1 when d is not exact in fp32
+   (round-to-odd).  Beyond the fp32 range this gives the largest finite fp32
+   with that sign, which still rounds to Inf in both 16-bit formats. */
+static float f64_to_f32_odd(double d) {
+    float f = (float)d;
+    if (isnan(d) || isinf(d) || (double)f == d) return f;
+    if (fabs((double)f) > fabs(d)) f = nextafterf(f, 0.0f);
+    return bits_to_f32(f32_to_bits(f) | 1u);
+}
+
+/* The activations in double precision, from their definitions.  For x far
+   below zero, 1 + erf(x/sqrt 2) and 1 + tanh(u) cancel to nothing; the same
+   values are written with functions that keep their precision there:
+   1 + erf(z) = erfc(-z), and (1 + tanh u) / 2 = 1 / (1 + e^(-2u)). */
+static double act_f64(int act, double x) {
+    switch (act) {
+        case ACT_GELU: return 0.5 * x * erfc(-x * 0.70710678118654752440);          /* x Phi(x) */
+        case ACT_GELU_TANH: {
+            const double u = 0.79788456080286535588 * (x + 0.044715 * x * x * x);   /* sqrt(2/pi) */
+            return x / (1.0 + exp(-2.0 * u));
+        }
+        case ACT_SILU: return x / (1.0 + exp(-x));
+        case ACT_SIGMOID: return 1.0 / (1.0 + exp(-x));
+        case ACT_TANH: return tanh(x);
+        default: return x;
+    }
+}
+
+/* Steps 3 and 4 (or 3' and 4') for output column j. */
+static uint16_t epilogue(int fmt, const Epi* ep, int64_t j, float acc) {
+    float x = acc;
+    if (ep->bias) x = x + widen(fmt, ep->bias[j]);
+    if (ep->act == ACT_RELU) return round_to(fmt, (x > 0.0f) ? x : 0.0f); /* NaN compares false -> +0 */
+    if (ep->act == ACT_NONE) return round_to(fmt, x);
+    return round_to(fmt, f64_to_f32_odd(act_f64(ep->act, (double)x)));
 }
 
 /* ---- thread control (used only to time the oracle) ----------------------- */
@@ -188,7 +252,7 @@ int oracle_max_threads(void) {
 /* ---- the four entry points (fp16 and bf16) -------------------------------- */
 
 /* One full output row i.  bf holds B widened to fp32, packed K x N. */
-static void one_row(int fmt, int64_t i, int64_t N, int64_t K, const uint16_t* A, int64_t lda,
+static void one_row(int fmt, const Epi* ep, int64_t i, int64_t N, int64_t K, const uint16_t* A, int64_t lda,
                     const float* bf, float* acc, uint16_t* out) {
     for (int64_t j = 0; j < N; ++j) acc[j] = 0.0f;
     for (int64_t k = 0; k < K; ++k) {
@@ -196,7 +260,7 @@ static void one_row(int fmt, int64_t i, int64_t N, int64_t K, const uint16_t* A,
         const float* brow = bf + k * N;
         for (int64_t j = 0; j < N; ++j) acc[j] = acc[j] + a * brow[j];
     }
-    for (int64_t j = 0; j < N; ++j) out[j] = epilogue(fmt, acc[j]);
+    for (int64_t j = 0; j < N; ++j) out[j] = epilogue(fmt, ep, j, acc[j]);
 }
 
 static float* widen_b(int fmt, int64_t N, int64_t K, const uint16_t* B, int64_t ldb) {
@@ -209,7 +273,7 @@ static float* widen_b(int fmt, int64_t N, int64_t K, const uint16_t* B, int64_t 
 
 /* C[i*ldc + j] for all 0 <= i < M, 0 <= j < N.  Returns 0, or -1 on allocation
    failure.  Columns j >= N of C are not touched. */
-static int gemm_full(int fmt, int64_t M, int64_t N, int64_t K, const uint16_t* A, int64_t lda,
+static int gemm_full(int fmt, const Epi* ep, int64_t M, int64_t N, int64_t K, const uint16_t* A, int64_t lda,
                      const uint16_t* B, int64_t ldb, uint16_t* C, int64_t ldc) {
     if (M <= 0 || N <= 0) return 0;
     float* bf = widen_b(fmt, N, K, B, ldb);
@@ -223,7 +287,7 @@ static int gemm_full(int fmt, int64_t M, int64_t N, int64_t K, const uint16_t* A
             failed = 1;
         } else {
 #pragma omp for schedule(dynamic, 1)
-            for (int64_t i = 0; i < M; ++i) one_row(fmt, i, N, K, A, lda, bf, acc, C + i * ldc);
+            for (int64_t i = 0; i < M; ++i) one_row(fmt, ep, i, N, K, A, lda, bf, acc, C + i * ldc);
             free(acc);
         }
     }
@@ -232,7 +296,7 @@ static int gemm_full(int fmt, int64_t M, int64_t N, int64_t K, const uint16_t* A
 }
 
 /* Full rows: out[r*N + j] = C[rows[r]][j] for r < nrows. */
-static int gemm_rows(int fmt, int64_t N, int64_t K, const uint16_t* A, int64_t lda, const uint16_t* B,
+static int gemm_rows(int fmt, const Epi* ep, int64_t N, int64_t K, const uint16_t* A, int64_t lda, const uint16_t* B,
                      int64_t ldb, const int64_t* rows, int64_t nrows, uint16_t* out) {
     if (nrows <= 0 || N <= 0) return 0;
     float* bf = widen_b(fmt, N, K, B, ldb);
@@ -246,7 +310,7 @@ static int gemm_rows(int fmt, int64_t N, int64_t K, const uint16_t* A, int64_t l
             failed = 1;
         } else {
 #pragma omp for schedule(dynamic, 1)
-            for (int64_t r = 0; r < nrows; ++r) one_row(fmt, rows[r], N, K, A, lda, bf, acc, out + r * N);
+            for (int64_t r = 0; r < nrows; ++r) one_row(fmt, ep, rows[r], N, K, A, lda, bf, acc, out + r * N);
             free(acc);
         }
     }
@@ -255,7 +319,7 @@ static int gemm_rows(int fmt, int64_t N, int64_t K, const uint16_t* A, int64_t l
 }
 
 /* Full columns: out[c*M + i] = C[i][cols[c]] for c < ncols. */
-static int gemm_cols(int fmt, int64_t M, int64_t K, const uint16_t* A, int64_t lda, const uint16_t* B,
+static int gemm_cols(int fmt, const Epi* ep, int64_t M, int64_t K, const uint16_t* A, int64_t lda, const uint16_t* B,
                      int64_t ldb, const int64_t* cols, int64_t ncols, uint16_t* out) {
     if (ncols <= 0 || M <= 0) return 0;
     int failed = 0;
@@ -273,7 +337,7 @@ static int gemm_cols(int fmt, int64_t M, int64_t K, const uint16_t* A, int64_t l
                 for (int64_t i = 0; i < M; ++i) {
                     float acc = 0.0f;
                     for (int64_t k = 0; k < K; ++k) acc = acc + widen(fmt, A[i * lda + k]) * bcol[k];
-                    out[c * M + i] = epilogue(fmt, acc);
+                    out[c * M + i] = epilogue(fmt, ep, j, acc);
                 }
             }
             free(bcol);
@@ -283,33 +347,33 @@ static int gemm_cols(int fmt, int64_t M, int64_t K, const uint16_t* A, int64_t l
 }
 
 /* Single elements: out[e] = C[ii[e]][jj[e]] for e < n. */
-static int gemm_elems(int fmt, int64_t K, const uint16_t* A, int64_t lda, const uint16_t* B, int64_t ldb,
+static int gemm_elems(int fmt, const Epi* ep, int64_t K, const uint16_t* A, int64_t lda, const uint16_t* B, int64_t ldb,
                       const int64_t* ii, const int64_t* jj, int64_t n, uint16_t* out) {
 #pragma omp parallel for schedule(static)
     for (int64_t e = 0; e < n; ++e) {
         float acc = 0.0f;
         for (int64_t k = 0; k < K; ++k)
             acc = acc + widen(fmt, A[ii[e] * lda + k]) * widen(fmt, B[k * ldb + jj[e]]);
-        out[e] = epilogue(fmt, acc);
+        out[e] = epilogue(fmt, ep, jj[e], acc);
     }
     return 0;
 }
 
 int oracle_gemm_relu_f16_full(int64_t M, int64_t N, int64_t K, const uint16_t* A, int64_t lda,
                               const uint16_t* B, int64_t ldb, uint16_t* C, int64_t ldc) {
-    return gemm_full(FMT_F16, M, N, K, A, lda, B, ldb, C, ldc);
+    return gemm_full(FMT_F16, &kRelu, M, N, K, A, lda, B, ldb, C, ldc);
 }
 
 int oracle_gemm_relu_f16_rows(int64_t M, int64_t N, int64_t K, const uint16_t* A, int64_t lda,
                               const uint16_t* B, int64_t ldb, const int64_t* rows, int64_t nrows, uint16_t* out) {
     (void)M;
-    return gemm_rows(FMT_F16, N, K, A, lda, B, ldb, rows, nrows, out);
+    return gemm_rows(FMT_F16, &kRelu, N, K, A, lda, B, ldb, rows, nrows, out);
 }
 
 int oracle_gemm_relu_f16_cols(int64_t M, int64_t N, int64_t K, const uint16_t* A, int64_t lda,
                               const uint16_t* B, int64_t ldb, const int64_t* cols, int64_t ncols, uint16_t* out) {
     (void)N;
-    return gemm_cols(FMT_F16, M, K, A, lda, B, ldb, cols, ncols, out);
+    return gemm_cols(FMT_F16, &kRelu, M, K, A, lda, B, ldb, cols, ncols, out);
 }
 
 int oracle_gemm_relu_f16_elems(int64_t M, int64_t N, int64_t K, const uint16_t* A, int64_t lda,
@@ -317,24 +381,24 @@ int oracle_gemm_relu_f16_elems(int64_t M, int64_t N, int64_t K, const uint16_t* 
                                uint16_t* out) {
     (void)M;
     (void)N;
-    return gemm_elems(FMT_F16, K, A, lda, B, ldb, ii, jj, n, out);
+    return gemm_elems(FMT_F16, &kRelu, K, A, lda, B, ldb, ii, jj, n, out);
 }
 
 int oracle_gemm_relu_bf16_full(int64_t M, int64_t N, int64_t K, const uint16_t* A, int64_t lda,
                                const uint16_t* B, int64_t ldb, uint16_t* C, int64_t ldc) {
-    return gemm_full(FMT_BF16, M, N, K, A, lda, B, ldb, C, ldc);
+    return gemm_full(FMT_BF16, &kRelu, M, N, K, A, lda, B, ldb, C, ldc);
 }
 
 int oracle_gemm_relu_bf16_rows(int64_t M, int64_t N, int64_t K, const uint16_t* A, int64_t lda,
                                const uint16_t* B, int64_t ldb, const int64_t* rows, int64_t nrows, uint16_t* out) {
     (void)M;
-    return gemm_rows(FMT_BF16, N, K, A, lda, B, ldb, rows, nrows, out);
+    return gemm_rows(FMT_BF16, &kRelu, N, K, A, lda, B, ldb, rows, nrows, out);
 }
 
 int oracle_gemm_relu_bf16_cols(int64_t M, int64_t N, int64_t K, const uint16_t* A, int64_t lda,
                                const uint16_t* B, int64_t ldb, const int64_t* cols, int64_t ncols, uint16_t* out) {
     (void)N;
-    return gemm_cols(FMT_BF16, M, K, A, lda, B, ldb, cols, ncols, out);
+    return gemm_cols(FMT_BF16, &kRelu, M, K, A, lda, B, ldb, cols, ncols, out);
 }
 
 int oracle_gemm_relu_bf16_elems(int64_t M, int64_t N, int64_t K, const uint16_t* A, int64_t lda,
@@ -342,5 +406,46 @@ int oracle_gemm_relu_bf16_elems(int64_t M, int64_t N, int64_t K, const uint16_t*
                                 uint16_t* out) {
     (void)M;
     (void)N;
-    return gemm_elems(FMT_BF16, K, A, lda, B, ldb, ii, jj, n, out);
+    return gemm_elems(FMT_BF16, &kRelu, K, A, lda, B, ldb, ii, jj, n, out);
+}
+
+/* C = act(A*B + bias) in format fmt (0 = fp16, 1 = bfloat16); bias holds N
+   values or is NULL.  Returns -2 for an unknown format or activation. */
+static int epi_check(int fmt, int act) {
+    return (fmt == FMT_F16 || fmt == FMT_BF16) && act >= 0 && act < ACT_COUNT;
+}
+
+int oracle_gemm_epi_full(int fmt, const uint16_t* bias, int act, int64_t M, int64_t N, int64_t K, const uint16_t* A,
+                         int64_t lda, const uint16_t* B, int64_t ldb, uint16_t* C, int64_t ldc) {
+    if (!epi_check(fmt, act)) return -2;
+    const Epi ep = {bias, act};
+    return gemm_full(fmt, &ep, M, N, K, A, lda, B, ldb, C, ldc);
+}
+
+int oracle_gemm_epi_rows(int fmt, const uint16_t* bias, int act, int64_t M, int64_t N, int64_t K, const uint16_t* A,
+                         int64_t lda, const uint16_t* B, int64_t ldb, const int64_t* rows, int64_t nrows,
+                         uint16_t* out) {
+    (void)M;
+    if (!epi_check(fmt, act)) return -2;
+    const Epi ep = {bias, act};
+    return gemm_rows(fmt, &ep, N, K, A, lda, B, ldb, rows, nrows, out);
+}
+
+int oracle_gemm_epi_cols(int fmt, const uint16_t* bias, int act, int64_t M, int64_t N, int64_t K, const uint16_t* A,
+                         int64_t lda, const uint16_t* B, int64_t ldb, const int64_t* cols, int64_t ncols,
+                         uint16_t* out) {
+    (void)N;
+    if (!epi_check(fmt, act)) return -2;
+    const Epi ep = {bias, act};
+    return gemm_cols(fmt, &ep, M, K, A, lda, B, ldb, cols, ncols, out);
+}
+
+int oracle_gemm_epi_elems(int fmt, const uint16_t* bias, int act, int64_t M, int64_t N, int64_t K,
+                          const uint16_t* A, int64_t lda, const uint16_t* B, int64_t ldb, const int64_t* ii,
+                          const int64_t* jj, int64_t n, uint16_t* out) {
+    (void)M;
+    (void)N;
+    if (!epi_check(fmt, act)) return -2;
+    const Epi ep = {bias, act};
+    return gemm_elems(fmt, &ep, K, A, lda, B, ldb, ii, jj, n, out);
 }

@@ -46,6 +46,21 @@ def test_library_exports_every_declared_symbol():
         assert hasattr(lib, n), n
 
 
+def test_library_shares_torchs_hip_runtime():
+    """Loading the library, even before anything imports torch, leaves one
+    HIP runtime in the process: a second copy would not see torch's device
+    or streams.  Checked in a fresh interpreter."""
+    import subprocess
+    import sys
+    code = ("import dense_gemm_epilogue_tiled_amd as gr; gr.lib(); "
+            "m = open('/proc/self/maps').read(); "
+            "print(len(set(l.split()[-1] for l in m.splitlines() if 'libamdhip64' in l)))")
+    out = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True,
+                         cwd=os.path.dirname(os.path.dirname(os.path.abspath(__file__))))
+    assert out.returncode == 0, out.stderr[-2000:]
+    assert out.stdout.strip() == "1"
+
+
 def test_python_constants_match_header():
     d = header_defines()
     for k, v in d.items():
@@ -410,6 +425,31 @@ def test_bf16_argument_checks_need_no_gpu():
         assert g(8, 256, 64, BASE_A, 64, BASE_B, 256, BASE_C, 256, None, path) == gr.GR_ERR_INVALID_PATH
     assert g(300, 256, 48, BASE_A, 48, BASE_B, 256, BASE_C, 256, None, gr.GR_PATH_TILE) == gr.GR_ERR_INVALID_PATH
     assert g(64, 256, 64, BASE_A, 64, BASE_B, 256, BASE_C, 256, None, gr.GR_PATH_SMALL_M) == gr.GR_ERR_INVALID_PATH
+
+
+def test_bias_act_argument_checks_need_no_gpu():
+    """gemm_bias_act_* run the shared argument checks before any HIP call,
+    then reject unknown activations and a bias that overlaps C."""
+    for f, g in ((gr.gemm_bias_act_f16, gr.gemm_bias_act_f16_forced),
+                 (gr.gemm_bias_act_bf16, gr.gemm_bias_act_bf16_forced)):
+        bias = BASE_C + (1 << 30)
+        assert f(-1, 8, 8, BASE_A, 8, BASE_B, 8, bias, gr.GR_ACT_GELU, BASE_C, 8) == gr.GR_ERR_INVALID_DIM
+        assert f(8, 8, 8, BASE_A, 8, BASE_B, 7, bias, gr.GR_ACT_GELU, BASE_C, 8) == gr.GR_ERR_INVALID_LD
+        assert f(8, 8, 8, BASE_A, 8, BASE_B, 8, bias, -1, BASE_C, 8) == gr.GR_ERR_INVALID_ARG
+        assert f(8, 8, 8, BASE_A, 8, BASE_B, 8, bias, 7, BASE_C, 8) == gr.GR_ERR_INVALID_ARG
+        # the bias's 16 bytes overlap C's last row / first row
+        assert f(8, 8, 8, BASE_A, 8, BASE_B, 8, BASE_C + 2 * 8 * 7, gr.GR_ACT_SILU, BASE_C, 8) == gr.GR_ERR_ALIAS
+        assert f(8, 8, 8, BASE_A, 8, BASE_B, 8, BASE_C - 14, gr.GR_ACT_SILU, BASE_C, 8) == gr.GR_ERR_ALIAS
+        assert f(0, 8, 8, 0, 8, BASE_B, 8, bias, gr.GR_ACT_TANH, 0, 8) == gr.GR_OK  # empty: nothing launched
+        for path in (gr.GR_PATH_TILE_PACKED, gr.GR_PATH_SMALL_M_SPLIT, gr.GR_PATH_TILE_SPLIT, 99):
+            assert g(8, 256, 64, BASE_A, 64, BASE_B, 256, bias, 2, BASE_C, 256, None, path) == gr.GR_ERR_INVALID_PATH
+        assert g(300, 256, 48, BASE_A, 48, BASE_B, 256, bias, 2, BASE_C, 256, None,
+                 gr.GR_PATH_TILE) == gr.GR_ERR_INVALID_PATH
+
+
+def test_act_codes_match_the_oracle():
+    import oracle
+    assert gr.ACT_CODES == oracle.ACTS
 
 
 def test_plan_null_output_struct():
