@@ -589,6 +589,37 @@ def test_random_problems_against_oracle(case):
     assert np.all(Cw[:, N:] == SENTINEL)
 
 
+# ---- more 256 x 256 tiles than CUs ---------------------------------------------
+
+MANY_TILE_CASES = [
+    # M, N, K, lda, ldb, ldc: tiles
+    (4352, 4352, 128, 128, 4352, 4352),   # 289 whole tiles, 64-deep kernel: a second round of 33
+    (4100, 4400, 96, 104, 4400, 4401),    # 17 x 18 = 306 partial tiles, 32-deep kernel
+    (6000, 2600, 64, 64, 2608, 2601),     # 24 x 11 = 264 partial tiles
+    (8192, 8192, 64, 64, 8192, 8192),     # 1024 tiles: four rounds
+]
+
+
+@pytest.mark.parametrize("M,N,K,lda,ldb,ldc", MANY_TILE_CASES)
+def test_more_tiles_than_compute_units(M, N, K, lda, ldb, ldc):
+    """Several rounds of workgroups (and a partial last round) produce every
+    tile exactly as the guarded kernel does, bit for bit, and match the
+    oracle; C's padding and the rows below stay untouched."""
+    st, plan = gr.gemm_relu_f16_plan(M, N, K, 0x100000, lda, 0x200000000000, ldb, 0x400000000000, ldc)
+    assert plan["path"] == gr.GR_PATH_TILE and plan["block_m"] == 256 and plan["grid"] > 256, plan
+    A, B = synth.random_operands(M, N, K, seed=M + N + K, lda=lda, ldb=ldb, b_scale=K ** -0.5)
+    C1 = run_full(A, B, M, N, K, lda, ldb, ldc, c_rows=M + 1)
+    C2 = run_full(A, B, M, N, K, lda, ldb, ldc, c_rows=M + 1, path=gr.GR_PATH_TILE_EDGE)
+    assert np.array_equal(C1, C2)
+    C = C1[:M * ldc].reshape(M, ldc)
+    assert np.all(C[:, N:] == SENTINEL) and np.all(C1[M * ldc:] == SENTINEL)
+    if M * N * K <= 4 << 30:
+        assert_parity(C[:, :N], oracle.gemm_relu_full(A, B, M=M, N=N, K=K, lda=lda, ldb=ldb), "many tiles")
+    else:
+        ii, jj = synth.sample_indices(M, N, 4096, 7)
+        assert_parity(C[ii, jj], oracle.gemm_relu_elems(A, B, ii, jj, M=M, N=N, K=K, lda=lda, ldb=ldb), "many tiles")
+
+
 # ---- B given transposed (Bt, N x K) --------------------------------------------
 
 def run_bt(A, Bt, M, N, K, lda, ldbt, ldc, path=None, c_rows=None, offsets=(0, 0, 0)):
@@ -633,6 +664,8 @@ BT_CASES = [
     (2400, 4000, 96, 96, 96, 4001, gr.GR_PATH_TILE),           # large partial tiles
     (17, 264, 64, 72, 64, 265, gr.GR_PATH_TILE),
     (300, 270, 100, 109, 105, 273, gr.GR_PATH_TILE_EDGE),      # odd pitches
+    (4352, 4352, 128, 128, 136, 4352, gr.GR_PATH_TILE),        # 289 tiles: a second round
+    (4100, 4400, 96, 96, 96, 4400, gr.GR_PATH_TILE),           # 306 partial tiles
 ]
 
 

@@ -34,6 +34,7 @@ FAMILY_CASES = [
 
 EXTRA_CASES = [
     (512, 768, 256, 256, 768, 768, gr.GR_PATH_TILE, "tile128 whole"),
+    (4352, 4100, 128, 128, 4104, 4101, gr.GR_PATH_TILE, "tile 256, 289 tiles"),
     (4096, 2304, 256, 256, 2304, 2304, gr.GR_PATH_TILE, "tile 256 whole"),
     (257, 130, 70, 70, 130, 130, gr.GR_PATH_TILE_EDGE, "guarded 4-byte rows"),
     (8, 4096, 1024, 1024, 4096, 4096, gr.GR_PATH_SMALL_M, "small-M whole"),
