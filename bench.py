@@ -278,6 +278,9 @@ EXTRA_SHAPES = [
     ("bias + GELU (tanh), MLP projection", 8192, 28672, 8192, "epi:f16:gelu_tanh"),
     ("bias + SiLU, bfloat16, MLP projection", 8192, 28672, 8192, "epi:bf16:silu"),
     ("bias + SiLU, small-M", 8, 16384, 8192, "epi:f16:silu"),
+    ("fp8 e4m3, square", 4096, 4096, 4096, "fp8"),
+    ("fp8 e4m3, square 8192", 8192, 8192, 8192, "fp8"),
+    ("fp8 e4m3, MLP projection", 8192, 28672, 8192, "fp8"),
 ]
 
 
@@ -295,7 +298,22 @@ def extra_shapes(gr, torch, reps=30):
         C = torch.empty(M, N, device="cuda", dtype=dt)
         row = {"shape": "%dx%dx%d" % (M, N, K), "what": label, "layout": layout}
         runs = {}
-        if layout.startswith("epi:"):
+        if layout == "fp8":
+            A8 = torch.randn(M, K, generator=g, device="cuda").to(torch.float8_e4m3fn)
+            Bt8 = torch.randn(N, K, generator=g, device="cuda").to(torch.float8_e4m3fn)
+            sa, sb = 1.0 / 64, 1.0 / 64
+            runs["ours"] = lambda: gr.gemm_fp8(A8, Bt8, sa, sb, act="relu", out=C, stream=stream)
+            ta = torch.tensor(sa, device="cuda")
+            tb = torch.tensor(sb, device="cuda")
+
+            def vendor():
+                return torch.relu_(torch._scaled_mm(A8, Bt8.t(), scale_a=ta, scale_b=tb, out_dtype=torch.float16))
+            try:
+                vendor()
+                runs["vendor"] = vendor
+            except Exception as e:  # the vendor fp8 path may be missing
+                row["vendor_error"] = str(e)[:120]
+        elif layout.startswith("epi:"):
             act = layout.split(":")[2]
             bias = torch.randn(N, generator=g, device="cuda").to(dt)
             fn = {"gelu": torch.nn.functional.gelu, "silu": torch.nn.functional.silu,

@@ -42,6 +42,9 @@ GR_ACT_SILU = 4
 GR_ACT_SIGMOID = 5
 GR_ACT_TANH = 6
 
+GR_FMT_F16 = 0
+GR_FMT_BF16 = 1
+
 ACT_CODES = {"none": GR_ACT_NONE, "relu": GR_ACT_RELU, "gelu": GR_ACT_GELU, "gelu_tanh": GR_ACT_GELU_TANH,
              "silu": GR_ACT_SILU, "sigmoid": GR_ACT_SIGMOID, "tanh": GR_ACT_TANH}
 
@@ -130,6 +133,14 @@ def lib() -> ctypes.CDLL:
                 getattr(l, nm).restype = i32
                 getattr(l, nm + "_forced").argtypes = [i64, i64, i64, p, i64, p, i64, p, i32, p, i64, p, i32]
                 getattr(l, nm + "_forced").restype = i32
+            f32 = ctypes.c_float
+            l.gemm_fp8_bt.argtypes = [i64, i64, i64, p, i64, p, i64, f32, f32, p, i32, p, i64, i32, p]
+            l.gemm_fp8_bt.restype = i32
+            l.gemm_fp8_bt_forced.argtypes = [i64, i64, i64, p, i64, p, i64, f32, f32, p, i32, p, i64, i32, p, i32]
+            l.gemm_fp8_bt_forced.restype = i32
+            l.gemm_fp8_bt_plan.argtypes = [i64, i64, i64, p, i64, p, i64, p, i32, p, i64, i32,
+                                           ctypes.POINTER(gr_plan_t)]
+            l.gemm_fp8_bt_plan.restype = i32
             l.gemm_relu_status_string.argtypes = [i32]
             l.gemm_relu_status_string.restype = ctypes.c_char_p
             l.gemm_relu_version.argtypes = []
@@ -236,6 +247,26 @@ def gemm_bias_act_f16_forced(M, N, K, A, lda, B, ldb, bias, act, C, ldc, stream=
 def gemm_bias_act_bf16_forced(M, N, K, A, lda, B, ldb, bias, act, C, ldc, stream=None, path=GR_PATH_TILE_EDGE) -> int:
     return lib().gemm_bias_act_bf16_forced(M, N, K, _ptr(A), lda, _ptr(B), ldb, _ptr(bias), act, _ptr(C), ldc,
                                            _ptr(stream), path)
+
+
+def gemm_fp8_bt(M, N, K, A, lda, Bt, ldbt, scale_a, scale_b, bias, act, C, ldc, out_fmt=GR_FMT_F16,
+                stream=None) -> int:
+    """C := act(scale_a * scale_b * A.Bt^T + bias), A and Bt OCP fp8 E4M3 (device pointers)."""
+    return lib().gemm_fp8_bt(M, N, K, _ptr(A), lda, _ptr(Bt), ldbt, float(scale_a), float(scale_b), _ptr(bias), act,
+                             _ptr(C), ldc, out_fmt, _ptr(stream))
+
+
+def gemm_fp8_bt_forced(M, N, K, A, lda, Bt, ldbt, scale_a, scale_b, bias, act, C, ldc, out_fmt=GR_FMT_F16,
+                       stream=None, path=GR_PATH_TILE_EDGE) -> int:
+    return lib().gemm_fp8_bt_forced(M, N, K, _ptr(A), lda, _ptr(Bt), ldbt, float(scale_a), float(scale_b),
+                                    _ptr(bias), act, _ptr(C), ldc, out_fmt, _ptr(stream), path)
+
+
+def gemm_fp8_bt_plan(M, N, K, A, lda, Bt, ldbt, bias, act, C, ldc, out_fmt=GR_FMT_F16):
+    plan = gr_plan_t()
+    st = lib().gemm_fp8_bt_plan(M, N, K, _ptr(A), lda, _ptr(Bt), ldbt, _ptr(bias), act, _ptr(C), ldc, out_fmt,
+                                ctypes.byref(plan))
+    return st, _plan_dict(plan)
 
 
 def gemm_relu_status_string(status: int) -> str:
@@ -374,4 +405,44 @@ def gemm_bias_act(a, b, bias=None, act="gelu", out=None, stream=None, path=None)
         st = (gemm_bias_act_bf16_forced if bf else gemm_bias_act_f16_forced)(*args, path)
     if st != GR_OK:
         raise GemmReluError(st, "gemm_bias_act_bf16" if bf else "gemm_bias_act_f16")
+    return out
+
+
+def gemm_fp8(a, bt, scale_a=1.0, scale_b=1.0, bias=None, act="relu", out_dtype=None, out=None, stream=None,
+             path=None):
+    """Tensor convenience: ``out = act(scale_a * scale_b * a @ bt.T + bias)``
+    with ``a`` (M x K) and ``bt`` (N x K) torch.float8_e4m3fn tensors on the
+    GPU (unit column stride), fp16 or bfloat16 output (``out_dtype``, default
+    float16) and an optional 1-D bias of N values in the output dtype."""
+    import torch
+    if a.dtype != torch.float8_e4m3fn or bt.dtype != torch.float8_e4m3fn:
+        raise TypeError("a and bt must be torch.float8_e4m3fn")
+    if a.dim() != 2 or bt.dim() != 2 or a.shape[1] != bt.shape[1]:
+        raise ValueError("shapes do not form a product: %s x %s^T" % (tuple(a.shape), tuple(bt.shape)))
+    M, K = a.shape
+    N = bt.shape[0]
+    if out is not None:
+        out_dtype = out.dtype
+    out_dtype = torch.float16 if out_dtype is None else out_dtype
+    if out_dtype not in (torch.float16, torch.bfloat16):
+        raise TypeError("the output is float16 or bfloat16")
+    fmt = GR_FMT_BF16 if out_dtype == torch.bfloat16 else GR_FMT_F16
+    if bias is not None and (bias.dtype != out_dtype or bias.dim() != 1 or bias.shape[0] != N or
+                             (N > 1 and bias.stride(0) != 1)):
+        raise ValueError("bias must be a contiguous 1-D tensor of N values of the output dtype")
+    if out is None:
+        out = torch.empty((M, N), dtype=out_dtype, device=a.device)
+    for t in (a, bt, out):
+        if t.numel() and t.stride(1) != 1:
+            raise ValueError("tensors need unit column stride")
+    lda = max(a.stride(0), 1) if M > 1 else max(K, 1)
+    ldbt = max(bt.stride(0), 1) if N > 1 else max(K, 1)
+    ldc = max(out.stride(0), 1) if M > 1 else max(N, 1)
+    code = ACT_CODES[act] if isinstance(act, str) else int(act)
+    bptr = bias.data_ptr() if bias is not None and bias.numel() else None
+    args = (M, N, K, a.data_ptr(), lda, bt.data_ptr(), ldbt, scale_a, scale_b, bptr, code, out.data_ptr(), ldc, fmt,
+            _stream_handle(stream))
+    st = gemm_fp8_bt(*args) if path is None else gemm_fp8_bt_forced(*args, path)
+    if st != GR_OK:
+        raise GemmReluError(st, "gemm_fp8_bt")
     return out

@@ -107,7 +107,7 @@ __device__ __forceinline__ uint32_t relu_pack2_e(float x0, float x1) {
 
 // ---- epilogues beyond ReLU ------------------------------------------------------
 //
-// out[m][n] = round(act(acc[m][n] + bias[n])): a bias broadcast along the
+// out[m][n] = round(act(scale * acc[m][n] + bias[n])): a bias broadcast along the
 // rows and one of the activations the elementwise pattern lists (relu,
 // sigmoid, tanh, gelu; "Tilelang Cuda Patterns", section 1), plus SiLU and
 // the tanh form of GELU.  The activation is evaluated in fp32 on the biased
@@ -130,6 +130,7 @@ enum : int {
 struct EpiArgs {
     const uint16_t* bias;  // N values of C's element type, or nullptr for none
     int act;               // kAct*
+    float scale;           // multiplies the accumulator first (1 except for the fp8 calls)
 };
 
 // The activations in fp32, in forms built from the hardware exp2 and
@@ -228,8 +229,8 @@ struct Epi : Base {
 template <typename E>
 __device__ __forceinline__ uint16_t epi_value(float acc, int64_t n, int64_t N, const EpiArgs& ep) {
     if constexpr (E::kGeneral) {
-        float x = acc;
-        if (ep.bias != nullptr && n < N) x += E::widen(ep.bias[n]);
+        float x = __fmul_rn(acc, ep.scale);
+        if (ep.bias != nullptr && n < N) x = __fadd_rn(x, E::widen(ep.bias[n]));
         return E::round(activate(x, ep.act));
     } else {
         return E::relu_round(acc);
@@ -392,7 +393,11 @@ __device__ __forceinline__ void store_wave_tile_general(const f32x16 (&acc)[FM][
                 if (EDGE && (m < row_min || m >= M)) continue;
                 uint16_t o[4];
 #pragma unroll
-                for (int t = 0; t < 4; ++t) o[t] = E::round(act::apply<A>(has_bias ? v[t] + b[t] : v[t]));
+                for (int t = 0; t < 4; ++t) {
+                    // scale, then bias: two roundings, never fused into one
+                    const float x = __fmul_rn(v[t], ep.scale);
+                    o[t] = E::round(act::apply<A>(has_bias ? __fadd_rn(x, b[t]) : x));
+                }
                 uint16_t* dst = C + m * ldc + n;
                 if (wide && (!EDGE || n + 4 <= N)) {
                     __builtin_nontemporal_store(u32x2{(uint32_t)o[0] | ((uint32_t)o[1] << 16),

@@ -13,6 +13,7 @@
 #include <cstring>
 
 #include "../../include/gemm_relu.h"
+#include "fp8_kernel.hpp"
 #include "pack_kernel.hpp"
 #include "smallm_kernel.hpp"
 #include "tile2_kernel.hpp"
@@ -534,7 +535,7 @@ static_assert(GR_ACT_NONE == gr::kActNone && GR_ACT_RELU == gr::kActRelu && GR_A
               "activation codes of the C ABI and the kernels agree");
 
 // Epilogue arguments of the fused-ReLU calls (their kernels ignore them).
-const gr::EpiArgs kReluOnly{nullptr, gr::kActRelu};
+const gr::EpiArgs kReluOnly{nullptr, gr::kActRelu, 1.0f};
 
 int entry(int64_t M, int64_t N, int64_t K, const uint16_t* A, int64_t lda, const uint16_t* B, int64_t ldb,
           uint16_t* C, int64_t ldc, void* ws, int64_t ws_bytes, void* stream, int forced) {
@@ -588,7 +589,7 @@ int entry_epi(int64_t M, int64_t N, int64_t K, const uint16_t* A, int64_t lda, c
     if (p.path == GR_PATH_NONE) return GR_OK;
     st = check_device();
     if (st != GR_OK) return st;
-    return run<gr::Epi<Base>>(p, M, N, K, A, lda, B, ldb, C, ldc, pk, sp, ts, nullptr, gr::EpiArgs{bias, act},
+    return run<gr::Epi<Base>>(p, M, N, K, A, lda, B, ldb, C, ldc, pk, sp, ts, nullptr, gr::EpiArgs{bias, act, 1.0f},
                               static_cast<hipStream_t>(stream));
 }
 
@@ -688,7 +689,7 @@ int launch_tile_bt(const gr_plan_t& p, int64_t M, int64_t N, int64_t K, const ui
 
 int run_bt(const gr_plan_t& p, int64_t M, int64_t N, int64_t K, const uint16_t* A, int64_t lda, const uint16_t* Bt,
            int64_t ldbt, uint16_t* C, int64_t ldc, hipStream_t stream) {
-    const gr::EpiArgs ep{nullptr, gr::kActRelu};  // the fused ReLU kernels ignore it
+    const gr::EpiArgs ep{nullptr, gr::kActRelu, 1.0f};  // the fused ReLU kernels ignore it
     switch (p.path) {
         case GR_PATH_NONE: return GR_OK;
         case GR_PATH_SMALL_M: {
@@ -785,6 +786,128 @@ int entry_bt(int64_t M, int64_t N, int64_t K, const uint16_t* A, int64_t lda, co
     st = check_device();
     if (st != GR_OK) return st;
     return run_bt(p, M, N, K, A, lda, Bt, ldbt, C, ldc, static_cast<hipStream_t>(stream));
+}
+
+// ---- fp8 (e4m3) operands, B given transposed -----------------------------------
+
+// Bytes spanned by a rows x cols matrix of 1-byte elements with pitch ld.
+int64_t span_bytes8(int64_t rows, int64_t cols, int64_t ld) {
+    if (rows == 0 || cols == 0) return 0;
+    const int64_t limit = kMaxSpanBytes;
+    if (rows - 1 > 0 && ld > (limit - cols) / (rows - 1)) return -1;
+    return (rows - 1) * ld + cols;
+}
+
+int validate_fp8(int64_t M, int64_t N, int64_t K, uintptr_t A, int64_t lda, uintptr_t Bt, int64_t ldbt,
+                 uintptr_t bias, int act, uintptr_t C, int64_t ldc, int out_fmt) {
+    if (M < 0 || N < 0 || K < 0) return GR_ERR_INVALID_DIM;
+    if (M > kMaxDim || N > kMaxDim || K > kMaxDim) return GR_ERR_TOO_LARGE;
+    const int64_t kmin = K > 1 ? K : 1, nmin = N > 1 ? N : 1;
+    if (lda < kmin || ldbt < kmin || ldc < nmin) return GR_ERR_INVALID_LD;
+    if (act < 0 || act >= gr::kActCount || (out_fmt != GR_FMT_F16 && out_fmt != GR_FMT_BF16))
+        return GR_ERR_INVALID_ARG;
+    const bool used = M > 0 && N > 0 && K > 0;
+    const bool c_used = M > 0 && N > 0;
+    if ((used && (!A || !Bt)) || (c_used && !C)) return GR_ERR_NULL_PTR;
+    const int64_t sa = used ? span_bytes8(M, K, lda) : 0;
+    const int64_t sb = used ? span_bytes8(N, K, ldbt) : 0;
+    const int64_t sc = c_used ? span_bytes(M, N, ldc) : 0;
+    if (sa < 0 || sb < 0 || sc < 0) return GR_ERR_TOO_LARGE;
+    if (overlaps(C, sc, A, sa) || overlaps(C, sc, Bt, sb)) return GR_ERR_ALIAS;
+    if (bias && c_used && overlaps(C, sc, bias, 2 * N)) return GR_ERR_ALIAS;
+    return GR_OK;
+}
+
+// The pipelined fp8 kernel: K a positive multiple of 64, 16-byte aligned rows
+// of A and Bt, pitches within the 32-bit copy offsets.
+bool fp8_tile_ok(int64_t M, int64_t N, int64_t K, uintptr_t A, int64_t lda, uintptr_t Bt, int64_t ldbt) {
+    using namespace gr::fp8;
+    return M >= 1 && N >= 1 && K > 0 && K % BK == 0 && A % 16 == 0 && lda % 16 == 0 && Bt % 16 == 0 &&
+           ldbt % 16 == 0 && lda <= MAX_LD && ldbt <= MAX_LD;
+}
+
+void fill_plan_fp8(int path, int64_t M, int64_t N, uintptr_t C, int64_t ldc, gr_plan_t* p) {
+    std::memset(p, 0, sizeof(*p));
+    p->path = path;
+    p->block_k = gr::fp8::BK;
+    p->threads = gr::fp8::THREADS;
+    p->vec_c = vec_width_c(C, ldc);
+    p->split_k = 1;
+    if (path == GR_PATH_TILE) {
+        using namespace gr::fp8;
+        p->block_m = BM;
+        p->block_n = BN;
+        p->stages = STAGES;
+        p->grid = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
+        p->vec_a = 16;
+        p->vec_b = 16;
+        p->group_m = kGroupM;
+    } else if (path == GR_PATH_TILE_EDGE) {
+        using namespace gr::fp8;
+        p->block_m = G_BM;
+        p->block_n = G_BN;
+        p->stages = 1;
+        p->grid = ((M + G_BM - 1) / G_BM) * ((N + G_BN - 1) / G_BN);
+        p->vec_a = 1;
+        p->vec_b = 1;
+        p->group_m = 1;
+    }
+}
+
+int plan_call_fp8(int64_t M, int64_t N, int64_t K, uintptr_t A, int64_t lda, uintptr_t Bt, int64_t ldbt,
+                  uintptr_t bias, int act, uintptr_t C, int64_t ldc, int out_fmt, int forced, gr_plan_t* p) {
+    int st = validate_fp8(M, N, K, A, lda, Bt, ldbt, bias, act, C, ldc, out_fmt);
+    if (st != GR_OK) return st;
+    int path;
+    if (M == 0 || N == 0) path = GR_PATH_NONE;
+    else path = fp8_tile_ok(M, N, K, A, lda, Bt, ldbt) ? GR_PATH_TILE : GR_PATH_TILE_EDGE;
+    if (forced >= 0 && path != GR_PATH_NONE) {
+        if (forced == GR_PATH_TILE && path != GR_PATH_TILE) return GR_ERR_INVALID_PATH;
+        if (forced != GR_PATH_TILE && forced != GR_PATH_TILE_EDGE) return GR_ERR_INVALID_PATH;
+        path = forced;
+    }
+    fill_plan_fp8(path, M, N, C, ldc, p);
+    return GR_OK;
+}
+
+template <typename E>
+int run_fp8(const gr_plan_t& p, int64_t M, int64_t N, int64_t K, const uint8_t* A, int64_t lda, const uint8_t* Bt,
+            int64_t ldbt, uint16_t* C, int64_t ldc, const gr::EpiArgs& ep, hipStream_t stream) {
+    using namespace gr::fp8;
+    if (p.path == GR_PATH_TILE) {
+        const uint32_t tiles_m = (uint32_t)((M + BM - 1) / BM);
+        const uint32_t tiles_n = (uint32_t)((N + BN - 1) / BN);
+        const bool whole = M % BM == 0 && N % BN == 0;
+        if (whole)
+            return launch(gemm_fp8_tile_kernel<false, E>, p.grid, THREADS, stream, A, Bt, C, M, N, K, lda, ldbt, ldc,
+                          tiles_m, tiles_n, (uint32_t)p.group_m, (int)p.vec_c, ep);
+        return launch(gemm_fp8_tile_kernel<true, E>, p.grid, THREADS, stream, A, Bt, C, M, N, K, lda, ldbt, ldc,
+                      tiles_m, tiles_n, (uint32_t)p.group_m, (int)p.vec_c, ep);
+    }
+    if (p.path == GR_PATH_TILE_EDGE) {
+        const uint32_t tiles_n = (uint32_t)((N + G_BN - 1) / G_BN);
+        return launch(gemm_fp8_guarded_kernel<E>, p.grid, 256, stream, A, Bt, C, M, N, K, lda, ldbt, ldc, tiles_n,
+                      (int)p.vec_c, ep);
+    }
+    return p.path == GR_PATH_NONE ? GR_OK : GR_ERR_INVALID_PATH;
+}
+
+int entry_fp8(int64_t M, int64_t N, int64_t K, const uint8_t* A, int64_t lda, const uint8_t* Bt, int64_t ldbt,
+              float scale_a, float scale_b, const uint16_t* bias, int act, uint16_t* C, int64_t ldc, int out_fmt,
+              void* stream, int forced) {
+    gr_plan_t p;
+    int st = plan_call_fp8(M, N, K, (uintptr_t)A, lda, (uintptr_t)Bt, ldbt, (uintptr_t)bias, act, (uintptr_t)C, ldc,
+                           out_fmt, forced, &p);
+    if (st != GR_OK) return st;
+    if (p.path == GR_PATH_NONE) return GR_OK;
+    st = check_device();
+    if (st != GR_OK) return st;
+    // One scale for the product: the two per-tensor scales multiplied in fp32.
+    const gr::EpiArgs ep{bias, act, scale_a * scale_b};
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (out_fmt == GR_FMT_BF16)
+        return run_fp8<gr::Epi<gr::ElemBF16>>(p, M, N, K, A, lda, Bt, ldbt, C, ldc, ep, s);
+    return run_fp8<gr::Epi<gr::ElemF16>>(p, M, N, K, A, lda, Bt, ldbt, C, ldc, ep, s);
 }
 
 }  // namespace
@@ -902,6 +1025,27 @@ int gemm_relu_f16_plan_ws(int64_t M, int64_t N, int64_t K, const uint16_t* A, in
     TileSplit ts;
     return plan_call(M, N, K, (uintptr_t)A, lda, (uintptr_t)B, ldb, (uintptr_t)C, ldc, 0, workspace_bytes, false,
                      -1, &pk, &sp, &ts, out);
+}
+
+int gemm_fp8_bt(int64_t M, int64_t N, int64_t K, const uint8_t* A, int64_t lda, const uint8_t* Bt, int64_t ldbt,
+                float scale_a, float scale_b, const uint16_t* bias, int act, uint16_t* C, int64_t ldc, int out_fmt,
+                void* stream) {
+    return entry_fp8(M, N, K, A, lda, Bt, ldbt, scale_a, scale_b, bias, act, C, ldc, out_fmt, stream, -1);
+}
+
+int gemm_fp8_bt_forced(int64_t M, int64_t N, int64_t K, const uint8_t* A, int64_t lda, const uint8_t* Bt,
+                       int64_t ldbt, float scale_a, float scale_b, const uint16_t* bias, int act, uint16_t* C,
+                       int64_t ldc, int out_fmt, void* stream, int path) {
+    if (path != GR_PATH_TILE && path != GR_PATH_TILE_EDGE) return GR_ERR_INVALID_PATH;
+    return entry_fp8(M, N, K, A, lda, Bt, ldbt, scale_a, scale_b, bias, act, C, ldc, out_fmt, stream, path);
+}
+
+int gemm_fp8_bt_plan(int64_t M, int64_t N, int64_t K, const uint8_t* A, int64_t lda, const uint8_t* Bt,
+                     int64_t ldbt, const uint16_t* bias, int act, const uint16_t* C, int64_t ldc, int out_fmt,
+                     gr_plan_t* out) {
+    if (!out) return GR_ERR_INVALID_ARG;
+    return plan_call_fp8(M, N, K, (uintptr_t)A, lda, (uintptr_t)Bt, ldbt, (uintptr_t)bias, act, (uintptr_t)C, ldc,
+                         out_fmt, -1, out);
 }
 
 const char* gemm_relu_status_string(int status) {

@@ -1,6 +1,6 @@
 /*
  * gemm_relu.h -- C ABI of the MI355X (gfx950) fused fp16 GEMM + ReLU library
- * (with bfloat16, transposed-B and bias + activation variants further down).
+ * (with bfloat16, transposed-B, bias + activation and fp8 variants further down).
  *
  * The one operation:  C := ReLU(A * B)
  *   A  M x K, B  K x N, C  M x N, all IEEE binary16, row-major with a row
@@ -371,6 +371,60 @@ int gemm_bias_act_bf16_forced(int64_t M, int64_t N, int64_t K,
                               const uint16_t* bias, int act,
                               uint16_t* C, int64_t ldc,
                               void* stream, int path);
+
+/*
+ * ---- fp8 operands ---------------------------------------------------------------
+ * C := act(scale_a * scale_b * (A * Bt^T) + bias) with A (M x K) and Bt
+ * (N x K) in OCP fp8 E4M3 (1 sign, 4 exponent bits with bias 7, 3 fraction
+ * bits; no infinities; S.1111.111 is NaN; largest finite 448), one byte per
+ * element, both row-major with row pitches lda, ldbt >= max(1, K) in bytes
+ * (elements).  B is given transposed, the layout of a weight matrix and of
+ * the usual fp8 GEMM; products accumulate in fp32; scale_a and scale_b are
+ * per-tensor dequantisation scales (host floats), multiplied together in fp32
+ * and applied to the fp32 sum; then the optional bias (N values in the output
+ * format) and the activation (GR_ACT_*), and one rounding to the output
+ * format out_fmt (GR_FMT_F16 or GR_FMT_BF16, nearest even).  The pages list
+ * an fp8 GEMM with per-block scales among the TileLang examples (blog
+ * "TileLang programming basics", section "推荐顺序", step 6) and fp8 as the
+ * tensor-core format after tf32 and int8 (TileLang tutorial, section
+ * "张量核与 CUDA core"); per-tensor scales are the plainest form of those
+ * scales.  Paths: GR_PATH_TILE (K a multiple of 64, A, Bt and their pitches
+ * 16-byte aligned; any M, N) and GR_PATH_TILE_EDGE (everything else,
+ * including K == 0, which gives act(bias)).  C is fp16 or bfloat16 bits with
+ * pitch ldc; the conventions of gemm_relu_f16 hold otherwise (C never read,
+ * outside the M x N window never written, GR_ERR_ALIAS when C overlaps A,
+ * Bt or the bias, GR_ERR_INVALID_ARG for an unknown act or out_fmt).
+ */
+#define GR_FMT_F16         0
+#define GR_FMT_BF16        1
+
+int gemm_fp8_bt(int64_t M, int64_t N, int64_t K,
+                const uint8_t* A, int64_t lda,
+                const uint8_t* Bt, int64_t ldbt,
+                float scale_a, float scale_b,
+                const uint16_t* bias, int act,
+                uint16_t* C, int64_t ldc, int out_fmt,
+                void* stream);
+
+/* gemm_fp8_bt on a given path (GR_PATH_TILE or GR_PATH_TILE_EDGE;
+   GR_ERR_INVALID_PATH otherwise or when the path's conditions do not
+   hold).  Test hook. */
+int gemm_fp8_bt_forced(int64_t M, int64_t N, int64_t K,
+                       const uint8_t* A, int64_t lda,
+                       const uint8_t* Bt, int64_t ldbt,
+                       float scale_a, float scale_b,
+                       const uint16_t* bias, int act,
+                       uint16_t* C, int64_t ldc, int out_fmt,
+                       void* stream, int path);
+
+/* Pure planner for gemm_fp8_bt (no GPU needed): vec_a and vec_b are in
+   bytes (16 on the pipelined path). */
+int gemm_fp8_bt_plan(int64_t M, int64_t N, int64_t K,
+                     const uint8_t* A, int64_t lda,
+                     const uint8_t* Bt, int64_t ldbt,
+                     const uint16_t* bias, int act,
+                     const uint16_t* C, int64_t ldc, int out_fmt,
+                     gr_plan_t* out);
 
 /* Static, NUL-terminated name of a status code ("GR_OK", "GR_ERR_ALIAS", ...).
    Unknown codes give "GR_ERR_UNKNOWN". */

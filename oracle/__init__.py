@@ -90,6 +90,14 @@ def _load():
                                                   i64, p]
             for name in ("full", "rows", "cols", "elems"):
                 getattr(lib, "oracle_gemm_epi_" + name).restype = ctypes.c_int
+            lib.oracle_e4m3_to_f32_array.argtypes = [p, p, i64]
+            lib.oracle_e4m3_to_f32_array.restype = None
+            f32 = ctypes.c_float
+            ci = ctypes.c_int
+            lib.oracle_gemm_fp8_bt_full.argtypes = [ci, p, ci, f32, f32, i64, i64, i64, p, i64, p, i64, p, i64]
+            lib.oracle_gemm_fp8_bt_full.restype = ci
+            lib.oracle_gemm_fp8_bt_elems.argtypes = [ci, p, ci, f32, f32, i64, i64, i64, p, i64, p, i64, p, p, i64, p]
+            lib.oracle_gemm_fp8_bt_elems.restype = ci
             _lib = lib
     return _lib
 
@@ -263,3 +271,73 @@ def max_threads() -> int:
 
 def set_threads(n: int) -> None:
     _load().oracle_set_threads(int(n))
+
+
+# ---- fp8 (OCP E4M3) operands, B given transposed --------------------------------
+
+def e4m3_to_f32(bits: np.ndarray) -> np.ndarray:
+    """Element-wise OCP fp8 E4M3 -> binary32 through the oracle's own decoding."""
+    lib = _load()
+    flat = np.ascontiguousarray(bits, dtype=np.uint8).ravel()
+    out = np.empty(flat.size, dtype=np.float32)
+    lib.oracle_e4m3_to_f32_array(_ptr(flat), _ptr(out), flat.size)
+    return out.reshape(np.shape(bits))
+
+
+def _fp8_args(A, Bt, bias, act, fmt, M, N, K, lda, ldbt):
+    if A.dtype != np.uint8 or Bt.dtype != np.uint8:
+        raise TypeError("A and Bt must be uint8 arrays of E4M3 bit patterns")
+    if not (A.flags.c_contiguous and Bt.flags.c_contiguous):
+        raise ValueError("operands must be C-contiguous")
+    if M is None:
+        M, K = A.shape
+    if N is None:
+        N = Bt.shape[0]
+    lda = K if lda is None else lda
+    ldbt = K if ldbt is None else ldbt
+    if M > 0 and K > 0 and A.size < (M - 1) * lda + K:
+        raise ValueError("A too small for M, K, lda")
+    if N > 0 and K > 0 and Bt.size < (N - 1) * ldbt + K:
+        raise ValueError("Bt too small for N, K, ldbt")
+    if fmt not in _FMTS or act not in ACTS:
+        raise ValueError("bad format or activation")
+    bptr = 0
+    if bias is not None:
+        if bias.dtype != np.uint16 or not bias.flags.c_contiguous or bias.ndim != 1 or bias.size < N:
+            raise TypeError("bias must be a contiguous 1-D uint16 array of N bit patterns")
+        bptr = _ptr(bias)
+    return int(M), int(N), int(K), int(lda), int(ldbt), bptr
+
+
+def gemm_fp8_bt_full(A, Bt, scale_a=1.0, scale_b=1.0, fmt="f16", bias=None, act="relu", M=None, N=None, K=None,
+                     lda=None, ldbt=None, threads=None):
+    """act(scale_a * scale_b * (A . Bt^T) + bias) as fp16 (or bf16) bits, M x N."""
+    M, N, K, lda, ldbt, bptr = _fp8_args(A, Bt, bias, act, fmt, M, N, K, lda, ldbt)
+    lib = _load()
+    if threads:
+        lib.oracle_set_threads(int(threads))
+    C = np.zeros((M, N), dtype=np.uint16)
+    if M > 0 and N > 0:
+        lib.oracle_gemm_fp8_bt_full(_FMTS.index(fmt), bptr, ACTS[act], scale_a, scale_b, M, N, K, _ptr(A), lda,
+                                    _ptr(Bt), ldbt, _ptr(C), N)
+    return C
+
+
+def gemm_fp8_bt_elems(A, Bt, ii, jj, scale_a=1.0, scale_b=1.0, fmt="f16", bias=None, act="relu", M=None, N=None,
+                      K=None, lda=None, ldbt=None, threads=None):
+    """Single elements C[ii[e], jj[e]] of gemm_fp8_bt_full."""
+    M, N, K, lda, ldbt, bptr = _fp8_args(A, Bt, bias, act, fmt, M, N, K, lda, ldbt)
+    i = np.ascontiguousarray(ii, dtype=np.int64)
+    j = np.ascontiguousarray(jj, dtype=np.int64)
+    if i.shape != j.shape:
+        raise ValueError("index arrays differ in length")
+    if i.size and (i.min() < 0 or i.max() >= M or j.min() < 0 or j.max() >= N):
+        raise IndexError("element index out of range")
+    lib = _load()
+    if threads:
+        lib.oracle_set_threads(int(threads))
+    out = np.zeros(i.size, dtype=np.uint16)
+    if i.size:
+        lib.oracle_gemm_fp8_bt_elems(_FMTS.index(fmt), bptr, ACTS[act], scale_a, scale_b, M, N, K, _ptr(A), lda,
+                                     _ptr(Bt), ldbt, _ptr(i), _ptr(j), i.size, _ptr(out))
+    return out

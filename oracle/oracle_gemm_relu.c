@@ -54,6 +54,13 @@
  *       in double precision with the C library (erf, tanh, exp); then y is
  *       rounded once to the output format, nearest with ties to even.  ReLU
  *       and the identity stay in fp32 (they are exact) and round as in step 4.
+ * The *_fp8_* entry points take A (M x K) and Bt (N x K) in OCP fp8 E4M3
+ * (decoded exactly to fp32 below), B given transposed: acc = sum over k of
+ * a[i][k] * bt[j][k] in fp32, k increasing (a product of two E4M3 values has
+ * at most 8 significant bits and stays in the fp32 normal range, so it is
+ * exact); then x = fl32(acc * s) with s = fl32(scale_a * scale_b), the
+ * per-tensor dequantisation scales, and steps 3' and 4' as above.
+ *
  * The single rounding from double goes through fp32 with round-to-odd (the
  * nearest fp32 toward zero with its last bit forced to 1 when inexact), which
  * keeps two or more spare bits over the fp16 and bfloat16 significands, so
@@ -156,6 +163,23 @@ uint16_t oracle_f32_to_bf16_rne(float f) {
     return (uint16_t)keep;
 }
 
+/* OCP fp8 E4M3: sign, 4 exponent bits (bias 7), 3 fraction bits.  Exponent
+   field 0 is the subnormal range (m / 8 * 2^-6); S.1111.111 is NaN; there is
+   no infinity (S.1111.110 = 448 is the largest finite value). */
+float oracle_e4m3_to_f32(uint8_t b) {
+    const uint32_t sign = (uint32_t)(b >> 7) << 31;
+    const uint32_t e = (b >> 3) & 0xFu, m = b & 7u;
+    if (e == 15u && m == 7u) return bits_to_f32(sign | 0x7FC00000u);
+    float v;
+    if (e == 0u) v = (float)m * 0.001953125f; /* m * 2^-9, exact */
+    else v = bits_to_f32(((e - 7u + 127u) << 23) | (m << 20));
+    return sign ? -v : v;
+}
+
+void oracle_e4m3_to_f32_array(const uint8_t* in, float* out, int64_t n) {
+    for (int64_t e = 0; e < n; ++e) out[e] = oracle_e4m3_to_f32(in[e]);
+}
+
 /* Array forms of the conversions (used by the conversion pins). */
 void oracle_bf16_to_f32_array(const uint16_t* in, float* out, int64_t n) {
     for (int64_t e = 0; e < n; ++e) out[e] = oracle_bf16_to_f32(in[e]);
@@ -184,9 +208,10 @@ enum { ACT_NONE = 0, ACT_RELU = 1, ACT_GELU = 2, ACT_GELU_TANH = 3, ACT_SILU = 4
 typedef struct {
     const uint16_t* bias;
     int act;
+    float scale; /* multiplies the fp32 sum first (1 except for the fp8 entry points) */
 } Epi;
 
-static const Epi kRelu = {NULL, ACT_RELU};
+static const Epi kRelu = {NULL, ACT_RELU, 1.0f};
 
 static float widen(int fmt, uint16_t h) { return fmt == FMT_BF16 ? oracle_bf16_to_f32(h) : oracle_f16_to_f32(h); }
 
@@ -224,7 +249,7 @@ static double act_f64(int act, double x) {
 
 /* Steps 3 and 4 (or 3' and 4') for output column j. */
 static uint16_t epilogue(int fmt, const Epi* ep, int64_t j, float acc) {
-    float x = acc;
+    float x = acc * ep->scale; /* exact when the scale is 1 */
     if (ep->bias) x = x + widen(fmt, ep->bias[j]);
     if (ep->act == ACT_RELU) return round_to(fmt, (x > 0.0f) ? x : 0.0f); /* NaN compares false -> +0 */
     if (ep->act == ACT_NONE) return round_to(fmt, x);
@@ -418,7 +443,7 @@ static int epi_check(int fmt, int act) {
 int oracle_gemm_epi_full(int fmt, const uint16_t* bias, int act, int64_t M, int64_t N, int64_t K, const uint16_t* A,
                          int64_t lda, const uint16_t* B, int64_t ldb, uint16_t* C, int64_t ldc) {
     if (!epi_check(fmt, act)) return -2;
-    const Epi ep = {bias, act};
+    const Epi ep = {bias, act, 1.0f};
     return gemm_full(fmt, &ep, M, N, K, A, lda, B, ldb, C, ldc);
 }
 
@@ -427,7 +452,7 @@ int oracle_gemm_epi_rows(int fmt, const uint16_t* bias, int act, int64_t M, int6
                          uint16_t* out) {
     (void)M;
     if (!epi_check(fmt, act)) return -2;
-    const Epi ep = {bias, act};
+    const Epi ep = {bias, act, 1.0f};
     return gemm_rows(fmt, &ep, N, K, A, lda, B, ldb, rows, nrows, out);
 }
 
@@ -436,7 +461,7 @@ int oracle_gemm_epi_cols(int fmt, const uint16_t* bias, int act, int64_t M, int6
                          uint16_t* out) {
     (void)N;
     if (!epi_check(fmt, act)) return -2;
-    const Epi ep = {bias, act};
+    const Epi ep = {bias, act, 1.0f};
     return gemm_cols(fmt, &ep, M, K, A, lda, B, ldb, cols, ncols, out);
 }
 
@@ -446,6 +471,43 @@ int oracle_gemm_epi_elems(int fmt, const uint16_t* bias, int act, int64_t M, int
     (void)M;
     (void)N;
     if (!epi_check(fmt, act)) return -2;
-    const Epi ep = {bias, act};
+    const Epi ep = {bias, act, 1.0f};
     return gemm_elems(fmt, &ep, K, A, lda, B, ldb, ii, jj, n, out);
+}
+
+/* ---- fp8 (E4M3) operands, B given transposed ---------------------------------- */
+
+/* One output element of the fp8 product. */
+static uint16_t fp8_element(int fmt, const Epi* ep, int64_t i, int64_t j, int64_t K, const uint8_t* A, int64_t lda,
+                            const uint8_t* Bt, int64_t ldbt) {
+    float acc = 0.0f;
+    for (int64_t k = 0; k < K; ++k)
+        acc = acc + oracle_e4m3_to_f32(A[i * lda + k]) * oracle_e4m3_to_f32(Bt[j * ldbt + k]);
+    return epilogue(fmt, ep, j, acc);
+}
+
+/* C[i*ldc + j] for all i < M, j < N.  fmt: output format (0 fp16, 1 bf16).
+   Returns -2 for an unknown format or activation. */
+int oracle_gemm_fp8_bt_full(int fmt, const uint16_t* bias, int act, float scale_a, float scale_b, int64_t M,
+                            int64_t N, int64_t K, const uint8_t* A, int64_t lda, const uint8_t* Bt, int64_t ldbt,
+                            uint16_t* C, int64_t ldc) {
+    if (!epi_check(fmt, act)) return -2;
+    const Epi ep = {bias, act, scale_a * scale_b};
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t i = 0; i < M; ++i)
+        for (int64_t j = 0; j < N; ++j) C[i * ldc + j] = fp8_element(fmt, &ep, i, j, K, A, lda, Bt, ldbt);
+    return 0;
+}
+
+/* Single elements: out[e] = C[ii[e]][jj[e]]. */
+int oracle_gemm_fp8_bt_elems(int fmt, const uint16_t* bias, int act, float scale_a, float scale_b, int64_t M,
+                             int64_t N, int64_t K, const uint8_t* A, int64_t lda, const uint8_t* Bt, int64_t ldbt,
+                             const int64_t* ii, const int64_t* jj, int64_t n, uint16_t* out) {
+    (void)M;
+    (void)N;
+    if (!epi_check(fmt, act)) return -2;
+    const Epi ep = {bias, act, scale_a * scale_b};
+#pragma omp parallel for schedule(static)
+    for (int64_t e = 0; e < n; ++e) out[e] = fp8_element(fmt, &ep, ii[e], jj[e], K, A, lda, Bt, ldbt);
+    return 0;
 }

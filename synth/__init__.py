@@ -111,3 +111,33 @@ def sample_indices(M: int, N: int, count: int, seed: int):
     """``count`` seeded (i, j) pairs, uniform over the M x N result."""
     rng = np.random.default_rng(10_000 + seed)
     return rng.integers(0, M, size=count), rng.integers(0, N, size=count)
+
+
+E4M3_MAX = 448.0  # largest finite OCP fp8 E4M3 value
+E4M3_LARGEST_BITS = 0x7E
+
+
+def e4m3(shape, gen, scale: float = 1.0) -> np.ndarray:
+    """N(0,1) * scale drawn in fp32, clamped to +-448 and rounded to OCP fp8
+    E4M3 (nearest even) by torch; returns uint8 bits."""
+    torch = _torch()
+    x = torch.randn(*shape, generator=gen, dtype=torch.float32) * scale
+    x = x.clamp(-E4M3_MAX, E4M3_MAX)
+    return x.to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+
+
+def fp8_operands(M: int, N: int, K: int, seed: int, lda: int | None = None, ldbt: int | None = None,
+                 scale_a: float = 1.0, scale_b: float = 1.0, pad_value: int = E4M3_LARGEST_BITS):
+    """A (M x lda) and Bt (N x ldbt) as E4M3 bits, entries N(0,1) times the
+    given scales; padding columns hold ``pad_value`` (default 448)."""
+    torch = _torch()
+    gen = torch.Generator().manual_seed(seed)
+    lda = K if lda is None else lda
+    ldbt = K if ldbt is None else ldbt
+    A = np.full((M, max(lda, 1)), pad_value, dtype=np.uint8)
+    Bt = np.full((N, max(ldbt, 1)), pad_value, dtype=np.uint8)
+    if M and K:
+        A[:, :K] = e4m3((M, K), gen, scale_a)
+    if N and K:
+        Bt[:, :K] = e4m3((N, K), gen, scale_b)
+    return A, Bt

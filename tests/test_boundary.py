@@ -447,6 +447,35 @@ def test_bias_act_argument_checks_need_no_gpu():
                  gr.GR_PATH_TILE) == gr.GR_ERR_INVALID_PATH
 
 
+def test_fp8_planner_and_checks_need_no_gpu():
+    """gemm_fp8_bt: the pipelined kernel for K % 64 == 0 with 16-byte rows (any
+    M, N), the guarded kernel otherwise; argument errors before any HIP call."""
+    def plan8(M, N, K, lda=None, ldbt=None, ldc=None, a=BASE_A, b=BASE_B, c=BASE_C, act=1, fmt=gr.GR_FMT_F16):
+        lda = max(K, 1) if lda is None else lda
+        ldbt = max(K, 1) if ldbt is None else ldbt
+        ldc = max(N, 1) if ldc is None else ldc
+        return gr.gemm_fp8_bt_plan(M, N, K, a, lda, b, ldbt, None, act, c, ldc, fmt)
+    st, p = plan8(4096, 4096, 4096)
+    assert st == gr.GR_OK and p["path"] == gr.GR_PATH_TILE and (p["block_m"], p["block_k"], p["grid"]) == (256, 64, 256)
+    assert plan8(17, 600, 256)[1]["path"] == gr.GR_PATH_TILE                       # M < 256: rows clamped
+    assert plan8(300, 270, 96)[1]["path"] == gr.GR_PATH_TILE_EDGE                  # K % 64 != 0
+    assert plan8(300, 270, 128, lda=136)[1]["path"] == gr.GR_PATH_TILE_EDGE        # lda not a multiple of 16
+    assert plan8(300, 270, 128, a=BASE_A + 8)[1]["path"] == gr.GR_PATH_TILE_EDGE   # A not 16-byte aligned
+    st, p = plan8(300, 270, 100)
+    assert p["grid"] == 3 * 3 and p["block_m"] == 128
+    assert plan8(0, 5, 5)[1]["path"] == gr.GR_PATH_NONE
+    assert plan8(8, 8, 8, lda=7)[0] == gr.GR_ERR_INVALID_LD
+    assert plan8(8, 8, 8, act=7)[0] == gr.GR_ERR_INVALID_ARG
+    assert plan8(8, 8, 8, fmt=2)[0] == gr.GR_ERR_INVALID_ARG
+    assert plan8(8, 8, 8, c=BASE_A + 4)[0] == gr.GR_ERR_ALIAS   # C's bytes overlap A (8 x 8 bytes)
+    assert plan8(8, 8, 8, c=BASE_A + 64)[0] == gr.GR_OK          # A spans 64 bytes, C starts after
+    assert gr.gemm_fp8_bt(8, 8, 8, BASE_A, 8, BASE_B, 8, 1.0, 1.0, BASE_C + 2, 1, BASE_C, 8) == gr.GR_ERR_ALIAS
+    assert gr.gemm_fp8_bt_forced(300, 270, 96, BASE_A, 96, BASE_B, 96, 1.0, 1.0, None, 1, BASE_C, 270, 0, None,
+                                 gr.GR_PATH_TILE) == gr.GR_ERR_INVALID_PATH
+    assert gr.gemm_fp8_bt_forced(300, 270, 128, BASE_A, 128, BASE_B, 128, 1.0, 1.0, None, 1, BASE_C, 270, 0, None,
+                                 gr.GR_PATH_SMALL_M) == gr.GR_ERR_INVALID_PATH
+
+
 def test_act_codes_match_the_oracle():
     import oracle
     assert gr.ACT_CODES == oracle.ACTS
