@@ -826,6 +826,21 @@ bool fp8_tile_ok(int64_t M, int64_t N, int64_t K, uintptr_t A, int64_t lda, uint
            ldbt % 16 == 0 && lda <= MAX_LD && ldbt <= MAX_LD;
 }
 
+// The fp8 small-M stream: M <= 16, K a positive multiple of the 512-deep
+// chunk, 16-byte aligned rows.
+bool fp8_smallm_ok(int64_t M, int64_t N, int64_t K, uintptr_t A, int64_t lda, uintptr_t Bt, int64_t ldbt) {
+    using namespace gr::fp8;
+    return M >= 1 && M <= SM_MAX_M && N >= 1 && K > 0 && K % SM_KC == 0 && A % 16 == 0 && lda % 16 == 0 &&
+           Bt % 16 == 0 && ldbt % 16 == 0 && lda <= SM_MAX_LD && ldbt <= SM_MAX_LD;
+}
+
+// 256 x 256 fp8 tiles unless they would fill less than half of one wave of
+// workgroups (or M < 256): then 128 x 128 tiles, two workgroups per CU.
+bool fp8_large_tiles(int64_t M, int64_t N) {
+    if (M < 256) return false;
+    return ((M + 255) / 256) * ((N + 255) / 256) > kSmallTileMaxLargeTiles;
+}
+
 void fill_plan_fp8(int path, int64_t M, int64_t N, uintptr_t C, int64_t ldc, gr_plan_t* p) {
     std::memset(p, 0, sizeof(*p));
     p->path = path;
@@ -835,13 +850,24 @@ void fill_plan_fp8(int path, int64_t M, int64_t N, uintptr_t C, int64_t ldc, gr_
     p->split_k = 1;
     if (path == GR_PATH_TILE) {
         using namespace gr::fp8;
-        p->block_m = BM;
-        p->block_n = BN;
+        const int64_t bm = fp8_large_tiles(M, N) ? 256 : 128;
+        p->block_m = (int32_t)bm;
+        p->block_n = (int32_t)bm;
         p->stages = STAGES;
-        p->grid = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
+        p->grid = ((M + bm - 1) / bm) * ((N + bm - 1) / bm);
         p->vec_a = 16;
         p->vec_b = 16;
         p->group_m = kGroupM;
+    } else if (path == GR_PATH_SMALL_M) {
+        using namespace gr::fp8;
+        p->block_m = SM_MAX_M;
+        p->block_n = SM_NB;
+        p->block_k = SM_KC;
+        p->stages = SM_SLOTS;
+        p->grid = (N + SM_NB - 1) / SM_NB;
+        p->vec_a = 16;
+        p->vec_b = 16;
+        p->group_m = 1;
     } else if (path == GR_PATH_TILE_EDGE) {
         using namespace gr::fp8;
         p->block_m = G_BM;
@@ -858,12 +884,16 @@ int plan_call_fp8(int64_t M, int64_t N, int64_t K, uintptr_t A, int64_t lda, uin
                   uintptr_t bias, int act, uintptr_t C, int64_t ldc, int out_fmt, int forced, gr_plan_t* p) {
     int st = validate_fp8(M, N, K, A, lda, Bt, ldbt, bias, act, C, ldc, out_fmt);
     if (st != GR_OK) return st;
+    const bool tile_ok = fp8_tile_ok(M, N, K, A, lda, Bt, ldbt);
+    const bool smallm_ok = fp8_smallm_ok(M, N, K, A, lda, Bt, ldbt);
     int path;
     if (M == 0 || N == 0) path = GR_PATH_NONE;
-    else path = fp8_tile_ok(M, N, K, A, lda, Bt, ldbt) ? GR_PATH_TILE : GR_PATH_TILE_EDGE;
+    else if (smallm_ok) path = GR_PATH_SMALL_M;
+    else path = tile_ok ? GR_PATH_TILE : GR_PATH_TILE_EDGE;
     if (forced >= 0 && path != GR_PATH_NONE) {
-        if (forced == GR_PATH_TILE && path != GR_PATH_TILE) return GR_ERR_INVALID_PATH;
-        if (forced != GR_PATH_TILE && forced != GR_PATH_TILE_EDGE) return GR_ERR_INVALID_PATH;
+        if ((forced == GR_PATH_TILE && !tile_ok) || (forced == GR_PATH_SMALL_M && !smallm_ok) ||
+            (forced != GR_PATH_TILE && forced != GR_PATH_TILE_EDGE && forced != GR_PATH_SMALL_M))
+            return GR_ERR_INVALID_PATH;
         path = forced;
     }
     fill_plan_fp8(path, M, N, C, ldc, p);
@@ -875,14 +905,30 @@ int run_fp8(const gr_plan_t& p, int64_t M, int64_t N, int64_t K, const uint8_t* 
             int64_t ldbt, uint16_t* C, int64_t ldc, const gr::EpiArgs& ep, hipStream_t stream) {
     using namespace gr::fp8;
     if (p.path == GR_PATH_TILE) {
-        const uint32_t tiles_m = (uint32_t)((M + BM - 1) / BM);
-        const uint32_t tiles_n = (uint32_t)((N + BN - 1) / BN);
-        const bool whole = M % BM == 0 && N % BN == 0;
+        const int64_t bm = p.block_m;
+        const uint32_t tiles_m = (uint32_t)((M + bm - 1) / bm);
+        const uint32_t tiles_n = (uint32_t)((N + bm - 1) / bm);
+        const bool whole = M % bm == 0 && N % bm == 0;
+        const uint32_t gm = (uint32_t)p.group_m;
+        const int vc = (int)p.vec_c;
+        if (bm == 256) {
+            if (whole)
+                return launch(gemm_fp8_tile_kernel<256, false, E>, p.grid, THREADS, stream, A, Bt, C, M, N, K, lda,
+                              ldbt, ldc, tiles_m, tiles_n, gm, vc, ep);
+            return launch(gemm_fp8_tile_kernel<256, true, E>, p.grid, THREADS, stream, A, Bt, C, M, N, K, lda, ldbt,
+                          ldc, tiles_m, tiles_n, gm, vc, ep);
+        }
         if (whole)
-            return launch(gemm_fp8_tile_kernel<false, E>, p.grid, THREADS, stream, A, Bt, C, M, N, K, lda, ldbt, ldc,
-                          tiles_m, tiles_n, (uint32_t)p.group_m, (int)p.vec_c, ep);
-        return launch(gemm_fp8_tile_kernel<true, E>, p.grid, THREADS, stream, A, Bt, C, M, N, K, lda, ldbt, ldc,
-                      tiles_m, tiles_n, (uint32_t)p.group_m, (int)p.vec_c, ep);
+            return launch(gemm_fp8_tile_kernel<128, false, E>, p.grid, THREADS, stream, A, Bt, C, M, N, K, lda, ldbt,
+                          ldc, tiles_m, tiles_n, gm, vc, ep);
+        return launch(gemm_fp8_tile_kernel<128, true, E>, p.grid, THREADS, stream, A, Bt, C, M, N, K, lda, ldbt, ldc,
+                      tiles_m, tiles_n, gm, vc, ep);
+    }
+    if (p.path == GR_PATH_SMALL_M) {
+        if (N % SM_NB == 0)
+            return launch(gemm_fp8_smallm_kernel<false, E>, p.grid, 256, stream, A, Bt, C, M, N, K, lda, ldbt, ldc,
+                          ep);
+        return launch(gemm_fp8_smallm_kernel<true, E>, p.grid, 256, stream, A, Bt, C, M, N, K, lda, ldbt, ldc, ep);
     }
     if (p.path == GR_PATH_TILE_EDGE) {
         const uint32_t tiles_n = (uint32_t)((N + G_BN - 1) / G_BN);
@@ -1036,7 +1082,7 @@ int gemm_fp8_bt(int64_t M, int64_t N, int64_t K, const uint8_t* A, int64_t lda, 
 int gemm_fp8_bt_forced(int64_t M, int64_t N, int64_t K, const uint8_t* A, int64_t lda, const uint8_t* Bt,
                        int64_t ldbt, float scale_a, float scale_b, const uint16_t* bias, int act, uint16_t* C,
                        int64_t ldc, int out_fmt, void* stream, int path) {
-    if (path != GR_PATH_TILE && path != GR_PATH_TILE_EDGE) return GR_ERR_INVALID_PATH;
+    if (path != GR_PATH_TILE && path != GR_PATH_TILE_EDGE && path != GR_PATH_SMALL_M) return GR_ERR_INVALID_PATH;
     return entry_fp8(M, N, K, A, lda, Bt, ldbt, scale_a, scale_b, bias, act, C, ldc, out_fmt, stream, path);
 }
 

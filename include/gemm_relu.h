@@ -388,9 +388,11 @@ int gemm_bias_act_bf16_forced(int64_t M, int64_t N, int64_t K,
  * "TileLang programming basics", section "推荐顺序", step 6) and fp8 as the
  * tensor-core format after tf32 and int8 (TileLang tutorial, section
  * "张量核与 CUDA core"); per-tensor scales are the plainest form of those
- * scales.  Paths: GR_PATH_TILE (K a multiple of 64, A, Bt and their pitches
- * 16-byte aligned; any M, N) and GR_PATH_TILE_EDGE (everything else,
- * including K == 0, which gives act(bias)).  C is fp16 or bfloat16 bits with
+ * scales.  Paths: GR_PATH_SMALL_M (M <= 16, K a multiple of 512, A, Bt and
+ * their pitches 16-byte aligned: a stream over Bt), GR_PATH_TILE (K a
+ * multiple of 64, the same alignment, any M and N; 256 x 256 tiles, or
+ * 128 x 128 when those would leave compute units idle) and GR_PATH_TILE_EDGE
+ * (everything else, including K == 0, which gives act(bias)).  C is fp16 or bfloat16 bits with
  * pitch ldc; the conventions of gemm_relu_f16 hold otherwise (C never read,
  * outside the M x N window never written, GR_ERR_ALIAS when C overlaps A,
  * Bt or the bias, GR_ERR_INVALID_ARG for an unknown act or out_fmt).
@@ -406,9 +408,9 @@ int gemm_fp8_bt(int64_t M, int64_t N, int64_t K,
                 uint16_t* C, int64_t ldc, int out_fmt,
                 void* stream);
 
-/* gemm_fp8_bt on a given path (GR_PATH_TILE or GR_PATH_TILE_EDGE;
-   GR_ERR_INVALID_PATH otherwise or when the path's conditions do not
-   hold).  Test hook. */
+/* gemm_fp8_bt on a given path (GR_PATH_TILE, GR_PATH_TILE_EDGE or
+   GR_PATH_SMALL_M; GR_ERR_INVALID_PATH otherwise or when the path's
+   conditions do not hold).  Test hook. */
 int gemm_fp8_bt_forced(int64_t M, int64_t N, int64_t K,
                        const uint8_t* A, int64_t lda,
                        const uint8_t* Bt, int64_t ldbt,

@@ -458,6 +458,10 @@ def test_fp8_planner_and_checks_need_no_gpu():
     st, p = plan8(4096, 4096, 4096)
     assert st == gr.GR_OK and p["path"] == gr.GR_PATH_TILE and (p["block_m"], p["block_k"], p["grid"]) == (256, 64, 256)
     assert plan8(17, 600, 256)[1]["path"] == gr.GR_PATH_TILE                       # M < 256: rows clamped
+    assert plan8(17, 600, 256)[1]["block_m"] == 128                                # few tiles: 128 x 128
+    st, p = plan8(8, 16384, 8192)
+    assert p["path"] == gr.GR_PATH_SMALL_M and p["grid"] == 16384 // 64          # M <= 16, K % 512 == 0
+    assert plan8(8, 16384, 8000)[1]["path"] == gr.GR_PATH_TILE                     # K % 512 != 0
     assert plan8(300, 270, 96)[1]["path"] == gr.GR_PATH_TILE_EDGE                  # K % 64 != 0
     assert plan8(300, 270, 128, lda=136)[1]["path"] == gr.GR_PATH_TILE_EDGE        # lda not a multiple of 16
     assert plan8(300, 270, 128, a=BASE_A + 8)[1]["path"] == gr.GR_PATH_TILE_EDGE   # A not 16-byte aligned
@@ -474,6 +478,8 @@ def test_fp8_planner_and_checks_need_no_gpu():
                                  gr.GR_PATH_TILE) == gr.GR_ERR_INVALID_PATH
     assert gr.gemm_fp8_bt_forced(300, 270, 128, BASE_A, 128, BASE_B, 128, 1.0, 1.0, None, 1, BASE_C, 270, 0, None,
                                  gr.GR_PATH_SMALL_M) == gr.GR_ERR_INVALID_PATH
+    assert gr.gemm_fp8_bt_forced(8, 270, 128, BASE_A, 128, BASE_B, 128, 1.0, 1.0, None, 1, BASE_C, 270, 0, None,
+                                 gr.GR_PATH_TILE_SPLIT) == gr.GR_ERR_INVALID_PATH
 
 
 def test_act_codes_match_the_oracle():

@@ -65,12 +65,18 @@ def bias_for(N, fmt, seed):
 
 
 CASES = [
-    # M, N, K, lda, ldbt, ldc, expected path, what
-    (512, 512, 256, 256, 256, 512, gr.GR_PATH_TILE, "whole tiles"),
-    (1024, 768, 512, 528, 512, 768, gr.GR_PATH_TILE, "whole tiles, padded A"),
-    (300, 270, 128, 128, 144, 273, gr.GR_PATH_TILE, "partial tiles"),
-    (17, 600, 256, 256, 256, 601, gr.GR_PATH_TILE, "M < 256"),
-    (2304, 1100, 192, 192, 192, 1100, gr.GR_PATH_TILE, "many tiles, 3 strips"),
+    # M, N, K, lda, ldbt, ldc, expected path (tile size), what
+    (512, 512, 256, 256, 256, 512, (gr.GR_PATH_TILE, 128), "128 tiles, whole"),
+    (1024, 768, 512, 528, 512, 768, (gr.GR_PATH_TILE, 128), "128 tiles, padded A"),
+    (300, 270, 128, 128, 144, 273, (gr.GR_PATH_TILE, 128), "128 tiles, partial"),
+    (17, 600, 256, 256, 256, 601, (gr.GR_PATH_TILE, 128), "M = 17"),
+    (2304, 1100, 192, 192, 192, 1100, (gr.GR_PATH_TILE, 128), "128 tiles, 3 strips"),
+    (2600, 3000, 128, 128, 144, 3001, (gr.GR_PATH_TILE, 256), "256 tiles, partial"),
+    (3072, 3072, 192, 192, 192, 3072, (gr.GR_PATH_TILE, 256), "256 tiles, whole"),
+    (8, 4096, 1024, 1024, 1024, 4096, (gr.GR_PATH_SMALL_M, 16), "small-M"),
+    (16, 1000, 512, 512, 528, 1001, (gr.GR_PATH_SMALL_M, 16), "small-M, partial column block"),
+    (1, 64, 2048, 2048, 2048, 64, (gr.GR_PATH_SMALL_M, 16), "small-M, one row"),
+    (12, 300, 640, 640, 640, 300, (gr.GR_PATH_TILE, 128), "M <= 16, K % 512 != 0"),
     (300, 270, 100, 101, 103, 273, gr.GR_PATH_TILE_EDGE, "guarded, odd K and pitches"),
     (5, 130, 1000, 1000, 1000, 130, gr.GR_PATH_TILE_EDGE, "guarded, K % 64 != 0"),
     (700, 500, 320, 330, 320, 500, gr.GR_PATH_TILE_EDGE, "guarded, misaligned A rows"),
@@ -81,7 +87,11 @@ CASES = [
 @pytest.mark.parametrize("case", CASES, ids=[c[-1] for c in CASES])
 def test_fp8_parity(case, fmt):
     M, N, K, lda, ldbt, ldc, path, what = case
-    assert plan(M, N, K, lda, ldbt, ldc)["path"] == path
+    p = plan(M, N, K, lda, ldbt, ldc)
+    if isinstance(path, tuple):
+        assert (p["path"], p["block_m"]) == path, p
+    else:
+        assert p["path"] == path, p
     A, Bt = synth.fp8_operands(M, N, K, seed=M + N + K, lda=lda, ldbt=ldbt)
     sa, sb = 0.125, 2.0 / np.sqrt(K)
     bias = bias_for(N, fmt, 3)
@@ -93,8 +103,9 @@ def test_fp8_parity(case, fmt):
 
 
 @pytest.mark.parametrize("act", list(gr.ACT_CODES))
-@pytest.mark.parametrize("path_case", [(300, 270, 128, 128, 128, 270), (300, 270, 100, 100, 100, 270)],
-                         ids=["tile", "guarded"])
+@pytest.mark.parametrize("path_case", [(300, 270, 128, 128, 128, 270), (300, 270, 100, 100, 100, 270),
+                                       (7, 270, 1024, 1024, 1024, 270)],
+                         ids=["tile", "guarded", "small-M"])
 def test_fp8_every_activation(act, path_case):
     M, N, K, lda, ldbt, ldc = path_case
     A, Bt = synth.fp8_operands(M, N, K, seed=21, lda=lda, ldbt=ldbt)
@@ -105,7 +116,8 @@ def test_fp8_every_activation(act, path_case):
     assert_parity(C, ref, "fp8 %s" % act)
 
 
-@pytest.mark.parametrize("M,N,K", [(512, 512, 256), (300, 270, 128), (2304, 1100, 192), (40, 2048, 1024)])
+@pytest.mark.parametrize("M,N,K", [(512, 512, 256), (300, 270, 128), (2304, 1100, 192), (40, 2048, 1024),
+                                   (2600, 3000, 128)])
 def test_fp8_tile_and_guarded_bitwise(M, N, K):
     A, Bt = synth.fp8_operands(M, N, K, seed=31)
     C1 = run(A, Bt, M, N, K, K, K, N, 0.5, 0.5, None, "silu", path=gr.GR_PATH_TILE)
@@ -155,3 +167,16 @@ def test_fp8_tensor_wrapper():
     assert c.dtype == t.bfloat16
     ref = oracle.gemm_fp8_bt_full(A, Bt, 0.5, 0.125, "bf16", bias_for(N, "bf16", 6), "gelu_tanh")
     assert_parity(c.view(t.int16).cpu().numpy().view(np.uint16), ref, "fp8 wrapper", fmt="bf16")
+
+
+@pytest.mark.parametrize("M,N,K", [(8, 16384, 8192), (16, 256, 512)])
+def test_fp8_small_m_against_tile(M, N, K):
+    """The small-M stream and the 128 x 128 tile kernel on the same input
+    (different matrix-core shapes: equal within the tolerance), and the
+    small-M result against the oracle."""
+    A, Bt = synth.fp8_operands(M, N, K, seed=71)
+    sa, sb = 1.0 / 16, 1.0 / 16
+    C1 = run(A, Bt, M, N, K, K, K, N, sa, sb, path=gr.GR_PATH_SMALL_M)[:M * N].reshape(M, N)
+    C2 = run(A, Bt, M, N, K, K, K, N, sa, sb, path=gr.GR_PATH_TILE)[:M * N].reshape(M, N)
+    assert_parity(C1, C2, "small-M vs tile")
+    assert_parity(C1, oracle.gemm_fp8_bt_full(A, Bt, sa, sb), "small-M vs oracle")
