@@ -27,7 +27,8 @@ constexpr int kVersion = 100;  // 0.1.0
 constexpr int64_t kMaxDim = (int64_t(1) << 31) - 1;
 constexpr int64_t kMaxSpanBytes = int64_t(1) << 62;
 constexpr int kGroupM = 4;          // tile rows per workgroup-order group
-constexpr int kSmallMThreshold = 16;  // rows of A handled by the small-M kernel
+constexpr int kSmallMThreshold = 16;  // rows of A handled by the small-M split and Bt kernels
+constexpr int kSmallMMaxRows = 64;    // rows the single-pass small-M kernel handles (4 blocks of 16)
 constexpr int64_t kPackMinMacs = int64_t(1) << 30;  // smallest M*N*K the planner packs for
 constexpr int64_t kWorkspaceAlign = 256;            // required alignment of a workspace (bytes)
 #ifndef GR_SMALLM_WAVES
@@ -102,6 +103,13 @@ bool smallm_ok(int64_t M, int64_t N, int64_t K, uintptr_t A, int64_t lda, uintpt
     (void)N;
     (void)K;
     return M >= 1 && M <= kSmallMThreshold && A % 16 == 0 && lda % 8 == 0 && B % 8 == 0 && ldb % 4 == 0;
+}
+
+// The single-pass small-M kernel with 2 or 4 blocks of 16 rows of A.
+bool smallm_rows_ok(int64_t M, int64_t N, int64_t K, uintptr_t A, int64_t lda, uintptr_t B, int64_t ldb) {
+    (void)N;
+    (void)K;
+    return M >= 1 && M <= kSmallMMaxRows && A % 16 == 0 && lda % 8 == 0 && B % 8 == 0 && ldb % 4 == 0;
 }
 
 // Split-K layout of the small-M path: S splits of k_per_split (a multiple of
@@ -181,6 +189,10 @@ bool tile_split_layout(int64_t M, int64_t N, int64_t K, bool allow_one, TileSpli
     if (S > kTileMaxSplits) S = kTileMaxSplits;
     if (S < 1) S = 1;
     const int64_t strips = K / BK;
+    // Splitting pays only while the unsplit grid fills at most half of the
+    // CUs' workgroup slots: with 224-256 tiles a split into 2 measured 15-20%
+    // slower (8192 x 28672 x 64..256, 256 x 16384 x 8192).
+    if (!allow_one && tiles > kSmallTileMaxLargeTiles) return false;
     if (!allow_one && (S < 2 || strips * (S - 1) < kTileSplitMinSavedStrips * S)) return false;
     TileSplit q;
     q.k_per_split = (strips + S - 1) / S * BK;
@@ -282,7 +294,7 @@ void fill_plan(int path, int64_t M, int64_t N, int64_t K, uintptr_t A, int64_t l
         p->split_k = (int32_t)sp.splits;
     } else if (path == GR_PATH_SMALL_M) {
         using namespace gr::smallm;
-        p->block_m = MAX_M;
+        p->block_m = M <= MAX_M ? MAX_M : (M <= 2 * MAX_M ? 2 * MAX_M : 4 * MAX_M);  // rows per workgroup
         p->block_n = NB;
         p->block_k = KSTEP;
         p->stages = kSmallMUnroll;
@@ -307,12 +319,13 @@ int choose_path(int64_t M, int64_t N, int64_t K, uintptr_t A, int64_t lda, uintp
             return GR_PATH_SMALL_M_SPLIT;
         return GR_PATH_SMALL_M;
     }
-    if (tile_fast_ok(M, N, K, A, lda, B, ldb)) {
-        if (ws_bytes > 0 && !use_large_tiles(M, N) && tile_split_layout(M, N, K, false, ts) &&
-            ts->bytes <= ws_bytes)
-            return GR_PATH_TILE_SPLIT;
-        return GR_PATH_TILE;
-    }
+    const bool fast = tile_fast_ok(M, N, K, A, lda, B, ldb);
+    if (fast && ws_bytes > 0 && !use_large_tiles(M, N) && tile_split_layout(M, N, K, false, ts) &&
+        ts->bytes <= ws_bytes)
+        return GR_PATH_TILE_SPLIT;
+    if (K > 0 && smallm_rows_ok(M, N, K, A, lda, B, ldb) && (N + gr::smallm::NB - 1) / gr::smallm::NB <= 256)
+        return GR_PATH_SMALL_M;
+    if (fast) return GR_PATH_TILE;
     if (ws_bytes > 0 && pack_layout(M, N, K, A, lda, B, ldb, pk) && pk->bytes <= ws_bytes &&
         (double)M * (double)N * (double)K >= (double)kPackMinMacs)
         return GR_PATH_TILE_PACKED;
@@ -486,11 +499,28 @@ int run(const gr_plan_t& p, int64_t M, int64_t N, int64_t K, const uint16_t* A, 
         case GR_PATH_SMALL_M: {
             using namespace gr::smallm;
             const bool whole = N % NB == 0 && K % KSTEP == 0;
+            constexpr int W = kSmallMWaves, U = kSmallMUnroll;
+            if (M <= MAX_M) {
+                if (whole)
+                    return launch(gemm_relu_smallm_kernel<W, U, false, E, 1>, p.grid, p.threads, stream, A, B, C, M,
+                                  N, K, lda, ldb, ldc, ep);
+                return launch(gemm_relu_smallm_kernel<W, U, true, E, 1>, p.grid, p.threads, stream, A, B, C, M, N, K,
+                              lda, ldb, ldc, ep);
+            }
+            if (M <= 2 * MAX_M) {
+                if (whole)
+                    return launch(gemm_relu_smallm_kernel<W, U, false, E, 2>, p.grid, p.threads, stream, A, B, C, M,
+                                  N, K, lda, ldb, ldc, ep);
+                return launch(gemm_relu_smallm_kernel<W, U, true, E, 2>, p.grid, p.threads, stream, A, B, C, M, N, K,
+                              lda, ldb, ldc, ep);
+            }
+            // four row blocks: one load group per register set keeps the
+            // kernel within its 256 registers per lane
             if (whole)
-                return launch(gemm_relu_smallm_kernel<kSmallMWaves, kSmallMUnroll, false, E>, p.grid, p.threads,
-                              stream, A, B, C, M, N, K, lda, ldb, ldc, ep);
-            return launch(gemm_relu_smallm_kernel<kSmallMWaves, kSmallMUnroll, true, E>, p.grid, p.threads, stream,
-                          A, B, C, M, N, K, lda, ldb, ldc, ep);
+                return launch(gemm_relu_smallm_kernel<W, 1, false, E, 4>, p.grid, p.threads, stream, A, B, C, M, N, K,
+                              lda, ldb, ldc, ep);
+            return launch(gemm_relu_smallm_kernel<W, 1, true, E, 4>, p.grid, p.threads, stream, A, B, C, M, N, K, lda,
+                          ldb, ldc, ep);
         }
         default: return GR_ERR_INVALID_PATH;
     }
@@ -511,7 +541,7 @@ int plan_call(int64_t M, int64_t N, int64_t K, uintptr_t a, int64_t lda, uintptr
         if (forced == GR_PATH_TILE) {
             if (!tile_fast_ok(M, N, K, a, lda, b, ldb)) return GR_ERR_INVALID_PATH;
         } else if (forced == GR_PATH_SMALL_M) {
-            if (K == 0 || !smallm_ok(M, N, K, a, lda, b, ldb)) return GR_ERR_INVALID_PATH;
+            if (K == 0 || !smallm_rows_ok(M, N, K, a, lda, b, ldb)) return GR_ERR_INVALID_PATH;
         } else if (forced == GR_PATH_TILE_PACKED) {
             if (!pack_layout(M, N, K, a, lda, b, ldb, pk) || pk->bytes > ws_bytes) return GR_ERR_INVALID_PATH;
         } else if (forced == GR_PATH_TILE_SPLIT) {

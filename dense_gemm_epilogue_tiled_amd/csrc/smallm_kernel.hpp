@@ -97,11 +97,14 @@ __device__ __forceinline__ u32x4 load_a8(const uint16_t* A, int64_t lda, int64_t
 }
 
 // E: element type (ElemF16 or ElemBF16; only the MFMA and the rounding differ).
-template <int W, int U, bool GUARD, typename E = ElemF16>
+// MB: blocks of 16 rows of A (M <= 16 * MB).  Each transposed B operand feeds
+// MB MFMAs, one per block of A rows, so up to 64 rows still read B once.
+template <int W, int U, bool GUARD, typename E = ElemF16, int MB = 1>
 __global__ __launch_bounds__(64 * W, 1) void gemm_relu_smallm_kernel(
     const uint16_t* __restrict__ A, const uint16_t* __restrict__ B, uint16_t* __restrict__ C,
     int64_t M, int64_t N, int64_t K, int64_t lda, int64_t ldb, int64_t ldc, EpiArgs ep) {
-    __shared__ __attribute__((aligned(16))) float red[W][MAX_M][NB];
+    constexpr int ROWS = MAX_M * MB;
+    __shared__ __attribute__((aligned(16))) float red[W][ROWS][NB];
 
     const uint32_t tid = threadIdx.x;
     const uint32_t lane = tid & 63u;
@@ -113,12 +116,14 @@ __global__ __launch_bounds__(64 * W, 1) void gemm_relu_smallm_kernel(
     const int64_t n_lane = n_base + 4 * li;
     const int64_t steps = (K + KSTEP - 1) / KSTEP;
 
-    f32x4 acc[4];
+    f32x4 acc[MB][4];
 #pragma unroll
-    for (int c = 0; c < 4; ++c) acc[c] = f32x4{};
+    for (int b = 0; b < MB; ++b)
+#pragma unroll
+        for (int c = 0; c < 4; ++c) acc[b][c] = f32x4{};
 
     // Loads of one group of U steps (this wave's steps s0, s0+W, ...).
-    auto load_group = [&](int64_t s0, u32x2 (&rb)[U][8], u32x4 (&ra)[U]) {
+    auto load_group = [&](int64_t s0, u32x2 (&rb)[U][8], u32x4 (&ra)[U][MB]) {
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const int64_t s = s0 + (int64_t)u * W;
@@ -126,24 +131,27 @@ __global__ __launch_bounds__(64 * W, 1) void gemm_relu_smallm_kernel(
             if (s < steps) {
 #pragma unroll
                 for (int r = 0; r < 8; ++r) rb[u][r] = load_b4<GUARD>(B, ldb, k + r, n_lane, K, N);
-                ra[u] = load_a8<GUARD>(A, lda, li, k, M, K);
+#pragma unroll
+                for (int b = 0; b < MB; ++b) ra[u][b] = load_a8<GUARD>(A, lda, li + 16 * b, k, M, K);
             } else {
 #pragma unroll
                 for (int r = 0; r < 8; ++r) rb[u][r] = u32x2{0u, 0u};
-                ra[u] = u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+                for (int b = 0; b < MB; ++b) ra[u][b] = u32x4{0u, 0u, 0u, 0u};
             }
         }
     };
-    auto compute_group = [&](const u32x2 (&rb)[U][8], const u32x4 (&ra)[U]) {
+    auto compute_group = [&](const u32x2 (&rb)[U][8], const u32x4 (&ra)[U][MB]) {
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-            const f16x8 a = __builtin_bit_cast(f16x8, ra[u]);
 #pragma unroll
             for (int c = 0; c < 4; ++c) {
                 u32x4 o;
 #pragma unroll
                 for (int d = 0; d < 4; ++d) o[d] = pair_halves(rb[u][2 * d][c >> 1], rb[u][2 * d + 1][c >> 1], c & 1);
-                acc[c] = E::mfma16(__builtin_bit_cast(f16x8, o), a, acc[c]);
+#pragma unroll
+                for (int b = 0; b < MB; ++b)
+                    acc[b][c] = E::mfma16(__builtin_bit_cast(f16x8, o), __builtin_bit_cast(f16x8, ra[u][b]), acc[b][c]);
             }
         }
     };
@@ -152,7 +160,7 @@ __global__ __launch_bounds__(64 * W, 1) void gemm_relu_smallm_kernel(
     // is transposed and multiplied, so each wave keeps U*8 loads outstanding.
     const int64_t stride = (int64_t)W * U;
     u32x2 rb0[U][8], rb1[U][8];
-    u32x4 ra0[U], ra1[U];
+    u32x4 ra0[U][MB], ra1[U][MB];
     int64_t s0 = wave;
     if (s0 < steps) load_group(s0, rb0, ra0);
     for (; s0 < steps; s0 += 2 * stride) {
@@ -163,15 +171,17 @@ __global__ __launch_bounds__(64 * W, 1) void gemm_relu_smallm_kernel(
         compute_group(rb1, ra1);
     }
 
-    // acc[c] holds C^T: lane l, register r is the partial sum for row
-    // m = l%16 and column n = n_base + 4(4(l/16) + r) + c.
+    // acc[b][c] holds C^T: lane l, register r is the partial sum for row
+    // m = 16b + l%16 and column n = n_base + 4(4(l/16) + r) + c.
 #pragma unroll
-    for (int c = 0; c < 4; ++c)
+    for (int b = 0; b < MB; ++b)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) red[wave][li][4 * (4 * lg + r) + c] = acc[c][r];
+        for (int c = 0; c < 4; ++c)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) red[wave][16 * b + li][4 * (4 * lg + r) + c] = acc[b][c][r];
     __syncthreads();
 
-    for (uint32_t o = tid; o < (uint32_t)(MAX_M * NB); o += 64 * W) {
+    for (uint32_t o = tid; o < (uint32_t)(ROWS * NB); o += 64 * W) {
         const uint32_t m = o / NB, nl = o % NB;
         const int64_t n = n_base + nl;
         if ((int64_t)m < M && n < N) {

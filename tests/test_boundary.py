@@ -166,9 +166,16 @@ def test_plan_partial_tiles_take_the_pipelined_kernel():
     st, p = plan(4099, 3071, 2048, lda=2048, ldb=3072, ldc=3071)
     assert st == gr.GR_OK and p["path"] == gr.GR_PATH_TILE and p["grid"] == 17 * 12 and p["vec_c"] == 1
     assert plan(256, 1, 32, ldb=8)[1]["path"] == gr.GR_PATH_TILE
-    # any M above the small-M threshold takes the pipelined kernel (rows past M
-    # clamped); K % 32 != 0 or rows not 16-byte aligned: guarded kernel
+    # up to 64 rows of A and at most 256 column strips: the small-M stream
+    # (2 or 4 row blocks); more rows or wider C: the pipelined kernel (rows
+    # past M clamped); K % 32 != 0 or rows not 16-byte aligned: guarded kernel
     st, p = plan(17, 512, 512)
+    assert p["path"] == gr.GR_PATH_SMALL_M and (p["block_m"], p["grid"]) == (32, 8)
+    st, p = plan(64, 16384, 512)
+    assert p["path"] == gr.GR_PATH_SMALL_M and (p["block_m"], p["grid"]) == (64, 256)
+    st, p = plan(64, 16448, 512)
+    assert p["path"] == gr.GR_PATH_TILE and (p["block_m"], p["grid"]) == (128, 129)
+    st, p = plan(65, 512, 512)
     assert p["path"] == gr.GR_PATH_TILE and (p["block_m"], p["grid"]) == (128, 4)
     assert plan(512, 512, 48)[1]["path"] == gr.GR_PATH_TILE_EDGE
     assert plan(512, 500, 512)[1]["path"] == gr.GR_PATH_TILE_EDGE
@@ -321,7 +328,9 @@ def test_plan_empty_and_k_zero():
 
 def test_plan_small_m_threshold():
     assert plan(16, 4096, 4096)[1]["path"] == gr.GR_PATH_SMALL_M
-    assert plan(17, 4096, 4096)[1]["path"] == gr.GR_PATH_TILE
+    assert plan(17, 4096, 4096)[1]["path"] == gr.GR_PATH_SMALL_M   # two row blocks
+    assert plan(64, 4096, 4096)[1]["path"] == gr.GR_PATH_SMALL_M   # four row blocks
+    assert plan(65, 4096, 4096)[1]["path"] == gr.GR_PATH_TILE
     assert plan(1, 1, 1)[1]["path"] == gr.GR_PATH_TILE_EDGE  # B row pitch 1: not 8-byte aligned
 
 
@@ -332,7 +341,7 @@ def test_planner_invariants_on_random_problems():
     import numpy as np
     rng = np.random.default_rng(7)
     for _ in range(3000):
-        M = int(rng.choice([rng.integers(0, 17), rng.integers(17, 5000)]))
+        M = int(rng.choice([rng.integers(0, 17), rng.integers(17, 65), rng.integers(17, 5000)]))
         N = int(rng.integers(0, 30000))
         K = int(rng.choice([0, rng.integers(1, 9000), 32 * rng.integers(1, 300)]))
         lda = max(K, 1) + int(rng.choice([0, 0, rng.integers(1, 17)]))
@@ -358,7 +367,8 @@ def test_planner_invariants_on_random_problems():
             assert bm in (128, 256) and (bm == 128 or M >= 256), key
             assert p["grid"] == -(-M // bm) * -(-N // bm), key
         elif p["path"] == gr.GR_PATH_SMALL_M:
-            assert 1 <= M <= 16 and K > 0 and p["grid"] == -(-N // 64), key
+            assert 1 <= M <= 64 and K > 0 and p["grid"] == -(-N // 64), key
+            assert M <= 16 or -(-N // 64) <= 256, key  # wider C with more rows: the tile kernel
         else:
             assert p["path"] == gr.GR_PATH_TILE_EDGE, key
             assert not (aligned and K % 32 == 0 and K > 0), key
@@ -424,7 +434,7 @@ def test_bf16_argument_checks_need_no_gpu():
     for path in (gr.GR_PATH_TILE_PACKED, gr.GR_PATH_SMALL_M_SPLIT, gr.GR_PATH_TILE_SPLIT, 99):
         assert g(8, 256, 64, BASE_A, 64, BASE_B, 256, BASE_C, 256, None, path) == gr.GR_ERR_INVALID_PATH
     assert g(300, 256, 48, BASE_A, 48, BASE_B, 256, BASE_C, 256, None, gr.GR_PATH_TILE) == gr.GR_ERR_INVALID_PATH
-    assert g(64, 256, 64, BASE_A, 64, BASE_B, 256, BASE_C, 256, None, gr.GR_PATH_SMALL_M) == gr.GR_ERR_INVALID_PATH
+    assert g(65, 256, 64, BASE_A, 64, BASE_B, 256, BASE_C, 256, None, gr.GR_PATH_SMALL_M) == gr.GR_ERR_INVALID_PATH
 
 
 def test_bias_act_argument_checks_need_no_gpu():
@@ -505,8 +515,8 @@ def test_calls_validate_before_touching_the_device():
                                    gr.GR_PATH_TILE) == gr.GR_ERR_INVALID_PATH
     assert gr.gemm_relu_f16_forced(300, 250, 64, BASE_A, 64, BASE_B, 250, BASE_C, 256, None,
                                    gr.GR_PATH_TILE) == gr.GR_ERR_INVALID_PATH
-    # small-M forced with too many rows
-    assert gr.gemm_relu_f16_forced(64, 256, 64, BASE_A, 64, BASE_B, 256, BASE_C, 256, None,
+    # small-M forced with too many rows (the stream takes at most 64)
+    assert gr.gemm_relu_f16_forced(65, 256, 64, BASE_A, 64, BASE_B, 256, BASE_C, 256, None,
                                    gr.GR_PATH_SMALL_M) == gr.GR_ERR_INVALID_PATH
     # empty problems succeed without a launch
     assert gr.gemm_relu_f16(0, 8, 8, 0, 8, BASE_B, 8, 0, 8) == gr.GR_OK

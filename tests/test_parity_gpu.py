@@ -252,7 +252,7 @@ def test_tile_pipeline_every_strip_count(M, N, K):
 # ---- the pipelined kernels on partial tiles (16-byte rows, K % 32 == 0) -------
 
 PARTIAL_TILE_CASES = [
-    (17, 264, 64, 72, 264, 265),           # 17 rows: rows past M clamped, padded A, odd ldc
+    (65, 264, 64, 72, 264, 265),           # 65 rows: rows past M clamped, padded A, odd ldc
     (100, 304, 96, 96, 304, 300 + 4),      # fewer rows than one tile, K % 64 == 32
     (128, 136, 32, 32, 136, 136),          # 128 x 128 tiles: one tile row, one partial tile column
     (257, 264, 64, 64, 264, 264),          # one row past a tile; N a multiple of 8
@@ -587,6 +587,35 @@ def test_random_problems_against_oracle(case):
         ref = oracle.gemm_relu_full(A, B, M=M, N=N, K=K, lda=lda, ldb=ldb)
         assert_parity(Cw[:, :N], ref, "fuzz%d %s" % (i, plan["path_name"]))
     assert np.all(Cw[:, N:] == SENTINEL)
+
+
+# ---- the small-M stream with 2 or 4 blocks of 16 rows ----------------------------
+
+MIDM_CASES = [
+    # M, N, K, lda, ldb, ldc
+    (17, 512, 512, 512, 512, 512),        # two row blocks, whole strips
+    (32, 4096, 1024, 1024, 4096, 4096),
+    (33, 2000, 1000, 1000, 2000, 2001),   # four row blocks, guarded: N % 64 != 0, K % 32 != 0
+    (48, 1000, 256, 264, 1008, 1003),     # padded pitches
+    (64, 16384, 2048, 2048, 16384, 16384),  # 256 strips, four row blocks
+    (24, 300, 130, 136, 300, 301),
+]
+
+
+@pytest.mark.parametrize("M,N,K,lda,ldb,ldc", MIDM_CASES)
+def test_small_m_row_blocks(M, N, K, lda, ldb, ldc):
+    """17-64 rows of A on the small-M stream (each B operand feeds 2 or 4
+    row blocks): full comparison with the oracle, poisoned padding, C
+    canaries, and agreement with the tile kernels within the tolerance."""
+    st, plan = gr.gemm_relu_f16_plan(M, N, K, 0x100000, lda, 0x200000000000, ldb, 0x400000000000, ldc)
+    assert plan["path"] == gr.GR_PATH_SMALL_M and plan["block_m"] == (32 if M <= 32 else 64), plan
+    A, B = synth.random_operands(M, N, K, seed=M * 3 + N + K, lda=lda, ldb=ldb, b_scale=K ** -0.5)
+    Cflat = run_full(A, B, M, N, K, lda, ldb, ldc, c_rows=M + 1)
+    C = Cflat[:M * ldc].reshape(M, ldc)
+    assert_parity(C[:, :N], oracle.gemm_relu_full(A, B, M=M, N=N, K=K, lda=lda, ldb=ldb), "small-M rows")
+    assert np.all(C[:, N:] == SENTINEL) and np.all(Cflat[M * ldc:] == SENTINEL)
+    C2 = run_full(A, B, M, N, K, lda, ldb, ldc, c_rows=M + 1, path=gr.GR_PATH_TILE_EDGE)
+    assert_parity(C[:, :N], C2[:M * ldc].reshape(M, ldc)[:, :N], "small-M rows vs guarded tile")
 
 
 # ---- more 256 x 256 tiles than CUs ---------------------------------------------

@@ -112,7 +112,7 @@ KERNEL_CASES = [
     # M, N, K, lda, ldb, ldc, expected path, what it exercises
     (512, 768, 256, 256, 768, 768, gr.GR_PATH_TILE, "128x128 whole"),
     (300, 250, 96, 104, 256, 251, gr.GR_PATH_TILE, "128x128 partial, rows clamped"),
-    (17, 264, 64, 72, 264, 265, gr.GR_PATH_TILE, "128x128, one row of tiles"),
+    (65, 264, 64, 72, 264, 265, gr.GR_PATH_TILE, "128x128, one row of tiles"),
     (4096, 2304, 256, 256, 2304, 2304, gr.GR_PATH_TILE, "256x256 64-deep whole"),
     (2400, 4000, 128, 128, 4008, 4001, gr.GR_PATH_TILE, "256x256 64-deep partial"),
     (4096, 2304, 160, 160, 2304, 2304, gr.GR_PATH_TILE, "256x256 32-deep whole"),
@@ -124,6 +124,8 @@ KERNEL_CASES = [
     (16, 1000, 1000, 1000, 1000, 1000, gr.GR_PATH_SMALL_M, "small-M guarded"),
     (5, 128, 8200, 8200, 128, 129, gr.GR_PATH_SMALL_M, "small-M long K tail"),
     (1, 100, 96, 96, 104, 100, gr.GR_PATH_SMALL_M, "small-M one row"),
+    (40, 1000, 512, 512, 1000, 1001, gr.GR_PATH_SMALL_M, "small-M four row blocks"),
+    (20, 4096, 300, 304, 4096, 4096, gr.GR_PATH_SMALL_M, "small-M two row blocks, K tail"),
 ]
 
 

@@ -30,6 +30,7 @@ FAMILY_CASES = [
     (2400, 4000, 96, 96, 4000, 4001, gr.GR_PATH_TILE, "tile 256 32-deep partial"),
     (300, 270, 100, 109, 277, 273, gr.GR_PATH_TILE_EDGE, "guarded"),
     (13, 1000, 1000, 1000, 1000, 1001, gr.GR_PATH_SMALL_M, "small-M guarded"),
+    (45, 700, 512, 512, 704, 701, gr.GR_PATH_SMALL_M, "small-M four row blocks"),
 ]
 
 EXTRA_CASES = [
