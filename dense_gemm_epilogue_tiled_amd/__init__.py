@@ -128,6 +128,12 @@ def lib() -> ctypes.CDLL:
             l.gemm_relu_bf16.restype = i32
             l.gemm_relu_bf16_forced.argtypes = [i64, i64, i64, p, i64, p, i64, p, i64, p, i32]
             l.gemm_relu_bf16_forced.restype = i32
+            l.gemm_relu_bf16_ws.argtypes = [i64, i64, i64, p, i64, p, i64, p, i64, p, i64, p]
+            l.gemm_relu_bf16_ws.restype = i32
+            l.gemm_relu_bf16_forced_ws.argtypes = [i64, i64, i64, p, i64, p, i64, p, i64, p, i64, p, i32]
+            l.gemm_relu_bf16_forced_ws.restype = i32
+            l.gemm_bias_act_ws.argtypes = [i64, i64, i64, p, i64, p, i64, p, i32, p, i64, i32, p, i64, p, i32]
+            l.gemm_bias_act_ws.restype = i32
             for nm in ("gemm_bias_act_f16", "gemm_bias_act_bf16"):
                 getattr(l, nm).argtypes = [i64, i64, i64, p, i64, p, i64, p, i32, p, i64, p]
                 getattr(l, nm).restype = i32
@@ -239,6 +245,24 @@ def gemm_bias_act_bf16(M, N, K, A, lda, B, ldb, bias, act, C, ldc, stream=None) 
     return lib().gemm_bias_act_bf16(M, N, K, _ptr(A), lda, _ptr(B), ldb, _ptr(bias), act, _ptr(C), ldc, _ptr(stream))
 
 
+def gemm_relu_bf16_ws(M, N, K, A, lda, B, ldb, C, ldc, workspace, workspace_bytes, stream=None) -> int:
+    return lib().gemm_relu_bf16_ws(M, N, K, _ptr(A), lda, _ptr(B), ldb, _ptr(C), ldc, _ptr(workspace),
+                                   workspace_bytes, _ptr(stream))
+
+
+def gemm_relu_bf16_forced_ws(M, N, K, A, lda, B, ldb, C, ldc, workspace, workspace_bytes, stream=None,
+                             path=GR_PATH_TILE_EDGE) -> int:
+    return lib().gemm_relu_bf16_forced_ws(M, N, K, _ptr(A), lda, _ptr(B), ldb, _ptr(C), ldc, _ptr(workspace),
+                                          workspace_bytes, _ptr(stream), path)
+
+
+def gemm_bias_act_ws(M, N, K, A, lda, B, ldb, bias, act, C, ldc, fmt, workspace, workspace_bytes, stream=None,
+                     path=-1) -> int:
+    """act(A.B + bias) in fmt (GR_FMT_F16 / GR_FMT_BF16) with a caller workspace; path -1 = planner."""
+    return lib().gemm_bias_act_ws(M, N, K, _ptr(A), lda, _ptr(B), ldb, _ptr(bias), act, _ptr(C), ldc, fmt,
+                                  _ptr(workspace), workspace_bytes, _ptr(stream), path)
+
+
 def gemm_bias_act_f16_forced(M, N, K, A, lda, B, ldb, bias, act, C, ldc, stream=None, path=GR_PATH_TILE_EDGE) -> int:
     return lib().gemm_bias_act_f16_forced(M, N, K, _ptr(A), lda, _ptr(B), ldb, _ptr(bias), act, _ptr(C), ldc,
                                           _ptr(stream), path)
@@ -318,10 +342,10 @@ def gemm_relu(a, b, out=None, stream=None, path=None, workspace="auto"):
     tensors on the GPU.
 
     Row pitches are taken from the tensors' strides (unit column stride
-    required). ``workspace`` (fp16 only): "auto" allocates (from torch's
-    caching allocator) the scratch the library asks for, if any; a uint8
-    device tensor is used as given; None means no workspace. Raises
-    GemmReluError on a non-zero status.
+    required). ``workspace``: "auto" allocates (from torch's caching
+    allocator) the scratch the library asks for, if any; a uint8 device
+    tensor is used as given; None means no workspace. Raises GemmReluError on
+    a non-zero status.
     """
     import torch
     if a.dtype not in (torch.float16, torch.bfloat16) or b.dtype != a.dtype:
@@ -341,26 +365,17 @@ def gemm_relu(a, b, out=None, stream=None, path=None, workspace="auto"):
     ldb = max(b.stride(0), 1) if K > 1 else max(N, 1)
     ldc = max(out.stride(0), 1) if M > 1 else max(N, 1)
     args = (M, N, K, a.data_ptr(), lda, b.data_ptr(), ldb, out.data_ptr(), ldc)
-    if a.dtype == torch.bfloat16:
-        if workspace is not None and not (isinstance(workspace, str) and workspace == "auto"):
-            raise ValueError("the bfloat16 paths take no workspace")
-        h = _stream_handle(stream)
-        st = gemm_relu_bf16(*args, h) if path is None else gemm_relu_bf16_forced(*args, h, path)
-        if st != GR_OK:
-            raise GemmReluError(st, "gemm_relu_bf16")
-        return out
-    if isinstance(workspace, str):
-        if workspace != "auto":
-            raise ValueError("workspace must be 'auto', None or a uint8 tensor")
-        st, size = gemm_relu_f16_workspace_size(*args)
-        if st != GR_OK:
-            raise GemmReluError(st, "gemm_relu_f16_workspace_size")
-        workspace = torch.empty(size, dtype=torch.uint8, device=a.device) if size else None
-        if workspace is not None and stream is not None and not isinstance(stream, int):
-            # the scratch block must not be handed out again before this stream is done with it
-            workspace.record_stream(stream)
+    workspace = _workspace_for(torch, args, workspace, a.device, stream)
     ws_ptr, ws_bytes = (workspace.data_ptr(), workspace.numel()) if workspace is not None else (0, 0)
     h = _stream_handle(stream)
+    if a.dtype == torch.bfloat16:
+        if path is None:
+            st = gemm_relu_bf16_ws(*args, ws_ptr, ws_bytes, h)
+        else:
+            st = gemm_relu_bf16_forced_ws(*args, ws_ptr, ws_bytes, h, path)
+        if st != GR_OK:
+            raise GemmReluError(st, "gemm_relu_bf16_ws")
+        return out
     if path is None:
         st = gemm_relu_f16_ws(*args, ws_ptr, ws_bytes, h)
     else:
@@ -370,10 +385,29 @@ def gemm_relu(a, b, out=None, stream=None, path=None, workspace="auto"):
     return out
 
 
-def gemm_bias_act(a, b, bias=None, act="gelu", out=None, stream=None, path=None):
+def _workspace_for(torch, args, workspace, device, stream):
+    """The workspace a tensor helper passes: "auto" allocates (from torch's
+    caching allocator) what the library asks for, if anything; a uint8
+    device tensor is used as given; None means none."""
+    if not isinstance(workspace, str):
+        return workspace
+    if workspace != "auto":
+        raise ValueError("workspace must be 'auto', None or a uint8 tensor")
+    st, size = gemm_relu_f16_workspace_size(*args)  # the sizes do not depend on the element format
+    if st != GR_OK:
+        raise GemmReluError(st, "gemm_relu_f16_workspace_size")
+    ws = torch.empty(size, dtype=torch.uint8, device=device) if size else None
+    if ws is not None and stream is not None and not isinstance(stream, int):
+        # the scratch block must not be handed out again before this stream is done with it
+        ws.record_stream(stream)
+    return ws
+
+
+def gemm_bias_act(a, b, bias=None, act="gelu", out=None, stream=None, path=None, workspace="auto"):
     """Tensor convenience: ``out = act(a @ b + bias)`` for 2-D fp16 or bfloat16
     tensors on the GPU; ``bias`` is None or a 1-D tensor of N values of the
-    same dtype, ``act`` a key of ACT_CODES or a GR_ACT_* code."""
+    same dtype, ``act`` a key of ACT_CODES or a GR_ACT_* code; ``workspace``
+    as for gemm_relu."""
     import torch
     if a.dtype not in (torch.float16, torch.bfloat16) or b.dtype != a.dtype:
         raise TypeError("a and b must both be float16 or both bfloat16")
@@ -397,14 +431,14 @@ def gemm_bias_act(a, b, bias=None, act="gelu", out=None, stream=None, path=None)
     ldc = max(out.stride(0), 1) if M > 1 else max(N, 1)
     bptr = bias.data_ptr() if bias is not None and bias.numel() else None
     h = _stream_handle(stream)
-    args = (M, N, K, a.data_ptr(), lda, b.data_ptr(), ldb, bptr, code, out.data_ptr(), ldc, h)
-    bf = a.dtype == torch.bfloat16
-    if path is None:
-        st = (gemm_bias_act_bf16 if bf else gemm_bias_act_f16)(*args)
-    else:
-        st = (gemm_bias_act_bf16_forced if bf else gemm_bias_act_f16_forced)(*args, path)
+    ws = _workspace_for(torch, (M, N, K, a.data_ptr(), lda, b.data_ptr(), ldb, out.data_ptr(), ldc), workspace,
+                        a.device, stream)
+    ws_ptr, ws_bytes = (ws.data_ptr(), ws.numel()) if ws is not None else (0, 0)
+    fmt = GR_FMT_BF16 if a.dtype == torch.bfloat16 else GR_FMT_F16
+    st = gemm_bias_act_ws(M, N, K, a.data_ptr(), lda, b.data_ptr(), ldb, bptr, code, out.data_ptr(), ldc, fmt,
+                          ws_ptr, ws_bytes, h, -1 if path is None else path)
     if st != GR_OK:
-        raise GemmReluError(st, "gemm_bias_act_bf16" if bf else "gemm_bias_act_f16")
+        raise GemmReluError(st, "gemm_bias_act_ws")
     return out
 
 

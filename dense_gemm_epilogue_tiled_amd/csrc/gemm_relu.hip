@@ -409,10 +409,6 @@ template <typename E>
 int run(const gr_plan_t& p, int64_t M, int64_t N, int64_t K, const uint16_t* A, int64_t lda, const uint16_t* B,
         int64_t ldb, uint16_t* C, int64_t ldc, const Pack& pk, const SmallMSplit& sp, const TileSplit& ts,
         uint8_t* ws, const gr::EpiArgs& ep, hipStream_t stream) {
-    if constexpr (!E::kIsF16 || E::kGeneral) {
-        if (p.path == GR_PATH_SMALL_M_SPLIT || p.path == GR_PATH_TILE_SPLIT || p.path == GR_PATH_TILE_PACKED)
-            return GR_ERR_INVALID_PATH;
-    }
     switch (p.path) {
         case GR_PATH_NONE: return GR_OK;
         case GR_PATH_SMALL_M_SPLIT: {
@@ -420,15 +416,15 @@ int run(const gr_plan_t& p, int64_t M, int64_t N, int64_t K, const uint16_t* A, 
             float* part = reinterpret_cast<float*>(ws);
             const bool whole = N % SPLIT_NB == 0 && K % KSTEP == 0;
             const uint32_t nb = (uint32_t)sp.n_blocks;
-            int st = whole ? launch(gemm_relu_smallm_split_kernel<false>, p.grid, SPLIT_THREADS, stream, A, B, part,
-                                    M, N, K, lda, ldb, sp.k_per_split, nb)
-                           : launch(gemm_relu_smallm_split_kernel<true>, p.grid, SPLIT_THREADS, stream, A, B, part, M,
-                                    N, K, lda, ldb, sp.k_per_split, nb);
+            int st = whole ? launch(gemm_relu_smallm_split_kernel<false, E>, p.grid, SPLIT_THREADS, stream, A, B,
+                                    part, M, N, K, lda, ldb, sp.k_per_split, nb)
+                           : launch(gemm_relu_smallm_split_kernel<true, E>, p.grid, SPLIT_THREADS, stream, A, B, part,
+                                    M, N, K, lda, ldb, sp.k_per_split, nb);
             if (st != GR_OK) return st;
             int64_t rblocks = (M * N + 255) / 256;
             if (rblocks > 2048) rblocks = 2048;
-            return launch(gemm_relu_smallm_reduce_kernel, rblocks, 256, stream, (const float*)part, C, M, N, ldc,
-                          (int)sp.splits);
+            return launch(gemm_relu_smallm_reduce_kernel<E>, rblocks, 256, stream, (const float*)part, C, M, N, ldc,
+                          (int)sp.splits, ep);
         }
         case GR_PATH_TILE_SPLIT: {
             using namespace gr::tile128;
@@ -439,15 +435,15 @@ int run(const gr_plan_t& p, int64_t M, int64_t N, int64_t K, const uint16_t* A, 
             const uint32_t gm = (uint32_t)p.group_m;
             const int vc = p.vec_c;
             const int64_t kps = ts.k_per_split;
-            int st = whole ? launch(gemm_relu_tile128_kernel<false, true>, p.grid, THREADS, stream, A, B, C, M, N, K,
-                                    lda, ldb, ldc, tiles_m, tiles_n, gm, vc, part, kps, ep)
-                           : launch(gemm_relu_tile128_kernel<true, true>, p.grid, THREADS, stream, A, B, C, M, N, K,
-                                    lda, ldb, ldc, tiles_m, tiles_n, gm, vc, part, kps, ep);
+            int st = whole ? launch(gemm_relu_tile128_kernel<false, true, false, E>, p.grid, THREADS, stream, A, B,
+                                    C, M, N, K, lda, ldb, ldc, tiles_m, tiles_n, gm, vc, part, kps, ep)
+                           : launch(gemm_relu_tile128_kernel<true, true, false, E>, p.grid, THREADS, stream, A, B, C,
+                                    M, N, K, lda, ldb, ldc, tiles_m, tiles_n, gm, vc, part, kps, ep);
             if (st != GR_OK) return st;
             int64_t rblocks = (M * N + 255) / 256;
             if (rblocks > 2048) rblocks = 2048;
-            return launch(gr::smallm::gemm_relu_smallm_reduce_kernel, rblocks, 256, stream, (const float*)part, C, M,
-                          N, ldc, (int)ts.splits);
+            return launch(gr::smallm::gemm_relu_smallm_reduce_kernel<E>, rblocks, 256, stream, (const float*)part, C,
+                          M, N, ldc, (int)ts.splits, ep);
         }
         case GR_PATH_TILE_PACKED: {
             const int st = launch_pack(pk, M, N, K, A, lda, B, ldb, ws, stream);
@@ -583,44 +579,47 @@ int entry(int64_t M, int64_t N, int64_t K, const uint16_t* A, int64_t lda, const
                             static_cast<hipStream_t>(stream));
 }
 
-// bfloat16 operands and output: the planner's paths without a workspace.
+// bfloat16 operands and output; the same paths as fp16 (a workspace, when
+// given, enables the packed and split paths).
 int entry_bf16(int64_t M, int64_t N, int64_t K, const uint16_t* A, int64_t lda, const uint16_t* B, int64_t ldb,
-               uint16_t* C, int64_t ldc, void* stream, int forced) {
+               uint16_t* C, int64_t ldc, void* ws, int64_t ws_bytes, void* stream, int forced) {
     Pack pk;
     SmallMSplit sp;
     TileSplit ts;
     gr_plan_t p;
-    int st = plan_call(M, N, K, (uintptr_t)A, lda, (uintptr_t)B, ldb, (uintptr_t)C, ldc, 0, 0, true, forced, &pk, &sp,
-                       &ts, &p);
+    int st = plan_call(M, N, K, (uintptr_t)A, lda, (uintptr_t)B, ldb, (uintptr_t)C, ldc, (uintptr_t)ws, ws_bytes,
+                       true, forced, &pk, &sp, &ts, &p);
     if (st != GR_OK) return st;
     if (p.path == GR_PATH_NONE) return GR_OK;
     st = check_device();
     if (st != GR_OK) return st;
-    return run<gr::ElemBF16>(p, M, N, K, A, lda, B, ldb, C, ldc, pk, sp, ts, nullptr, kReluOnly,
+    return run<gr::ElemBF16>(p, M, N, K, A, lda, B, ldb, C, ldc, pk, sp, ts, static_cast<uint8_t*>(ws), kReluOnly,
                              static_cast<hipStream_t>(stream));
 }
 
-// Bias + activation epilogue (Base: element type), on the planner's paths
-// without a workspace.  The bias (N values, or none) must not overlap C.
+// Bias + activation epilogue (Base: element type), on the planner's paths.
+// The bias (N values, or none) must not overlap C or the workspace.
 template <typename Base>
 int entry_epi(int64_t M, int64_t N, int64_t K, const uint16_t* A, int64_t lda, const uint16_t* B, int64_t ldb,
-              const uint16_t* bias, int act, uint16_t* C, int64_t ldc, void* stream, int forced) {
+              const uint16_t* bias, int act, uint16_t* C, int64_t ldc, void* ws, int64_t ws_bytes, void* stream,
+              int forced) {
     if (act < 0 || act >= gr::kActCount) return GR_ERR_INVALID_ARG;
     Pack pk;
     SmallMSplit sp;
     TileSplit ts;
     gr_plan_t p;
-    int st = plan_call(M, N, K, (uintptr_t)A, lda, (uintptr_t)B, ldb, (uintptr_t)C, ldc, 0, 0, true, forced, &pk, &sp,
-                       &ts, &p);
+    int st = plan_call(M, N, K, (uintptr_t)A, lda, (uintptr_t)B, ldb, (uintptr_t)C, ldc, (uintptr_t)ws, ws_bytes,
+                       true, forced, &pk, &sp, &ts, &p);
     if (st != GR_OK) return st;
     if (bias != nullptr && M > 0 && N > 0 &&
-        overlaps((uintptr_t)C, span_bytes(M, N, ldc), (uintptr_t)bias, 2 * N))
+        (overlaps((uintptr_t)C, span_bytes(M, N, ldc), (uintptr_t)bias, 2 * N) ||
+         overlaps((uintptr_t)ws, ws_bytes, (uintptr_t)bias, 2 * N)))
         return GR_ERR_ALIAS;
     if (p.path == GR_PATH_NONE) return GR_OK;
     st = check_device();
     if (st != GR_OK) return st;
-    return run<gr::Epi<Base>>(p, M, N, K, A, lda, B, ldb, C, ldc, pk, sp, ts, nullptr, gr::EpiArgs{bias, act, 1.0f},
-                              static_cast<hipStream_t>(stream));
+    return run<gr::Epi<Base>>(p, M, N, K, A, lda, B, ldb, C, ldc, pk, sp, ts, static_cast<uint8_t*>(ws),
+                              gr::EpiArgs{bias, act, 1.0f}, static_cast<hipStream_t>(stream));
 }
 
 bool known_path(int path) {
@@ -992,37 +991,61 @@ extern "C" {
 
 int gemm_relu_bf16(int64_t M, int64_t N, int64_t K, const uint16_t* A, int64_t lda, const uint16_t* B, int64_t ldb,
                    uint16_t* C, int64_t ldc, void* stream) {
-    return entry_bf16(M, N, K, A, lda, B, ldb, C, ldc, stream, -1);
+    return entry_bf16(M, N, K, A, lda, B, ldb, C, ldc, nullptr, 0, stream, -1);
 }
 
 int gemm_relu_bf16_forced(int64_t M, int64_t N, int64_t K, const uint16_t* A, int64_t lda, const uint16_t* B,
                           int64_t ldb, uint16_t* C, int64_t ldc, void* stream, int path) {
     if (path != GR_PATH_TILE && path != GR_PATH_TILE_EDGE && path != GR_PATH_SMALL_M) return GR_ERR_INVALID_PATH;
-    return entry_bf16(M, N, K, A, lda, B, ldb, C, ldc, stream, path);
+    return entry_bf16(M, N, K, A, lda, B, ldb, C, ldc, nullptr, 0, stream, path);
+}
+
+int gemm_relu_bf16_ws(int64_t M, int64_t N, int64_t K, const uint16_t* A, int64_t lda, const uint16_t* B, int64_t ldb,
+                      uint16_t* C, int64_t ldc, void* workspace, int64_t workspace_bytes, void* stream) {
+    return entry_bf16(M, N, K, A, lda, B, ldb, C, ldc, workspace, workspace_bytes, stream, -1);
+}
+
+int gemm_relu_bf16_forced_ws(int64_t M, int64_t N, int64_t K, const uint16_t* A, int64_t lda, const uint16_t* B,
+                             int64_t ldb, uint16_t* C, int64_t ldc, void* workspace, int64_t workspace_bytes,
+                             void* stream, int path) {
+    if (!known_path(path)) return GR_ERR_INVALID_PATH;
+    return entry_bf16(M, N, K, A, lda, B, ldb, C, ldc, workspace, workspace_bytes, stream, path);
 }
 
 int gemm_bias_act_f16(int64_t M, int64_t N, int64_t K, const uint16_t* A, int64_t lda, const uint16_t* B,
                       int64_t ldb, const uint16_t* bias, int act, uint16_t* C, int64_t ldc, void* stream) {
-    return entry_epi<gr::ElemF16>(M, N, K, A, lda, B, ldb, bias, act, C, ldc, stream, -1);
+    return entry_epi<gr::ElemF16>(M, N, K, A, lda, B, ldb, bias, act, C, ldc, nullptr, 0, stream, -1);
 }
 
 int gemm_bias_act_f16_forced(int64_t M, int64_t N, int64_t K, const uint16_t* A, int64_t lda, const uint16_t* B,
                              int64_t ldb, const uint16_t* bias, int act, uint16_t* C, int64_t ldc, void* stream,
                              int path) {
     if (path != GR_PATH_TILE && path != GR_PATH_TILE_EDGE && path != GR_PATH_SMALL_M) return GR_ERR_INVALID_PATH;
-    return entry_epi<gr::ElemF16>(M, N, K, A, lda, B, ldb, bias, act, C, ldc, stream, path);
+    return entry_epi<gr::ElemF16>(M, N, K, A, lda, B, ldb, bias, act, C, ldc, nullptr, 0, stream, path);
 }
 
 int gemm_bias_act_bf16(int64_t M, int64_t N, int64_t K, const uint16_t* A, int64_t lda, const uint16_t* B,
                        int64_t ldb, const uint16_t* bias, int act, uint16_t* C, int64_t ldc, void* stream) {
-    return entry_epi<gr::ElemBF16>(M, N, K, A, lda, B, ldb, bias, act, C, ldc, stream, -1);
+    return entry_epi<gr::ElemBF16>(M, N, K, A, lda, B, ldb, bias, act, C, ldc, nullptr, 0, stream, -1);
 }
 
 int gemm_bias_act_bf16_forced(int64_t M, int64_t N, int64_t K, const uint16_t* A, int64_t lda, const uint16_t* B,
                               int64_t ldb, const uint16_t* bias, int act, uint16_t* C, int64_t ldc, void* stream,
                               int path) {
     if (path != GR_PATH_TILE && path != GR_PATH_TILE_EDGE && path != GR_PATH_SMALL_M) return GR_ERR_INVALID_PATH;
-    return entry_epi<gr::ElemBF16>(M, N, K, A, lda, B, ldb, bias, act, C, ldc, stream, path);
+    return entry_epi<gr::ElemBF16>(M, N, K, A, lda, B, ldb, bias, act, C, ldc, nullptr, 0, stream, path);
+}
+
+int gemm_bias_act_ws(int64_t M, int64_t N, int64_t K, const uint16_t* A, int64_t lda, const uint16_t* B, int64_t ldb,
+                     const uint16_t* bias, int act, uint16_t* C, int64_t ldc, int fmt, void* workspace,
+                     int64_t workspace_bytes, void* stream, int path) {
+    if (path != -1 && !known_path(path)) return GR_ERR_INVALID_PATH;
+    if (fmt == GR_FMT_BF16)
+        return entry_epi<gr::ElemBF16>(M, N, K, A, lda, B, ldb, bias, act, C, ldc, workspace, workspace_bytes, stream,
+                                       path);
+    if (fmt != GR_FMT_F16) return GR_ERR_INVALID_ARG;
+    return entry_epi<gr::ElemF16>(M, N, K, A, lda, B, ldb, bias, act, C, ldc, workspace, workspace_bytes, stream,
+                                  path);
 }
 
 int gemm_relu_f16_bt(int64_t M, int64_t N, int64_t K, const uint16_t* A, int64_t lda, const uint16_t* Bt,

@@ -242,7 +242,8 @@ __device__ __forceinline__ u32x4 load_b8(const uint16_t* B, int64_t ldb, int64_t
     }
 }
 
-template <bool GUARD>
+// E: element type of A and B (only its MFMA is used here; pass 2 rounds).
+template <bool GUARD, typename E = ElemF16>
 __global__ __launch_bounds__(SPLIT_THREADS, 1) void gemm_relu_smallm_split_kernel(
     const uint16_t* __restrict__ A, const uint16_t* __restrict__ B, float* __restrict__ part, int64_t M, int64_t N,
     int64_t K, int64_t lda, int64_t ldb, int64_t k_per_split, uint32_t n_blocks) {
@@ -293,7 +294,7 @@ __global__ __launch_bounds__(SPLIT_THREADS, 1) void gemm_relu_smallm_split_kerne
                 u32x4 o;
 #pragma unroll
                 for (int d = 0; d < 4; ++d) o[d] = pair_halves(rb[u][2 * d][j >> 1], rb[u][2 * d + 1][j >> 1], j & 1);
-                acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, o), a, acc[j], 0, 0, 0);
+                acc[j] = E::mfma16(__builtin_bit_cast(f16x8, o), a, acc[j]);
             }
         }
     };
@@ -329,16 +330,19 @@ __global__ __launch_bounds__(SPLIT_THREADS, 1) void gemm_relu_smallm_split_kerne
     }
 }
 
-// Pass 2: C[m][n] = ReLU(sum over s of part[s][m][n]), rounded to fp16.
+// Pass 2: C[m][n] = epilogue(sum over s of part[s][m][n]) -- the fused ReLU
+// and rounding, or (E = Epi<...>) scale, bias, activation and rounding.
+template <typename E = ElemF16>
 __global__ __launch_bounds__(256) void gemm_relu_smallm_reduce_kernel(const float* __restrict__ part,
                                                                       uint16_t* __restrict__ C, int64_t M,
-                                                                      int64_t N, int64_t ldc, int splits) {
+                                                                      int64_t N, int64_t ldc, int splits,
+                                                                      EpiArgs ep) {
     const int64_t total = M * N;
     for (int64_t o = (int64_t)blockIdx.x * 256 + threadIdx.x; o < total; o += (int64_t)gridDim.x * 256) {
         float sum = 0.0f;
         for (int s = 0; s < splits; ++s) sum += part[(int64_t)s * total + o];
         const int64_t m = o / N, n = o - m * N;
-        C[m * ldc + n] = relu_to_f16(sum);
+        C[m * ldc + n] = epi_value<E>(sum, n, N, ep);
     }
 }
 

@@ -64,6 +64,10 @@ extern "C" {
 #define GR_ERR_INVALID_PATH         -9 /* forced path unknown or not applicable            */
 #define GR_ERR_INVALID_ARG         -10 /* a NULL output struct or other bad argument        */
 
+/* ---- element formats (fmt / out_fmt arguments) ----------------------------- */
+#define GR_FMT_F16         0 /* IEEE binary16                                        */
+#define GR_FMT_BF16        1 /* bfloat16                                             */
+
 /* ---- execution paths chosen by the planner --------------------------------- */
 #define GR_PATH_NONE       0 /* empty output: nothing to launch                            */
 #define GR_PATH_TILE       1 /* pipelined MFMA tile kernel, direct-to-LDS copies: 16-B rows  */
@@ -289,7 +293,9 @@ int gemm_relu_f16_bt_forced(int64_t M, int64_t N, int64_t K,
  *                     128x128 tiles, as for fp16);
  *   GR_PATH_TILE_EDGE everything else (guarded register-staged kernel).
  * gemm_relu_f16_plan describes the plan these calls follow (the path does not
- * depend on the element format).  There is no workspace variant.
+ * depend on the element format).  gemm_relu_bf16_ws takes a caller workspace
+ * exactly like gemm_relu_f16_ws (same sizes: gemm_relu_f16_workspace_size)
+ * and then also uses the packed and split paths.
  */
 int gemm_relu_bf16(int64_t M, int64_t N, int64_t K,
                    const uint16_t* A, int64_t lda,
@@ -305,6 +311,23 @@ int gemm_relu_bf16_forced(int64_t M, int64_t N, int64_t K,
                           const uint16_t* B, int64_t ldb,
                           uint16_t* C, int64_t ldc,
                           void* stream, int path);
+
+/* gemm_relu_bf16 with a caller workspace (see gemm_relu_f16_ws). */
+int gemm_relu_bf16_ws(int64_t M, int64_t N, int64_t K,
+                      const uint16_t* A, int64_t lda,
+                      const uint16_t* B, int64_t ldb,
+                      uint16_t* C, int64_t ldc,
+                      void* workspace, int64_t workspace_bytes,
+                      void* stream);
+
+/* gemm_relu_bf16_ws on a given path (any GR_PATH_*; see
+   gemm_relu_f16_forced_ws).  Test hook. */
+int gemm_relu_bf16_forced_ws(int64_t M, int64_t N, int64_t K,
+                             const uint16_t* A, int64_t lda,
+                             const uint16_t* B, int64_t ldb,
+                             uint16_t* C, int64_t ldc,
+                             void* workspace, int64_t workspace_bytes,
+                             void* stream, int path);
 
 /*
  * ---- bias and other activations -------------------------------------------------
@@ -330,8 +353,8 @@ int gemm_relu_bf16_forced(int64_t M, int64_t N, int64_t K,
  * Every convention of gemm_relu_f16 holds; in addition GR_ERR_INVALID_ARG
  * for an unknown act and GR_ERR_ALIAS when the bias overlaps C.  K == 0
  * gives C = act(bias) (act(0) without a bias).  Paths: GR_PATH_SMALL_M,
- * GR_PATH_TILE, GR_PATH_TILE_EDGE, chosen as gemm_relu_f16_plan says; no
- * workspace variant.
+ * GR_PATH_TILE, GR_PATH_TILE_EDGE, chosen as gemm_relu_f16_plan says;
+ * gemm_bias_act_ws below adds the workspace paths.
  */
 #define GR_ACT_NONE        0
 #define GR_ACT_RELU        1
@@ -372,6 +395,19 @@ int gemm_bias_act_bf16_forced(int64_t M, int64_t N, int64_t K,
                               uint16_t* C, int64_t ldc,
                               void* stream, int path);
 
+/* gemm_bias_act_f16 / _bf16 with a caller workspace (see gemm_relu_f16_ws;
+   the sizes of gemm_relu_f16_workspace_size apply): fmt is GR_FMT_F16 or GR_FMT_BF16 (the
+   format of A, B, bias and C), path -1 lets the planner choose (then the
+   packed and split paths run bias and activation in their final pass), any
+   GR_PATH_* forces one.  The bias must not overlap C or the workspace. */
+int gemm_bias_act_ws(int64_t M, int64_t N, int64_t K,
+                     const uint16_t* A, int64_t lda,
+                     const uint16_t* B, int64_t ldb,
+                     const uint16_t* bias, int act,
+                     uint16_t* C, int64_t ldc, int fmt,
+                     void* workspace, int64_t workspace_bytes,
+                     void* stream, int path);
+
 /*
  * ---- fp8 operands ---------------------------------------------------------------
  * C := act(scale_a * scale_b * (A * Bt^T) + bias) with A (M x K) and Bt
@@ -397,9 +433,6 @@ int gemm_bias_act_bf16_forced(int64_t M, int64_t N, int64_t K,
  * outside the M x N window never written, GR_ERR_ALIAS when C overlaps A,
  * Bt or the bias, GR_ERR_INVALID_ARG for an unknown act or out_fmt).
  */
-#define GR_FMT_F16         0
-#define GR_FMT_BF16        1
-
 int gemm_fp8_bt(int64_t M, int64_t N, int64_t K,
                 const uint8_t* A, int64_t lda,
                 const uint8_t* Bt, int64_t ldbt,

@@ -457,6 +457,30 @@ def test_bias_act_argument_checks_need_no_gpu():
                  gr.GR_PATH_TILE) == gr.GR_ERR_INVALID_PATH
 
 
+def test_workspace_variants_argument_checks_need_no_gpu():
+    """gemm_relu_bf16_ws / _forced_ws and gemm_bias_act_ws: the shared checks,
+    then the format code, the activation code and a bias overlapping the
+    workspace, all before any HIP call."""
+    ws = BASE_C + (1 << 32)
+    bias = BASE_C + (1 << 30)
+    assert gr.gemm_relu_bf16_ws(-1, 8, 8, BASE_A, 8, BASE_B, 8, BASE_C, 8, ws, 1 << 20) == gr.GR_ERR_INVALID_DIM
+    assert gr.gemm_relu_bf16_ws(8, 8, 8, BASE_A, 8, BASE_B, 8, BASE_C, 8, ws, -1) == gr.GR_ERR_INVALID_ARG
+    assert gr.gemm_relu_bf16_ws(8, 8, 8, BASE_A, 8, BASE_B, 8, BASE_C, 8, BASE_A, 1 << 20) == gr.GR_ERR_ALIAS
+    assert gr.gemm_relu_bf16_forced_ws(8, 256, 64, BASE_A, 64, BASE_B, 256, BASE_C, 256, ws, 1 << 20, None,
+                                       99) == gr.GR_ERR_INVALID_PATH
+    # too small a workspace for the forced split
+    assert gr.gemm_relu_bf16_forced_ws(8, 4096, 8192, BASE_A, 8192, BASE_B, 4096, BASE_C, 4096, ws, 1024, None,
+                                       gr.GR_PATH_SMALL_M_SPLIT) == gr.GR_ERR_INVALID_PATH
+    f = gr.gemm_bias_act_ws
+    args = (8, 8, 8, BASE_A, 8, BASE_B, 8)
+    assert f(*args, bias, gr.GR_ACT_GELU, BASE_C, 8, 2, ws, 1 << 20) == gr.GR_ERR_INVALID_ARG      # format
+    assert f(*args, bias, gr.GR_ACT_GELU, BASE_C, 8, -1, ws, 1 << 20) == gr.GR_ERR_INVALID_ARG     # format
+    assert f(*args, bias, 7, BASE_C, 8, gr.GR_FMT_F16, ws, 1 << 20) == gr.GR_ERR_INVALID_ARG       # activation
+    assert f(*args, ws + 64, gr.GR_ACT_GELU, BASE_C, 8, gr.GR_FMT_BF16, ws, 1 << 20) == gr.GR_ERR_ALIAS
+    assert f(*args, bias, gr.GR_ACT_GELU, BASE_C, 8, gr.GR_FMT_BF16, ws, 1 << 20, None, 99) == gr.GR_ERR_INVALID_PATH
+    assert f(0, 8, 8, 0, 8, BASE_B, 8, bias, gr.GR_ACT_TANH, 0, 8, gr.GR_FMT_F16, None, 0) == gr.GR_OK
+
+
 def test_fp8_planner_and_checks_need_no_gpu():
     """gemm_fp8_bt: the pipelined kernel for K % 64 == 0 with 16-byte rows (any
     M, N), the guarded kernel otherwise; argument errors before any HIP call."""

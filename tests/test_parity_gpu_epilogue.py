@@ -191,3 +191,74 @@ def test_tensor_wrapper():
                       oracle.gemm_relu_full(A, B, fmt=fmt, bias=bias, act="gelu_tanh"), "wrapper " + fmt, fmt=fmt)
     with pytest.raises(ValueError):
         gr.gemm_bias_act(a, b, bb[:10], act="gelu")
+
+
+# ---- workspace paths: packed operands and the split passes ------------------------
+
+WS_CASES = [
+    # M, N, K, lda, ldb, ldc, path
+    (700, 500, 322, 322, 501, 500, gr.GR_PATH_TILE_PACKED),   # misaligned pitches, K % 32 != 0
+    (8, 4096, 8192, 8192, 4096, 4096, gr.GR_PATH_SMALL_M_SPLIT),
+    (13, 1000, 1000, 1000, 1000, 1001, gr.GR_PATH_SMALL_M_SPLIT),
+    (300, 520, 4096, 4104, 520, 521, gr.GR_PATH_TILE_SPLIT),
+    (128, 128, 1024, 1024, 128, 128, gr.GR_PATH_TILE_SPLIT),
+]
+
+
+def run_ws(A, B, bias, M, N, K, lda, ldb, ldc, act, fmt, path):
+    import torch as t
+    st, size = gr.gemm_relu_f16_workspace_size(M, N, K, 0x100000, lda, 0x200000000000, ldb, 0x400000000000, ldc)
+    assert st == gr.GR_OK
+    size = max(size, 4 << 20)  # the forced paths may need more than the planner's own choice
+    ws = t.full((size,), 0x5A, dtype=t.uint8, device="cuda")  # dirty: every path must overwrite what it reads
+    dA, dB = to_dev(A), to_dev(B)
+    db = to_dev(bias) if bias is not None else None
+    dC = full_dev((M * ldc + 8,), SENTINEL)
+    log("epi ws %s %s M=%d N=%d K=%d path=%s" % (fmt, act, M, N, K, path))
+    st = gr.gemm_bias_act_ws(M, N, K, dA.data_ptr(), lda, dB.data_ptr(), ldb,
+                             db.data_ptr() if db is not None else None, gr.ACT_CODES[act], dC.data_ptr(), ldc,
+                             gr.GR_FMT_BF16 if fmt == "bf16" else gr.GR_FMT_F16, ws.data_ptr(), ws.numel(),
+                             t.cuda.current_stream().cuda_stream, path)
+    t.cuda.synchronize()
+    assert st == gr.GR_OK, gr.gemm_relu_status_string(st)
+    return from_dev(dC)
+
+
+@pytest.mark.parametrize("fmt", ["f16", "bf16"])
+@pytest.mark.parametrize("act", ["relu", "gelu", "none"])
+@pytest.mark.parametrize("case", WS_CASES, ids=["packed", "smallm-split", "smallm-split-guarded", "tile-split",
+                                                "tile-split-one-tile"])
+def test_workspace_paths(case, act, fmt):
+    """Bias + activation (and bfloat16) through the packed copy and the two
+    split-K passes: the epilogue runs once, on the complete sum."""
+    M, N, K, lda, ldb, ldc, path = case
+    A, B, bias = operands(M, N, K, 11 + M, lda, ldb, fmt)
+    Cflat = run_ws(A, B, bias, M, N, K, lda, ldb, ldc, act, fmt, path)
+    C = Cflat[:M * ldc].reshape(M, ldc)
+    ref = oracle.gemm_relu_full(A, B, M=M, N=N, K=K, lda=lda, ldb=ldb, fmt=fmt, bias=bias, act=act)
+    assert_parity(C[:, :N], ref, "ws %s %s %s" % (fmt, act, path), fmt=fmt)
+    assert np.all(C[:, N:] == SENTINEL) and np.all(Cflat[M * ldc:] == SENTINEL)
+
+
+@pytest.mark.parametrize("fmt", ["f16", "bf16"])
+def test_planner_picks_workspace_paths(fmt):
+    """With a workspace the planner's own choice (path -1) matches the
+    forced runs above for the narrow small-M shape."""
+    M, N, K = 8, 4096, 8192
+    A, B, bias = operands(M, N, K, 3, K, N, fmt)
+    st, p = gr.gemm_relu_f16_plan_ws(M, N, K, 0x100000, K, 0x200000000000, N, 0x400000000000, N, 1 << 24)
+    assert p["path"] == gr.GR_PATH_SMALL_M_SPLIT
+    C = run_ws(A, B, bias, M, N, K, K, N, N, "silu", fmt, -1)[:M * N].reshape(M, N)
+    assert_parity(C, oracle.gemm_relu_full(A, B, fmt=fmt, bias=bias, act="silu"), "ws auto", fmt=fmt)
+
+
+def test_bf16_tensor_wrapper_workspace():
+    t = pytest.importorskip("torch")
+    M, N, K = 700, 500, 322
+    A, B, _ = operands(M, N, K, 17, K, N, "bf16")
+    a = to_dev(A).view(t.bfloat16).reshape(M, K)
+    b = to_dev(B).view(t.bfloat16).reshape(K, N)
+    c = gr.gemm_relu(a, b, path=gr.GR_PATH_TILE_PACKED, workspace=t.empty(1 << 22, dtype=t.uint8, device="cuda"))
+    t.cuda.synchronize()
+    assert_parity(c.view(t.int16).cpu().numpy().view(np.uint16), oracle.gemm_relu_full(A, B, fmt="bf16"),
+                  "bf16 packed wrapper", fmt="bf16")
