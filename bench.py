@@ -281,6 +281,8 @@ EXTRA_SHAPES = [
     ("fp8 e4m3, square", 4096, 4096, 4096, "fp8"),
     ("fp8 e4m3, square 8192", 8192, 8192, 8192, "fp8"),
     ("fp8 e4m3, MLP projection", 8192, 28672, 8192, "fp8"),
+    ("fp8 e4m3, mid-M", 128, 8192, 8192, "fp8"),
+    ("fp8 e4m3, long K, few tiles", 1024, 1024, 8192, "fp8"),
 ]
 
 
@@ -302,7 +304,12 @@ def extra_shapes(gr, torch, reps=30):
             A8 = torch.randn(M, K, generator=g, device="cuda").to(torch.float8_e4m3fn)
             Bt8 = torch.randn(N, K, generator=g, device="cuda").to(torch.float8_e4m3fn)
             sa, sb = 1.0 / 64, 1.0 / 64
-            runs["ours"] = lambda: gr.gemm_fp8(A8, Bt8, sa, sb, act="relu", out=C, stream=stream)
+            runs["ours"] = lambda: gr.gemm_fp8(A8, Bt8, sa, sb, act="relu", out=C, stream=stream, workspace=None)
+            st, size = gr.gemm_fp8_bt_workspace_size(M, N, K, A8.data_ptr(), K, Bt8.data_ptr(), K, C.data_ptr(), N)
+            if size:
+                ws8 = torch.empty(size, dtype=torch.uint8, device="cuda")
+                runs["ours_ws"] = lambda: gr.gemm_fp8(A8, Bt8, sa, sb, act="relu", out=C, stream=stream, workspace=ws8)
+                row["workspace_bytes"] = size
             ta = torch.tensor(sa, device="cuda")
             tb = torch.tensor(sb, device="cuda")
 

@@ -147,6 +147,14 @@ def lib() -> ctypes.CDLL:
             l.gemm_fp8_bt_plan.argtypes = [i64, i64, i64, p, i64, p, i64, p, i32, p, i64, i32,
                                            ctypes.POINTER(gr_plan_t)]
             l.gemm_fp8_bt_plan.restype = i32
+            l.gemm_fp8_bt_ws.argtypes = [i64, i64, i64, p, i64, p, i64, f32, f32, p, i32, p, i64, i32, p, i64, p, i32]
+            l.gemm_fp8_bt_ws.restype = i32
+            l.gemm_fp8_bt_workspace_size.argtypes = [i64, i64, i64, p, i64, p, i64, p, i64,
+                                                     ctypes.POINTER(ctypes.c_int64)]
+            l.gemm_fp8_bt_workspace_size.restype = i32
+            l.gemm_fp8_bt_plan_ws.argtypes = [i64, i64, i64, p, i64, p, i64, p, i32, p, i64, i32, i64,
+                                              ctypes.POINTER(gr_plan_t)]
+            l.gemm_fp8_bt_plan_ws.restype = i32
             l.gemm_relu_status_string.argtypes = [i32]
             l.gemm_relu_status_string.restype = ctypes.c_char_p
             l.gemm_relu_version.argtypes = []
@@ -290,6 +298,27 @@ def gemm_fp8_bt_plan(M, N, K, A, lda, Bt, ldbt, bias, act, C, ldc, out_fmt=GR_FM
     plan = gr_plan_t()
     st = lib().gemm_fp8_bt_plan(M, N, K, _ptr(A), lda, _ptr(Bt), ldbt, _ptr(bias), act, _ptr(C), ldc, out_fmt,
                                 ctypes.byref(plan))
+    return st, _plan_dict(plan)
+
+
+def gemm_fp8_bt_ws(M, N, K, A, lda, Bt, ldbt, scale_a, scale_b, bias, act, C, ldc, out_fmt, workspace,
+                   workspace_bytes, stream=None, path=-1) -> int:
+    """gemm_fp8_bt with a caller workspace (split-K for few tiles and a long K); path -1 = planner."""
+    return lib().gemm_fp8_bt_ws(M, N, K, _ptr(A), lda, _ptr(Bt), ldbt, float(scale_a), float(scale_b), _ptr(bias),
+                                act, _ptr(C), ldc, out_fmt, _ptr(workspace), workspace_bytes, _ptr(stream), path)
+
+
+def gemm_fp8_bt_workspace_size(M, N, K, A, lda, Bt, ldbt, C, ldc):
+    """(status, bytes): the workspace with which gemm_fp8_bt_ws splits K (0: never)."""
+    size = ctypes.c_int64(-1)
+    st = lib().gemm_fp8_bt_workspace_size(M, N, K, _ptr(A), lda, _ptr(Bt), ldbt, _ptr(C), ldc, ctypes.byref(size))
+    return st, size.value
+
+
+def gemm_fp8_bt_plan_ws(M, N, K, A, lda, Bt, ldbt, bias, act, C, ldc, out_fmt, workspace_bytes):
+    plan = gr_plan_t()
+    st = lib().gemm_fp8_bt_plan_ws(M, N, K, _ptr(A), lda, _ptr(Bt), ldbt, _ptr(bias), act, _ptr(C), ldc, out_fmt,
+                                   workspace_bytes, ctypes.byref(plan))
     return st, _plan_dict(plan)
 
 
@@ -443,11 +472,14 @@ def gemm_bias_act(a, b, bias=None, act="gelu", out=None, stream=None, path=None,
 
 
 def gemm_fp8(a, bt, scale_a=1.0, scale_b=1.0, bias=None, act="relu", out_dtype=None, out=None, stream=None,
-             path=None):
+             path=None, workspace="auto"):
     """Tensor convenience: ``out = act(scale_a * scale_b * a @ bt.T + bias)``
     with ``a`` (M x K) and ``bt`` (N x K) torch.float8_e4m3fn tensors on the
     GPU (unit column stride), fp16 or bfloat16 output (``out_dtype``, default
-    float16) and an optional 1-D bias of N values in the output dtype."""
+    float16) and an optional 1-D bias of N values in the output dtype.
+    ``workspace``: "auto" allocates what gemm_fp8_bt_workspace_size asks for
+    (split-K for few tiles and a long K), a uint8 device tensor is used as
+    given, None means none."""
     import torch
     if a.dtype != torch.float8_e4m3fn or bt.dtype != torch.float8_e4m3fn:
         raise TypeError("a and bt must be torch.float8_e4m3fn")
@@ -474,9 +506,18 @@ def gemm_fp8(a, bt, scale_a=1.0, scale_b=1.0, bias=None, act="relu", out_dtype=N
     ldc = max(out.stride(0), 1) if M > 1 else max(N, 1)
     code = ACT_CODES[act] if isinstance(act, str) else int(act)
     bptr = bias.data_ptr() if bias is not None and bias.numel() else None
-    args = (M, N, K, a.data_ptr(), lda, bt.data_ptr(), ldbt, scale_a, scale_b, bptr, code, out.data_ptr(), ldc, fmt,
-            _stream_handle(stream))
-    st = gemm_fp8_bt(*args) if path is None else gemm_fp8_bt_forced(*args, path)
+    if isinstance(workspace, str):
+        if workspace != "auto":
+            raise ValueError("workspace must be 'auto', None or a uint8 tensor")
+        st, size = gemm_fp8_bt_workspace_size(M, N, K, a.data_ptr(), lda, bt.data_ptr(), ldbt, out.data_ptr(), ldc)
+        if st != GR_OK:
+            raise GemmReluError(st, "gemm_fp8_bt_workspace_size")
+        workspace = torch.empty(size, dtype=torch.uint8, device=a.device) if size else None
+        if workspace is not None and stream is not None and not isinstance(stream, int):
+            workspace.record_stream(stream)
+    ws_ptr, ws_bytes = (workspace.data_ptr(), workspace.numel()) if workspace is not None else (0, 0)
+    st = gemm_fp8_bt_ws(M, N, K, a.data_ptr(), lda, bt.data_ptr(), ldbt, scale_a, scale_b, bptr, code,
+                        out.data_ptr(), ldc, fmt, ws_ptr, ws_bytes, _stream_handle(stream), -1 if path is None else path)
     if st != GR_OK:
-        raise GemmReluError(st, "gemm_fp8_bt")
+        raise GemmReluError(st, "gemm_fp8_bt_ws")
     return out

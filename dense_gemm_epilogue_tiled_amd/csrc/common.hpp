@@ -413,6 +413,36 @@ __device__ __forceinline__ void store_wave_tile_general(const f32x16 (&acc)[FM][
     }
 }
 
+// fp32 partial sums of a wave tile (split-K): block (i, j) of the
+// accumulators holds C^T, so lane l register r is row row0 + 32i + l%32,
+// column col0 + 32j + 8(r/4) + 4(l/32) + r%4.  part is the split's M x N
+// array (pitch N); only rows < M and columns < N are written (EDGE).
+template <bool EDGE, int FM, int FN>
+__device__ __forceinline__ void store_partials(const f32x16 (&acc)[FM][FN], float* __restrict__ part,
+                                               uint32_t lane, int64_t row0, int64_t col0, int64_t M, int64_t N) {
+#pragma unroll
+    for (int i = 0; i < FM; ++i) {
+        const int64_t m = row0 + 32 * i + (lane & 31u);
+        const bool row_ok = !EDGE || m < M;
+#pragma unroll
+        for (int j = 0; j < FN; ++j) {
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int64_t n = col0 + 32 * j + 8 * q + 4 * (lane >> 5);
+                float* dst = part + m * N + n;
+                if (!EDGE || (row_ok && n + 4 <= N && (N & 3) == 0)) {
+                    *reinterpret_cast<f32x4*>(dst) = f32x4{acc[i][j][4 * q], acc[i][j][4 * q + 1],
+                                                           acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
+                } else if (row_ok) {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        if (n + e < N) dst[e] = acc[i][j][4 * q + e];
+                }
+            }
+        }
+    }
+}
+
 template <bool EDGE, typename E = ElemF16, int FM, int FN>
 __device__ __forceinline__ void store_wave_tile(const f32x16 (&acc)[FM][FN], uint8_t* region, uint32_t lane,
                                                 uint16_t* __restrict__ C, int64_t ldc, int64_t row0, int64_t col0,

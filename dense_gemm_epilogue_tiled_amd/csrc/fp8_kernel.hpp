@@ -80,11 +80,15 @@ __device__ __forceinline__ u32x4 read16(const GR_LDS uint8_t* p) { return *(cons
 
 // E: output element type with the general epilogue (Epi<ElemF16> or
 // Epi<ElemBF16>); ep.scale carries scale_a * scale_b.
-template <int BMT, bool EDGE, typename E>
+// SPLIT=true (split-K, with a workspace): workgroup g covers tile g % tiles
+// over the K range of split g / tiles (k_per_split bytes, a multiple of 64;
+// no split is empty) and writes its unscaled fp32 sums to part[split][m][n];
+// a second pass adds the splits in order and applies the epilogue.
+template <int BMT, bool EDGE, typename E, bool SPLIT = false>
 __global__ __launch_bounds__(THREADS, Tile<BMT>::MIN_WAVES) void gemm_fp8_tile_kernel(
     const uint8_t* __restrict__ A, const uint8_t* __restrict__ Bt, uint16_t* __restrict__ C, int64_t M, int64_t N,
     int64_t K, int64_t lda, int64_t ldb, int64_t ldc, uint32_t tiles_m, uint32_t tiles_n, uint32_t group_m,
-    int vec_c, EpiArgs ep) {
+    int vec_c, float* __restrict__ part, int64_t k_per_split, EpiArgs ep) {
     static_assert(E::kGeneral, "the fp8 kernels use the general epilogue");
     using T = Tile<BMT>;
     constexpr int FM = T::FM, FN = T::FN, COPIES = T::COPIES;
@@ -102,16 +106,23 @@ __global__ __launch_bounds__(THREADS, Tile<BMT>::MIN_WAVES) void gemm_fp8_tile_k
     const uint32_t wm = wave >> 1;
     const uint32_t wn = wave & 1u;
 
+    const uint32_t tiles = tiles_m * tiles_n;
+    const uint32_t wg = SPLIT ? blockIdx.x % tiles : blockIdx.x;
+    const int64_t split = SPLIT ? blockIdx.x / tiles : 0;
     uint32_t tm, tn;
-    tile_of_workgroup(blockIdx.x, gridDim.x, tiles_m, tiles_n, group_m, tm, tn);
+    tile_of_workgroup(wg, SPLIT ? tiles : gridDim.x, tiles_m, tiles_n, group_m, tm, tn);
     const int64_t m0 = (int64_t)tm * T::BM;
     const int64_t n0 = (int64_t)tn * T::BN;
+    // K range of this workgroup (all of K unless split).
+    const int64_t k_begin = SPLIT ? split * k_per_split : 0;
+    const int64_t k_rest = K - k_begin > 0 ? K - k_begin : 0;
+    const int64_t k_len = SPLIT ? (k_rest < k_per_split ? k_rest : k_per_split) : K;
 
     // ---- copies: copy i of this wave fills LDS block COPIES*wave + i of a
     // slot; block = 16 rows x 64 bytes; lane -> row lane/4, slot lane%4 (chunk
     // slot XOR (row/4)%4).  Rows past M (N) read row M-1 (N-1).
-    const uint8_t* base_a = A + m0 * lda;
-    const uint8_t* base_b = Bt + n0 * ldb;
+    const uint8_t* base_a = A + m0 * lda + k_begin;
+    const uint8_t* base_b = Bt + n0 * ldb + k_begin;
     uint32_t off_a[COPIES], off_b[COPIES];
 #pragma unroll
     for (int i = 0; i < COPIES; ++i) {
@@ -185,7 +196,7 @@ __global__ __launch_bounds__(THREADS, Tile<BMT>::MIN_WAVES) void gemm_fp8_tile_k
         acc[i][j] = mfma(f.b[0][j], f.b[1][j], f.a[0][i], f.a[1][i], acc[i][j]);
     };
 
-    const uint32_t KT = (uint32_t)(K / BK);  // >= 1, whole strips only
+    const uint32_t KT = (uint32_t)(k_len / BK);  // >= 1, whole strips only
 
     // Prologue: strips 0, 1, 2 in flight; strip 0 landed and read.
     issue(0, 0);
@@ -285,9 +296,18 @@ __global__ __launch_bounds__(THREADS, Tile<BMT>::MIN_WAVES) void gemm_fp8_tile_k
     step_tail(kt + 4, f0, f1);
     step_tail(kt + 5, f1, f0);
 
-    // Epilogue (scale, bias, activation, rounding), staged through LDS.
-    epi::store_wave_tile<EDGE, E>(acc, lds + wave * T::REGION, lane, C, ldc, m0 + wm * T::WAVE_T,
-                                  n0 + wn * T::WAVE_T, m0, M, N, vec_c, ep);
+    if constexpr (SPLIT) {
+        epi::store_partials<EDGE>(acc, part + split * M * N, lane, m0 + wm * T::WAVE_T, n0 + wn * T::WAVE_T, M,
+                                  N);
+        (void)C;
+        (void)ldc;
+        (void)vec_c;
+    } else {
+        // Epilogue (scale, bias, activation, rounding), staged through LDS.
+        epi::store_wave_tile<EDGE, E>(acc, lds + wave * T::REGION, lane, C, ldc, m0 + wm * T::WAVE_T,
+                                      n0 + wn * T::WAVE_T, m0, M, N, vec_c, ep);
+        (void)part;
+    }
 }
 
 // ---- guarded kernel: any K, any alignment ------------------------------------

@@ -181,21 +181,24 @@ struct TileSplit {
 constexpr int64_t kTileMaxSplits = 16;
 constexpr int64_t kTileMinSplitK = 256;
 
-bool tile_split_layout(int64_t M, int64_t N, int64_t K, bool allow_one, TileSplit* ts) {
+// bk: K per strip of the kernel (32 fp16 elements; 64 for the fp8 kernel,
+// whose strips take the same matrix-core time); min_k: shortest split.
+bool tile_split_layout(int64_t M, int64_t N, int64_t K, bool allow_one, TileSplit* ts,
+                       int64_t bk = gr::tile128::BK, int64_t min_k = kTileMinSplitK) {
     using namespace gr::tile128;
     const int64_t tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
     int64_t S = 512 / tiles;
-    if (S > K / kTileMinSplitK) S = K / kTileMinSplitK;
+    if (S > K / min_k) S = K / min_k;
     if (S > kTileMaxSplits) S = kTileMaxSplits;
     if (S < 1) S = 1;
-    const int64_t strips = K / BK;
+    const int64_t strips = K / bk;
     // Splitting pays only while the unsplit grid fills at most half of the
     // CUs' workgroup slots: with 224-256 tiles a split into 2 measured 15-20%
     // slower (8192 x 28672 x 64..256, 256 x 16384 x 8192).
     if (!allow_one && tiles > kSmallTileMaxLargeTiles) return false;
     if (!allow_one && (S < 2 || strips * (S - 1) < kTileSplitMinSavedStrips * S)) return false;
     TileSplit q;
-    q.k_per_split = (strips + S - 1) / S * BK;
+    q.k_per_split = (strips + S - 1) / S * bk;
     q.splits = (K + q.k_per_split - 1) / q.k_per_split;  // no empty split
     q.bytes = (q.splits * M * N * 4 + kWorkspaceAlign - 1) / kWorkspaceAlign * kWorkspaceAlign;
     *ts = q;
@@ -362,6 +365,23 @@ int launch(void (*kernel)(Args...), int64_t grid, int threads, hipStream_t strea
     return e == hipSuccess ? GR_OK : GR_ERR_LAUNCH;
 }
 
+// Second pass of every split path: sum the fp32 partial sums in order and
+// apply the epilogue (4 outputs per thread when rows hold a multiple of 4).
+template <typename E>
+int launch_reduce(const float* part, uint16_t* C, int64_t M, int64_t N, int64_t ldc, int64_t splits, int vec_c,
+                  const gr::EpiArgs& ep, hipStream_t stream) {
+    const bool vec4 = N % 4 == 0;
+    const int64_t items = vec4 ? M * N / 4 : M * N;
+    int64_t blocks = (items + 255) / 256;
+    if (blocks > 2048) blocks = 2048;
+    const int s = (int)splits;
+    if (vec4)
+        return launch(gr::smallm::gemm_relu_smallm_reduce_kernel<E, true>, blocks, 256, stream, part, C, M, N, ldc, s,
+                      vec_c, ep);
+    return launch(gr::smallm::gemm_relu_smallm_reduce_kernel<E, false>, blocks, 256, stream, part, C, M, N, ldc, s,
+                  vec_c, ep);
+}
+
 template <bool GUARD, int VA, int VB, typename E>
 int launch_tile(const gr_plan_t& p, int64_t M, int64_t N, int64_t K, const uint16_t* A, int64_t lda,
                 const uint16_t* B, int64_t ldb, uint16_t* C, int64_t ldc, const gr::EpiArgs& ep, hipStream_t stream) {
@@ -421,10 +441,7 @@ int run(const gr_plan_t& p, int64_t M, int64_t N, int64_t K, const uint16_t* A, 
                            : launch(gemm_relu_smallm_split_kernel<true, E>, p.grid, SPLIT_THREADS, stream, A, B, part,
                                     M, N, K, lda, ldb, sp.k_per_split, nb);
             if (st != GR_OK) return st;
-            int64_t rblocks = (M * N + 255) / 256;
-            if (rblocks > 2048) rblocks = 2048;
-            return launch(gemm_relu_smallm_reduce_kernel<E>, rblocks, 256, stream, (const float*)part, C, M, N, ldc,
-                          (int)sp.splits, ep);
+            return launch_reduce<E>(part, C, M, N, ldc, sp.splits, p.vec_c, ep, stream);
         }
         case GR_PATH_TILE_SPLIT: {
             using namespace gr::tile128;
@@ -440,10 +457,7 @@ int run(const gr_plan_t& p, int64_t M, int64_t N, int64_t K, const uint16_t* A, 
                            : launch(gemm_relu_tile128_kernel<true, true, false, E>, p.grid, THREADS, stream, A, B, C,
                                     M, N, K, lda, ldb, ldc, tiles_m, tiles_n, gm, vc, part, kps, ep);
             if (st != GR_OK) return st;
-            int64_t rblocks = (M * N + 255) / 256;
-            if (rblocks > 2048) rblocks = 2048;
-            return launch(gr::smallm::gemm_relu_smallm_reduce_kernel<E>, rblocks, 256, stream, (const float*)part, C,
-                          M, N, ldc, (int)ts.splits, ep);
+            return launch_reduce<E>(part, C, M, N, ldc, ts.splits, p.vec_c, ep, stream);
         }
         case GR_PATH_TILE_PACKED: {
             const int st = launch_pack(pk, M, N, K, A, lda, B, ldb, ws, stream);
@@ -827,8 +841,11 @@ int64_t span_bytes8(int64_t rows, int64_t cols, int64_t ld) {
     return (rows - 1) * ld + cols;
 }
 
+// Argument checks of the fp8 calls; the workspace (ws, ws_bytes) as in
+// validate(), and it must not overlap the bias either.
 int validate_fp8(int64_t M, int64_t N, int64_t K, uintptr_t A, int64_t lda, uintptr_t Bt, int64_t ldbt,
-                 uintptr_t bias, int act, uintptr_t C, int64_t ldc, int out_fmt) {
+                 uintptr_t bias, int act, uintptr_t C, int64_t ldc, int out_fmt, uintptr_t ws = 0,
+                 int64_t ws_bytes = 0) {
     if (M < 0 || N < 0 || K < 0) return GR_ERR_INVALID_DIM;
     if (M > kMaxDim || N > kMaxDim || K > kMaxDim) return GR_ERR_TOO_LARGE;
     const int64_t kmin = K > 1 ? K : 1, nmin = N > 1 ? N : 1;
@@ -844,6 +861,14 @@ int validate_fp8(int64_t M, int64_t N, int64_t K, uintptr_t A, int64_t lda, uint
     if (sa < 0 || sb < 0 || sc < 0) return GR_ERR_TOO_LARGE;
     if (overlaps(C, sc, A, sa) || overlaps(C, sc, Bt, sb)) return GR_ERR_ALIAS;
     if (bias && c_used && overlaps(C, sc, bias, 2 * N)) return GR_ERR_ALIAS;
+    if (ws_bytes < 0) return GR_ERR_INVALID_ARG;
+    if (ws_bytes > 0) {
+        if (!ws) return GR_ERR_NULL_PTR;
+        if (ws % kWorkspaceAlign != 0) return GR_ERR_INVALID_ARG;
+        if (overlaps(ws, ws_bytes, A, sa) || overlaps(ws, ws_bytes, Bt, sb) || overlaps(ws, ws_bytes, C, sc) ||
+            (bias && c_used && overlaps(ws, ws_bytes, bias, 2 * N)))
+            return GR_ERR_ALIAS;
+    }
     return GR_OK;
 }
 
@@ -870,7 +895,16 @@ bool fp8_large_tiles(int64_t M, int64_t N) {
     return ((M + 255) / 256) * ((N + 255) / 256) > kSmallTileMaxLargeTiles;
 }
 
-void fill_plan_fp8(int path, int64_t M, int64_t N, uintptr_t C, int64_t ldc, gr_plan_t* p) {
+// Split-K of the 128 x 128 fp8 tiles (workspace): the rule of the fp16 tile
+// split, in 64-byte strips, each split at least 8 strips long.
+constexpr int64_t kFp8MinSplitK = 512;
+bool fp8_split_layout(int64_t M, int64_t N, int64_t K, bool forced, TileSplit* ts) {
+    if (!forced && fp8_large_tiles(M, N)) return false;
+    return tile_split_layout(M, N, K, forced, ts, gr::fp8::BK, kFp8MinSplitK);
+}
+
+void fill_plan_fp8(int path, int64_t M, int64_t N, uintptr_t C, int64_t ldc, const TileSplit& ts,
+                   gr_plan_t* p) {
     std::memset(p, 0, sizeof(*p));
     p->path = path;
     p->block_k = gr::fp8::BK;
@@ -887,6 +921,17 @@ void fill_plan_fp8(int path, int64_t M, int64_t N, uintptr_t C, int64_t ldc, gr_
         p->vec_a = 16;
         p->vec_b = 16;
         p->group_m = kGroupM;
+    } else if (path == GR_PATH_TILE_SPLIT) {
+        using namespace gr::fp8;
+        p->block_m = 128;
+        p->block_n = 128;
+        p->stages = STAGES;
+        p->grid = ((M + 127) / 128) * ((N + 127) / 128) * ts.splits;
+        p->vec_a = 16;
+        p->vec_b = 16;
+        p->group_m = kGroupM;
+        p->split_k = (int32_t)ts.splits;
+        p->workspace = ts.bytes;
     } else if (path == GR_PATH_SMALL_M) {
         using namespace gr::fp8;
         p->block_m = SM_MAX_M;
@@ -909,30 +954,59 @@ void fill_plan_fp8(int path, int64_t M, int64_t N, uintptr_t C, int64_t ldc, gr_
     }
 }
 
+// Validate, choose (or check a forced) path, fill the plan; no HIP call.
+// ws_known: the workspace pointer is real and is checked (a plan made from a
+// size alone skips the pointer checks).
 int plan_call_fp8(int64_t M, int64_t N, int64_t K, uintptr_t A, int64_t lda, uintptr_t Bt, int64_t ldbt,
-                  uintptr_t bias, int act, uintptr_t C, int64_t ldc, int out_fmt, int forced, gr_plan_t* p) {
-    int st = validate_fp8(M, N, K, A, lda, Bt, ldbt, bias, act, C, ldc, out_fmt);
+                  uintptr_t bias, int act, uintptr_t C, int64_t ldc, int out_fmt, uintptr_t ws, int64_t ws_bytes,
+                  bool ws_known, int forced, TileSplit* ts, gr_plan_t* p) {
+    if (ws_bytes < 0) return GR_ERR_INVALID_ARG;
+    int st = ws_known ? validate_fp8(M, N, K, A, lda, Bt, ldbt, bias, act, C, ldc, out_fmt, ws, ws_bytes)
+                      : validate_fp8(M, N, K, A, lda, Bt, ldbt, bias, act, C, ldc, out_fmt);
     if (st != GR_OK) return st;
     const bool tile_ok = fp8_tile_ok(M, N, K, A, lda, Bt, ldbt);
     const bool smallm_ok = fp8_smallm_ok(M, N, K, A, lda, Bt, ldbt);
     int path;
     if (M == 0 || N == 0) path = GR_PATH_NONE;
     else if (smallm_ok) path = GR_PATH_SMALL_M;
+    else if (tile_ok && ws_bytes > 0 && fp8_split_layout(M, N, K, false, ts) && ts->bytes <= ws_bytes)
+        path = GR_PATH_TILE_SPLIT;
     else path = tile_ok ? GR_PATH_TILE : GR_PATH_TILE_EDGE;
     if (forced >= 0 && path != GR_PATH_NONE) {
-        if ((forced == GR_PATH_TILE && !tile_ok) || (forced == GR_PATH_SMALL_M && !smallm_ok) ||
-            (forced != GR_PATH_TILE && forced != GR_PATH_TILE_EDGE && forced != GR_PATH_SMALL_M))
+        if (forced == GR_PATH_TILE_SPLIT) {
+            if (!tile_ok || !fp8_split_layout(M, N, K, true, ts) || ts->bytes > ws_bytes) return GR_ERR_INVALID_PATH;
+        } else if ((forced == GR_PATH_TILE && !tile_ok) || (forced == GR_PATH_SMALL_M && !smallm_ok) ||
+                   (forced != GR_PATH_TILE && forced != GR_PATH_TILE_EDGE && forced != GR_PATH_SMALL_M)) {
             return GR_ERR_INVALID_PATH;
+        }
         path = forced;
     }
-    fill_plan_fp8(path, M, N, C, ldc, p);
+    fill_plan_fp8(path, M, N, C, ldc, *ts, p);
     return GR_OK;
 }
 
 template <typename E>
 int run_fp8(const gr_plan_t& p, int64_t M, int64_t N, int64_t K, const uint8_t* A, int64_t lda, const uint8_t* Bt,
-            int64_t ldbt, uint16_t* C, int64_t ldc, const gr::EpiArgs& ep, hipStream_t stream) {
+            int64_t ldbt, uint16_t* C, int64_t ldc, const TileSplit& ts, uint8_t* ws, const gr::EpiArgs& ep,
+            hipStream_t stream) {
     using namespace gr::fp8;
+    float* const no_part = nullptr;  // the unsplit kernels take no workspace
+    const int64_t no_kps = 0;
+    if (p.path == GR_PATH_TILE_SPLIT) {
+        float* part = reinterpret_cast<float*>(ws);
+        const uint32_t tiles_m = (uint32_t)((M + 127) / 128);
+        const uint32_t tiles_n = (uint32_t)((N + 127) / 128);
+        const uint32_t gm = (uint32_t)p.group_m;
+        const int vc = (int)p.vec_c;
+        const int64_t kps = ts.k_per_split;
+        const bool whole = M % 128 == 0 && N % 128 == 0;
+        int st = whole ? launch(gemm_fp8_tile_kernel<128, false, E, true>, p.grid, THREADS, stream, A, Bt, C, M, N, K,
+                                lda, ldbt, ldc, tiles_m, tiles_n, gm, vc, part, kps, ep)
+                       : launch(gemm_fp8_tile_kernel<128, true, E, true>, p.grid, THREADS, stream, A, Bt, C, M, N, K,
+                                lda, ldbt, ldc, tiles_m, tiles_n, gm, vc, part, kps, ep);
+        if (st != GR_OK) return st;
+        return launch_reduce<E>(part, C, M, N, ldc, ts.splits, p.vec_c, ep, stream);
+    }
     if (p.path == GR_PATH_TILE) {
         const int64_t bm = p.block_m;
         const uint32_t tiles_m = (uint32_t)((M + bm - 1) / bm);
@@ -943,15 +1017,15 @@ int run_fp8(const gr_plan_t& p, int64_t M, int64_t N, int64_t K, const uint8_t* 
         if (bm == 256) {
             if (whole)
                 return launch(gemm_fp8_tile_kernel<256, false, E>, p.grid, THREADS, stream, A, Bt, C, M, N, K, lda,
-                              ldbt, ldc, tiles_m, tiles_n, gm, vc, ep);
+                              ldbt, ldc, tiles_m, tiles_n, gm, vc, no_part, no_kps, ep);
             return launch(gemm_fp8_tile_kernel<256, true, E>, p.grid, THREADS, stream, A, Bt, C, M, N, K, lda, ldbt,
-                          ldc, tiles_m, tiles_n, gm, vc, ep);
+                          ldc, tiles_m, tiles_n, gm, vc, no_part, no_kps, ep);
         }
         if (whole)
             return launch(gemm_fp8_tile_kernel<128, false, E>, p.grid, THREADS, stream, A, Bt, C, M, N, K, lda, ldbt,
-                          ldc, tiles_m, tiles_n, gm, vc, ep);
+                          ldc, tiles_m, tiles_n, gm, vc, no_part, no_kps, ep);
         return launch(gemm_fp8_tile_kernel<128, true, E>, p.grid, THREADS, stream, A, Bt, C, M, N, K, lda, ldbt, ldc,
-                      tiles_m, tiles_n, gm, vc, ep);
+                      tiles_m, tiles_n, gm, vc, no_part, no_kps, ep);
     }
     if (p.path == GR_PATH_SMALL_M) {
         if (N % SM_NB == 0)
@@ -969,10 +1043,11 @@ int run_fp8(const gr_plan_t& p, int64_t M, int64_t N, int64_t K, const uint8_t* 
 
 int entry_fp8(int64_t M, int64_t N, int64_t K, const uint8_t* A, int64_t lda, const uint8_t* Bt, int64_t ldbt,
               float scale_a, float scale_b, const uint16_t* bias, int act, uint16_t* C, int64_t ldc, int out_fmt,
-              void* stream, int forced) {
+              void* ws, int64_t ws_bytes, void* stream, int forced) {
     gr_plan_t p;
+    TileSplit ts;
     int st = plan_call_fp8(M, N, K, (uintptr_t)A, lda, (uintptr_t)Bt, ldbt, (uintptr_t)bias, act, (uintptr_t)C, ldc,
-                           out_fmt, forced, &p);
+                           out_fmt, (uintptr_t)ws, ws_bytes, true, forced, &ts, &p);
     if (st != GR_OK) return st;
     if (p.path == GR_PATH_NONE) return GR_OK;
     st = check_device();
@@ -980,9 +1055,10 @@ int entry_fp8(int64_t M, int64_t N, int64_t K, const uint8_t* A, int64_t lda, co
     // One scale for the product: the two per-tensor scales multiplied in fp32.
     const gr::EpiArgs ep{bias, act, scale_a * scale_b};
     hipStream_t s = static_cast<hipStream_t>(stream);
+    uint8_t* w = static_cast<uint8_t*>(ws);
     if (out_fmt == GR_FMT_BF16)
-        return run_fp8<gr::Epi<gr::ElemBF16>>(p, M, N, K, A, lda, Bt, ldbt, C, ldc, ep, s);
-    return run_fp8<gr::Epi<gr::ElemF16>>(p, M, N, K, A, lda, Bt, ldbt, C, ldc, ep, s);
+        return run_fp8<gr::Epi<gr::ElemBF16>>(p, M, N, K, A, lda, Bt, ldbt, C, ldc, ts, w, ep, s);
+    return run_fp8<gr::Epi<gr::ElemF16>>(p, M, N, K, A, lda, Bt, ldbt, C, ldc, ts, w, ep, s);
 }
 
 }  // namespace
@@ -1129,22 +1205,58 @@ int gemm_relu_f16_plan_ws(int64_t M, int64_t N, int64_t K, const uint16_t* A, in
 int gemm_fp8_bt(int64_t M, int64_t N, int64_t K, const uint8_t* A, int64_t lda, const uint8_t* Bt, int64_t ldbt,
                 float scale_a, float scale_b, const uint16_t* bias, int act, uint16_t* C, int64_t ldc, int out_fmt,
                 void* stream) {
-    return entry_fp8(M, N, K, A, lda, Bt, ldbt, scale_a, scale_b, bias, act, C, ldc, out_fmt, stream, -1);
+    return entry_fp8(M, N, K, A, lda, Bt, ldbt, scale_a, scale_b, bias, act, C, ldc, out_fmt, nullptr, 0, stream,
+                     -1);
 }
 
 int gemm_fp8_bt_forced(int64_t M, int64_t N, int64_t K, const uint8_t* A, int64_t lda, const uint8_t* Bt,
                        int64_t ldbt, float scale_a, float scale_b, const uint16_t* bias, int act, uint16_t* C,
                        int64_t ldc, int out_fmt, void* stream, int path) {
     if (path != GR_PATH_TILE && path != GR_PATH_TILE_EDGE && path != GR_PATH_SMALL_M) return GR_ERR_INVALID_PATH;
-    return entry_fp8(M, N, K, A, lda, Bt, ldbt, scale_a, scale_b, bias, act, C, ldc, out_fmt, stream, path);
+    return entry_fp8(M, N, K, A, lda, Bt, ldbt, scale_a, scale_b, bias, act, C, ldc, out_fmt, nullptr, 0, stream,
+                     path);
+}
+
+int gemm_fp8_bt_ws(int64_t M, int64_t N, int64_t K, const uint8_t* A, int64_t lda, const uint8_t* Bt, int64_t ldbt,
+                   float scale_a, float scale_b, const uint16_t* bias, int act, uint16_t* C, int64_t ldc,
+                   int out_fmt, void* workspace, int64_t workspace_bytes, void* stream, int path) {
+    if (path != -1 && path != GR_PATH_TILE && path != GR_PATH_TILE_EDGE && path != GR_PATH_SMALL_M &&
+        path != GR_PATH_TILE_SPLIT)
+        return GR_ERR_INVALID_PATH;
+    return entry_fp8(M, N, K, A, lda, Bt, ldbt, scale_a, scale_b, bias, act, C, ldc, out_fmt, workspace,
+                     workspace_bytes, stream, path);
+}
+
+int gemm_fp8_bt_workspace_size(int64_t M, int64_t N, int64_t K, const uint8_t* A, int64_t lda, const uint8_t* Bt,
+                               int64_t ldbt, const uint16_t* C, int64_t ldc, int64_t* bytes) {
+    if (!bytes) return GR_ERR_INVALID_ARG;
+    *bytes = 0;
+    int st = validate_fp8(M, N, K, (uintptr_t)A, lda, (uintptr_t)Bt, ldbt, 0, GR_ACT_RELU, (uintptr_t)C, ldc,
+                          GR_FMT_F16);
+    if (st != GR_OK) return st;
+    TileSplit ts;
+    if (M > 0 && N > 0 && !fp8_smallm_ok(M, N, K, (uintptr_t)A, lda, (uintptr_t)Bt, ldbt) &&
+        fp8_tile_ok(M, N, K, (uintptr_t)A, lda, (uintptr_t)Bt, ldbt) && fp8_split_layout(M, N, K, false, &ts))
+        *bytes = ts.bytes;
+    return GR_OK;
+}
+
+int gemm_fp8_bt_plan_ws(int64_t M, int64_t N, int64_t K, const uint8_t* A, int64_t lda, const uint8_t* Bt,
+                        int64_t ldbt, const uint16_t* bias, int act, const uint16_t* C, int64_t ldc, int out_fmt,
+                        int64_t workspace_bytes, gr_plan_t* out) {
+    if (!out) return GR_ERR_INVALID_ARG;
+    TileSplit ts;
+    return plan_call_fp8(M, N, K, (uintptr_t)A, lda, (uintptr_t)Bt, ldbt, (uintptr_t)bias, act, (uintptr_t)C, ldc,
+                         out_fmt, 0, workspace_bytes, false, -1, &ts, out);
 }
 
 int gemm_fp8_bt_plan(int64_t M, int64_t N, int64_t K, const uint8_t* A, int64_t lda, const uint8_t* Bt,
                      int64_t ldbt, const uint16_t* bias, int act, const uint16_t* C, int64_t ldc, int out_fmt,
                      gr_plan_t* out) {
     if (!out) return GR_ERR_INVALID_ARG;
+    TileSplit ts;
     return plan_call_fp8(M, N, K, (uintptr_t)A, lda, (uintptr_t)Bt, ldbt, (uintptr_t)bias, act, (uintptr_t)C, ldc,
-                         out_fmt, -1, out);
+                         out_fmt, 0, 0, false, -1, &ts, out);
 }
 
 const char* gemm_relu_status_string(int status) {

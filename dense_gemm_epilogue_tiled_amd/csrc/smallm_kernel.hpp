@@ -331,18 +331,46 @@ __global__ __launch_bounds__(SPLIT_THREADS, 1) void gemm_relu_smallm_split_kerne
 }
 
 // Pass 2: C[m][n] = epilogue(sum over s of part[s][m][n]) -- the fused ReLU
-// and rounding, or (E = Epi<...>) scale, bias, activation and rounding.
-template <typename E = ElemF16>
+// and rounding, or (E = Epi<...>) scale, bias, activation and rounding.  The
+// sum starts from +0 and adds the splits in order, whatever the variant.
+// VEC4 (N % 4 == 0): each thread owns four consecutive outputs of one row,
+// reads them with 16-byte loads and (vec_c >= 4) stores them with one 8-byte
+// store.
+template <typename E = ElemF16, bool VEC4 = false>
 __global__ __launch_bounds__(256) void gemm_relu_smallm_reduce_kernel(const float* __restrict__ part,
                                                                       uint16_t* __restrict__ C, int64_t M,
                                                                       int64_t N, int64_t ldc, int splits,
-                                                                      EpiArgs ep) {
+                                                                      int vec_c, EpiArgs ep) {
     const int64_t total = M * N;
-    for (int64_t o = (int64_t)blockIdx.x * 256 + threadIdx.x; o < total; o += (int64_t)gridDim.x * 256) {
-        float sum = 0.0f;
-        for (int s = 0; s < splits; ++s) sum += part[(int64_t)s * total + o];
-        const int64_t m = o / N, n = o - m * N;
-        C[m * ldc + n] = epi_value<E>(sum, n, N, ep);
+    if constexpr (VEC4) {
+        for (int64_t o = (int64_t)blockIdx.x * 256 + threadIdx.x; 4 * o < total; o += (int64_t)gridDim.x * 256) {
+            f32x4 sum = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll 4
+            for (int s = 0; s < splits; ++s) {
+                const f32x4 v = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(part + (int64_t)s * total) + o);
+                sum = f32x4{sum[0] + v[0], sum[1] + v[1], sum[2] + v[2], sum[3] + v[3]};
+            }
+            const int64_t m = 4 * o / N, n = 4 * o - m * N;
+            uint16_t r[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) r[e] = epi_value<E>(sum[e], n + e, N, ep);
+            uint16_t* dst = C + m * ldc + n;
+            if (vec_c >= 4) {
+                *reinterpret_cast<u32x2*>(dst) =
+                    u32x2{(uint32_t)r[0] | ((uint32_t)r[1] << 16), (uint32_t)r[2] | ((uint32_t)r[3] << 16)};
+            } else {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) dst[e] = r[e];
+            }
+        }
+    } else {
+        (void)vec_c;
+        for (int64_t o = (int64_t)blockIdx.x * 256 + threadIdx.x; o < total; o += (int64_t)gridDim.x * 256) {
+            float sum = 0.0f;
+            for (int s = 0; s < splits; ++s) sum += part[(int64_t)s * total + o];
+            const int64_t m = o / N, n = o - m * N;
+            C[m * ldc + n] = epi_value<E>(sum, n, N, ep);
+        }
     }
 }
 

@@ -204,31 +204,7 @@ __global__ __launch_bounds__(THREADS, 2) void gemm_relu_tile128_kernel(
     }
 
     if constexpr (SPLIT) {
-        // fp32 partial sums of the outputs this tile owns: block (i, j) holds
-        // C^T, lane l register r is row 32i + l%32, column 32j + 8(r/4) +
-        // 4(l/32) + r%4 of the wave's tile.
-        float* pbase = part + split * M * N;
-#pragma unroll
-        for (int i = 0; i < FM; ++i) {
-            const int64_t m = m0 + wm * WAVE_TM + 32 * i + (lane & 31u);
-            const bool row_ok = !EDGE || m < M;
-#pragma unroll
-            for (int j = 0; j < FN; ++j) {
-#pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    const int64_t n = n0 + wn * WAVE_TN + 32 * j + 8 * q + 4 * (lane >> 5);
-                    float* dst = pbase + m * N + n;
-                    if (!EDGE || (row_ok && n + 4 <= N && (N & 3) == 0)) {
-                        *reinterpret_cast<f32x4*>(dst) = f32x4{acc[i][j][4 * q], acc[i][j][4 * q + 1],
-                                                               acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
-                    } else if (row_ok) {
-#pragma unroll
-                        for (int e = 0; e < 4; ++e)
-                            if (n + e < N) dst[e] = acc[i][j][4 * q + e];
-                    }
-                }
-            }
-        }
+        epi::store_partials<EDGE>(acc, part + split * M * N, lane, m0 + wm * WAVE_TM, n0 + wn * WAVE_TN, M, N);
         (void)C;
         (void)ldc;
         (void)vec_c;

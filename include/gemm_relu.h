@@ -461,6 +461,49 @@ int gemm_fp8_bt_plan(int64_t M, int64_t N, int64_t K,
                      const uint16_t* C, int64_t ldc, int out_fmt,
                      gr_plan_t* out);
 
+/*
+ * gemm_fp8_bt with a caller workspace.  When the 128 x 128 tiles of the
+ * pipelined kernel would leave most CUs idle (at most 128 tiles) and K is
+ * long, K is split S ways (GR_PATH_TILE_SPLIT): each split's fp32 sums of
+ * A * Bt^T go to the workspace (S x M x N floats), and a second kernel adds
+ * the splits in order, then applies scale_a * scale_b, the bias, the
+ * activation and the rounding once, as the unsplit path does.  This is the
+ * split-K the pages give for a small M x N with a long K (blog "TileLang
+ * programming basics", section 5.1 "Split-K"), with ordered fp32 partial
+ * sums in place of atomic adds.  Workspace rules as for
+ * gemm_relu_f16_ws (256-byte aligned; NULL, 0 = none; GR_ERR_ALIAS when it
+ * overlaps A, Bt, C or the bias).  path -1 lets the planner choose;
+ * GR_PATH_TILE, GR_PATH_TILE_EDGE, GR_PATH_SMALL_M or GR_PATH_TILE_SPLIT
+ * force one (GR_ERR_INVALID_PATH when its conditions do not hold or the
+ * workspace is too small).
+ */
+int gemm_fp8_bt_ws(int64_t M, int64_t N, int64_t K,
+                   const uint8_t* A, int64_t lda,
+                   const uint8_t* Bt, int64_t ldbt,
+                   float scale_a, float scale_b,
+                   const uint16_t* bias, int act,
+                   uint16_t* C, int64_t ldc, int out_fmt,
+                   void* workspace, int64_t workspace_bytes,
+                   void* stream, int path);
+
+/* Bytes of workspace with which gemm_fp8_bt_ws splits K for this problem
+   (0: it never does).  Validates like gemm_fp8_bt; no HIP call.  bytes is a
+   host pointer (not NULL). */
+int gemm_fp8_bt_workspace_size(int64_t M, int64_t N, int64_t K,
+                               const uint8_t* A, int64_t lda,
+                               const uint8_t* Bt, int64_t ldbt,
+                               const uint16_t* C, int64_t ldc,
+                               int64_t* bytes);
+
+/* The planner's decision for gemm_fp8_bt_ws with a workspace of
+   workspace_bytes bytes (its address is not checked).  Pure. */
+int gemm_fp8_bt_plan_ws(int64_t M, int64_t N, int64_t K,
+                        const uint8_t* A, int64_t lda,
+                        const uint8_t* Bt, int64_t ldbt,
+                        const uint16_t* bias, int act,
+                        const uint16_t* C, int64_t ldc, int out_fmt,
+                        int64_t workspace_bytes, gr_plan_t* out);
+
 /* Static, NUL-terminated name of a status code ("GR_OK", "GR_ERR_ALIAS", ...).
    Unknown codes give "GR_ERR_UNKNOWN". */
 const char* gemm_relu_status_string(int status);

@@ -481,6 +481,50 @@ def test_workspace_variants_argument_checks_need_no_gpu():
     assert f(0, 8, 8, 0, 8, BASE_B, 8, bias, gr.GR_ACT_TANH, 0, 8, gr.GR_FMT_F16, None, 0) == gr.GR_OK
 
 
+def test_fp8_split_planner_and_checks_need_no_gpu():
+    """gemm_fp8_bt_ws: split-K only for at most 128 tiles of 128 x 128 and a
+    long K, a workspace large enough, the small-M stream first; workspace
+    checks before any HIP call."""
+    def plan(M, N, K, ws_bytes=1 << 30):
+        st, p = gr.gemm_fp8_bt_plan_ws(M, N, K, BASE_A, K, BASE_B, K, None, 1, BASE_C, N, gr.GR_FMT_F16, ws_bytes)
+        assert st == gr.GR_OK
+        return p
+
+    def size(M, N, K):
+        st, b = gr.gemm_fp8_bt_workspace_size(M, N, K, BASE_A, K, BASE_B, K, BASE_C, N)
+        assert st == gr.GR_OK
+        return b
+    p = plan(128, 8192, 8192)
+    assert (p["path"], p["split_k"], p["grid"], p["block_m"]) == (gr.GR_PATH_TILE_SPLIT, 8, 512, 128)
+    assert p["workspace"] == size(128, 8192, 8192) == 8 * 128 * 8192 * 4
+    assert plan(128, 8192, 8192, size(128, 8192, 8192) - 256)["path"] == gr.GR_PATH_TILE   # too small
+    assert plan(128, 8192, 8192, 0)["path"] == gr.GR_PATH_TILE
+    assert plan(512, 8192, 8192)["path"] == gr.GR_PATH_TILE and size(512, 8192, 8192) == 0   # 256 tiles
+    assert plan(4096, 4096, 4096)["path"] == gr.GR_PATH_TILE and size(4096, 4096, 4096) == 0
+    assert plan(64, 4096, 4096)["path"] == gr.GR_PATH_TILE                  # K too short to pay
+    assert plan(16, 4096, 8192)["path"] == gr.GR_PATH_SMALL_M and size(16, 4096, 8192) == 0
+    assert size(128, 8192, 8032) == 0                                       # K % 64 != 0: guarded kernel
+    # every split non-empty and a whole number of 64-byte strips
+    for (M, N, K) in ((300, 270, 8192), (17, 130, 8128), (20, 1, 16384), (128, 4096, 16384)):
+        p = plan(M, N, K)
+        assert p["path"] == gr.GR_PATH_TILE_SPLIT, (M, N, K)
+        tiles = ((M + 127) // 128) * ((N + 127) // 128)
+        assert p["grid"] == tiles * p["split_k"] and 2 <= p["split_k"] <= 16 and tiles * p["split_k"] <= 512
+    f = gr.gemm_fp8_bt_ws
+    ws = BASE_C + (1 << 32)
+    args = (128, 8192, 8192, BASE_A, 8192, BASE_B, 8192, 1.0, 1.0)
+    assert f(*args, None, 1, BASE_C, 8192, 0, ws, -1) == gr.GR_ERR_INVALID_ARG
+    assert f(*args, None, 1, BASE_C, 8192, 0, ws + 16, 1 << 20) == gr.GR_ERR_INVALID_ARG        # alignment
+    assert f(*args, None, 1, BASE_C, 8192, 0, 0, 1 << 20) == gr.GR_ERR_NULL_PTR
+    assert f(*args, None, 1, BASE_C, 8192, 0, BASE_B, 1 << 20) == gr.GR_ERR_ALIAS              # overlaps Bt
+    assert f(*args, ws + 1024, 1, BASE_C, 8192, 0, ws, 1 << 20) == gr.GR_ERR_ALIAS              # overlaps bias
+    assert f(*args, None, 1, BASE_C, 8192, 0, ws, 1 << 20, None, gr.GR_PATH_SMALL_M_SPLIT) == gr.GR_ERR_INVALID_PATH
+    assert f(*args, None, 1, BASE_C, 8192, 0, ws, 1024, None, gr.GR_PATH_TILE_SPLIT) == gr.GR_ERR_INVALID_PATH
+    assert f(128, 8192, 8032, BASE_A, 8032, BASE_B, 8032, 1.0, 1.0, None, 1, BASE_C, 8192, 0, ws, 1 << 30, None,
+             gr.GR_PATH_TILE_SPLIT) == gr.GR_ERR_INVALID_PATH
+    assert f(0, 8, 8, 0, 8, BASE_B, 8, 1.0, 1.0, None, 1, 0, 8, 0, None, 0) == gr.GR_OK
+
+
 def test_fp8_planner_and_checks_need_no_gpu():
     """gemm_fp8_bt: the pipelined kernel for K % 64 == 0 with 16-byte rows (any
     M, N), the guarded kernel otherwise; argument errors before any HIP call."""

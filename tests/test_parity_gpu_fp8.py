@@ -180,3 +180,107 @@ def test_fp8_small_m_against_tile(M, N, K):
     C2 = run(A, Bt, M, N, K, K, K, N, sa, sb, path=gr.GR_PATH_TILE)[:M * N].reshape(M, N)
     assert_parity(C1, C2, "small-M vs tile")
     assert_parity(C1, oracle.gemm_fp8_bt_full(A, Bt, sa, sb), "small-M vs oracle")
+
+
+# ---- split-K with a workspace (gemm_fp8_bt_ws) -------------------------------------
+
+def run_ws(A, Bt, M, N, K, lda, ldbt, ldc, sa, sb, bias, act, fmt, path=-1, ws_bytes=None):
+    import torch as t
+    dA = dev8(np.concatenate([A.ravel(), np.zeros(16, np.uint8)]))
+    dB = dev8(np.concatenate([Bt.ravel(), np.zeros(16, np.uint8)]))
+    db = dev16(bias) if bias is not None else None
+    dC = full_dev((M * ldc + 8,), SENTINEL)
+    if ws_bytes is None:
+        st, ws_bytes = gr.gemm_fp8_bt_workspace_size(M, N, K, dA.data_ptr(), lda, dB.data_ptr(), ldbt, dC.data_ptr(),
+                                                     ldc)
+        assert st == gr.GR_OK
+        ws_bytes = max(ws_bytes, 32 << 20)  # forced splits may need more than the planner's choice
+    ws = t.full((ws_bytes,), 0x7F, dtype=t.uint8, device="cuda")  # dirty: NaN-ish floats if a partial is not written
+    log("fp8 ws M=%d N=%d K=%d lda=%d ldbt=%d ldc=%d act=%s fmt=%s path=%s ws=%d" %
+        (M, N, K, lda, ldbt, ldc, act, fmt, path, ws_bytes))
+    st = gr.gemm_fp8_bt_ws(M, N, K, dA.data_ptr(), lda, dB.data_ptr(), ldbt, sa, sb,
+                           db.data_ptr() if db is not None else None, gr.ACT_CODES[act], dC.data_ptr(), ldc, FMTS[fmt],
+                           ws.data_ptr(), ws_bytes, t.cuda.current_stream().cuda_stream, path)
+    t.cuda.synchronize()
+    assert st == gr.GR_OK, gr.gemm_relu_status_string(st)
+    return from_dev(dC)
+
+
+SPLIT_CASES = [
+    # M, N, K, lda, ldbt, ldc, forced path (-1: the planner must pick the split), what
+    (300, 270, 8192, 8192, 8192, 273, -1, "3 x 3 partial tiles, 16 splits"),
+    (256, 512, 4096, 4096, 4112, 512, gr.GR_PATH_TILE_SPLIT, "whole tiles, padded Bt"),
+    (129, 1000, 2048, 2064, 2048, 1001, gr.GR_PATH_TILE_SPLIT, "partial tiles, odd N"),
+    (40, 256, 64, 64, 64, 256, gr.GR_PATH_TILE_SPLIT, "one strip: a single split"),
+    (17, 130, 1984, 1984, 1984, 130, gr.GR_PATH_TILE_SPLIT, "K not a multiple of the split"),
+]
+
+
+@pytest.mark.parametrize("fmt", ["f16", "bf16"])
+@pytest.mark.parametrize("case", SPLIT_CASES, ids=[c[-1] for c in SPLIT_CASES])
+def test_fp8_split_parity(case, fmt):
+    M, N, K, lda, ldbt, ldc, path, what = case
+    if path == -1:
+        st, p = gr.gemm_fp8_bt_plan_ws(M, N, K, 0x100000, lda, 0x200000000000, ldbt, None, 2, 0x400000000000, ldc,
+                                       FMTS[fmt], 1 << 30)
+        assert p["path"] == gr.GR_PATH_TILE_SPLIT and p["split_k"] > 1, p
+    A, Bt = synth.fp8_operands(M, N, K, seed=M + N + K + 7, lda=lda, ldbt=ldbt)
+    sa, sb = 0.125, 2.0 / np.sqrt(K)
+    bias = bias_for(N, fmt, 9)
+    Cflat = run_ws(A, Bt, M, N, K, lda, ldbt, ldc, sa, sb, bias, "gelu", fmt, path)
+    C = Cflat[:M * ldc].reshape(M, ldc)
+    ref = oracle.gemm_fp8_bt_full(A, Bt, sa, sb, fmt, bias, "gelu", M=M, N=N, K=K, lda=lda, ldbt=ldbt)
+    assert_parity(C[:, :N], ref, "fp8 split %s %s" % (what, fmt), fmt=fmt)
+    assert np.all(C[:, N:] == SENTINEL) and np.all(Cflat[M * ldc:] == SENTINEL)
+
+
+@pytest.mark.parametrize("act", list(gr.ACT_CODES))
+def test_fp8_split_every_activation(act):
+    M, N, K = 200, 300, 4096
+    A, Bt = synth.fp8_operands(M, N, K, seed=81)
+    sa, sb = 0.25, 1.0 / 16
+    bias = bias_for(N, "f16", 8) if act != "relu" else None
+    C = run_ws(A, Bt, M, N, K, K, K, N, sa, sb, bias, act, "f16", gr.GR_PATH_TILE_SPLIT)[:M * N].reshape(M, N)
+    assert_parity(C, oracle.gemm_fp8_bt_full(A, Bt, sa, sb, "f16", bias, act), "fp8 split %s" % act)
+
+
+def test_fp8_split_mid_m_sampled():
+    """128 x 8192 x 8192 (64 tiles, 8 splits): the planner's split on the
+    shape it is for, sampled against the oracle, and against the unsplit
+    kernel within the tolerance."""
+    M, N, K = 128, 8192, 8192
+    A, Bt = synth.fp8_operands(M, N, K, seed=91)
+    sa, sb = 1.0 / 16, 1.0 / 16
+    st, p = gr.gemm_fp8_bt_plan_ws(M, N, K, 0x100000, K, 0x200000000000, K, None, 1, 0x400000000000, N, 0, 1 << 30)
+    assert p["path"] == gr.GR_PATH_TILE_SPLIT
+    C = run_ws(A, Bt, M, N, K, K, K, N, sa, sb, None, "relu", "f16")[:M * N].reshape(M, N)
+    ii, jj = synth.sample_indices(M, N, 4096, 91)
+    assert_parity(C[ii, jj], oracle.gemm_fp8_bt_elems(A, Bt, ii, jj, sa, sb), "fp8 split 128x8192x8192 sampled")
+    for r in (0, 127):
+        jj = np.arange(N)
+        assert_parity(C[r, :], oracle.gemm_fp8_bt_elems(A, Bt, np.full(N, r), jj, sa, sb), "row %d" % r)
+    C1 = run(A, Bt, M, N, K, K, K, N, sa, sb)[:M * N].reshape(M, N)
+    assert_parity(C, C1, "split vs unsplit")
+
+
+def test_fp8_split_workspace_reuse_and_wrapper():
+    """Two calls in a row on one workspace (the second smaller), then the
+    tensor helper with its own workspace."""
+    t = pytest.importorskip("torch")
+    ws = t.empty(64 << 20, dtype=t.uint8, device="cuda")
+    for (M, N, K) in ((256, 1024, 8192), (100, 300, 2048)):
+        A, Bt = synth.fp8_operands(M, N, K, seed=M)
+        dA, dB = dev8(A), dev8(Bt)
+        dC = full_dev((M * N,), SENTINEL)
+        st = gr.gemm_fp8_bt_ws(M, N, K, dA.data_ptr(), K, dB.data_ptr(), K, 0.5, 0.25, None, gr.GR_ACT_RELU,
+                               dC.data_ptr(), N, gr.GR_FMT_F16, ws.data_ptr(), ws.numel(),
+                               t.cuda.current_stream().cuda_stream, gr.GR_PATH_TILE_SPLIT)
+        t.cuda.synchronize()
+        assert st == gr.GR_OK
+        assert_parity(from_dev(dC).reshape(M, N), oracle.gemm_fp8_bt_full(A, Bt, 0.5, 0.25), "reuse %d" % M)
+    M, N, K = 300, 270, 8192
+    A, Bt = synth.fp8_operands(M, N, K, seed=95)
+    c = gr.gemm_fp8(dev8(A).view(t.float8_e4m3fn), dev8(Bt).view(t.float8_e4m3fn), 0.5, 1.0 / 64, act="silu")
+    t.cuda.synchronize()
+    assert_parity(c.view(t.int16).cpu().numpy().view(np.uint16),
+                  oracle.gemm_fp8_bt_full(A, Bt, 0.5, 1.0 / 64, act="silu"), "fp8 wrapper split")
