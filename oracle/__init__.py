@@ -98,6 +98,13 @@ def _load():
             lib.oracle_gemm_fp8_bt_full.restype = ci
             lib.oracle_gemm_fp8_bt_elems.argtypes = [ci, p, ci, f32, f32, i64, i64, i64, p, i64, p, i64, p, p, i64, p]
             lib.oracle_gemm_fp8_bt_elems.restype = ci
+            lib.oracle_e8m0_to_f64_array.argtypes = [p, p, i64]
+            lib.oracle_e8m0_to_f64_array.restype = None
+            lib.oracle_gemm_mxfp8_bt_full.argtypes = [ci, p, ci, i64, i64, i64, p, i64, p, i64, p, i64, p, i64, p, i64]
+            lib.oracle_gemm_mxfp8_bt_full.restype = ci
+            lib.oracle_gemm_mxfp8_bt_elems.argtypes = [ci, p, ci, i64, i64, i64, p, i64, p, i64, p, i64, p, i64, p, p,
+                                                       i64, p]
+            lib.oracle_gemm_mxfp8_bt_elems.restype = ci
             _lib = lib
     return _lib
 
@@ -340,4 +347,63 @@ def gemm_fp8_bt_elems(A, Bt, ii, jj, scale_a=1.0, scale_b=1.0, fmt="f16", bias=N
     if i.size:
         lib.oracle_gemm_fp8_bt_elems(_FMTS.index(fmt), bptr, ACTS[act], scale_a, scale_b, M, N, K, _ptr(A), lda,
                                      _ptr(Bt), ldbt, _ptr(i), _ptr(j), i.size, _ptr(out))
+    return out
+
+
+def e8m0_to_f64(bits: np.ndarray) -> np.ndarray:
+    """Element-wise OCP MX E8M0 scale -> float64 (2^(x-127); 255 -> NaN) through the oracle."""
+    lib = _load()
+    flat = np.ascontiguousarray(bits, dtype=np.uint8).ravel()
+    out = np.empty(flat.size, dtype=np.float64)
+    lib.oracle_e8m0_to_f64_array(_ptr(flat), _ptr(out), flat.size)
+    return out.reshape(np.shape(bits))
+
+
+def _mx_args(A, SA, Bt, SB, bias, act, fmt, M, N, K, lda, ldsa, ldbt, ldsb):
+    M, N, K, lda, ldbt, bptr = _fp8_args(A, Bt, bias, act, fmt, M, N, K, lda, ldbt)
+    if K % 32:
+        raise ValueError("K must be a multiple of the 32-element block")
+    if SA.dtype != np.uint8 or SB.dtype != np.uint8 or not (SA.flags.c_contiguous and SB.flags.c_contiguous):
+        raise TypeError("scales must be C-contiguous uint8 arrays of E8M0 codes")
+    kb = K // 32
+    ldsa = kb if ldsa is None else int(ldsa)
+    ldsb = kb if ldsb is None else int(ldsb)
+    if kb and ((M and SA.size < (M - 1) * ldsa + kb) or (N and SB.size < (N - 1) * ldsb + kb)):
+        raise ValueError("scale arrays too small")
+    return M, N, K, lda, ldbt, bptr, ldsa, ldsb
+
+
+def gemm_mxfp8_bt_full(A, SA, Bt, SB, fmt="f16", bias=None, act="relu", M=None, N=None, K=None, lda=None,
+                       ldsa=None, ldbt=None, ldsb=None, threads=None):
+    """act(sum_k A[i,k] 2^(SA[i,k/32]-127) Bt[j,k] 2^(SB[j,k/32]-127) + bias) as fp16 (or bf16) bits."""
+    M, N, K, lda, ldbt, bptr, ldsa, ldsb = _mx_args(A, SA, Bt, SB, bias, act, fmt, M, N, K, lda, ldsa, ldbt, ldsb)
+    lib = _load()
+    if threads:
+        lib.oracle_set_threads(int(threads))
+    C = np.zeros((M, N), dtype=np.uint16)
+    if M > 0 and N > 0:
+        st = lib.oracle_gemm_mxfp8_bt_full(_FMTS.index(fmt), bptr, ACTS[act], M, N, K, _ptr(A), lda, _ptr(SA), ldsa,
+                                           _ptr(Bt), ldbt, _ptr(SB), ldsb, _ptr(C), N)
+        assert st == 0
+    return C
+
+
+def gemm_mxfp8_bt_elems(A, SA, Bt, SB, ii, jj, fmt="f16", bias=None, act="relu", M=None, N=None, K=None, lda=None,
+                        ldsa=None, ldbt=None, ldsb=None, threads=None):
+    """Single elements C[ii[e], jj[e]] of gemm_mxfp8_bt_full."""
+    M, N, K, lda, ldbt, bptr, ldsa, ldsb = _mx_args(A, SA, Bt, SB, bias, act, fmt, M, N, K, lda, ldsa, ldbt, ldsb)
+    i = np.ascontiguousarray(ii, dtype=np.int64)
+    j = np.ascontiguousarray(jj, dtype=np.int64)
+    if i.shape != j.shape:
+        raise ValueError("index arrays differ in length")
+    if i.size and (i.min() < 0 or i.max() >= M or j.min() < 0 or j.max() >= N):
+        raise IndexError("element index out of range")
+    lib = _load()
+    if threads:
+        lib.oracle_set_threads(int(threads))
+    out = np.zeros(i.size, dtype=np.uint16)
+    if i.size:
+        st = lib.oracle_gemm_mxfp8_bt_elems(_FMTS.index(fmt), bptr, ACTS[act], M, N, K, _ptr(A), lda, _ptr(SA), ldsa,
+                                            _ptr(Bt), ldbt, _ptr(SB), ldsb, _ptr(i), _ptr(j), i.size, _ptr(out))
+        assert st == 0
     return out

@@ -61,6 +61,16 @@
  * exact); then x = fl32(acc * s) with s = fl32(scale_a * scale_b), the
  * per-tensor dequantisation scales, and steps 3' and 4' as above.
  *
+ * The *_mxfp8_* entry points take the same E4M3 operands in OCP MX form:
+ * every run of 32 consecutive k of a row of A (of Bt) shares one E8M0 scale
+ * (8 exponent bits, value 2^(x - 127); x = 255 is NaN), sa[i][k/32] and
+ * sb[j][k/32].  Each product is a[i][k] * 2^(sa - 127) * bt[j][k] * 2^(sb -
+ * 127), formed exactly in double and converted to fp32 (exact while it stays
+ * in the fp32 range, as in the tests), then added in fp32, k increasing; then
+ * steps 3' and 4' with no further scale.  The pages point to block-scaled
+ * GEMMs (per-block scales on quantised operands) as examples; MX is the
+ * block format the gfx950 matrix cores scale in hardware.
+ *
  * The single rounding from double goes through fp32 with round-to-odd (the
  * nearest fp32 toward zero with its last bit forced to 1 when inexact), which
  * keeps two or more spare bits over the fp16 and bfloat16 significands, so
@@ -509,5 +519,63 @@ int oracle_gemm_fp8_bt_elems(int fmt, const uint16_t* bias, int act, float scale
     const Epi ep = {bias, act, scale_a * scale_b};
 #pragma omp parallel for schedule(static)
     for (int64_t e = 0; e < n; ++e) out[e] = fp8_element(fmt, &ep, ii[e], jj[e], K, A, lda, Bt, ldbt);
+    return 0;
+}
+
+/* ---- MX fp8: E4M3 elements with one E8M0 scale per 32 consecutive k --------- */
+
+/* E8M0: 2^(x - 127) for x = 0 .. 254 (2^-127 .. 2^127), NaN for 255. */
+double oracle_e8m0_to_f64(uint8_t x) {
+    if (x == 255u) return NAN;
+    return ldexp(1.0, (int)x - 127);
+}
+
+void oracle_e8m0_to_f64_array(const uint8_t* in, double* out, int64_t n) {
+    for (int64_t e = 0; e < n; ++e) out[e] = oracle_e8m0_to_f64(in[e]);
+}
+
+/* One output element of the MX product: scaled products formed exactly in
+   double, converted to fp32, added in fp32 in increasing k. */
+static uint16_t mx_element(int fmt, const Epi* ep, int64_t i, int64_t j, int64_t K, const uint8_t* A, int64_t lda,
+                           const uint8_t* SA, int64_t ldsa, const uint8_t* Bt, int64_t ldbt, const uint8_t* SB,
+                           int64_t ldsb) {
+    float acc = 0.0f;
+    for (int64_t k = 0; k < K; ++k) {
+        const double a = (double)oracle_e4m3_to_f32(A[i * lda + k]) * oracle_e8m0_to_f64(SA[i * ldsa + k / 32]);
+        const double b = (double)oracle_e4m3_to_f32(Bt[j * ldbt + k]) * oracle_e8m0_to_f64(SB[j * ldsb + k / 32]);
+        acc = acc + (float)(a * b);
+    }
+    return epilogue(fmt, ep, j, acc);
+}
+
+/* C[i*ldc + j] for all i < M, j < N.  K is a multiple of 32; SA is M x K/32
+   (pitch ldsa), SB is N x K/32 (pitch ldsb).  Returns -2 for an unknown
+   format or activation, -3 when K is not a multiple of 32. */
+int oracle_gemm_mxfp8_bt_full(int fmt, const uint16_t* bias, int act, int64_t M, int64_t N, int64_t K,
+                              const uint8_t* A, int64_t lda, const uint8_t* SA, int64_t ldsa, const uint8_t* Bt,
+                              int64_t ldbt, const uint8_t* SB, int64_t ldsb, uint16_t* C, int64_t ldc) {
+    if (!epi_check(fmt, act)) return -2;
+    if (K % 32 != 0) return -3;
+    const Epi ep = {bias, act, 1.0f};
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t i = 0; i < M; ++i)
+        for (int64_t j = 0; j < N; ++j)
+            C[i * ldc + j] = mx_element(fmt, &ep, i, j, K, A, lda, SA, ldsa, Bt, ldbt, SB, ldsb);
+    return 0;
+}
+
+/* Single elements: out[e] = C[ii[e]][jj[e]]. */
+int oracle_gemm_mxfp8_bt_elems(int fmt, const uint16_t* bias, int act, int64_t M, int64_t N, int64_t K,
+                               const uint8_t* A, int64_t lda, const uint8_t* SA, int64_t ldsa, const uint8_t* Bt,
+                               int64_t ldbt, const uint8_t* SB, int64_t ldsb, const int64_t* ii, const int64_t* jj,
+                               int64_t n, uint16_t* out) {
+    (void)M;
+    (void)N;
+    if (!epi_check(fmt, act)) return -2;
+    if (K % 32 != 0) return -3;
+    const Epi ep = {bias, act, 1.0f};
+#pragma omp parallel for schedule(static)
+    for (int64_t e = 0; e < n; ++e)
+        out[e] = mx_element(fmt, &ep, ii[e], jj[e], K, A, lda, SA, ldsa, Bt, ldbt, SB, ldsb);
     return 0;
 }
