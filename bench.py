@@ -205,11 +205,19 @@ def bench_workload(gr, torch, w, reps, cold):
             times.append(t[0])
     else:
         times = time_launches(torch, runs[0], stream, reps)
-    del A, Bs, C, ws, runs
+    del A, Bs, C, runs
+    torch.cuda.empty_cache()
+    flushed = None if cold else bench_flushed(gr, torch, w, reps, ws)
+    del ws
     torch.cuda.empty_cache()
     times.sort()
     med = statistics.median(times)
     flops, nbytes = algorithmic(w)
+    extra = {}
+    if flushed is not None:
+        fmed = statistics.median(flushed)
+        extra = {"flushed_median_us": round(fmed * 1e3, 2), "flushed_tflops": round(flops / (fmed * 1e-3) / 1e12, 1),
+                 "flushed_pairs": flush_pairs(w)}
     return {
         "median_us": round(med * 1e3, 2),
         "min_us": round(times[0] * 1e3, 2),
@@ -222,7 +230,40 @@ def bench_workload(gr, torch, w, reps, cold):
         "reps": reps,
         "path": plan["path_name"],
         "workspace_bytes": plan["workspace"],
+        **extra,
     }
+
+
+def flush_pairs(w):
+    """Operand pairs rotated for the flushed timing: enough that the pairs
+    together hold at least 512 MiB, twice the 256 MB last-level cache."""
+    pair = 2 * (w.M * w.K + w.K * w.N)
+    return max(2, min(128, -(-(512 << 20) // pair)))
+
+
+def bench_flushed(gr, torch, w, reps, ws):
+    """Per-launch times with A and B evicted from every cache: each launch
+    reads its own copy of both operands, rotating over flush_pairs(w) copies.
+    No flush buffer is written (its write-back would land in the timed
+    launch)."""
+    n = flush_pairs(w)
+    g = torch.Generator(device="cuda").manual_seed(w.seed)
+    pairs = []
+    for _ in range(n):
+        a = torch.randn(w.M, w.K, generator=g, device="cuda", dtype=torch.float32).half()
+        b = torch.randn(w.K, w.N, generator=g, device="cuda", dtype=torch.float32)
+        if w.b_scaled:
+            b.mul_(w.K ** -0.5)
+        pairs.append((a, b.half()))
+    C = torch.empty(w.M, w.N, device="cuda", dtype=torch.float16)
+    stream = torch.cuda.current_stream()
+    runs = [launcher(gr, torch, w, a, b, C, stream, ws) for a, b in pairs]
+    for r in runs:
+        r()
+    torch.cuda.synchronize()
+    times = [time_launches(torch, runs[i % n], stream, 1)[0] for i in range(reps)]
+    del pairs, runs, C
+    return times
 
 
 def copy_probe(torch, mib):
@@ -283,6 +324,9 @@ EXTRA_SHAPES = [
     ("fp8 e4m3, MLP projection", 8192, 28672, 8192, "fp8"),
     ("fp8 e4m3, mid-M", 128, 8192, 8192, "fp8"),
     ("fp8 e4m3, long K, few tiles", 1024, 1024, 8192, "fp8"),
+    ("MX fp8 (E8M0 scale per 32 k), square", 4096, 4096, 4096, "mxfp8"),
+    ("MX fp8, square 8192", 8192, 8192, 8192, "mxfp8"),
+    ("MX fp8, MLP projection", 8192, 28672, 8192, "mxfp8"),
 ]
 
 
@@ -300,7 +344,22 @@ def extra_shapes(gr, torch, reps=30):
         C = torch.empty(M, N, device="cuda", dtype=dt)
         row = {"shape": "%dx%dx%d" % (M, N, K), "what": label, "layout": layout}
         runs = {}
-        if layout == "fp8":
+        if layout == "mxfp8":
+            A8 = torch.randn(M, K, generator=g, device="cuda").to(torch.float8_e4m3fn)
+            Bt8 = torch.randn(N, K, generator=g, device="cuda").to(torch.float8_e4m3fn)
+            sa8 = torch.randint(124, 130, (M, K // 32), generator=g, device="cuda", dtype=torch.int32).to(torch.uint8)
+            sb8 = torch.randint(124, 130, (N, K // 32), generator=g, device="cuda", dtype=torch.int32).to(torch.uint8)
+            runs["ours"] = lambda: gr.gemm_mxfp8(A8, sa8, Bt8, sb8, act="relu", out=C, stream=stream)
+
+            def vendor_mx():
+                return torch.relu_(torch._scaled_mm(A8, Bt8.t(), scale_a=sa8.view(torch.float8_e8m0fnu),
+                                                    scale_b=sb8.view(torch.float8_e8m0fnu), out_dtype=torch.float16))
+            try:
+                vendor_mx()
+                runs["vendor"] = vendor_mx
+            except Exception as e:  # the vendor MX path may be missing
+                row["vendor_error"] = str(e)[:120]
+        elif layout == "fp8":
             A8 = torch.randn(M, K, generator=g, device="cuda").to(torch.float8_e4m3fn)
             Bt8 = torch.randn(N, K, generator=g, device="cuda").to(torch.float8_e4m3fn)
             sa, sb = 1.0 / 64, 1.0 / 64

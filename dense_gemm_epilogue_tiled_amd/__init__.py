@@ -155,6 +155,14 @@ def lib() -> ctypes.CDLL:
             l.gemm_fp8_bt_plan_ws.argtypes = [i64, i64, i64, p, i64, p, i64, p, i32, p, i64, i32, i64,
                                               ctypes.POINTER(gr_plan_t)]
             l.gemm_fp8_bt_plan_ws.restype = i32
+            l.gemm_mxfp8_bt.argtypes = [i64, i64, i64, p, i64, p, i64, p, i64, p, i64, p, i32, p, i64, i32, p]
+            l.gemm_mxfp8_bt.restype = i32
+            l.gemm_mxfp8_bt_forced.argtypes = [i64, i64, i64, p, i64, p, i64, p, i64, p, i64, p, i32, p, i64, i32, p,
+                                               i32]
+            l.gemm_mxfp8_bt_forced.restype = i32
+            l.gemm_mxfp8_bt_plan.argtypes = [i64, i64, i64, p, i64, p, i64, p, i64, p, i64, p, i32, p, i64, i32,
+                                             ctypes.POINTER(gr_plan_t)]
+            l.gemm_mxfp8_bt_plan.restype = i32
             l.gemm_relu_status_string.argtypes = [i32]
             l.gemm_relu_status_string.restype = ctypes.c_char_p
             l.gemm_relu_version.argtypes = []
@@ -319,6 +327,26 @@ def gemm_fp8_bt_plan_ws(M, N, K, A, lda, Bt, ldbt, bias, act, C, ldc, out_fmt, w
     plan = gr_plan_t()
     st = lib().gemm_fp8_bt_plan_ws(M, N, K, _ptr(A), lda, _ptr(Bt), ldbt, _ptr(bias), act, _ptr(C), ldc, out_fmt,
                                    workspace_bytes, ctypes.byref(plan))
+    return st, _plan_dict(plan)
+
+
+def gemm_mxfp8_bt(M, N, K, A, lda, SA, ld_sa, Bt, ldbt, SB, ld_sb, bias, act, C, ldc, out_fmt=GR_FMT_F16,
+                  stream=None) -> int:
+    """C := act(A~ . Bt~^T + bias): E4M3 operands, one E8M0 scale per 32 k of each row (device pointers)."""
+    return lib().gemm_mxfp8_bt(M, N, K, _ptr(A), lda, _ptr(SA), ld_sa, _ptr(Bt), ldbt, _ptr(SB), ld_sb, _ptr(bias),
+                               act, _ptr(C), ldc, out_fmt, _ptr(stream))
+
+
+def gemm_mxfp8_bt_forced(M, N, K, A, lda, SA, ld_sa, Bt, ldbt, SB, ld_sb, bias, act, C, ldc, out_fmt=GR_FMT_F16,
+                         stream=None, path=GR_PATH_TILE_EDGE) -> int:
+    return lib().gemm_mxfp8_bt_forced(M, N, K, _ptr(A), lda, _ptr(SA), ld_sa, _ptr(Bt), ldbt, _ptr(SB), ld_sb,
+                                      _ptr(bias), act, _ptr(C), ldc, out_fmt, _ptr(stream), path)
+
+
+def gemm_mxfp8_bt_plan(M, N, K, A, lda, SA, ld_sa, Bt, ldbt, SB, ld_sb, bias, act, C, ldc, out_fmt=GR_FMT_F16):
+    plan = gr_plan_t()
+    st = lib().gemm_mxfp8_bt_plan(M, N, K, _ptr(A), lda, _ptr(SA), ld_sa, _ptr(Bt), ldbt, _ptr(SB), ld_sb,
+                                  _ptr(bias), act, _ptr(C), ldc, out_fmt, ctypes.byref(plan))
     return st, _plan_dict(plan)
 
 
@@ -520,4 +548,53 @@ def gemm_fp8(a, bt, scale_a=1.0, scale_b=1.0, bias=None, act="relu", out_dtype=N
                         out.data_ptr(), ldc, fmt, ws_ptr, ws_bytes, _stream_handle(stream), -1 if path is None else path)
     if st != GR_OK:
         raise GemmReluError(st, "gemm_fp8_bt_ws")
+    return out
+
+
+def gemm_mxfp8(a, scale_a, bt, scale_b, bias=None, act="relu", out_dtype=None, out=None, stream=None, path=None):
+    """Tensor convenience for the MX (block-scaled) fp8 product:
+    ``out = act((a * 2^(scale_a - 127)) @ (bt * 2^(scale_b - 127)).T + bias)``
+    with ``a`` (M x K) and ``bt`` (N x K) torch.float8_e4m3fn tensors and
+    ``scale_a`` (M x K/32), ``scale_b`` (N x K/32) uint8 E8M0 codes (each
+    expanded over its 32 consecutive k), all on the GPU with unit column
+    stride; fp16 or bfloat16 output as for gemm_fp8."""
+    import torch
+    if a.dtype != torch.float8_e4m3fn or bt.dtype != torch.float8_e4m3fn:
+        raise TypeError("a and bt must be torch.float8_e4m3fn")
+    if scale_a.dtype != torch.uint8 or scale_b.dtype != torch.uint8:
+        raise TypeError("scales must be uint8 E8M0 codes")
+    if a.dim() != 2 or bt.dim() != 2 or a.shape[1] != bt.shape[1]:
+        raise ValueError("shapes do not form a product: %s x %s^T" % (tuple(a.shape), tuple(bt.shape)))
+    M, K = a.shape
+    N = bt.shape[0]
+    if K % 32:
+        raise ValueError("K must be a multiple of 32")
+    if scale_a.dim() != 2 or tuple(scale_a.shape) != (M, K // 32) or tuple(scale_b.shape) != (N, K // 32):
+        raise ValueError("scales must be M x K/32 and N x K/32")
+    if out is not None:
+        out_dtype = out.dtype
+    out_dtype = torch.float16 if out_dtype is None else out_dtype
+    if out_dtype not in (torch.float16, torch.bfloat16):
+        raise TypeError("the output is float16 or bfloat16")
+    fmt = GR_FMT_BF16 if out_dtype == torch.bfloat16 else GR_FMT_F16
+    if bias is not None and (bias.dtype != out_dtype or bias.dim() != 1 or bias.shape[0] != N or
+                             (N > 1 and bias.stride(0) != 1)):
+        raise ValueError("bias must be a contiguous 1-D tensor of N values of the output dtype")
+    if out is None:
+        out = torch.empty((M, N), dtype=out_dtype, device=a.device)
+    for t in (a, bt, scale_a, scale_b, out):
+        if t.numel() and t.stride(1) != 1:
+            raise ValueError("tensors need unit column stride")
+    lda = max(a.stride(0), 1) if M > 1 else max(K, 1)
+    ldbt = max(bt.stride(0), 1) if N > 1 else max(K, 1)
+    ldsa = max(scale_a.stride(0), 1) if M > 1 else max(K // 32, 1)
+    ldsb = max(scale_b.stride(0), 1) if N > 1 else max(K // 32, 1)
+    ldc = max(out.stride(0), 1) if M > 1 else max(N, 1)
+    code = ACT_CODES[act] if isinstance(act, str) else int(act)
+    bptr = bias.data_ptr() if bias is not None and bias.numel() else None
+    args = (M, N, K, a.data_ptr(), lda, scale_a.data_ptr(), ldsa, bt.data_ptr(), ldbt, scale_b.data_ptr(), ldsb, bptr,
+            code, out.data_ptr(), ldc, fmt, _stream_handle(stream))
+    st = gemm_mxfp8_bt(*args) if path is None else gemm_mxfp8_bt_forced(*args, path)
+    if st != GR_OK:
+        raise GemmReluError(st, "gemm_mxfp8_bt")
     return out

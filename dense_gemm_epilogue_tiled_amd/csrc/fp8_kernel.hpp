@@ -6,11 +6,12 @@
 //
 // Operand layout.  Each lane supplies 32 bytes (8 VGPRs) per operand: the 32
 // rows of a block are the lanes mod 32, and the two lane halves split the 64
-// k of the step.  Which k a given byte position stands for inside the
-// instruction does not matter here: A and B use the same positions for the
-// same k, so filling both operands by one rule -- lane half h gets the two
-// 16-byte chunks h and 2 + h (chunk 2s + h, s = 0, 1) of its row's 64-byte k
-// strip -- pairs every A[m][k] with B[k][n] exactly once.  The output block follows the usual
+// k of the step.  Without scales, which k a given byte position stands for
+// inside the instruction does not matter: A and B use the same positions
+// for the same k, so filling both operands by one rule -- lane half h gets
+// the two 16-byte chunks h and 2 + h (chunk 2s + h, s = 0, 1) of its row's
+// 64-byte k strip -- pairs every A[m][k] with B[k][n] exactly once.  (With
+// MX scales it does matter; see below.)  The output block follows the usual
 // 32 x 32 MFMA layout; B goes in as the first operand, so each lane ends with
 // 4 consecutive columns of one row of C (as in the fp16 kernels).
 //
@@ -23,6 +24,16 @@
 // A and Bt past M and N read row M-1 and N-1 (their results are never
 // stored), so any M and N work; K must be a multiple of 64 and rows 16-byte
 // aligned.
+// MX=true (OCP MX fp8: one E8M0 scale per 32 consecutive k of every row of
+// A and Bt): here the k order inside the instruction matters.  The
+// assignment above is the instruction's own (register quad s of lane half h
+// holds k 32s + 16h .. 32s + 16h + 15 of the step), and the scale byte of
+// lane (h, row) multiplies that row's 32-k block h, i.e. quad h of both lane
+// halves; so the operands are fetched exactly as without scales, and lane
+// half h supplies the scale of block 2kt + h of its row (measured: per-row
+// and per-block scales both match the oracle only with this pairing).  The
+// scales travel through LDS beside the ring: 4 bytes of each row (the blocks
+// of two strips) per copy, with the copies of every even strip.
 // gemm_fp8_smallm_kernel: M <= 16, a bandwidth-bound stream over Bt.
 // gemm_fp8_guarded_kernel: every other shape (any K, any alignment), operands
 // loaded straight into registers with bounds checks, out-of-range bytes 0.
@@ -46,6 +57,27 @@ __device__ __forceinline__ f32x16 mfma(const u32x4& b0, const u32x4& b1, const u
     const i32x8 bo = {(int)b0[0], (int)b0[1], (int)b0[2], (int)b0[3], (int)b1[0], (int)b1[1], (int)b1[2], (int)b1[3]};
     const i32x8 ao = {(int)a0[0], (int)a0[1], (int)a0[2], (int)a0[3], (int)a1[0], (int)a1[1], (int)a1[2], (int)a1[3]};
     return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(bo, ao, c, 0, 0, 0, 0, 0, 0);
+}
+
+// The same block product with E8M0 scales: lane l scales the 32 bytes of
+// its B operand by 2^(sb - 127) and those of its A operand by 2^(sa - 127)
+// (the low byte of each scale word).
+__device__ __forceinline__ f32x16 mfma_mx(const u32x4& b0, const u32x4& b1, const u32x4& a0, const u32x4& a1,
+                                          f32x16 c, uint32_t sb, uint32_t sa) {
+    const i32x8 bo = {(int)b0[0], (int)b0[1], (int)b0[2], (int)b0[3], (int)b1[0], (int)b1[1], (int)b1[2], (int)b1[3]};
+    const i32x8 ao = {(int)a0[0], (int)a0[1], (int)a0[2], (int)a0[3], (int)a1[0], (int)a1[1], (int)a1[2], (int)a1[3]};
+    return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(bo, ao, c, 0, 0, 0, (int)sb, 0, (int)sa);
+}
+
+// Copy of 4 bytes per lane from global memory into LDS (lane l writes LDS
+// bytes [m0 + 4l, m0 + 4l + 4)); waits as for tile2::dma16.
+__device__ __forceinline__ void dma4(const void* base, uint32_t voff, uint32_t lds_addr) {
+    asm volatile(
+        "s_nop 0\n\t"
+        "global_load_lds_dword %0, %1"
+        :
+        : "v"(voff), "s"(base), "{m0}"(lds_addr)
+        : "memory");
 }
 
 constexpr int BK = 64;  // k per strip (bytes)
@@ -74,6 +106,14 @@ struct Tile {
     static constexpr int REGION = epi::WaveTile<FM, FN>::REGION_BYTES;
     static constexpr int MIN_WAVES = BMT == 256 ? 1 : 2;       // workgroups per CU
     static_assert(LDS_BYTES >= 4 * REGION, "the epilogue stages four wave tiles in LDS");
+    // MX scales: slot q % SC_SLOTS holds 4 bytes (the E8M0 scales of strips
+    // 2q and 2q + 1) of every A row, then of every Bt row, after the ring.
+    static constexpr int SC_SLOTS = 4;
+    static constexpr int SC_SLOT_BYTES = (BM + BN) * 4;
+    static constexpr int SC_BASE = LDS_BYTES;
+    static constexpr int LDS_BYTES_MX = LDS_BYTES + SC_SLOTS * SC_SLOT_BYTES;  // 136 or 68 KiB
+    static constexpr int SC_COPIES = (BM + BN) / 256;  // 64-row scale copies per wave per even strip
+    static_assert(BM % 64 == 0 && (SC_COPIES * THREADS / 64) * 64 == BM + BN, "scale copies cover every row");
 };
 
 __device__ __forceinline__ u32x4 read16(const GR_LDS uint8_t* p) { return *(const GR_LDS u32x4*)p; }
@@ -84,21 +124,26 @@ __device__ __forceinline__ u32x4 read16(const GR_LDS uint8_t* p) { return *(cons
 // over the K range of split g / tiles (k_per_split bytes, a multiple of 64;
 // no split is empty) and writes its unscaled fp32 sums to part[split][m][n];
 // a second pass adds the splits in order and applies the epilogue.
-template <int BMT, bool EDGE, typename E, bool SPLIT = false>
+// MX=true: SA (M x K/32, pitch ldsa) and SB (N x K/32, pitch ldsb) hold the
+// E8M0 scales; K a multiple of 128, scale rows 4-byte aligned.
+template <int BMT, bool EDGE, typename E, bool SPLIT = false, bool MX = false>
 __global__ __launch_bounds__(THREADS, Tile<BMT>::MIN_WAVES) void gemm_fp8_tile_kernel(
     const uint8_t* __restrict__ A, const uint8_t* __restrict__ Bt, uint16_t* __restrict__ C, int64_t M, int64_t N,
     int64_t K, int64_t lda, int64_t ldb, int64_t ldc, uint32_t tiles_m, uint32_t tiles_n, uint32_t group_m,
-    int vec_c, float* __restrict__ part, int64_t k_per_split, EpiArgs ep) {
+    int vec_c, float* __restrict__ part, int64_t k_per_split, const uint8_t* __restrict__ SA, int64_t ldsa,
+    const uint8_t* __restrict__ SB, int64_t ldsb, EpiArgs ep) {
     static_assert(E::kGeneral, "the fp8 kernels use the general epilogue");
+    static_assert(!(MX && SPLIT), "the MX path has no split-K variant");
     using T = Tile<BMT>;
     constexpr int FM = T::FM, FN = T::FN, COPIES = T::COPIES;
+    constexpr int SC_COPIES = MX ? T::SC_COPIES : 0;
     using tile2::a_off;
     using tile2::barrier;
     using tile2::dma16;
     using tile2::pin;
     using tile2::wait_vmcnt;
 
-    __shared__ __attribute__((aligned(1024))) uint8_t lds[T::LDS_BYTES];
+    __shared__ __attribute__((aligned(1024))) uint8_t lds[MX ? T::LDS_BYTES_MX : T::LDS_BYTES];
 
     const uint32_t tid = threadIdx.x;
     const uint32_t lane = tid & 63u;
@@ -150,13 +195,46 @@ __global__ __launch_bounds__(THREADS, Tile<BMT>::MIN_WAVES) void gemm_fp8_tile_k
             dma16(base_b + (int64_t)kt * BK, off_b[i],
                   lds_base + slot * T::STAGE_BYTES + T::A_BYTES + blk * 1024u);
     };
+    // MX scale copy c of this wave: scale rows R = 64 (SC_COPIES w + c) +
+    // lane of the slot (A rows 0 .. BM-1, then Bt rows); a copy never mixes
+    // the two (64-row groups), so its base address is wave-uniform.
+    const uint8_t* base_s[SC_COPIES > 0 ? SC_COPIES : 1];
+    uint32_t off_s[SC_COPIES > 0 ? SC_COPIES : 1];
+    if constexpr (MX) {
+#pragma unroll
+        for (int c = 0; c < SC_COPIES; ++c) {
+            const uint32_t g0 = 64u * ((uint32_t)SC_COPIES * wave + (uint32_t)c);  // first row of the group
+            const bool is_a = g0 < (uint32_t)T::BM;
+            uint32_t r = (is_a ? g0 : g0 - (uint32_t)T::BM) + lane;
+            if constexpr (EDGE) {
+                if (is_a) r = m0 + r < M ? r : (uint32_t)(M - 1 - m0);
+                else r = n0 + r < N ? r : (uint32_t)(N - 1 - n0);
+            }
+            base_s[c] = is_a ? SA + m0 * ldsa : SB + n0 * ldsb;
+            off_s[c] = (uint32_t)(r * (is_a ? ldsa : ldsb));
+        }
+    }
+    // Scale copies of strip kt (even): the blocks of strips kt, kt + 1.
+    auto dma_scale = [&](uint32_t kt, int c) {
+        if constexpr (MX) {
+            const uint32_t q = kt >> 1;
+            dma4(base_s[c] + 4 * (int64_t)q, off_s[c],
+                 lds_base + T::SC_BASE + (q % T::SC_SLOTS) * T::SC_SLOT_BYTES +
+                     256u * ((uint32_t)SC_COPIES * wave + (uint32_t)c));
+        }
+    };
     auto issue = [&](uint32_t slot, uint32_t kt) {
 #pragma unroll
         for (int c = 0; c < 2 * COPIES; ++c) dma_one(slot, kt, c);
+        if (MX && (kt & 1u) == 0u) {
+#pragma unroll
+            for (int c = 0; c < SC_COPIES; ++c) dma_scale(kt, c);
+        }
     };
 
     // ---- fragment addresses: row wm*WAVE_T + 32i + lane%32 (A) or
-    // wn*WAVE_T + 32j + lane%32 (Bt), chunk 2s + lane/32; block i or j is 2 KiB on.
+    // wn*WAVE_T + 32j + lane%32 (Bt), chunk 2s + lane/32; block i or j is
+    // 2 KiB on.
     const GR_LDS uint8_t* lds_p = (const GR_LDS uint8_t*)lds;
     const uint32_t ar = wm * T::WAVE_T + (lane & 31u);
     const uint32_t br = wn * T::WAVE_T + (lane & 31u);
@@ -164,13 +242,20 @@ __global__ __launch_bounds__(THREADS, Tile<BMT>::MIN_WAVES) void gemm_fp8_tile_k
     const GR_LDS uint8_t* b_ptr[2];
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
-        a_ptr[s] = lds_p + a_off(ar, 2u * s + (lane >> 5));
-        b_ptr[s] = lds_p + T::A_BYTES + a_off(br, 2u * s + (lane >> 5));
+        const uint32_t ch = 2u * (uint32_t)s + (lane >> 5);
+        a_ptr[s] = lds_p + a_off(ar, ch);
+        b_ptr[s] = lds_p + T::A_BYTES + a_off(br, ch);
     }
+    // MX: scale byte of strip kt for A row ar + 32i (Bt row br + 32j) at
+    // slot (kt/2) % SC_SLOTS, row * 4 + 2 (kt % 2) + lane/32.
+    const uint32_t sc_a = T::SC_BASE + ar * 4u + (lane >> 5);
+    const uint32_t sc_b = T::SC_BASE + ((uint32_t)T::BM + br) * 4u + (lane >> 5);
 
     struct Frags {
         u32x4 a[2][FM];
         u32x4 b[2][FN];
+        uint32_t sa[FM];
+        uint32_t sb[FN];
     };
 
     f32x16 acc[FM][FN];
@@ -182,49 +267,69 @@ __global__ __launch_bounds__(THREADS, Tile<BMT>::MIN_WAVES) void gemm_fp8_tile_k
     // The 2 (FM + FN) fragment reads of one strip, in the order the next
     // step's MFMAs (block row i, then column j) first need them: A0, B0 ..,
     // A1 .., each as its two chunks.
-    constexpr int READS = 2 * (FM + FN);
-    auto read_one = [&](Frags& f, uint32_t slot, int r) {
-        const int q = r >> 1, s = r & 1;
-        const uint32_t so = slot * T::STAGE_BYTES;
-        if (q == 0) f.a[s][0] = read16(a_ptr[s] + so);
-        else if (q <= FN) f.b[s][q - 1] = read16(b_ptr[s] + so + 2048u * (q - 1));
-        else f.a[s][q - FN] = read16(a_ptr[s] + so + 2048u * (q - FN));
+    // MX adds FM + FN one-byte scale reads (strip kt) after them.
+    constexpr int FRAG_READS = 2 * (FM + FN);
+    constexpr int READS = FRAG_READS + (MX ? FM + FN : 0);
+    auto read_one = [&](Frags& f, uint32_t slot, uint32_t kt, int r) {
+        if (r < FRAG_READS) {
+            const int q = r >> 1, s = r & 1;
+            const uint32_t so = slot * T::STAGE_BYTES;
+            if (q == 0) f.a[s][0] = read16(a_ptr[s] + so);
+            else if (q <= FN) f.b[s][q - 1] = read16(b_ptr[s] + so + 2048u * (q - 1));
+            else f.a[s][q - FN] = read16(a_ptr[s] + so + 2048u * (q - FN));
+        } else if constexpr (MX) {
+            const int x = r - FRAG_READS;
+            const uint32_t so = ((kt >> 1) % T::SC_SLOTS) * T::SC_SLOT_BYTES + 2u * (kt & 1u);
+            if (x < FM) f.sa[x] = *(const GR_LDS uint8_t*)(lds_p + sc_a + so + 128u * x);
+            else f.sb[x - FM] = *(const GR_LDS uint8_t*)(lds_p + sc_b + so + 128u * (x - FM));
+        }
     };
     constexpr int MFMAS = FM * FN;
     auto mfma_one = [&](const Frags& f, int t) {
         const int i = t / FN, j = t % FN;
-        acc[i][j] = mfma(f.b[0][j], f.b[1][j], f.a[0][i], f.a[1][i], acc[i][j]);
+        if constexpr (MX) acc[i][j] = mfma_mx(f.b[0][j], f.b[1][j], f.a[0][i], f.a[1][i], acc[i][j], f.sb[j], f.sa[i]);
+        else acc[i][j] = mfma(f.b[0][j], f.b[1][j], f.a[0][i], f.a[1][i], acc[i][j]);
     };
 
     const uint32_t KT = (uint32_t)(k_len / BK);  // >= 1, whole strips only
 
     // Prologue: strips 0, 1, 2 in flight; strip 0 landed and read.
+    // (MX: the copies of strips 0 and 2 carry scales.)
     issue(0, 0);
     if (KT > 1) issue(1, 1);
     if (KT > 2) issue(2, 2);
-    if (KT > 2) wait_vmcnt<2 * 2 * COPIES>();
+    if (KT > 2) wait_vmcnt<2 * 2 * COPIES + SC_COPIES>();
     else if (KT > 1) wait_vmcnt<2 * COPIES>();
     else wait_vmcnt<0>();
     barrier();
 
     Frags f0, f1;
 #pragma unroll
-    for (int r = 0; r < READS; ++r) read_one(f0, 0, r);
+    for (int r = 0; r < READS; ++r) read_one(f0, 0, 0, r);
 
     // Steady step on strip kt (slot SLOT = kt % 4), fragments in `cur`: PRE
     // MFMAs; wait for this wave's copies of strip kt+1; barrier (all copies of
     // kt+1 landed, every wave done with the slot of kt-1); then the other
     // MFMAs with the READS reads of strip kt+1 and the 2*COPIES copies of
     // strip kt+3 (every third operation) spread evenly behind them.
+    // MX: the batch of an even strip adds SC_COPIES scale copies; strip kt+2
+    // (the batch allowed to stay in flight) is even when SLOT is, strip kt+3
+    // (the batch issued here) when SLOT is odd.
     constexpr int PRE = 2;
-    constexpr int OPS = READS + 2 * COPIES;
-    constexpr int PER = (OPS + (MFMAS - PRE) - 1) / (MFMAS - PRE);
     auto step = [&](auto slot_c, uint32_t kt, Frags& cur, Frags& nxt) {
         constexpr uint32_t SLOT = decltype(slot_c)::value;
+        constexpr int IN_FLIGHT = 2 * COPIES + (SLOT % 2 == 0 ? SC_COPIES : 0);
+        constexpr int CPS = 2 * COPIES + (SLOT % 2 == 1 ? SC_COPIES : 0);
+        constexpr int OPS = READS + CPS;
+        constexpr int PER = (OPS + (MFMAS - PRE) - 1) / (MFMAS - PRE);
+        auto copy_one = [&](int cp) {
+            if (cp < 2 * COPIES) dma_one((SLOT + 3) % STAGES, kt + 3, cp);
+            else dma_scale(kt + 3, cp - 2 * COPIES);
+        };
 #pragma unroll
         for (int t = 0; t < PRE; ++t) mfma_one(cur, t);
         pin();
-        wait_vmcnt<2 * COPIES>();
+        wait_vmcnt<IN_FLIGHT>();
         barrier();
         pin();
         int rd = 0, cp = 0;
@@ -236,14 +341,14 @@ __global__ __launch_bounds__(THREADS, Tile<BMT>::MIN_WAVES) void gemm_fp8_tile_k
             for (int u = 0; u < PER; ++u) {
                 const int k = PER * (t - PRE) + u;
                 if (k < OPS) {
-                    if (k % 3 == 1 && cp < 2 * COPIES) {
-                        dma_one((SLOT + 3) % STAGES, kt + 3, cp);
+                    if (k % 3 == 1 && cp < CPS) {
+                        copy_one(cp);
                         ++cp;
                     } else if (rd < READS) {
-                        read_one(nxt, (SLOT + 1) % STAGES, rd);
+                        read_one(nxt, (SLOT + 1) % STAGES, kt + 1, rd);
                         ++rd;
                     } else {
-                        dma_one((SLOT + 3) % STAGES, kt + 3, cp);
+                        copy_one(cp);
                         ++cp;
                     }
                 }
@@ -264,8 +369,12 @@ __global__ __launch_bounds__(THREADS, Tile<BMT>::MIN_WAVES) void gemm_fp8_tile_k
         for (int t = 0; t < PRE; ++t) mfma_one(cur, t);
         pin();
         if (more) {
-            if (kt + 2 < KT) wait_vmcnt<2 * COPIES>();
-            else wait_vmcnt<0>();
+            if (kt + 2 < KT) {
+                if (MX && ((kt + 2) & 1u) == 0u) wait_vmcnt<2 * COPIES + SC_COPIES>();
+                else wait_vmcnt<2 * COPIES>();
+            } else {
+                wait_vmcnt<0>();
+            }
             barrier();
         }
         pin();
@@ -273,7 +382,7 @@ __global__ __launch_bounds__(THREADS, Tile<BMT>::MIN_WAVES) void gemm_fp8_tile_k
         pin();
         if (more) {
 #pragma unroll
-            for (int r = 0; r < READS; ++r) read_one(nxt, (kt + 1) % STAGES, r);
+            for (int r = 0; r < READS; ++r) read_one(nxt, (kt + 1) % STAGES, kt + 1, r);
         }
         pin();
 #pragma unroll
@@ -330,12 +439,24 @@ __device__ __forceinline__ u32x4 load16(const uint8_t* __restrict__ base, int64_
     return u32x4{w[0], w[1], w[2], w[3]};
 }
 
-template <typename E>
+// E8M0 scale of the 32-k block holding byte k of row `row`: 127 (a factor
+// of 1) outside [0, rows) x [0, K), so that the zeros loaded there stay zero.
+__device__ __forceinline__ uint32_t load_scale(const uint8_t* __restrict__ S, int64_t ld, int64_t row, int64_t rows,
+                                               int64_t k, int64_t K) {
+    return (row < rows && k < K) ? (uint32_t)S[row * ld + k / 32] : 127u;
+}
+
+// MX=true: E8M0 scales SA (M x K/32, pitch ldsa) and SB (N x K/32, pitch
+// ldsb); K a multiple of 32.
+template <typename E, bool MX = false>
 __global__ __launch_bounds__(256) void gemm_fp8_guarded_kernel(const uint8_t* __restrict__ A,
                                                               const uint8_t* __restrict__ Bt,
                                                               uint16_t* __restrict__ C, int64_t M, int64_t N,
                                                               int64_t K, int64_t lda, int64_t ldb, int64_t ldc,
-                                                              uint32_t tiles_n, int vec_c, EpiArgs ep) {
+                                                              uint32_t tiles_n, int vec_c,
+                                                              const uint8_t* __restrict__ SA, int64_t ldsa,
+                                                              const uint8_t* __restrict__ SB, int64_t ldsb,
+                                                              EpiArgs ep) {
     static_assert(E::kGeneral, "the fp8 kernels use the general epilogue");
     // The epilogue stages each wave's fp32 blocks here (8 KiB per wave).
     __shared__ __attribute__((aligned(1024))) uint8_t lds[4 * epi::WaveTile<2, 2>::REGION_BYTES];
@@ -353,20 +474,36 @@ __global__ __launch_bounds__(256) void gemm_fp8_guarded_kernel(const uint8_t* __
 
     // Lane half h takes chunks h and 2 + h (16 bytes each) of each 64-byte k
     // step, for both operands: the assignment of the pipelined kernel, so the
-    // two kernels feed the matrix cores identical operands.
+    // two kernels feed the matrix cores identical operands.  MX: lane half h
+    // supplies the scale of the 32-k block k0/32 + h of its row.
     for (int64_t k0 = 0; k0 < K; k0 += BK) {
         u32x4 a[2][2], b[2][2];
 #pragma unroll
         for (int s = 0; s < 2; ++s) {
+            const int64_t kc = k0 + 32 * s + 16 * h;
 #pragma unroll
-            for (int i = 0; i < 2; ++i) a[i][s] = load16(A, lda, m0 + 32 * i + r, M, k0 + 32 * s + 16 * h, K);
+            for (int i = 0; i < 2; ++i) a[i][s] = load16(A, lda, m0 + 32 * i + r, M, kc, K);
 #pragma unroll
-            for (int j = 0; j < 2; ++j) b[j][s] = load16(Bt, ldb, n0 + 32 * j + r, N, k0 + 32 * s + 16 * h, K);
+            for (int j = 0; j < 2; ++j) b[j][s] = load16(Bt, ldb, n0 + 32 * j + r, N, kc, K);
         }
+        if constexpr (MX) {
+            const int64_t kb = k0 + 32 * h;
+            uint32_t sa[2], sb[2];
 #pragma unroll
-        for (int i = 0; i < 2; ++i)
+            for (int i = 0; i < 2; ++i) sa[i] = load_scale(SA, ldsa, m0 + 32 * i + r, M, kb, K);
 #pragma unroll
-            for (int j = 0; j < 2; ++j) acc[i][j] = mfma(b[j][0], b[j][1], a[i][0], a[i][1], acc[i][j]);
+            for (int j = 0; j < 2; ++j) sb[j] = load_scale(SB, ldsb, n0 + 32 * j + r, N, kb, K);
+#pragma unroll
+            for (int i = 0; i < 2; ++i)
+#pragma unroll
+                for (int j = 0; j < 2; ++j)
+                    acc[i][j] = mfma_mx(b[j][0], b[j][1], a[i][0], a[i][1], acc[i][j], sb[j], sa[i]);
+        } else {
+#pragma unroll
+            for (int i = 0; i < 2; ++i)
+#pragma unroll
+                for (int j = 0; j < 2; ++j) acc[i][j] = mfma(b[j][0], b[j][1], a[i][0], a[i][1], acc[i][j]);
+        }
     }
 
     // The same write-back as the pipelined kernels (scale, bias, activation

@@ -992,6 +992,8 @@ int run_fp8(const gr_plan_t& p, int64_t M, int64_t N, int64_t K, const uint8_t* 
     using namespace gr::fp8;
     float* const no_part = nullptr;  // the unsplit kernels take no workspace
     const int64_t no_kps = 0;
+    const uint8_t* const no_s = nullptr;  // nor MX scales
+    const int64_t no_ld = 0;
     if (p.path == GR_PATH_TILE_SPLIT) {
         float* part = reinterpret_cast<float*>(ws);
         const uint32_t tiles_m = (uint32_t)((M + 127) / 128);
@@ -1001,9 +1003,9 @@ int run_fp8(const gr_plan_t& p, int64_t M, int64_t N, int64_t K, const uint8_t* 
         const int64_t kps = ts.k_per_split;
         const bool whole = M % 128 == 0 && N % 128 == 0;
         int st = whole ? launch(gemm_fp8_tile_kernel<128, false, E, true>, p.grid, THREADS, stream, A, Bt, C, M, N, K,
-                                lda, ldbt, ldc, tiles_m, tiles_n, gm, vc, part, kps, ep)
+                                lda, ldbt, ldc, tiles_m, tiles_n, gm, vc, part, kps, no_s, no_ld, no_s, no_ld, ep)
                        : launch(gemm_fp8_tile_kernel<128, true, E, true>, p.grid, THREADS, stream, A, Bt, C, M, N, K,
-                                lda, ldbt, ldc, tiles_m, tiles_n, gm, vc, part, kps, ep);
+                                lda, ldbt, ldc, tiles_m, tiles_n, gm, vc, part, kps, no_s, no_ld, no_s, no_ld, ep);
         if (st != GR_OK) return st;
         return launch_reduce<E>(part, C, M, N, ldc, ts.splits, p.vec_c, ep, stream);
     }
@@ -1017,15 +1019,15 @@ int run_fp8(const gr_plan_t& p, int64_t M, int64_t N, int64_t K, const uint8_t* 
         if (bm == 256) {
             if (whole)
                 return launch(gemm_fp8_tile_kernel<256, false, E>, p.grid, THREADS, stream, A, Bt, C, M, N, K, lda,
-                              ldbt, ldc, tiles_m, tiles_n, gm, vc, no_part, no_kps, ep);
+                              ldbt, ldc, tiles_m, tiles_n, gm, vc, no_part, no_kps, no_s, no_ld, no_s, no_ld, ep);
             return launch(gemm_fp8_tile_kernel<256, true, E>, p.grid, THREADS, stream, A, Bt, C, M, N, K, lda, ldbt,
-                          ldc, tiles_m, tiles_n, gm, vc, no_part, no_kps, ep);
+                          ldc, tiles_m, tiles_n, gm, vc, no_part, no_kps, no_s, no_ld, no_s, no_ld, ep);
         }
         if (whole)
             return launch(gemm_fp8_tile_kernel<128, false, E>, p.grid, THREADS, stream, A, Bt, C, M, N, K, lda, ldbt,
-                          ldc, tiles_m, tiles_n, gm, vc, no_part, no_kps, ep);
+                          ldc, tiles_m, tiles_n, gm, vc, no_part, no_kps, no_s, no_ld, no_s, no_ld, ep);
         return launch(gemm_fp8_tile_kernel<128, true, E>, p.grid, THREADS, stream, A, Bt, C, M, N, K, lda, ldbt, ldc,
-                      tiles_m, tiles_n, gm, vc, no_part, no_kps, ep);
+                      tiles_m, tiles_n, gm, vc, no_part, no_kps, no_s, no_ld, no_s, no_ld, ep);
     }
     if (p.path == GR_PATH_SMALL_M) {
         if (N % SM_NB == 0)
@@ -1036,7 +1038,7 @@ int run_fp8(const gr_plan_t& p, int64_t M, int64_t N, int64_t K, const uint8_t* 
     if (p.path == GR_PATH_TILE_EDGE) {
         const uint32_t tiles_n = (uint32_t)((N + G_BN - 1) / G_BN);
         return launch(gemm_fp8_guarded_kernel<E>, p.grid, 256, stream, A, Bt, C, M, N, K, lda, ldbt, ldc, tiles_n,
-                      (int)p.vec_c, ep);
+                      (int)p.vec_c, no_s, no_ld, no_s, no_ld, ep);
     }
     return p.path == GR_PATH_NONE ? GR_OK : GR_ERR_INVALID_PATH;
 }
@@ -1059,6 +1061,107 @@ int entry_fp8(int64_t M, int64_t N, int64_t K, const uint8_t* A, int64_t lda, co
     if (out_fmt == GR_FMT_BF16)
         return run_fp8<gr::Epi<gr::ElemBF16>>(p, M, N, K, A, lda, Bt, ldbt, C, ldc, ts, w, ep, s);
     return run_fp8<gr::Epi<gr::ElemF16>>(p, M, N, K, A, lda, Bt, ldbt, C, ldc, ts, w, ep, s);
+}
+
+// ---- MX fp8: E4M3 operands with one E8M0 scale per 32 k ------------------------
+
+// Argument checks of the MX calls: those of the fp8 calls, then K a multiple
+// of the 32-element block (GR_ERR_INVALID_DIM), scale pitches of at least
+// K/32 bytes, scale arrays present and clear of C.
+int validate_mx(int64_t M, int64_t N, int64_t K, uintptr_t A, int64_t lda, uintptr_t SA, int64_t ldsa, uintptr_t Bt,
+                int64_t ldbt, uintptr_t SB, int64_t ldsb, uintptr_t bias, int act, uintptr_t C, int64_t ldc,
+                int out_fmt) {
+    int st = validate_fp8(M, N, K, A, lda, Bt, ldbt, bias, act, C, ldc, out_fmt);
+    if (st != GR_OK) return st;
+    if (K % 32 != 0) return GR_ERR_INVALID_DIM;
+    const int64_t kb = K / 32, kbmin = kb > 1 ? kb : 1;
+    if (ldsa < kbmin || ldsb < kbmin) return GR_ERR_INVALID_LD;
+    const bool used = M > 0 && N > 0 && K > 0;
+    if (used && (!SA || !SB)) return GR_ERR_NULL_PTR;
+    const int64_t ssa = used ? span_bytes8(M, kb, ldsa) : 0;
+    const int64_t ssb = used ? span_bytes8(N, kb, ldsb) : 0;
+    if (ssa < 0 || ssb < 0) return GR_ERR_TOO_LARGE;
+    const int64_t sc = (M > 0 && N > 0) ? span_bytes(M, N, ldc) : 0;
+    if (overlaps(C, sc, SA, ssa) || overlaps(C, sc, SB, ssb)) return GR_ERR_ALIAS;
+    return GR_OK;
+}
+
+// The pipelined kernel with MX scales: its fp8 conditions, K a multiple of
+// 128 (every scale copy moves the 4 bytes of two strips) and 4-byte aligned
+// scale rows.
+bool mx_tile_ok(int64_t M, int64_t N, int64_t K, uintptr_t A, int64_t lda, uintptr_t SA, int64_t ldsa, uintptr_t Bt,
+                int64_t ldbt, uintptr_t SB, int64_t ldsb) {
+    using namespace gr::fp8;
+    return fp8_tile_ok(M, N, K, A, lda, Bt, ldbt) && K % 128 == 0 && SA % 4 == 0 && ldsa % 4 == 0 && SB % 4 == 0 &&
+           ldsb % 4 == 0 && ldsa <= MAX_LD && ldsb <= MAX_LD;
+}
+
+int plan_call_mx(int64_t M, int64_t N, int64_t K, uintptr_t A, int64_t lda, uintptr_t SA, int64_t ldsa,
+                 uintptr_t Bt, int64_t ldbt, uintptr_t SB, int64_t ldsb, uintptr_t bias, int act, uintptr_t C,
+                 int64_t ldc, int out_fmt, int forced, gr_plan_t* p) {
+    int st = validate_mx(M, N, K, A, lda, SA, ldsa, Bt, ldbt, SB, ldsb, bias, act, C, ldc, out_fmt);
+    if (st != GR_OK) return st;
+    const bool tile_ok = mx_tile_ok(M, N, K, A, lda, SA, ldsa, Bt, ldbt, SB, ldsb);
+    int path = (M == 0 || N == 0) ? GR_PATH_NONE : (tile_ok ? GR_PATH_TILE : GR_PATH_TILE_EDGE);
+    if (forced >= 0 && path != GR_PATH_NONE) {
+        if ((forced == GR_PATH_TILE && !tile_ok) || (forced != GR_PATH_TILE && forced != GR_PATH_TILE_EDGE))
+            return GR_ERR_INVALID_PATH;
+        path = forced;
+    }
+    fill_plan_fp8(path, M, N, C, ldc, TileSplit{}, p);
+    return GR_OK;
+}
+
+template <typename E>
+int run_mx(const gr_plan_t& p, int64_t M, int64_t N, int64_t K, const uint8_t* A, int64_t lda, const uint8_t* SA,
+           int64_t ldsa, const uint8_t* Bt, int64_t ldbt, const uint8_t* SB, int64_t ldsb, uint16_t* C, int64_t ldc,
+           const gr::EpiArgs& ep, hipStream_t stream) {
+    using namespace gr::fp8;
+    float* const no_part = nullptr;
+    const int64_t no_kps = 0;
+    if (p.path == GR_PATH_TILE) {
+        const int64_t bm = p.block_m;
+        const uint32_t tiles_m = (uint32_t)((M + bm - 1) / bm);
+        const uint32_t tiles_n = (uint32_t)((N + bm - 1) / bm);
+        const bool whole = M % bm == 0 && N % bm == 0;
+        const uint32_t gm = (uint32_t)p.group_m;
+        const int vc = (int)p.vec_c;
+        if (bm == 256) {
+            if (whole)
+                return launch(gemm_fp8_tile_kernel<256, false, E, false, true>, p.grid, THREADS, stream, A, Bt, C, M,
+                              N, K, lda, ldbt, ldc, tiles_m, tiles_n, gm, vc, no_part, no_kps, SA, ldsa, SB, ldsb, ep);
+            return launch(gemm_fp8_tile_kernel<256, true, E, false, true>, p.grid, THREADS, stream, A, Bt, C, M, N, K,
+                          lda, ldbt, ldc, tiles_m, tiles_n, gm, vc, no_part, no_kps, SA, ldsa, SB, ldsb, ep);
+        }
+        if (whole)
+            return launch(gemm_fp8_tile_kernel<128, false, E, false, true>, p.grid, THREADS, stream, A, Bt, C, M, N,
+                          K, lda, ldbt, ldc, tiles_m, tiles_n, gm, vc, no_part, no_kps, SA, ldsa, SB, ldsb, ep);
+        return launch(gemm_fp8_tile_kernel<128, true, E, false, true>, p.grid, THREADS, stream, A, Bt, C, M, N, K,
+                      lda, ldbt, ldc, tiles_m, tiles_n, gm, vc, no_part, no_kps, SA, ldsa, SB, ldsb, ep);
+    }
+    if (p.path == GR_PATH_TILE_EDGE) {
+        const uint32_t tiles_n = (uint32_t)((N + G_BN - 1) / G_BN);
+        return launch(gemm_fp8_guarded_kernel<E, true>, p.grid, 256, stream, A, Bt, C, M, N, K, lda, ldbt, ldc,
+                      tiles_n, (int)p.vec_c, SA, ldsa, SB, ldsb, ep);
+    }
+    return p.path == GR_PATH_NONE ? GR_OK : GR_ERR_INVALID_PATH;
+}
+
+int entry_mx(int64_t M, int64_t N, int64_t K, const uint8_t* A, int64_t lda, const uint8_t* SA, int64_t ldsa,
+             const uint8_t* Bt, int64_t ldbt, const uint8_t* SB, int64_t ldsb, const uint16_t* bias, int act,
+             uint16_t* C, int64_t ldc, int out_fmt, void* stream, int forced) {
+    gr_plan_t p;
+    int st = plan_call_mx(M, N, K, (uintptr_t)A, lda, (uintptr_t)SA, ldsa, (uintptr_t)Bt, ldbt, (uintptr_t)SB, ldsb,
+                          (uintptr_t)bias, act, (uintptr_t)C, ldc, out_fmt, forced, &p);
+    if (st != GR_OK) return st;
+    if (p.path == GR_PATH_NONE) return GR_OK;
+    st = check_device();
+    if (st != GR_OK) return st;
+    const gr::EpiArgs ep{bias, act, 1.0f};
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (out_fmt == GR_FMT_BF16)
+        return run_mx<gr::Epi<gr::ElemBF16>>(p, M, N, K, A, lda, SA, ldsa, Bt, ldbt, SB, ldsb, C, ldc, ep, s);
+    return run_mx<gr::Epi<gr::ElemF16>>(p, M, N, K, A, lda, SA, ldsa, Bt, ldbt, SB, ldsb, C, ldc, ep, s);
 }
 
 }  // namespace
@@ -1257,6 +1360,29 @@ int gemm_fp8_bt_plan(int64_t M, int64_t N, int64_t K, const uint8_t* A, int64_t 
     TileSplit ts;
     return plan_call_fp8(M, N, K, (uintptr_t)A, lda, (uintptr_t)Bt, ldbt, (uintptr_t)bias, act, (uintptr_t)C, ldc,
                          out_fmt, 0, 0, false, -1, &ts, out);
+}
+
+int gemm_mxfp8_bt(int64_t M, int64_t N, int64_t K, const uint8_t* A, int64_t lda, const uint8_t* scale_a,
+                  int64_t ld_sa, const uint8_t* Bt, int64_t ldbt, const uint8_t* scale_b, int64_t ld_sb,
+                  const uint16_t* bias, int act, uint16_t* C, int64_t ldc, int out_fmt, void* stream) {
+    return entry_mx(M, N, K, A, lda, scale_a, ld_sa, Bt, ldbt, scale_b, ld_sb, bias, act, C, ldc, out_fmt, stream, -1);
+}
+
+int gemm_mxfp8_bt_forced(int64_t M, int64_t N, int64_t K, const uint8_t* A, int64_t lda, const uint8_t* scale_a,
+                         int64_t ld_sa, const uint8_t* Bt, int64_t ldbt, const uint8_t* scale_b, int64_t ld_sb,
+                         const uint16_t* bias, int act, uint16_t* C, int64_t ldc, int out_fmt, void* stream,
+                         int path) {
+    if (path != GR_PATH_TILE && path != GR_PATH_TILE_EDGE) return GR_ERR_INVALID_PATH;
+    return entry_mx(M, N, K, A, lda, scale_a, ld_sa, Bt, ldbt, scale_b, ld_sb, bias, act, C, ldc, out_fmt, stream,
+                    path);
+}
+
+int gemm_mxfp8_bt_plan(int64_t M, int64_t N, int64_t K, const uint8_t* A, int64_t lda, const uint8_t* scale_a,
+                       int64_t ld_sa, const uint8_t* Bt, int64_t ldbt, const uint8_t* scale_b, int64_t ld_sb,
+                       const uint16_t* bias, int act, const uint16_t* C, int64_t ldc, int out_fmt, gr_plan_t* out) {
+    if (!out) return GR_ERR_INVALID_ARG;
+    return plan_call_mx(M, N, K, (uintptr_t)A, lda, (uintptr_t)scale_a, ld_sa, (uintptr_t)Bt, ldbt,
+                        (uintptr_t)scale_b, ld_sb, (uintptr_t)bias, act, (uintptr_t)C, ldc, out_fmt, -1, out);
 }
 
 const char* gemm_relu_status_string(int status) {

@@ -504,6 +504,59 @@ int gemm_fp8_bt_plan_ws(int64_t M, int64_t N, int64_t K,
                         const uint16_t* C, int64_t ldc, int out_fmt,
                         int64_t workspace_bytes, gr_plan_t* out);
 
+/*
+ * ---- MX fp8 (block-scaled) operands ---------------------------------------------
+ * C := act(A~ * Bt~^T + bias) where A~[m][k] = A[m][k] * 2^(SA[m][k/32] - 127)
+ * and Bt~[n][k] = Bt[n][k] * 2^(SB[n][k/32] - 127): A (M x K) and Bt (N x K)
+ * hold OCP fp8 E4M3 bytes as for gemm_fp8_bt, and every run of 32 consecutive
+ * k of a row shares one OCP MX E8M0 scale byte (value 2^(x - 127), 0 <= x <=
+ * 254; x = 255 is NaN).  scale_a is M x K/32 bytes (row pitch ld_sa >=
+ * max(1, K/32)), scale_b is N x K/32 bytes (pitch ld_sb).  Products
+ * accumulate in fp32 (the matrix cores apply the scales, one per lane and
+ * 32-k block); then bias, activation and one rounding to out_fmt as for
+ * gemm_fp8_bt.  The pages name block-scaled GEMMs -- quantised operands with
+ * per-block scales -- among the TileLang examples (blog "TileLang programming
+ * basics", section "推荐顺序", step 6, and the block-scaled MMA row of the
+ * table in section 5.4); OCP MX is the block format gfx950 scales in
+ * hardware.
+ *   K must be a multiple of 32 (GR_ERR_INVALID_DIM otherwise).
+ *   Paths: GR_PATH_TILE (the pipelined fp8 kernel; K % 128 == 0, 16-byte
+ *   aligned rows of A and Bt, 4-byte aligned scale rows: scale pointers and
+ *   pitches multiples of 4) or GR_PATH_TILE_EDGE (guarded, any alignment).
+ *   Other conventions as gemm_fp8_bt; the scale arrays must not overlap C
+ *   (GR_ERR_ALIAS).  No workspace variant.
+ */
+int gemm_mxfp8_bt(int64_t M, int64_t N, int64_t K,
+                  const uint8_t* A, int64_t lda,
+                  const uint8_t* scale_a, int64_t ld_sa,
+                  const uint8_t* Bt, int64_t ldbt,
+                  const uint8_t* scale_b, int64_t ld_sb,
+                  const uint16_t* bias, int act,
+                  uint16_t* C, int64_t ldc, int out_fmt,
+                  void* stream);
+
+/* gemm_mxfp8_bt on a given path (GR_PATH_TILE or GR_PATH_TILE_EDGE;
+   GR_ERR_INVALID_PATH otherwise or when the path's conditions do not hold).
+   Test hook. */
+int gemm_mxfp8_bt_forced(int64_t M, int64_t N, int64_t K,
+                         const uint8_t* A, int64_t lda,
+                         const uint8_t* scale_a, int64_t ld_sa,
+                         const uint8_t* Bt, int64_t ldbt,
+                         const uint8_t* scale_b, int64_t ld_sb,
+                         const uint16_t* bias, int act,
+                         uint16_t* C, int64_t ldc, int out_fmt,
+                         void* stream, int path);
+
+/* Pure planner for gemm_mxfp8_bt (no GPU needed). */
+int gemm_mxfp8_bt_plan(int64_t M, int64_t N, int64_t K,
+                       const uint8_t* A, int64_t lda,
+                       const uint8_t* scale_a, int64_t ld_sa,
+                       const uint8_t* Bt, int64_t ldbt,
+                       const uint8_t* scale_b, int64_t ld_sb,
+                       const uint16_t* bias, int act,
+                       const uint16_t* C, int64_t ldc, int out_fmt,
+                       gr_plan_t* out);
+
 /* Static, NUL-terminated name of a status code ("GR_OK", "GR_ERR_ALIAS", ...).
    Unknown codes give "GR_ERR_UNKNOWN". */
 const char* gemm_relu_status_string(int status);

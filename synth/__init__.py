@@ -141,3 +141,51 @@ def fp8_operands(M: int, N: int, K: int, seed: int, lda: int | None = None, ldbt
     if N and K:
         Bt[:, :K] = e4m3((N, K), gen, scale_b)
     return A, Bt
+
+
+def mx_quantize(x: np.ndarray):
+    """OCP MX quantisation of a float32 matrix (rows x K, K a multiple of 32)
+    to E4M3 elements with one E8M0 scale per 32 consecutive k: the shared
+    exponent of a block is floor(log2(max |x|)) - 8 (8 = the largest E4M3
+    exponent), the elements are x / 2^exponent rounded to E4M3 (nearest even,
+    saturating at +-448).  An all-zero block gets the code 127."""
+    torch = _torch()
+    rows, K = x.shape
+    blocks = x.reshape(rows, K // 32, 32).astype(np.float32)
+    amax = np.abs(blocks).max(axis=2)
+    with np.errstate(divide="ignore"):
+        e = np.where(amax > 0, np.floor(np.log2(np.where(amax > 0, amax, 1.0))) - 8, 0).astype(np.int64)
+    e = np.clip(e, -127, 127)
+    scaled = (blocks / np.exp2(e)[:, :, None].astype(np.float64)).astype(np.float32)
+    scaled = np.clip(scaled, -E4M3_MAX, E4M3_MAX).reshape(rows, K)
+    elems = torch.from_numpy(scaled).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    return elems, (e + 127).astype(np.uint8)
+
+
+def mx_operands(M: int, N: int, K: int, seed: int, lda: int | None = None, ldbt: int | None = None,
+                ldsa: int | None = None, ldsb: int | None = None, spread: int = 2,
+                pad_value: int = E4M3_LARGEST_BITS, pad_scale: int = 255):
+    """A, SA, Bt, SB for the MX fp8 product: N(0,1) values times 2^u, u drawn
+    per 32-k block from [-spread, spread] (so the scales vary from block to
+    block), quantised by mx_quantize.  Padding columns hold ``pad_value``
+    (448) and the scale padding ``pad_scale`` (255, the NaN code), so a read
+    outside the matrices shows in the result."""
+    torch = _torch()
+    gen = torch.Generator().manual_seed(seed)
+    kb = K // 32
+    lda = K if lda is None else lda
+    ldbt = K if ldbt is None else ldbt
+    ldsa = max(kb, 1) if ldsa is None else ldsa
+    ldsb = max(kb, 1) if ldsb is None else ldsb
+    out = []
+    for rows, ld, lds in ((M, lda, ldsa), (N, ldbt, ldsb)):
+        E = np.full((rows, max(ld, 1)), pad_value, dtype=np.uint8)
+        S = np.full((rows, max(lds, 1)), pad_scale, dtype=np.uint8)
+        if rows and K:
+            x = torch.randn(rows, K, generator=gen, dtype=torch.float32).numpy()
+            u = torch.randint(-spread, spread + 1, (rows, kb), generator=gen).numpy()
+            x = x * np.repeat(np.exp2(u), 32, axis=1).astype(np.float32)
+            E[:, :K], S[:, :kb] = mx_quantize(x)
+        out.append((E, S))
+    (A, SA), (Bt, SB) = out
+    return A, SA, Bt, SB

@@ -525,6 +525,37 @@ def test_fp8_split_planner_and_checks_need_no_gpu():
     assert f(0, 8, 8, 0, 8, BASE_B, 8, 1.0, 1.0, None, 1, 0, 8, 0, None, 0) == gr.GR_OK
 
 
+def test_mxfp8_planner_and_checks_need_no_gpu():
+    """gemm_mxfp8_bt: the pipelined kernel for K % 128 == 0 with 16-byte
+    operand rows and 4-byte scale rows, the guarded kernel otherwise;
+    argument errors before any HIP call."""
+    SA, SB = BASE_C + (1 << 31), BASE_C + (1 << 32)
+
+    def plan(M, N, K, ldsa=None, ldsb=None, sa=SA, sb=SB, lda=None):
+        kb = max(K // 32, 1)
+        return gr.gemm_mxfp8_bt_plan(M, N, K, BASE_A, lda or max(K, 1), sa, ldsa or kb, BASE_B, max(K, 1), sb,
+                                     ldsb or kb, None, 1, BASE_C, max(N, 1), gr.GR_FMT_F16)
+    st, p = plan(4096, 4096, 4096)
+    assert st == gr.GR_OK and (p["path"], p["block_m"], p["grid"]) == (gr.GR_PATH_TILE, 256, 256)
+    assert plan(300, 270, 384)[1]["path"] == gr.GR_PATH_TILE and plan(300, 270, 384)[1]["block_m"] == 128
+    assert plan(300, 270, 96)[1]["path"] == gr.GR_PATH_TILE_EDGE            # K % 128 != 0
+    assert plan(300, 270, 384, ldsa=13)[1]["path"] == gr.GR_PATH_TILE_EDGE  # scale pitch not a multiple of 4
+    assert plan(300, 270, 384, sb=SB + 2)[1]["path"] == gr.GR_PATH_TILE_EDGE
+    assert plan(300, 270, 384, lda=392)[1]["path"] == gr.GR_PATH_TILE_EDGE  # A rows not 16-byte aligned
+    assert plan(300, 270, 100)[0] == gr.GR_ERR_INVALID_DIM                  # K % 32 != 0
+    assert plan(300, 270, 384, ldsa=11)[0] == gr.GR_ERR_INVALID_LD          # pitch < K/32
+    assert plan(0, 270, 384)[1]["path"] == gr.GR_PATH_NONE
+    f = gr.gemm_mxfp8_bt
+    assert f(8, 8, 64, BASE_A, 64, 0, 2, BASE_B, 64, SB, 2, None, 1, BASE_C, 8) == gr.GR_ERR_NULL_PTR
+    assert f(8, 8, 64, BASE_A, 64, BASE_C + 4, 2, BASE_B, 64, SB, 2, None, 1, BASE_C, 8) == gr.GR_ERR_ALIAS
+    assert f(8, 8, 64, BASE_A, 64, SA, 2, BASE_B, 64, SB, 2, None, 7, BASE_C, 8) == gr.GR_ERR_INVALID_ARG
+    assert gr.gemm_mxfp8_bt_forced(300, 270, 96, BASE_A, 96, SA, 3, BASE_B, 96, SB, 3, None, 1, BASE_C, 270,
+                                   gr.GR_FMT_F16, None, gr.GR_PATH_TILE) == gr.GR_ERR_INVALID_PATH
+    assert gr.gemm_mxfp8_bt_forced(8, 8, 64, BASE_A, 64, SA, 2, BASE_B, 64, SB, 2, None, 1, BASE_C, 8,
+                                   gr.GR_FMT_F16, None, gr.GR_PATH_SMALL_M) == gr.GR_ERR_INVALID_PATH
+    assert f(0, 8, 64, 0, 64, 0, 2, BASE_B, 64, SB, 2, None, 1, 0, 8) == gr.GR_OK
+
+
 def test_fp8_planner_and_checks_need_no_gpu():
     """gemm_fp8_bt: the pipelined kernel for K % 64 == 0 with 16-byte rows (any
     M, N), the guarded kernel otherwise; argument errors before any HIP call."""
