@@ -7,6 +7,7 @@ case: total work, whole-problem intensity, ideal versus per-tile traffic).
 """
 from __future__ import annotations
 
+MI355X_PEAK_SCLK_MHZ = 2400.0     # the clock of the published peaks
 MI355X_MFMA_F16_TFLOPS = 2516.6   # 256 CU x 4096 FLOP/clk x 2.4 GHz (published 2.5 PFLOP/s)
 MI355X_HBM_GBS = 8000.0           # published 8 TB/s
 FP16_BYTES = 2
