@@ -105,6 +105,12 @@ def _load():
             lib.oracle_gemm_mxfp8_bt_elems.argtypes = [ci, p, ci, i64, i64, i64, p, i64, p, i64, p, i64, p, i64, p, p,
                                                        i64, p]
             lib.oracle_gemm_mxfp8_bt_elems.restype = ci
+            lib.oracle_e2m1_to_f32_array.argtypes = [p, p, i64]
+            lib.oracle_e2m1_to_f32_array.restype = None
+            lib.oracle_gemm_mxfp4_bt_full.argtypes = lib.oracle_gemm_mxfp8_bt_full.argtypes
+            lib.oracle_gemm_mxfp4_bt_full.restype = ci
+            lib.oracle_gemm_mxfp4_bt_elems.argtypes = lib.oracle_gemm_mxfp8_bt_elems.argtypes
+            lib.oracle_gemm_mxfp4_bt_elems.restype = ci
             _lib = lib
     return _lib
 
@@ -404,6 +410,81 @@ def gemm_mxfp8_bt_elems(A, SA, Bt, SB, ii, jj, fmt="f16", bias=None, act="relu",
     out = np.zeros(i.size, dtype=np.uint16)
     if i.size:
         st = lib.oracle_gemm_mxfp8_bt_elems(_FMTS.index(fmt), bptr, ACTS[act], M, N, K, _ptr(A), lda, _ptr(SA), ldsa,
+                                            _ptr(Bt), ldbt, _ptr(SB), ldsb, _ptr(i), _ptr(j), i.size, _ptr(out))
+        assert st == 0
+    return out
+
+
+def e2m1_to_f32(nibbles: np.ndarray) -> np.ndarray:
+    """Element-wise OCP fp4 E2M1 code (low 4 bits) -> binary32 through the oracle."""
+    lib = _load()
+    flat = np.ascontiguousarray(nibbles, dtype=np.uint8).ravel()
+    out = np.empty(flat.size, dtype=np.float32)
+    lib.oracle_e2m1_to_f32_array(_ptr(flat), _ptr(out), flat.size)
+    return out.reshape(np.shape(nibbles))
+
+
+def _mx4_args(A, SA, Bt, SB, bias, act, fmt, M, N, K, lda, ldsa, ldbt, ldsb):
+    if A.dtype != np.uint8 or Bt.dtype != np.uint8 or SA.dtype != np.uint8 or SB.dtype != np.uint8:
+        raise TypeError("packed E2M1 operands and E8M0 scales are uint8 arrays")
+    if not all(x.flags.c_contiguous for x in (A, SA, Bt, SB)):
+        raise ValueError("arrays must be C-contiguous")
+    M = A.shape[0] if M is None else M
+    N = Bt.shape[0] if N is None else N
+    K = 2 * A.shape[1] if K is None else K
+    if K % 32:
+        raise ValueError("K must be a multiple of the 32-element block")
+    kb = K // 32
+    lda = K // 2 if lda is None else int(lda)
+    ldbt = K // 2 if ldbt is None else int(ldbt)
+    ldsa = max(kb, 1) if ldsa is None else int(ldsa)
+    ldsb = max(kb, 1) if ldsb is None else int(ldsb)
+    if K and ((M and A.size < (M - 1) * lda + K // 2) or (N and Bt.size < (N - 1) * ldbt + K // 2)):
+        raise ValueError("operands too small")
+    if kb and ((M and SA.size < (M - 1) * ldsa + kb) or (N and SB.size < (N - 1) * ldsb + kb)):
+        raise ValueError("scale arrays too small")
+    if fmt not in _FMTS or act not in ACTS:
+        raise ValueError("bad format or activation")
+    bptr = 0
+    if bias is not None:
+        if bias.dtype != np.uint16 or not bias.flags.c_contiguous or bias.ndim != 1 or bias.size < N:
+            raise TypeError("bias must be a contiguous 1-D uint16 array of N bit patterns")
+        bptr = _ptr(bias)
+    return int(M), int(N), int(K), lda, ldbt, bptr, ldsa, ldsb
+
+
+def gemm_mxfp4_bt_full(A, SA, Bt, SB, fmt="f16", bias=None, act="relu", M=None, N=None, K=None, lda=None,
+                       ldsa=None, ldbt=None, ldsb=None, threads=None):
+    """gemm_mxfp8_bt_full with packed E2M1 operands (two per byte, k even in
+    the low nibble); lda, ldbt in bytes."""
+    M, N, K, lda, ldbt, bptr, ldsa, ldsb = _mx4_args(A, SA, Bt, SB, bias, act, fmt, M, N, K, lda, ldsa, ldbt, ldsb)
+    lib = _load()
+    if threads:
+        lib.oracle_set_threads(int(threads))
+    C = np.zeros((M, N), dtype=np.uint16)
+    if M > 0 and N > 0:
+        st = lib.oracle_gemm_mxfp4_bt_full(_FMTS.index(fmt), bptr, ACTS[act], M, N, K, _ptr(A), lda, _ptr(SA), ldsa,
+                                           _ptr(Bt), ldbt, _ptr(SB), ldsb, _ptr(C), N)
+        assert st == 0
+    return C
+
+
+def gemm_mxfp4_bt_elems(A, SA, Bt, SB, ii, jj, fmt="f16", bias=None, act="relu", M=None, N=None, K=None, lda=None,
+                        ldsa=None, ldbt=None, ldsb=None, threads=None):
+    """Single elements C[ii[e], jj[e]] of gemm_mxfp4_bt_full."""
+    M, N, K, lda, ldbt, bptr, ldsa, ldsb = _mx4_args(A, SA, Bt, SB, bias, act, fmt, M, N, K, lda, ldsa, ldbt, ldsb)
+    i = np.ascontiguousarray(ii, dtype=np.int64)
+    j = np.ascontiguousarray(jj, dtype=np.int64)
+    if i.shape != j.shape:
+        raise ValueError("index arrays differ in length")
+    if i.size and (i.min() < 0 or i.max() >= M or j.min() < 0 or j.max() >= N):
+        raise IndexError("element index out of range")
+    lib = _load()
+    if threads:
+        lib.oracle_set_threads(int(threads))
+    out = np.zeros(i.size, dtype=np.uint16)
+    if i.size:
+        st = lib.oracle_gemm_mxfp4_bt_elems(_FMTS.index(fmt), bptr, ACTS[act], M, N, K, _ptr(A), lda, _ptr(SA), ldsa,
                                             _ptr(Bt), ldbt, _ptr(SB), ldsb, _ptr(i), _ptr(j), i.size, _ptr(out))
         assert st == 0
     return out

@@ -71,6 +71,12 @@
  * GEMMs (per-block scales on quantised operands) as examples; MX is the
  * block format the gfx950 matrix cores scale in hardware.
  *
+ * The *_mxfp4_* entry points are the same with OCP fp4 E2M1 elements (1 sign
+ * bit, 2 exponent bits with bias 1, 1 fraction bit: 0, 0.5, 1, 1.5, 2, 3, 4,
+ * 6), two per byte: element k of a row is the low nibble of byte k/2 when k
+ * is even, the high nibble when k is odd; K counts elements, the pitches
+ * count bytes.
+ *
  * The single rounding from double goes through fp32 with round-to-odd (the
  * nearest fp32 toward zero with its last bit forced to 1 when inexact), which
  * keeps two or more spare bits over the fp16 and bfloat16 significands, so
@@ -577,5 +583,67 @@ int oracle_gemm_mxfp8_bt_elems(int fmt, const uint16_t* bias, int act, int64_t M
 #pragma omp parallel for schedule(static)
     for (int64_t e = 0; e < n; ++e)
         out[e] = mx_element(fmt, &ep, ii[e], jj[e], K, A, lda, SA, ldsa, Bt, ldbt, SB, ldsb);
+    return 0;
+}
+
+/* ---- MX fp4: E2M1 elements (two per byte) with one E8M0 scale per 32 k ------- */
+
+/* E2M1: bit 3 sign, bits 2..1 exponent (bias 1), bit 0 fraction; exponent 0
+   is the subnormal 0.5 * m.  No infinity or NaN. */
+float oracle_e2m1_to_f32(uint8_t nib) {
+    const int sign = (nib >> 3) & 1, e = (nib >> 1) & 3, m = nib & 1;
+    const float v = e == 0 ? 0.5f * (float)m : ldexpf(1.0f + 0.5f * (float)m, e - 1);
+    return sign ? -v : v;
+}
+
+void oracle_e2m1_to_f32_array(const uint8_t* in, float* out, int64_t n) {
+    for (int64_t e = 0; e < n; ++e) out[e] = oracle_e2m1_to_f32(in[e] & 15u);
+}
+
+/* Element k of a row of packed E2M1. */
+static float e2m1_at(const uint8_t* row, int64_t k) {
+    const uint8_t b = row[k >> 1];
+    return oracle_e2m1_to_f32((k & 1) ? (uint8_t)(b >> 4) : (uint8_t)(b & 15u));
+}
+
+static uint16_t mx4_element(int fmt, const Epi* ep, int64_t i, int64_t j, int64_t K, const uint8_t* A,
+                            int64_t lda, const uint8_t* SA, int64_t ldsa, const uint8_t* Bt, int64_t ldbt,
+                            const uint8_t* SB, int64_t ldsb) {
+    float acc = 0.0f;
+    for (int64_t k = 0; k < K; ++k) {
+        const double a = (double)e2m1_at(A + i * lda, k) * oracle_e8m0_to_f64(SA[i * ldsa + k / 32]);
+        const double b = (double)e2m1_at(Bt + j * ldbt, k) * oracle_e8m0_to_f64(SB[j * ldsb + k / 32]);
+        acc = acc + (float)(a * b);
+    }
+    return epilogue(fmt, ep, j, acc);
+}
+
+/* As oracle_gemm_mxfp8_bt_full with packed E2M1 operands (lda, ldbt in
+   bytes, at least K/2). */
+int oracle_gemm_mxfp4_bt_full(int fmt, const uint16_t* bias, int act, int64_t M, int64_t N, int64_t K,
+                              const uint8_t* A, int64_t lda, const uint8_t* SA, int64_t ldsa, const uint8_t* Bt,
+                              int64_t ldbt, const uint8_t* SB, int64_t ldsb, uint16_t* C, int64_t ldc) {
+    if (!epi_check(fmt, act)) return -2;
+    if (K % 32 != 0) return -3;
+    const Epi ep = {bias, act, 1.0f};
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t i = 0; i < M; ++i)
+        for (int64_t j = 0; j < N; ++j)
+            C[i * ldc + j] = mx4_element(fmt, &ep, i, j, K, A, lda, SA, ldsa, Bt, ldbt, SB, ldsb);
+    return 0;
+}
+
+int oracle_gemm_mxfp4_bt_elems(int fmt, const uint16_t* bias, int act, int64_t M, int64_t N, int64_t K,
+                               const uint8_t* A, int64_t lda, const uint8_t* SA, int64_t ldsa, const uint8_t* Bt,
+                               int64_t ldbt, const uint8_t* SB, int64_t ldsb, const int64_t* ii, const int64_t* jj,
+                               int64_t n, uint16_t* out) {
+    (void)M;
+    (void)N;
+    if (!epi_check(fmt, act)) return -2;
+    if (K % 32 != 0) return -3;
+    const Epi ep = {bias, act, 1.0f};
+#pragma omp parallel for schedule(static)
+    for (int64_t e = 0; e < n; ++e)
+        out[e] = mx4_element(fmt, &ep, ii[e], jj[e], K, A, lda, SA, ldsa, Bt, ldbt, SB, ldsb);
     return 0;
 }
