@@ -370,6 +370,9 @@ EXTRA_SHAPES = [
     ("MX fp8 (E8M0 scale per 32 k), square", 4096, 4096, 4096, "mxfp8"),
     ("MX fp8, square 8192", 8192, 8192, 8192, "mxfp8"),
     ("MX fp8, MLP projection", 8192, 28672, 8192, "mxfp8"),
+    ("MX fp4 (E2M1, E8M0 scale per 32 k), square", 4096, 4096, 4096, "mxfp4"),
+    ("MX fp4, square 8192", 8192, 8192, 8192, "mxfp4"),
+    ("MX fp4, MLP projection", 8192, 28672, 8192, "mxfp4"),
 ]
 
 
@@ -387,7 +390,31 @@ def extra_shapes(gr, torch, reps=30):
         C = torch.empty(M, N, device="cuda", dtype=dt)
         row = {"shape": "%dx%dx%d" % (M, N, K), "what": label, "layout": layout}
         runs = {}
-        if layout == "mxfp8":
+        if layout == "mxfp4":
+            # random E2M1 pairs (every byte is two valid codes) and scales
+            A4 = torch.randint(0, 256, (M, K // 2), generator=g, device="cuda", dtype=torch.int32).to(torch.uint8)
+            B4 = torch.randint(0, 256, (N, K // 2), generator=g, device="cuda", dtype=torch.int32).to(torch.uint8)
+            sa4 = torch.randint(124, 130, (M, K // 32), generator=g, device="cuda", dtype=torch.int32).to(torch.uint8)
+            sb4 = torch.randint(124, 130, (N, K // 32), generator=g, device="cuda", dtype=torch.int32).to(torch.uint8)
+            h = stream.cuda_stream
+
+            def ours4():
+                st = gr.gemm_mxfp4_bt(M, N, K, A4.data_ptr(), K // 2, sa4.data_ptr(), K // 32, B4.data_ptr(), K // 2,
+                                      sb4.data_ptr(), K // 32, None, gr.GR_ACT_RELU, C.data_ptr(), N, gr.GR_FMT_F16, h)
+                if st != gr.GR_OK:
+                    raise gr.GemmReluError(st, "gemm_mxfp4_bt")
+            runs["ours"] = ours4
+
+            def vendor4():
+                a, b = A4.view(torch.float4_e2m1fn_x2), B4.view(torch.float4_e2m1fn_x2)
+                return torch.relu_(torch._scaled_mm(a, b.t(), scale_a=sa4.view(torch.float8_e8m0fnu),
+                                                    scale_b=sb4.view(torch.float8_e8m0fnu), out_dtype=torch.float16))
+            try:
+                vendor4()
+                runs["vendor"] = vendor4
+            except Exception as e:  # the vendor MX fp4 path may be missing
+                row["vendor_error"] = str(e)[:120]
+        elif layout == "mxfp8":
             A8 = torch.randn(M, K, generator=g, device="cuda").to(torch.float8_e4m3fn)
             Bt8 = torch.randn(N, K, generator=g, device="cuda").to(torch.float8_e4m3fn)
             sa8 = torch.randint(124, 130, (M, K // 32), generator=g, device="cuda", dtype=torch.int32).to(torch.uint8)

@@ -163,6 +163,9 @@ def lib() -> ctypes.CDLL:
             l.gemm_mxfp8_bt_plan.argtypes = [i64, i64, i64, p, i64, p, i64, p, i64, p, i64, p, i32, p, i64, i32,
                                              ctypes.POINTER(gr_plan_t)]
             l.gemm_mxfp8_bt_plan.restype = i32
+            for nm in ("gemm_mxfp4_bt", "gemm_mxfp4_bt_forced", "gemm_mxfp4_bt_plan"):
+                getattr(l, nm).argtypes = getattr(l, nm.replace("mxfp4", "mxfp8")).argtypes
+                getattr(l, nm).restype = i32
             l.gemm_relu_status_string.argtypes = [i32]
             l.gemm_relu_status_string.restype = ctypes.c_char_p
             l.gemm_relu_version.argtypes = []
@@ -346,6 +349,26 @@ def gemm_mxfp8_bt_forced(M, N, K, A, lda, SA, ld_sa, Bt, ldbt, SB, ld_sb, bias, 
 def gemm_mxfp8_bt_plan(M, N, K, A, lda, SA, ld_sa, Bt, ldbt, SB, ld_sb, bias, act, C, ldc, out_fmt=GR_FMT_F16):
     plan = gr_plan_t()
     st = lib().gemm_mxfp8_bt_plan(M, N, K, _ptr(A), lda, _ptr(SA), ld_sa, _ptr(Bt), ldbt, _ptr(SB), ld_sb,
+                                  _ptr(bias), act, _ptr(C), ldc, out_fmt, ctypes.byref(plan))
+    return st, _plan_dict(plan)
+
+
+def gemm_mxfp4_bt(M, N, K, A, lda, SA, ld_sa, Bt, ldbt, SB, ld_sb, bias, act, C, ldc, out_fmt=GR_FMT_F16,
+                  stream=None) -> int:
+    """gemm_mxfp8_bt with packed E2M1 operands (two per byte; lda, ldbt in bytes, K in elements)."""
+    return lib().gemm_mxfp4_bt(M, N, K, _ptr(A), lda, _ptr(SA), ld_sa, _ptr(Bt), ldbt, _ptr(SB), ld_sb, _ptr(bias),
+                               act, _ptr(C), ldc, out_fmt, _ptr(stream))
+
+
+def gemm_mxfp4_bt_forced(M, N, K, A, lda, SA, ld_sa, Bt, ldbt, SB, ld_sb, bias, act, C, ldc, out_fmt=GR_FMT_F16,
+                         stream=None, path=GR_PATH_TILE_EDGE) -> int:
+    return lib().gemm_mxfp4_bt_forced(M, N, K, _ptr(A), lda, _ptr(SA), ld_sa, _ptr(Bt), ldbt, _ptr(SB), ld_sb,
+                                      _ptr(bias), act, _ptr(C), ldc, out_fmt, _ptr(stream), path)
+
+
+def gemm_mxfp4_bt_plan(M, N, K, A, lda, SA, ld_sa, Bt, ldbt, SB, ld_sb, bias, act, C, ldc, out_fmt=GR_FMT_F16):
+    plan = gr_plan_t()
+    st = lib().gemm_mxfp4_bt_plan(M, N, K, _ptr(A), lda, _ptr(SA), ld_sa, _ptr(Bt), ldbt, _ptr(SB), ld_sb,
                                   _ptr(bias), act, _ptr(C), ldc, out_fmt, ctypes.byref(plan))
     return st, _plan_dict(plan)
 
@@ -545,7 +568,8 @@ def gemm_fp8(a, bt, scale_a=1.0, scale_b=1.0, bias=None, act="relu", out_dtype=N
             workspace.record_stream(stream)
     ws_ptr, ws_bytes = (workspace.data_ptr(), workspace.numel()) if workspace is not None else (0, 0)
     st = gemm_fp8_bt_ws(M, N, K, a.data_ptr(), lda, bt.data_ptr(), ldbt, scale_a, scale_b, bptr, code,
-                        out.data_ptr(), ldc, fmt, ws_ptr, ws_bytes, _stream_handle(stream), -1 if path is None else path)
+                        out.data_ptr(), ldc, fmt, ws_ptr, ws_bytes, _stream_handle(stream),
+                        -1 if path is None else path)
     if st != GR_OK:
         raise GemmReluError(st, "gemm_fp8_bt_ws")
     return out

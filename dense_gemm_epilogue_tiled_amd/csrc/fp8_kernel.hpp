@@ -34,6 +34,12 @@
 // and per-block scales both match the oracle only with this pairing).  The
 // scales travel through LDS beside the ring: 4 bytes of each row (the blocks
 // of two strips) per copy, with the copies of every even strip.
+// MX=4 (OCP MX fp4: E2M1 elements, two per byte, one E8M0 scale per 32 k):
+// the same kernel byte for byte -- a 64-byte strip row now holds 128 k --
+// with two scaled fp4 instructions per strip and block pair (32 x 32 x 64,
+// one 16-byte quad per lane: quad s of the strip, k 64s + 32h .. + 31 in
+// lane half h, whose scale is that of block 4kt + 2s + h); the scales of a
+// strip (4 blocks per row) travel with every strip's copies.
 // gemm_fp8_smallm_kernel: M <= 16, a bandwidth-bound stream over Bt.
 // gemm_fp8_guarded_kernel: every other shape (any K, any alignment), operands
 // loaded straight into registers with bounds checks, out-of-range bytes 0.
@@ -61,12 +67,20 @@ __device__ __forceinline__ f32x16 mfma(const u32x4& b0, const u32x4& b1, const u
 
 // The same block product with E8M0 scales: lane l scales the 32 bytes of
 // its B operand by 2^(sb - 127) and those of its A operand by 2^(sa - 127)
-// (the low byte of each scale word).
+// (the low byte of each scale word; see MX below for which k that is).
 __device__ __forceinline__ f32x16 mfma_mx(const u32x4& b0, const u32x4& b1, const u32x4& a0, const u32x4& a1,
                                           f32x16 c, uint32_t sb, uint32_t sa) {
     const i32x8 bo = {(int)b0[0], (int)b0[1], (int)b0[2], (int)b0[3], (int)b1[0], (int)b1[1], (int)b1[2], (int)b1[3]};
     const i32x8 ao = {(int)a0[0], (int)a0[1], (int)a0[2], (int)a0[3], (int)a1[0], (int)a1[1], (int)a1[2], (int)a1[3]};
     return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(bo, ao, c, 0, 0, 0, (int)sb, 0, (int)sa);
+}
+
+// One 32 x 32 x 64 product of OCP fp4 E2M1 operands (format code 4): one
+// 16-byte quad (32 elements) per lane and operand, with E8M0 scales.
+__device__ __forceinline__ f32x16 mfma_mx4(const u32x4& b, const u32x4& a, f32x16 c, uint32_t sb, uint32_t sa) {
+    const i32x8 bo = {(int)b[0], (int)b[1], (int)b[2], (int)b[3], 0, 0, 0, 0};
+    const i32x8 ao = {(int)a[0], (int)a[1], (int)a[2], (int)a[3], 0, 0, 0, 0};
+    return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(bo, ao, c, 4, 4, 0, (int)sb, 0, (int)sa);
 }
 
 // Copy of 4 bytes per lane from global memory into LDS (lane l writes LDS
@@ -124,19 +138,24 @@ __device__ __forceinline__ u32x4 read16(const GR_LDS uint8_t* p) { return *(cons
 // over the K range of split g / tiles (k_per_split bytes, a multiple of 64;
 // no split is empty) and writes its unscaled fp32 sums to part[split][m][n];
 // a second pass adds the splits in order and applies the epilogue.
-// MX=true: SA (M x K/32, pitch ldsa) and SB (N x K/32, pitch ldsb) hold the
-// E8M0 scales; K a multiple of 128, scale rows 4-byte aligned.
-template <int BMT, bool EDGE, typename E, bool SPLIT = false, bool MX = false>
+// MX = 8 (MX fp8) or 4 (MX fp4; K, lda and ldb then count bytes, two
+// elements each): SA (M x K/32, pitch ldsa) and SB (N x K/32, pitch ldsb)
+// hold the E8M0 scales; 128 elements per two strips (fp8) or per strip
+// (fp4), scale rows 4-byte aligned.  MX = 0: no scales.
+template <int BMT, bool EDGE, typename E, bool SPLIT = false, int MX = 0>
 __global__ __launch_bounds__(THREADS, Tile<BMT>::MIN_WAVES) void gemm_fp8_tile_kernel(
     const uint8_t* __restrict__ A, const uint8_t* __restrict__ Bt, uint16_t* __restrict__ C, int64_t M, int64_t N,
     int64_t K, int64_t lda, int64_t ldb, int64_t ldc, uint32_t tiles_m, uint32_t tiles_n, uint32_t group_m,
     int vec_c, float* __restrict__ part, int64_t k_per_split, const uint8_t* __restrict__ SA, int64_t ldsa,
     const uint8_t* __restrict__ SB, int64_t ldsb, EpiArgs ep) {
     static_assert(E::kGeneral, "the fp8 kernels use the general epilogue");
+    static_assert(MX == 0 || MX == 8 || MX == 4, "scale formats: none, MX fp8, MX fp4");
     static_assert(!(MX && SPLIT), "the MX path has no split-K variant");
     using T = Tile<BMT>;
     constexpr int FM = T::FM, FN = T::FN, COPIES = T::COPIES;
     constexpr int SC_COPIES = MX ? T::SC_COPIES : 0;
+    constexpr bool FP4 = MX == 4;
+    constexpr uint32_t SC_EVERY = FP4 ? 1u : 2u;  // strips per 4-byte scale copy
     using tile2::a_off;
     using tile2::barrier;
     using tile2::dma16;
@@ -214,10 +233,11 @@ __global__ __launch_bounds__(THREADS, Tile<BMT>::MIN_WAVES) void gemm_fp8_tile_k
             off_s[c] = (uint32_t)(r * (is_a ? ldsa : ldsb));
         }
     }
-    // Scale copies of strip kt (even): the blocks of strips kt, kt + 1.
+    // Scale copies of strip kt (kt % SC_EVERY == 0): the blocks of strips
+    // kt .. kt + SC_EVERY - 1.
     auto dma_scale = [&](uint32_t kt, int c) {
-        if constexpr (MX) {
-            const uint32_t q = kt >> 1;
+        if constexpr (MX != 0) {
+            const uint32_t q = kt / SC_EVERY;
             dma4(base_s[c] + 4 * (int64_t)q, off_s[c],
                  lds_base + T::SC_BASE + (q % T::SC_SLOTS) * T::SC_SLOT_BYTES +
                      256u * ((uint32_t)SC_COPIES * wave + (uint32_t)c));
@@ -226,7 +246,7 @@ __global__ __launch_bounds__(THREADS, Tile<BMT>::MIN_WAVES) void gemm_fp8_tile_k
     auto issue = [&](uint32_t slot, uint32_t kt) {
 #pragma unroll
         for (int c = 0; c < 2 * COPIES; ++c) dma_one(slot, kt, c);
-        if (MX && (kt & 1u) == 0u) {
+        if (MX && kt % SC_EVERY == 0u) {
 #pragma unroll
             for (int c = 0; c < SC_COPIES; ++c) dma_scale(kt, c);
         }
@@ -247,15 +267,17 @@ __global__ __launch_bounds__(THREADS, Tile<BMT>::MIN_WAVES) void gemm_fp8_tile_k
         b_ptr[s] = lds_p + T::A_BYTES + a_off(br, ch);
     }
     // MX: scale byte of strip kt for A row ar + 32i (Bt row br + 32j) at
-    // slot (kt/2) % SC_SLOTS, row * 4 + 2 (kt % 2) + lane/32.
+    // slot (kt/SC_EVERY) % SC_SLOTS, row * 4 + b + lane/32 with b = 2 (kt %
+    // 2) (fp8) or 2s for the fp4 instruction s.
     const uint32_t sc_a = T::SC_BASE + ar * 4u + (lane >> 5);
     const uint32_t sc_b = T::SC_BASE + ((uint32_t)T::BM + br) * 4u + (lane >> 5);
 
+    constexpr int SCS = FP4 ? 2 : 1;  // scale bytes per row block and strip
     struct Frags {
         u32x4 a[2][FM];
         u32x4 b[2][FN];
-        uint32_t sa[FM];
-        uint32_t sb[FN];
+        uint32_t sa[SCS][FM];
+        uint32_t sb[SCS][FN];
     };
 
     f32x16 acc[FM][FN];
@@ -267,9 +289,9 @@ __global__ __launch_bounds__(THREADS, Tile<BMT>::MIN_WAVES) void gemm_fp8_tile_k
     // The 2 (FM + FN) fragment reads of one strip, in the order the next
     // step's MFMAs (block row i, then column j) first need them: A0, B0 ..,
     // A1 .., each as its two chunks.
-    // MX adds FM + FN one-byte scale reads (strip kt) after them.
+    // MX adds SCS (FM + FN) one-byte scale reads (strip kt) after them.
     constexpr int FRAG_READS = 2 * (FM + FN);
-    constexpr int READS = FRAG_READS + (MX ? FM + FN : 0);
+    constexpr int READS = FRAG_READS + (MX ? SCS * (FM + FN) : 0);
     auto read_one = [&](Frags& f, uint32_t slot, uint32_t kt, int r) {
         if (r < FRAG_READS) {
             const int q = r >> 1, s = r & 1;
@@ -277,29 +299,38 @@ __global__ __launch_bounds__(THREADS, Tile<BMT>::MIN_WAVES) void gemm_fp8_tile_k
             if (q == 0) f.a[s][0] = read16(a_ptr[s] + so);
             else if (q <= FN) f.b[s][q - 1] = read16(b_ptr[s] + so + 2048u * (q - 1));
             else f.a[s][q - FN] = read16(a_ptr[s] + so + 2048u * (q - FN));
-        } else if constexpr (MX) {
-            const int x = r - FRAG_READS;
-            const uint32_t so = ((kt >> 1) % T::SC_SLOTS) * T::SC_SLOT_BYTES + 2u * (kt & 1u);
-            if (x < FM) f.sa[x] = *(const GR_LDS uint8_t*)(lds_p + sc_a + so + 128u * x);
-            else f.sb[x - FM] = *(const GR_LDS uint8_t*)(lds_p + sc_b + so + 128u * (x - FM));
+        } else if constexpr (MX != 0) {
+            const int x0 = r - FRAG_READS, sc = x0 / (FM + FN), x = x0 % (FM + FN);
+            const uint32_t bsel = FP4 ? 2u * (uint32_t)sc : 2u * (kt & 1u);
+            const uint32_t so = ((kt / SC_EVERY) % T::SC_SLOTS) * T::SC_SLOT_BYTES + bsel;
+            if (x < FM) f.sa[sc][x] = *(const GR_LDS uint8_t*)(lds_p + sc_a + so + 128u * x);
+            else f.sb[sc][x - FM] = *(const GR_LDS uint8_t*)(lds_p + sc_b + so + 128u * (x - FM));
         }
     };
-    constexpr int MFMAS = FM * FN;
+    // fp4: instruction t covers quad t / (FM FN) of the strip.
+    constexpr int MFMAS = (FP4 ? 2 : 1) * FM * FN;
     auto mfma_one = [&](const Frags& f, int t) {
-        const int i = t / FN, j = t % FN;
-        if constexpr (MX) acc[i][j] = mfma_mx(f.b[0][j], f.b[1][j], f.a[0][i], f.a[1][i], acc[i][j], f.sb[j], f.sa[i]);
-        else acc[i][j] = mfma(f.b[0][j], f.b[1][j], f.a[0][i], f.a[1][i], acc[i][j]);
+        const int q = t / (FM * FN), u = t % (FM * FN);
+        const int i = u / FN, j = u % FN;
+        if constexpr (FP4)
+            acc[i][j] = mfma_mx4(f.b[q][j], f.a[q][i], acc[i][j], f.sb[q][j], f.sa[q][i]);
+        else if constexpr (MX == 8)
+            acc[i][j] = mfma_mx(f.b[0][j], f.b[1][j], f.a[0][i], f.a[1][i], acc[i][j], f.sb[0][j], f.sa[0][i]);
+        else
+            acc[i][j] = mfma(f.b[0][j], f.b[1][j], f.a[0][i], f.a[1][i], acc[i][j]);
     };
 
     const uint32_t KT = (uint32_t)(k_len / BK);  // >= 1, whole strips only
 
     // Prologue: strips 0, 1, 2 in flight; strip 0 landed and read.
-    // (MX: the copies of strips 0 and 2 carry scales.)
+    // (MX fp8: the copies of strips 0 and 2 carry scales; MX fp4: all.)
+    constexpr int N1 = 2 * COPIES + (FP4 ? SC_COPIES : 0);  // copies of strip 1
+    constexpr int N2 = 2 * COPIES + SC_COPIES;              // copies of strip 2
     issue(0, 0);
     if (KT > 1) issue(1, 1);
     if (KT > 2) issue(2, 2);
-    if (KT > 2) wait_vmcnt<2 * 2 * COPIES + SC_COPIES>();
-    else if (KT > 1) wait_vmcnt<2 * COPIES>();
+    if (KT > 2) wait_vmcnt<N1 + N2>();
+    else if (KT > 1) wait_vmcnt<N1>();
     else wait_vmcnt<0>();
     barrier();
 
@@ -312,14 +343,14 @@ __global__ __launch_bounds__(THREADS, Tile<BMT>::MIN_WAVES) void gemm_fp8_tile_k
     // kt+1 landed, every wave done with the slot of kt-1); then the other
     // MFMAs with the READS reads of strip kt+1 and the 2*COPIES copies of
     // strip kt+3 (every third operation) spread evenly behind them.
-    // MX: the batch of an even strip adds SC_COPIES scale copies; strip kt+2
-    // (the batch allowed to stay in flight) is even when SLOT is, strip kt+3
-    // (the batch issued here) when SLOT is odd.
+    // MX fp8: the batch of an even strip adds SC_COPIES scale copies; strip
+    // kt+2 (the batch allowed to stay in flight) is even when SLOT is, strip
+    // kt+3 (the batch issued here) when SLOT is odd.  MX fp4: every batch.
     constexpr int PRE = 2;
     auto step = [&](auto slot_c, uint32_t kt, Frags& cur, Frags& nxt) {
         constexpr uint32_t SLOT = decltype(slot_c)::value;
-        constexpr int IN_FLIGHT = 2 * COPIES + (SLOT % 2 == 0 ? SC_COPIES : 0);
-        constexpr int CPS = 2 * COPIES + (SLOT % 2 == 1 ? SC_COPIES : 0);
+        constexpr int IN_FLIGHT = 2 * COPIES + (FP4 || SLOT % 2 == 0 ? SC_COPIES : 0);
+        constexpr int CPS = 2 * COPIES + (FP4 || SLOT % 2 == 1 ? SC_COPIES : 0);
         constexpr int OPS = READS + CPS;
         constexpr int PER = (OPS + (MFMAS - PRE) - 1) / (MFMAS - PRE);
         auto copy_one = [&](int cp) {
@@ -370,7 +401,7 @@ __global__ __launch_bounds__(THREADS, Tile<BMT>::MIN_WAVES) void gemm_fp8_tile_k
         pin();
         if (more) {
             if (kt + 2 < KT) {
-                if (MX && ((kt + 2) & 1u) == 0u) wait_vmcnt<2 * COPIES + SC_COPIES>();
+                if (MX && (kt + 2) % SC_EVERY == 0u) wait_vmcnt<2 * COPIES + SC_COPIES>();
                 else wait_vmcnt<2 * COPIES>();
             } else {
                 wait_vmcnt<0>();
@@ -439,16 +470,18 @@ __device__ __forceinline__ u32x4 load16(const uint8_t* __restrict__ base, int64_
     return u32x4{w[0], w[1], w[2], w[3]};
 }
 
-// E8M0 scale of the 32-k block holding byte k of row `row`: 127 (a factor
-// of 1) outside [0, rows) x [0, K), so that the zeros loaded there stay zero.
+// E8M0 scale of the 32-element block holding element k of row `row`: 127 (a
+// factor of 1) outside [0, rows) x [0, K), so that the zeros loaded there
+// stay zero.
 __device__ __forceinline__ uint32_t load_scale(const uint8_t* __restrict__ S, int64_t ld, int64_t row, int64_t rows,
                                                int64_t k, int64_t K) {
     return (row < rows && k < K) ? (uint32_t)S[row * ld + k / 32] : 127u;
 }
 
-// MX=true: E8M0 scales SA (M x K/32, pitch ldsa) and SB (N x K/32, pitch
-// ldsb); K a multiple of 32.
-template <typename E, bool MX = false>
+// MX = 8 or 4: E8M0 scales SA (M x K/32, pitch ldsa) and SB (N x K/32, pitch
+// ldsb), K (elements) a multiple of 32; for MX fp4 the K, lda and ldb passed
+// here count bytes (two elements each).
+template <typename E, int MX = 0>
 __global__ __launch_bounds__(256) void gemm_fp8_guarded_kernel(const uint8_t* __restrict__ A,
                                                               const uint8_t* __restrict__ Bt,
                                                               uint16_t* __restrict__ C, int64_t M, int64_t N,
@@ -474,8 +507,9 @@ __global__ __launch_bounds__(256) void gemm_fp8_guarded_kernel(const uint8_t* __
 
     // Lane half h takes chunks h and 2 + h (16 bytes each) of each 64-byte k
     // step, for both operands: the assignment of the pipelined kernel, so the
-    // two kernels feed the matrix cores identical operands.  MX: lane half h
-    // supplies the scale of the 32-k block k0/32 + h of its row.
+    // two kernels feed the matrix cores identical operands.  MX fp8: lane
+    // half h supplies the scale of block k0/32 + h of its row; MX fp4: chunk
+    // s of lane half h holds elements 2 k0 + 64s + 32h .. + 31, one block.
     for (int64_t k0 = 0; k0 < K; k0 += BK) {
         u32x4 a[2][2], b[2][2];
 #pragma unroll
@@ -486,7 +520,7 @@ __global__ __launch_bounds__(256) void gemm_fp8_guarded_kernel(const uint8_t* __
 #pragma unroll
             for (int j = 0; j < 2; ++j) b[j][s] = load16(Bt, ldb, n0 + 32 * j + r, N, kc, K);
         }
-        if constexpr (MX) {
+        if constexpr (MX == 8) {
             const int64_t kb = k0 + 32 * h;
             uint32_t sa[2], sb[2];
 #pragma unroll
@@ -498,6 +532,20 @@ __global__ __launch_bounds__(256) void gemm_fp8_guarded_kernel(const uint8_t* __
 #pragma unroll
                 for (int j = 0; j < 2; ++j)
                     acc[i][j] = mfma_mx(b[j][0], b[j][1], a[i][0], a[i][1], acc[i][j], sb[j], sa[i]);
+        } else if constexpr (MX == 4) {
+#pragma unroll
+            for (int s = 0; s < 2; ++s) {
+                const int64_t ke = 2 * k0 + 64 * s + 32 * h;  // first element of this lane's block
+                uint32_t sa[2], sb[2];
+#pragma unroll
+                for (int i = 0; i < 2; ++i) sa[i] = load_scale(SA, ldsa, m0 + 32 * i + r, M, ke, 2 * K);
+#pragma unroll
+                for (int j = 0; j < 2; ++j) sb[j] = load_scale(SB, ldsb, n0 + 32 * j + r, N, ke, 2 * K);
+#pragma unroll
+                for (int i = 0; i < 2; ++i)
+#pragma unroll
+                    for (int j = 0; j < 2; ++j) acc[i][j] = mfma_mx4(b[j][s], a[i][s], acc[i][j], sb[j], sa[i]);
+            }
         } else {
 #pragma unroll
             for (int i = 0; i < 2; ++i)

@@ -1063,17 +1063,22 @@ int entry_fp8(int64_t M, int64_t N, int64_t K, const uint8_t* A, int64_t lda, co
     return run_fp8<gr::Epi<gr::ElemF16>>(p, M, N, K, A, lda, Bt, ldbt, C, ldc, ts, w, ep, s);
 }
 
-// ---- MX fp8: E4M3 operands with one E8M0 scale per 32 k ------------------------
+// ---- MX fp8 and fp4: E4M3 / E2M1 operands with one E8M0 scale per 32 k -----------
 
-// Argument checks of the MX calls: those of the fp8 calls, then K a multiple
-// of the 32-element block (GR_ERR_INVALID_DIM), scale pitches of at least
-// K/32 bytes, scale arrays present and clear of C.
+// mxf: 8 (MX fp8, one byte per element) or 4 (MX fp4, two elements per
+// byte).  Bytes of K elements of one row.
+int64_t mx_row_bytes(int64_t K, int mxf) { return mxf == 4 ? K / 2 : K; }
+
+// Argument checks of the MX calls: K a multiple of the 32-element block
+// (GR_ERR_INVALID_DIM), then those of the fp8 calls on the operand bytes,
+// scale pitches of at least K/32 bytes, scale arrays present and clear of C.
 int validate_mx(int64_t M, int64_t N, int64_t K, uintptr_t A, int64_t lda, uintptr_t SA, int64_t ldsa, uintptr_t Bt,
                 int64_t ldbt, uintptr_t SB, int64_t ldsb, uintptr_t bias, int act, uintptr_t C, int64_t ldc,
-                int out_fmt) {
-    int st = validate_fp8(M, N, K, A, lda, Bt, ldbt, bias, act, C, ldc, out_fmt);
-    if (st != GR_OK) return st;
+                int out_fmt, int mxf) {
+    if (M < 0 || N < 0 || K < 0) return GR_ERR_INVALID_DIM;
     if (K % 32 != 0) return GR_ERR_INVALID_DIM;
+    int st = validate_fp8(M, N, mx_row_bytes(K, mxf), A, lda, Bt, ldbt, bias, act, C, ldc, out_fmt);
+    if (st != GR_OK) return st;
     const int64_t kb = K / 32, kbmin = kb > 1 ? kb : 1;
     if (ldsa < kbmin || ldsb < kbmin) return GR_ERR_INVALID_LD;
     const bool used = M > 0 && N > 0 && K > 0;
@@ -1086,22 +1091,22 @@ int validate_mx(int64_t M, int64_t N, int64_t K, uintptr_t A, int64_t lda, uintp
     return GR_OK;
 }
 
-// The pipelined kernel with MX scales: its fp8 conditions, K a multiple of
-// 128 (every scale copy moves the 4 bytes of two strips) and 4-byte aligned
-// scale rows.
+// The pipelined kernel with MX scales: its fp8 conditions on the operand
+// bytes, K a multiple of 128 elements (every scale copy moves 4 bytes of a
+// row: two strips of MX fp8, one of MX fp4) and 4-byte aligned scale rows.
 bool mx_tile_ok(int64_t M, int64_t N, int64_t K, uintptr_t A, int64_t lda, uintptr_t SA, int64_t ldsa, uintptr_t Bt,
-                int64_t ldbt, uintptr_t SB, int64_t ldsb) {
+                int64_t ldbt, uintptr_t SB, int64_t ldsb, int mxf) {
     using namespace gr::fp8;
-    return fp8_tile_ok(M, N, K, A, lda, Bt, ldbt) && K % 128 == 0 && SA % 4 == 0 && ldsa % 4 == 0 && SB % 4 == 0 &&
-           ldsb % 4 == 0 && ldsa <= MAX_LD && ldsb <= MAX_LD;
+    return fp8_tile_ok(M, N, mx_row_bytes(K, mxf), A, lda, Bt, ldbt) && K % 128 == 0 && SA % 4 == 0 &&
+           ldsa % 4 == 0 && SB % 4 == 0 && ldsb % 4 == 0 && ldsa <= MAX_LD && ldsb <= MAX_LD;
 }
 
 int plan_call_mx(int64_t M, int64_t N, int64_t K, uintptr_t A, int64_t lda, uintptr_t SA, int64_t ldsa,
                  uintptr_t Bt, int64_t ldbt, uintptr_t SB, int64_t ldsb, uintptr_t bias, int act, uintptr_t C,
-                 int64_t ldc, int out_fmt, int forced, gr_plan_t* p) {
-    int st = validate_mx(M, N, K, A, lda, SA, ldsa, Bt, ldbt, SB, ldsb, bias, act, C, ldc, out_fmt);
+                 int64_t ldc, int out_fmt, int mxf, int forced, gr_plan_t* p) {
+    int st = validate_mx(M, N, K, A, lda, SA, ldsa, Bt, ldbt, SB, ldsb, bias, act, C, ldc, out_fmt, mxf);
     if (st != GR_OK) return st;
-    const bool tile_ok = mx_tile_ok(M, N, K, A, lda, SA, ldsa, Bt, ldbt, SB, ldsb);
+    const bool tile_ok = mx_tile_ok(M, N, K, A, lda, SA, ldsa, Bt, ldbt, SB, ldsb, mxf);
     int path = (M == 0 || N == 0) ? GR_PATH_NONE : (tile_ok ? GR_PATH_TILE : GR_PATH_TILE_EDGE);
     if (forced >= 0 && path != GR_PATH_NONE) {
         if ((forced == GR_PATH_TILE && !tile_ok) || (forced != GR_PATH_TILE && forced != GR_PATH_TILE_EDGE))
@@ -1112,8 +1117,9 @@ int plan_call_mx(int64_t M, int64_t N, int64_t K, uintptr_t A, int64_t lda, uint
     return GR_OK;
 }
 
-template <typename E>
-int run_mx(const gr_plan_t& p, int64_t M, int64_t N, int64_t K, const uint8_t* A, int64_t lda, const uint8_t* SA,
+// Kb: bytes of K per row (the kernels count bytes).
+template <typename E, int MXF>
+int run_mx(const gr_plan_t& p, int64_t M, int64_t N, int64_t Kb, const uint8_t* A, int64_t lda, const uint8_t* SA,
            int64_t ldsa, const uint8_t* Bt, int64_t ldbt, const uint8_t* SB, int64_t ldsb, uint16_t* C, int64_t ldc,
            const gr::EpiArgs& ep, hipStream_t stream) {
     using namespace gr::fp8;
@@ -1128,40 +1134,46 @@ int run_mx(const gr_plan_t& p, int64_t M, int64_t N, int64_t K, const uint8_t* A
         const int vc = (int)p.vec_c;
         if (bm == 256) {
             if (whole)
-                return launch(gemm_fp8_tile_kernel<256, false, E, false, true>, p.grid, THREADS, stream, A, Bt, C, M,
-                              N, K, lda, ldbt, ldc, tiles_m, tiles_n, gm, vc, no_part, no_kps, SA, ldsa, SB, ldsb, ep);
-            return launch(gemm_fp8_tile_kernel<256, true, E, false, true>, p.grid, THREADS, stream, A, Bt, C, M, N, K,
+                return launch(gemm_fp8_tile_kernel<256, false, E, false, MXF>, p.grid, THREADS, stream, A, Bt, C, M, N,
+                              Kb, lda, ldbt, ldc, tiles_m, tiles_n, gm, vc, no_part, no_kps, SA, ldsa, SB, ldsb, ep);
+            return launch(gemm_fp8_tile_kernel<256, true, E, false, MXF>, p.grid, THREADS, stream, A, Bt, C, M, N, Kb,
                           lda, ldbt, ldc, tiles_m, tiles_n, gm, vc, no_part, no_kps, SA, ldsa, SB, ldsb, ep);
         }
         if (whole)
-            return launch(gemm_fp8_tile_kernel<128, false, E, false, true>, p.grid, THREADS, stream, A, Bt, C, M, N,
-                          K, lda, ldbt, ldc, tiles_m, tiles_n, gm, vc, no_part, no_kps, SA, ldsa, SB, ldsb, ep);
-        return launch(gemm_fp8_tile_kernel<128, true, E, false, true>, p.grid, THREADS, stream, A, Bt, C, M, N, K,
-                      lda, ldbt, ldc, tiles_m, tiles_n, gm, vc, no_part, no_kps, SA, ldsa, SB, ldsb, ep);
+            return launch(gemm_fp8_tile_kernel<128, false, E, false, MXF>, p.grid, THREADS, stream, A, Bt, C, M, N, Kb,
+                          lda, ldbt, ldc, tiles_m, tiles_n, gm, vc, no_part, no_kps, SA, ldsa, SB, ldsb, ep);
+        return launch(gemm_fp8_tile_kernel<128, true, E, false, MXF>, p.grid, THREADS, stream, A, Bt, C, M, N, Kb, lda,
+                      ldbt, ldc, tiles_m, tiles_n, gm, vc, no_part, no_kps, SA, ldsa, SB, ldsb, ep);
     }
     if (p.path == GR_PATH_TILE_EDGE) {
         const uint32_t tiles_n = (uint32_t)((N + G_BN - 1) / G_BN);
-        return launch(gemm_fp8_guarded_kernel<E, true>, p.grid, 256, stream, A, Bt, C, M, N, K, lda, ldbt, ldc,
-                      tiles_n, (int)p.vec_c, SA, ldsa, SB, ldsb, ep);
+        return launch(gemm_fp8_guarded_kernel<E, MXF>, p.grid, 256, stream, A, Bt, C, M, N, Kb, lda, ldbt, ldc, tiles_n,
+                      (int)p.vec_c, SA, ldsa, SB, ldsb, ep);
     }
     return p.path == GR_PATH_NONE ? GR_OK : GR_ERR_INVALID_PATH;
 }
 
 int entry_mx(int64_t M, int64_t N, int64_t K, const uint8_t* A, int64_t lda, const uint8_t* SA, int64_t ldsa,
              const uint8_t* Bt, int64_t ldbt, const uint8_t* SB, int64_t ldsb, const uint16_t* bias, int act,
-             uint16_t* C, int64_t ldc, int out_fmt, void* stream, int forced) {
+             uint16_t* C, int64_t ldc, int out_fmt, int mxf, void* stream, int forced) {
     gr_plan_t p;
     int st = plan_call_mx(M, N, K, (uintptr_t)A, lda, (uintptr_t)SA, ldsa, (uintptr_t)Bt, ldbt, (uintptr_t)SB, ldsb,
-                          (uintptr_t)bias, act, (uintptr_t)C, ldc, out_fmt, forced, &p);
+                          (uintptr_t)bias, act, (uintptr_t)C, ldc, out_fmt, mxf, forced, &p);
     if (st != GR_OK) return st;
     if (p.path == GR_PATH_NONE) return GR_OK;
     st = check_device();
     if (st != GR_OK) return st;
     const gr::EpiArgs ep{bias, act, 1.0f};
     hipStream_t s = static_cast<hipStream_t>(stream);
+    const int64_t Kb = mx_row_bytes(K, mxf);
+    if (mxf == 4) {
+        if (out_fmt == GR_FMT_BF16)
+            return run_mx<gr::Epi<gr::ElemBF16>, 4>(p, M, N, Kb, A, lda, SA, ldsa, Bt, ldbt, SB, ldsb, C, ldc, ep, s);
+        return run_mx<gr::Epi<gr::ElemF16>, 4>(p, M, N, Kb, A, lda, SA, ldsa, Bt, ldbt, SB, ldsb, C, ldc, ep, s);
+    }
     if (out_fmt == GR_FMT_BF16)
-        return run_mx<gr::Epi<gr::ElemBF16>>(p, M, N, K, A, lda, SA, ldsa, Bt, ldbt, SB, ldsb, C, ldc, ep, s);
-    return run_mx<gr::Epi<gr::ElemF16>>(p, M, N, K, A, lda, SA, ldsa, Bt, ldbt, SB, ldsb, C, ldc, ep, s);
+        return run_mx<gr::Epi<gr::ElemBF16>, 8>(p, M, N, Kb, A, lda, SA, ldsa, Bt, ldbt, SB, ldsb, C, ldc, ep, s);
+    return run_mx<gr::Epi<gr::ElemF16>, 8>(p, M, N, Kb, A, lda, SA, ldsa, Bt, ldbt, SB, ldsb, C, ldc, ep, s);
 }
 
 }  // namespace
@@ -1365,7 +1377,8 @@ int gemm_fp8_bt_plan(int64_t M, int64_t N, int64_t K, const uint8_t* A, int64_t 
 int gemm_mxfp8_bt(int64_t M, int64_t N, int64_t K, const uint8_t* A, int64_t lda, const uint8_t* scale_a,
                   int64_t ld_sa, const uint8_t* Bt, int64_t ldbt, const uint8_t* scale_b, int64_t ld_sb,
                   const uint16_t* bias, int act, uint16_t* C, int64_t ldc, int out_fmt, void* stream) {
-    return entry_mx(M, N, K, A, lda, scale_a, ld_sa, Bt, ldbt, scale_b, ld_sb, bias, act, C, ldc, out_fmt, stream, -1);
+    return entry_mx(M, N, K, A, lda, scale_a, ld_sa, Bt, ldbt, scale_b, ld_sb, bias, act, C, ldc, out_fmt, 8, stream,
+                    -1);
 }
 
 int gemm_mxfp8_bt_forced(int64_t M, int64_t N, int64_t K, const uint8_t* A, int64_t lda, const uint8_t* scale_a,
@@ -1373,7 +1386,7 @@ int gemm_mxfp8_bt_forced(int64_t M, int64_t N, int64_t K, const uint8_t* A, int6
                          const uint16_t* bias, int act, uint16_t* C, int64_t ldc, int out_fmt, void* stream,
                          int path) {
     if (path != GR_PATH_TILE && path != GR_PATH_TILE_EDGE) return GR_ERR_INVALID_PATH;
-    return entry_mx(M, N, K, A, lda, scale_a, ld_sa, Bt, ldbt, scale_b, ld_sb, bias, act, C, ldc, out_fmt, stream,
+    return entry_mx(M, N, K, A, lda, scale_a, ld_sa, Bt, ldbt, scale_b, ld_sb, bias, act, C, ldc, out_fmt, 8, stream,
                     path);
 }
 
@@ -1382,7 +1395,31 @@ int gemm_mxfp8_bt_plan(int64_t M, int64_t N, int64_t K, const uint8_t* A, int64_
                        const uint16_t* bias, int act, const uint16_t* C, int64_t ldc, int out_fmt, gr_plan_t* out) {
     if (!out) return GR_ERR_INVALID_ARG;
     return plan_call_mx(M, N, K, (uintptr_t)A, lda, (uintptr_t)scale_a, ld_sa, (uintptr_t)Bt, ldbt,
-                        (uintptr_t)scale_b, ld_sb, (uintptr_t)bias, act, (uintptr_t)C, ldc, out_fmt, -1, out);
+                        (uintptr_t)scale_b, ld_sb, (uintptr_t)bias, act, (uintptr_t)C, ldc, out_fmt, 8, -1, out);
+}
+
+int gemm_mxfp4_bt(int64_t M, int64_t N, int64_t K, const uint8_t* A, int64_t lda, const uint8_t* scale_a,
+                  int64_t ld_sa, const uint8_t* Bt, int64_t ldbt, const uint8_t* scale_b, int64_t ld_sb,
+                  const uint16_t* bias, int act, uint16_t* C, int64_t ldc, int out_fmt, void* stream) {
+    return entry_mx(M, N, K, A, lda, scale_a, ld_sa, Bt, ldbt, scale_b, ld_sb, bias, act, C, ldc, out_fmt, 4, stream,
+                    -1);
+}
+
+int gemm_mxfp4_bt_forced(int64_t M, int64_t N, int64_t K, const uint8_t* A, int64_t lda, const uint8_t* scale_a,
+                         int64_t ld_sa, const uint8_t* Bt, int64_t ldbt, const uint8_t* scale_b, int64_t ld_sb,
+                         const uint16_t* bias, int act, uint16_t* C, int64_t ldc, int out_fmt, void* stream,
+                         int path) {
+    if (path != GR_PATH_TILE && path != GR_PATH_TILE_EDGE) return GR_ERR_INVALID_PATH;
+    return entry_mx(M, N, K, A, lda, scale_a, ld_sa, Bt, ldbt, scale_b, ld_sb, bias, act, C, ldc, out_fmt, 4, stream,
+                    path);
+}
+
+int gemm_mxfp4_bt_plan(int64_t M, int64_t N, int64_t K, const uint8_t* A, int64_t lda, const uint8_t* scale_a,
+                       int64_t ld_sa, const uint8_t* Bt, int64_t ldbt, const uint8_t* scale_b, int64_t ld_sb,
+                       const uint16_t* bias, int act, const uint16_t* C, int64_t ldc, int out_fmt, gr_plan_t* out) {
+    if (!out) return GR_ERR_INVALID_ARG;
+    return plan_call_mx(M, N, K, (uintptr_t)A, lda, (uintptr_t)scale_a, ld_sa, (uintptr_t)Bt, ldbt,
+                        (uintptr_t)scale_b, ld_sb, (uintptr_t)bias, act, (uintptr_t)C, ldc, out_fmt, 4, -1, out);
 }
 
 const char* gemm_relu_status_string(int status) {

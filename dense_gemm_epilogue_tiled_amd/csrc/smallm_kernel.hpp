@@ -347,7 +347,8 @@ __global__ __launch_bounds__(256) void gemm_relu_smallm_reduce_kernel(const floa
             f32x4 sum = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll 4
             for (int s = 0; s < splits; ++s) {
-                const f32x4 v = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(part + (int64_t)s * total) + o);
+                const f32x4* src = reinterpret_cast<const f32x4*>(part + (int64_t)s * total) + o;
+                const f32x4 v = __builtin_nontemporal_load(src);
                 sum = f32x4{sum[0] + v[0], sum[1] + v[1], sum[2] + v[2], sum[3] + v[3]};
             }
             const int64_t m = 4 * o / N, n = 4 * o - m * N;

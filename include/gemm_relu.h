@@ -557,6 +557,49 @@ int gemm_mxfp8_bt_plan(int64_t M, int64_t N, int64_t K,
                        const uint16_t* C, int64_t ldc, int out_fmt,
                        gr_plan_t* out);
 
+/*
+ * ---- MX fp4 (block-scaled) operands ---------------------------------------------
+ * gemm_mxfp8_bt with OCP fp4 E2M1 elements (1 sign bit, 2 exponent bits with
+ * bias 1, 1 fraction bit: magnitudes 0, 0.5, 1, 1.5, 2, 3, 4, 6) packed two
+ * per byte, element k of a row in the low nibble of byte k/2 when k is even
+ * and in the high nibble when it is odd.  K counts elements (a multiple of
+ * 32); lda and ldbt count bytes (>= K/2); the scales are as for MX fp8 (one
+ * E8M0 byte per 32 elements).  The pages name NVFP4 block-scaled MMA (fp4
+ * elements with per-block scales; blog "TileLang programming basics", table
+ * of section 5.4); MX fp4 is the fp4 block format gfx950 scales in hardware.
+ * Paths: GR_PATH_TILE (K % 128 == 0, 16-byte aligned rows, 4-byte aligned
+ * scale rows) or GR_PATH_TILE_EDGE.  Other conventions as gemm_mxfp8_bt.
+ */
+int gemm_mxfp4_bt(int64_t M, int64_t N, int64_t K,
+                  const uint8_t* A, int64_t lda,
+                  const uint8_t* scale_a, int64_t ld_sa,
+                  const uint8_t* Bt, int64_t ldbt,
+                  const uint8_t* scale_b, int64_t ld_sb,
+                  const uint16_t* bias, int act,
+                  uint16_t* C, int64_t ldc, int out_fmt,
+                  void* stream);
+
+/* gemm_mxfp4_bt on a given path (GR_PATH_TILE or GR_PATH_TILE_EDGE).
+   Test hook. */
+int gemm_mxfp4_bt_forced(int64_t M, int64_t N, int64_t K,
+                         const uint8_t* A, int64_t lda,
+                         const uint8_t* scale_a, int64_t ld_sa,
+                         const uint8_t* Bt, int64_t ldbt,
+                         const uint8_t* scale_b, int64_t ld_sb,
+                         const uint16_t* bias, int act,
+                         uint16_t* C, int64_t ldc, int out_fmt,
+                         void* stream, int path);
+
+/* Pure planner for gemm_mxfp4_bt (no GPU needed). */
+int gemm_mxfp4_bt_plan(int64_t M, int64_t N, int64_t K,
+                       const uint8_t* A, int64_t lda,
+                       const uint8_t* scale_a, int64_t ld_sa,
+                       const uint8_t* Bt, int64_t ldbt,
+                       const uint8_t* scale_b, int64_t ld_sb,
+                       const uint16_t* bias, int act,
+                       const uint16_t* C, int64_t ldc, int out_fmt,
+                       gr_plan_t* out);
+
 /* Static, NUL-terminated name of a status code ("GR_OK", "GR_ERR_ALIAS", ...).
    Unknown codes give "GR_ERR_UNKNOWN". */
 const char* gemm_relu_status_string(int status);

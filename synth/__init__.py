@@ -189,3 +189,54 @@ def mx_operands(M: int, N: int, K: int, seed: int, lda: int | None = None, ldbt:
         out.append((E, S))
     (A, SA), (Bt, SB) = out
     return A, SA, Bt, SB
+
+
+E2M1_VALUES = np.array([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0])
+
+
+def e2m1_codes(v: np.ndarray) -> np.ndarray:
+    """Round to OCP fp4 E2M1 (nearest, ties to the even code, saturating at
+    +-6); returns codes 0..15 (sign in bit 3)."""
+    a = np.minimum(np.abs(v), 6.0)
+    d = np.abs(a[..., None] - E2M1_VALUES)
+    best = d.min(axis=-1, keepdims=True)
+    cand = np.where(d == best, np.arange(8), 99)
+    even = np.where(cand % 2 == 0, cand, 99).min(axis=-1)
+    code = np.where(even < 99, even, cand.min(axis=-1)).astype(np.uint8)
+    return code | np.where(np.signbit(v) & (code != 0), 8, 0).astype(np.uint8)
+
+
+def mxfp4_operands(M: int, N: int, K: int, seed: int, lda: int | None = None, ldbt: int | None = None,
+                   ldsa: int | None = None, ldsb: int | None = None, spread: int = 2):
+    """A, SA, Bt, SB for the MX fp4 product: N(0,1) values times 2^u (u per
+    32-k block from [-spread, spread]) quantised the OCP MX way -- shared
+    exponent floor(log2 max|x|) - 2 per block (2 = the largest E2M1
+    exponent), elements rounded to E2M1 -- and packed two per byte (k even in
+    the low nibble).  lda, ldbt count bytes; padding bytes hold 0x77 (6.0
+    twice), scale padding the NaN code 255."""
+    torch = _torch()
+    gen = torch.Generator().manual_seed(seed)
+    kb = K // 32
+    lda = K // 2 if lda is None else lda
+    ldbt = K // 2 if ldbt is None else ldbt
+    ldsa = max(kb, 1) if ldsa is None else ldsa
+    ldsb = max(kb, 1) if ldsb is None else ldsb
+    out = []
+    for rows, ld, lds in ((M, lda, ldsa), (N, ldbt, ldsb)):
+        P = np.full((rows, max(ld, 1)), 0x77, dtype=np.uint8)
+        S = np.full((rows, max(lds, 1)), 255, dtype=np.uint8)
+        if rows and K:
+            x = torch.randn(rows, K, generator=gen, dtype=torch.float64).numpy()
+            u = torch.randint(-spread, spread + 1, (rows, kb), generator=gen).numpy()
+            x = x * np.repeat(np.exp2(u), 32, axis=1)
+            blocks = x.reshape(rows, kb, 32)
+            amax = np.abs(blocks).max(axis=2)
+            with np.errstate(divide="ignore"):
+                e = np.where(amax > 0, np.floor(np.log2(np.where(amax > 0, amax, 1.0))) - 2, 0).astype(np.int64)
+            e = np.clip(e, -127, 127)
+            codes = e2m1_codes((blocks / np.exp2(e)[:, :, None]).reshape(rows, K))
+            P[:, :K // 2] = codes[:, 0::2] | (codes[:, 1::2] << 4)
+            S[:, :kb] = (e + 127).astype(np.uint8)
+        out.append((P, S))
+    (A, SA), (Bt, SB) = out
+    return A, SA, Bt, SB

@@ -556,6 +556,28 @@ def test_mxfp8_planner_and_checks_need_no_gpu():
     assert f(0, 8, 64, 0, 64, 0, 2, BASE_B, 64, SB, 2, None, 1, 0, 8) == gr.GR_OK
 
 
+def test_mxfp4_planner_and_checks_need_no_gpu():
+    """gemm_mxfp4_bt: K counts elements, pitches count bytes (>= K/2); the
+    pipelined kernel for K % 128 == 0 with 16-byte rows, else guarded."""
+    SA, SB = BASE_C + (1 << 31), BASE_C + (1 << 32)
+
+    def plan(M, N, K, lda=None, ldbt=None):
+        kb = max(K // 32, 1)
+        return gr.gemm_mxfp4_bt_plan(M, N, K, BASE_A, lda or max(K // 2, 1), SA, kb, BASE_B, ldbt or max(K // 2, 1),
+                                     SB, kb, None, 1, BASE_C, max(N, 1), gr.GR_FMT_F16)
+    st, p = plan(4096, 4096, 4096)
+    assert st == gr.GR_OK and (p["path"], p["block_m"], p["grid"]) == (gr.GR_PATH_TILE, 256, 256)
+    assert plan(300, 270, 384)[1]["path"] == gr.GR_PATH_TILE          # 192-byte rows
+    assert plan(300, 270, 96)[1]["path"] == gr.GR_PATH_TILE_EDGE      # K % 128 != 0
+    assert plan(300, 270, 384, lda=200)[1]["path"] == gr.GR_PATH_TILE_EDGE
+    assert plan(300, 270, 384, lda=191)[0] == gr.GR_ERR_INVALID_LD    # fewer than K/2 bytes
+    assert plan(300, 270, 100)[0] == gr.GR_ERR_INVALID_DIM            # K % 32 != 0
+    assert gr.gemm_mxfp4_bt(-1, 8, 64, BASE_A, 32, SA, 2, BASE_B, 32, SB, 2, None, 1, BASE_C, 8) == \
+        gr.GR_ERR_INVALID_DIM
+    assert gr.gemm_mxfp4_bt_forced(300, 270, 96, BASE_A, 48, SA, 3, BASE_B, 48, SB, 3, None, 1, BASE_C, 270,
+                                   gr.GR_FMT_F16, None, gr.GR_PATH_TILE) == gr.GR_ERR_INVALID_PATH
+
+
 def test_fp8_planner_and_checks_need_no_gpu():
     """gemm_fp8_bt: the pipelined kernel for K % 64 == 0 with 16-byte rows (any
     M, N), the guarded kernel otherwise; argument errors before any HIP call."""
