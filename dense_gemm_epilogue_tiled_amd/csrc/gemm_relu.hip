@@ -241,9 +241,8 @@ bool pack_layout(int64_t M, int64_t N, int64_t K, uintptr_t A, int64_t lda, uint
     return true;
 }
 
-void fill_plan(int path, int64_t M, int64_t N, int64_t K, uintptr_t A, int64_t lda, uintptr_t B,
-               int64_t ldb, uintptr_t C, int64_t ldc, const Pack& pk, const SmallMSplit& sp, const TileSplit& ts,
-               gr_plan_t* p) {
+void fill_plan(int path, int64_t M, int64_t N, uintptr_t A, int64_t lda, uintptr_t B, int64_t ldb, uintptr_t C,
+               int64_t ldc, const Pack& pk, const SmallMSplit& sp, const TileSplit& ts, gr_plan_t* p) {
     std::memset(p, 0, sizeof(*p));
     p->path = path;
     if (path == GR_PATH_TILE || path == GR_PATH_TILE_PACKED || path == GR_PATH_TILE_SPLIT) {
@@ -565,7 +564,7 @@ int plan_call(int64_t M, int64_t N, int64_t K, uintptr_t a, int64_t lda, uintptr
         }
         path = forced;
     }
-    fill_plan(path, M, N, K, a, lda, b, ldb, c, ldc, *pk, *sp, *ts, p);
+    fill_plan(path, M, N, a, lda, b, ldb, c, ldc, *pk, *sp, *ts, p);
     return GR_OK;
 }
 
@@ -691,12 +690,12 @@ int choose_path_bt(int64_t M, int64_t N, int64_t K, uintptr_t A, int64_t lda, ui
     return GR_PATH_TILE_EDGE;
 }
 
-void fill_plan_bt(int path, int64_t M, int64_t N, int64_t K, uintptr_t A, int64_t lda, uintptr_t Bt, int64_t ldbt,
-                  uintptr_t C, int64_t ldc, gr_plan_t* p) {
+void fill_plan_bt(int path, int64_t M, int64_t N, uintptr_t A, int64_t lda, uintptr_t Bt, int64_t ldbt, uintptr_t C,
+                  int64_t ldc, gr_plan_t* p) {
     Pack pk;
     SmallMSplit sp;
     TileSplit ts;
-    fill_plan(path == GR_PATH_SMALL_M ? GR_PATH_NONE : path, M, N, K, A, lda, Bt, ldbt, C, ldc, pk, sp, ts, p);
+    fill_plan(path == GR_PATH_SMALL_M ? GR_PATH_NONE : path, M, N, A, lda, Bt, ldbt, C, ldc, pk, sp, ts, p);
     p->path = path;
     if (path == GR_PATH_TILE) {
         p->block_k = gr::tile2::BK;
@@ -816,7 +815,7 @@ int plan_call_bt(int64_t M, int64_t N, int64_t K, uintptr_t a, int64_t lda, uint
         }
         path = forced;
     }
-    fill_plan_bt(path, M, N, K, a, lda, bt, ldbt, c, ldc, p);
+    fill_plan_bt(path, M, N, a, lda, bt, ldbt, c, ldc, p);
     return GR_OK;
 }
 

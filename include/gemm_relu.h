@@ -1,6 +1,7 @@
 /*
  * gemm_relu.h -- C ABI of the MI355X (gfx950) fused fp16 GEMM + ReLU library
- * (with bfloat16, transposed-B, bias + activation and fp8 variants further down).
+ * (with bfloat16, transposed-B, bias + activation, fp8 and block-scaled MX
+ * fp8 / fp4 variants further down).
  *
  * The one operation:  C := ReLU(A * B)
  *   A  M x K, B  K x N, C  M x N, all IEEE binary16, row-major with a row
@@ -53,7 +54,7 @@ extern "C" {
 
 /* ---- status codes --------------------------------------------------------- */
 #define GR_OK                        0
-#define GR_ERR_INVALID_DIM          -1 /* M, N or K negative                              */
+#define GR_ERR_INVALID_DIM          -1 /* M, N or K negative (MX calls: K % 32 != 0)     */
 #define GR_ERR_INVALID_LD           -2 /* lda < max(1,K), ldb < max(1,N) or ldc < max(1,N) */
 #define GR_ERR_NULL_PTR             -3 /* NULL pointer for a non-empty operand            */
 #define GR_ERR_ALIAS                -4 /* C's byte range overlaps A's or B's              */
