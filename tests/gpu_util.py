@@ -74,11 +74,29 @@ def as_f64(bits, fmt: str = "f16") -> np.ndarray:
     return b.view(np.float16).astype(np.float64)
 
 
-def parity_report(got_bits, ref_bits, fmt: str = "f16"):
+# The fp8 / fp4 matrix-core instructions (v_mfma_*_f8f6f4) do not add their
+# 64 products in IEEE fp32 order: measured against the exact sum, their error
+# beyond the output rounding reaches 2^-17.6 of sum_k |a_k b_k| (MX fp8 with
+# block magnitudes spread over 16x), 2^-19.3 with plain per-tensor fp8 (the
+# fp16 instruction: 2^-27.5).  The fp8 paths are checked with this allowance
+# on top of the common bar: F8_SUM_ALLOWANCE * sum_k |a_k b_k| * 1.2 (the
+# steepest activation slope), where the sum is of the dequantised products.
+F8_SUM_ALLOWANCE = 2.0 ** -16
+
+
+def f8_extra(abs_sum):
+    """Extra absolute allowance for an fp8 / MX result whose dequantised
+    products have absolute sum ``abs_sum`` (array)."""
+    return 1.2 * F8_SUM_ALLOWANCE * np.asarray(abs_sum, dtype=np.float64)
+
+
+def parity_report(got_bits, ref_bits, fmt: str = "f16", extra=None):
     g = as_f64(got_bits, fmt)
     o = as_f64(ref_bits, fmt)
     err = np.abs(g - o)
     bound = ATOL + RTOL * np.abs(o)
+    if extra is not None:
+        bound = bound + extra
     bad = ~(err <= bound) | ~np.isfinite(g)
     rel = err / np.maximum(np.abs(o), 1e-30)
     rep = {
@@ -95,8 +113,8 @@ def parity_report(got_bits, ref_bits, fmt: str = "f16"):
     return rep
 
 
-def assert_parity(got_bits, ref_bits, label="", fmt: str = "f16"):
-    rep = parity_report(got_bits, ref_bits, fmt)
+def assert_parity(got_bits, ref_bits, label="", fmt: str = "f16", extra=None):
+    rep = parity_report(got_bits, ref_bits, fmt, extra)
     assert rep["violations"] == 0, "%s: %s" % (label, rep)
     return rep
 
