@@ -167,14 +167,18 @@ bool use_large_tiles(int64_t M, int64_t N) {
 }
 
 // Split-K of the 128 x 128 tile path (workspace): when the small tiles do not
-// fill the chip (two workgroups per CU, 512 in all) and K is long, each tile's
-// K range is split S ways (S x tiles <= 512, at least 8 strips per split,
-// S <= 16); fp32 partial sums S x M x N go to the workspace and a second pass
-// adds them in order and applies ReLU.  The planner splits only when that
-// saves each workgroup at least 96 strips (measured: the second pass and the
-// partial sums cost about as much as 60-70 strips; 1024^3 and 2048^3 run
-// slower split, 1024 x 1024 x 4096 and up faster).
-constexpr int64_t kTileSplitMinSavedStrips = 96;
+// fill the chip and K is long, each tile's K range is split S ways (S x tiles
+// <= 256, one workgroup per CU; at least 8 strips per split, S <= 16); fp32
+// partial sums S x M x N go to the workspace and a second pass adds them in
+// order and applies ReLU.  Filling both workgroup slots of every CU (S x
+// tiles <= 512) measured 10-25% slower: the extra partial sums cost more than
+// the second slot gains (fp16 1024 x 1024 x 4096: 27.1 -> 23.4 us, 128 x 8192
+// x 4096: 30.3 -> 26.1 us; fp8 128 x 8192 x 8192: 30.4 -> 23.7 us).  The
+// planner splits only when that saves each workgroup at least 64 strips
+// (measured, fp16 and fp8 alike: 64 saved strips win -- fp16 256 x 8192 x
+// 4096 40.1 -> 34.4 us, fp8 256 x 8192 x 8192 39.0 -> 32.3 us; 32 saved
+// strips tie; fp8 1024 x 1024 x 4096 with 48 saved loses, 15.6 -> 19.3 us).
+constexpr int64_t kTileSplitMinSavedStrips = 64;
 struct TileSplit {
     int64_t splits = 0, k_per_split = 0, bytes = 0;
 };
@@ -187,7 +191,7 @@ bool tile_split_layout(int64_t M, int64_t N, int64_t K, bool allow_one, TileSpli
                        int64_t bk = gr::tile128::BK, int64_t min_k = kTileMinSplitK) {
     using namespace gr::tile128;
     const int64_t tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
-    int64_t S = 512 / tiles;
+    int64_t S = 256 / tiles;
     if (S > K / min_k) S = K / min_k;
     if (S > kTileMaxSplits) S = kTileMaxSplits;
     if (S < 1) S = 1;

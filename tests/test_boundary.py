@@ -266,16 +266,19 @@ def test_small_m_split_plan():
 
 
 def test_tile_split_plan():
-    # 1024 x 1024: 64 tiles of 128 x 128; K = 16384 -> 8 splits (512 workgroups)
+    # 1024 x 1024: 64 tiles of 128 x 128; K = 16384 -> 4 splits (256 workgroups, one per CU)
     st, size = ws_size(1024, 1024, 16384)
-    assert st == gr.GR_OK and size == 8 * 1024 * 1024 * 4
+    assert st == gr.GR_OK and size == 4 * 1024 * 1024 * 4
     st, p = plan_ws(1024, 1024, 16384, size)
-    assert p["path"] == gr.GR_PATH_TILE_SPLIT and p["split_k"] == 8 and p["grid"] == 512
+    assert p["path"] == gr.GR_PATH_TILE_SPLIT and p["split_k"] == 4 and p["grid"] == 256
     assert p["block_m"] == 128 and p["workspace"] == size
-    # K = 4096: 8 splits of 512 save 112 of 128 strips per workgroup
-    assert plan_ws(1024, 1024, 4096, 1 << 30)[1]["split_k"] == 8
-    # a split must save at least 96 strips: not at 1024^3 (4 splits save 24)
-    # nor 2048^3 (2 splits save 32); large tiles that fill the chip never split
+    # K = 4096: 4 splits of 1024 save 96 of 128 strips per workgroup
+    assert plan_ws(1024, 1024, 4096, 1 << 30)[1]["split_k"] == 4
+    # 128 tiles: 2 splits; at K = 4096 they save 64 of 128 strips, just enough
+    assert plan_ws(256, 8192, 4096, 1 << 30)[1]["split_k"] == 2
+    assert plan_ws(256, 8192, 2048, 1 << 30)[1]["path"] == gr.GR_PATH_TILE
+    # a split must save at least 64 strips: not at 1024^3 (4 splits save 24)
+    # nor 2048^3 (256 tiles); large tiles that fill the chip never split
     assert ws_size(1024, 1024, 1024) == (gr.GR_OK, 0)
     assert ws_size(2048, 2048, 2048) == (gr.GR_OK, 0)
     assert ws_size(1024, 1024, 256) == (gr.GR_OK, 0)
@@ -495,8 +498,8 @@ def test_fp8_split_planner_and_checks_need_no_gpu():
         assert st == gr.GR_OK
         return b
     p = plan(128, 8192, 8192)
-    assert (p["path"], p["split_k"], p["grid"], p["block_m"]) == (gr.GR_PATH_TILE_SPLIT, 8, 512, 128)
-    assert p["workspace"] == size(128, 8192, 8192) == 8 * 128 * 8192 * 4
+    assert (p["path"], p["split_k"], p["grid"], p["block_m"]) == (gr.GR_PATH_TILE_SPLIT, 4, 256, 128)
+    assert p["workspace"] == size(128, 8192, 8192) == 4 * 128 * 8192 * 4
     assert plan(128, 8192, 8192, size(128, 8192, 8192) - 256)["path"] == gr.GR_PATH_TILE   # too small
     assert plan(128, 8192, 8192, 0)["path"] == gr.GR_PATH_TILE
     assert plan(512, 8192, 8192)["path"] == gr.GR_PATH_TILE and size(512, 8192, 8192) == 0   # 256 tiles
@@ -509,7 +512,7 @@ def test_fp8_split_planner_and_checks_need_no_gpu():
         p = plan(M, N, K)
         assert p["path"] == gr.GR_PATH_TILE_SPLIT, (M, N, K)
         tiles = ((M + 127) // 128) * ((N + 127) // 128)
-        assert p["grid"] == tiles * p["split_k"] and 2 <= p["split_k"] <= 16 and tiles * p["split_k"] <= 512
+        assert p["grid"] == tiles * p["split_k"] and 2 <= p["split_k"] <= 16 and tiles * p["split_k"] <= 256
     f = gr.gemm_fp8_bt_ws
     ws = BASE_C + (1 << 32)
     args = (128, 8192, 8192, BASE_A, 8192, BASE_B, 8192, 1.0, 1.0)

@@ -480,10 +480,11 @@ def test_ws_call_picks_split_path_for_narrow_small_m():
 
 TILE_SPLIT_CASES = [
     # M, N, K, lda, ldb, ldc
-    (1024, 1024, 16384, 16384, 1024, 1024),  # 64 tiles x 8 splits
+    (1024, 1024, 16384, 16384, 1024, 1024),  # 64 tiles x 4 splits
     (128, 128, 1024, 1024, 128, 128),        # one tile, 4 splits
     (300, 520, 4096, 4104, 520, 521),        # partial tiles, padded A, odd ldc
-    (640, 1000, 2080, 2080, 1000, 1000),     # 40 tiles x 8 splits, last split 2 strips deep
+    (640, 1000, 2080, 2080, 1000, 1000),     # 40 tiles x 6 splits of 11 strips, the last 10 deep
+    (640, 1000, 1568, 1568, 1000, 1000),     # 40 tiles x 6 splits of 9 strips, the last 4 deep
 ]
 
 

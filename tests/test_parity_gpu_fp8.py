@@ -245,7 +245,7 @@ def test_fp8_split_every_activation(act):
 
 
 def test_fp8_split_mid_m_sampled():
-    """128 x 8192 x 8192 (64 tiles, 8 splits): the planner's split on the
+    """128 x 8192 x 8192 (64 tiles, 4 splits): the planner's split on the
     shape it is for, sampled against the oracle, and against the unsplit
     kernel within the tolerance."""
     M, N, K = 128, 8192, 8192
