@@ -362,6 +362,9 @@ EXTRA_SHAPES = [
     ("bias + GELU (tanh), MLP projection", 8192, 28672, 8192, "epi:f16:gelu_tanh"),
     ("bias + SiLU, bfloat16, MLP projection", 8192, 28672, 8192, "epi:bf16:silu"),
     ("bias + SiLU, small-M", 8, 16384, 8192, "epi:f16:silu"),
+    ("linear layer (weight N x K), bfloat16, bias + GELU", 4096, 4096, 4096, "lin:bf16:gelu"),
+    ("linear layer, bfloat16, bias + SiLU, MLP projection", 8192, 28672, 8192, "lin:bf16:silu"),
+    ("linear layer, fp16, bias + GELU (tanh), small-M", 8, 16384, 8192, "lin:f16:gelu_tanh"),
     ("fp8 e4m3, square", 4096, 4096, 4096, "fp8"),
     ("fp8 e4m3, square 8192", 8192, 8192, 8192, "fp8"),
     ("fp8 e4m3, MLP projection", 8192, 28672, 8192, "fp8"),
@@ -449,6 +452,14 @@ def extra_shapes(gr, torch, reps=30):
                 runs["vendor"] = vendor
             except Exception as e:  # the vendor fp8 path may be missing
                 row["vendor_error"] = str(e)[:120]
+        elif layout.startswith("lin:"):
+            act = layout.split(":")[2]
+            W = B.t().contiguous()  # N x K
+            bias = torch.randn(N, generator=g, device="cuda").to(dt)
+            fn = {"gelu": torch.nn.functional.gelu, "silu": torch.nn.functional.silu,
+                  "gelu_tanh": lambda x: torch.nn.functional.gelu(x, approximate="tanh")}[act]
+            runs["ours"] = lambda: gr.linear(A, W, bias, act, C, stream)
+            runs["vendor"] = lambda: fn(torch.nn.functional.linear(A, W, bias))
         elif layout.startswith("epi:"):
             act = layout.split(":")[2]
             bias = torch.randn(N, generator=g, device="cuda").to(dt)

@@ -134,6 +134,8 @@ def lib() -> ctypes.CDLL:
             l.gemm_relu_bf16_forced_ws.restype = i32
             l.gemm_bias_act_ws.argtypes = [i64, i64, i64, p, i64, p, i64, p, i32, p, i64, i32, p, i64, p, i32]
             l.gemm_bias_act_ws.restype = i32
+            l.gemm_bias_act_bt.argtypes = [i64, i64, i64, p, i64, p, i64, p, i32, p, i64, i32, p, i32]
+            l.gemm_bias_act_bt.restype = i32
             for nm in ("gemm_bias_act_f16", "gemm_bias_act_bf16"):
                 getattr(l, nm).argtypes = [i64, i64, i64, p, i64, p, i64, p, i32, p, i64, p]
                 getattr(l, nm).restype = i32
@@ -280,6 +282,12 @@ def gemm_bias_act_ws(M, N, K, A, lda, B, ldb, bias, act, C, ldc, fmt, workspace,
     """act(A.B + bias) in fmt (GR_FMT_F16 / GR_FMT_BF16) with a caller workspace; path -1 = planner."""
     return lib().gemm_bias_act_ws(M, N, K, _ptr(A), lda, _ptr(B), ldb, _ptr(bias), act, _ptr(C), ldc, fmt,
                                   _ptr(workspace), workspace_bytes, _ptr(stream), path)
+
+
+def gemm_bias_act_bt(M, N, K, A, lda, Bt, ldbt, bias, act, C, ldc, fmt=GR_FMT_F16, stream=None, path=-1) -> int:
+    """act(A.Bt^T + bias) with B given transposed (N x K), fp16 or bfloat16; path -1 = planner."""
+    return lib().gemm_bias_act_bt(M, N, K, _ptr(A), lda, _ptr(Bt), ldbt, _ptr(bias), act, _ptr(C), ldc, fmt,
+                                  _ptr(stream), path)
 
 
 def gemm_bias_act_f16_forced(M, N, K, A, lda, B, ldb, bias, act, C, ldc, stream=None, path=GR_PATH_TILE_EDGE) -> int:
@@ -621,4 +629,40 @@ def gemm_mxfp8(a, scale_a, bt, scale_b, bias=None, act="relu", out_dtype=None, o
     st = gemm_mxfp8_bt(*args) if path is None else gemm_mxfp8_bt_forced(*args, path)
     if st != GR_OK:
         raise GemmReluError(st, "gemm_mxfp8_bt")
+    return out
+
+
+def linear(x, weight, bias=None, act="none", out=None, stream=None, path=None):
+    """Tensor convenience in the layout of a linear layer:
+    ``out = act(x @ weight.T + bias)`` with ``x`` (M x K) and ``weight``
+    (N x K) both float16 or both bfloat16 on the GPU (unit column stride),
+    ``bias`` None or N values of the same dtype, ``act`` a key of ACT_CODES
+    (default: none) or a GR_ACT_* code."""
+    import torch
+    if x.dtype not in (torch.float16, torch.bfloat16) or weight.dtype != x.dtype:
+        raise TypeError("x and weight must both be float16 or both bfloat16")
+    if x.dim() != 2 or weight.dim() != 2 or x.shape[1] != weight.shape[1]:
+        raise ValueError("shapes do not form x @ weight.T: %s, %s" % (tuple(x.shape), tuple(weight.shape)))
+    M, K = x.shape
+    N = weight.shape[0]
+    code = ACT_CODES[act] if isinstance(act, str) else int(act)
+    if bias is not None:
+        if bias.dtype != x.dtype or bias.dim() != 1 or bias.shape[0] != N or (N > 1 and bias.stride(0) != 1):
+            raise ValueError("bias must be a contiguous 1-D tensor of N values of x's dtype")
+    if out is None:
+        out = torch.empty((M, N), dtype=x.dtype, device=x.device)
+    elif out.dtype != x.dtype:
+        raise TypeError("out must have x's dtype")
+    for t in (x, weight, out):
+        if t.numel() and t.stride(1) != 1:
+            raise ValueError("tensors need unit column stride")
+    lda = max(x.stride(0), 1) if M > 1 else max(K, 1)
+    ldbt = max(weight.stride(0), 1) if N > 1 else max(K, 1)
+    ldc = max(out.stride(0), 1) if M > 1 else max(N, 1)
+    bptr = bias.data_ptr() if bias is not None and bias.numel() else None
+    fmt = GR_FMT_BF16 if x.dtype == torch.bfloat16 else GR_FMT_F16
+    st = gemm_bias_act_bt(M, N, K, x.data_ptr(), lda, weight.data_ptr(), ldbt, bptr, code, out.data_ptr(), ldc, fmt,
+                          _stream_handle(stream), -1 if path is None else path)
+    if st != GR_OK:
+        raise GemmReluError(st, "gemm_bias_act_bt")
     return out

@@ -722,20 +722,21 @@ void fill_plan_bt(int path, int64_t M, int64_t N, uintptr_t A, int64_t lda, uint
     }
 }
 
-template <int VA, int VB>
+template <int VA, int VB, typename E>
 int launch_tile_bt(const gr_plan_t& p, int64_t M, int64_t N, int64_t K, const uint16_t* A, int64_t lda,
                    const uint16_t* Bt, int64_t ldbt, uint16_t* C, int64_t ldc, const gr::EpiArgs& ep,
                    hipStream_t stream) {
     using namespace gr::tile;
     const uint32_t tiles_m = (uint32_t)((M + BM - 1) / BM);
     const uint32_t tiles_n = (uint32_t)((N + BN - 1) / BN);
-    return launch(gemm_relu_tile_kernel<true, VA, VB, true>, p.grid, THREADS, stream, A, Bt, C, M, N, K, lda, ldbt,
+    return launch(gemm_relu_tile_kernel<true, VA, VB, true, E>, p.grid, THREADS, stream, A, Bt, C, M, N, K, lda, ldbt,
                   ldc, tiles_m, tiles_n, (uint32_t)p.group_m, (int)p.vec_c, ep);
 }
 
+// E: ElemF16 (the fused ReLU; ep is ignored) or Epi<ElemF16 / ElemBF16>.
+template <typename E>
 int run_bt(const gr_plan_t& p, int64_t M, int64_t N, int64_t K, const uint16_t* A, int64_t lda, const uint16_t* Bt,
-           int64_t ldbt, uint16_t* C, int64_t ldc, hipStream_t stream) {
-    const gr::EpiArgs ep{nullptr, gr::kActRelu, 1.0f};  // the fused ReLU kernels ignore it
+           int64_t ldbt, uint16_t* C, int64_t ldc, const gr::EpiArgs& ep, hipStream_t stream) {
     switch (p.path) {
         case GR_PATH_NONE: return GR_OK;
         case GR_PATH_SMALL_M: {
@@ -744,17 +745,17 @@ int run_bt(const gr_plan_t& p, int64_t M, int64_t N, int64_t K, const uint16_t* 
                 // K in whole 256-deep chunks: the direct-to-LDS variant
                 const int64_t grid = (N + BTL_NB - 1) / BTL_NB;
                 if (N % BTL_NB == 0)
-                    return launch(gemm_relu_smallm_bt_lds_kernel<false>, grid, 256, stream, A, Bt, C, M, N, K, lda,
-                                  ldbt, ldc);
-                return launch(gemm_relu_smallm_bt_lds_kernel<true>, grid, 256, stream, A, Bt, C, M, N, K, lda, ldbt,
-                              ldc);
+                    return launch(gemm_relu_smallm_bt_lds_kernel<false, E>, grid, 256, stream, A, Bt, C, M, N, K, lda,
+                                  ldbt, ldc, ep);
+                return launch(gemm_relu_smallm_bt_lds_kernel<true, E>, grid, 256, stream, A, Bt, C, M, N, K, lda,
+                              ldbt, ldc, ep);
             }
             const bool whole = N % BT_NB == 0 && K % KSTEP == 0;
             if (whole)
-                return launch(gemm_relu_smallm_bt_kernel<false>, p.grid, p.threads, stream, A, Bt, C, M, N, K, lda,
-                              ldbt, ldc);
-            return launch(gemm_relu_smallm_bt_kernel<true>, p.grid, p.threads, stream, A, Bt, C, M, N, K, lda, ldbt,
-                          ldc);
+                return launch(gemm_relu_smallm_bt_kernel<false, E>, p.grid, p.threads, stream, A, Bt, C, M, N, K, lda,
+                              ldbt, ldc, ep);
+            return launch(gemm_relu_smallm_bt_kernel<true, E>, p.grid, p.threads, stream, A, Bt, C, M, N, K, lda,
+                          ldbt, ldc, ep);
         }
         case GR_PATH_TILE: {
             const int64_t bm = p.block_m, bn = p.block_n;
@@ -768,37 +769,37 @@ int run_bt(const gr_plan_t& p, int64_t M, int64_t N, int64_t K, const uint16_t* 
                 float* no_part = nullptr;
                 const int64_t no_split = 0;
                 if (whole)
-                    return launch(gemm_relu_tile128_kernel<false, false, true>, p.grid, THREADS, stream, A, Bt, C, M,
-                                  N, K, lda, ldbt, ldc, tiles_m, tiles_n, gm, vc, no_part, no_split, ep);
-                return launch(gemm_relu_tile128_kernel<true, false, true>, p.grid, THREADS, stream, A, Bt, C, M, N,
+                    return launch(gemm_relu_tile128_kernel<false, false, true, E>, p.grid, THREADS, stream, A, Bt, C,
+                                  M, N, K, lda, ldbt, ldc, tiles_m, tiles_n, gm, vc, no_part, no_split, ep);
+                return launch(gemm_relu_tile128_kernel<true, false, true, E>, p.grid, THREADS, stream, A, Bt, C, M, N,
                               K, lda, ldbt, ldc, tiles_m, tiles_n, gm, vc, no_part, no_split, ep);
             }
             if (K % gr::tile3::BKA == 0) {
                 using namespace gr::tile3;
                 if (whole)
-                    return launch(gemm_relu_tile3_kernel<false, true>, p.grid, THREADS, stream, A, Bt, C, M, N, K,
+                    return launch(gemm_relu_tile3_kernel<false, true, E>, p.grid, THREADS, stream, A, Bt, C, M, N, K,
                                   lda, ldbt, ldc, tiles_m, tiles_n, gm, vc, ep);
-                return launch(gemm_relu_tile3_kernel<true, true>, p.grid, THREADS, stream, A, Bt, C, M, N, K, lda,
+                return launch(gemm_relu_tile3_kernel<true, true, E>, p.grid, THREADS, stream, A, Bt, C, M, N, K, lda,
                               ldbt, ldc, tiles_m, tiles_n, gm, vc, ep);
             }
             using namespace gr::tile2;
             if (whole)
-                return launch(gemm_relu_tile2_kernel<false, true>, p.grid, THREADS, stream, A, Bt, C, M, N, K, lda,
+                return launch(gemm_relu_tile2_kernel<false, true, E>, p.grid, THREADS, stream, A, Bt, C, M, N, K, lda,
                               ldbt, ldc, tiles_m, tiles_n, gm, vc, ep);
-            return launch(gemm_relu_tile2_kernel<true, true>, p.grid, THREADS, stream, A, Bt, C, M, N, K, lda, ldbt,
-                          ldc, tiles_m, tiles_n, gm, vc, ep);
+            return launch(gemm_relu_tile2_kernel<true, true, E>, p.grid, THREADS, stream, A, Bt, C, M, N, K, lda,
+                          ldbt, ldc, tiles_m, tiles_n, gm, vc, ep);
         }
         case GR_PATH_TILE_EDGE: {
             const int va = p.vec_a, vb = p.vec_b;
-            if (va == 8 && vb == 8) return launch_tile_bt<8, 8>(p, M, N, K, A, lda, Bt, ldbt, C, ldc, ep, stream);
-            if (va == 8 && vb == 2) return launch_tile_bt<8, 2>(p, M, N, K, A, lda, Bt, ldbt, C, ldc, ep, stream);
-            if (va == 8) return launch_tile_bt<8, 1>(p, M, N, K, A, lda, Bt, ldbt, C, ldc, ep, stream);
-            if (va == 2 && vb == 8) return launch_tile_bt<2, 8>(p, M, N, K, A, lda, Bt, ldbt, C, ldc, ep, stream);
-            if (va == 2 && vb == 2) return launch_tile_bt<2, 2>(p, M, N, K, A, lda, Bt, ldbt, C, ldc, ep, stream);
-            if (va == 2) return launch_tile_bt<2, 1>(p, M, N, K, A, lda, Bt, ldbt, C, ldc, ep, stream);
-            if (vb == 8) return launch_tile_bt<1, 8>(p, M, N, K, A, lda, Bt, ldbt, C, ldc, ep, stream);
-            if (vb == 2) return launch_tile_bt<1, 2>(p, M, N, K, A, lda, Bt, ldbt, C, ldc, ep, stream);
-            return launch_tile_bt<1, 1>(p, M, N, K, A, lda, Bt, ldbt, C, ldc, ep, stream);
+            if (va == 8 && vb == 8) return launch_tile_bt<8, 8, E>(p, M, N, K, A, lda, Bt, ldbt, C, ldc, ep, stream);
+            if (va == 8 && vb == 2) return launch_tile_bt<8, 2, E>(p, M, N, K, A, lda, Bt, ldbt, C, ldc, ep, stream);
+            if (va == 8) return launch_tile_bt<8, 1, E>(p, M, N, K, A, lda, Bt, ldbt, C, ldc, ep, stream);
+            if (va == 2 && vb == 8) return launch_tile_bt<2, 8, E>(p, M, N, K, A, lda, Bt, ldbt, C, ldc, ep, stream);
+            if (va == 2 && vb == 2) return launch_tile_bt<2, 2, E>(p, M, N, K, A, lda, Bt, ldbt, C, ldc, ep, stream);
+            if (va == 2) return launch_tile_bt<2, 1, E>(p, M, N, K, A, lda, Bt, ldbt, C, ldc, ep, stream);
+            if (vb == 8) return launch_tile_bt<1, 8, E>(p, M, N, K, A, lda, Bt, ldbt, C, ldc, ep, stream);
+            if (vb == 2) return launch_tile_bt<1, 2, E>(p, M, N, K, A, lda, Bt, ldbt, C, ldc, ep, stream);
+            return launch_tile_bt<1, 1, E>(p, M, N, K, A, lda, Bt, ldbt, C, ldc, ep, stream);
         }
         default: return GR_ERR_INVALID_PATH;
     }
@@ -831,7 +832,25 @@ int entry_bt(int64_t M, int64_t N, int64_t K, const uint16_t* A, int64_t lda, co
     if (p.path == GR_PATH_NONE) return GR_OK;
     st = check_device();
     if (st != GR_OK) return st;
-    return run_bt(p, M, N, K, A, lda, Bt, ldbt, C, ldc, static_cast<hipStream_t>(stream));
+    return run_bt<gr::ElemF16>(p, M, N, K, A, lda, Bt, ldbt, C, ldc, kReluOnly, static_cast<hipStream_t>(stream));
+}
+
+// C = act(A Bt^T + bias) in fp16 or bfloat16 (fmt): the transposed-B paths
+// with the general epilogue.
+template <typename Base>
+int entry_bt_epi(int64_t M, int64_t N, int64_t K, const uint16_t* A, int64_t lda, const uint16_t* Bt, int64_t ldbt,
+                 const uint16_t* bias, int act, uint16_t* C, int64_t ldc, void* stream, int forced) {
+    if (act < 0 || act >= gr::kActCount) return GR_ERR_INVALID_ARG;
+    gr_plan_t p;
+    int st = plan_call_bt(M, N, K, (uintptr_t)A, lda, (uintptr_t)Bt, ldbt, (uintptr_t)C, ldc, forced, &p);
+    if (st != GR_OK) return st;
+    if (bias != nullptr && M > 0 && N > 0 && overlaps((uintptr_t)C, span_bytes(M, N, ldc), (uintptr_t)bias, 2 * N))
+        return GR_ERR_ALIAS;
+    if (p.path == GR_PATH_NONE) return GR_OK;
+    st = check_device();
+    if (st != GR_OK) return st;
+    return run_bt<gr::Epi<Base>>(p, M, N, K, A, lda, Bt, ldbt, C, ldc, gr::EpiArgs{bias, act, 1.0f},
+                                 static_cast<hipStream_t>(stream));
 }
 
 // ---- fp8 (e4m3) operands, B given transposed -----------------------------------
@@ -1318,6 +1337,17 @@ int gemm_relu_f16_plan_ws(int64_t M, int64_t N, int64_t K, const uint16_t* A, in
     TileSplit ts;
     return plan_call(M, N, K, (uintptr_t)A, lda, (uintptr_t)B, ldb, (uintptr_t)C, ldc, 0, workspace_bytes, false,
                      -1, &pk, &sp, &ts, out);
+}
+
+int gemm_bias_act_bt(int64_t M, int64_t N, int64_t K, const uint16_t* A, int64_t lda, const uint16_t* Bt,
+                     int64_t ldbt, const uint16_t* bias, int act, uint16_t* C, int64_t ldc, int fmt, void* stream,
+                     int path) {
+    if (path != -1 && path != GR_PATH_TILE && path != GR_PATH_TILE_EDGE && path != GR_PATH_SMALL_M)
+        return GR_ERR_INVALID_PATH;
+    if (fmt == GR_FMT_BF16)
+        return entry_bt_epi<gr::ElemBF16>(M, N, K, A, lda, Bt, ldbt, bias, act, C, ldc, stream, path);
+    if (fmt != GR_FMT_F16) return GR_ERR_INVALID_ARG;
+    return entry_bt_epi<gr::ElemF16>(M, N, K, A, lda, Bt, ldbt, bias, act, C, ldc, stream, path);
 }
 
 int gemm_fp8_bt(int64_t M, int64_t N, int64_t K, const uint8_t* A, int64_t lda, const uint8_t* Bt, int64_t ldbt,

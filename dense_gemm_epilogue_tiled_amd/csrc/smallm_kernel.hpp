@@ -419,10 +419,12 @@ __device__ __forceinline__ u32x4 load_bt8(const uint16_t* Bt, int64_t ldbt, int6
     }
 }
 
-template <bool GUARD>
+// E: element type and epilogue (ElemF16, ElemBF16, or Epi<...> for bias +
+// activation with ep).
+template <bool GUARD, typename E = ElemF16>
 __global__ __launch_bounds__(64 * BT_WAVES) void gemm_relu_smallm_bt_kernel(
     const uint16_t* __restrict__ A, const uint16_t* __restrict__ Bt, uint16_t* __restrict__ C, int64_t M, int64_t N,
-    int64_t K, int64_t lda, int64_t ldbt, int64_t ldc) {
+    int64_t K, int64_t lda, int64_t ldbt, int64_t ldc, EpiArgs ep) {
     __shared__ __attribute__((aligned(16))) float red[BT_PHASES][MAX_M][BT_NB];
 
     const uint32_t tid = threadIdx.x;
@@ -456,8 +458,7 @@ __global__ __launch_bounds__(64 * BT_WAVES) void gemm_relu_smallm_bt_kernel(
     auto compute_group = [&](const u32x4 (&rb)[BT_U], const u32x4 (&ra)[BT_U]) {
 #pragma unroll
         for (int u = 0; u < BT_U; ++u)
-            acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, rb[u]),
-                                                         __builtin_bit_cast(f16x8, ra[u]), acc, 0, 0, 0);
+            acc = E::mfma16(__builtin_bit_cast(f16x8, rb[u]), __builtin_bit_cast(f16x8, ra[u]), acc);
     };
 
     // Phase kp takes the step groups kp, kp + 2, kp + 4, ... (BT_U steps each).
@@ -481,7 +482,7 @@ __global__ __launch_bounds__(64 * BT_WAVES) void gemm_relu_smallm_bt_kernel(
     for (uint32_t o = tid; o < (uint32_t)(MAX_M * BT_NB); o += 64 * BT_WAVES) {
         const uint32_t m = o / BT_NB, nl = o % BT_NB;
         const int64_t n = n_wg + nl;
-        if ((int64_t)m < M && n < N) C[(int64_t)m * ldc + n] = relu_to_f16(red[0][m][nl] + red[1][m][nl]);
+        if ((int64_t)m < M && n < N) C[(int64_t)m * ldc + n] = epi_value<E>(red[0][m][nl] + red[1][m][nl], n, N, ep);
     }
 }
 
@@ -508,10 +509,10 @@ constexpr int BTL_SLOT = BTL_BT_BYTES + BTL_A_BYTES;
 constexpr int BTL_SLOTS = 4;
 constexpr int BTL_COPIES = 10;  // copies per wave per chunk: 8 (Bt) + 2 (A)
 
-template <bool GUARD>
+template <bool GUARD, typename E = ElemF16>
 __global__ __launch_bounds__(256, 1) void gemm_relu_smallm_bt_lds_kernel(
     const uint16_t* __restrict__ A, const uint16_t* __restrict__ Bt, uint16_t* __restrict__ C, int64_t M, int64_t N,
-    int64_t K, int64_t lda, int64_t ldbt, int64_t ldc) {
+    int64_t K, int64_t lda, int64_t ldbt, int64_t ldc, EpiArgs ep) {
     __shared__ __attribute__((aligned(1024))) uint8_t lds[BTL_SLOTS * BTL_SLOT];
 
     const uint32_t lane = threadIdx.x & 63u;
@@ -572,8 +573,8 @@ __global__ __launch_bounds__(256, 1) void gemm_relu_smallm_bt_lds_kernel(
             const uint32_t chunk = 4u * st + lg;
             const f16x8 b = *reinterpret_cast<const f16x8*>(slot + bt_row * 512u + ((chunk ^ (bt_row & 15u)) << 4));
             const f16x8 a = *reinterpret_cast<const f16x8*>(slot + BTL_BT_BYTES + li * 512u + ((chunk ^ li) << 4));
-            if (st & 1) acc1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(b, a, acc1, 0, 0, 0);
-            else acc0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(b, a, acc0, 0, 0, 0);
+            if (st & 1) acc1 = E::mfma16(b, a, acc1);
+            else acc0 = E::mfma16(b, a, acc0);
         }
     }
 
@@ -584,7 +585,7 @@ __global__ __launch_bounds__(256, 1) void gemm_relu_smallm_bt_lds_kernel(
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             const int64_t n = n_wg + 16 * wave + 4 * lg + r;
-            if (!GUARD || n < N) C[m * ldc + n] = relu_to_f16(acc0[r] + acc1[r]);
+            if (!GUARD || n < N) C[m * ldc + n] = epi_value<E>(acc0[r] + acc1[r], n, N, ep);
         }
     }
 }

@@ -410,6 +410,24 @@ int gemm_bias_act_ws(int64_t M, int64_t N, int64_t K,
                      void* stream, int path);
 
 /*
+ * gemm_bias_act_bt -- C := act(A * Bt^T + bias) with B given transposed (Bt,
+ * N x K row-major, pitch ldbt; the layout of a linear layer's weight), in
+ * fp16 or bfloat16 (fmt: GR_FMT_F16 / GR_FMT_BF16, the format of A, Bt, bias
+ * and C): the epilogue of gemm_bias_act_f16 on the paths of gemm_relu_f16_bt
+ * (GR_PATH_SMALL_M, GR_PATH_TILE, GR_PATH_TILE_EDGE, chosen as
+ * gemm_relu_f16_bt_plan says).  path -1 lets the planner choose; one of those
+ * three forces it (test hook; GR_ERR_INVALID_PATH when its conditions do not
+ * hold).  Errors as gemm_bias_act_f16, plus GR_ERR_INVALID_ARG for an unknown
+ * fmt.
+ */
+int gemm_bias_act_bt(int64_t M, int64_t N, int64_t K,
+                     const uint16_t* A, int64_t lda,
+                     const uint16_t* Bt, int64_t ldbt,
+                     const uint16_t* bias, int act,
+                     uint16_t* C, int64_t ldc, int fmt,
+                     void* stream, int path);
+
+/*
  * ---- fp8 operands ---------------------------------------------------------------
  * C := act(scale_a * scale_b * (A * Bt^T) + bias) with A (M x K) and Bt
  * (N x K) in OCP fp8 E4M3 (1 sign, 4 exponent bits with bias 7, 3 fraction

@@ -581,6 +581,23 @@ def test_mxfp4_planner_and_checks_need_no_gpu():
                                    gr.GR_FMT_F16, None, gr.GR_PATH_TILE) == gr.GR_ERR_INVALID_PATH
 
 
+def test_bias_act_bt_argument_checks_need_no_gpu():
+    """gemm_bias_act_bt: the transposed-B checks, then format, activation,
+    path and a bias overlapping C, before any HIP call."""
+    f = gr.gemm_bias_act_bt
+    bias = BASE_C + (1 << 30)
+    args = (8, 8, 8, BASE_A, 8, BASE_B, 8)
+    assert f(-1, 8, 8, BASE_A, 8, BASE_B, 8, bias, 2, BASE_C, 8) == gr.GR_ERR_INVALID_DIM
+    assert f(8, 8, 8, BASE_A, 8, BASE_B, 7, bias, 2, BASE_C, 8) == gr.GR_ERR_INVALID_LD  # ldbt < K
+    assert f(*args, bias, 2, BASE_C, 8, 2) == gr.GR_ERR_INVALID_ARG                      # format
+    assert f(*args, bias, 7, BASE_C, 8, gr.GR_FMT_BF16) == gr.GR_ERR_INVALID_ARG         # activation
+    assert f(*args, BASE_C + 8, 2, BASE_C, 8, gr.GR_FMT_F16) == gr.GR_ERR_ALIAS          # bias inside C
+    assert f(*args, bias, 2, BASE_C, 8, gr.GR_FMT_F16, None, gr.GR_PATH_TILE_SPLIT) == gr.GR_ERR_INVALID_PATH
+    assert f(300, 256, 48, BASE_A, 48, BASE_B, 48, bias, 2, BASE_C, 256, gr.GR_FMT_F16, None,
+             gr.GR_PATH_TILE) == gr.GR_ERR_INVALID_PATH                                  # K % 32 != 0
+    assert f(0, 8, 8, 0, 8, BASE_B, 8, bias, 2, 0, 8) == gr.GR_OK
+
+
 def test_fp8_planner_and_checks_need_no_gpu():
     """gemm_fp8_bt: the pipelined kernel for K % 64 == 0 with 16-byte rows (any
     M, N), the guarded kernel otherwise; argument errors before any HIP call."""
