@@ -19,6 +19,7 @@
 #include "tile2_kernel.hpp"
 #include "tile128_kernel.hpp"
 #include "tile3_kernel.hpp"
+#include "tile3t_kernel.hpp"
 #include "tile_kernel.hpp"
 
 namespace {
@@ -774,13 +775,13 @@ int run_bt(const gr_plan_t& p, int64_t M, int64_t N, int64_t K, const uint16_t* 
                 return launch(gemm_relu_tile128_kernel<true, false, true, E>, p.grid, THREADS, stream, A, Bt, C, M, N,
                               K, lda, ldbt, ldc, tiles_m, tiles_n, gm, vc, no_part, no_split, ep);
             }
-            if (K % gr::tile3::BKA == 0) {
-                using namespace gr::tile3;
+            if (K % gr::tile3t::BKS == 0) {
+                using namespace gr::tile3t;
                 if (whole)
-                    return launch(gemm_relu_tile3_kernel<false, true, E>, p.grid, THREADS, stream, A, Bt, C, M, N, K,
-                                  lda, ldbt, ldc, tiles_m, tiles_n, gm, vc, ep);
-                return launch(gemm_relu_tile3_kernel<true, true, E>, p.grid, THREADS, stream, A, Bt, C, M, N, K, lda,
-                              ldbt, ldc, tiles_m, tiles_n, gm, vc, ep);
+                    return launch(gemm_relu_tile3t_kernel<false, E>, p.grid, THREADS, stream, A, Bt, C, M, N, K, lda,
+                                  ldbt, ldc, tiles_m, tiles_n, gm, vc, ep);
+                return launch(gemm_relu_tile3t_kernel<true, E>, p.grid, THREADS, stream, A, Bt, C, M, N, K, lda, ldbt,
+                              ldc, tiles_m, tiles_n, gm, vc, ep);
             }
             using namespace gr::tile2;
             if (whole)
