@@ -332,6 +332,59 @@ struct WaveTile {
 
 constexpr uint32_t REGION_BYTES = WaveTile<4, 4>::REGION_BYTES;  // 32 KiB for a 128 x 128 wave tile
 
+// Accumulator layouts of a wave tile of 32*FM x 32*FN, both from MFMAs
+// issued with B as the first operand, so every block holds C^T:
+//   f32x16 [FM][FN] (v_mfma_f32_32x32x16): lane l, register 4q + t of block
+//     (i, j) is row 32i + l%32, column 32j + 8q + 4(l/32) + t;
+//   f32x4 [2FM][2FN] (v_mfma_f32_16x16x32): lane l, register t of block
+//     (i, j) is row 16i + l%16, column 16j + 4(l/16) + t.
+// Either way a lane holds runs of 4 consecutive columns of one row.
+template <typename Acc>
+struct AccTile;
+template <int BM, int BN>
+struct AccTile<f32x16[BM][BN]> {
+    static constexpr int FM = BM, FN = BN;
+};
+template <int BM, int BN>
+struct AccTile<f32x4[BM][BN]> {
+    static_assert(BM % 2 == 0 && BN % 2 == 0, "16 x 16 blocks pair up into 32 x 32 ones");
+    static constexpr int FM = BM / 2, FN = BN / 2;
+};
+
+// fp32 values of the 32-row block i of a wave tile into LDS: element (r, c)
+// of the block is word c%4 of 16-byte chunk off(r, c/4).
+template <int FM, int FN, typename Off>
+__device__ __forceinline__ void stage_fp32_rows(const f32x16 (&acc)[FM][FN], int i, uint8_t* region, uint32_t lane,
+                                                Off off) {
+    const uint32_t r_lane = lane & 31u, half = lane >> 5;
+#pragma unroll
+    for (int ii = 0; ii < FM; ++ii) {
+        if (ii != i) continue;
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+                *reinterpret_cast<f32x4*>(region + off(r_lane, 8u * j + 2u * q + half)) =
+                    f32x4{acc[ii][j][4 * q + 0], acc[ii][j][4 * q + 1], acc[ii][j][4 * q + 2], acc[ii][j][4 * q + 3]};
+    }
+}
+// 16 x 16 blocks, called for i = 0, 1, ... in turn: writes the first two
+// block rows, then moves the others up by two, so that the rolled caller
+// never selects registers by its loop counter (which made the compiler keep
+// the 64 accumulators in scratch memory).
+template <int BM, int BN, typename Off>
+__device__ __forceinline__ void stage_fp32_rows(f32x4 (&acc)[BM][BN], int, uint8_t* region, uint32_t lane, Off off) {
+    const uint32_t r = lane & 15u, g = lane >> 4;
+#pragma unroll
+    for (int ii = 0; ii < 2; ++ii)
+#pragma unroll
+        for (int j = 0; j < BN; ++j) *reinterpret_cast<f32x4*>(region + off(16u * ii + r, 4u * j + g)) = acc[ii][j];
+#pragma unroll
+    for (int ii = 0; ii + 2 < BM; ++ii)
+#pragma unroll
+        for (int j = 0; j < BN; ++j) acc[ii][j] = acc[ii + 2][j];
+}
+
 // General epilogue (bias + activation) for one wave's tile, one 32-row block
 // at a time: the wave writes the block's fp32 accumulators to its LDS region
 // (32 rows x 32*FN columns, 16-byte chunk c of row r at slot c XOR (r mod
@@ -339,11 +392,13 @@ constexpr uint32_t REGION_BYTES = WaveTile<4, 4>::REGION_BYTES;  // 32 KiB for a
 // columns, so the bias is loaded once per lane and every store covers whole
 // row segments (8-byte stores when C's rows allow, else 2-byte ones).  Needs
 // 16 KiB (FN = 4) or 8 KiB (FN = 2) of LDS per wave; all waves call it.
-template <bool EDGE, typename E, int FM, int FN>
-__device__ __forceinline__ void store_wave_tile_general(const f32x16 (&acc)[FM][FN], uint8_t* region, uint32_t lane,
+// acc may be overwritten.
+template <bool EDGE, typename E, typename Acc>
+__device__ __forceinline__ void store_wave_tile_general(Acc& acc, uint8_t* region, uint32_t lane,
                                                         uint16_t* __restrict__ C, int64_t ldc, int64_t row0,
                                                         int64_t col0, int64_t row_min, int64_t M, int64_t N,
                                                         int vec_c, const EpiArgs& ep) {
+    constexpr int FM = AccTile<Acc>::FM, FN = AccTile<Acc>::FN;
     constexpr uint32_t COLS = 32 * FN;
     constexpr uint32_t CHUNKS = COLS / 4;  // 16-byte fp32 chunks per row, also lanes per row on the way back
     constexpr uint32_t ROW_BYTES = 4 * COLS;
@@ -351,7 +406,6 @@ __device__ __forceinline__ void store_wave_tile_general(const f32x16 (&acc)[FM][
     auto off = [](uint32_t row, uint32_t chunk) -> uint32_t {
         return row * ROW_BYTES + ((chunk ^ (row & (CHUNKS - 1))) << 4);
     };
-    const uint32_t r_lane = lane & 31u, half = lane >> 5;
     const uint32_t ch = lane & (CHUNKS - 1);  // this lane's chunk on the way back
     const int64_t n = col0 + 4 * ch;
     const bool has_bias = ep.bias != nullptr;
@@ -368,19 +422,7 @@ __device__ __forceinline__ void store_wave_tile_general(const f32x16 (&acc)[FM][
 #pragma unroll 1
     for (int i = 0; i < FM; ++i) {
         __syncthreads();
-        // Block (i, j) holds C^T: lane l, register 4q + t is row l%32,
-        // column 32j + 8q + 4(l/32) + t, i.e. fp32 chunk 8j + 2q + l/32.
-#pragma unroll
-        for (int ii = 0; ii < FM; ++ii) {
-            if (ii != i) continue;
-#pragma unroll
-            for (int j = 0; j < FN; ++j)
-#pragma unroll
-                for (int q = 0; q < 4; ++q)
-                    *reinterpret_cast<f32x4*>(region + off(r_lane, 8u * j + 2u * q + half)) =
-                        f32x4{acc[ii][j][4 * q + 0], acc[ii][j][4 * q + 1], acc[ii][j][4 * q + 2],
-                              acc[ii][j][4 * q + 3]};
-        }
+        stage_fp32_rows(acc, i, region, lane, off);
         __syncthreads();
         // One copy of the read-back per activation; two rows in flight.
         act::dispatch(ep.act, [&](auto tag) {
@@ -443,18 +485,9 @@ __device__ __forceinline__ void store_partials(const f32x16 (&acc)[FM][FN], floa
     }
 }
 
-template <bool EDGE, typename E = ElemF16, int FM, int FN>
-__device__ __forceinline__ void store_wave_tile(const f32x16 (&acc)[FM][FN], uint8_t* region, uint32_t lane,
-                                                uint16_t* __restrict__ C, int64_t ldc, int64_t row0, int64_t col0,
-                                                int64_t row_min, int64_t M, int64_t N, int vec_c,
-                                                const EpiArgs& ep) {
-    using T = WaveTile<FM, FN>;
-    if constexpr (E::kGeneral) {
-        static_assert(32 * 32 * FN * 4 <= T::REGION_BYTES, "the fp32 block fits the wave's region");
-        store_wave_tile_general<EDGE, E>(acc, region, lane, C, ldc, row0, col0, row_min, M, N, vec_c, ep);
-        return;
-    }
-    __syncthreads();
+// ReLU'd fp16 values of a whole wave tile into LDS (layout of WaveTile T).
+template <typename T, typename E, int FM, int FN>
+__device__ __forceinline__ void stage_relu_tile(const f32x16 (&acc)[FM][FN], uint8_t* region, uint32_t lane) {
     const uint32_t r_lane = lane & 31u, half = lane >> 5;
 #pragma unroll
     for (int i = 0; i < FM; ++i) {
@@ -470,6 +503,40 @@ __device__ __forceinline__ void store_wave_tile(const f32x16 (&acc)[FM][FN], uin
             }
         }
     }
+}
+// 16 x 16 blocks: the 4 columns of lane l in block (i, j) are half (l/16)%2
+// of 16-byte chunk 2j + l/32 of row 16i + l%16.
+template <typename T, typename E, int BM, int BN>
+__device__ __forceinline__ void stage_relu_tile(const f32x4 (&acc)[BM][BN], uint8_t* region, uint32_t lane) {
+    const uint32_t r = lane & 15u, g = lane >> 4;
+#pragma unroll
+    for (int i = 0; i < BM; ++i) {
+        const uint32_t row = 16u * i + r;
+#pragma unroll
+        for (int j = 0; j < BN; ++j) {
+            u32x2 p;
+            p[0] = relu_pack2_e<E>(acc[i][j][0], acc[i][j][1]);
+            p[1] = relu_pack2_e<E>(acc[i][j][2], acc[i][j][3]);
+            *reinterpret_cast<u32x2*>(region + T::off(row, 2u * j + (g >> 1)) + 8u * T::half_slot(row, g & 1u)) = p;
+        }
+    }
+}
+
+// acc may be overwritten.
+template <bool EDGE, typename E = ElemF16, typename Acc>
+__device__ __forceinline__ void store_wave_tile(Acc& acc, uint8_t* region, uint32_t lane,
+                                                uint16_t* __restrict__ C, int64_t ldc, int64_t row0, int64_t col0,
+                                                int64_t row_min, int64_t M, int64_t N, int vec_c,
+                                                const EpiArgs& ep) {
+    constexpr int FM = AccTile<Acc>::FM, FN = AccTile<Acc>::FN;
+    using T = WaveTile<FM, FN>;
+    if constexpr (E::kGeneral) {
+        static_assert(32 * 32 * FN * 4 <= T::REGION_BYTES, "the fp32 block fits the wave's region");
+        store_wave_tile_general<EDGE, E>(acc, region, lane, C, ldc, row0, col0, row_min, M, N, vec_c, ep);
+        return;
+    }
+    __syncthreads();
+    stage_relu_tile<T, E>(acc, region, lane);
     __syncthreads();
     if (vec_c >= 4) {
         constexpr uint32_t ROWS_PER = 64u / T::CHUNKS;  // rows per wave instruction

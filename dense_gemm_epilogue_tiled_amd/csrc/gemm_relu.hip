@@ -492,9 +492,9 @@ int run(const gr_plan_t& p, int64_t M, int64_t N, int64_t K, const uint16_t* A, 
             if (K % gr::tile3::BKA == 0) {
                 using namespace gr::tile3;
                 if (whole)
-                    return launch(gemm_relu_tile3_kernel<false, false, E>, p.grid, THREADS, stream, A, B, C, M, N, K,
+                    return launch(gemm_relu_tile3_kernel<false, E>, p.grid, THREADS, stream, A, B, C, M, N, K,
                                   lda, ldb, ldc, tiles_m, tiles_n, gm, vc, ep);
-                return launch(gemm_relu_tile3_kernel<true, false, E>, p.grid, THREADS, stream, A, B, C, M, N, K, lda,
+                return launch(gemm_relu_tile3_kernel<true, E>, p.grid, THREADS, stream, A, B, C, M, N, K, lda,
                               ldb, ldc, tiles_m, tiles_n, gm, vc, ep);
             }
             using namespace gr::tile2;

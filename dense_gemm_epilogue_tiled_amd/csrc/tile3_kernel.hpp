@@ -18,7 +18,15 @@
 //   two halves of strip a+2 are copied in steps 2a and 2a+1.
 //   A tile layout [256 m][64 k]: 128-byte rows, chunk index XOR (m/2)%8, so
 //   16 consecutive rows reading one chunk hit 16 distinct bank groups.
+//
+// Each wave owns 128 x 128 of C as 8 x 8 blocks of 16 x 16
+// (v_mfma_f32_16x16x32, 64 per step, each taking all 32 k of the step):
+// measured 7% faster than 4 x 4 blocks of 32 x 32 (v_mfma_f32_32x32x16, two
+// per block and step) with the same copies and fragment bytes.  A fragments:
+// ds_read_b128 of 8 consecutive k of one row, 16 rows per read; B fragments:
+// two ds_read_b64_tr_b16, each 16-lane group taking a 4 k x 16 n block.
 #pragma once
+
 
 #include <type_traits>
 
@@ -38,9 +46,8 @@ constexpr int A_SLOTS = 3;
 constexpr int THREADS = 256;
 constexpr int WAVE_TM = 128;
 constexpr int WAVE_TN = 128;
-constexpr int FM = WAVE_TM / 32;
-constexpr int FN = WAVE_TN / 32;
-constexpr int KSUB = BK / 16;
+constexpr int FM = WAVE_TM / 16;
+constexpr int FN = WAVE_TN / 16;
 constexpr int B_SLOT_BYTES = BK * BN * 2;     // 16 KiB
 constexpr int A_SLOT_BYTES = BM * BKA * 2;    // 32 KiB
 constexpr int A_BASE = B_SLOTS * B_SLOT_BYTES;  // 64 KiB
@@ -56,16 +63,13 @@ static_assert(LDS_BYTES >= 4 * epi::REGION_BYTES, "the epilogue stages four wave
 __device__ __forceinline__ uint32_t a64_off(uint32_t m, uint32_t c) { return m * 128u + ((c ^ ((m >> 1) & 7u)) << 4); }
 
 struct Frags {
-    f16x8 a[KSUB][FM];
-    f16x8 b[KSUB][FN];
+    f16x8 a[FM];
+    f16x8 b[FN];
 };
 
-// BT=true: B given transposed (Bt, N x K row-major, pitch ldb); its 32-deep
-// strips [256 n][32 k] are staged like the 32-deep kernel's A strips (64-byte
-// rows, chunk XOR (n/4)%4, same 16 KiB slots) and its fragments are read with
-// ds_read_b128; rows of Bt past N are clamped to row N-1.
-// E: element type (ElemF16 or ElemBF16; only the MFMA and the rounding differ).
-template <bool EDGE, bool BT = false, typename E = ElemF16>
+// E: element type (ElemF16 or ElemBF16; only the MFMA and the rounding
+// differ) or Epi<...> for bias + activation.
+template <bool EDGE, typename E = ElemF16>
 __global__ __launch_bounds__(THREADS, 1) void gemm_relu_tile3_kernel(
     const uint16_t* __restrict__ A, const uint16_t* __restrict__ B, uint16_t* __restrict__ C, int64_t M, int64_t N,
     int64_t K, int64_t lda, int64_t ldb, int64_t ldc, uint32_t tiles_m, uint32_t tiles_n, uint32_t group_m,
@@ -99,9 +103,9 @@ __global__ __launch_bounds__(THREADS, 1) void gemm_relu_tile3_kernel(
     // B strip (16 KiB) = 16 blocks of 2 rows x 512 bytes; this wave fills
     // blocks 4w .. 4w+3.  lane -> row lane/32, slot lane%32.
     const uint8_t* base_a = reinterpret_cast<const uint8_t*>(A + m0 * lda);
-    const uint8_t* base_b = reinterpret_cast<const uint8_t*>(BT ? B + n0 * ldb : B + n0);
+    const uint8_t* base_b = reinterpret_cast<const uint8_t*>(B + n0);
     const int64_t step_a = BKA * 2;
-    const int64_t step_b = BT ? (int64_t)BK * 2 : (int64_t)BK * ldb * 2;
+    const int64_t step_b = (int64_t)BK * ldb * 2;
     // The odd-step half (blocks +4, rows +32) only adds a wave-uniform
     // 32-row offset: the chunk XOR term, (row/2)%8, is unchanged by it.
     uint32_t off_a[4], off_b[4];
@@ -116,19 +120,10 @@ __global__ __launch_bounds__(THREADS, 1) void gemm_relu_tile3_kernel(
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         const uint32_t blk = 4u * wave + (uint32_t)i;
-        if constexpr (BT) {
-            // block = 16 rows of Bt x 64 bytes; lane -> row lane/4, slot lane%4
-            const uint32_t rn = 16u * blk + (lane >> 2);
-            const uint32_t cn = (lane & 3u) ^ ((rn >> 2) & 3u);
-            uint32_t rn_src = rn;
-            if constexpr (EDGE) rn_src = n0 + rn < N ? rn : (uint32_t)(N - 1 - n0);
-            off_b[i] = (uint32_t)((rn_src * ldb + 8u * cn) * 2);
-        } else {
-            const uint32_t rb = 2u * blk + (lane >> 5);
-            uint32_t cb = (lane & 31u) ^ ((rb & 3u) << 2);
-            if constexpr (EDGE) cb = edge::clamp_chunk(cb, n0, N);
-            off_b[i] = (uint32_t)((rb * ldb + 8u * cb) * 2);
-        }
+        const uint32_t rb = 2u * blk + (lane >> 5);
+        uint32_t cb = (lane & 31u) ^ ((rb & 3u) << 2);
+        if constexpr (EDGE) cb = edge::clamp_chunk(cb, n0, N);
+        off_b[i] = (uint32_t)((rb * ldb + 8u * cb) * 2);
     }
     const uint32_t lds_base = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(GR_LDS uint8_t*)lds);
 
@@ -144,52 +139,44 @@ __global__ __launch_bounds__(THREADS, 1) void gemm_relu_tile3_kernel(
     };
 
     // ---- fragment addresses --------------------------------------------------
-    // A operand for half h, MFMA step s, block i: row wm*128 + 32i + lane%32,
-    // chunk 4h + 2s + lane/32 of the 64-deep strip; block i is +4 KiB.  The
-    // chunk of half 1 is the chunk of half 0 plus 4, i.e. XOR 4 (chunks of
-    // half 0 are below 4), and XOR commutes with the row swizzle: half 1's
-    // address is half 0's address XOR 64 (slot and block offsets are
-    // multiples of 1 KiB and leave that bit alone).
+    // A operand for half h, block i: row wm*128 + 16i + lane%16, chunk
+    // 4h + lane/16 of the 64-deep strip (16 rows move the swizzle term
+    // (row/2)%8 by a multiple of 8: none); block i is +2 KiB.  The chunk of
+    // half 1 is the chunk of half 0 plus 4, i.e. XOR 4 (chunks of half 0 are
+    // below 4), and XOR commutes with the row swizzle: half 1's address is
+    // half 0's address XOR 64 (slot and block offsets are multiples of 1 KiB
+    // and leave that bit alone).
+    // B operand, block j: lane l gets column wn*128 + 16j + l%16, k 8(l/16)
+    // .. +7 of the 32-deep strip.  Each 16-lane group reads a 4 k x 16 n block
+    // with ds_read_b64_tr_b16 (lane address: row 8(l/16) + (l%16)/4, columns
+    // 4(l%4) .. +3), then the one 4 rows further on.  Block j adds 2j to the
+    // 16-byte chunk index, which the swizzle (chunk XOR 4(k%4)) leaves on
+    // address bits 5-7 together with the XOR term: block j's address is
+    // block 0's XOR 32j.
     const GR_LDS uint8_t* lds_p = (const GR_LDS uint8_t*)lds;
-    const uint32_t ar = wm * WAVE_TM + (lane & 31u);
-    uint32_t a_addr[KSUB];
-#pragma unroll
-    for (int s = 0; s < KSUB; ++s)
-        a_addr[s] = (uint32_t)(uintptr_t)(lds_p + A_BASE + a64_off(ar, 2u * s + (lane >> 5)));
-    const uint32_t bk = 8u * (lane >> 5) + ((lane & 15u) >> 2);
-    const GR_LDS uint8_t* b_ptr[FN];
-#pragma unroll
-    for (int j = 0; j < FN; ++j) {
-        const uint32_t n = wn * WAVE_TN + 32u * j + 16u * ((lane >> 4) & 1u) + 4u * (lane & 3u);
-        b_ptr[j] = lds_p + b_off(bk, n >> 3) + 2u * (n & 7u);
-    }
-    // BT: B operand of step s, block j is row wn*128 + 32j + lane%32 of the
-    // Bt strip, chunk 2s + lane/32 (block j is 2 KiB further on).
-    const uint32_t br = wn * WAVE_TN + (lane & 31u);
-    const GR_LDS uint8_t* bt_ptr[KSUB];
-#pragma unroll
-    for (int s = 0; s < KSUB; ++s) bt_ptr[s] = lds_p + tile2::a_off(br, 2u * s + (lane >> 5));
+    const uint32_t a_addr = (uint32_t)(uintptr_t)(lds_p + A_BASE + a64_off(wm * WAVE_TM + (lane & 15u), lane >> 4));
+    const uint32_t bk = 8u * (lane >> 4) + ((lane & 15u) >> 2);
+    const uint32_t bn = wn * WAVE_TN + 4u * (lane & 3u);
+    const uint32_t b_addr = (uint32_t)(uintptr_t)(lds_p + b_off(bk, bn >> 3) + 2u * (bn & 7u));
 
-    f32x16 acc[FM][FN];
+    f32x4 acc[FM][FN];
 #pragma unroll
     for (int i = 0; i < FM; ++i)
 #pragma unroll
-        for (int j = 0; j < FN; ++j) acc[i][j] = f32x16{};
+        for (int j = 0; j < FN; ++j) acc[i][j] = f32x4{};
 
     // Read r (0..15) of the fragments of a step using half H of the A strip in
     // slot byte offset `ao` and the B strip at `bo`, in the order the MFMAs
-    // consume them: A(0,0), B(0,0..3), A(0,1..3), A(1,0), B(1,0..3), A(1,1..3).
+    // consume them: A0, B0 .. B7, A1 .. A7.
     auto read_one = [&](auto h_c, Frags& f, uint32_t ao, uint32_t bo, int r) {
         constexpr uint32_t H = decltype(h_c)::value;
-        const int s = r >> 3, q = r & 7;
-        if (q == 0 || q > 4) {
-            const int i = q == 0 ? 0 : q - 4;
-            const uint32_t addr = ((a_addr[s] + ao) ^ (64u * H)) + 4096u * i;
-            f.a[s][i] = read_a_operand((const GR_LDS uint8_t*)(uintptr_t)addr);
+        if (r == 0 || r > FN) {
+            const int i = r == 0 ? 0 : r - FN;
+            const uint32_t addr = ((a_addr + ao) ^ (64u * H)) + 2048u * i;
+            f.a[i] = read_a_operand((const GR_LDS uint8_t*)(uintptr_t)addr);
         } else {
-            const int j = q - 1;
-            if constexpr (BT) f.b[s][j] = read_a_operand(bt_ptr[s] + bo + 2048u * j);
-            else f.b[s][j] = read_b_operand(b_ptr[j] + bo + 8192u * s);
+            const int j = r - 1;
+            f.b[j] = read_b_operand((const GR_LDS uint8_t*)(uintptr_t)((b_addr + bo) ^ (32u * j)));
         }
     };
     auto a_slot = [&](uint32_t kt) { return ((kt >> 1) % A_SLOTS) * A_SLOT_BYTES; };
@@ -197,9 +184,10 @@ __global__ __launch_bounds__(THREADS, 1) void gemm_relu_tile3_kernel(
     using H0 = std::integral_constant<uint32_t, 0>;
     using H1 = std::integral_constant<uint32_t, 1>;
 
+    // MFMA t (0..63) of a step: block row t/8, block column t%8.
     auto mfma_one = [&](const Frags& f, int t) {
-        const int s = t >> 4, i = (t >> 2) & 3, j = t & 3;
-        acc[i][j] = E::mfma32(f.b[s][j], f.a[s][i], acc[i][j]);
+        const int i = t >> 3, j = t & 7;
+        acc[i][j] = E::mfma16(f.b[j], f.a[i], acc[i][j]);
     };
 
     const uint32_t KT = (uint32_t)(K / BK);  // even, >= 2
@@ -255,12 +243,12 @@ __global__ __launch_bounds__(THREADS, 1) void gemm_relu_tile3_kernel(
     auto n_issued = [&](uint32_t s) -> uint32_t { return 4u * ((s >> 1) + 2 < KTA) + 4u * (s + 3 < KT); };
 
     // Steady step: every copy of step kt exists and the wait is "only the
-    // previous step's 8 copies may remain".  Same interleaving as the 32-deep
-    // pipelined kernel: 4 MFMAs, wait + barrier, then one memory operation
-    // after each of the next 24 MFMAs.  NH = half of A used by step kt+1.
+    // previous step's 8 copies may remain".  8 MFMAs, wait + barrier, then
+    // one memory operation after every second of the next 48 MFMAs (a copy
+    // after every third of those).  NH = half of A used by step kt+1.
     auto step = [&](auto nh_c, uint32_t kt, Frags& cur, Frags& nxt) {
 #pragma unroll
-        for (int t = 0; t < 4; ++t) mfma_one(cur, t);
+        for (int t = 0; t < 8; ++t) mfma_one(cur, t);
         pin();
         wait_vmcnt<8>();
         barrier();
@@ -269,12 +257,12 @@ __global__ __launch_bounds__(THREADS, 1) void gemm_relu_tile3_kernel(
         const uint32_t ao = a_slot(kt + 1), bo = b_slot(kt + 1);
         int rd = 0, cp = 0;
 #pragma unroll
-        for (int t = 4; t < 32; ++t) {
+        for (int t = 8; t < 64; ++t) {
             mfma_one(cur, t);
             pin();
-            const int k = t - 4;
-            if (k < 24) {
-                if (k % 3 == 1) {
+            const int k = t - 8;
+            if (k < 48 && (k & 1) == 0) {
+                if ((k >> 1) % 3 == 1) {
                     if (cp < 4) dma_a(ja, kt & 1u, cp);
                     else dma_b(kt + 3, cp - 4);
                     ++cp;
@@ -293,7 +281,7 @@ __global__ __launch_bounds__(THREADS, 1) void gemm_relu_tile3_kernel(
         if (kt >= KT) return;
         const bool more = kt + 1 < KT;
 #pragma unroll
-        for (int t = 0; t < 4; ++t) mfma_one(cur, t);
+        for (int t = 0; t < 8; ++t) mfma_one(cur, t);
         pin();
         if (more) {
             uint32_t allowed;
@@ -321,7 +309,7 @@ __global__ __launch_bounds__(THREADS, 1) void gemm_relu_tile3_kernel(
         }
         pin();
 #pragma unroll
-        for (int t = 4; t < 32; ++t) mfma_one(cur, t);
+        for (int t = 8; t < 64; ++t) mfma_one(cur, t);
         pin();
     };
 

@@ -12,14 +12,24 @@
 // Bt strip t/2) in a ring of 5 slots of 32 KiB (160 KiB): strip t lives in slot
 // t % 5.  Step kt (32 MFMAs per wave) uses half kt%2 of the pair of strips
 // 2(kt/2), 2(kt/2)+1; the fragments for step kt+1 are read while step kt runs.
-// Step s copies strip s+4 (8 copies per wave), which overwrites strip s-1,
-// whose pair was last read in step s-1 or earlier.  Before the barrier of each
-// step every wave waits for its own fragment reads (lgkmcnt 0; the last one was
-// issued 8 MFMAs before), so after that barrier no wave still reads strip s-1.
-// Strip t is needed by the reads in step 2(t/2)-1 and was copied in step t-4:
-// A strips two steps ahead of that, Bt strips one more.  Steady waits: odd
-// steps let the previous step's 8 copies stay in flight, even steps the
-// previous two steps' 16.
+// Step s copies strip s+4 (8 copies per wave), which overwrites strip s-1.
+//
+// Only odd steps 2p-1, whose reads start on pair p, wait for copies and meet
+// at a barrier; the reads of an even step 2p use the pair made visible one
+// step before.  Before that barrier every wave waits for its own fragment
+// reads as well (lgkmcnt 0; the last one was issued 8 MFMAs before).  After
+// the barrier of step 2p-1 every read of pair p-1 (issued in steps 2p-3 and
+// 2p-2) has completed in every wave, so the copies of steps 2p-1 and 2p
+// (strips 2p+3 and 2p+4, over strips 2p-2 and 2p-1 of pair p-1) may start.
+// Pair p+1 must have landed by the wait of step 2p+1: its A strip was copied
+// three steps before, its Bt strip two, and the wait lets the previous step's
+// 8 copies stay in flight.
+//
+// Each wave owns 128 x 128 of C as 8 x 8 blocks of 16 x 16
+// (v_mfma_f32_16x16x32, 64 per step, each taking all 32 k of the step; with
+// the same reads and copies this measured 5-8% faster than 16 blocks of
+// 32 x 32 with two v_mfma_f32_32x32x16 per step).  Fragments: ds_read_b128
+// of 8 consecutive k of one row, 16 rows per read.
 #pragma once
 
 #include <type_traits>
@@ -40,9 +50,8 @@ constexpr int SLOTS = 5;
 constexpr int THREADS = 256;
 constexpr int WAVE_TM = 128;
 constexpr int WAVE_TN = 128;
-constexpr int FM = WAVE_TM / 32;
-constexpr int FN = WAVE_TN / 32;
-constexpr int KSUB = BK / 16;
+constexpr int FM = WAVE_TM / 16;  // 16-row blocks of A per wave
+constexpr int FN = WAVE_TN / 16;  // 16-row blocks of Bt per wave
 constexpr int SLOT_BYTES = BM * BKS * 2;   // 32 KiB (BM == BN)
 constexpr int LDS_BYTES = SLOTS * SLOT_BYTES;  // 160 KiB
 
@@ -52,6 +61,12 @@ static_assert(BM == BN, "A and Bt strips share one slot size");
 static_assert(LDS_BYTES >= 4 * epi::REGION_BYTES, "the epilogue stages four wave tiles in LDS");
 
 __device__ __forceinline__ void wait_lgkm0() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
+
+// Operands of one 32-deep step.
+struct Frags {
+    f16x8 a[FM];
+    f16x8 b[FN];
+};
 
 // E: element type (ElemF16 or ElemBF16) or Epi<...> for bias + activation.
 template <bool EDGE, typename E = ElemF16>
@@ -65,7 +80,6 @@ __global__ __launch_bounds__(THREADS, 1) void gemm_relu_tile3t_kernel(
     using tile2::read_a_operand;
     using tile2::wait_vmcnt;
     using tile3::a64_off;
-    using tile3::Frags;
 
     __shared__ __attribute__((aligned(1024))) uint8_t lds[LDS_BYTES];
 
@@ -121,40 +135,34 @@ __global__ __launch_bounds__(THREADS, 1) void gemm_relu_tile3t_kernel(
     };
 
     // ---- fragment addresses --------------------------------------------------
-    // Operand for half h, MFMA step s, block i: row 128*wm (A) or 128*wn (Bt)
-    // + 32i + lane%32, chunk 4h + 2s + lane/32; block i is +4 KiB, and half 1
+    // Operand for half h, block i: row 128*wm (A) or 128*wn (Bt) + 16i +
+    // lane%16, chunk 4h + lane/16 (the 16-row block moves the row swizzle
+    // term (row/2)%8 by a multiple of 8: none).  Block i is +2 KiB, and half 1
     // is half 0 XOR 64 (chunks of half 0 are below 4; slot offsets are
     // multiples of 1 KiB).
     const GR_LDS uint8_t* lds_p = (const GR_LDS uint8_t*)lds;
-    const uint32_t ar = wm * WAVE_TM + (lane & 31u);
-    const uint32_t br = wn * WAVE_TN + (lane & 31u);
-    uint32_t a_addr[KSUB], b_addr[KSUB];
-#pragma unroll
-    for (int s = 0; s < KSUB; ++s) {
-        a_addr[s] = (uint32_t)(uintptr_t)(lds_p + a64_off(ar, 2u * s + (lane >> 5)));
-        b_addr[s] = (uint32_t)(uintptr_t)(lds_p + a64_off(br, 2u * s + (lane >> 5)));
-    }
+    const uint32_t a_addr = (uint32_t)(uintptr_t)(lds_p + a64_off(wm * WAVE_TM + (lane & 15u), lane >> 4));
+    const uint32_t b_addr = (uint32_t)(uintptr_t)(lds_p + a64_off(wn * WAVE_TN + (lane & 15u), lane >> 4));
 
-    f32x16 acc[FM][FN];
+    f32x4 acc[FM][FN];
 #pragma unroll
     for (int i = 0; i < FM; ++i)
 #pragma unroll
-        for (int j = 0; j < FN; ++j) acc[i][j] = f32x16{};
+        for (int j = 0; j < FN; ++j) acc[i][j] = f32x4{};
 
     // Read r (0..15) of the fragments of a step using half H of the pair in
     // slots at byte offsets ao (A) and bo (Bt), in the order the MFMAs consume
-    // them: A(0,0), B(0,0..3), A(0,1..3), A(1,0), B(1,0..3), A(1,1..3).
+    // them: A0, B0 .. B7, A1 .. A7.
     auto read_one = [&](auto h_c, Frags& f, uint32_t ao, uint32_t bo, int r) {
         constexpr uint32_t H = decltype(h_c)::value;
-        const int s = r >> 3, q = r & 7;
-        if (q == 0 || q > 4) {
-            const int i = q == 0 ? 0 : q - 4;
-            const uint32_t addr = ((a_addr[s] + ao) ^ (64u * H)) + 4096u * i;
-            f.a[s][i] = read_a_operand((const GR_LDS uint8_t*)(uintptr_t)addr);
+        if (r == 0 || r > FN) {
+            const int i = r == 0 ? 0 : r - FN;
+            const uint32_t addr = ((a_addr + ao) ^ (64u * H)) + 2048u * i;
+            f.a[i] = read_a_operand((const GR_LDS uint8_t*)(uintptr_t)addr);
         } else {
-            const int j = q - 1;
-            const uint32_t addr = ((b_addr[s] + bo) ^ (64u * H)) + 4096u * j;
-            f.b[s][j] = read_a_operand((const GR_LDS uint8_t*)(uintptr_t)addr);
+            const int j = r - 1;
+            const uint32_t addr = ((b_addr + bo) ^ (64u * H)) + 2048u * j;
+            f.b[j] = read_a_operand((const GR_LDS uint8_t*)(uintptr_t)addr);
         }
     };
     auto a_slot = [&](uint32_t kt) { return ((kt & ~1u) % SLOTS) * SLOT_BYTES; };
@@ -162,9 +170,10 @@ __global__ __launch_bounds__(THREADS, 1) void gemm_relu_tile3t_kernel(
     using H0 = std::integral_constant<uint32_t, 0>;
     using H1 = std::integral_constant<uint32_t, 1>;
 
+    // MFMA t (0..63) of a step: block row t/8, block column t%8.
     auto mfma_one = [&](const Frags& f, int t) {
-        const int s = t >> 4, i = (t >> 2) & 3, j = t & 3;
-        acc[i][j] = E::mfma32(f.b[s][j], f.a[s][i], acc[i][j]);
+        const int i = t >> 3, j = t & 7;
+        acc[i][j] = E::mfma16(f.b[j], f.a[i], acc[i][j]);
     };
 
     // Prologue: strips 0 .. 3 (A0, Bt0, A1, Bt1); wait for the first pair.
@@ -181,31 +190,33 @@ __global__ __launch_bounds__(THREADS, 1) void gemm_relu_tile3t_kernel(
     for (int r = 0; r < 16; ++r) read_one(H0{}, f0, a_slot(0), b_slot(0), r);
 
     // Steady step: strip kt+4 exists and strips up to kt+3 were issued before
-    // the wait.  4 MFMAs, the waits and the barrier, then one memory operation
-    // after each of the next 24 MFMAs (a copy after every third).  NH = half
-    // used by step kt+1 (kt odd: NH = 0, the next pair's strips were copied
-    // by step kt-2 at the latest and step kt-1's 8 copies may remain; kt even:
-    // NH = 1, steps kt-1 and kt-2 may remain).
+    // it.  8 MFMAs, the waits and the barrier (odd kt only), then one memory
+    // operation after every second of the next 48 MFMAs (a copy after every
+    // third of those).
+    // NH = half used by step kt+1 (kt odd: NH = 0, the next pair's strips
+    // were copied by step kt-2 at the latest and step kt-1's 8 copies may
+    // remain; kt even: NH = 1, no wait).
     auto step = [&](auto nh_c, uint32_t kt, Frags& cur, Frags& nxt) {
         constexpr uint32_t NH = decltype(nh_c)::value;
 #pragma unroll
-        for (int t = 0; t < 4; ++t) mfma_one(cur, t);
+        for (int t = 0; t < 8; ++t) mfma_one(cur, t);
         pin();
-        if constexpr (NH == 0) wait_vmcnt<8>();
-        else wait_vmcnt<16>();
-        wait_lgkm0();
-        barrier();
+        if constexpr (NH == 0) {
+            wait_vmcnt<8>();
+            wait_lgkm0();
+            barrier();
+        }
         pin();
         const uint32_t ao = a_slot(kt + 1), bo = b_slot(kt + 1);
         const uint32_t t_copy = kt + 4;
         int rd = 0, cp = 0;
 #pragma unroll
-        for (int t = 4; t < 32; ++t) {
+        for (int t = 8; t < 64; ++t) {
             mfma_one(cur, t);
             pin();
-            const int k = t - 4;
-            if (k < 24) {
-                if (k % 3 == 1) {
+            const int k = t - 8;
+            if (k < 48 && (k & 1) == 0) {
+                if ((k >> 1) % 3 == 1) {
                     dma_strip(t_copy, cp);
                     ++cp;
                 } else {
@@ -218,16 +229,17 @@ __global__ __launch_bounds__(THREADS, 1) void gemm_relu_tile3t_kernel(
     };
 
     // Generic step with its decisions taken at run time (first step and the
-    // last few): before the reads for step kt+1, every strip up to that step's
-    // pair (2p+1, p = (kt+1)/2) must have landed; issued so far are the strips
-    // up to min(kt+3, NS-1).
+    // last few): for odd kt, before the reads for step kt+1, every strip up to
+    // that step's pair (2p+1, p = (kt+1)/2) must have landed; issued so far
+    // are the strips up to min(kt+3, NS-1).  Even kt: no wait (step 0 reads
+    // pair 0, which the prologue waited for).
     auto step_any = [&](uint32_t kt, Frags& cur, Frags& nxt) {
         if (kt >= KT) return;
         const bool more = kt + 1 < KT;
 #pragma unroll
-        for (int t = 0; t < 4; ++t) mfma_one(cur, t);
+        for (int t = 0; t < 8; ++t) mfma_one(cur, t);
         pin();
-        if (more) {
+        if (more && (kt & 1u)) {
             const uint32_t need = 2u * ((kt + 1) >> 1) + 1u;
             const uint32_t issued = kt + 3 < NS - 1 ? kt + 3 : NS - 1;
             const uint32_t allowed = issued > need ? 8u * (issued - need) : 0u;
@@ -252,7 +264,7 @@ __global__ __launch_bounds__(THREADS, 1) void gemm_relu_tile3t_kernel(
         }
         pin();
 #pragma unroll
-        for (int t = 4; t < 32; ++t) mfma_one(cur, t);
+        for (int t = 8; t < 64; ++t) mfma_one(cur, t);
         pin();
     };
 

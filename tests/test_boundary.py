@@ -704,8 +704,9 @@ def test_no_kernel_spills_to_scratch():
     scratch = [int(x) for x in re.findall(r"ScratchSize \[bytes/lane\]: (\d+)", res.stderr)]
     assert names and len(names) == len(scratch)
     hot = {n: s for n, s in zip(names, scratch)
-           if any(k in n for k in ("gemm_relu_tile2_kernel", "gemm_relu_tile3_kernel", "gemm_relu_tile128_kernel",
-                                   "gemm_relu_smallm_kernel", "gemm_relu_smallm_split_kernel"))}
+           if any(k in n for k in ("gemm_relu_tile2_kernel", "gemm_relu_tile3_kernel", "gemm_relu_tile3t_kernel",
+                                   "gemm_relu_tile128_kernel", "gemm_relu_smallm_kernel",
+                                   "gemm_relu_smallm_split_kernel"))}
     assert hot, names
     # the pipelined whole-tile kernels may spill a few bytes outside their
     # steady loop; the small-M kernel must not spill at all
