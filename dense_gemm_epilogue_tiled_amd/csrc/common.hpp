@@ -351,29 +351,29 @@ struct AccTile<f32x4[BM][BN]> {
     static constexpr int FM = BM / 2, FN = BN / 2;
 };
 
-// fp32 values of the 32-row block i of a wave tile into LDS: element (r, c)
-// of the block is word c%4 of 16-byte chunk off(r, c/4).
+// fp32 values of the next 32-row block of a wave tile into LDS: element
+// (r, c) of the block is word c%4 of 16-byte chunk off(r, c/4).  Called for
+// the blocks in order from a rolled loop: each call writes the first block
+// and moves the others up, so that no register is selected by the caller's
+// loop counter (which makes the compiler keep the accumulators in scratch
+// memory).
 template <int FM, int FN, typename Off>
-__device__ __forceinline__ void stage_fp32_rows(const f32x16 (&acc)[FM][FN], int i, uint8_t* region, uint32_t lane,
-                                                Off off) {
+__device__ __forceinline__ void stage_fp32_rows(f32x16 (&acc)[FM][FN], uint8_t* region, uint32_t lane, Off off) {
     const uint32_t r_lane = lane & 31u, half = lane >> 5;
 #pragma unroll
-    for (int ii = 0; ii < FM; ++ii) {
-        if (ii != i) continue;
+    for (int j = 0; j < FN; ++j)
 #pragma unroll
-        for (int j = 0; j < FN; ++j)
+        for (int q = 0; q < 4; ++q)
+            *reinterpret_cast<f32x4*>(region + off(r_lane, 8u * j + 2u * q + half)) =
+                f32x4{acc[0][j][4 * q + 0], acc[0][j][4 * q + 1], acc[0][j][4 * q + 2], acc[0][j][4 * q + 3]};
 #pragma unroll
-            for (int q = 0; q < 4; ++q)
-                *reinterpret_cast<f32x4*>(region + off(r_lane, 8u * j + 2u * q + half)) =
-                    f32x4{acc[ii][j][4 * q + 0], acc[ii][j][4 * q + 1], acc[ii][j][4 * q + 2], acc[ii][j][4 * q + 3]};
-    }
+    for (int ii = 0; ii + 1 < FM; ++ii)
+#pragma unroll
+        for (int j = 0; j < FN; ++j) acc[ii][j] = acc[ii + 1][j];
 }
-// 16 x 16 blocks, called for i = 0, 1, ... in turn: writes the first two
-// block rows, then moves the others up by two, so that the rolled caller
-// never selects registers by its loop counter (which made the compiler keep
-// the 64 accumulators in scratch memory).
+// 16 x 16 blocks: the first two block rows, then the others move up by two.
 template <int BM, int BN, typename Off>
-__device__ __forceinline__ void stage_fp32_rows(f32x4 (&acc)[BM][BN], int, uint8_t* region, uint32_t lane, Off off) {
+__device__ __forceinline__ void stage_fp32_rows(f32x4 (&acc)[BM][BN], uint8_t* region, uint32_t lane, Off off) {
     const uint32_t r = lane & 15u, g = lane >> 4;
 #pragma unroll
     for (int ii = 0; ii < 2; ++ii)
@@ -422,7 +422,7 @@ __device__ __forceinline__ void store_wave_tile_general(Acc& acc, uint8_t* regio
 #pragma unroll 1
     for (int i = 0; i < FM; ++i) {
         __syncthreads();
-        stage_fp32_rows(acc, i, region, lane, off);
+        stage_fp32_rows(acc, region, lane, off);
         __syncthreads();
         // One copy of the read-back per activation; two rows in flight.
         act::dispatch(ep.act, [&](auto tag) {

@@ -703,13 +703,11 @@ def test_no_kernel_spills_to_scratch():
     names = re.findall(r"Function Name: (\S+)", res.stderr)
     scratch = [int(x) for x in re.findall(r"ScratchSize \[bytes/lane\]: (\d+)", res.stderr)]
     assert names and len(names) == len(scratch)
-    hot = {n: s for n, s in zip(names, scratch)
-           if any(k in n for k in ("gemm_relu_tile2_kernel", "gemm_relu_tile3_kernel", "gemm_relu_tile3t_kernel",
-                                   "gemm_relu_tile128_kernel", "gemm_relu_smallm_kernel",
-                                   "gemm_relu_smallm_split_kernel"))}
-    assert hot, names
-    # the pipelined whole-tile kernels may spill a few bytes outside their
-    # steady loop; the small-M kernel must not spill at all
+    hot = dict(zip(names, scratch))
+    assert any("gemm_relu_tile3_kernel" in n for n in hot) and any("gemm_fp8_tile_kernel" in n for n in hot), names
+    # every kernel, whatever its epilogue: the pipelined 256 x 256 kernels
+    # may spill a few bytes outside their steady loop; the small-M and
+    # 128 x 128 kernels must not spill at all
     for n, s in hot.items():
         limit = 0 if ("smallm" in n or "tile128" in n) else 16
         assert s <= limit, (n, s)
