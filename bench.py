@@ -9,7 +9,7 @@ Prints ONE JSON line (rank 0) with the metric, the roofline of the dominant
 kernel measured live with HIP events on the launch stream, and the CPU oracle
 timed on a bounded sample of the same workload.
 
-  python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+  python bench.py [--gpus 1] [--steps K] [--warmup W] [--settle-ms MS] [--no-cpu-baseline]
                   [--no-workloads] [--workload NAME] [--copy-probe MIB]
                   [--vendor-reference] [--extra-shapes]
 
@@ -266,6 +266,23 @@ def bench_flushed(gr, torch, w, reps, ws):
     return times
 
 
+def settle(torch, run, ms):
+    """Untimed back-to-back launches for ``ms`` milliseconds of wall time.
+    Under full load the shader clock moves for tens of milliseconds (at
+    4096^3 the first launches take about 125 us, the ones after 40 ms about
+    103 us, after 70 ms about 102 us), longer than a few warmup steps last, so
+    the timed region would otherwise measure the ramp.  Returns the number of
+    launches."""
+    n = 0
+    t_end = time.perf_counter() + ms / 1e3
+    while time.perf_counter() < t_end:
+        for _ in range(20):
+            run()
+        n += 20
+        torch.cuda.synchronize()
+    return n
+
+
 def observed_sclk(torch, run, seconds=1.0):
     """The shader clock under this load: the kernel runs back-to-back for
     ``seconds`` (outside the timed region) while a thread reads the current
@@ -501,6 +518,9 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=25)
+    ap.add_argument("--settle-ms", type=float, default=250.0,
+                    help="untimed back-to-back launches for this long before the warmup steps: the shader "
+                         "clock takes some 40-70 ms of full load to settle")
     ap.add_argument("--workload", default="square4096", choices=sorted(synth.WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-workloads", action="store_true", help="skip the secondary per-workload table")
@@ -546,6 +566,7 @@ def main():
     run = launcher(gr, torch, w, A, Bs[0], C, stream, ws)
     plan = plan_for(gr, w, A, Bs[0], C, ws)
 
+    settle_launches = settle(torch, run, args.settle_ms)
     for _ in range(args.warmup):
         run()
     torch.cuda.synchronize()
@@ -593,6 +614,8 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "settle_ms": args.settle_ms,
+        "settle_launches": settle_launches,
         "ms_per_step": round(wall * 1e3 / args.steps, 5),
         "higher_is_better": True,
         "scaling": "weak",
