@@ -696,6 +696,11 @@ BT_CASES = [
     (300, 270, 100, 109, 105, 273, gr.GR_PATH_TILE_EDGE),      # odd pitches
     (4352, 4352, 128, 128, 136, 4352, gr.GR_PATH_TILE),        # 289 tiles: a second round
     (4100, 4400, 96, 96, 96, 4400, gr.GR_PATH_TILE),           # 306 partial tiles
+    # 256 x 256 tiles with K % 64 = 0 (A and Bt in one ring of 64-deep strips):
+    (2600, 3000, 1024, 1024, 1032, 3001, gr.GR_PATH_TILE),     # partial tiles, clamped Bt rows, steady steps
+    (4096, 2304, 64, 64, 64, 2304, gr.GR_PATH_TILE),           # one pair of strips
+    (4096, 2304, 192, 200, 192, 2304, gr.GR_PATH_TILE),        # three pairs: no steady step
+    (4096, 2304, 320, 320, 328, 2304, gr.GR_PATH_TILE),        # steady steps, then the tail
 ]
 
 
