@@ -30,6 +30,11 @@
  *   - Any M, N, K >= 0 work with the same library: tile shapes are fixed when
  *     the library is built; edges that do not fill a tile are guarded.
  *     M == 0 or N == 0: nothing is launched, GR_OK.  K == 0: C = +0.
+ *     (One compiled kernel serving every shape, with the sizes read from the
+ *     arguments of each call and guards on the ragged edges: TileLang
+ *     tutorial, chapter "动态形状与变长序列" (dynamic shapes and variable
+ *     length), section "T.dynamic 的机制".  Zero K iterations leave the
+ *     cleared accumulator: chapter "GEMM 走读与参数推导", T.clear.)
  *   - Pitches: lda >= max(1, K), ldb >= max(1, N), ldc >= max(1, N).  Any
  *     element alignment is accepted; 16-byte aligned rows take faster code.
  *   - The byte range C spans must not overlap the ranges of A or B.
@@ -39,7 +44,14 @@
  *   - Errors: every entry point returns GR_OK (0) or a negative GR_ERR_* code
  *     and never throws across the ABI.  Argument checks run before any HIP
  *     call, so they work without a GPU.  gemm_relu_status_string() names a
- *     code.
+ *     code.  A call never degrades silently: a problem it cannot run is
+ *     refused with a code before anything is launched, the way the pages'
+ *     tool chain rejects what it cannot lower (TileLang tutorial: chapter
+ *     "自动调优", an unknown config key is an error; chapter "归约、扫描与
+ *     原子", a mismatched output shape raises ValueError; chapter "动态形状
+ *     与变长序列", a size with no source raises TypeError; chapter "后端与
+ *     codegen", a missing lowering is a compile error, never silently wrong
+ *     code; chapter "CUDA 硬件故障手册", launch-time errors are fatal).
  *   - Thread safety: calls are reentrant; per-device properties are cached
  *     once with thread-safe initialisation.
  */
@@ -52,7 +64,13 @@
 extern "C" {
 #endif
 
-/* ---- status codes --------------------------------------------------------- */
+/* ---- status codes ----------------------------------------------------------
+ * Each code names one way a call is refused before launch (GR_ERR_LAUNCH:
+ * the runtime rejected the launch).  Failing loudly, with the cause named,
+ * follows the pages' error behaviour listed under "Errors" above (TileLang
+ * tutorial, chapters "自动调优", "归约、扫描与原子", "动态形状与变长序列",
+ * "后端与 codegen" and "CUDA 硬件故障手册").
+ */
 #define GR_OK                        0
 #define GR_ERR_INVALID_DIM          -1 /* M, N or K negative (MX calls: K % 32 != 0)     */
 #define GR_ERR_INVALID_LD           -2 /* lda < max(1,K), ldb < max(1,N) or ldc < max(1,N) */
@@ -123,6 +141,12 @@ int gemm_relu_f16(int64_t M, int64_t N, int64_t K,
 /*
  * gemm_relu_f16_plan -- pure planner: validates the arguments exactly as
  * gemm_relu_f16 does and reports the path, tile and grid it would launch.
+ * It is the library's "look at what the kernel became" hook: the pages
+ * inspect the generated kernel (tile sizes, stages, shared-memory buffers)
+ * before any performance discussion ("TileLang programming basics", section
+ * "六、写完之后的三个动作", step 2, get_kernel_source; TileLang tutorial,
+ * chapter "安装与第一个 kernel").  Tests and the benchmark use it to name the
+ * tile edges they check and the path they time.
  * Makes no HIP call and touches no memory behind the pointers: it only uses
  * their values (for alignment and overlap checks), so it runs without a GPU.
  *   out   host pointer to a gr_plan_t to fill (must not be NULL)
@@ -138,6 +162,10 @@ int gemm_relu_f16_plan(int64_t M, int64_t N, int64_t K,
 /*
  * gemm_relu_f16_forced -- as gemm_relu_f16, but runs the given path instead of
  * the planner's choice, for tests that cross-check the paths on one input.
+ * The pages check every candidate kernel configuration against one
+ * reference on the same inputs ("TileLang programming basics", section
+ * "六、写完之后的三个动作", step 1: the autotuner validates each config the
+ * same way); this hook lets the tests do that for every path.
  *   path  GR_PATH_TILE, GR_PATH_TILE_EDGE or GR_PATH_SMALL_M.
  * GR_PATH_TILE is accepted only when the planner's conditions for it hold
  * (16-byte aligned rows of A and B, K a positive multiple of 32, pitches of
@@ -175,6 +203,16 @@ int gemm_relu_f16_forced(int64_t M, int64_t N, int64_t K,
  *     fp32 partial sums go to the workspace and the same second launch sums
  *     them in order and applies ReLU.  Same result as GR_PATH_TILE up to fp32
  *     summation order.
+ *
+ * Where this comes from: the packed copy applies, ahead of time, the pages'
+ * edge rule that out-of-range elements of both operands read as zero
+ * (TileLang tutorial, chapter "动态形状与变长序列"); the split paths are the
+ * split-K of "TileLang programming basics", section 5.1 "Split-K" and of the
+ * tutorial's chapter "归约、扫描与原子" (partial sums over K slices), made
+ * deterministic by adding the partials in a fixed order, and with ReLU
+ * applied once to the complete sum.  The caller owns the scratch memory as
+ * it owns C (destination passing: "Writing high-performance kernels in
+ * TileLang", section "編寫一個 GEMM").
  *
  * Workspace rules: a DEVICE pointer, 256-byte aligned, owned by the caller,
  * not overlapping A, B or C; its contents on entry are ignored and on return
@@ -619,11 +657,14 @@ int gemm_mxfp4_bt_plan(int64_t M, int64_t N, int64_t K,
                        const uint16_t* C, int64_t ldc, int out_fmt,
                        gr_plan_t* out);
 
-/* Static, NUL-terminated name of a status code ("GR_OK", "GR_ERR_ALIAS", ...).
-   Unknown codes give "GR_ERR_UNKNOWN". */
+/* Static, NUL-terminated name of a status code ("GR_OK", "GR_ERR_ALIAS", ...),
+ * so that a refused call can be reported with its cause (the fail-loudly
+ * behaviour cited at the status codes above).  Unknown codes give
+ * "GR_ERR_UNKNOWN". */
 const char* gemm_relu_status_string(int status);
 
-/* Library version as MAJOR*10000 + MINOR*100 + PATCH. */
+/* Library version as MAJOR*10000 + MINOR*100 + PATCH.  Not an operation of
+ * the pages: it identifies the build in test and benchmark reports. */
 int gemm_relu_version(void);
 
 #ifdef __cplusplus
