@@ -282,6 +282,10 @@ namespace edge {
 __device__ __forceinline__ int64_t shifted_row0(int64_t m_tile, int64_t M, int64_t bm) {
     return m_tile + bm <= M ? m_tile : M - bm;
 }
+// The same move for a last tile column (N >= bn): it ends at column N.
+__device__ __forceinline__ int64_t shifted_col0(int64_t n_tile, int64_t N, int64_t bn) {
+    return n_tile + bn <= N ? n_tile : N - bn;
+}
 
 // Chunk (8 columns) `c` of the tile starting at column n0, clamped to the
 // last chunk holding a column < N.
@@ -397,7 +401,7 @@ template <bool EDGE, typename E, typename Acc>
 __device__ __forceinline__ void store_wave_tile_general(Acc& acc, uint8_t* region, uint32_t lane,
                                                         uint16_t* __restrict__ C, int64_t ldc, int64_t row0,
                                                         int64_t col0, int64_t row_min, int64_t M, int64_t N,
-                                                        int vec_c, const EpiArgs& ep) {
+                                                        int vec_c, const EpiArgs& ep, int64_t col_min = 0) {
     constexpr int FM = AccTile<Acc>::FM, FN = AccTile<Acc>::FN;
     constexpr uint32_t COLS = 32 * FN;
     constexpr uint32_t CHUNKS = COLS / 4;  // 16-byte fp32 chunks per row, also lanes per row on the way back
@@ -441,14 +445,14 @@ __device__ __forceinline__ void store_wave_tile_general(Acc& acc, uint8_t* regio
                     o[t] = E::round(act::apply<A>(has_bias ? __fadd_rn(x, b[t]) : x));
                 }
                 uint16_t* dst = C + m * ldc + n;
-                if (wide && (!EDGE || n + 4 <= N)) {
+                if (wide && (!EDGE || (n + 4 <= N && n >= col_min))) {
                     __builtin_nontemporal_store(u32x2{(uint32_t)o[0] | ((uint32_t)o[1] << 16),
                                                       (uint32_t)o[2] | ((uint32_t)o[3] << 16)},
                                                 reinterpret_cast<u32x2*>(dst));
                 } else {
 #pragma unroll
                     for (int t = 0; t < 4; ++t)
-                        if (!EDGE || n + t < N) dst[t] = o[t];
+                        if (!EDGE || (n + t < N && n + t >= col_min)) dst[t] = o[t];
                 }
             }
         });
@@ -523,16 +527,18 @@ __device__ __forceinline__ void stage_relu_tile(const f32x4 (&acc)[BM][BN], uint
 }
 
 // acc may be overwritten.
+// col_min: with EDGE, columns below it belong to the tile on the left (a last
+// tile column moved left to end at column N) and are not stored either.
 template <bool EDGE, typename E = ElemF16, typename Acc>
 __device__ __forceinline__ void store_wave_tile(Acc& acc, uint8_t* region, uint32_t lane,
                                                 uint16_t* __restrict__ C, int64_t ldc, int64_t row0, int64_t col0,
                                                 int64_t row_min, int64_t M, int64_t N, int vec_c,
-                                                const EpiArgs& ep) {
+                                                const EpiArgs& ep, int64_t col_min = 0) {
     constexpr int FM = AccTile<Acc>::FM, FN = AccTile<Acc>::FN;
     using T = WaveTile<FM, FN>;
     if constexpr (E::kGeneral) {
         static_assert(32 * 32 * FN * 4 <= T::REGION_BYTES, "the fp32 block fits the wave's region");
-        store_wave_tile_general<EDGE, E>(acc, region, lane, C, ldc, row0, col0, row_min, M, N, vec_c, ep);
+        store_wave_tile_general<EDGE, E>(acc, region, lane, C, ldc, row0, col0, row_min, M, N, vec_c, ep, col_min);
         return;
     }
     __syncthreads();
@@ -550,7 +556,7 @@ __device__ __forceinline__ void store_wave_tile(Acc& acc, uint8_t* region, uint3
             const int64_t n = col0 + 8 * ch;
             uint16_t* dst = C + m * ldc + n;
             if (EDGE && (m < row_min || m >= M)) continue;
-            if (!EDGE || n + 8 <= N) {
+            if (!EDGE || (n + 8 <= N && n >= col_min)) {
                 // C is written once and never read back here: nontemporal
                 // stores keep it from displacing the A and B panels in L2.
                 if (vec_c == 8) {
@@ -562,7 +568,7 @@ __device__ __forceinline__ void store_wave_tile(Acc& acc, uint8_t* region, uint3
             } else {
 #pragma unroll
                 for (int e = 0; e < 8; ++e)
-                    if (n + e < N) dst[e] = (uint16_t)(v[e >> 1] >> (16 * (e & 1)));
+                    if (n + e < N && n + e >= col_min) dst[e] = (uint16_t)(v[e >> 1] >> (16 * (e & 1)));
             }
         }
     } else {
@@ -576,7 +582,7 @@ __device__ __forceinline__ void store_wave_tile(Acc& acc, uint8_t* region, uint3
                                                                   8u * T::half_slot(row, e >> 2) + 2u * (e & 3u));
             const int64_t m = row0 + row;
             const int64_t n = col0 + col;
-            if (EDGE && (m < row_min || m >= M || n >= N)) continue;
+            if (EDGE && (m < row_min || m >= M || n >= N || n < col_min)) continue;
             C[m * ldc + n] = h;
         }
     }

@@ -156,6 +156,15 @@ bool tile_fast_ok(int64_t M, int64_t N, int64_t K, uintptr_t A, int64_t lda, uin
            lda <= MAX_LDA && ldb <= MAX_LDB;
 }
 
+// The pipelined 256 x 256 kernel in place on misaligned rows and a K that
+// is no multiple of 64 (tile3's UA variant): M and N of at least one tile
+// (the last tile row and column move to end at M and N), K > 128 (the tail
+// of 1..64 plus at least two 64-deep strips) and pitches within its 32-bit
+// copy offsets.  The planner takes it when there are also more than 128
+// tiles (as for the aligned 256 x 256 kernel); the forced hook only needs
+// the kernel's own conditions.
+bool tile_unaligned_ok(int64_t M, int64_t N, int64_t K, int64_t lda, int64_t ldb);
+
 // 256 x 256 tiles unless they would fill less than half of one wave of
 // workgroups over the 256 CUs (or M < 256): then 128 x 128 tiles, which give
 // four times as many workgroups.
@@ -165,6 +174,11 @@ bool use_large_tiles(int64_t M, int64_t N) {
     if (M < BM) return false;
     const int64_t tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
     return tiles > kSmallTileMaxLargeTiles;
+}
+
+bool tile_unaligned_ok(int64_t M, int64_t N, int64_t K, int64_t lda, int64_t ldb) {
+    using namespace gr::tile3;
+    return M >= BM && N >= BN && K > 2 * BKA && lda <= MAX_LDA && ldb <= MAX_LDB;
 }
 
 // Split-K of the 128 x 128 tile path (workspace): when the small tiles do not
@@ -250,7 +264,20 @@ void fill_plan(int path, int64_t M, int64_t N, uintptr_t A, int64_t lda, uintptr
                int64_t ldc, const Pack& pk, const SmallMSplit& sp, const TileSplit& ts, gr_plan_t* p) {
     std::memset(p, 0, sizeof(*p));
     p->path = path;
-    if (path == GR_PATH_TILE || path == GR_PATH_TILE_PACKED || path == GR_PATH_TILE_SPLIT) {
+    if (path == GR_PATH_TILE_UNALIGNED) {
+        using namespace gr::tile3;
+        p->block_m = BM;
+        p->block_n = BN;
+        p->block_k = BK;
+        p->stages = B_SLOTS;
+        p->threads = THREADS;
+        p->grid = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
+        p->vec_a = vec_width(A, lda);
+        p->vec_b = vec_width(B, ldb);
+        p->vec_c = vec_width_c(C, ldc);
+        p->group_m = kGroupM;
+        p->split_k = 1;
+    } else if (path == GR_PATH_TILE || path == GR_PATH_TILE_PACKED || path == GR_PATH_TILE_SPLIT) {
         const bool large = path != GR_PATH_TILE_SPLIT && use_large_tiles(M, N);
         const int64_t bm = large ? gr::tile2::BM : gr::tile128::BM;
         const int64_t bn = large ? gr::tile2::BN : gr::tile128::BN;
@@ -333,6 +360,7 @@ int choose_path(int64_t M, int64_t N, int64_t K, uintptr_t A, int64_t lda, uintp
     if (K > 0 && smallm_rows_ok(M, N, K, A, lda, B, ldb) && (N + gr::smallm::NB - 1) / gr::smallm::NB <= 256)
         return GR_PATH_SMALL_M;
     if (fast) return GR_PATH_TILE;
+    if (tile_unaligned_ok(M, N, K, lda, ldb) && use_large_tiles(M, N)) return GR_PATH_TILE_UNALIGNED;
     if (ws_bytes > 0 && pack_layout(M, N, K, A, lda, B, ldb, pk) && pk->bytes <= ws_bytes &&
         (double)M * (double)N * (double)K >= (double)kPackMinMacs)
         return GR_PATH_TILE_PACKED;
@@ -504,6 +532,13 @@ int run(const gr_plan_t& p, int64_t M, int64_t N, int64_t K, const uint16_t* A, 
             return launch(gemm_relu_tile2_kernel<true, false, E>, p.grid, THREADS, stream, A, B, C, M, N, K, lda, ldb,
                           ldc, tiles_m, tiles_n, gm, vc, ep);
         }
+        case GR_PATH_TILE_UNALIGNED: {
+            using namespace gr::tile3;
+            const uint32_t tiles_m = (uint32_t)((M + BM - 1) / BM);
+            const uint32_t tiles_n = (uint32_t)((N + BN - 1) / BN);
+            return launch(gemm_relu_tile3_kernel<true, E, true>, p.grid, THREADS, stream, A, B, C, M, N, K, lda, ldb,
+                          ldc, tiles_m, tiles_n, (uint32_t)p.group_m, (int)p.vec_c, ep);
+        }
         case GR_PATH_TILE_EDGE:
             switch (p.vec_a) {
                 case 8: return launch_tile_vb<true, 8, E>(p, M, N, K, A, lda, B, ldb, C, ldc, ep, stream);
@@ -554,6 +589,8 @@ int plan_call(int64_t M, int64_t N, int64_t K, uintptr_t a, int64_t lda, uintptr
     if (forced >= 0 && path != GR_PATH_NONE) {
         if (forced == GR_PATH_TILE) {
             if (!tile_fast_ok(M, N, K, a, lda, b, ldb)) return GR_ERR_INVALID_PATH;
+        } else if (forced == GR_PATH_TILE_UNALIGNED) {
+            if (!tile_unaligned_ok(M, N, K, lda, ldb)) return GR_ERR_INVALID_PATH;
         } else if (forced == GR_PATH_SMALL_M) {
             if (K == 0 || !smallm_rows_ok(M, N, K, a, lda, b, ldb)) return GR_ERR_INVALID_PATH;
         } else if (forced == GR_PATH_TILE_PACKED) {
@@ -642,7 +679,8 @@ int entry_epi(int64_t M, int64_t N, int64_t K, const uint16_t* A, int64_t lda, c
 
 bool known_path(int path) {
     return path == GR_PATH_TILE || path == GR_PATH_TILE_EDGE || path == GR_PATH_SMALL_M ||
-           path == GR_PATH_TILE_PACKED || path == GR_PATH_SMALL_M_SPLIT || path == GR_PATH_TILE_SPLIT;
+           path == GR_PATH_TILE_PACKED || path == GR_PATH_SMALL_M_SPLIT || path == GR_PATH_TILE_SPLIT ||
+           path == GR_PATH_TILE_UNALIGNED;
 }
 
 bool needs_workspace(int path) {
@@ -1234,7 +1272,8 @@ int gemm_bias_act_f16(int64_t M, int64_t N, int64_t K, const uint16_t* A, int64_
 int gemm_bias_act_f16_forced(int64_t M, int64_t N, int64_t K, const uint16_t* A, int64_t lda, const uint16_t* B,
                              int64_t ldb, const uint16_t* bias, int act, uint16_t* C, int64_t ldc, void* stream,
                              int path) {
-    if (path != GR_PATH_TILE && path != GR_PATH_TILE_EDGE && path != GR_PATH_SMALL_M) return GR_ERR_INVALID_PATH;
+    if (path != GR_PATH_TILE && path != GR_PATH_TILE_EDGE && path != GR_PATH_SMALL_M && path != GR_PATH_TILE_UNALIGNED)
+        return GR_ERR_INVALID_PATH;
     return entry_epi<gr::ElemF16>(M, N, K, A, lda, B, ldb, bias, act, C, ldc, nullptr, 0, stream, path);
 }
 
@@ -1246,7 +1285,8 @@ int gemm_bias_act_bf16(int64_t M, int64_t N, int64_t K, const uint16_t* A, int64
 int gemm_bias_act_bf16_forced(int64_t M, int64_t N, int64_t K, const uint16_t* A, int64_t lda, const uint16_t* B,
                               int64_t ldb, const uint16_t* bias, int act, uint16_t* C, int64_t ldc, void* stream,
                               int path) {
-    if (path != GR_PATH_TILE && path != GR_PATH_TILE_EDGE && path != GR_PATH_SMALL_M) return GR_ERR_INVALID_PATH;
+    if (path != GR_PATH_TILE && path != GR_PATH_TILE_EDGE && path != GR_PATH_SMALL_M && path != GR_PATH_TILE_UNALIGNED)
+        return GR_ERR_INVALID_PATH;
     return entry_epi<gr::ElemBF16>(M, N, K, A, lda, B, ldb, bias, act, C, ldc, nullptr, 0, stream, path);
 }
 
@@ -1312,6 +1352,8 @@ int gemm_relu_f16_workspace_size(int64_t M, int64_t N, int64_t K, const uint16_t
             *bytes = sp.bytes;
     } else if (tile_fast_ok(M, N, K, a, lda, b, ldb)) {
         if (!use_large_tiles(M, N) && tile_split_layout(M, N, K, false, &ts)) *bytes = ts.bytes;
+    } else if (tile_unaligned_ok(M, N, K, lda, ldb) && use_large_tiles(M, N)) {
+        // the pipelined kernel runs in place on these rows: no workspace
     } else if (pack_layout(M, N, K, a, lda, b, ldb, &pk)) {
         *bytes = pk.bytes;
     }

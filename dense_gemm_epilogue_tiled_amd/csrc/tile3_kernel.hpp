@@ -67,9 +67,33 @@ struct Frags {
     f16x8 b[FN];
 };
 
+// Tail of K for misaligned rows (UA): the first T = (K - 1) % 64 + 1 columns
+// of A and rows of B, loaded element by element with guards (zero past k = T)
+// and written to LDS in the layout of one A strip and two B strips.  Thread t
+// owns 8 chunks of 8 elements of each operand: A rows t/8 + 32 i, chunk t%8;
+// B rows t/32 + 8 i, chunk t%32.
+template <typename F>
+__device__ __forceinline__ u32x4 load8_guarded(const uint16_t* p, int64_t valid, F&& ok) {
+    uint32_t h[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) h[e] = (e < valid && ok()) ? (uint32_t)p[e] : 0u;
+    return u32x4{h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16), h[6] | (h[7] << 16)};
+}
+
 // E: element type (ElemF16 or ElemBF16; only the MFMA and the rounding
 // differ) or Epi<...> for bias + activation.
-template <bool EDGE, typename E = ElemF16>
+// UA (with EDGE, M >= 256, N >= 256, K > 128): rows of A and B need not be
+// 16-byte aligned and K need not be a multiple of 64.  The direct-to-LDS
+// copies read any 2-byte aligned address (measured on this part: every
+// offset gives the bytes of the offset address); the first T = (K - 1) % 64
+// + 1 steps of k are staged through registers with guards and multiplied
+// before the pipeline starts, and the pipeline then runs over the remaining
+// K - T (a multiple of 64).  The last tile column is moved left to end at
+// column N, like the last tile row, so every copy reads inside [0, M) x
+// [T, K) of A and [T, K) x [0, N) of B: nothing outside the operands is ever
+// read, whatever their alignment.  Tail first means a different k order
+// than the aligned kernels (a different fp32 rounding order, equally valid).
+template <bool EDGE, typename E = ElemF16, bool UA = false>
 __global__ __launch_bounds__(THREADS, 1) void gemm_relu_tile3_kernel(
     const uint16_t* __restrict__ A, const uint16_t* __restrict__ B, uint16_t* __restrict__ C, int64_t M, int64_t N,
     int64_t K, int64_t lda, int64_t ldb, int64_t ldc, uint32_t tiles_m, uint32_t tiles_n, uint32_t group_m,
@@ -90,11 +114,15 @@ __global__ __launch_bounds__(THREADS, 1) void gemm_relu_tile3_kernel(
     const uint32_t wm = wave >> 1;
     const uint32_t wn = wave & 1u;
 
+    static_assert(!UA || EDGE, "the unaligned variant moves edge tiles");
     uint32_t tm, tn;
     tile_of_workgroup(blockIdx.x, gridDim.x, tiles_m, tiles_n, group_m, tm, tn);
     const int64_t m_tile = (int64_t)tm * BM;
     const int64_t m0 = EDGE ? edge::shifted_row0(m_tile, M, BM) : m_tile;
-    const int64_t n0 = (int64_t)tn * BN;
+    const int64_t n_tile = (int64_t)tn * BN;
+    const int64_t n0 = UA ? edge::shifted_col0(n_tile, N, BN) : n_tile;
+    // UA: the K tail handled first (1..64 deep); the pipeline covers [T, K).
+    const int64_t T = UA ? (K - 1) % BKA + 1 : 0;
 
     // ---- copies -------------------------------------------------------------
     // A strip (32 KiB) = 32 blocks of 8 rows x 128 bytes; this wave fills
@@ -102,8 +130,8 @@ __global__ __launch_bounds__(THREADS, 1) void gemm_relu_tile3_kernel(
     // one.  lane -> row lane/8, slot lane%8 (chunk slot XOR (row/2)%8).
     // B strip (16 KiB) = 16 blocks of 2 rows x 512 bytes; this wave fills
     // blocks 4w .. 4w+3.  lane -> row lane/32, slot lane%32.
-    const uint8_t* base_a = reinterpret_cast<const uint8_t*>(A + m0 * lda);
-    const uint8_t* base_b = reinterpret_cast<const uint8_t*>(B + n0);
+    const uint8_t* base_a = reinterpret_cast<const uint8_t*>(A + m0 * lda + T);
+    const uint8_t* base_b = reinterpret_cast<const uint8_t*>(B + T * ldb + n0);
     const int64_t step_a = BKA * 2;
     const int64_t step_b = (int64_t)BK * ldb * 2;
     // The odd-step half (blocks +4, rows +32) only adds a wave-uniform
@@ -122,7 +150,7 @@ __global__ __launch_bounds__(THREADS, 1) void gemm_relu_tile3_kernel(
         const uint32_t blk = 4u * wave + (uint32_t)i;
         const uint32_t rb = 2u * blk + (lane >> 5);
         uint32_t cb = (lane & 31u) ^ ((rb & 3u) << 2);
-        if constexpr (EDGE) cb = edge::clamp_chunk(cb, n0, N);
+        if constexpr (EDGE && !UA) cb = edge::clamp_chunk(cb, n0, N);
         off_b[i] = (uint32_t)((rb * ldb + 8u * cb) * 2);
     }
     const uint32_t lds_base = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(GR_LDS uint8_t*)lds);
@@ -190,8 +218,24 @@ __global__ __launch_bounds__(THREADS, 1) void gemm_relu_tile3_kernel(
         acc[i][j] = E::mfma16(f.b[j], f.a[i], acc[i][j]);
     };
 
-    const uint32_t KT = (uint32_t)(K / BK);  // even, >= 2
+    const uint32_t KT = (uint32_t)((K - T) / BK);  // even, >= 2 (UA: >= 4)
     const uint32_t KTA = KT / 2;
+
+    // UA: the tail's guarded loads go out first, so that they complete before
+    // the prologue copies behind them.
+    u32x4 tail_a[8], tail_b[8];
+    if constexpr (UA) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const uint32_t r = tid / 8 + 32 * i, c = tid % 8;
+            tail_a[i] = load8_guarded(A + (m0 + r) * lda + 8 * c, T - 8 * (int64_t)c, [] { return true; });
+        }
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const uint32_t k = tid / 32 + 8 * i, c = tid % 32;
+            tail_b[i] = load8_guarded(B + k * ldb + n0 + 8 * c, 8, [&] { return (int64_t)k < T; });
+        }
+    }
 
     // Prologue copies, in this order: A0, B0, B1, A1, B2.
 #pragma unroll
@@ -209,6 +253,38 @@ __global__ __launch_bounds__(THREADS, 1) void gemm_relu_tile3_kernel(
         for (int c = 0; c < 4; ++c) dma_a(1, 0, c);
 #pragma unroll
         for (int c = 0; c < 4; ++c) dma_a(1, 1, c);
+    }
+    if constexpr (UA) {
+        // The tail's loads have landed once at most the 24 copies above
+        // (A0, B0, B1, A1) remain.  A tail -> A slot 2, B tail -> B slots 3
+        // (k < 32) and 2 (k >= 32): the slots the prologue leaves free.
+        wait_vmcnt<24>();
+        uint8_t* lds_a2 = lds + A_BASE + 2 * A_SLOT_BYTES;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const uint32_t r = tid / 8 + 32 * i, c = tid % 8;
+            *reinterpret_cast<u32x4*>(lds_a2 + a64_off(r, c)) = tail_a[i];
+        }
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const uint32_t k = tid / 32 + 8 * i, c = tid % 32;
+            uint8_t* slot = lds + (k < 32 ? 3 : 2) * B_SLOT_BYTES;
+            *reinterpret_cast<u32x4*>(slot + b_off(k & 31u, c)) = tail_b[i];
+        }
+        __syncthreads();
+        Frags ft;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) read_one(H0{}, ft, 2 * A_SLOT_BYTES, 3 * B_SLOT_BYTES, r);
+#pragma unroll
+        for (int t = 0; t < 64; ++t) mfma_one(ft, t);
+        if (T > BK) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) read_one(H1{}, ft, 2 * A_SLOT_BYTES, 2 * B_SLOT_BYTES, r);
+#pragma unroll
+            for (int t = 0; t < 64; ++t) mfma_one(ft, t);
+        }
+        // every wave is done with B slot 2 before B strip 2 is copied into it
+        __syncthreads();
     }
     if (KT > 2) {
 #pragma unroll
@@ -332,7 +408,7 @@ __global__ __launch_bounds__(THREADS, 1) void gemm_relu_tile3_kernel(
     // Epilogue: ReLU, fp16 and the store of C, staged through LDS (the
     // operand ring is no longer needed).
     epi::store_wave_tile<EDGE, E>(acc, lds + wave * epi::REGION_BYTES, lane, C, ldc, m0 + wm * WAVE_TM,
-                               n0 + wn * WAVE_TN, m_tile, M, N, vec_c, ep);
+                               n0 + wn * WAVE_TN, m_tile, M, N, vec_c, ep, n_tile);
 }
 
 #undef GR_LDS

@@ -100,6 +100,11 @@ extern "C" {
                                 /* workspace, then a pass that sums them and applies ReLU  */
 #define GR_PATH_TILE_SPLIT    6 /* 128x128-tile kernel split over K (few tiles, long K):     */
                                 /* fp32 partial sums in the workspace, then the same pass  */
+#define GR_PATH_TILE_UNALIGNED 7 /* the pipelined 256x256 kernel in place on rows that are  */
+                                 /* not 16-byte aligned and/or K % 64 != 0: direct-to-LDS */
+                                 /* copies from any 2-byte address, the K tail (1..64)    */
+                                 /* staged with guards first; M, N >= 256, K > 128, more  */
+                                 /* than 128 tiles (planner); no workspace                 */
 
 /* What the planner decided for one problem.  Filled by gemm_relu_f16_plan. */
 typedef struct gr_plan_t {
@@ -166,10 +171,15 @@ int gemm_relu_f16_plan(int64_t M, int64_t N, int64_t K,
  * reference on the same inputs ("TileLang programming basics", section
  * "六、写完之后的三个动作", step 1: the autotuner validates each config the
  * same way); this hook lets the tests do that for every path.
- *   path  GR_PATH_TILE, GR_PATH_TILE_EDGE or GR_PATH_SMALL_M.
+ *   path  GR_PATH_TILE, GR_PATH_TILE_UNALIGNED, GR_PATH_TILE_EDGE or
+ *         GR_PATH_SMALL_M.
  * GR_PATH_TILE is accepted only when the planner's conditions for it hold
  * (16-byte aligned rows of A and B, K a positive multiple of 32, pitches of
- * at most 2^22 elements for A and 2^25 for B); GR_PATH_SMALL_M
+ * at most 2^22 elements for A and 2^25 for B); GR_PATH_TILE_UNALIGNED when M
+ * >= 256, N >= 256, K > 128, there are more than 128 tiles of 256 x 256 and
+ * the pitches are within the same limits (any alignment; the planner also
+ * asks for more than 128 tiles of 256 x 256, the forced hook does not);
+ * GR_PATH_SMALL_M
  * only when the small-M kernel's alignment conditions hold (see
  * gemm_relu_f16_plan).  Otherwise GR_ERR_INVALID_PATH and nothing is
  * launched.  GR_PATH_TILE_EDGE accepts any valid problem.
@@ -186,8 +196,10 @@ int gemm_relu_f16_forced(int64_t M, int64_t N, int64_t K,
  *   - GR_PATH_TILE_PACKED.  The pipelined kernel reads A and B in whole
  *     16-byte chunks and walks K in whole 32-deep strips.  When an operand's
  *     rows are not 16-byte aligned, or K is not a multiple of 32, the calls
- *     above fall back to the guarded register-staged kernel.  With a
- *     workspace the library instead copies the offending operand(s) into it
+ *     above take GR_PATH_TILE_UNALIGNED where its conditions hold and fall
+ *     back to the guarded register-staged kernel otherwise.  With a
+ *     workspace, for the problems GR_PATH_TILE_UNALIGNED does not take, the
+ *     library instead copies the offending operand(s) into it
  *     -- rows 16-byte aligned, K padded with zeros to a multiple of 64 (the
  *     padded steps add exact zeros, the same rule as the edge guards) -- and
  *     runs the pipelined kernel on the copies: two launches on the stream,
@@ -417,9 +429,9 @@ int gemm_bias_act_bf16(int64_t M, int64_t N, int64_t K,
                        uint16_t* C, int64_t ldc,
                        void* stream);
 
-/* The two calls above on a given path (GR_PATH_TILE, GR_PATH_TILE_EDGE or
-   GR_PATH_SMALL_M; GR_ERR_INVALID_PATH otherwise or when the path's
-   conditions do not hold).  Test hooks. */
+/* The two calls above on a given path (GR_PATH_TILE, GR_PATH_TILE_UNALIGNED,
+   GR_PATH_TILE_EDGE or GR_PATH_SMALL_M; GR_ERR_INVALID_PATH otherwise or when
+   the path's conditions do not hold).  Test hooks. */
 int gemm_bias_act_f16_forced(int64_t M, int64_t N, int64_t K,
                              const uint16_t* A, int64_t lda,
                              const uint16_t* B, int64_t ldb,

@@ -136,7 +136,7 @@ def test_plan_for_each_workload():
     expect = {
         "square1024": gr.GR_PATH_TILE,
         "square4096": gr.GR_PATH_TILE,
-        "ragged4099x3071x2050": gr.GR_PATH_TILE_EDGE,
+        "ragged4099x3071x2050": gr.GR_PATH_TILE_UNALIGNED,
         "mlp8192x28672x8192": gr.GR_PATH_TILE,
         "smallm8x16384x8192": gr.GR_PATH_SMALL_M,
     }
@@ -144,7 +144,7 @@ def test_plan_for_each_workload():
         st, p = plan(w.M, w.N, w.K)
         assert st == gr.GR_OK
         assert p["path"] == expect[name], (name, p)
-        if p["path"] in (gr.GR_PATH_TILE, gr.GR_PATH_TILE_EDGE):
+        if p["path"] in (gr.GR_PATH_TILE, gr.GR_PATH_TILE_EDGE, gr.GR_PATH_TILE_UNALIGNED):
             tiles = -(-w.M // p["block_m"]) * -(-w.N // p["block_n"])
             assert p["grid"] == tiles
         else:
@@ -200,25 +200,46 @@ def rup(x, m):
     return -(-x // m) * m
 
 
+def test_unaligned_path_takes_large_misaligned_problems_in_place():
+    # the ragged workload: rows of A (4100 B) and B (6142 B) misaligned, K % 32
+    # == 2, 17 x 12 tiles: the pipelined kernel in place, no workspace asked for
+    st, p = plan(4099, 3071, 2050)
+    assert st == gr.GR_OK and p["path"] == gr.GR_PATH_TILE_UNALIGNED and p["grid"] == 17 * 12
+    assert (p["block_m"], p["block_n"], p["workspace"]) == (256, 256, 0)
+    assert ws_size(4099, 3071, 2050) == (gr.GR_OK, 0)
+    assert plan_ws(4099, 3071, 2050, 1 << 30)[1]["path"] == gr.GR_PATH_TILE_UNALIGNED
+    # only B misaligned, only A misaligned, aligned rows with K % 32 != 0
+    assert plan(4096, 3071, 2048)[1]["path"] == gr.GR_PATH_TILE_UNALIGNED
+    assert plan(4096, 4096, 4096, a=BASE_A + 2)[1]["path"] == gr.GR_PATH_TILE_UNALIGNED
+    assert plan(4096, 4096, 4100)[1]["path"] == gr.GR_PATH_TILE_UNALIGNED
+    # its limits: one tile in M and N, K > 128, more than 128 tiles
+    assert plan(4096, 255, 4100)[1]["path"] == gr.GR_PATH_TILE_EDGE
+    assert plan(255, 65536, 4100)[1]["path"] == gr.GR_PATH_TILE_EDGE
+    assert plan(4096, 4096, 127)[1]["path"] == gr.GR_PATH_TILE_EDGE
+    assert plan(4096, 4096, 129)[1]["path"] == gr.GR_PATH_TILE_UNALIGNED
+    assert plan(2048, 4096, 4100)[1]["path"] == gr.GR_PATH_TILE_EDGE  # 128 tiles
+    assert plan(2304, 4096, 4100)[1]["path"] == gr.GR_PATH_TILE_UNALIGNED  # 144 tiles
+
+
 def test_workspace_size_and_packed_plan():
-    # the ragged workload: rows of A (4100 B) and B (6142 B) misaligned, K % 32 == 2
-    st, size = ws_size(4099, 3071, 2050)
-    kp = rup(2050, 64)
-    assert st == gr.GR_OK and size == rup(4099 * kp * 2, 256) + kp * rup(3071, 8) * 2
-    st, p = plan_ws(4099, 3071, 2050, size)
+    # 8 x 8 large tiles, too few for the unaligned kernel: the packed copy, K padded to 1024
+    st, size = ws_size(2048, 2048, 1000, lda=1001, ldb=2049)
+    kp = rup(1000, 64)
+    assert st == gr.GR_OK and size == rup(2048 * kp * 2, 256) + kp * rup(2048, 8) * 2
+    st, p = plan_ws(2048, 2048, 1000, size, lda=1001, ldb=2049)
     assert st == gr.GR_OK and p["path"] == gr.GR_PATH_TILE_PACKED and p["packed"] == 3
-    assert p["workspace"] == size and p["grid"] == 17 * 12
+    assert p["workspace"] == size and p["grid"] == 16 * 16  # 128 x 128 tiles (64 large ones are too few)
     # one byte short, or no workspace: the guarded kernel
-    assert plan_ws(4099, 3071, 2050, size - 1)[1]["path"] == gr.GR_PATH_TILE_EDGE
-    assert plan(4099, 3071, 2050)[1]["path"] == gr.GR_PATH_TILE_EDGE
+    assert plan_ws(2048, 2048, 1000, size - 1, lda=1001, ldb=2049)[1]["path"] == gr.GR_PATH_TILE_EDGE
+    assert plan(2048, 2048, 1000, lda=1001, ldb=2049)[1]["path"] == gr.GR_PATH_TILE_EDGE
     # K % 32 == 0 with only B misaligned: only B is copied, K unchanged
-    st, size = ws_size(4096, 3071, 2048)
+    st, size = ws_size(2048, 3071, 2048)
     assert size == 2048 * rup(3071, 8) * 2
-    assert plan_ws(4096, 3071, 2048, size)[1]["packed"] == 2
+    assert plan_ws(2048, 3071, 2048, size)[1]["packed"] == 2
     # only A misaligned
-    st, size = ws_size(4096, 4096, 4096, a=BASE_A + 2)
-    assert size == 4096 * 4096 * 2
-    assert plan_ws(4096, 4096, 4096, size, a=BASE_A + 2)[1]["packed"] == 1
+    st, size = ws_size(2048, 2048, 4096, a=BASE_A + 2)
+    assert size == 2048 * 4096 * 2
+    assert plan_ws(2048, 2048, 4096, size, a=BASE_A + 2)[1]["packed"] == 1
     # aligned K % 64 != 0 (but K % 32 != 0 too): both padded
     st, size = ws_size(1024, 1024, 1000)
     assert size == 1024 * 1024 * 2 + 1024 * 1024 * 2
@@ -372,6 +393,11 @@ def test_planner_invariants_on_random_problems():
         elif p["path"] == gr.GR_PATH_SMALL_M:
             assert 1 <= M <= 64 and K > 0 and p["grid"] == -(-N // 64), key
             assert M <= 16 or -(-N // 64) <= 256, key  # wider C with more rows: the tile kernel
+        elif p["path"] == gr.GR_PATH_TILE_UNALIGNED:
+            assert not (aligned and K % 32 == 0), key
+            assert M >= 256 and N >= 256 and K > 128, key
+            tiles = -(-M // 256) * -(-N // 256)
+            assert tiles > 128 and p["grid"] == tiles and p["block_m"] == 256 and size == 0, key
         else:
             assert p["path"] == gr.GR_PATH_TILE_EDGE, key
             assert not (aligned and K % 32 == 0 and K > 0), key
