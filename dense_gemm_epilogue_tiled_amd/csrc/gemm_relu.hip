@@ -113,35 +113,68 @@ bool smallm_rows_ok(int64_t M, int64_t N, int64_t K, uintptr_t A, int64_t lda, u
     return M >= 1 && M <= kSmallMMaxRows && A % 16 == 0 && lda % 8 == 0 && B % 8 == 0 && ldb % 4 == 0;
 }
 
+// The streaming small-M kernel (gemm_relu_smallm_stream_kernel): M <= 16, K
+// a positive multiple of 32 (whole 32-row slots), 16-byte rows of A, B of
+// any alignment and a pitch within 32-bit copy offsets, N of at least one
+// column block of nb.  Without a split it runs with 64-column blocks; the
+// split uses 128-column blocks (256-byte row pieces, the faster read
+// pattern, measured 6.5 TB/s for the first pass at 8 x 16384 x 8192).
+constexpr int kStreamNB = 64, kStreamW = 8, kStreamR = 4;             // single pass
+constexpr int kStreamSplitNB = 128, kStreamSplitW = 4, kStreamSplitR = 4;  // split first pass
+bool smallm_stream_ok(int64_t M, int64_t N, int64_t K, uintptr_t A, int64_t lda, int64_t ldb, int64_t nb) {
+    return M >= 1 && M <= kSmallMThreshold && K > 0 && K % 32 == 0 && A % 16 == 0 && lda % 8 == 0 && N >= nb &&
+           ldb <= gr::tile2::MAX_LDB;
+}
+
 // Split-K layout of the small-M path: S splits of k_per_split (a multiple of
-// 32, at least two 32-deep steps) over ceil(N / 256) column blocks, about 256
-// workgroups in all, and the fp32 partial sums S x M x N in the workspace.
-// Needs 16-byte rows of B.
+// 32) over ceil(N / NB) column blocks, about 256 workgroups in all, and the
+// fp32 partial sums S x M x N in the workspace.  The streaming kernel
+// (stream = true, NB = 128) splits whenever its column blocks leave CUs
+// idle, with at least four 32-row slots per split; otherwise the
+// register-staged split kernel (NB = 256, 16-byte rows of B) where the
+// single pass has fewer than 256 strips of 64 columns.
 struct SmallMSplit {
     int64_t splits = 0, k_per_split = 0, n_blocks = 0, bytes = 0;
+    bool stream = false;
 };
 constexpr int64_t kSmallMMaxSplits = 64;
 
-// The split pays only where the single-pass kernel (one workgroup per
-// 64-column strip) leaves CUs idle: measured at N = 16384 (256 strips) the
-// split's first pass is 4% faster, and its second pass costs more than that.
+// The register-staged split pays only where the single-pass kernel (one
+// workgroup per 64-column strip) leaves CUs idle: measured at N = 16384 (256
+// strips) its first pass is 4% faster, and its second pass costs more.
 bool smallm_split_pays(int64_t N) { return (N + gr::smallm::NB - 1) / gr::smallm::NB < 256; }
 
 bool smallm_split_layout(int64_t M, int64_t N, int64_t K, uintptr_t A, int64_t lda, uintptr_t B, int64_t ldb,
                          SmallMSplit* sp) {
     using namespace gr::smallm;
-    if (K < 1 || N < 1 || !smallm_ok(M, N, K, A, lda, B, ldb) || B % 16 != 0 || ldb % 8 != 0) return false;
+    if (K < 1 || N < 1) return false;
     SmallMSplit q;
-    q.n_blocks = (N + SPLIT_NB - 1) / SPLIT_NB;
+    int64_t nb, min_steps;
+    if (smallm_stream_ok(M, N, K, A, lda, ldb, kStreamSplitNB)) {
+        q.stream = true;
+        nb = kStreamSplitNB;
+        min_steps = kStreamSplitW;  // one slot per wave
+    } else if (smallm_ok(M, N, K, A, lda, B, ldb) && B % 16 == 0 && ldb % 8 == 0) {
+        nb = SPLIT_NB;
+        min_steps = 2;
+    } else {
+        return false;
+    }
+    q.n_blocks = (N + nb - 1) / nb;
     int64_t S = 256 / q.n_blocks;
     S = S < 1 ? 1 : (S > kSmallMMaxSplits ? kSmallMMaxSplits : S);
     const int64_t ksteps = (K + KSTEP - 1) / KSTEP;
-    if (S > ksteps / 2) S = ksteps / 2 > 0 ? ksteps / 2 : 1;
+    if (S > ksteps / min_steps) S = ksteps / min_steps > 0 ? ksteps / min_steps : 1;
     q.k_per_split = (ksteps + S - 1) / S * KSTEP;
     q.splits = (K + q.k_per_split - 1) / q.k_per_split;  // no empty split
     q.bytes = (q.splits * M * N * 4 + kWorkspaceAlign - 1) / kWorkspaceAlign * kWorkspaceAlign;
     *sp = q;
     return true;
+}
+
+// Whether the planner takes the split (with a big enough workspace).
+bool smallm_split_wanted(int64_t N, const SmallMSplit& sp) {
+    return sp.splits >= 2 && (sp.stream || smallm_split_pays(N));
 }
 
 // Conditions of the pipelined direct-to-LDS kernels: 16-byte aligned rows of
@@ -260,7 +293,7 @@ bool pack_layout(int64_t M, int64_t N, int64_t K, uintptr_t A, int64_t lda, uint
     return true;
 }
 
-void fill_plan(int path, int64_t M, int64_t N, uintptr_t A, int64_t lda, uintptr_t B, int64_t ldb, uintptr_t C,
+void fill_plan(int path, int64_t M, int64_t N, int64_t K, uintptr_t A, int64_t lda, uintptr_t B, int64_t ldb, uintptr_t C,
                int64_t ldc, const Pack& pk, const SmallMSplit& sp, const TileSplit& ts, gr_plan_t* p) {
     std::memset(p, 0, sizeof(*p));
     p->path = path;
@@ -315,27 +348,30 @@ void fill_plan(int path, int64_t M, int64_t N, uintptr_t A, int64_t lda, uintptr
     } else if (path == GR_PATH_SMALL_M_SPLIT) {
         using namespace gr::smallm;
         p->block_m = MAX_M;
-        p->block_n = SPLIT_NB;
+        p->block_n = sp.stream ? kStreamSplitNB : SPLIT_NB;
         p->block_k = KSTEP;
-        p->stages = SPLIT_U;
-        p->threads = SPLIT_THREADS;
+        p->stages = sp.stream ? kStreamSplitR : SPLIT_U;
+        p->threads = sp.stream ? 64 * kStreamSplitW : SPLIT_THREADS;
         p->grid = sp.n_blocks * sp.splits;
         p->vec_a = 8;
-        p->vec_b = 8;
+        p->vec_b = sp.stream ? vec_width(B, ldb) : 8;
         p->vec_c = 1;
         p->group_m = 1;
         p->workspace = sp.bytes;
         p->split_k = (int32_t)sp.splits;
     } else if (path == GR_PATH_SMALL_M) {
         using namespace gr::smallm;
+        // the streaming kernel where it applies (vec_b 8: 16-byte copies of B
+        // from any address), else the register-staged one (vec_b 4)
+        const bool stream = smallm_stream_ok(M, N, K, A, lda, ldb, kStreamNB);
         p->block_m = M <= MAX_M ? MAX_M : (M <= 2 * MAX_M ? 2 * MAX_M : 4 * MAX_M);  // rows per workgroup
-        p->block_n = NB;
+        p->block_n = stream ? kStreamNB : NB;
         p->block_k = KSTEP;
-        p->stages = kSmallMUnroll;
-        p->threads = 64 * kSmallMWaves;
-        p->grid = (N + NB - 1) / NB;
+        p->stages = stream ? kStreamR : kSmallMUnroll;
+        p->threads = 64 * (stream ? kStreamW : kSmallMWaves);
+        p->grid = (N + p->block_n - 1) / p->block_n;
         p->vec_a = 8;
-        p->vec_b = 4;
+        p->vec_b = stream ? 8 : 4;
         p->vec_c = 1;
         p->group_m = 1;
         p->split_k = 1;
@@ -347,9 +383,9 @@ int choose_path(int64_t M, int64_t N, int64_t K, uintptr_t A, int64_t lda, uintp
     (void)C;
     (void)ldc;
     if (M == 0 || N == 0) return GR_PATH_NONE;
-    if (K > 0 && smallm_ok(M, N, K, A, lda, B, ldb)) {
-        if (ws_bytes > 0 && smallm_split_pays(N) && smallm_split_layout(M, N, K, A, lda, B, ldb, sp) &&
-            sp->splits >= 2 && sp->bytes <= ws_bytes)
+    if (K > 0 && (smallm_ok(M, N, K, A, lda, B, ldb) || smallm_stream_ok(M, N, K, A, lda, ldb, kStreamNB))) {
+        if (ws_bytes > 0 && smallm_split_layout(M, N, K, A, lda, B, ldb, sp) && smallm_split_wanted(N, *sp) &&
+            sp->bytes <= ws_bytes)
             return GR_PATH_SMALL_M_SPLIT;
         return GR_PATH_SMALL_M;
     }
@@ -466,6 +502,14 @@ int run(const gr_plan_t& p, int64_t M, int64_t N, int64_t K, const uint16_t* A, 
         case GR_PATH_SMALL_M_SPLIT: {
             using namespace gr::smallm;
             float* part = reinterpret_cast<float*>(ws);
+            if (sp.stream) {
+                const int st = launch(gemm_relu_smallm_stream_kernel<kStreamSplitNB, kStreamSplitW, kStreamSplitR,
+                                                                      true, E>,
+                                      p.grid, p.threads, stream, A, B, C, part, M, N, K, lda, ldb, ldc,
+                                      sp.k_per_split, (uint32_t)sp.n_blocks, ep);
+                if (st != GR_OK) return st;
+                return launch_reduce<E>(part, C, M, N, ldc, sp.splits, p.vec_c, ep, stream);
+            }
             const bool whole = N % SPLIT_NB == 0 && K % KSTEP == 0;
             const uint32_t nb = (uint32_t)sp.n_blocks;
             int st = whole ? launch(gemm_relu_smallm_split_kernel<false, E>, p.grid, SPLIT_THREADS, stream, A, B,
@@ -547,6 +591,12 @@ int run(const gr_plan_t& p, int64_t M, int64_t N, int64_t K, const uint16_t* A, 
             }
         case GR_PATH_SMALL_M: {
             using namespace gr::smallm;
+            if (p.vec_b == 8 && M <= MAX_M) {
+                float* no_part = nullptr;
+                return launch(gemm_relu_smallm_stream_kernel<kStreamNB, kStreamW, kStreamR, false, E>, p.grid,
+                              p.threads, stream, A, B, C, no_part, M, N, K, lda, ldb, ldc, K,
+                              (uint32_t)p.grid, ep);
+            }
             const bool whole = N % NB == 0 && K % KSTEP == 0;
             constexpr int W = kSmallMWaves, U = kSmallMUnroll;
             if (M <= MAX_M) {
@@ -592,7 +642,8 @@ int plan_call(int64_t M, int64_t N, int64_t K, uintptr_t a, int64_t lda, uintptr
         } else if (forced == GR_PATH_TILE_UNALIGNED) {
             if (!tile_unaligned_ok(M, N, K, lda, ldb)) return GR_ERR_INVALID_PATH;
         } else if (forced == GR_PATH_SMALL_M) {
-            if (K == 0 || !smallm_rows_ok(M, N, K, a, lda, b, ldb)) return GR_ERR_INVALID_PATH;
+            if (K == 0 || !(smallm_rows_ok(M, N, K, a, lda, b, ldb) || smallm_stream_ok(M, N, K, a, lda, ldb, kStreamNB)))
+                return GR_ERR_INVALID_PATH;
         } else if (forced == GR_PATH_TILE_PACKED) {
             if (!pack_layout(M, N, K, a, lda, b, ldb, pk) || pk->bytes > ws_bytes) return GR_ERR_INVALID_PATH;
         } else if (forced == GR_PATH_TILE_SPLIT) {
@@ -606,7 +657,7 @@ int plan_call(int64_t M, int64_t N, int64_t K, uintptr_t a, int64_t lda, uintptr
         }
         path = forced;
     }
-    fill_plan(path, M, N, a, lda, b, ldb, c, ldc, *pk, *sp, *ts, p);
+    fill_plan(path, M, N, K, a, lda, b, ldb, c, ldc, *pk, *sp, *ts, p);
     return GR_OK;
 }
 
@@ -738,7 +789,8 @@ void fill_plan_bt(int path, int64_t M, int64_t N, uintptr_t A, int64_t lda, uint
     Pack pk;
     SmallMSplit sp;
     TileSplit ts;
-    fill_plan(path == GR_PATH_SMALL_M ? GR_PATH_NONE : path, M, N, A, lda, Bt, ldbt, C, ldc, pk, sp, ts, p);
+    // K only matters to the row-major small-M plan, which this one replaces
+    fill_plan(path == GR_PATH_SMALL_M ? GR_PATH_NONE : path, M, N, 0, A, lda, Bt, ldbt, C, ldc, pk, sp, ts, p);
     p->path = path;
     if (path == GR_PATH_TILE) {
         p->block_k = gr::tile2::BK;
@@ -1347,9 +1399,8 @@ int gemm_relu_f16_workspace_size(int64_t M, int64_t N, int64_t K, const uint16_t
     Pack pk;
     SmallMSplit sp;
     TileSplit ts;
-    if (smallm_ok(M, N, K, a, lda, b, ldb)) {
-        if (smallm_split_pays(N) && smallm_split_layout(M, N, K, a, lda, b, ldb, &sp) && sp.splits >= 2)
-            *bytes = sp.bytes;
+    if (K > 0 && (smallm_ok(M, N, K, a, lda, b, ldb) || smallm_stream_ok(M, N, K, a, lda, ldb, kStreamNB))) {
+        if (smallm_split_layout(M, N, K, a, lda, b, ldb, &sp) && smallm_split_wanted(N, sp)) *bytes = sp.bytes;
     } else if (tile_fast_ok(M, N, K, a, lda, b, ldb)) {
         if (!use_large_tiles(M, N) && tile_split_layout(M, N, K, false, &ts)) *bytes = ts.bytes;
     } else if (tile_unaligned_ok(M, N, K, lda, ldb) && use_large_tiles(M, N)) {

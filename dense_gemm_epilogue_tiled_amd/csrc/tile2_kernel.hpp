@@ -84,6 +84,17 @@ __device__ __forceinline__ void dma16(const void* base, uint32_t voff, uint32_t 
         : "memory");
 }
 
+// The same copy marked nontemporal (a stream read once: the lines are not
+// kept in the caches for reuse).
+__device__ __forceinline__ void dma16_nt(const void* base, uint32_t voff, uint32_t lds_addr) {
+    asm volatile(
+        "s_nop 0\n\t"
+        "global_load_lds_dwordx4 %0, %1 nt"
+        :
+        : "v"(voff), "s"(base), "{m0}"(lds_addr)
+        : "memory");
+}
+
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
     static_assert(N >= 0 && N < 64, "vmcnt range");

@@ -257,30 +257,41 @@ def test_workspace_not_used_where_it_cannot_help():
 
 
 def test_small_m_split_plan():
-    # N = 4096: the single-pass kernel would run 64 workgroups; the split runs
-    # 16 column blocks of 256 x 16 splits of 512 = 256 workgroups
+    # N = 4096: the single-pass kernel would run 64 workgroups; the streaming
+    # split runs 32 column blocks of 128 x 8 splits of 1024 = 256 workgroups
     st, size = ws_size(8, 4096, 8192)
-    assert st == gr.GR_OK and size == 16 * 8 * 4096 * 4
+    assert st == gr.GR_OK and size == 8 * 8 * 4096 * 4
     st, p = plan_ws(8, 4096, 8192, size)
-    assert p["path"] == gr.GR_PATH_SMALL_M_SPLIT and p["split_k"] == 16 and p["grid"] == 256
-    assert p["workspace"] == size and p["block_n"] == 256
+    assert p["path"] == gr.GR_PATH_SMALL_M_SPLIT and p["split_k"] == 8 and p["grid"] == 256
+    assert p["workspace"] == size and p["block_n"] == 128
     # too small a workspace, or none: the single-pass small-M kernel
     assert plan_ws(8, 4096, 8192, size - 1)[1]["path"] == gr.GR_PATH_SMALL_M
     assert plan(8, 4096, 8192)[1]["path"] == gr.GR_PATH_SMALL_M
-    # 256 strips or more already fill the chip: no workspace asked for
-    assert ws_size(8, 16384, 8192) == (gr.GR_OK, 0)
-    assert plan_ws(8, 16384, 8192, 1 << 30)[1]["path"] == gr.GR_PATH_SMALL_M
-    # B rows only 8-byte aligned: no split
-    assert ws_size(8, 4096, 8192, b=BASE_B + 8) == (gr.GR_OK, 0)
-    assert ws_size(8, 4096, 8192, ldb=4100) == (gr.GR_OK, 0)
+    # the small-M workload: 128 column blocks x 2 splits (256-byte row pieces
+    # over half of K each)
+    st, size = ws_size(8, 16384, 8192)
+    assert size == 2 * 8 * 16384 * 4
+    st, p = plan_ws(8, 16384, 8192, size)
+    assert (p["path"], p["split_k"], p["grid"], p["block_n"]) == (gr.GR_PATH_SMALL_M_SPLIT, 2, 256, 128)
+    # 256 column blocks or more already fill the chip: no workspace asked for
+    assert ws_size(8, 32768, 8192) == (gr.GR_OK, 0)
+    # B needs no alignment on the streaming kernels
+    assert ws_size(8, 4096, 8192, b=BASE_B + 8)[1] == 8 * 8 * 4096 * 4
+    assert ws_size(8, 4096, 8192, ldb=4100)[1] == 8 * 8 * 4096 * 4
+    assert plan(8, 4096, 8192, b=BASE_B + 2)[1]["path"] == gr.GR_PATH_SMALL_M
     # K of fewer than four 32-deep steps is not split
     assert ws_size(8, 4096, 96) == (gr.GR_OK, 0)
-    # one column block: up to 64 splits, each at least two steps deep
+    # K % 32 != 0: the register-staged split (256-column blocks, 16-byte rows
+    # of B), only where its single pass leaves CUs idle
+    st, p = plan_ws(8, 4096, 8200, 1 << 24)
+    assert p["path"] == gr.GR_PATH_SMALL_M_SPLIT and p["block_n"] == 256 and p["grid"] == 256
+    assert ws_size(8, 16384, 8200) == (gr.GR_OK, 0)
+    # two column blocks: up to 32 splits here, each at least four slots deep
     st, p = plan_ws(4, 256, 4096, 1 << 24)
-    assert p["path"] == gr.GR_PATH_SMALL_M_SPLIT and p["split_k"] == 64 and p["grid"] == 64
-    assert p["workspace"] == 64 * 4 * 256 * 4
+    assert p["path"] == gr.GR_PATH_SMALL_M_SPLIT and p["split_k"] == 32 and p["grid"] == 64
+    assert p["workspace"] == 32 * 4 * 256 * 4
     st, p = plan_ws(4, 256, 1024, 1 << 24)
-    assert p["split_k"] == 16
+    assert p["split_k"] == 8
     # forced without a workspace is refused
     assert gr.gemm_relu_f16_forced(8, 16384, 8192, BASE_A, 8192, BASE_B, 16384, BASE_C, 16384, None,
                                    gr.GR_PATH_SMALL_M_SPLIT) == gr.GR_ERR_INVALID_PATH
@@ -410,7 +421,9 @@ def test_planner_invariants_on_random_problems():
                 assert pw["path"] in (gr.GR_PATH_TILE_PACKED, gr.GR_PATH_SMALL_M_SPLIT, gr.GR_PATH_TILE_SPLIT), key
                 assert pw["workspace"] == size, key
             if pw["path"] == gr.GR_PATH_SMALL_M_SPLIT:
-                assert pw["grid"] == -(-N // 256) * pw["split_k"] and pw["workspace"] >= 4 * M * N * pw["split_k"]
+                assert pw["block_n"] in (128, 256), key
+                assert pw["grid"] == -(-N // pw["block_n"]) * pw["split_k"], key
+                assert pw["workspace"] >= 4 * M * N * pw["split_k"], key
             if pw["path"] == gr.GR_PATH_TILE_SPLIT:
                 assert pw["block_m"] == 128 and pw["grid"] == -(-M // 128) * -(-N // 128) * pw["split_k"]
                 assert pw["workspace"] >= 4 * M * N * pw["split_k"], key
