@@ -25,6 +25,10 @@ GR_ERR_UNSUPPORTED_DEVICE = -7
 GR_ERR_LAUNCH = -8
 GR_ERR_INVALID_PATH = -9
 GR_ERR_INVALID_ARG = -10
+GR_ERR_SCRATCH = -11
+
+# bytes of the static scratch behind gemm_relu_f16_noalloc (GR_NOALLOC_SCRATCH_BYTES)
+NOALLOC_SCRATCH_BYTES = 32 << 20
 
 GR_PATH_NONE = 0
 GR_PATH_TILE = 1
@@ -120,6 +124,8 @@ def lib() -> ctypes.CDLL:
             l.gemm_relu_f16_plan_ws.argtypes = [i64, i64, i64, p, i64, p, i64, p, i64, i64,
                                                 ctypes.POINTER(gr_plan_t)]
             l.gemm_relu_f16_plan_ws.restype = i32
+            l.gemm_relu_f16_noalloc.argtypes = [i64, i64, i64, p, i64, p, i64, p, i64, p]
+            l.gemm_relu_f16_noalloc.restype = i32
             l.gemm_relu_f16_bt.argtypes = [i64, i64, i64, p, i64, p, i64, p, i64, p]
             l.gemm_relu_f16_bt.restype = i32
             l.gemm_relu_f16_bt_forced.argtypes = [i64, i64, i64, p, i64, p, i64, p, i64, p, i32]
@@ -185,6 +191,13 @@ def _ptr(x) -> int:
 def gemm_relu_f16(M, N, K, A, lda, B, ldb, C, ldc, stream=None) -> int:
     """C := ReLU(A.B) on device pointers (ints); returns the C status code."""
     return lib().gemm_relu_f16(M, N, K, _ptr(A), lda, _ptr(B), ldb, _ptr(C), ldc, _ptr(stream))
+
+
+def gemm_relu_f16_noalloc(M, N, K, A, lda, B, ldb, C, ldc, stream=None) -> int:
+    """As gemm_relu_f16_ws with the library's static scratch as the workspace
+    (no allocation; overlapping calls on one GPU race); returns the status code
+    (GR_ERR_SCRATCH when the problem needs more scratch than there is)."""
+    return lib().gemm_relu_f16_noalloc(M, N, K, _ptr(A), lda, _ptr(B), ldb, _ptr(C), ldc, _ptr(stream))
 
 
 def gemm_relu_f16_forced(M, N, K, A, lda, B, ldb, C, ldc, stream=None, path=GR_PATH_TILE_EDGE) -> int:

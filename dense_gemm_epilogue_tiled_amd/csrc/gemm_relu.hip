@@ -11,6 +11,7 @@
 #include <atomic>
 #include <cstdint>
 #include <cstring>
+#include <mutex>
 
 #include "../../include/gemm_relu.h"
 #include "fp8_kernel.hpp"
@@ -21,6 +22,13 @@
 #include "tile3_kernel.hpp"
 #include "tile3t_kernel.hpp"
 #include "tile_kernel.hpp"
+
+// Scratch of gemm_relu_f16_noalloc: a static device array, one copy per GPU
+// the library runs on.  Host code never uses this name as an address (on the
+// host it is only a stand-in for the symbol); the device address of each
+// GPU's copy comes from hipGetSymbolAddress, looked up once per device with
+// that device current (scratch_on_current_device below).
+static __device__ __align__(256) uint8_t scratch[GR_NOALLOC_SCRATCH_BYTES];
 
 namespace {
 
@@ -421,6 +429,30 @@ int check_device() {
         g_device_state[dev].store(state, std::memory_order_release);
     }
     return state == 1 ? GR_OK : GR_ERR_UNSUPPORTED_DEVICE;
+}
+
+// Device address of the current device's copy of `scratch`, looked up once
+// per device (thread-safe) and kept for later calls.
+std::atomic<uintptr_t> g_scratch_ptr[kMaxDevices];
+std::mutex g_scratch_mutex;
+
+int scratch_on_current_device(uint8_t** out) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0) return GR_ERR_NO_DEVICE;
+    if (dev >= kMaxDevices) return GR_ERR_UNSUPPORTED_DEVICE;
+    uintptr_t p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+    if (p == 0) {
+        std::lock_guard<std::mutex> lock(g_scratch_mutex);
+        p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+        if (p == 0) {
+            void* q = nullptr;
+            if (hipGetSymbolAddress(&q, HIP_SYMBOL(scratch)) != hipSuccess || q == nullptr) return GR_ERR_LAUNCH;
+            p = reinterpret_cast<uintptr_t>(q);
+            g_scratch_ptr[dev].store(p, std::memory_order_release);
+        }
+    }
+    *out = reinterpret_cast<uint8_t*>(p);
+    return GR_OK;
 }
 
 // ---- launches ----------------------------------------------------------------
@@ -1549,6 +1581,21 @@ int gemm_mxfp4_bt_plan(int64_t M, int64_t N, int64_t K, const uint8_t* A, int64_
                         (uintptr_t)scale_b, ld_sb, (uintptr_t)bias, act, (uintptr_t)C, ldc, out_fmt, 4, -1, out);
 }
 
+int gemm_relu_f16_noalloc(int64_t M, int64_t N, int64_t K, const uint16_t* A, int64_t lda, const uint16_t* B,
+                          int64_t ldb, uint16_t* C, int64_t ldc, void* stream) {
+    int64_t need = 0;
+    int st = gemm_relu_f16_workspace_size(M, N, K, A, lda, B, ldb, C, ldc, &need);
+    if (st != GR_OK) return st;
+    if (need > GR_NOALLOC_SCRATCH_BYTES) return GR_ERR_SCRATCH;
+    if (need == 0) return entry(M, N, K, A, lda, B, ldb, C, ldc, nullptr, 0, stream, -1);
+    st = check_device();
+    if (st != GR_OK) return st;
+    uint8_t* ws = nullptr;
+    st = scratch_on_current_device(&ws);
+    if (st != GR_OK) return st;
+    return entry(M, N, K, A, lda, B, ldb, C, ldc, ws, need, stream, -1);
+}
+
 const char* gemm_relu_status_string(int status) {
     switch (status) {
         case GR_OK: return "GR_OK";
@@ -1562,6 +1609,7 @@ const char* gemm_relu_status_string(int status) {
         case GR_ERR_LAUNCH: return "GR_ERR_LAUNCH";
         case GR_ERR_INVALID_PATH: return "GR_ERR_INVALID_PATH";
         case GR_ERR_INVALID_ARG: return "GR_ERR_INVALID_ARG";
+        case GR_ERR_SCRATCH: return "GR_ERR_SCRATCH";
         default: return "GR_ERR_UNKNOWN";
     }
 }

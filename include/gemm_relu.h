@@ -82,6 +82,8 @@ extern "C" {
 #define GR_ERR_LAUNCH               -8 /* the kernel launch was rejected by the runtime    */
 #define GR_ERR_INVALID_PATH         -9 /* forced path unknown or not applicable            */
 #define GR_ERR_INVALID_ARG         -10 /* a NULL output struct or other bad argument        */
+#define GR_ERR_SCRATCH             -11 /* gemm_relu_f16_noalloc: the problem needs more      */
+                                       /* scratch than the library's static buffer holds   */
 
 /* ---- element formats (fmt / out_fmt arguments) ----------------------------- */
 #define GR_FMT_F16         0 /* IEEE binary16                                        */
@@ -668,6 +670,31 @@ int gemm_mxfp4_bt_plan(int64_t M, int64_t N, int64_t K,
                        const uint16_t* bias, int act,
                        const uint16_t* C, int64_t ldc, int out_fmt,
                        gr_plan_t* out);
+
+/*
+ * gemm_relu_f16_noalloc -- gemm_relu_f16_ws without a caller workspace and
+ * without any allocation: for callers that cannot allocate device memory
+ * (code being captured into a HIP graph, tight serving loops, harnesses that
+ * forbid hipMalloc).  Same arguments, result and paths as gemm_relu_f16_ws
+ * with a workspace of the size gemm_relu_f16_workspace_size reports; the
+ * workspace is a static device array of the library, GR_NOALLOC_SCRATCH_BYTES
+ * bytes, one per GPU, held from the library's first use of that GPU until
+ * the process ends.  Problems whose workspace would exceed it are refused
+ * with GR_ERR_SCRATCH before anything is launched (pure check, no HIP call);
+ * problems that need no workspace run the in-place paths and do not touch
+ * it.  Calls no hipMalloc, hipFree or allocating library routine.
+ * Every call on one GPU shares that GPU's array: two calls that overlap in
+ * time on one GPU (on different streams, or from different threads) race
+ * and give undefined results; calls ordered on one stream are safe.  The
+ * paths that use it overwrite what they read within the call (nothing in it
+ * has to start at zero).
+ */
+#define GR_NOALLOC_SCRATCH_BYTES (32ll << 20)
+int gemm_relu_f16_noalloc(int64_t M, int64_t N, int64_t K,
+                          const uint16_t* A, int64_t lda,
+                          const uint16_t* B, int64_t ldb,
+                          uint16_t* C, int64_t ldc,
+                          void* stream);
 
 /* Static, NUL-terminated name of a status code ("GR_OK", "GR_ERR_ALIAS", ...),
  * so that a refused call can be reported with its cause (the fail-loudly

@@ -750,3 +750,20 @@ def test_no_kernel_spills_to_scratch():
     for n, s in hot.items():
         limit = 0 if ("smallm" in n or "tile128" in n) else 16
         assert s <= limit, (n, s)
+
+
+def test_noalloc_refuses_problems_beyond_its_scratch():
+    """gemm_relu_f16_noalloc checks its arguments and the scratch the problem
+    needs before any HIP call: bad arguments keep their codes, a workspace
+    need above the static scratch is GR_ERR_SCRATCH (no GPU needed)."""
+    M, N, K = 2048, 2048, 8001
+    lda = K + 1  # K % 32 != 0 and too few tiles for the in-place kernel: both operands copied
+    st, need = gr.gemm_relu_f16_workspace_size(M, N, K, BASE_A, lda, BASE_B, N, BASE_C, N)
+    assert st == gr.GR_OK and need > gr.NOALLOC_SCRATCH_BYTES
+    assert gr.gemm_relu_f16_noalloc(M, N, K, BASE_A, lda, BASE_B, N, BASE_C, N) == gr.GR_ERR_SCRATCH
+    assert gr.gemm_relu_status_string(gr.GR_ERR_SCRATCH) == "GR_ERR_SCRATCH"
+    assert gr.gemm_relu_f16_noalloc(-1, N, K, BASE_A, lda, BASE_B, N, BASE_C, N) == gr.GR_ERR_INVALID_DIM
+    assert gr.gemm_relu_f16_noalloc(M, N, K, BASE_A, K - 1, BASE_B, N, BASE_C, N) == gr.GR_ERR_INVALID_LD
+    assert gr.gemm_relu_f16_noalloc(M, N, K, 0, lda, BASE_B, N, BASE_C, N) == gr.GR_ERR_NULL_PTR
+    # an empty problem launches nothing and succeeds anywhere
+    assert gr.gemm_relu_f16_noalloc(0, N, K, BASE_A, lda, BASE_B, N, BASE_C, N) == gr.GR_OK
