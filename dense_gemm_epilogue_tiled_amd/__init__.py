@@ -124,6 +124,16 @@ def lib() -> ctypes.CDLL:
             l.gemm_relu_f16_plan_ws.argtypes = [i64, i64, i64, p, i64, p, i64, p, i64, i64,
                                                 ctypes.POINTER(gr_plan_t)]
             l.gemm_relu_f16_plan_ws.restype = i32
+            l.gemm_relu_f16_ta.argtypes = [i64, i64, i64, p, i64, p, i64, p, i64, p]
+            l.gemm_relu_f16_ta.restype = i32
+            l.gemm_relu_f16_ta_forced.argtypes = [i64, i64, i64, p, i64, p, i64, p, i64, p, i32]
+            l.gemm_relu_f16_ta_forced.restype = i32
+            l.gemm_relu_f16_ta_plan.argtypes = [i64, i64, i64, p, i64, p, i64, p, i64, ctypes.POINTER(gr_plan_t)]
+            l.gemm_relu_f16_ta_plan.restype = i32
+            l.gemm_relu_f16_forced_order.argtypes = [i64, i64, i64, p, i64, p, i64, p, i64, p, i32, i32, i32]
+            l.gemm_relu_f16_forced_order.restype = i32
+            l.gemm_relu_stream_read.argtypes = [p, i64, p, p]
+            l.gemm_relu_stream_read.restype = i32
             l.gemm_relu_f16_noalloc.argtypes = [i64, i64, i64, p, i64, p, i64, p, i64, p]
             l.gemm_relu_f16_noalloc.restype = i32
             l.gemm_relu_f16_bt.argtypes = [i64, i64, i64, p, i64, p, i64, p, i64, p]
@@ -191,6 +201,33 @@ def _ptr(x) -> int:
 def gemm_relu_f16(M, N, K, A, lda, B, ldb, C, ldc, stream=None) -> int:
     """C := ReLU(A.B) on device pointers (ints); returns the C status code."""
     return lib().gemm_relu_f16(M, N, K, _ptr(A), lda, _ptr(B), ldb, _ptr(C), ldc, _ptr(stream))
+
+
+def gemm_relu_f16_ta(M, N, K, At, ldat, B, ldb, C, ldc, stream=None) -> int:
+    """C := ReLU(At^T B) with A given transposed (At, K x M row-major); returns the status code."""
+    return lib().gemm_relu_f16_ta(M, N, K, _ptr(At), ldat, _ptr(B), ldb, _ptr(C), ldc, _ptr(stream))
+
+
+def gemm_relu_f16_ta_forced(M, N, K, At, ldat, B, ldb, C, ldc, stream=None, path=GR_PATH_TILE_EDGE) -> int:
+    return lib().gemm_relu_f16_ta_forced(M, N, K, _ptr(At), ldat, _ptr(B), ldb, _ptr(C), ldc, _ptr(stream), path)
+
+
+def gemm_relu_f16_ta_plan(M, N, K, At, ldat, B, ldb, C, ldc):
+    plan = gr_plan_t()
+    st = lib().gemm_relu_f16_ta_plan(M, N, K, _ptr(At), ldat, _ptr(B), ldb, _ptr(C), ldc, ctypes.byref(plan))
+    return st, _plan_dict(plan)
+
+
+def gemm_relu_f16_forced_order(M, N, K, A, lda, B, ldb, C, ldc, stream=None, path=GR_PATH_TILE, group_m=4,
+                               xcd_remap=1) -> int:
+    """gemm_relu_f16_forced with a chosen workgroup order (test hook)."""
+    return lib().gemm_relu_f16_forced_order(M, N, K, _ptr(A), lda, _ptr(B), ldb, _ptr(C), ldc, _ptr(stream), path,
+                                            group_m, xcd_remap)
+
+
+def gemm_relu_stream_read(src, nbytes, sink, stream=None) -> int:
+    """Read nbytes (a multiple of 8 MiB) of device memory once: the HBM read-ceiling probe."""
+    return lib().gemm_relu_stream_read(_ptr(src), nbytes, _ptr(sink), _ptr(stream))
 
 
 def gemm_relu_f16_noalloc(M, N, K, A, lda, B, ldb, C, ldc, stream=None) -> int:

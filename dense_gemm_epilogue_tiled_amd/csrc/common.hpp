@@ -247,14 +247,18 @@ __device__ __forceinline__ uint16_t epi_value(float acc, int64_t n, int64_t N, c
 //     same panels from L2 (the grid-level swizzle of the TileLang tutorial,
 //     chapter "Layout and bank conflicts").
 // Both steps are bijections on [0, tiles_m * tiles_n): they change only when
-// a tile runs, never what it computes.
+// a tile runs, never what it computes.  group_m with kNoXcdRemap set skips
+// step 1 (logical id = workgroup id): a test hook that checks exactly that.
+constexpr uint32_t kNoXcdRemap = 0x80000000u;
 __device__ __forceinline__ void tile_of_workgroup(uint32_t wg, uint32_t n_wg, uint32_t tiles_m,
                                                   uint32_t tiles_n, uint32_t group_m,
                                                   uint32_t& tm, uint32_t& tn) {
     const uint32_t kXcds = 8;
+    const bool remap = (group_m & kNoXcdRemap) == 0;
+    group_m &= ~kNoXcdRemap;
     uint32_t x = wg % kXcds, s = wg / kXcds;
     uint32_t q = n_wg / kXcds, r = n_wg % kXcds;
-    uint32_t lid = x * q + (x < r ? x : r) + s;
+    uint32_t lid = remap ? x * q + (x < r ? x : r) + s : wg;
     uint32_t per_group = group_m * tiles_n;
     uint32_t g = lid / per_group;
     uint32_t first_m = g * group_m;

@@ -16,6 +16,7 @@
 #include "../../include/gemm_relu.h"
 #include "fp8_kernel.hpp"
 #include "pack_kernel.hpp"
+#include "probe_kernel.hpp"
 #include "smallm_kernel.hpp"
 #include "tile2_kernel.hpp"
 #include "tile128_kernel.hpp"
@@ -127,8 +128,8 @@ bool smallm_rows_ok(int64_t M, int64_t N, int64_t K, uintptr_t A, int64_t lda, u
 // column block of nb.  Without a split it runs with 64-column blocks; the
 // split uses 128-column blocks (256-byte row pieces, the faster read
 // pattern, measured 6.5 TB/s for the first pass at 8 x 16384 x 8192).
-constexpr int kStreamNB = 64, kStreamW = 8, kStreamR = 4;             // single pass
-constexpr int kStreamSplitNB = 128, kStreamSplitW = 4, kStreamSplitR = 4;  // split first pass
+constexpr int kStreamNB = 64, kStreamW = 8;         // single pass: 64-column blocks, 8 waves
+constexpr int kStreamSplitNB = 128, kStreamSplitW = 4;  // split first pass: 128-column blocks, 4 waves
 bool smallm_stream_ok(int64_t M, int64_t N, int64_t K, uintptr_t A, int64_t lda, int64_t ldb, int64_t nb) {
     return M >= 1 && M <= kSmallMThreshold && K > 0 && K % 32 == 0 && A % 16 == 0 && lda % 8 == 0 && N >= nb &&
            ldb <= gr::tile2::MAX_LDB;
@@ -358,7 +359,7 @@ void fill_plan(int path, int64_t M, int64_t N, int64_t K, uintptr_t A, int64_t l
         p->block_m = MAX_M;
         p->block_n = sp.stream ? kStreamSplitNB : SPLIT_NB;
         p->block_k = KSTEP;
-        p->stages = sp.stream ? kStreamSplitR : SPLIT_U;
+        p->stages = sp.stream ? 1 : SPLIT_U;
         p->threads = sp.stream ? 64 * kStreamSplitW : SPLIT_THREADS;
         p->grid = sp.n_blocks * sp.splits;
         p->vec_a = 8;
@@ -375,7 +376,7 @@ void fill_plan(int path, int64_t M, int64_t N, int64_t K, uintptr_t A, int64_t l
         p->block_m = M <= MAX_M ? MAX_M : (M <= 2 * MAX_M ? 2 * MAX_M : 4 * MAX_M);  // rows per workgroup
         p->block_n = stream ? kStreamNB : NB;
         p->block_k = KSTEP;
-        p->stages = stream ? kStreamR : kSmallMUnroll;
+        p->stages = stream ? 1 : kSmallMUnroll;
         p->threads = 64 * (stream ? kStreamW : kSmallMWaves);
         p->grid = (N + p->block_n - 1) / p->block_n;
         p->vec_a = 8;
@@ -535,8 +536,7 @@ int run(const gr_plan_t& p, int64_t M, int64_t N, int64_t K, const uint16_t* A, 
             using namespace gr::smallm;
             float* part = reinterpret_cast<float*>(ws);
             if (sp.stream) {
-                const int st = launch(gemm_relu_smallm_stream_kernel<kStreamSplitNB, kStreamSplitW, kStreamSplitR,
-                                                                      true, E>,
+                const int st = launch(gemm_relu_smallm_stream_kernel<kStreamSplitNB, kStreamSplitW, true, E>,
                                       p.grid, p.threads, stream, A, B, C, part, M, N, K, lda, ldb, ldc,
                                       sp.k_per_split, (uint32_t)sp.n_blocks, ep);
                 if (st != GR_OK) return st;
@@ -625,7 +625,7 @@ int run(const gr_plan_t& p, int64_t M, int64_t N, int64_t K, const uint16_t* A, 
             using namespace gr::smallm;
             if (p.vec_b == 8 && M <= MAX_M) {
                 float* no_part = nullptr;
-                return launch(gemm_relu_smallm_stream_kernel<kStreamNB, kStreamW, kStreamR, false, E>, p.grid,
+                return launch(gemm_relu_smallm_stream_kernel<kStreamNB, kStreamW, false, E>, p.grid,
                               p.threads, stream, A, B, C, no_part, M, N, K, lda, ldb, ldc, K,
                               (uint32_t)p.grid, ep);
             }
@@ -701,8 +701,11 @@ static_assert(GR_ACT_NONE == gr::kActNone && GR_ACT_RELU == gr::kActRelu && GR_A
 // Epilogue arguments of the fused-ReLU calls (their kernels ignore them).
 const gr::EpiArgs kReluOnly{nullptr, gr::kActRelu, 1.0f};
 
+// order: -1 keeps the planner's workgroup order; otherwise bits 0-30 are the
+// group of tile rows (>= 1) and bit 31 turns the XCD renumbering off (the
+// test hook gemm_relu_f16_forced_order).
 int entry(int64_t M, int64_t N, int64_t K, const uint16_t* A, int64_t lda, const uint16_t* B, int64_t ldb,
-          uint16_t* C, int64_t ldc, void* ws, int64_t ws_bytes, void* stream, int forced) {
+          uint16_t* C, int64_t ldc, void* ws, int64_t ws_bytes, void* stream, int forced, int64_t order = -1) {
     Pack pk;
     SmallMSplit sp;
     TileSplit ts;
@@ -710,6 +713,7 @@ int entry(int64_t M, int64_t N, int64_t K, const uint16_t* A, int64_t lda, const
     int st = plan_call(M, N, K, (uintptr_t)A, lda, (uintptr_t)B, ldb, (uintptr_t)C, ldc, (uintptr_t)ws, ws_bytes,
                        true, forced, &pk, &sp, &ts, &p);
     if (st != GR_OK) return st;
+    if (order >= 0) p.group_m = (int32_t)(uint32_t)order;
     if (p.path == GR_PATH_NONE) return GR_OK;
     st = check_device();
     if (st != GR_OK) return st;
@@ -974,6 +978,168 @@ int entry_bt_epi(int64_t M, int64_t N, int64_t K, const uint16_t* A, int64_t lda
     if (st != GR_OK) return st;
     return run_bt<gr::Epi<Base>>(p, M, N, K, A, lda, Bt, ldbt, C, ldc, gr::EpiArgs{bias, act, 1.0f},
                                  static_cast<hipStream_t>(stream));
+}
+
+// ---- A given transposed (At, K x M) --------------------------------------------
+
+// Argument checks for the transposed-A call: At is K x M with pitch ldat >=
+// max(1, M); otherwise as validate().
+int validate_ta(int64_t M, int64_t N, int64_t K, uintptr_t At, int64_t ldat, uintptr_t B, int64_t ldb,
+                uintptr_t C, int64_t ldc) {
+    if (M < 0 || N < 0 || K < 0) return GR_ERR_INVALID_DIM;
+    if (M > kMaxDim || N > kMaxDim || K > kMaxDim) return GR_ERR_TOO_LARGE;
+    const int64_t mmin = M > 1 ? M : 1, nmin = N > 1 ? N : 1;
+    if (ldat < mmin || ldb < nmin || ldc < nmin) return GR_ERR_INVALID_LD;
+    const bool used = M > 0 && N > 0 && K > 0;
+    const bool c_used = M > 0 && N > 0;
+    if ((used && (!At || !B)) || (c_used && !C)) return GR_ERR_NULL_PTR;
+    const int64_t sa = used ? span_bytes(K, M, ldat) : 0;
+    const int64_t sb = used ? span_bytes(K, N, ldb) : 0;
+    const int64_t sc = c_used ? span_bytes(M, N, ldc) : 0;
+    if (sa < 0 || sb < 0 || sc < 0) return GR_ERR_TOO_LARGE;
+    if (overlaps(C, sc, At, sa) || overlaps(C, sc, B, sb)) return GR_ERR_ALIAS;
+    return GR_OK;
+}
+
+// The streaming small-M kernel with At: M <= 16, K % 32 == 0, N of at least
+// one 64-column block, B of any alignment, pitches within 32-bit offsets.
+bool smallm_ta_ok(int64_t M, int64_t N, int64_t K, int64_t ldb) {
+    return M >= 1 && M <= kSmallMThreshold && K > 0 && K % 32 == 0 && N >= kStreamNB && ldb <= gr::tile2::MAX_LDB;
+}
+
+// The 32-deep pipelined kernel with At staged like B: 16-byte rows of At and
+// B, K a positive multiple of 32, M >= 256 (the last tile row moves up to end
+// at M, so no copy reads a column of At past M), pitches within its 32-bit
+// copy offsets (32 rows of At or B per strip).
+bool tile_ta_ok(int64_t M, int64_t N, int64_t K, uintptr_t At, int64_t ldat, uintptr_t B, int64_t ldb) {
+    using namespace gr::tile2;
+    return M >= BM && N >= 1 && K > 0 && K % BK == 0 && vec_width(At, ldat) == 8 && vec_width(B, ldb) == 8 &&
+           ldat <= MAX_LDB && ldb <= MAX_LDB;
+}
+
+int choose_path_ta(int64_t M, int64_t N, int64_t K, uintptr_t At, int64_t ldat, uintptr_t B, int64_t ldb) {
+    if (M == 0 || N == 0) return GR_PATH_NONE;
+    if (smallm_ta_ok(M, N, K, ldb)) return GR_PATH_SMALL_M;
+    if (tile_ta_ok(M, N, K, At, ldat, B, ldb)) return GR_PATH_TILE;
+    return GR_PATH_TILE_EDGE;
+}
+
+void fill_plan_ta(int path, int64_t M, int64_t N, int64_t K, uintptr_t At, int64_t ldat, uintptr_t B, int64_t ldb,
+                  uintptr_t C, int64_t ldc, gr_plan_t* p) {
+    Pack pk;
+    SmallMSplit sp;
+    TileSplit ts;
+    std::memset(p, 0, sizeof(*p));
+    if (path == GR_PATH_TILE) {
+        using namespace gr::tile2;
+        p->block_m = BM;
+        p->block_n = BN;
+        p->block_k = BK;
+        p->stages = STAGES;
+        p->threads = THREADS;
+        p->grid = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
+        p->vec_a = 8;
+        p->vec_b = 8;
+        p->vec_c = vec_width_c(C, ldc);
+        p->group_m = kGroupM;
+        p->split_k = 1;
+    } else if (path == GR_PATH_SMALL_M) {
+        using namespace gr::smallm;
+        p->block_m = MAX_M;
+        p->block_n = kStreamNB;
+        p->block_k = KSTEP;
+        p->stages = 1;
+        p->threads = 64 * kStreamW;
+        p->grid = (N + kStreamNB - 1) / kStreamNB;
+        p->vec_a = 1;
+        p->vec_b = 8;
+        p->vec_c = 1;
+        p->group_m = 1;
+        p->split_k = 1;
+    } else if (path == GR_PATH_TILE_EDGE) {
+        fill_plan(path, M, N, K, At, ldat, B, ldb, C, ldc, pk, sp, ts, p);
+    }
+    p->path = path;
+}
+
+template <int VA, int VB>
+int launch_tile_ta(const gr_plan_t& p, int64_t M, int64_t N, int64_t K, const uint16_t* At, int64_t ldat,
+                   const uint16_t* B, int64_t ldb, uint16_t* C, int64_t ldc, hipStream_t stream) {
+    using namespace gr::tile;
+    const uint32_t tiles_m = (uint32_t)((M + BM - 1) / BM);
+    const uint32_t tiles_n = (uint32_t)((N + BN - 1) / BN);
+    return launch(gemm_relu_tile_kernel<true, VA, VB, false, gr::ElemF16, true>, p.grid, THREADS, stream, At, B, C,
+                  M, N, K, ldat, ldb, ldc, tiles_m, tiles_n, (uint32_t)p.group_m, (int)p.vec_c, kReluOnly);
+}
+
+int run_ta(const gr_plan_t& p, int64_t M, int64_t N, int64_t K, const uint16_t* At, int64_t ldat, const uint16_t* B,
+           int64_t ldb, uint16_t* C, int64_t ldc, hipStream_t stream) {
+    using E = gr::ElemF16;
+    switch (p.path) {
+        case GR_PATH_NONE: return GR_OK;
+        case GR_PATH_SMALL_M: {
+            float* no_part = nullptr;
+            return launch(gr::smallm::gemm_relu_smallm_stream_kernel<kStreamNB, kStreamW, false, E, true>,
+                          p.grid, p.threads, stream, At, B, C, no_part, M, N, K, ldat, ldb, ldc, K, (uint32_t)p.grid,
+                          kReluOnly);
+        }
+        case GR_PATH_TILE: {
+            using namespace gr::tile2;
+            const bool whole = tile_whole(M, N, BM, BN);
+            const uint32_t tiles_m = (uint32_t)((M + BM - 1) / BM);
+            const uint32_t tiles_n = (uint32_t)((N + BN - 1) / BN);
+            const uint32_t gm = (uint32_t)p.group_m;
+            const int vc = p.vec_c;
+            if (whole)
+                return launch(gemm_relu_tile2_kernel<false, false, E, true>, p.grid, THREADS, stream, At, B, C, M, N,
+                              K, ldat, ldb, ldc, tiles_m, tiles_n, gm, vc, kReluOnly);
+            return launch(gemm_relu_tile2_kernel<true, false, E, true>, p.grid, THREADS, stream, At, B, C, M, N, K,
+                          ldat, ldb, ldc, tiles_m, tiles_n, gm, vc, kReluOnly);
+        }
+        case GR_PATH_TILE_EDGE: {
+            const int va = p.vec_a, vb = p.vec_b;
+            if (va == 8 && vb == 8) return launch_tile_ta<8, 8>(p, M, N, K, At, ldat, B, ldb, C, ldc, stream);
+            if (va == 8 && vb == 2) return launch_tile_ta<8, 2>(p, M, N, K, At, ldat, B, ldb, C, ldc, stream);
+            if (va == 8) return launch_tile_ta<8, 1>(p, M, N, K, At, ldat, B, ldb, C, ldc, stream);
+            if (va == 2 && vb == 8) return launch_tile_ta<2, 8>(p, M, N, K, At, ldat, B, ldb, C, ldc, stream);
+            if (va == 2 && vb == 2) return launch_tile_ta<2, 2>(p, M, N, K, At, ldat, B, ldb, C, ldc, stream);
+            if (va == 2) return launch_tile_ta<2, 1>(p, M, N, K, At, ldat, B, ldb, C, ldc, stream);
+            if (vb == 8) return launch_tile_ta<1, 8>(p, M, N, K, At, ldat, B, ldb, C, ldc, stream);
+            if (vb == 2) return launch_tile_ta<1, 2>(p, M, N, K, At, ldat, B, ldb, C, ldc, stream);
+            return launch_tile_ta<1, 1>(p, M, N, K, At, ldat, B, ldb, C, ldc, stream);
+        }
+        default: return GR_ERR_INVALID_PATH;
+    }
+}
+
+int plan_call_ta(int64_t M, int64_t N, int64_t K, uintptr_t at, int64_t ldat, uintptr_t b, int64_t ldb, uintptr_t c,
+                 int64_t ldc, int forced, gr_plan_t* p) {
+    int st = validate_ta(M, N, K, at, ldat, b, ldb, c, ldc);
+    if (st != GR_OK) return st;
+    int path = choose_path_ta(M, N, K, at, ldat, b, ldb);
+    if (forced >= 0 && path != GR_PATH_NONE) {
+        if (forced == GR_PATH_TILE) {
+            if (!tile_ta_ok(M, N, K, at, ldat, b, ldb)) return GR_ERR_INVALID_PATH;
+        } else if (forced == GR_PATH_SMALL_M) {
+            if (!smallm_ta_ok(M, N, K, ldb)) return GR_ERR_INVALID_PATH;
+        } else if (forced != GR_PATH_TILE_EDGE) {
+            return GR_ERR_INVALID_PATH;
+        }
+        path = forced;
+    }
+    fill_plan_ta(path, M, N, K, at, ldat, b, ldb, c, ldc, p);
+    return GR_OK;
+}
+
+int entry_ta(int64_t M, int64_t N, int64_t K, const uint16_t* At, int64_t ldat, const uint16_t* B, int64_t ldb,
+             uint16_t* C, int64_t ldc, void* stream, int forced) {
+    gr_plan_t p;
+    int st = plan_call_ta(M, N, K, (uintptr_t)At, ldat, (uintptr_t)B, ldb, (uintptr_t)C, ldc, forced, &p);
+    if (st != GR_OK) return st;
+    if (p.path == GR_PATH_NONE) return GR_OK;
+    st = check_device();
+    if (st != GR_OK) return st;
+    return run_ta(p, M, N, K, At, ldat, B, ldb, C, ldc, static_cast<hipStream_t>(stream));
 }
 
 // ---- fp8 (e4m3) operands, B given transposed -----------------------------------
@@ -1581,6 +1747,32 @@ int gemm_mxfp4_bt_plan(int64_t M, int64_t N, int64_t K, const uint8_t* A, int64_
                         (uintptr_t)scale_b, ld_sb, (uintptr_t)bias, act, (uintptr_t)C, ldc, out_fmt, 4, -1, out);
 }
 
+int gemm_relu_f16_ta(int64_t M, int64_t N, int64_t K, const uint16_t* At, int64_t ldat, const uint16_t* B,
+                     int64_t ldb, uint16_t* C, int64_t ldc, void* stream) {
+    return entry_ta(M, N, K, At, ldat, B, ldb, C, ldc, stream, -1);
+}
+
+int gemm_relu_f16_ta_forced(int64_t M, int64_t N, int64_t K, const uint16_t* At, int64_t ldat, const uint16_t* B,
+                            int64_t ldb, uint16_t* C, int64_t ldc, void* stream, int path) {
+    if (path != GR_PATH_TILE && path != GR_PATH_TILE_EDGE && path != GR_PATH_SMALL_M) return GR_ERR_INVALID_PATH;
+    return entry_ta(M, N, K, At, ldat, B, ldb, C, ldc, stream, path);
+}
+
+int gemm_relu_f16_ta_plan(int64_t M, int64_t N, int64_t K, const uint16_t* At, int64_t ldat, const uint16_t* B,
+                          int64_t ldb, const uint16_t* C, int64_t ldc, gr_plan_t* out) {
+    if (!out) return GR_ERR_INVALID_ARG;
+    return plan_call_ta(M, N, K, (uintptr_t)At, ldat, (uintptr_t)B, ldb, (uintptr_t)C, ldc, -1, out);
+}
+
+int gemm_relu_f16_forced_order(int64_t M, int64_t N, int64_t K, const uint16_t* A, int64_t lda, const uint16_t* B,
+                               int64_t ldb, uint16_t* C, int64_t ldc, void* stream, int path, int group_m,
+                               int xcd_remap) {
+    if (!known_path(path) || needs_workspace(path)) return GR_ERR_INVALID_PATH;
+    if (group_m < 1 || (xcd_remap != 0 && xcd_remap != 1)) return GR_ERR_INVALID_ARG;
+    const int64_t order = (int64_t)(uint32_t)group_m | (xcd_remap ? 0 : (int64_t)gr::kNoXcdRemap);
+    return entry(M, N, K, A, lda, B, ldb, C, ldc, nullptr, 0, stream, path, order);
+}
+
 int gemm_relu_f16_noalloc(int64_t M, int64_t N, int64_t K, const uint16_t* A, int64_t lda, const uint16_t* B,
                           int64_t ldb, uint16_t* C, int64_t ldc, void* stream) {
     int64_t need = 0;
@@ -1594,6 +1786,21 @@ int gemm_relu_f16_noalloc(int64_t M, int64_t N, int64_t K, const uint16_t* A, in
     st = scratch_on_current_device(&ws);
     if (st != GR_OK) return st;
     return entry(M, N, K, A, lda, B, ldb, C, ldc, ws, need, stream, -1);
+}
+
+int gemm_relu_stream_read(const void* src, int64_t bytes, uint64_t* sink, void* stream) {
+    using namespace gr::probe;
+    if (bytes <= 0 || bytes % GRANULE != 0) return GR_ERR_INVALID_ARG;
+    if (!src || !sink) return GR_ERR_NULL_PTR;
+    if (reinterpret_cast<uintptr_t>(src) % 16 != 0 || reinterpret_cast<uintptr_t>(sink) % 8 != 0)
+        return GR_ERR_INVALID_ARG;
+    if (overlaps(reinterpret_cast<uintptr_t>(src), bytes, reinterpret_cast<uintptr_t>(sink), 8 * WGS))
+        return GR_ERR_ALIAS;
+    int st = check_device();
+    if (st != GR_OK) return st;
+    const int64_t vec_per_wg = bytes / 16 / WGS;
+    return launch(stream_read_kernel, WGS, THREADS, static_cast<hipStream_t>(stream),
+                  reinterpret_cast<const gr::u32x4*>(src), vec_per_wg, sink);
 }
 
 const char* gemm_relu_status_string(int status) {

@@ -134,7 +134,12 @@ constexpr int64_t MAX_LDB = (int64_t(1) << 31) / (BK * 2);
 // and its fragments are read like A's (ds_read_b128); rows of Bt past N are
 // clamped to row N-1 (their columns are never stored).
 // E: element type (ElemF16 or ElemBF16; only the MFMA and the rounding differ).
-template <bool EDGE, bool BT = false, typename E = ElemF16>
+// AT=true: A is given transposed (At, K x M row-major, pitch lda): its strips
+// [32 k][256 m] are staged exactly like B's (512-byte rows, chunk XOR
+// 4(k%4)) and its fragments are read like B's (ds_read_b64_tr_b16); with
+// EDGE the last tile row moves up to end at row M as usual (M >= 256), so
+// every copied column of At is < M.
+template <bool EDGE, bool BT = false, typename E = ElemF16, bool AT = false>
 __global__ __launch_bounds__(THREADS, 1) void gemm_relu_tile2_kernel(
     const uint16_t* __restrict__ A, const uint16_t* __restrict__ B, uint16_t* __restrict__ C, int64_t M, int64_t N,
     int64_t K, int64_t lda, int64_t ldb, int64_t ldc, uint32_t tiles_m, uint32_t tiles_n, uint32_t group_m,
@@ -157,9 +162,10 @@ __global__ __launch_bounds__(THREADS, 1) void gemm_relu_tile2_kernel(
     // A block = 16 rows x 64 bytes; lane -> row lane/4, slot lane%4.
     // B block = 2 rows x 512 bytes; lane -> row lane/32, slot lane%32.
     // Wave-uniform bases (advanced one strip per step) + per-lane offsets.
-    const uint8_t* base_a = reinterpret_cast<const uint8_t*>(A + m0 * lda);
+    static_assert(!(AT && BT), "one transposed operand at a time");
+    const uint8_t* base_a = reinterpret_cast<const uint8_t*>(AT ? A + m0 : A + m0 * lda);
     const uint8_t* base_b = reinterpret_cast<const uint8_t*>(BT ? B + n0 * ldb : B + n0);
-    const int64_t step_a = BK * 2;
+    const int64_t step_a = AT ? (int64_t)BK * lda * 2 : BK * 2;
     const int64_t step_b = BT ? (int64_t)BK * 2 : (int64_t)BK * ldb * 2;
     uint32_t off_a[COPIES], off_b[COPIES];
 #pragma unroll
@@ -167,7 +173,14 @@ __global__ __launch_bounds__(THREADS, 1) void gemm_relu_tile2_kernel(
         const uint32_t blk = 4u * wave + (uint32_t)i;
         const uint32_t ra = 16u * blk + (lane >> 2);
         const uint32_t ca = (lane & 3u) ^ ((ra >> 2) & 3u);
-        off_a[i] = (uint32_t)((ra * lda + 8u * ca) * 2);
+        if constexpr (AT) {
+            // At strip row k = 2 blk + lane/32, chunk slot lane%32 (the B layout)
+            const uint32_t rk = 2u * blk + (lane >> 5);
+            const uint32_t cm = (lane & 31u) ^ ((rk & 3u) << 2);
+            off_a[i] = (uint32_t)((rk * lda + 8u * cm) * 2);
+        } else {
+            off_a[i] = (uint32_t)((ra * lda + 8u * ca) * 2);
+        }
         if constexpr (BT) {
             uint32_t rb_src = ra;  // row n0 + ra of Bt, clamped to N-1
             if constexpr (EDGE) rb_src = n0 + ra < N ? ra : (uint32_t)(N - 1 - n0);
@@ -204,6 +217,16 @@ __global__ __launch_bounds__(THREADS, 1) void gemm_relu_tile2_kernel(
     const GR_LDS uint8_t* a_ptr[KSUB];
 #pragma unroll
     for (int s = 0; s < KSUB; ++s) a_ptr[s] = lds_p + a_off(ar, 2u * s + (lane >> 5));
+    // AT: A operand of step s, block i, read like a B operand (row 16s +
+    // 8(lane/32) + 4h + (lane%16)/4 of the At strip, column wm*128 + 32i +
+    // 16((lane/16)%2) + 4(lane%4)).
+    const uint32_t ak = 8u * (lane >> 5) + ((lane & 15u) >> 2);
+    const GR_LDS uint8_t* at_ptr[FM];
+#pragma unroll
+    for (int i = 0; i < FM; ++i) {
+        const uint32_t m = wm * WAVE_TM + 32u * i + 16u * ((lane >> 4) & 1u) + 4u * (lane & 3u);
+        at_ptr[i] = lds_p + b_off(ak, m >> 3) + 2u * (m & 7u);
+    }
     // B operand of step s, block j, half h: row 16s + 8(lane/32) + 4h +
     // (lane%16)/4, column wn*128 + 32j + 16((lane/16)%2) + 4(lane%4); the XOR
     // term depends on j, so each j has its own base; s and h are constant
@@ -234,15 +257,14 @@ __global__ __launch_bounds__(THREADS, 1) void gemm_relu_tile2_kernel(
     auto read_one = [&](Frags& f, uint32_t slot, int r) {
         const int s = r >> 3, q = r & 7;
         const uint32_t so = slot * STAGE_BYTES;
-        if (q == 0) {
-            f.a[s][0] = read_a_operand(a_ptr[s] + so);
-        } else if (q <= 4) {
+        if (q == 0 || q > 4) {
+            const int i = q == 0 ? 0 : q - 4;
+            if constexpr (AT) f.a[s][i] = read_b_operand(at_ptr[i] + so + 8192u * s);
+            else f.a[s][i] = read_a_operand(a_ptr[s] + so + 2048u * i);
+        } else {
             const int j = q - 1;
             if constexpr (BT) f.b[s][j] = read_a_operand(bt_ptr[s] + so + 2048u * j);
             else f.b[s][j] = read_b_operand(b_ptr[j] + so + 8192u * s);
-        } else {
-            const int i = q - 4;
-            f.a[s][i] = read_a_operand(a_ptr[s] + so + 2048u * i);
         }
     };
 

@@ -112,8 +112,11 @@ __device__ __forceinline__ u32x4 load8(const uint16_t* base, int64_t ld, int64_t
 // BT=true: B is given transposed (Bt, N x K row-major, pitch ldb); its
 // chunks are loaded like A's (rows n, 8 consecutive k) and stored as they
 // are, since the LDS B tile is k-contiguous already.
+// AT=true: A is given transposed (At, K x M row-major, pitch lda); it is
+// loaded like row-major B (8 x 8 blocks of k rows x m columns) and transposed
+// in registers into the k-contiguous LDS A tile.
 // E: element type (ElemF16 or ElemBF16; only the MFMA and the rounding differ).
-template <bool GUARD, int VA, int VB, bool BT = false, typename E = ElemF16>
+template <bool GUARD, int VA, int VB, bool BT = false, typename E = ElemF16, bool AT = false>
 __global__ __launch_bounds__(THREADS, 1) void gemm_relu_tile_kernel(
     const uint16_t* __restrict__ A, const uint16_t* __restrict__ B, uint16_t* __restrict__ C,
     int64_t M, int64_t N, int64_t K, int64_t lda, int64_t ldb, int64_t ldc,
@@ -144,8 +147,10 @@ __global__ __launch_bounds__(THREADS, 1) void gemm_relu_tile_kernel(
     auto load_tiles = [&](int64_t kt) {
         const int64_t k0 = kt * BK;
 #pragma unroll
-        for (int j = 0; j < 8; ++j)
-            ra[j] = load8<GUARD, VA>(A, lda, m0 + a_row + 32 * j, k0 + 8 * a_chunk, M, K);
+        for (int j = 0; j < 8; ++j) {
+            if constexpr (AT) ra[j] = load8<GUARD, VA>(A, lda, k0 + 8 * b_kb + j, m0 + 8 * b_ng, K, M);
+            else ra[j] = load8<GUARD, VA>(A, lda, m0 + a_row + 32 * j, k0 + 8 * a_chunk, M, K);
+        }
 #pragma unroll
         for (int r = 0; r < 8; ++r) {
             if constexpr (BT) rb[r] = load8<GUARD, VB>(B, ldb, n0 + a_row + 32 * r, k0 + 8 * a_chunk, N, K);
@@ -156,9 +161,20 @@ __global__ __launch_bounds__(THREADS, 1) void gemm_relu_tile_kernel(
     auto store_tiles = [&](uint32_t stage) {
         uint8_t* sa = lds + stage * STAGE_BYTES;
         uint8_t* sb = sa + B_OFFSET;
+        if constexpr (AT) {
+            // Transpose the 8 (k) x 8 (m) block: column c becomes one k-chunk.
 #pragma unroll
-        for (int j = 0; j < 8; ++j)
-            *reinterpret_cast<u32x4*>(sa + lds_chunk(a_row + 32 * j, a_chunk)) = ra[j];
+            for (int c = 0; c < 8; ++c) {
+                u32x4 o;
+#pragma unroll
+                for (int d = 0; d < 4; ++d) o[d] = pair_halves(ra[2 * d][c >> 1], ra[2 * d + 1][c >> 1], c & 1);
+                *reinterpret_cast<u32x4*>(sa + lds_chunk(8 * b_ng + c, b_kb)) = o;
+            }
+        } else {
+#pragma unroll
+            for (int j = 0; j < 8; ++j)
+                *reinterpret_cast<u32x4*>(sa + lds_chunk(a_row + 32 * j, a_chunk)) = ra[j];
+        }
         if constexpr (BT) {
 #pragma unroll
             for (int j = 0; j < 8; ++j)

@@ -193,6 +193,26 @@ int gemm_relu_f16_forced(int64_t M, int64_t N, int64_t K,
                          void* stream, int path);
 
 /*
+ * gemm_relu_f16_forced_order -- gemm_relu_f16_forced with the workgroup order
+ * of the tile kernels chosen by the caller: `group_m` tile rows per group of
+ * the grid-level swizzle (>= 1; the planner uses 4) and `xcd_remap` 1 (the
+ * planner's choice: each XCD takes a contiguous range of tiles) or 0 (tile
+ * order follows the workgroup id).  The order decides only when each tile
+ * runs, never what it computes, so every setting must give the same bits:
+ * the test hook that checks exactly that.  The pages give the grid swizzle
+ * (panel size, ordering) as a free scheduling choice for L2 reuse (TileLang
+ * tutorial, chapter "布局与存储体冲突", T.use_swizzle; "Writing
+ * high-performance kernels in TileLang", section "編寫一個 GEMM").
+ * GR_ERR_INVALID_ARG for group_m < 1 or xcd_remap not 0 or 1; paths as
+ * gemm_relu_f16_forced.
+ */
+int gemm_relu_f16_forced_order(int64_t M, int64_t N, int64_t K,
+                               const uint16_t* A, int64_t lda,
+                               const uint16_t* B, int64_t ldb,
+                               uint16_t* C, int64_t ldc,
+                               void* stream, int path, int group_m, int xcd_remap);
+
+/*
  * ---- calls with a caller-provided workspace ---------------------------------
  * Two paths use scratch device memory when the caller provides it:
  *   - GR_PATH_TILE_PACKED.  The pipelined kernel reads A and B in whole
@@ -328,6 +348,47 @@ int gemm_relu_f16_bt_plan(int64_t M, int64_t N, int64_t K,
 int gemm_relu_f16_bt_forced(int64_t M, int64_t N, int64_t K,
                             const uint16_t* A, int64_t lda,
                             const uint16_t* Bt, int64_t ldbt,
+                            uint16_t* C, int64_t ldc,
+                            void* stream, int path);
+
+/*
+ * ---- A given transposed -----------------------------------------------------
+ * The same operation with A stored as its transpose At (K x M row-major,
+ * element (k, m) at At[k*ldat + m], pitch ldat >= max(1, M)): C := ReLU(At^T
+ * * B).  This is the transpose_A option of the pages' tile GEMM (T.gemm takes
+ * transpose_A and transpose_B: "Writing high-performance kernels in
+ * TileLang", section "編寫一個 GEMM"; the tutorial's dynamic-shape GEMM takes
+ * trans_A and trans_B, chapter "动态形状与变长序列").  Every convention above
+ * holds, with At in the place of A; the paths are:
+ *   GR_PATH_SMALL_M   M <= 16, K % 32 == 0, N >= 64: the streaming small-M
+ *                     kernel (B of any alignment), each lane gathering its k
+ *                     run of one column of At;
+ *   GR_PATH_TILE      M >= 256, 16-byte rows of At and B, K % 32 == 0,
+ *                     pitches of at most 2^25 elements: the 32-deep pipelined
+ *                     kernel with At strips staged and read like B's;
+ *   GR_PATH_TILE_EDGE everything else (the guarded kernel, At transposed in
+ *                     registers).
+ * There is no workspace variant; fp16 with the fused ReLU only.
+ */
+int gemm_relu_f16_ta(int64_t M, int64_t N, int64_t K,
+                     const uint16_t* At, int64_t ldat,
+                     const uint16_t* B, int64_t ldb,
+                     uint16_t* C, int64_t ldc,
+                     void* stream);
+
+/* Pure planner for gemm_relu_f16_ta (no GPU needed); see gemm_relu_f16_plan. */
+int gemm_relu_f16_ta_plan(int64_t M, int64_t N, int64_t K,
+                          const uint16_t* At, int64_t ldat,
+                          const uint16_t* B, int64_t ldb,
+                          const uint16_t* C, int64_t ldc,
+                          gr_plan_t* out);
+
+/* gemm_relu_f16_ta on a given path (GR_PATH_TILE, GR_PATH_TILE_EDGE or
+   GR_PATH_SMALL_M; GR_ERR_INVALID_PATH otherwise or when the path's
+   conditions do not hold).  Test hook. */
+int gemm_relu_f16_ta_forced(int64_t M, int64_t N, int64_t K,
+                            const uint16_t* At, int64_t ldat,
+                            const uint16_t* B, int64_t ldb,
                             uint16_t* C, int64_t ldc,
                             void* stream, int path);
 
@@ -695,6 +756,20 @@ int gemm_relu_f16_noalloc(int64_t M, int64_t N, int64_t K,
                           const uint16_t* B, int64_t ldb,
                           uint16_t* C, int64_t ldc,
                           void* stream);
+
+/*
+ * gemm_relu_stream_read -- a measurement aid, not part of the operation:
+ * reads `bytes` bytes of the device buffer `src` once (256 workgroups of 512
+ * threads, each streaming one contiguous 1/256 of it with nontemporal
+ * 16-byte loads) and writes one 64-bit XOR of each workgroup's words to
+ * `sink` (device, 256 x 8 bytes), so that timing it gives the HBM read
+ * ceiling a bandwidth-bound path is judged against (the roofline's memory
+ * leg; TileLang tutorial, chapter "性能取证", sections "三层归因" and
+ * "Roofline 计算器").  bytes: a positive multiple of 8 MiB; src 16-byte and
+ * sink 8-byte aligned and disjoint.  Errors: GR_ERR_INVALID_ARG,
+ * GR_ERR_NULL_PTR, GR_ERR_ALIAS, device errors.  Enqueues on `stream`.
+ */
+int gemm_relu_stream_read(const void* src, int64_t bytes, uint64_t* sink, void* stream);
 
 /* Static, NUL-terminated name of a status code ("GR_OK", "GR_ERR_ALIAS", ...),
  * so that a refused call can be reported with its cause (the fail-loudly
