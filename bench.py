@@ -10,11 +10,17 @@ kernel measured live with HIP events on the launch stream, and the CPU oracle
 timed on a bounded sample of the same workload.
 
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--settle-ms MS] [--no-cpu-baseline]
-                  [--no-workloads] [--workload NAME] [--copy-probe MIB]
+                  [--no-workloads] [--workload NAME] [--reps R] [--workload-settle-ms MS]
+                  [--no-oracle-table] [--copy-probe MIB] [--read-probe MIB]
                   [--vendor-reference] [--extra-shapes]
 
+The JSON line also carries the HBM read ceiling measured by the library's
+read probe, a per-workload table (every call variant timed after its own
+clock settling, R >= 100 launches back to back and R event-bracketed ones)
+and the oracle's timings per workload on one thread and on all cores.
 ``--copy-probe`` runs only a device-to-device copy of known size; it is what
-the HBM-traffic counters are calibrated against.  ``--vendor-reference`` only
+the HBM-traffic counters are calibrated against.  ``--read-probe`` runs only
+the read probe.  ``--vendor-reference`` only
 times torch.mm + relu_ (the vendor BLAS) on the same workloads, for context;
 ``--extra-shapes`` times the library (and torch.mm + relu_) on shapes beyond
 the workloads: mid-M, narrow small-M, long K, B given transposed.
@@ -166,6 +172,61 @@ def cpu_baseline(w, max_seconds=20.0):
     }
 
 
+# rows of the result the oracle computes for the per-workload timings where
+# the whole matrix would take too long: (all cores, one thread)
+ORACLE_ROWS = {"square4096": (256, 16), "mlp8192x28672x8192": (64, 2), "ragged4099x3071x2050": (None, 128)}
+
+
+def cpu_oracle_table():
+    """The oracle (as it stands) per workload, on all host cores and on one
+    thread: the whole matrix for the 1024^3 and small-M workloads (and the
+    ragged one on all cores), R full rows elsewhere (work per row is exactly
+    2 N K FLOP).  ``parity_check_s`` is the wall time of the oracle calls the
+    workload's GPU parity test makes: the whole matrix, or 4096 sampled
+    elements plus 8 full rows and 8 full columns."""
+    import numpy as np
+    import oracle
+
+    allc = len(os.sched_getaffinity(0))
+    if os.environ.get("OMP_NUM_THREADS", "").isdigit():
+        allc = min(allc, int(os.environ["OMP_NUM_THREADS"]))
+    allc = max(1, allc)
+    table = {}
+    for name, w in synth.WORKLOADS.items():
+        A, B = synth.operands(w)
+        row = {}
+        for label, threads, pick in (("all_cores", allc, 0), ("single_thread", 1, 1)):
+            r = ORACLE_ROWS.get(name, (None, None))[pick]
+            t0 = time.perf_counter()
+            if r is None:
+                oracle.gemm_relu_full(A, B, threads=threads)
+                rows = w.M
+            else:
+                oracle.gemm_relu_rows(A, B, np.arange(r), threads=threads)
+                rows = r
+            dt = time.perf_counter() - t0
+            flops = 2.0 * rows * w.N * w.K
+            row[label] = {"threads": threads, "sample": "full matrix" if r is None else "%d rows" % r,
+                          "seconds": round(dt, 3), "tflops": round(flops / dt / 1e12, 5)}
+        t0 = time.perf_counter()
+        if w.check == "full":
+            oracle.gemm_relu_full(A, B, threads=allc)
+            what = "full matrix"
+        else:
+            ii, jj = synth.sample_indices(w.M, w.N, 4096, w.seed)
+            oracle.gemm_relu_elems(A, B, ii, jj, threads=allc)
+            oracle.gemm_relu_rows(A, B, np.linspace(0, w.M - 1, 8).astype(np.int64), threads=allc)
+            oracle.gemm_relu_cols(A, B, np.linspace(0, w.N - 1, 8).astype(np.int64), threads=allc)
+            what = "4096 elements + 8 rows + 8 columns"
+        row["parity_check_s"] = round(time.perf_counter() - t0, 3)
+        row["parity_check"] = what
+        table[name] = row
+        print("[oracle] %s %s" % (name, row), file=sys.stderr, flush=True)
+        del A, B
+    oracle.set_threads(allc)
+    return table
+
+
 def traffic_for(workload: str, src_hash: str):
     """HBM bytes per launch (fetched + written) from the committed counter
     summary, if it was taken on the current kernel sources; else None."""
@@ -182,56 +243,105 @@ def traffic_for(workload: str, src_hash: str):
     return None
 
 
-def bench_workload(gr, torch, w, reps, cold):
-    """Secondary measurement of one workload: median/min/p90 launch time."""
+def time_back_to_back(torch, runs, stream, reps):
+    """Average launch time (ms) over ``reps`` back-to-back launches between one
+    event pair on the launch stream, cycling through ``runs``."""
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for i in range(reps):
+        runs[i % len(runs)]()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / reps
+
+
+def measure(torch, runs, stream, reps, settle_ms):
+    """Settle the clock on the launches, then time them back to back (the
+    figure the rates use) and one event pair per launch (median, min, p90)."""
+    settle(torch, lambda: [r() for r in runs], settle_ms)
+    avg = time_back_to_back(torch, runs, stream, reps)
+    per = sorted(time_launches(torch, runs[i % len(runs)], stream, 1)[0] for i in range(reps))
+    return {
+        "avg_us": round(avg * 1e3, 2),
+        "per_launch_median_us": round(statistics.median(per) * 1e3, 2),
+        "per_launch_min_us": round(per[0] * 1e3, 2),
+        "per_launch_p90_us": round(per[int(0.9 * (len(per) - 1))] * 1e3, 2),
+    }
+
+
+def rates(w, stats):
+    flops, nbytes = algorithmic(w)
+    t = stats["avg_us"] * 1e-6
+    return {
+        "tflops": round(flops / t / 1e12, 1),
+        "gbs": round(nbytes / t / 1e9, 1),
+        "frac_mfma": round(flops / t / 1e12 / MFMA_F16_PEAK_TFLOPS, 4),
+        "frac_hbm": round(nbytes / t / 1e9 / HBM_PEAK_GBS, 4),
+    }
+
+
+def forced_ws_launcher(gr, w, A, B, C, stream, ws, path):
+    fn = gr.lib().gemm_relu_f16_forced_ws
+    M, N, K = w.M, w.N, w.K
+    a, b, c, h = A.data_ptr(), B.data_ptr(), C.data_ptr(), stream.cuda_stream
+    wp, wb = ws.data_ptr(), ws.numel()
+
+    def run():
+        st = fn(M, N, K, a, K, b, N, c, N, wp, wb, h, path)
+        if st != 0:
+            raise gr.GemmReluError(st, "gemm_relu_f16_forced_ws")
+    return run
+
+
+def bench_workload(gr, torch, w, reps, settle_ms, read_ceiling=None):
+    """Secondary measurement of one workload, per call variant: the plain call
+    (gemm_relu_f16, in place), the call with a workspace (gemm_relu_f16_ws,
+    with what the library asks for, or 1 MiB where it asks for none), and on
+    the ragged workload the packed path forced.  Each variant: clock settled
+    first, ``reps`` back-to-back launches between one event pair (the figure
+    the rates use), and ``reps`` event-bracketed launches for the spread.
+    The small-M workload rotates four copies of B (4 x 256 MiB, well above
+    the 256 MB last-level cache) so every launch streams B from HBM."""
+    cold = w.name.startswith("smallm")
     copies = 4 if cold else 1
     A, Bs, C = make_device_operands(torch, w, copies=copies)
     stream = torch.cuda.current_stream()
     ws = workspace_for(gr, torch, w, A, Bs[0], C)
-    plan = plan_for(gr, w, A, Bs[0], C, ws)
-    runs = [launcher(gr, torch, w, A, B, C, stream, ws) for B in Bs]
-    for r in runs:
-        for _ in range(3):
-            r()
-    torch.cuda.synchronize()
-    if cold:
-        # Rotate 4 copies of B (4 x |B| is well above the 256 MB last-level
-        # cache), so every launch streams B from HBM.  No flush buffer is
-        # written: its dirty lines would be written back during the timed
-        # launch and count against it.
-        times = []
-        for i in range(reps):
-            t = time_launches(torch, runs[i % copies], stream, 1)
-            times.append(t[0])
-    else:
-        times = time_launches(torch, runs[0], stream, reps)
-    del A, Bs, C, runs
+    if ws is None:
+        ws = torch.empty(1 << 20, dtype=torch.uint8, device="cuda")
+    variants = {"in_place": None, "workspace": ws}
+    out = {"cache": "cold (4 rotating copies of B)" if cold else "warm", "reps": reps, "variants": {}}
+    for name, wsv in variants.items():
+        runs = [launcher(gr, torch, w, A, B, C, stream, wsv) for B in Bs]
+        plan = plan_for(gr, w, A, Bs[0], C, wsv)
+        st = measure(torch, runs, stream, reps, settle_ms)
+        st.update(rates(w, st))
+        st.update({"path": plan["path_name"], "workspace_bytes": plan["workspace"], "grid": plan["grid"],
+                   "split_k": plan["split_k"]})
+        out["variants"][name] = st
+    if w.name.startswith("ragged"):
+        big = torch.empty(64 << 20, dtype=torch.uint8, device="cuda")
+        runs = [forced_ws_launcher(gr, w, A, Bs[0], C, stream, big, gr.GR_PATH_TILE_PACKED)]
+        st = measure(torch, runs, stream, reps, settle_ms)
+        st.update(rates(w, st))
+        st.update({"path": "tile_packed (forced)", "workspace_bytes": 64 << 20})
+        out["variants"]["packed_forced"] = st
+        del big
+    # top-level figures: the fastest variant, named
+    best = min(out["variants"], key=lambda k: out["variants"][k]["avg_us"])
+    out["best_variant"] = best
+    out.update({k: out["variants"][best][k] for k in ("avg_us", "tflops", "gbs", "frac_mfma", "frac_hbm", "path")})
+    if cold and read_ceiling:
+        out["frac_of_read_ceiling"] = round(out["gbs"] / read_ceiling["gbs"], 4)
+    del A, Bs, C, ws, variants
     torch.cuda.empty_cache()
-    flushed = None if cold else bench_flushed(gr, torch, w, reps, ws)
-    del ws
+    if not cold:
+        fl = bench_flushed(gr, torch, w, reps, settle_ms)
+        out["flushed"] = fl
     torch.cuda.empty_cache()
-    times.sort()
-    med = statistics.median(times)
-    flops, nbytes = algorithmic(w)
-    extra = {}
-    if flushed is not None:
-        fmed = statistics.median(flushed)
-        extra = {"flushed_median_us": round(fmed * 1e3, 2), "flushed_tflops": round(flops / (fmed * 1e-3) / 1e12, 1),
-                 "flushed_pairs": flush_pairs(w)}
-    return {
-        "median_us": round(med * 1e3, 2),
-        "min_us": round(times[0] * 1e3, 2),
-        "p90_us": round(times[int(0.9 * (len(times) - 1))] * 1e3, 2),
-        "tflops": round(flops / (med * 1e-3) / 1e12, 1),
-        "gbs": round(nbytes / (med * 1e-3) / 1e9, 1),
-        "frac_mfma": round(flops / (med * 1e-3) / 1e12 / MFMA_F16_PEAK_TFLOPS, 4),
-        "frac_hbm": round(nbytes / (med * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
-        "cache": "cold" if cold else "warm",
-        "reps": reps,
-        "path": plan["path_name"],
-        "workspace_bytes": plan["workspace"],
-        **extra,
-    }
+    return out
 
 
 def flush_pairs(w):
@@ -241,9 +351,10 @@ def flush_pairs(w):
     return max(2, min(128, -(-(512 << 20) // pair)))
 
 
-def bench_flushed(gr, torch, w, reps, ws):
-    """Per-launch times with A and B evicted from every cache: each launch
-    reads its own copy of both operands, rotating over flush_pairs(w) copies.
+def bench_flushed(gr, torch, w, reps, settle_ms):
+    """Launch times with A and B evicted from every cache: back-to-back
+    launches, each on its own copy of both operands, rotating over
+    flush_pairs(w) copies (with the workspace the library asks for, if any).
     No flush buffer is written (its write-back would land in the timed
     launch)."""
     n = flush_pairs(w)
@@ -257,13 +368,41 @@ def bench_flushed(gr, torch, w, reps, ws):
         pairs.append((a, b.half()))
     C = torch.empty(w.M, w.N, device="cuda", dtype=torch.float16)
     stream = torch.cuda.current_stream()
+    ws = workspace_for(gr, torch, w, pairs[0][0], pairs[0][1], C)
     runs = [launcher(gr, torch, w, a, b, C, stream, ws) for a, b in pairs]
-    for r in runs:
-        r()
-    torch.cuda.synchronize()
-    times = [time_launches(torch, runs[i % n], stream, 1)[0] for i in range(reps)]
-    del pairs, runs, C
-    return times
+    st = measure(torch, runs, stream, reps, settle_ms)
+    st.update(rates(w, st))
+    st["pairs"] = n
+    del pairs, runs, C, ws
+    return st
+
+
+def read_ceiling(gr, torch, nbytes=256 << 20, copies=4, reps=100, settle_ms=100.0):
+    """The HBM read ceiling the small-M path is judged against: the library's
+    read probe (gemm_relu_stream_read) on ``copies`` rotating buffers of
+    ``nbytes`` each, back to back."""
+    bufs = [torch.randint(0, 1 << 30, (nbytes // 4,), device="cuda", dtype=torch.int32) for _ in range(copies)]
+    sink = torch.empty(256, dtype=torch.int64, device="cuda")
+    stream = torch.cuda.current_stream()
+    h = stream.cuda_stream
+    fn = gr.lib().gemm_relu_stream_read
+
+    def mk(b):
+        def run():
+            st = fn(b.data_ptr(), nbytes, sink.data_ptr(), h)
+            if st != 0:
+                raise gr.GemmReluError(st, "gemm_relu_stream_read")
+        return run
+    runs = [mk(b) for b in bufs]
+    st = measure(torch, runs, stream, reps, settle_ms)
+    gbs = nbytes / (st["avg_us"] * 1e-6) / 1e9
+    del bufs, sink
+    torch.cuda.empty_cache()
+    return {"bytes_per_launch": nbytes, "rotating_buffers": copies, "avg_us": st["avg_us"],
+            "per_launch_median_us": st["per_launch_median_us"], "gbs": round(gbs, 1),
+            "frac_of_peak": round(gbs / HBM_PEAK_GBS, 4),
+            "what": "gemm_relu_stream_read: 256 workgroups x 512 threads, one contiguous 1/256 of the buffer "
+                    "each, nontemporal 16-byte loads, 32 KiB in flight per workgroup"}
 
 
 def settle(torch, run, ms):
@@ -525,6 +664,14 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-workloads", action="store_true", help="skip the secondary per-workload table")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB")
+    ap.add_argument("--read-probe", type=int, default=0, metavar="MIB",
+                    help="only time the library's HBM read probe on 4 rotating buffers of MIB MiB "
+                         "(a multiple of 8)")
+    ap.add_argument("--reps", type=int, default=100,
+                    help="launches per variant in the per-workload table (back to back, and one event pair each)")
+    ap.add_argument("--workload-settle-ms", type=float, default=100.0,
+                    help="clock settling before each variant of the per-workload table")
+    ap.add_argument("--no-oracle-table", action="store_true", help="skip the per-workload oracle timings")
     ap.add_argument("--vendor-reference", action="store_true",
                     help="only time torch.mm + relu_ on the workloads (context, not the product)")
     ap.add_argument("--extra-shapes", action="store_true",
@@ -550,6 +697,9 @@ def main():
 
     if args.copy_probe:
         copy_probe(torch, args.copy_probe)
+        return
+    if args.read_probe:
+        print(json.dumps({"read_ceiling": read_ceiling(gr, torch, nbytes=args.read_probe << 20)}), flush=True)
         return
     if args.vendor_reference:
         vendor_reference(torch)
@@ -631,16 +781,19 @@ def main():
     }
 
     if not args.no_workloads:
+        ceiling = read_ceiling(gr, torch, settle_ms=args.workload_settle_ms)
+        out["read_ceiling"] = ceiling
+        print("[bench] read ceiling %s" % (ceiling,), file=sys.stderr, flush=True)
         table = {}
         for name, wl in synth.WORKLOADS.items():
-            cold = wl.name.startswith("smallm")
-            reps = 20 if wl.M * wl.N * wl.K > 1e12 else 50
-            table[name] = bench_workload(gr, torch, wl, reps, cold)
+            table[name] = bench_workload(gr, torch, wl, max(args.reps, 1), args.workload_settle_ms, ceiling)
             print("[bench] %s %s" % (name, table[name]), file=sys.stderr, flush=True)
         out["workloads"] = table
 
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(w)
+        out["cpu_baseline"] = cpu_baseline(w, max_seconds=15.0)
+        if not args.no_oracle_table:
+            out["cpu_oracle"] = cpu_oracle_table()
     print(json.dumps(out), flush=True)
 
 

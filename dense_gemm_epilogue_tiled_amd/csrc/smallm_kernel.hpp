@@ -195,19 +195,21 @@ __global__ __launch_bounds__(64 * W, 1) void gemm_relu_smallm_kernel(
 
 // ---- streaming variant: B copied straight into LDS ----------------------------
 //
-// The kernel above holds B in registers, so each wave can keep only two
-// 32-deep steps in flight, and its 64-column strips read B in 128-byte row
-// pieces.  Measured on this part, streaming reads reach about 6.8 TB/s when
-// every workgroup reads 256-byte (or longer) row pieces with plenty of bytes
-// in flight, against about 6.0 TB/s for 128-byte pieces.  This variant moves
-// B with direct-to-LDS copies instead (global_load_lds_dwordx4, nontemporal:
-// no registers held while the bytes travel), so each wave keeps R - 1 slots
-// of 32 rows x NB columns in flight:
+// The kernel above holds B in registers and reads it in 128-byte row pieces
+// (64-column strips).  Measured on this part, streaming reads reach about
+// 6.8 TB/s when every workgroup reads 256-byte (or longer) row pieces, against
+// about 6.0 TB/s for 128-byte pieces, and they are fastest with about 32 KiB
+// in flight per workgroup: more outstanding copies per workgroup measured
+// slower (one 8 KiB slot per wave 41.7 us, two 44.5 us, three 45.0 us for the
+// first pass of 8 x 16384 x 8192; 8 waves of one slot 45.0 us).  This
+// variant moves B with direct-to-LDS copies (global_load_lds_dwordx4,
+// nontemporal) and keeps exactly one slot per wave in flight:
 //   * workgroup (cb, s): columns [NB cb, NB cb + NB) and the K range of split
 //     s (all of K without a split); its W waves take the range's 32-row slots
-//     in turn (wave w: slots w, w + W, ...), each into a ring of R slots of
-//     its own, so a wave reads back only what it copied itself: its own
-//     vmcnt says when a slot has landed and no barrier is needed;
+//     in turn (wave w: slots w, w + W, ...), each into an LDS slot of its own:
+//     copy the slot, wait for this wave's copies (vmcnt 0), multiply, next
+//     slot; a wave reads back only what it copied itself, so no barrier is
+//     needed, and the W waves of a workgroup keep W slots in flight;
 //   * copies: a slot is 32 rows of 2 NB bytes; one copy instruction moves
 //     1 KiB (1024 / 2NB whole rows); 16-byte chunk c of row r sits at chunk
 //     slot c XOR 2(r mod 4) (the 4 rows one 16-lane group reads below land in
@@ -216,7 +218,7 @@ __global__ __launch_bounds__(64 * W, 1) void gemm_relu_smallm_kernel(
 //     v_mfma_f32_16x16x32 (16 columns x 32 k) comes from two
 //     ds_read_b64_tr_b16, the A operand (16 rows of A x 32 k; rows >= M are
 //     zero) from one 16-byte load of A per lane and slot (A is small and
-//     stays in the caches);
+//     stays in the caches), issued with the slot's copies;
 //   * B may have any 2-byte alignment (the copies read any address); the
 //     last column block moves left to end at column N (N >= NB), so every
 //     copy reads inside [0, K) x [0, N) and only the block's own columns
@@ -226,6 +228,9 @@ __global__ __launch_bounds__(64 * W, 1) void gemm_relu_smallm_kernel(
 //     the fp32 sum of the range goes to part[s][m][n] for the ordered second
 //     pass (gemm_relu_smallm_reduce_kernel below).
 // Needs M <= 16, K % 32 == 0 (whole slots), 16-byte rows of A.
+// AT=true: A is given transposed (At, K x M row-major, pitch lda, any
+// alignment): each lane gathers its 8 consecutive k of one column of At with
+// 2-byte loads (A is small and stays in the caches).
 namespace stream {
 
 constexpr int SLOT_ROWS = 32;
@@ -234,7 +239,7 @@ __device__ __forceinline__ uint32_t chunk_slot(uint32_t row, uint32_t c) { retur
 
 }  // namespace stream
 
-template <int NB, int W, int R, bool SPLIT, typename E = ElemF16>
+template <int NB, int W, bool SPLIT, typename E = ElemF16, bool AT = false>
 __global__ __launch_bounds__(64 * W, 1) void gemm_relu_smallm_stream_kernel(
     const uint16_t* __restrict__ A, const uint16_t* __restrict__ B, uint16_t* __restrict__ C,
     float* __restrict__ part, int64_t M, int64_t N, int64_t K, int64_t lda, int64_t ldb, int64_t ldc,
@@ -247,11 +252,9 @@ __global__ __launch_bounds__(64 * W, 1) void gemm_relu_smallm_stream_kernel(
     constexpr int RPI = 1024 / ROWB;                     // rows per copy instruction
     constexpr int NBLK = NB / 16;                        // MFMA column blocks per slot
     constexpr int T = 64 * W;
-    constexpr int WAIT = (R - 1) * (DPS + 1);            // copies + A loads of R - 1 slots
     static_assert(CH >= 8 && DPS * RPI == stream::SLOT_ROWS, "whole rows per copy instruction");
-    static_assert(W * MAX_M * NB * 4 <= W * R * SLOT, "the cross-wave sum fits the ring");
-    static_assert(WAIT < 64, "vmcnt range");
-    __shared__ __attribute__((aligned(1024))) uint8_t lds[W * R * SLOT];
+    static_assert(MAX_M * NB * 4 <= SLOT, "the cross-wave sum fits the slots");
+    __shared__ __attribute__((aligned(1024))) uint8_t lds[W * SLOT];
 
     const uint32_t tid = threadIdx.x, lane = tid & 63u;
     const uint32_t w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -262,8 +265,7 @@ __global__ __launch_bounds__(64 * W, 1) void gemm_relu_smallm_stream_kernel(
     const int64_t k_begin = s * k_per_split;
     const int64_t k_end = k_begin + k_per_split < K ? k_begin + k_per_split : K;
     const int64_t slots = (k_end - k_begin) / stream::SLOT_ROWS;
-    const int64_t n_mine = slots > (int64_t)w ? (slots - w + W - 1) / W : 0;
-    const uint32_t ring = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t*)lds + w * R * SLOT;
+    const uint32_t base = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t*)lds + w * SLOT;
 
     // copy instruction i of a slot: lane -> row i RPI + lane / CH, chunk slot
     // lane % CH, which holds chunk (lane % CH) XOR 2 (row mod 4)
@@ -275,16 +277,6 @@ __global__ __launch_bounds__(64 * W, 1) void gemm_relu_smallm_stream_kernel(
     }
     const uint16_t* b_range = B + k_begin * ldb + n0;
     const uint32_t am = lane & 15u, ag = lane >> 4;
-    u32x4 areg[R];
-    auto issue = [&](int64_t q) {  // this wave's q-th slot
-        const int64_t t = w + (int64_t)W * q;
-        const uint8_t* src = reinterpret_cast<const uint8_t*>(b_range + t * stream::SLOT_ROWS * ldb);
-        const uint32_t dst = ring + (uint32_t)(q % R) * SLOT;
-#pragma unroll
-        for (int i = 0; i < DPS; ++i) dma16_nt(src, voff[i], dst + i * 1024);
-        const int64_t k = k_begin + t * stream::SLOT_ROWS + 8 * ag;
-        areg[q % R] = (int64_t)am < M ? *reinterpret_cast<const u32x4*>(A + am * lda + k) : u32x4{0u, 0u, 0u, 0u};
-    };
 
     // B operand of column block j: lane l (group g = l/16, i = l%16) reads
     // row 8g + i/4 (then + 4), columns 16j + 4(i%4) .. +3.
@@ -294,17 +286,24 @@ __global__ __launch_bounds__(64 * W, 1) void gemm_relu_smallm_stream_kernel(
 #pragma unroll
     for (int j = 0; j < NBLK; ++j) acc[j] = f32x4{};
 
-    const int64_t pro = n_mine < R - 1 ? n_mine : R - 1;
-    for (int64_t q = 0; q < pro; ++q) issue(q);
-    for (int64_t q = 0; q < n_mine; ++q) {
-        // slot q + R - 1 reuses the ring place of slot q - 1, whose reads the
-        // MFMAs of the previous iteration have consumed
-        const bool more = q + R - 1 < n_mine;
-        if (more) issue(q + R - 1);
-        if (more) tile2::wait_vmcnt<WAIT>();  // slot q has landed
-        else tile2::wait_vmcnt<0>();
-        const uint32_t base = ring + (uint32_t)(q % R) * SLOT;
-        const f16x8 a = __builtin_bit_cast(f16x8, areg[q % R]);
+    for (int64_t t = w; t < slots; t += W) {
+        // this wave's slot t: copies of B, the A operand; the LDS slot is free
+        // (the previous slot's reads were consumed by its MFMAs)
+        const uint8_t* src = reinterpret_cast<const uint8_t*>(b_range + t * stream::SLOT_ROWS * ldb);
+#pragma unroll
+        for (int i = 0; i < DPS; ++i) dma16_nt(src, voff[i], base + i * 1024);
+        const int64_t k = k_begin + t * stream::SLOT_ROWS + 8 * ag;
+        u32x4 areg;
+        if constexpr (AT) {
+            uint32_t h[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) h[e] = (int64_t)am < M ? (uint32_t)A[(k + e) * lda + am] : 0u;
+            areg = u32x4{h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16), h[6] | (h[7] << 16)};
+        } else {
+            areg = (int64_t)am < M ? *reinterpret_cast<const u32x4*>(A + am * lda + k) : u32x4{0u, 0u, 0u, 0u};
+        }
+        tile2::wait_vmcnt<0>();  // the slot's copies and A have landed
+        const f16x8 a = __builtin_bit_cast(f16x8, areg);
 #pragma unroll
         for (int j = 0; j < NBLK; ++j) {
             const uint32_t c = 2 * j + ((fi >> 1) & 1u);
@@ -321,13 +320,15 @@ __global__ __launch_bounds__(64 * W, 1) void gemm_relu_smallm_stream_kernel(
     }
 
     // acc[j] holds C^T: lane l, register r is row m = l%16, column 16j +
-    // 4(l/16) + r of the block.  Sum the waves in order through LDS.
+    // 4(l/16) + r of the block.  Sum the waves in order through LDS (each
+    // wave's partials in its own slot).
     __syncthreads();
-    float* red = reinterpret_cast<float*>(lds);  // [W][16][NB]
+    float* red = reinterpret_cast<float*>(lds);  // wave w at w * SLOT: [16][NB]
 #pragma unroll
     for (int j = 0; j < NBLK; ++j)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) red[(w * MAX_M + (lane & 15u)) * NB + 16 * j + 4 * (lane >> 4) + r] = acc[j][r];
+        for (int r = 0; r < 4; ++r)
+            red[w * (SLOT / 4) + (lane & 15u) * NB + 16 * j + 4 * (lane >> 4) + r] = acc[j][r];
     __syncthreads();
     for (uint32_t o = tid; o < (uint32_t)(MAX_M * NB); o += T) {
         const uint32_t m = o / NB, nl = o % NB;
@@ -335,7 +336,7 @@ __global__ __launch_bounds__(64 * W, 1) void gemm_relu_smallm_stream_kernel(
         if ((int64_t)m >= M || n < n_own) continue;
         float v = 0.0f;
 #pragma unroll
-        for (int ww = 0; ww < W; ++ww) v += red[(ww * MAX_M + m) * NB + nl];
+        for (int ww = 0; ww < W; ++ww) v += red[ww * (SLOT / 4) + m * NB + nl];
         if constexpr (SPLIT) part[(s * M + m) * N + n] = v;
         else C[(int64_t)m * ldc + n] = epi_value<E>(v, n, N, ep);
     }

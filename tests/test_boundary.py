@@ -767,3 +767,69 @@ def test_noalloc_refuses_problems_beyond_its_scratch():
     assert gr.gemm_relu_f16_noalloc(M, N, K, 0, lda, BASE_B, N, BASE_C, N) == gr.GR_ERR_NULL_PTR
     # an empty problem launches nothing and succeeds anywhere
     assert gr.gemm_relu_f16_noalloc(0, N, K, BASE_A, lda, BASE_B, N, BASE_C, N) == gr.GR_OK
+
+
+def plan_ta(M, N, K, ldat=None, ldb=None, ldc=None, a=BASE_A, b=BASE_B, c=BASE_C):
+    ldat = max(M, 1) if ldat is None else ldat
+    ldb = max(N, 1) if ldb is None else ldb
+    ldc = max(N, 1) if ldc is None else ldc
+    return gr.gemm_relu_f16_ta_plan(M, N, K, a, ldat, b, ldb, c, ldc)
+
+
+def test_transposed_a_planner_and_checks():
+    # the three paths
+    assert plan_ta(8, 16384, 8192)[1]["path"] == gr.GR_PATH_SMALL_M
+    assert plan_ta(4096, 4096, 4096)[1]["path"] == gr.GR_PATH_TILE
+    assert plan_ta(300, 520, 96, ldat=304)[1]["path"] == gr.GR_PATH_TILE
+    st, p = plan_ta(4096, 4096, 4096)
+    assert (p["block_m"], p["block_n"], p["block_k"], p["grid"]) == (256, 256, 32, 256)
+    assert plan_ta(255, 4096, 4096)[1]["path"] == gr.GR_PATH_TILE_EDGE          # M < 256
+    assert plan_ta(4096, 4096, 4100)[1]["path"] == gr.GR_PATH_TILE_EDGE         # K % 32 != 0
+    assert plan_ta(4096, 4096, 4096, ldat=4100)[1]["path"] == gr.GR_PATH_TILE_EDGE  # At rows not 16-byte
+    assert plan_ta(8, 32, 4096)[1]["path"] == gr.GR_PATH_TILE_EDGE              # N < 64
+    assert plan_ta(8, 4096, 4096, ldat=9, b=BASE_B + 2)[1]["path"] == gr.GR_PATH_SMALL_M  # any alignment
+    # argument checks: At is K x M with pitch >= M
+    assert plan_ta(512, 512, 64, ldat=511)[0] == gr.GR_ERR_INVALID_LD
+    assert plan_ta(-1, 512, 64)[0] == gr.GR_ERR_INVALID_DIM
+    assert plan_ta(0, 512, 64)[1]["path"] == gr.GR_PATH_NONE
+    assert gr.gemm_relu_f16_ta(512, 512, 64, 0, 512, BASE_B, 512, BASE_C, 512) == gr.GR_ERR_NULL_PTR
+    assert gr.gemm_relu_f16_ta_forced(4096, 4096, 4100, BASE_A, 4096, BASE_B, 4096, BASE_C, 4096, None,
+                                      gr.GR_PATH_TILE) == gr.GR_ERR_INVALID_PATH
+    assert gr.gemm_relu_f16_ta_forced(4096, 4096, 4096, BASE_A, 4096, BASE_B, 4096, BASE_C, 4096, None,
+                                      gr.GR_PATH_TILE_PACKED) == gr.GR_ERR_INVALID_PATH
+    # C overlapping At
+    assert plan_ta(64, 64, 64, a=BASE_A, c=BASE_A + 64)[0] == gr.GR_ERR_ALIAS
+
+
+def test_stream_read_probe_checks_arguments():
+    """The read-ceiling probe refuses sizes that are not whole 8 MiB granules,
+    null and misaligned pointers and a sink inside the buffer before any HIP
+    call (no GPU needed)."""
+    g = 8 << 20
+    assert gr.gemm_relu_stream_read(BASE_A, g - 16, BASE_C) == gr.GR_ERR_INVALID_ARG
+    assert gr.gemm_relu_stream_read(BASE_A, 0, BASE_C) == gr.GR_ERR_INVALID_ARG
+    assert gr.gemm_relu_stream_read(0, g, BASE_C) == gr.GR_ERR_NULL_PTR
+    assert gr.gemm_relu_stream_read(BASE_A, g, 0) == gr.GR_ERR_NULL_PTR
+    assert gr.gemm_relu_stream_read(BASE_A + 8, g, BASE_C) == gr.GR_ERR_INVALID_ARG
+    assert gr.gemm_relu_stream_read(BASE_A, g, BASE_C + 4) == gr.GR_ERR_INVALID_ARG
+    assert gr.gemm_relu_stream_read(BASE_A, g, BASE_A + 4096) == gr.GR_ERR_ALIAS
+
+
+def test_every_kernel_has_device_code():
+    """Each kernel the host code registers (its launch stub) has a kernel
+    descriptor in the embedded gfx950 code object.  A library whose device
+    pass was compiled from older sources than its host pass would otherwise
+    pass every CPU check and fail only at launch."""
+    with open(gr.LIB_PATH, "rb") as f:
+        data = f.read()
+    toks = set(re.findall(rb"[A-Za-z0-9_.$]{8,}", data))
+    stubs = [t for t in toks if b"__device_stub__" in t]
+    assert len(stubs) > 50
+    missing = []
+    for s in stubs:
+        # the stub's mangled name differs from the kernel's only in its
+        # identifier: <n>__device_stub__name -> <n-15>name
+        k = re.sub(rb"(\d+)__device_stub__", lambda m: str(int(m.group(1)) - 15).encode(), s, count=1)
+        if k + b".kd" not in toks:
+            missing.append(k.decode())
+    assert not missing, missing[:5]
