@@ -38,6 +38,8 @@ GR_PATH_TILE_PACKED = 4
 GR_PATH_SMALL_M_SPLIT = 5
 GR_PATH_TILE_SPLIT = 6
 GR_PATH_TILE_UNALIGNED = 7
+GR_READ_CONTIGUOUS = 0
+GR_READ_ROW_PIECES = 1
 
 GR_ACT_NONE = 0
 GR_ACT_RELU = 1
@@ -132,7 +134,7 @@ def lib() -> ctypes.CDLL:
             l.gemm_relu_f16_ta_plan.restype = i32
             l.gemm_relu_f16_forced_order.argtypes = [i64, i64, i64, p, i64, p, i64, p, i64, p, i32, i32, i32]
             l.gemm_relu_f16_forced_order.restype = i32
-            l.gemm_relu_stream_read.argtypes = [p, i64, p, p]
+            l.gemm_relu_stream_read.argtypes = [p, i64, i32, p, p]
             l.gemm_relu_stream_read.restype = i32
             l.gemm_relu_f16_noalloc.argtypes = [i64, i64, i64, p, i64, p, i64, p, i64, p]
             l.gemm_relu_f16_noalloc.restype = i32
@@ -225,9 +227,10 @@ def gemm_relu_f16_forced_order(M, N, K, A, lda, B, ldb, C, ldc, stream=None, pat
                                             group_m, xcd_remap)
 
 
-def gemm_relu_stream_read(src, nbytes, sink, stream=None) -> int:
-    """Read nbytes (a multiple of 8 MiB) of device memory once: the HBM read-ceiling probe."""
-    return lib().gemm_relu_stream_read(_ptr(src), nbytes, _ptr(sink), _ptr(stream))
+def gemm_relu_stream_read(src, nbytes, sink, stream=None, pattern=0) -> int:
+    """Read nbytes (a multiple of 8 MiB) of device memory once: the HBM
+    read-ceiling probe (pattern GR_READ_CONTIGUOUS or GR_READ_ROW_PIECES)."""
+    return lib().gemm_relu_stream_read(_ptr(src), nbytes, pattern, _ptr(sink), _ptr(stream))
 
 
 def gemm_relu_f16_noalloc(M, N, K, A, lda, B, ldb, C, ldc, stream=None) -> int:

@@ -9,9 +9,12 @@
 #include <hip/hip_runtime.h>
 
 #include <atomic>
+#include <chrono>
 #include <cstdint>
 #include <cstring>
 #include <mutex>
+
+#include <unistd.h>
 
 #include "../../include/gemm_relu.h"
 #include "fp8_kernel.hpp"
@@ -144,6 +147,7 @@ bool smallm_stream_ok(int64_t M, int64_t N, int64_t K, uintptr_t A, int64_t lda,
 // single pass has fewer than 256 strips of 64 columns.
 struct SmallMSplit {
     int64_t splits = 0, k_per_split = 0, n_blocks = 0, bytes = 0;
+    int64_t flags_offset = -1;  // >= 0: two splits summed in one launch, flags at this offset
     bool stream = false;
 };
 constexpr int64_t kSmallMMaxSplits = 64;
@@ -177,8 +181,29 @@ bool smallm_split_layout(int64_t M, int64_t N, int64_t K, uintptr_t A, int64_t l
     q.k_per_split = (ksteps + S - 1) / S * KSTEP;
     q.splits = (K + q.k_per_split - 1) / q.k_per_split;  // no empty split
     q.bytes = (q.splits * M * N * 4 + kWorkspaceAlign - 1) / kWorkspaceAlign * kWorkspaceAlign;
+    if (q.stream && q.splits == 2) {
+        // the streaming kernel sums two splits in the same launch: one 64-bit
+        // flag per column block after the partial sums
+        q.flags_offset = q.bytes;
+        q.bytes += (q.n_blocks * 8 + kWorkspaceAlign - 1) / kWorkspaceAlign * kWorkspaceAlign;
+    }
     *sp = q;
     return true;
+}
+
+// A fresh 64-bit value for every launch that sums two splits in one launch
+// (its workgroups compare it with their column block's flag): splitmix64 of a
+// per-process start (clock and process id) plus a call counter.
+uint64_t next_epoch() {
+    static std::atomic<uint64_t> counter{0};
+    static const uint64_t start = [] {
+        const uint64_t t = (uint64_t)std::chrono::steady_clock::now().time_since_epoch().count();
+        return t * 0x9E3779B97F4A7C15ull ^ ((uint64_t)getpid() << 32);
+    }();
+    uint64_t z = start + counter.fetch_add(1, std::memory_order_relaxed) * 0x9E3779B97F4A7C15ull;
+    z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
+    z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
+    return z ^ (z >> 31);
 }
 
 // Whether the planner takes the split (with a big enough workspace).
@@ -535,10 +560,16 @@ int run(const gr_plan_t& p, int64_t M, int64_t N, int64_t K, const uint16_t* A, 
         case GR_PATH_SMALL_M_SPLIT: {
             using namespace gr::smallm;
             float* part = reinterpret_cast<float*>(ws);
+            if (sp.stream && sp.flags_offset >= 0) {
+                uint64_t* flags = reinterpret_cast<uint64_t*>(ws + sp.flags_offset);
+                return launch(gemm_relu_smallm_stream_kernel<kStreamSplitNB, kStreamSplitW, stream::LAST_OF_TWO, E>,
+                              p.grid, p.threads, stream, A, B, C, part, M, N, K, lda, ldb, ldc, sp.k_per_split,
+                              (uint32_t)sp.n_blocks, ep, flags, next_epoch());
+            }
             if (sp.stream) {
-                const int st = launch(gemm_relu_smallm_stream_kernel<kStreamSplitNB, kStreamSplitW, true, E>,
+                const int st = launch(gemm_relu_smallm_stream_kernel<kStreamSplitNB, kStreamSplitW, stream::PARTIAL, E>,
                                       p.grid, p.threads, stream, A, B, C, part, M, N, K, lda, ldb, ldc,
-                                      sp.k_per_split, (uint32_t)sp.n_blocks, ep);
+                                      sp.k_per_split, (uint32_t)sp.n_blocks, ep, (uint64_t*)nullptr, (uint64_t)0);
                 if (st != GR_OK) return st;
                 return launch_reduce<E>(part, C, M, N, ldc, sp.splits, p.vec_c, ep, stream);
             }
@@ -625,9 +656,9 @@ int run(const gr_plan_t& p, int64_t M, int64_t N, int64_t K, const uint16_t* A, 
             using namespace gr::smallm;
             if (p.vec_b == 8 && M <= MAX_M) {
                 float* no_part = nullptr;
-                return launch(gemm_relu_smallm_stream_kernel<kStreamNB, kStreamW, false, E>, p.grid,
+                return launch(gemm_relu_smallm_stream_kernel<kStreamNB, kStreamW, stream::WHOLE, E>, p.grid,
                               p.threads, stream, A, B, C, no_part, M, N, K, lda, ldb, ldc, K,
-                              (uint32_t)p.grid, ep);
+                              (uint32_t)p.grid, ep, (uint64_t*)nullptr, (uint64_t)0);
             }
             const bool whole = N % NB == 0 && K % KSTEP == 0;
             constexpr int W = kSmallMWaves, U = kSmallMUnroll;
@@ -1079,9 +1110,10 @@ int run_ta(const gr_plan_t& p, int64_t M, int64_t N, int64_t K, const uint16_t* 
         case GR_PATH_NONE: return GR_OK;
         case GR_PATH_SMALL_M: {
             float* no_part = nullptr;
-            return launch(gr::smallm::gemm_relu_smallm_stream_kernel<kStreamNB, kStreamW, false, E, true>,
+            return launch(gr::smallm::gemm_relu_smallm_stream_kernel<kStreamNB, kStreamW, gr::smallm::stream::WHOLE,
+                                                                     E, true>,
                           p.grid, p.threads, stream, At, B, C, no_part, M, N, K, ldat, ldb, ldc, K, (uint32_t)p.grid,
-                          kReluOnly);
+                          kReluOnly, (uint64_t*)nullptr, (uint64_t)0);
         }
         case GR_PATH_TILE: {
             using namespace gr::tile2;
@@ -1788,9 +1820,10 @@ int gemm_relu_f16_noalloc(int64_t M, int64_t N, int64_t K, const uint16_t* A, in
     return entry(M, N, K, A, lda, B, ldb, C, ldc, ws, need, stream, -1);
 }
 
-int gemm_relu_stream_read(const void* src, int64_t bytes, uint64_t* sink, void* stream) {
+int gemm_relu_stream_read(const void* src, int64_t bytes, int pattern, uint64_t* sink, void* stream) {
     using namespace gr::probe;
     if (bytes <= 0 || bytes % GRANULE != 0) return GR_ERR_INVALID_ARG;
+    if (pattern != CONTIGUOUS && pattern != ROW_PIECES) return GR_ERR_INVALID_ARG;
     if (!src || !sink) return GR_ERR_NULL_PTR;
     if (reinterpret_cast<uintptr_t>(src) % 16 != 0 || reinterpret_cast<uintptr_t>(sink) % 8 != 0)
         return GR_ERR_INVALID_ARG;
@@ -1798,9 +1831,10 @@ int gemm_relu_stream_read(const void* src, int64_t bytes, uint64_t* sink, void* 
         return GR_ERR_ALIAS;
     int st = check_device();
     if (st != GR_OK) return st;
-    const int64_t vec_per_wg = bytes / 16 / WGS;
-    return launch(stream_read_kernel, WGS, THREADS, static_cast<hipStream_t>(stream),
-                  reinterpret_cast<const gr::u32x4*>(src), vec_per_wg, sink);
+    const gr::u32x4* s = reinterpret_cast<const gr::u32x4*>(src);
+    if (pattern == ROW_PIECES)
+        return launch(stream_read_kernel<ROW_PIECES>, WGS, THREADS, static_cast<hipStream_t>(stream), s, bytes, sink);
+    return launch(stream_read_kernel<CONTIGUOUS>, WGS, THREADS, static_cast<hipStream_t>(stream), s, bytes, sink);
 }
 
 const char* gemm_relu_status_string(int status) {

@@ -235,15 +235,21 @@ namespace stream {
 
 constexpr int SLOT_ROWS = 32;
 
+// What a workgroup does with its range sum: store C (no split), store the
+// fp32 partial for the ordered second pass, or (two splits) store the
+// partial and let the second workgroup of the column block to finish add both
+// in split order and store C, in the same launch.
+enum Mode { WHOLE = 0, PARTIAL = 1, LAST_OF_TWO = 2 };
+
 __device__ __forceinline__ uint32_t chunk_slot(uint32_t row, uint32_t c) { return c ^ ((row & 3u) << 1); }
 
 }  // namespace stream
 
-template <int NB, int W, bool SPLIT, typename E = ElemF16, bool AT = false>
+template <int NB, int W, int MODE, typename E = ElemF16, bool AT = false>
 __global__ __launch_bounds__(64 * W, 1) void gemm_relu_smallm_stream_kernel(
     const uint16_t* __restrict__ A, const uint16_t* __restrict__ B, uint16_t* __restrict__ C,
     float* __restrict__ part, int64_t M, int64_t N, int64_t K, int64_t lda, int64_t ldb, int64_t ldc,
-    int64_t k_per_split, uint32_t n_blocks, EpiArgs ep) {
+    int64_t k_per_split, uint32_t n_blocks, EpiArgs ep, uint64_t* __restrict__ flags, uint64_t epoch) {
     using tile2::dma16_nt;
     constexpr int ROWB = 2 * NB;                         // bytes of one row piece
     constexpr int CH = NB / 8;                           // 16-byte chunks per row piece
@@ -337,8 +343,44 @@ __global__ __launch_bounds__(64 * W, 1) void gemm_relu_smallm_stream_kernel(
         float v = 0.0f;
 #pragma unroll
         for (int ww = 0; ww < W; ++ww) v += red[ww * (SLOT / 4) + m * NB + nl];
-        if constexpr (SPLIT) part[(s * M + m) * N + n] = v;
-        else C[(int64_t)m * ldc + n] = epi_value<E>(v, n, N, ep);
+        if constexpr (MODE == stream::WHOLE) {
+            C[(int64_t)m * ldc + n] = epi_value<E>(v, n, N, ep);
+        } else if constexpr (MODE == stream::PARTIAL) {
+            part[(s * M + m) * N + n] = v;
+        } else {
+            // agent-scope stores: they bypass this XCD's L2, so the other
+            // workgroup of the block reads them from any XCD
+            __hip_atomic_store(&part[(s * M + m) * N + n], v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            red[m * NB + nl] = v;  // own sum, kept for the last workgroup (wave 0's region)
+        }
+    }
+    if constexpr (MODE == stream::LAST_OF_TWO) {
+        // Every partial store of this workgroup has completed before the
+        // exchange below announces it.  Each call brings a fresh 64-bit epoch:
+        // the workgroup that finds the epoch already in its block's flag
+        // arrives second and owns the sum; the flag's earlier contents
+        // (another call's epoch or anything a caller left) only ever mean
+        // "first", so the flags need no clearing.
+        tile2::wait_vmcnt<0>();
+        __syncthreads();
+        __shared__ uint32_t last;
+        if (tid == 0) {
+            const uint64_t prev = __hip_atomic_exchange(&flags[cb], epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            last = prev == epoch ? 1u : 0u;
+        }
+        __syncthreads();
+        if (last) {
+            for (uint32_t o = tid; o < (uint32_t)(MAX_M * NB); o += T) {
+                const uint32_t m = o / NB, nl = o % NB;
+                const int64_t n = n0 + nl;
+                if ((int64_t)m >= M || n < n_own) continue;
+                const float own = red[m * NB + nl];
+                const float other =
+                    __hip_atomic_load(&part[((1 - s) * M + m) * N + n], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                const float v = s == 0 ? own + other : other + own;  // split order
+                C[(int64_t)m * ldc + n] = epi_value<E>(v, n, N, ep);
+            }
+        }
     }
 }
 

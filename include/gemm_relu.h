@@ -759,17 +759,22 @@ int gemm_relu_f16_noalloc(int64_t M, int64_t N, int64_t K,
 
 /*
  * gemm_relu_stream_read -- a measurement aid, not part of the operation:
- * reads `bytes` bytes of the device buffer `src` once (256 workgroups of 512
- * threads, each streaming one contiguous 1/256 of it with nontemporal
- * 16-byte loads) and writes one 64-bit XOR of each workgroup's words to
- * `sink` (device, 256 x 8 bytes), so that timing it gives the HBM read
- * ceiling a bandwidth-bound path is judged against (the roofline's memory
- * leg; TileLang tutorial, chapter "性能取证", sections "三层归因" and
- * "Roofline 计算器").  bytes: a positive multiple of 8 MiB; src 16-byte and
- * sink 8-byte aligned and disjoint.  Errors: GR_ERR_INVALID_ARG,
- * GR_ERR_NULL_PTR, GR_ERR_ALIAS, device errors.  Enqueues on `stream`.
+ * reads `bytes` bytes of the device buffer `src` once with 256 workgroups of
+ * 512 threads and nontemporal 16-byte loads, and writes the 64-bit XOR of
+ * each workgroup's words to `sink` (device, 256 x 8 bytes), so that timing
+ * it gives the HBM read ceiling a bandwidth-bound path is judged against
+ * (the roofline's memory leg; TileLang tutorial, chapter "性能取证",
+ * sections "三层归因" and "Roofline 计算器").  pattern 0
+ * (GR_READ_CONTIGUOUS): workgroup g reads the g-th contiguous 1/256 of the
+ * buffer; pattern 1 (GR_READ_ROW_PIECES): the buffer as rows of 32 KiB,
+ * workgroup g reads 256-byte piece g % 128 of each row of half g / 128 of
+ * the rows.  bytes: a positive multiple of 8 MiB; src 16-byte and sink
+ * 8-byte aligned and disjoint.  Errors: GR_ERR_INVALID_ARG, GR_ERR_NULL_PTR,
+ * GR_ERR_ALIAS, device errors.  Enqueues on `stream`.
  */
-int gemm_relu_stream_read(const void* src, int64_t bytes, uint64_t* sink, void* stream);
+#define GR_READ_CONTIGUOUS 0
+#define GR_READ_ROW_PIECES 1
+int gemm_relu_stream_read(const void* src, int64_t bytes, int pattern, uint64_t* sink, void* stream);
 
 /* Static, NUL-terminated name of a status code ("GR_OK", "GR_ERR_ALIAS", ...),
  * so that a refused call can be reported with its cause (the fail-loudly

@@ -268,9 +268,10 @@ def test_small_m_split_plan():
     assert plan_ws(8, 4096, 8192, size - 1)[1]["path"] == gr.GR_PATH_SMALL_M
     assert plan(8, 4096, 8192)[1]["path"] == gr.GR_PATH_SMALL_M
     # the small-M workload: 128 column blocks x 2 splits (256-byte row pieces
-    # over half of K each)
+    # over half of K each), summed in the same launch: the two partial sums
+    # and one 8-byte flag per column block (rounded up to 256 bytes)
     st, size = ws_size(8, 16384, 8192)
-    assert size == 2 * 8 * 16384 * 4
+    assert size == 2 * 8 * 16384 * 4 + 1024
     st, p = plan_ws(8, 16384, 8192, size)
     assert (p["path"], p["split_k"], p["grid"], p["block_n"]) == (gr.GR_PATH_SMALL_M_SPLIT, 2, 256, 128)
     # 256 column blocks or more already fill the chip: no workspace asked for
@@ -813,6 +814,8 @@ def test_stream_read_probe_checks_arguments():
     assert gr.gemm_relu_stream_read(BASE_A + 8, g, BASE_C) == gr.GR_ERR_INVALID_ARG
     assert gr.gemm_relu_stream_read(BASE_A, g, BASE_C + 4) == gr.GR_ERR_INVALID_ARG
     assert gr.gemm_relu_stream_read(BASE_A, g, BASE_A + 4096) == gr.GR_ERR_ALIAS
+    assert gr.gemm_relu_stream_read(BASE_A, g, BASE_C, pattern=2) == gr.GR_ERR_INVALID_ARG
+    assert gr.gemm_relu_stream_read(BASE_A, g, BASE_C, pattern=-1) == gr.GR_ERR_INVALID_ARG
 
 
 def test_every_kernel_has_device_code():
