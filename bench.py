@@ -678,6 +678,10 @@ def main():
     ap.add_argument("--workload-settle-ms", type=float, default=100.0,
                     help="clock settling before each variant of the per-workload table")
     ap.add_argument("--no-oracle-table", action="store_true", help="skip the per-workload oracle timings")
+    ap.add_argument("--no-sclk", action="store_true", help="skip the shader-clock reading (counter runs)")
+    ap.add_argument("--rotate", type=int, default=1, metavar="COPIES",
+                    help="the timed steps cycle through this many copies of B (4 x 256 MiB on the small-M "
+                         "workload: every launch streams B from HBM)")
     ap.add_argument("--vendor-reference", action="store_true",
                     help="only time torch.mm + relu_ on the workloads (context, not the product)")
     ap.add_argument("--extra-shapes", action="store_true",
@@ -716,10 +720,15 @@ def main():
 
     w = synth.WORKLOADS[args.workload]
     flops, nbytes = algorithmic(w)
-    A, Bs, C = make_device_operands(torch, w)
+    A, Bs, C = make_device_operands(torch, w, copies=max(1, args.rotate))
     stream = torch.cuda.current_stream()
     ws = workspace_for(gr, torch, w, A, Bs[0], C)
-    run = launcher(gr, torch, w, A, Bs[0], C, stream, ws)
+    runs = [launcher(gr, torch, w, A, B, C, stream, ws) for B in Bs]
+    turn = [0]
+
+    def run():
+        runs[turn[0] % len(runs)]()
+        turn[0] += 1
     plan = plan_for(gr, w, A, Bs[0], C, ws)
 
     settle_launches = settle(torch, run, args.settle_ms)
@@ -752,7 +761,7 @@ def main():
                 "frac": round(achieved / HBM_PEAK_GBS, 4)}
     roof["traffic"] = traffic_for(args.workload, src_hash)
     roof["kernel_avg_us"] = round(ev_ms * 1e3, 2)
-    sclk = observed_sclk(torch, run)
+    sclk = None if args.no_sclk else observed_sclk(torch, run)
     if sclk and dominant_bound == "mfma":
         # the same achieved rate against the peak at the clock the chip held
         roof["observed_sclk_mhz"] = sclk
@@ -760,7 +769,7 @@ def main():
         roof["frac_at_observed_sclk"] = round(achieved / peak_at_sclk, 4)
     roof["algorithmic_flops"] = flops
     roof["algorithmic_bytes"] = nbytes
-    del A, Bs, C, ws, run
+    del A, Bs, C, ws, run, runs
     torch.cuda.empty_cache()
 
     out = {
@@ -779,6 +788,7 @@ def main():
         "dtype": "f16",
         "data": "synthetic",
         "config": {"workload": w.name, "M": w.M, "N": w.N, "K": w.K, "layout": "row-major A(MxK) B(KxN) C(MxN)",
+                   "b_copies_rotated": max(1, args.rotate),
                    "accumulate": "fp32", "path": plan["path_name"],
                    "tile": [plan["block_m"], plan["block_n"], plan["block_k"]], "grid": plan["grid"],
                    "threads": plan["threads"], "workspace_bytes": plan["workspace"],
