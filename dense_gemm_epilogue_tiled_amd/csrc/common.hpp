@@ -592,6 +592,55 @@ __device__ __forceinline__ void store_wave_tile(Acc& acc, uint8_t* region, uint3
     }
 }
 
+// ReLU(acc) of a 128 x 128 wave tile (8 x 8 blocks of 16 x 16) stored 32
+// rows at a time through an 8 KiB LDS region of the wave's own, for the
+// persistent tile loop, which keeps the rest of LDS for the next tile's
+// copies.  Whole tiles, 16-byte aligned rows of C.  Each round: block rows
+// 2r and 2r+1 packed to fp16 into the region (layout of a 32 x 128 wave
+// tile), read back as 16-byte row segments, four rows per instruction, and
+// written with nontemporal stores.  The region is the wave's alone and a
+// wave's LDS operations complete in order, so no barrier is needed.
+constexpr uint32_t ROWS32_BYTES = WaveTile<1, 4>::REGION_BYTES;  // 8 KiB
+
+template <typename E, int BM, int BN>
+__device__ __forceinline__ void store_wave_tile_rows32(const f32x4 (&acc)[BM][BN], uint8_t* region, uint32_t lane,
+                                                       uint16_t* __restrict__ C, int64_t ldc, int64_t row0,
+                                                       int64_t col0) {
+    static_assert(BM == 8 && BN == 8, "a 128 x 128 wave tile of 16 x 16 blocks");
+    using T = WaveTile<1, 4>;
+    constexpr uint32_t ROWS_PER = 64u / T::CHUNKS;  // 4
+    // Called once per tile of a loop: computing the lane's addresses here,
+    // and not once before the loop, keeps them from living (and spilling)
+    // through the main loop.
+    asm volatile("" : "+v"(lane));
+    const uint32_t r = lane & 15u, g = lane >> 4;
+    const uint32_t ch = lane & (T::CHUNKS - 1);
+#pragma unroll
+    for (int round = 0; round < BM / 2; ++round) {
+#pragma unroll
+        for (int ii = 0; ii < 2; ++ii) {
+            const uint32_t row = 16u * ii + r;
+#pragma unroll
+            for (int j = 0; j < BN; ++j) {
+                const f32x4& a = acc[2 * round + ii][j];
+                u32x2 p;
+                p[0] = relu_pack2_e<E>(a[0], a[1]);
+                p[1] = relu_pack2_e<E>(a[2], a[3]);
+                *reinterpret_cast<u32x2*>(region + T::off(row, 2u * j + (g >> 1)) + 8u * T::half_slot(row, g & 1u)) =
+                    p;
+            }
+        }
+#pragma unroll
+        for (uint32_t k = 0; k < 32u / ROWS_PER; ++k) {
+            const uint32_t row = ROWS_PER * k + (lane >> T::SHIFT);
+            u32x4 v = *reinterpret_cast<const u32x4*>(region + T::off(row, ch));
+            if ((row >> T::SHIFT) & 1u) v = u32x4{v[2], v[3], v[0], v[1]};
+            uint16_t* dst = C + (row0 + 32 * round + row) * ldc + col0 + 8 * ch;
+            __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(dst));
+        }
+    }
+}
+
 }  // namespace epi
 
 }  // namespace gr

@@ -223,6 +223,16 @@ bool tile_fast_ok(int64_t M, int64_t N, int64_t K, uintptr_t A, int64_t lda, uin
            lda <= MAX_LDA && ldb <= MAX_LDB;
 }
 
+// The persistent tile loop: whole 256 x 256 tiles, K % 64 == 0 (the 64-deep
+// A strips), 16-byte rows of C (its 32-row epilogue writes 16-byte segments).
+constexpr int64_t kPersistentWorkgroups = 256;  // one per CU
+bool tile_persistent_ok(int64_t M, int64_t N, int64_t K, uintptr_t A, int64_t lda, uintptr_t B, int64_t ldb,
+                        uintptr_t C, int64_t ldc) {
+    using namespace gr::tile3;
+    return tile_fast_ok(M, N, K, A, lda, B, ldb) && M % BM == 0 && N % BN == 0 && K % BKA == 0 &&
+           vec_width_c(C, ldc) == 8;
+}
+
 // The pipelined 256 x 256 kernel in place on misaligned rows and a K that
 // is no multiple of 64 (tile3's UA variant): M and N of at least one tile
 // (the last tile row and column move to end at M and N), K > 128 (the tail
@@ -331,7 +341,7 @@ void fill_plan(int path, int64_t M, int64_t N, int64_t K, uintptr_t A, int64_t l
                int64_t ldc, const Pack& pk, const SmallMSplit& sp, const TileSplit& ts, gr_plan_t* p) {
     std::memset(p, 0, sizeof(*p));
     p->path = path;
-    if (path == GR_PATH_TILE_UNALIGNED) {
+    if (path == GR_PATH_TILE_UNALIGNED || path == GR_PATH_TILE_PERSISTENT) {
         using namespace gr::tile3;
         p->block_m = BM;
         p->block_n = BN;
@@ -339,6 +349,7 @@ void fill_plan(int path, int64_t M, int64_t N, int64_t K, uintptr_t A, int64_t l
         p->stages = B_SLOTS;
         p->threads = THREADS;
         p->grid = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
+        if (path == GR_PATH_TILE_PERSISTENT && p->grid > kPersistentWorkgroups) p->grid = kPersistentWorkgroups;
         p->vec_a = vec_width(A, lda);
         p->vec_b = vec_width(B, ldb);
         p->vec_c = vec_width_c(C, ldc);
@@ -639,6 +650,19 @@ int run(const gr_plan_t& p, int64_t M, int64_t N, int64_t K, const uint16_t* A, 
             return launch(gemm_relu_tile2_kernel<true, false, E>, p.grid, THREADS, stream, A, B, C, M, N, K, lda, ldb,
                           ldc, tiles_m, tiles_n, gm, vc, ep);
         }
+        case GR_PATH_TILE_PERSISTENT: {
+            using namespace gr::tile3;
+            const uint32_t tiles_m = (uint32_t)(M / BM), tiles_n = (uint32_t)(N / BN);
+            if constexpr (E::kGeneral) {
+                // the bias + activation epilogue stages fp32 blocks through
+                // all of LDS: the same tiles, one workgroup each
+                return launch(gemm_relu_tile3_kernel<false, E>, (int64_t)tiles_m * tiles_n, THREADS, stream, A, B, C,
+                              M, N, K, lda, ldb, ldc, tiles_m, tiles_n, (uint32_t)p.group_m, (int)p.vec_c, ep);
+            } else {
+                return launch(gemm_relu_tile3_kernel<false, E, false, true>, p.grid, THREADS, stream, A, B, C, M, N,
+                              K, lda, ldb, ldc, tiles_m, tiles_n, (uint32_t)p.group_m, (int)p.vec_c, ep);
+            }
+        }
         case GR_PATH_TILE_UNALIGNED: {
             using namespace gr::tile3;
             const uint32_t tiles_m = (uint32_t)((M + BM - 1) / BM);
@@ -704,6 +728,8 @@ int plan_call(int64_t M, int64_t N, int64_t K, uintptr_t a, int64_t lda, uintptr
             if (!tile_fast_ok(M, N, K, a, lda, b, ldb)) return GR_ERR_INVALID_PATH;
         } else if (forced == GR_PATH_TILE_UNALIGNED) {
             if (!tile_unaligned_ok(M, N, K, lda, ldb)) return GR_ERR_INVALID_PATH;
+        } else if (forced == GR_PATH_TILE_PERSISTENT) {
+            if (!tile_persistent_ok(M, N, K, a, lda, b, ldb, c, ldc)) return GR_ERR_INVALID_PATH;
         } else if (forced == GR_PATH_SMALL_M) {
             if (K == 0 || !(smallm_rows_ok(M, N, K, a, lda, b, ldb) || smallm_stream_ok(M, N, K, a, lda, ldb, kStreamNB)))
                 return GR_ERR_INVALID_PATH;
@@ -798,7 +824,7 @@ int entry_epi(int64_t M, int64_t N, int64_t K, const uint16_t* A, int64_t lda, c
 bool known_path(int path) {
     return path == GR_PATH_TILE || path == GR_PATH_TILE_EDGE || path == GR_PATH_SMALL_M ||
            path == GR_PATH_TILE_PACKED || path == GR_PATH_SMALL_M_SPLIT || path == GR_PATH_TILE_SPLIT ||
-           path == GR_PATH_TILE_UNALIGNED;
+           path == GR_PATH_TILE_UNALIGNED || path == GR_PATH_TILE_PERSISTENT;
 }
 
 bool needs_workspace(int path) {
@@ -1530,7 +1556,7 @@ int gemm_relu_bf16(int64_t M, int64_t N, int64_t K, const uint16_t* A, int64_t l
 
 int gemm_relu_bf16_forced(int64_t M, int64_t N, int64_t K, const uint16_t* A, int64_t lda, const uint16_t* B,
                           int64_t ldb, uint16_t* C, int64_t ldc, void* stream, int path) {
-    if (path != GR_PATH_TILE && path != GR_PATH_TILE_EDGE && path != GR_PATH_SMALL_M) return GR_ERR_INVALID_PATH;
+    if (!known_path(path) || needs_workspace(path)) return GR_ERR_INVALID_PATH;
     return entry_bf16(M, N, K, A, lda, B, ldb, C, ldc, nullptr, 0, stream, path);
 }
 
@@ -1554,8 +1580,7 @@ int gemm_bias_act_f16(int64_t M, int64_t N, int64_t K, const uint16_t* A, int64_
 int gemm_bias_act_f16_forced(int64_t M, int64_t N, int64_t K, const uint16_t* A, int64_t lda, const uint16_t* B,
                              int64_t ldb, const uint16_t* bias, int act, uint16_t* C, int64_t ldc, void* stream,
                              int path) {
-    if (path != GR_PATH_TILE && path != GR_PATH_TILE_EDGE && path != GR_PATH_SMALL_M && path != GR_PATH_TILE_UNALIGNED)
-        return GR_ERR_INVALID_PATH;
+    if (!known_path(path) || needs_workspace(path)) return GR_ERR_INVALID_PATH;
     return entry_epi<gr::ElemF16>(M, N, K, A, lda, B, ldb, bias, act, C, ldc, nullptr, 0, stream, path);
 }
 
@@ -1567,8 +1592,7 @@ int gemm_bias_act_bf16(int64_t M, int64_t N, int64_t K, const uint16_t* A, int64
 int gemm_bias_act_bf16_forced(int64_t M, int64_t N, int64_t K, const uint16_t* A, int64_t lda, const uint16_t* B,
                               int64_t ldb, const uint16_t* bias, int act, uint16_t* C, int64_t ldc, void* stream,
                               int path) {
-    if (path != GR_PATH_TILE && path != GR_PATH_TILE_EDGE && path != GR_PATH_SMALL_M && path != GR_PATH_TILE_UNALIGNED)
-        return GR_ERR_INVALID_PATH;
+    if (!known_path(path) || needs_workspace(path)) return GR_ERR_INVALID_PATH;
     return entry_epi<gr::ElemBF16>(M, N, K, A, lda, B, ldb, bias, act, C, ldc, nullptr, 0, stream, path);
 }
 

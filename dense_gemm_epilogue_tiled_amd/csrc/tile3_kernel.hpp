@@ -93,7 +93,21 @@ __device__ __forceinline__ u32x4 load8_guarded(const uint16_t* p, int64_t valid,
 // [T, K) of A and [T, K) x [0, N) of B: nothing outside the operands is ever
 // read, whatever their alignment.  Tail first means a different k order
 // than the aligned kernels (a different fp32 rounding order, equally valid).
-template <bool EDGE, typename E = ElemF16, bool UA = false>
+//
+// PERSIST (whole tiles, 16-byte rows of C, the fp16/bf16 ReLU epilogue): a
+// persistent tile loop, the TileLang tutorial's "Persistent kernel": the
+// grid holds at most one workgroup per CU and workgroup g takes the tiles
+// of the logical ids g, g + grid, g + 2 grid, ... (the XCD renumbering and
+// tile-row groups of tile_of_workgroup apply to the logical ids).  When a
+// tile's last step is done, the workgroup issues the next tile's first
+// copies (A strips 0 and 1, B strips 0 to 2: every slot but A slot 2) before
+// it stores the finished tile, 32 rows at a time through an 8 KiB region per
+// wave in A slot 2; the copies' latency, the launch of a new workgroup and
+// the stores overlap.  The copy waits stay those of the first tile: the
+// copies complete in order among themselves, so "at most n operations
+// outstanding" still means "all but the last n copies landed" when stores
+// are outstanding as well (it then waits a little longer).
+template <bool EDGE, typename E = ElemF16, bool UA = false, bool PERSIST = false>
 __global__ __launch_bounds__(THREADS, 1) void gemm_relu_tile3_kernel(
     const uint16_t* __restrict__ A, const uint16_t* __restrict__ B, uint16_t* __restrict__ C, int64_t M, int64_t N,
     int64_t K, int64_t lda, int64_t ldb, int64_t ldc, uint32_t tiles_m, uint32_t tiles_n, uint32_t group_m,
@@ -115,12 +129,15 @@ __global__ __launch_bounds__(THREADS, 1) void gemm_relu_tile3_kernel(
     const uint32_t wn = wave & 1u;
 
     static_assert(!UA || EDGE, "the unaligned variant moves edge tiles");
+    static_assert(!PERSIST || (!EDGE && !UA && !E::kGeneral), "the persistent loop takes whole tiles, ReLU");
+    const uint32_t n_tiles = tiles_m * tiles_n;
+    uint32_t vt = blockIdx.x;  // logical workgroup id (PERSIST: of the current tile)
     uint32_t tm, tn;
-    tile_of_workgroup(blockIdx.x, gridDim.x, tiles_m, tiles_n, group_m, tm, tn);
+    tile_of_workgroup(vt, PERSIST ? n_tiles : gridDim.x, tiles_m, tiles_n, group_m, tm, tn);
     const int64_t m_tile = (int64_t)tm * BM;
-    const int64_t m0 = EDGE ? edge::shifted_row0(m_tile, M, BM) : m_tile;
+    int64_t m0 = EDGE ? edge::shifted_row0(m_tile, M, BM) : m_tile;
     const int64_t n_tile = (int64_t)tn * BN;
-    const int64_t n0 = UA ? edge::shifted_col0(n_tile, N, BN) : n_tile;
+    int64_t n0 = UA ? edge::shifted_col0(n_tile, N, BN) : n_tile;
     // UA: the K tail handled first (1..64 deep); the pipeline covers [T, K).
     const int64_t T = UA ? (K - 1) % BKA + 1 : 0;
 
@@ -131,7 +148,7 @@ __global__ __launch_bounds__(THREADS, 1) void gemm_relu_tile3_kernel(
     // B strip (16 KiB) = 16 blocks of 2 rows x 512 bytes; this wave fills
     // blocks 4w .. 4w+3.  lane -> row lane/32, slot lane%32.
     const uint8_t* base_a = reinterpret_cast<const uint8_t*>(A + m0 * lda + T);
-    const uint8_t* base_b = reinterpret_cast<const uint8_t*>(B + T * ldb + n0);
+    const uint8_t* base_b = reinterpret_cast<const uint8_t*>(B + T * ldb + n0);  // PERSIST: next tile's later
     const int64_t step_a = BKA * 2;
     const int64_t step_b = (int64_t)BK * ldb * 2;
     // The odd-step half (blocks +4, rows +32) only adds a wave-uniform
@@ -182,10 +199,10 @@ __global__ __launch_bounds__(THREADS, 1) void gemm_relu_tile3_kernel(
     // address bits 5-7 together with the XOR term: block j's address is
     // block 0's XOR 32j.
     const GR_LDS uint8_t* lds_p = (const GR_LDS uint8_t*)lds;
-    const uint32_t a_addr = (uint32_t)(uintptr_t)(lds_p + A_BASE + a64_off(wm * WAVE_TM + (lane & 15u), lane >> 4));
+    uint32_t a_addr = (uint32_t)(uintptr_t)(lds_p + A_BASE + a64_off(wm * WAVE_TM + (lane & 15u), lane >> 4));
     const uint32_t bk = 8u * (lane >> 4) + ((lane & 15u) >> 2);
     const uint32_t bn = wn * WAVE_TN + 4u * (lane & 3u);
-    const uint32_t b_addr = (uint32_t)(uintptr_t)(lds_p + b_off(bk, bn >> 3) + 2u * (bn & 7u));
+    uint32_t b_addr = (uint32_t)(uintptr_t)(lds_p + b_off(bk, bn >> 3) + 2u * (bn & 7u));
 
     f32x4 acc[FM][FN];
 #pragma unroll
@@ -238,22 +255,31 @@ __global__ __launch_bounds__(THREADS, 1) void gemm_relu_tile3_kernel(
     }
 
     // Prologue copies, in this order: A0, B0, B1, A1, B2.
+    auto prologue_a0_b0_b1_a1 = [&]() {
 #pragma unroll
-    for (int c = 0; c < 4; ++c) dma_a(0, 0, c);
+        for (int c = 0; c < 4; ++c) dma_a(0, 0, c);
 #pragma unroll
-    for (int c = 0; c < 4; ++c) dma_a(0, 1, c);
+        for (int c = 0; c < 4; ++c) dma_a(0, 1, c);
 #pragma unroll
-    for (int c = 0; c < 4; ++c) dma_b(0, c);
-    if (KT > 1) {
+        for (int c = 0; c < 4; ++c) dma_b(0, c);
+        if (KT > 1) {
 #pragma unroll
-        for (int c = 0; c < 4; ++c) dma_b(1, c);
-    }
-    if (KTA > 1) {
+            for (int c = 0; c < 4; ++c) dma_b(1, c);
+        }
+        if (KTA > 1) {
 #pragma unroll
-        for (int c = 0; c < 4; ++c) dma_a(1, 0, c);
+            for (int c = 0; c < 4; ++c) dma_a(1, 0, c);
 #pragma unroll
-        for (int c = 0; c < 4; ++c) dma_a(1, 1, c);
-    }
+            for (int c = 0; c < 4; ++c) dma_a(1, 1, c);
+        }
+    };
+    auto prologue_b2 = [&]() {
+        if (KT > 2) {
+#pragma unroll
+            for (int c = 0; c < 4; ++c) dma_b(2, c);
+        }
+    };
+    prologue_a0_b0_b1_a1();
     if constexpr (UA) {
         // The tail's loads have landed once at most the 24 copies above
         // (A0, B0, B1, A1) remain.  A tail -> A slot 2, B tail -> B slots 3
@@ -286,23 +312,7 @@ __global__ __launch_bounds__(THREADS, 1) void gemm_relu_tile3_kernel(
         // every wave is done with B slot 2 before B strip 2 is copied into it
         __syncthreads();
     }
-    if (KT > 2) {
-#pragma unroll
-        for (int c = 0; c < 4; ++c) dma_b(2, c);
-    }
-    // A0 and B0 landed: the copies after them may stay in flight.
-    {
-        const uint32_t after = 4u * (KT > 1) + 8u * (KTA > 1) + 4u * (KT > 2);
-        if (after == 16) wait_vmcnt<16>();
-        else if (after == 12) wait_vmcnt<12>();
-        else if (after == 4) wait_vmcnt<4>();
-        else wait_vmcnt<0>();
-    }
-    barrier();
-
-    Frags f0, f1;
-#pragma unroll
-    for (int r = 0; r < 16; ++r) read_one(H0{}, f0, a_slot(0), b_slot(0), r);
+    prologue_b2();
 
     // Copies issued in step s (the A half, then the B strip).
     auto issue_step = [&](uint32_t s) {
@@ -317,6 +327,30 @@ __global__ __launch_bounds__(THREADS, 1) void gemm_relu_tile3_kernel(
         }
     };
     auto n_issued = [&](uint32_t s) -> uint32_t { return 4u * ((s >> 1) + 2 < KTA) + 4u * (s + 3 < KT); };
+
+    for (;;) {  // one tile per pass; only PERSIST comes back
+    if constexpr (PERSIST) {
+        // The per-lane copy offsets and fragment addresses are the same for
+        // every tile.  Marking them as redefined here keeps the compiler from
+        // hoisting the many addresses it derives from them out of the tile
+        // loop, where they would stay live through the epilogue and spill.
+#pragma unroll
+        for (int i = 0; i < 4; ++i) asm volatile("" : "+v"(off_a[i]), "+v"(off_b[i]));
+        asm volatile("" : "+v"(a_addr), "+v"(b_addr));
+    }
+    // A0 and B0 landed: the copies after them may stay in flight.
+    {
+        const uint32_t after = 4u * (KT > 1) + 8u * (KTA > 1) + 4u * (KT > 2);
+        if (after == 16) wait_vmcnt<16>();
+        else if (after == 12) wait_vmcnt<12>();
+        else if (after == 4) wait_vmcnt<4>();
+        else wait_vmcnt<0>();
+    }
+    barrier();
+
+    Frags f0, f1;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) read_one(H0{}, f0, a_slot(0), b_slot(0), r);
 
     // Steady step: every copy of step kt exists and the wait is "only the
     // previous step's 8 copies may remain".  8 MFMAs, wait + barrier, then
@@ -405,10 +439,39 @@ __global__ __launch_bounds__(THREADS, 1) void gemm_relu_tile3_kernel(
     step_any(kt + 4, f1, f0);
     step_any(kt + 5, f0, f1);
 
-    // Epilogue: ReLU, fp16 and the store of C, staged through LDS (the
-    // operand ring is no longer needed).
-    epi::store_wave_tile<EDGE, E>(acc, lds + wave * epi::REGION_BYTES, lane, C, ldc, m0 + wm * WAVE_TM,
-                               n0 + wn * WAVE_TN, m_tile, M, N, vec_c, ep, n_tile);
+    if constexpr (PERSIST) {
+        // Every wave is done with the operand slots (its last fragment reads
+        // were consumed by its MFMAs): the next tile's first copies may go
+        // out, then this tile is stored through A slot 2, which they leave
+        // alone (the next tile's step 0 copies into it after its barrier).
+        const int64_t c_row = m0 + wm * WAVE_TM, c_col = n0 + wn * WAVE_TN;
+        barrier();
+        const uint32_t next = vt + gridDim.x;
+        if (next < n_tiles) {
+            vt = next;
+            tile_of_workgroup(vt, n_tiles, tiles_m, tiles_n, group_m, tm, tn);
+            m0 = (int64_t)tm * BM;
+            n0 = (int64_t)tn * BN;
+            base_a = reinterpret_cast<const uint8_t*>(A + m0 * lda);
+            base_b = reinterpret_cast<const uint8_t*>(B + n0);
+            prologue_a0_b0_b1_a1();
+            prologue_b2();
+        }
+        epi::store_wave_tile_rows32<E>(acc, lds + A_BASE + 2 * A_SLOT_BYTES + wave * epi::ROWS32_BYTES, lane, C,
+                                       ldc, c_row, c_col);
+        if (next >= n_tiles) break;
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+#pragma unroll
+            for (int j = 0; j < FN; ++j) acc[i][j] = f32x4{};
+    } else {
+        // Epilogue: ReLU, fp16 and the store of C, staged through LDS (the
+        // operand ring is no longer needed).
+        epi::store_wave_tile<EDGE, E>(acc, lds + wave * epi::REGION_BYTES, lane, C, ldc, m0 + wm * WAVE_TM,
+                                   n0 + wn * WAVE_TN, m_tile, M, N, vec_c, ep, n_tile);
+        break;
+    }
+    }  // tile loop
 }
 
 #undef GR_LDS

@@ -107,6 +107,11 @@ extern "C" {
                                  /* copies from any 2-byte address, the K tail (1..64)    */
                                  /* staged with guards first; M, N >= 256, K > 128, more  */
                                  /* than 128 tiles (planner); no workspace                 */
+#define GR_PATH_TILE_PERSISTENT 8 /* the pipelined 256x256 kernel as a persistent tile loop: */
+                                  /* at most one workgroup per CU, each storing a finished */
+                                  /* tile while the next tile's first copies are in flight */
+                                  /* (TileLang tutorial, "Persistent kernel"); whole tiles, */
+                                  /* K % 64 == 0, 16-byte rows of A, B and C               */
 
 /* What the planner decided for one problem.  Filled by gemm_relu_f16_plan. */
 typedef struct gr_plan_t {
@@ -417,9 +422,9 @@ int gemm_relu_bf16(int64_t M, int64_t N, int64_t K,
                    uint16_t* C, int64_t ldc,
                    void* stream);
 
-/* gemm_relu_bf16 on a given path (GR_PATH_TILE, GR_PATH_TILE_EDGE or
-   GR_PATH_SMALL_M; GR_ERR_INVALID_PATH for any other path, or when the path's
-   conditions do not hold).  Test hook. */
+/* gemm_relu_bf16 on a given path (any path that needs no workspace;
+   GR_ERR_INVALID_PATH for the others, or when the path's conditions do not
+   hold).  Test hook. */
 int gemm_relu_bf16_forced(int64_t M, int64_t N, int64_t K,
                           const uint16_t* A, int64_t lda,
                           const uint16_t* B, int64_t ldb,
@@ -492,9 +497,11 @@ int gemm_bias_act_bf16(int64_t M, int64_t N, int64_t K,
                        uint16_t* C, int64_t ldc,
                        void* stream);
 
-/* The two calls above on a given path (GR_PATH_TILE, GR_PATH_TILE_UNALIGNED,
-   GR_PATH_TILE_EDGE or GR_PATH_SMALL_M; GR_ERR_INVALID_PATH otherwise or when
-   the path's conditions do not hold).  Test hooks. */
+/* The two calls above on a given path (any path that needs no workspace;
+   GR_PATH_TILE_PERSISTENT runs the same tiles one workgroup each, since the
+   bias + activation epilogue stages fp32 blocks through all of LDS;
+   GR_ERR_INVALID_PATH for the others or when the path's conditions do not
+   hold).  Test hooks. */
 int gemm_bias_act_f16_forced(int64_t M, int64_t N, int64_t K,
                              const uint16_t* A, int64_t lda,
                              const uint16_t* B, int64_t ldb,

@@ -836,3 +836,17 @@ def test_every_kernel_has_device_code():
         if k + b".kd" not in toks:
             missing.append(k.decode())
     assert not missing, missing[:5]
+
+
+def test_persistent_path_checks():
+    """The persistent tile loop takes whole tiles, K % 64 == 0 and 16-byte
+    rows of A, B and C; anything else is refused before any HIP call."""
+    base = (0x100000, 0x200000000000, 0x400000000000)
+
+    def forced(M, N, K, lda, ldb, ldc, a=base[0], b=base[1], c=base[2]):
+        return gr.gemm_relu_f16_forced(M, N, K, a, lda, b, ldb, c, ldc, None, gr.GR_PATH_TILE_PERSISTENT)
+    assert forced(4096, 4100, 256, 256, 4100, 4100) == gr.GR_ERR_INVALID_PATH   # N not whole tiles
+    assert forced(4000, 4096, 256, 256, 4096, 4096) == gr.GR_ERR_INVALID_PATH   # M not whole tiles
+    assert forced(4096, 4096, 96, 96, 4096, 4096) == gr.GR_ERR_INVALID_PATH     # K % 64 != 0
+    assert forced(4096, 4096, 256, 256, 4096, 4100) == gr.GR_ERR_INVALID_PATH   # rows of C not 16-byte
+    assert forced(4096, 4096, 256, 260, 4096, 4096) == gr.GR_ERR_INVALID_PATH   # rows of A not 16-byte
