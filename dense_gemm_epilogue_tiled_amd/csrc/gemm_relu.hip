@@ -9,12 +9,9 @@
 #include <hip/hip_runtime.h>
 
 #include <atomic>
-#include <chrono>
 #include <cstdint>
 #include <cstring>
 #include <mutex>
-
-#include <unistd.h>
 
 #include "../../include/gemm_relu.h"
 #include "fp8_kernel.hpp"
@@ -131,8 +128,9 @@ bool smallm_rows_ok(int64_t M, int64_t N, int64_t K, uintptr_t A, int64_t lda, u
 // column block of nb.  Without a split it runs with 64-column blocks; the
 // split uses 128-column blocks (256-byte row pieces, the faster read
 // pattern, measured 6.5 TB/s for the first pass at 8 x 16384 x 8192).
-constexpr int kStreamNB = 64, kStreamW = 8;         // single pass: 64-column blocks, 8 waves
-constexpr int kStreamSplitNB = 128, kStreamSplitW = 4;  // split first pass: 128-column blocks, 4 waves
+constexpr int kStreamNB = 64, kStreamW = 4, kStreamR = 2;  // single pass: 64-column blocks, 4 waves x 2 slots
+constexpr int kStreamSplitNB = 128, kStreamSplitW = 2, kStreamSplitR = 2;  // split: 128 columns, 2 waves x 2 slots
+constexpr int kStreamTaW = 8;  // A given transposed (gathered into registers): 8 waves x 1 slot
 bool smallm_stream_ok(int64_t M, int64_t N, int64_t K, uintptr_t A, int64_t lda, int64_t ldb, int64_t nb) {
     return M >= 1 && M <= kSmallMThreshold && K > 0 && K % 32 == 0 && A % 16 == 0 && lda % 8 == 0 && N >= nb &&
            ldb <= gr::tile2::MAX_LDB;
@@ -147,7 +145,6 @@ bool smallm_stream_ok(int64_t M, int64_t N, int64_t K, uintptr_t A, int64_t lda,
 // single pass has fewer than 256 strips of 64 columns.
 struct SmallMSplit {
     int64_t splits = 0, k_per_split = 0, n_blocks = 0, bytes = 0;
-    int64_t flags_offset = -1;  // >= 0: two splits summed in one launch, flags at this offset
     bool stream = false;
 };
 constexpr int64_t kSmallMMaxSplits = 64;
@@ -166,7 +163,7 @@ bool smallm_split_layout(int64_t M, int64_t N, int64_t K, uintptr_t A, int64_t l
     if (smallm_stream_ok(M, N, K, A, lda, ldb, kStreamSplitNB)) {
         q.stream = true;
         nb = kStreamSplitNB;
-        min_steps = kStreamSplitW;  // one slot per wave
+        min_steps = kStreamSplitW * kStreamSplitR;  // a full ring per wave
     } else if (smallm_ok(M, N, K, A, lda, B, ldb) && B % 16 == 0 && ldb % 8 == 0) {
         nb = SPLIT_NB;
         min_steps = 2;
@@ -181,29 +178,8 @@ bool smallm_split_layout(int64_t M, int64_t N, int64_t K, uintptr_t A, int64_t l
     q.k_per_split = (ksteps + S - 1) / S * KSTEP;
     q.splits = (K + q.k_per_split - 1) / q.k_per_split;  // no empty split
     q.bytes = (q.splits * M * N * 4 + kWorkspaceAlign - 1) / kWorkspaceAlign * kWorkspaceAlign;
-    if (q.stream && q.splits == 2) {
-        // the streaming kernel sums two splits in the same launch: one 64-bit
-        // flag per column block after the partial sums
-        q.flags_offset = q.bytes;
-        q.bytes += (q.n_blocks * 8 + kWorkspaceAlign - 1) / kWorkspaceAlign * kWorkspaceAlign;
-    }
     *sp = q;
     return true;
-}
-
-// A fresh 64-bit value for every launch that sums two splits in one launch
-// (its workgroups compare it with their column block's flag): splitmix64 of a
-// per-process start (clock and process id) plus a call counter.
-uint64_t next_epoch() {
-    static std::atomic<uint64_t> counter{0};
-    static const uint64_t start = [] {
-        const uint64_t t = (uint64_t)std::chrono::steady_clock::now().time_since_epoch().count();
-        return t * 0x9E3779B97F4A7C15ull ^ ((uint64_t)getpid() << 32);
-    }();
-    uint64_t z = start + counter.fetch_add(1, std::memory_order_relaxed) * 0x9E3779B97F4A7C15ull;
-    z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
-    z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
-    return z ^ (z >> 31);
 }
 
 // Whether the planner takes the split (with a big enough workspace).
@@ -571,16 +547,11 @@ int run(const gr_plan_t& p, int64_t M, int64_t N, int64_t K, const uint16_t* A, 
         case GR_PATH_SMALL_M_SPLIT: {
             using namespace gr::smallm;
             float* part = reinterpret_cast<float*>(ws);
-            if (sp.stream && sp.flags_offset >= 0) {
-                uint64_t* flags = reinterpret_cast<uint64_t*>(ws + sp.flags_offset);
-                return launch(gemm_relu_smallm_stream_kernel<kStreamSplitNB, kStreamSplitW, stream::LAST_OF_TWO, E>,
-                              p.grid, p.threads, stream, A, B, C, part, M, N, K, lda, ldb, ldc, sp.k_per_split,
-                              (uint32_t)sp.n_blocks, ep, flags, next_epoch());
-            }
             if (sp.stream) {
-                const int st = launch(gemm_relu_smallm_stream_kernel<kStreamSplitNB, kStreamSplitW, stream::PARTIAL, E>,
-                                      p.grid, p.threads, stream, A, B, C, part, M, N, K, lda, ldb, ldc,
-                                      sp.k_per_split, (uint32_t)sp.n_blocks, ep, (uint64_t*)nullptr, (uint64_t)0);
+                const int st = launch(
+                    gemm_relu_smallm_stream_kernel<kStreamSplitNB, kStreamSplitW, kStreamSplitR, stream::PARTIAL, E>,
+                    p.grid, p.threads, stream, A, B, C, part, M, N, K, lda, ldb, ldc, sp.k_per_split,
+                    (uint32_t)sp.n_blocks, ep);
                 if (st != GR_OK) return st;
                 return launch_reduce<E>(part, C, M, N, ldc, sp.splits, p.vec_c, ep, stream);
             }
@@ -680,9 +651,8 @@ int run(const gr_plan_t& p, int64_t M, int64_t N, int64_t K, const uint16_t* A, 
             using namespace gr::smallm;
             if (p.vec_b == 8 && M <= MAX_M) {
                 float* no_part = nullptr;
-                return launch(gemm_relu_smallm_stream_kernel<kStreamNB, kStreamW, stream::WHOLE, E>, p.grid,
-                              p.threads, stream, A, B, C, no_part, M, N, K, lda, ldb, ldc, K,
-                              (uint32_t)p.grid, ep, (uint64_t*)nullptr, (uint64_t)0);
+                return launch(gemm_relu_smallm_stream_kernel<kStreamNB, kStreamW, kStreamR, stream::WHOLE, E>, p.grid,
+                              p.threads, stream, A, B, C, no_part, M, N, K, lda, ldb, ldc, K, (uint32_t)p.grid, ep);
             }
             const bool whole = N % NB == 0 && K % KSTEP == 0;
             constexpr int W = kSmallMWaves, U = kSmallMUnroll;
@@ -1106,7 +1076,7 @@ void fill_plan_ta(int path, int64_t M, int64_t N, int64_t K, uintptr_t At, int64
         p->block_n = kStreamNB;
         p->block_k = KSTEP;
         p->stages = 1;
-        p->threads = 64 * kStreamW;
+        p->threads = 64 * kStreamTaW;
         p->grid = (N + kStreamNB - 1) / kStreamNB;
         p->vec_a = 1;
         p->vec_b = 8;
@@ -1136,10 +1106,10 @@ int run_ta(const gr_plan_t& p, int64_t M, int64_t N, int64_t K, const uint16_t* 
         case GR_PATH_NONE: return GR_OK;
         case GR_PATH_SMALL_M: {
             float* no_part = nullptr;
-            return launch(gr::smallm::gemm_relu_smallm_stream_kernel<kStreamNB, kStreamW, gr::smallm::stream::WHOLE,
-                                                                     E, true>,
+            return launch(gr::smallm::gemm_relu_smallm_stream_kernel<kStreamNB, kStreamTaW, 1,
+                                                                     gr::smallm::stream::WHOLE, E, true>,
                           p.grid, p.threads, stream, At, B, C, no_part, M, N, K, ldat, ldb, ldc, K, (uint32_t)p.grid,
-                          kReluOnly, (uint64_t*)nullptr, (uint64_t)0);
+                          kReluOnly);
         }
         case GR_PATH_TILE: {
             using namespace gr::tile2;

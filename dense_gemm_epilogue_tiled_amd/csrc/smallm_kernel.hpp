@@ -196,71 +196,81 @@ __global__ __launch_bounds__(64 * W, 1) void gemm_relu_smallm_kernel(
 // ---- streaming variant: B copied straight into LDS ----------------------------
 //
 // The kernel above holds B in registers and reads it in 128-byte row pieces
-// (64-column strips).  Measured on this part, streaming reads reach about
-// 6.8 TB/s when every workgroup reads 256-byte (or longer) row pieces, against
-// about 6.0 TB/s for 128-byte pieces, and they are fastest with about 32 KiB
-// in flight per workgroup: more outstanding copies per workgroup measured
-// slower (one 8 KiB slot per wave 41.7 us, two 44.5 us, three 45.0 us for the
-// first pass of 8 x 16384 x 8192; 8 waves of one slot 45.0 us).  This
-// variant moves B with direct-to-LDS copies (global_load_lds_dwordx4,
-// nontemporal) and keeps exactly one slot per wave in flight:
+// (64-column strips).  Measured on this part, streaming reads are fastest
+// with 256-byte row pieces and 32 KiB in flight per workgroup (a plain read
+// of the small-M workload's B in that pattern: 39.2-39.9 us, 6.7-6.9 TB/s;
+// 512-byte to 4 KiB pieces were slower), and the in-flight bytes should stay
+// there: when each wave waits for its own slot and then computes, the
+// workgroup's copies in flight dip while it computes.  This variant moves B
+// (and A) with direct-to-LDS copies (global_load_lds_dwordx4, nontemporal):
 //   * workgroup (cb, s): columns [NB cb, NB cb + NB) and the K range of split
 //     s (all of K without a split); its W waves take the range's 32-row slots
-//     in turn (wave w: slots w, w + W, ...), each into an LDS slot of its own:
-//     copy the slot, wait for this wave's copies (vmcnt 0), multiply, next
-//     slot; a wave reads back only what it copied itself, so no barrier is
-//     needed, and the W waves of a workgroup keep W slots in flight;
-//   * copies: a slot is 32 rows of 2 NB bytes; one copy instruction moves
-//     1 KiB (1024 / 2NB whole rows); 16-byte chunk c of row r sits at chunk
-//     slot c XOR 2(r mod 4) (the 4 rows one 16-lane group reads below land in
-//     distinct banks);
+//     in turn (wave w: slots w, w + W, ...) through a ring of R slots of its
+//     own: slot q + R - 1 is copied before slot q is waited for, so every
+//     wave keeps R - 1 to R slots in flight and the workgroup W (R - 1) to
+//     W R; a wave reads back only what it copied itself, so no barrier is
+//     needed.  Measured first pass of the small-M split (8 x 16384 x 8192, two
+//     splits, NB = 128): 2 waves x ring of 2 40.0-40.5 us, 4 waves x 1 slot
+//     41.9-42.2 us, 4 waves x 2 slots 47.2 us, 8 waves x 1 slot 45.1 us;
+//     single pass (NB = 64): 4 waves x 2 slots 47.1-47.5 us, 8 waves x 1
+//     slot 48.8 us;
+//   * copies: a slot is 32 rows of 2 NB bytes of B, then (when A is given
+//     row-major) 16 rows x 32 k of A; one copy instruction moves 1 KiB
+//     (1024 / 2NB whole rows of B); 16-byte chunk c of row r of B sits at
+//     chunk slot c XOR 2(r mod 4), chunk c of row r of A at c XOR (r/4) mod 4
+//     (the rows one 16-lane group reads land in distinct banks);
 //   * compute: per slot and 16-column block j, the B operand of
 //     v_mfma_f32_16x16x32 (16 columns x 32 k) comes from two
-//     ds_read_b64_tr_b16, the A operand (16 rows of A x 32 k; rows >= M are
-//     zero) from one 16-byte load of A per lane and slot (A is small and
-//     stays in the caches), issued with the slot's copies;
+//     ds_read_b64_tr_b16, the A operand (16 rows of A x 32 k; rows >= M copy
+//     row M - 1, whose outputs are never stored) from one 16-byte LDS read;
 //   * B may have any 2-byte alignment (the copies read any address); the
 //     last column block moves left to end at column N (N >= NB), so every
 //     copy reads inside [0, K) x [0, N) and only the block's own columns
 //     are stored;
 //   * at the end the W waves' partial sums are added in LDS in wave order;
-//     without a split the epilogue (ReLU, rounding) follows, with a split
+//     without a split the epilogue (ReLU, rounding) follows; with a split
 //     the fp32 sum of the range goes to part[s][m][n] for the ordered second
-//     pass (gemm_relu_smallm_reduce_kernel below).
+//     pass (gemm_relu_smallm_reduce_kernel below).  Adding two splits in the
+//     same launch instead (the second workgroup of a column block to finish
+//     reads the other's agent-scope partial sums after an exchange on a
+//     per-block flag) measured 0.7 us slower: the stores, the exchange and
+//     the reloads sit one after another at the end of every workgroup.
 // Needs M <= 16, K % 32 == 0 (whole slots), 16-byte rows of A.
 // AT=true: A is given transposed (At, K x M row-major, pitch lda, any
 // alignment): each lane gathers its 8 consecutive k of one column of At with
-// 2-byte loads (A is small and stays in the caches).
+// 2-byte loads (A is small and stays in the caches), one slot per wave.
 namespace stream {
 
 constexpr int SLOT_ROWS = 32;
 
-// What a workgroup does with its range sum: store C (no split), store the
-// fp32 partial for the ordered second pass, or (two splits) store the
-// partial and let the second workgroup of the column block to finish add both
-// in split order and store C, in the same launch.
-enum Mode { WHOLE = 0, PARTIAL = 1, LAST_OF_TWO = 2 };
+// What a workgroup does with its range sum: store C (no split), or store
+// the fp32 partial sum for the ordered second pass.
+enum Mode { WHOLE = 0, PARTIAL = 1 };
 
 __device__ __forceinline__ uint32_t chunk_slot(uint32_t row, uint32_t c) { return c ^ ((row & 3u) << 1); }
 
 }  // namespace stream
 
-template <int NB, int W, int MODE, typename E = ElemF16, bool AT = false>
+template <int NB, int W, int R, int MODE, typename E = ElemF16, bool AT = false>
 __global__ __launch_bounds__(64 * W, 1) void gemm_relu_smallm_stream_kernel(
     const uint16_t* __restrict__ A, const uint16_t* __restrict__ B, uint16_t* __restrict__ C,
     float* __restrict__ part, int64_t M, int64_t N, int64_t K, int64_t lda, int64_t ldb, int64_t ldc,
-    int64_t k_per_split, uint32_t n_blocks, EpiArgs ep, uint64_t* __restrict__ flags, uint64_t epoch) {
+    int64_t k_per_split, uint32_t n_blocks, EpiArgs ep) {
     using tile2::dma16_nt;
+    constexpr bool ADMA = !AT;                           // A copied into the slot beside B
     constexpr int ROWB = 2 * NB;                         // bytes of one row piece
     constexpr int CH = NB / 8;                           // 16-byte chunks per row piece
-    constexpr int SLOT = stream::SLOT_ROWS * ROWB;       // bytes per slot
-    constexpr int DPS = SLOT / 1024;                     // copy instructions per slot
+    constexpr int BSLOT = stream::SLOT_ROWS * ROWB;      // bytes of B per slot
+    constexpr int SLOT = BSLOT + (ADMA ? 1024 : 0);      // + 16 rows x 32 k of A
+    constexpr int DPS = BSLOT / 1024;                    // copy instructions of B per slot
+    constexpr int OPS = DPS + (ADMA ? 1 : 0);            // memory operations per slot
     constexpr int RPI = 1024 / ROWB;                     // rows per copy instruction
     constexpr int NBLK = NB / 16;                        // MFMA column blocks per slot
     constexpr int T = 64 * W;
     static_assert(CH >= 8 && DPS * RPI == stream::SLOT_ROWS, "whole rows per copy instruction");
-    static_assert(MAX_M * NB * 4 <= SLOT, "the cross-wave sum fits the slots");
-    __shared__ __attribute__((aligned(1024))) uint8_t lds[W * SLOT];
+    static_assert(MAX_M * NB * 4 <= R * SLOT, "the cross-wave sum fits a wave's slots");
+    static_assert(!AT || R == 1, "A gathered into registers: one slot per wave");
+    __shared__ __attribute__((aligned(1024))) uint8_t lds[W * R * SLOT];
 
     const uint32_t tid = threadIdx.x, lane = tid & 63u;
     const uint32_t w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -271,7 +281,8 @@ __global__ __launch_bounds__(64 * W, 1) void gemm_relu_smallm_stream_kernel(
     const int64_t k_begin = s * k_per_split;
     const int64_t k_end = k_begin + k_per_split < K ? k_begin + k_per_split : K;
     const int64_t slots = (k_end - k_begin) / stream::SLOT_ROWS;
-    const uint32_t base = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t*)lds + w * SLOT;
+    const int64_t nw = slots > (int64_t)w ? (slots - w + W - 1) / W : 0;  // this wave's slots
+    const uint32_t ring = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t*)lds + w * R * SLOT;
 
     // copy instruction i of a slot: lane -> row i RPI + lane / CH, chunk slot
     // lane % CH, which holds chunk (lane % CH) XOR 2 (row mod 4)
@@ -282,6 +293,12 @@ __global__ __launch_bounds__(64 * W, 1) void gemm_relu_smallm_stream_kernel(
         voff[i] = (uint32_t)((row * ldb + 8 * stream::chunk_slot(row, lane % CH)) * 2);
     }
     const uint16_t* b_range = B + k_begin * ldb + n0;
+    // A copy of a slot (ADMA): lane -> row lane / 4 (rows >= M read row M - 1;
+    // their outputs are never stored), chunk slot lane % 4 holding chunk
+    // (lane % 4) XOR (row / 4) % 4 of the row's 32 k.
+    const uint32_t arow = lane >> 2, apos = lane & 3u;
+    const uint32_t asrc = (int64_t)arow < M ? arow : (uint32_t)(M - 1);
+    const uint32_t aoff = (uint32_t)((asrc * lda + 8 * (apos ^ ((arow >> 2) & 3u))) * 2);
     const uint32_t am = lane & 15u, ag = lane >> 4;
 
     // B operand of column block j: lane l (group g = l/16, i = l%16) reads
@@ -292,24 +309,42 @@ __global__ __launch_bounds__(64 * W, 1) void gemm_relu_smallm_stream_kernel(
 #pragma unroll
     for (int j = 0; j < NBLK; ++j) acc[j] = f32x4{};
 
-    for (int64_t t = w; t < slots; t += W) {
-        // this wave's slot t: copies of B, the A operand; the LDS slot is free
-        // (the previous slot's reads were consumed by its MFMAs)
+    // Slot q of this wave is slot t = w + W q of the range, in ring entry q % R.
+    u32x4 areg = u32x4{0u, 0u, 0u, 0u};
+    auto issue = [&](int64_t q) {
+        const int64_t t = (int64_t)w + (int64_t)W * q;
+        const uint32_t dst = ring + (uint32_t)(q % R) * SLOT;
         const uint8_t* src = reinterpret_cast<const uint8_t*>(b_range + t * stream::SLOT_ROWS * ldb);
 #pragma unroll
-        for (int i = 0; i < DPS; ++i) dma16_nt(src, voff[i], base + i * 1024);
-        const int64_t k = k_begin + t * stream::SLOT_ROWS + 8 * ag;
-        u32x4 areg;
-        if constexpr (AT) {
+        for (int i = 0; i < DPS; ++i) dma16_nt(src, voff[i], dst + i * 1024);
+        if constexpr (ADMA) {
+            dma16_nt(reinterpret_cast<const uint8_t*>(A + k_begin + t * stream::SLOT_ROWS), aoff, dst + BSLOT);
+        } else {
+            const int64_t k = k_begin + t * stream::SLOT_ROWS + 8 * ag;
             uint32_t h[8];
 #pragma unroll
             for (int e = 0; e < 8; ++e) h[e] = (int64_t)am < M ? (uint32_t)A[(k + e) * lda + am] : 0u;
             areg = u32x4{h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16), h[6] | (h[7] << 16)};
-        } else {
-            areg = (int64_t)am < M ? *reinterpret_cast<const u32x4*>(A + am * lda + k) : u32x4{0u, 0u, 0u, 0u};
         }
-        tile2::wait_vmcnt<0>();  // the slot's copies and A have landed
-        const f16x8 a = __builtin_bit_cast(f16x8, areg);
+    };
+
+    // R - 1 slots ahead: slot q + R - 1 goes out (into the entry slot q - 1
+    // used, whose reads its MFMAs consumed) before slot q is waited for.
+    const int64_t ahead = nw < R - 1 ? nw : R - 1;
+    for (int64_t q = 0; q < ahead; ++q) issue(q);
+    for (int64_t q = 0; q < nw; ++q) {
+        const bool more = q + R - 1 < nw;
+        if (more) issue(q + R - 1);
+        if (more) tile2::wait_vmcnt<(R - 1) * OPS>();  // slot q's copies have landed
+        else tile2::wait_vmcnt<0>();
+        const uint32_t base = ring + (uint32_t)(q % R) * SLOT;
+        f16x8 a;
+        if constexpr (ADMA) {
+            a = *reinterpret_cast<const __attribute__((address_space(3))) f16x8*>(
+                (uintptr_t)(base + BSLOT + am * 64 + ((ag ^ ((am >> 2) & 3u)) << 4)));
+        } else {
+            a = __builtin_bit_cast(f16x8, areg);
+        }
 #pragma unroll
         for (int j = 0; j < NBLK; ++j) {
             const uint32_t c = 2 * j + ((fi >> 1) & 1u);
@@ -329,12 +364,12 @@ __global__ __launch_bounds__(64 * W, 1) void gemm_relu_smallm_stream_kernel(
     // 4(l/16) + r of the block.  Sum the waves in order through LDS (each
     // wave's partials in its own slot).
     __syncthreads();
-    float* red = reinterpret_cast<float*>(lds);  // wave w at w * SLOT: [16][NB]
+    float* red = reinterpret_cast<float*>(lds);  // wave w at w * R * SLOT: [16][NB]
 #pragma unroll
     for (int j = 0; j < NBLK; ++j)
 #pragma unroll
         for (int r = 0; r < 4; ++r)
-            red[w * (SLOT / 4) + (lane & 15u) * NB + 16 * j + 4 * (lane >> 4) + r] = acc[j][r];
+            red[w * (R * SLOT / 4) + (lane & 15u) * NB + 16 * j + 4 * (lane >> 4) + r] = acc[j][r];
     __syncthreads();
     for (uint32_t o = tid; o < (uint32_t)(MAX_M * NB); o += T) {
         const uint32_t m = o / NB, nl = o % NB;
@@ -342,45 +377,9 @@ __global__ __launch_bounds__(64 * W, 1) void gemm_relu_smallm_stream_kernel(
         if ((int64_t)m >= M || n < n_own) continue;
         float v = 0.0f;
 #pragma unroll
-        for (int ww = 0; ww < W; ++ww) v += red[ww * (SLOT / 4) + m * NB + nl];
-        if constexpr (MODE == stream::WHOLE) {
-            C[(int64_t)m * ldc + n] = epi_value<E>(v, n, N, ep);
-        } else if constexpr (MODE == stream::PARTIAL) {
-            part[(s * M + m) * N + n] = v;
-        } else {
-            // agent-scope stores: they bypass this XCD's L2, so the other
-            // workgroup of the block reads them from any XCD
-            __hip_atomic_store(&part[(s * M + m) * N + n], v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            red[m * NB + nl] = v;  // own sum, kept for the last workgroup (wave 0's region)
-        }
-    }
-    if constexpr (MODE == stream::LAST_OF_TWO) {
-        // Every partial store of this workgroup has completed before the
-        // exchange below announces it.  Each call brings a fresh 64-bit epoch:
-        // the workgroup that finds the epoch already in its block's flag
-        // arrives second and owns the sum; the flag's earlier contents
-        // (another call's epoch or anything a caller left) only ever mean
-        // "first", so the flags need no clearing.
-        tile2::wait_vmcnt<0>();
-        __syncthreads();
-        __shared__ uint32_t last;
-        if (tid == 0) {
-            const uint64_t prev = __hip_atomic_exchange(&flags[cb], epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            last = prev == epoch ? 1u : 0u;
-        }
-        __syncthreads();
-        if (last) {
-            for (uint32_t o = tid; o < (uint32_t)(MAX_M * NB); o += T) {
-                const uint32_t m = o / NB, nl = o % NB;
-                const int64_t n = n0 + nl;
-                if ((int64_t)m >= M || n < n_own) continue;
-                const float own = red[m * NB + nl];
-                const float other =
-                    __hip_atomic_load(&part[((1 - s) * M + m) * N + n], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                const float v = s == 0 ? own + other : other + own;  // split order
-                C[(int64_t)m * ldc + n] = epi_value<E>(v, n, N, ep);
-            }
-        }
+        for (int ww = 0; ww < W; ++ww) v += red[ww * (R * SLOT / 4) + m * NB + nl];
+        if constexpr (MODE == stream::WHOLE) C[(int64_t)m * ldc + n] = epi_value<E>(v, n, N, ep);
+        else part[(s * M + m) * N + n] = v;
     }
 }
 

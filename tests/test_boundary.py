@@ -268,10 +268,9 @@ def test_small_m_split_plan():
     assert plan_ws(8, 4096, 8192, size - 1)[1]["path"] == gr.GR_PATH_SMALL_M
     assert plan(8, 4096, 8192)[1]["path"] == gr.GR_PATH_SMALL_M
     # the small-M workload: 128 column blocks x 2 splits (256-byte row pieces
-    # over half of K each), summed in the same launch: the two partial sums
-    # and one 8-byte flag per column block (rounded up to 256 bytes)
+    # over half of K each)
     st, size = ws_size(8, 16384, 8192)
-    assert size == 2 * 8 * 16384 * 4 + 1024
+    assert size == 2 * 8 * 16384 * 4
     st, p = plan_ws(8, 16384, 8192, size)
     assert (p["path"], p["split_k"], p["grid"], p["block_n"]) == (gr.GR_PATH_SMALL_M_SPLIT, 2, 256, 128)
     # 256 column blocks or more already fill the chip: no workspace asked for
