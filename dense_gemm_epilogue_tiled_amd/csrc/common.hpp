@@ -603,16 +603,19 @@ __device__ __forceinline__ void store_wave_tile(Acc& acc, uint8_t* region, uint3
 constexpr uint32_t ROWS32_BYTES = WaveTile<1, 4>::REGION_BYTES;  // 8 KiB
 
 template <typename E, int BM, int BN>
-__device__ __forceinline__ void store_wave_tile_rows32(const f32x4 (&acc)[BM][BN], uint8_t* region, uint32_t lane,
+__device__ __forceinline__ void store_wave_tile_rows32(const f32x4 (&acc)[BM][BN], uint8_t* region,
                                                        uint16_t* __restrict__ C, int64_t ldc, int64_t row0,
                                                        int64_t col0) {
     static_assert(BM == 8 && BN == 8, "a 128 x 128 wave tile of 16 x 16 blocks");
     using T = WaveTile<1, 4>;
     constexpr uint32_t ROWS_PER = 64u / T::CHUNKS;  // 4
-    // Called once per tile of a loop: computing the lane's addresses here,
-    // and not once before the loop, keeps them from living (and spilling)
-    // through the main loop.
-    asm volatile("" : "+v"(lane));
+    // Called once per tile of a loop: the lane id is recomputed here (from
+    // the exec mask count), so neither it nor the addresses derived from it
+    // live, or spill, through the main loop; a reload of a spill would wait
+    // for every copy of the next tile already in flight.
+    // (volatile: a plain mbcnt is loop-invariant, and the compiler hoists it)
+    uint32_t lane;
+    asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(lane));
     const uint32_t r = lane & 15u, g = lane >> 4;
     const uint32_t ch = lane & (T::CHUNKS - 1);
 #pragma unroll

@@ -375,7 +375,12 @@ __global__ __launch_bounds__(THREADS, 1) void gemm_relu_tile2_kernel(
 
     // Epilogue: ReLU, fp16 and the store of C, staged through LDS (the
     // operand ring is no longer needed).
-    epi::store_wave_tile<EDGE, E>(acc, lds + wave * epi::REGION_BYTES, lane, C, ldc, m0 + wm * WAVE_TM,
+    // The lane index is marked as redefined so the epilogue's lane addresses
+    // are computed here, not kept from before the main loop (a spilled
+    // register otherwise).
+    uint32_t elane = lane;
+    asm volatile("" : "+v"(elane));
+    epi::store_wave_tile<EDGE, E>(acc, lds + wave * epi::REGION_BYTES, elane, C, ldc, m0 + wm * WAVE_TM,
                                n0 + wn * WAVE_TN, m_tile, M, N, vec_c, ep);
 }
 

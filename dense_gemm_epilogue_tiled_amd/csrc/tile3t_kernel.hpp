@@ -285,7 +285,12 @@ __global__ __launch_bounds__(THREADS, 1) void gemm_relu_tile3t_kernel(
     step_any(kt + 5, f0, f1);
 
     // Epilogue: activation, rounding and the store of C, staged through LDS.
-    epi::store_wave_tile<EDGE, E>(acc, lds + wave * epi::REGION_BYTES, lane, C, ldc, m0 + wm * WAVE_TM,
+    // The lane index is marked as redefined so the epilogue's lane addresses
+    // are computed here, not kept from before the main loop (a spilled
+    // register otherwise).
+    uint32_t elane = lane;
+    asm volatile("" : "+v"(elane));
+    epi::store_wave_tile<EDGE, E>(acc, lds + wave * epi::REGION_BYTES, elane, C, ldc, m0 + wm * WAVE_TM,
                                   n0 + wn * WAVE_TN, m_tile, M, N, vec_c, ep);
 }
 

@@ -744,11 +744,13 @@ def test_no_kernel_spills_to_scratch():
     assert names and len(names) == len(scratch)
     hot = dict(zip(names, scratch))
     assert any("gemm_relu_tile3_kernel" in n for n in hot) and any("gemm_fp8_tile_kernel" in n for n in hot), names
-    # every kernel, whatever its epilogue: the pipelined 256 x 256 kernels
-    # may spill a few bytes outside their steady loop; the small-M and
-    # 128 x 128 kernels must not spill at all
+    # every kernel, whatever its epilogue: the other pipelined 256 x 256
+    # kernels may spill a few bytes outside their steady loop; the 256 x 256
+    # kernel for K % 64 == 0 (in place, unaligned and persistent), the
+    # small-M and the 128 x 128 kernels must not spill at all (a reload in
+    # the persistent loop would wait for the next tile's copies in flight)
     for n, s in hot.items():
-        limit = 0 if ("smallm" in n or "tile128" in n) else 16
+        limit = 0 if ("smallm" in n or "tile128" in n or "tile322gemm_relu_tile3_kernel" in n) else 16
         assert s <= limit, (n, s)
 
 
