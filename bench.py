@@ -207,7 +207,9 @@ def cpu_oracle_table():
             dt = time.perf_counter() - t0
             flops = 2.0 * rows * w.N * w.K
             row[label] = {"threads": threads, "sample": "full matrix" if r is None else "%d rows" % r,
-                          "seconds": round(dt, 3), "tflops": round(flops / dt / 1e12, 5)}
+                          "seconds": round(dt, 3), "tflops": round(flops / dt / 1e12, 5),
+                          # work per row is exactly 2 N K FLOP, so this is exact in work
+                          "full_matrix_s": round(dt * w.M / rows, 3)}
         t0 = time.perf_counter()
         if w.check == "full":
             oracle.gemm_relu_full(A, B, threads=allc)
@@ -224,6 +226,18 @@ def cpu_oracle_table():
         print("[oracle] %s %s" % (name, row), file=sys.stderr, flush=True)
         del A, B
     oracle.set_threads(allc)
+    model = ""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    table["host"] = {"os_cpu_count": os.cpu_count(), "affinity": len(os.sched_getaffinity(0)),
+                     "OMP_NUM_THREADS": os.environ.get("OMP_NUM_THREADS"), "cpu_model": model,
+                     "what": "the oracle as it stands, a reported baseline, not the optimisation target"}
     return table
 
 
@@ -471,17 +485,24 @@ def observed_sclk(torch, run, seconds=1.0):
     return best
 
 
-def copy_probe(torch, mib):
+def copy_probe(torch, mib, reps=20):
+    """A device-to-device copy of ``mib`` MiB (torch's copy kernel): the
+    STREAM-like copy rate (bytes read + written per second), and the kernel
+    the HBM-traffic counters are calibrated against."""
     n = mib * 1024 * 1024 // 2
     src = torch.randn(n, device="cuda", dtype=torch.float32).half()
     dst = torch.empty_like(src)
     for _ in range(3):
         dst.copy_(src)
     torch.cuda.synchronize()
-    times = time_launches(torch, lambda: dst.copy_(src), torch.cuda.current_stream(), 20)
-    med = statistics.median(times)
-    print(json.dumps({"copy_probe_bytes_read": n * 2, "copy_probe_bytes_written": n * 2,
-                      "median_us": round(med * 1e3, 2), "gbs_rw": round(4.0 * n / (med * 1e-3) / 1e9, 1)}))
+    stream = torch.cuda.current_stream()
+    avg = time_back_to_back(torch, [lambda: dst.copy_(src)], stream, reps)
+    med = statistics.median(time_launches(torch, lambda: dst.copy_(src), stream, reps))
+    del src, dst
+    torch.cuda.empty_cache()
+    return {"bytes_read": n * 2, "bytes_written": n * 2, "avg_us": round(avg * 1e3, 2),
+            "per_launch_median_us": round(med * 1e3, 2), "gbs_rw": round(4.0 * n / (avg * 1e-3) / 1e9, 1),
+            "frac_of_peak": round(4.0 * n / (avg * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
 
 
 def vendor_reference(torch, reps=30):
@@ -706,7 +727,7 @@ def main():
     gr.lib()  # fail loudly if the HIP library is missing
 
     if args.copy_probe:
-        copy_probe(torch, args.copy_probe)
+        print(json.dumps(copy_probe(torch, args.copy_probe)))
         return
     if args.read_probe:
         print(json.dumps({"read_ceiling": read_ceiling(gr, torch, nbytes=args.read_probe << 20)}), flush=True)
@@ -799,6 +820,7 @@ def main():
     if not args.no_workloads:
         ceiling = read_ceiling(gr, torch, settle_ms=args.workload_settle_ms)
         out["read_ceiling"] = ceiling
+        out["copy_probe"] = copy_probe(torch, 1024)
         print("[bench] read ceiling %s" % (ceiling,), file=sys.stderr, flush=True)
         table = {}
         for name, wl in synth.WORKLOADS.items():

@@ -206,6 +206,22 @@ def test_scaling_by_two_bitwise():
     assert np.array_equal(C2[normal], 2 * C1[normal])
 
 
+@pytest.mark.parametrize("M,N,K,path", [(512, 640, 384, None), (4096, 4096, 256, gr.GR_PATH_TILE_PERSISTENT),
+                                          (300, 520, 130, None), (8, 4096, 1024, None)])
+def test_relu_of_a_minus_relu_of_minus_a_is_the_product(M, N, K, path):
+    """ReLU(x) - ReLU(-x) = x: C(A) - C(-A) matches the float64 product A.B
+    within the bar at every element, and at every element one of the two is
+    +0 (covers the planner's tile, unaligned and small-M paths and the
+    persistent loop)."""
+    A, B = synth.random_operands(M, N, K, seed=63 + M)
+    An = A ^ np.uint16(0x8000)  # -A, exactly (sign bit)
+    C1 = as_f64(window(run_full(A, B, M, N, K, path=path), M, N, N))
+    C2 = as_f64(window(run_full(An, B, M, N, K, path=path), M, N, N))
+    x = A.view(np.float16).astype(np.float64) @ B.view(np.float16).astype(np.float64)
+    assert np.all((C1 == 0) | (C2 == 0))
+    assert np.all(np.abs((C1 - C2) - x) <= 1e-2 + 1e-2 * np.abs(x))
+
+
 def test_deterministic_bitwise():
     M, N, K = 1024, 768, 512
     A, B = synth.random_operands(M, N, K, seed=62)
