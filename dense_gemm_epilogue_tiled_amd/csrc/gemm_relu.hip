@@ -131,8 +131,9 @@ bool smallm_rows_ok(int64_t M, int64_t N, int64_t K, uintptr_t A, int64_t lda, u
 constexpr int kStreamNB = 64, kStreamW = 4, kStreamR = 2;  // single pass: 64-column blocks, 4 waves x 2 slots
 constexpr int kStreamSplitNB = 128, kStreamSplitW = 2, kStreamSplitR = 2;  // split: 128 columns, 2 waves x 2 slots
 constexpr int kStreamTaW = 8;  // A given transposed (gathered into registers): 8 waves x 1 slot
-bool smallm_stream_ok(int64_t M, int64_t N, int64_t K, uintptr_t A, int64_t lda, int64_t ldb, int64_t nb) {
-    return M >= 1 && M <= kSmallMThreshold && K > 0 && K % 32 == 0 && A % 16 == 0 && lda % 8 == 0 && N >= nb &&
+bool smallm_stream_ok(int64_t M, int64_t N, int64_t K, uintptr_t A, int64_t lda, int64_t ldb, int64_t nb,
+                      int64_t max_rows = kSmallMThreshold) {
+    return M >= 1 && M <= max_rows && K > 0 && K % 32 == 0 && A % 16 == 0 && lda % 8 == 0 && N >= nb &&
            ldb <= gr::tile2::MAX_LDB;
 }
 
@@ -384,7 +385,7 @@ void fill_plan(int path, int64_t M, int64_t N, int64_t K, uintptr_t A, int64_t l
         using namespace gr::smallm;
         // the streaming kernel where it applies (vec_b 8: 16-byte copies of B
         // from any address), else the register-staged one (vec_b 4)
-        const bool stream = smallm_stream_ok(M, N, K, A, lda, ldb, kStreamNB);
+        const bool stream = smallm_stream_ok(M, N, K, A, lda, ldb, kStreamNB, kSmallMMaxRows);
         p->block_m = M <= MAX_M ? MAX_M : (M <= 2 * MAX_M ? 2 * MAX_M : 4 * MAX_M);  // rows per workgroup
         p->block_n = stream ? kStreamNB : NB;
         p->block_k = KSTEP;
@@ -414,7 +415,9 @@ int choose_path(int64_t M, int64_t N, int64_t K, uintptr_t A, int64_t lda, uintp
     if (fast && ws_bytes > 0 && !use_large_tiles(M, N) && tile_split_layout(M, N, K, false, ts) &&
         ts->bytes <= ws_bytes)
         return GR_PATH_TILE_SPLIT;
-    if (K > 0 && smallm_rows_ok(M, N, K, A, lda, B, ldb) && (N + gr::smallm::NB - 1) / gr::smallm::NB <= 256)
+    if (K > 0 &&
+        (smallm_rows_ok(M, N, K, A, lda, B, ldb) || smallm_stream_ok(M, N, K, A, lda, ldb, kStreamNB, kSmallMMaxRows)) &&
+        (N + gr::smallm::NB - 1) / gr::smallm::NB <= 256)
         return GR_PATH_SMALL_M;
     if (fast) return GR_PATH_TILE;
     if (tile_unaligned_ok(M, N, K, lda, ldb) && use_large_tiles(M, N)) return GR_PATH_TILE_UNALIGNED;
@@ -649,10 +652,20 @@ int run(const gr_plan_t& p, int64_t M, int64_t N, int64_t K, const uint16_t* A, 
             }
         case GR_PATH_SMALL_M: {
             using namespace gr::smallm;
-            if (p.vec_b == 8 && M <= MAX_M) {
+            if (p.vec_b == 8) {
+                // the streaming kernel with 1, 2 or 4 blocks of 16 rows of A
                 float* no_part = nullptr;
-                return launch(gemm_relu_smallm_stream_kernel<kStreamNB, kStreamW, kStreamR, stream::WHOLE, E>, p.grid,
-                              p.threads, stream, A, B, C, no_part, M, N, K, lda, ldb, ldc, K, (uint32_t)p.grid, ep);
+                if (M <= MAX_M)
+                    return launch(gemm_relu_smallm_stream_kernel<kStreamNB, kStreamW, kStreamR, stream::WHOLE, E>,
+                                  p.grid, p.threads, stream, A, B, C, no_part, M, N, K, lda, ldb, ldc, K,
+                                  (uint32_t)p.grid, ep);
+                if (M <= 2 * MAX_M)
+                    return launch(
+                        gemm_relu_smallm_stream_kernel<kStreamNB, kStreamW, kStreamR, stream::WHOLE, E, false, 2>,
+                        p.grid, p.threads, stream, A, B, C, no_part, M, N, K, lda, ldb, ldc, K, (uint32_t)p.grid, ep);
+                return launch(gemm_relu_smallm_stream_kernel<kStreamNB, kStreamW, kStreamR, stream::WHOLE, E, false, 4>,
+                              p.grid, p.threads, stream, A, B, C, no_part, M, N, K, lda, ldb, ldc, K,
+                              (uint32_t)p.grid, ep);
             }
             const bool whole = N % NB == 0 && K % KSTEP == 0;
             constexpr int W = kSmallMWaves, U = kSmallMUnroll;
@@ -701,7 +714,8 @@ int plan_call(int64_t M, int64_t N, int64_t K, uintptr_t a, int64_t lda, uintptr
         } else if (forced == GR_PATH_TILE_PERSISTENT) {
             if (!tile_persistent_ok(M, N, K, a, lda, b, ldb, c, ldc)) return GR_ERR_INVALID_PATH;
         } else if (forced == GR_PATH_SMALL_M) {
-            if (K == 0 || !(smallm_rows_ok(M, N, K, a, lda, b, ldb) || smallm_stream_ok(M, N, K, a, lda, ldb, kStreamNB)))
+            if (K == 0 || !(smallm_rows_ok(M, N, K, a, lda, b, ldb) ||
+                            smallm_stream_ok(M, N, K, a, lda, ldb, kStreamNB, kSmallMMaxRows)))
                 return GR_ERR_INVALID_PATH;
         } else if (forced == GR_PATH_TILE_PACKED) {
             if (!pack_layout(M, N, K, a, lda, b, ldb, pk) || pk->bytes > ws_bytes) return GR_ERR_INVALID_PATH;

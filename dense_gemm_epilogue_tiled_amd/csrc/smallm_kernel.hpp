@@ -251,7 +251,7 @@ __device__ __forceinline__ uint32_t chunk_slot(uint32_t row, uint32_t c) { retur
 
 }  // namespace stream
 
-template <int NB, int W, int R, int MODE, typename E = ElemF16, bool AT = false>
+template <int NB, int W, int R, int MODE, typename E = ElemF16, bool AT = false, int MB = 1>
 __global__ __launch_bounds__(64 * W, 1) void gemm_relu_smallm_stream_kernel(
     const uint16_t* __restrict__ A, const uint16_t* __restrict__ B, uint16_t* __restrict__ C,
     float* __restrict__ part, int64_t M, int64_t N, int64_t K, int64_t lda, int64_t ldb, int64_t ldc,
@@ -260,16 +260,18 @@ __global__ __launch_bounds__(64 * W, 1) void gemm_relu_smallm_stream_kernel(
     constexpr bool ADMA = !AT;                           // A copied into the slot beside B
     constexpr int ROWB = 2 * NB;                         // bytes of one row piece
     constexpr int CH = NB / 8;                           // 16-byte chunks per row piece
+    constexpr int ROWS = MAX_M * MB;                     // rows of A: MB blocks of 16
     constexpr int BSLOT = stream::SLOT_ROWS * ROWB;      // bytes of B per slot
-    constexpr int SLOT = BSLOT + (ADMA ? 1024 : 0);      // + 16 rows x 32 k of A
+    constexpr int SLOT = BSLOT + (ADMA ? 1024 * MB : 0); // + MB x 16 rows x 32 k of A
     constexpr int DPS = BSLOT / 1024;                    // copy instructions of B per slot
-    constexpr int OPS = DPS + (ADMA ? 1 : 0);            // memory operations per slot
+    constexpr int OPS = DPS + (ADMA ? MB : 0);           // memory operations per slot
     constexpr int RPI = 1024 / ROWB;                     // rows per copy instruction
     constexpr int NBLK = NB / 16;                        // MFMA column blocks per slot
     constexpr int T = 64 * W;
     static_assert(CH >= 8 && DPS * RPI == stream::SLOT_ROWS, "whole rows per copy instruction");
-    static_assert(MAX_M * NB * 4 <= R * SLOT, "the cross-wave sum fits a wave's slots");
-    static_assert(!AT || R == 1, "A gathered into registers: one slot per wave");
+    static_assert(ROWS * NB * 4 <= R * SLOT, "the cross-wave sum fits a wave's slots");
+    static_assert(!AT || (R == 1 && MB == 1), "A gathered into registers: one slot per wave, 16 rows");
+    static_assert(MB == 1 || MB == 2 || MB == 4, "1, 2 or 4 blocks of 16 rows");
     __shared__ __attribute__((aligned(1024))) uint8_t lds[W * R * SLOT];
 
     const uint32_t tid = threadIdx.x, lane = tid & 63u;
@@ -293,21 +295,29 @@ __global__ __launch_bounds__(64 * W, 1) void gemm_relu_smallm_stream_kernel(
         voff[i] = (uint32_t)((row * ldb + 8 * stream::chunk_slot(row, lane % CH)) * 2);
     }
     const uint16_t* b_range = B + k_begin * ldb + n0;
-    // A copy of a slot (ADMA): lane -> row lane / 4 (rows >= M read row M - 1;
-    // their outputs are never stored), chunk slot lane % 4 holding chunk
-    // (lane % 4) XOR (row / 4) % 4 of the row's 32 k.
+    // A copy of a slot (ADMA), one per block of 16 rows: lane -> row 16 mb +
+    // lane / 4 (rows >= M read row M - 1; their outputs are never stored),
+    // chunk slot lane % 4 holding chunk (lane % 4) XOR (row / 4) % 4 of the
+    // row's 32 k.
     const uint32_t arow = lane >> 2, apos = lane & 3u;
-    const uint32_t asrc = (int64_t)arow < M ? arow : (uint32_t)(M - 1);
-    const uint32_t aoff = (uint32_t)((asrc * lda + 8 * (apos ^ ((arow >> 2) & 3u))) * 2);
+    uint32_t aoff[MB];
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) {
+        const int64_t r = 16 * mb + arow;
+        const uint32_t asrc = r < M ? (uint32_t)r : (uint32_t)(M - 1);
+        aoff[mb] = (uint32_t)((asrc * lda + 8 * (apos ^ ((arow >> 2) & 3u))) * 2);
+    }
     const uint32_t am = lane & 15u, ag = lane >> 4;
 
     // B operand of column block j: lane l (group g = l/16, i = l%16) reads
     // row 8g + i/4 (then + 4), columns 16j + 4(i%4) .. +3.
     const uint32_t fi = lane & 15u, fg = lane >> 4;
     const uint32_t frow = 8 * fg + (fi >> 2);
-    f32x4 acc[NBLK];
+    f32x4 acc[MB][NBLK];
 #pragma unroll
-    for (int j = 0; j < NBLK; ++j) acc[j] = f32x4{};
+    for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+        for (int j = 0; j < NBLK; ++j) acc[mb][j] = f32x4{};
 
     // Slot q of this wave is slot t = w + W q of the range, in ring entry q % R.
     u32x4 areg = u32x4{0u, 0u, 0u, 0u};
@@ -318,7 +328,10 @@ __global__ __launch_bounds__(64 * W, 1) void gemm_relu_smallm_stream_kernel(
 #pragma unroll
         for (int i = 0; i < DPS; ++i) dma16_nt(src, voff[i], dst + i * 1024);
         if constexpr (ADMA) {
-            dma16_nt(reinterpret_cast<const uint8_t*>(A + k_begin + t * stream::SLOT_ROWS), aoff, dst + BSLOT);
+#pragma unroll
+            for (int mb = 0; mb < MB; ++mb)
+                dma16_nt(reinterpret_cast<const uint8_t*>(A + k_begin + t * stream::SLOT_ROWS), aoff[mb],
+                         dst + BSLOT + 1024 * mb);
         } else {
             const int64_t k = k_begin + t * stream::SLOT_ROWS + 8 * ag;
             uint32_t h[8];
@@ -338,12 +351,14 @@ __global__ __launch_bounds__(64 * W, 1) void gemm_relu_smallm_stream_kernel(
         if (more) tile2::wait_vmcnt<(R - 1) * OPS>();  // slot q's copies have landed
         else tile2::wait_vmcnt<0>();
         const uint32_t base = ring + (uint32_t)(q % R) * SLOT;
-        f16x8 a;
+        f16x8 a[MB];
         if constexpr (ADMA) {
-            a = *reinterpret_cast<const __attribute__((address_space(3))) f16x8*>(
-                (uintptr_t)(base + BSLOT + am * 64 + ((ag ^ ((am >> 2) & 3u)) << 4)));
+#pragma unroll
+            for (int mb = 0; mb < MB; ++mb)
+                a[mb] = *reinterpret_cast<const __attribute__((address_space(3))) f16x8*>(
+                    (uintptr_t)(base + BSLOT + 1024 * mb + am * 64 + ((ag ^ ((am >> 2) & 3u)) << 4)));
         } else {
-            a = __builtin_bit_cast(f16x8, areg);
+            a[0] = __builtin_bit_cast(f16x8, areg);
         }
 #pragma unroll
         for (int j = 0; j < NBLK; ++j) {
@@ -356,7 +371,8 @@ __global__ __launch_bounds__(64 * W, 1) void gemm_relu_smallm_stream_kernel(
             const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
                 (__attribute__((address_space(3))) s16x4*)(uintptr_t)p1);
             const f16x8 b = __builtin_bit_cast(f16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-            acc[j] = E::mfma16(b, a, acc[j]);
+#pragma unroll
+            for (int mb = 0; mb < MB; ++mb) acc[mb][j] = E::mfma16(b, a[mb], acc[mb][j]);
         }
     }
 
@@ -364,14 +380,17 @@ __global__ __launch_bounds__(64 * W, 1) void gemm_relu_smallm_stream_kernel(
     // 4(l/16) + r of the block.  Sum the waves in order through LDS (each
     // wave's partials in its own slot).
     __syncthreads();
-    float* red = reinterpret_cast<float*>(lds);  // wave w at w * R * SLOT: [16][NB]
+    float* red = reinterpret_cast<float*>(lds);  // wave w at w * R * SLOT: [ROWS][NB]
 #pragma unroll
-    for (int j = 0; j < NBLK; ++j)
+    for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
-        for (int r = 0; r < 4; ++r)
-            red[w * (R * SLOT / 4) + (lane & 15u) * NB + 16 * j + 4 * (lane >> 4) + r] = acc[j][r];
+        for (int j = 0; j < NBLK; ++j)
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                red[w * (R * SLOT / 4) + (16 * mb + (lane & 15u)) * NB + 16 * j + 4 * (lane >> 4) + r] =
+                    acc[mb][j][r];
     __syncthreads();
-    for (uint32_t o = tid; o < (uint32_t)(MAX_M * NB); o += T) {
+    for (uint32_t o = tid; o < (uint32_t)(ROWS * NB); o += T) {
         const uint32_t m = o / NB, nl = o % NB;
         const int64_t n = n0 + nl;
         if ((int64_t)m >= M || n < n_own) continue;
