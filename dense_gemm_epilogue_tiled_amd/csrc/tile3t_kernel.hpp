@@ -285,9 +285,21 @@ __global__ __launch_bounds__(THREADS, 1) void gemm_relu_tile3t_kernel(
     step_any(kt + 5, f0, f1);
 
     // Epilogue: activation, rounding and the store of C, staged through LDS.
-    // The lane index is marked as redefined so the epilogue's lane addresses
-    // are computed here, not kept from before the main loop (a spilled
-    // register otherwise).
+    // Whole tiles with 16-byte rows of C (the fp16/bf16 ReLU): after one
+    // barrier (no copy is in flight any more, so all of LDS is free) each
+    // wave stores its tile 32 rows at a time through 8 KiB of its own, with
+    // no further barrier.  Otherwise the whole wave tile is staged; the lane
+    // index is then marked as redefined so the epilogue's lane addresses are
+    // computed here, not kept from before the main loop (a spilled register
+    // otherwise).
+    if constexpr (!EDGE && !E::kGeneral) {
+        if (vec_c == 8) {
+            barrier();
+            epi::store_wave_tile_rows32<E>(acc, lds + wave * epi::ROWS32_BYTES, C, ldc, m0 + wm * WAVE_TM,
+                                           n0 + wn * WAVE_TN);
+            return;
+        }
+    }
     uint32_t elane = lane;
     asm volatile("" : "+v"(elane));
     epi::store_wave_tile<EDGE, E>(acc, lds + wave * epi::REGION_BYTES, elane, C, ldc, m0 + wm * WAVE_TM,
