@@ -130,3 +130,31 @@ def test_stream_kernel_with_bias_and_activation(fmt, act):
     assert np.all(np.isfinite(got))
     err = np.abs(got - ref)
     assert np.all(err <= 1e-2 + 1e-2 * np.abs(ref)), (fmt, act, float(err.max()))
+
+
+@pytest.mark.parametrize("M", [24, 64])
+@pytest.mark.parametrize("fmt,act", [("f16", "gelu"), ("bf16", "silu"), ("bf16", "relu")])
+def test_stream_kernel_row_blocks_with_bias_and_activation(M, fmt, act):
+    """The streaming kernel with 2 and 4 blocks of 16 rows of A (M = 24, 64)
+    under the bias + activation epilogue and bfloat16, against the oracle's
+    double-precision epilogue; rows past M of the last block are never
+    stored."""
+    import torch as t
+    N, K = 1088, 2048
+    A, B = synth.random_operands(M, N, K, seed=M + 93, b_scale=K ** -0.5, fmt=fmt)
+    bias = synth.random_operands(1, N, 1, seed=94, fmt=fmt)[1].reshape(N)
+    dA, dB, db = to_dev(A), to_dev(B), to_dev(bias)
+    dC = full_dev(((M + 2) * N,), SENTINEL)
+    s = t.cuda.current_stream().cuda_stream
+    fn = gr.gemm_bias_act_f16_forced if fmt == "f16" else gr.gemm_bias_act_bf16_forced
+    st = fn(M, N, K, dA.data_ptr(), K, dB.data_ptr(), N, db.data_ptr(), gr.ACT_CODES[act], dC.data_ptr(), N, s,
+            gr.GR_PATH_SMALL_M)
+    t.cuda.synchronize()
+    assert st == gr.GR_OK
+    Cf = from_dev(dC)
+    assert np.all(Cf[M * N:] == SENTINEL), "a row past M was written"
+    got = as_f64(Cf[:M * N].reshape(M, N), fmt)
+    ref = as_f64(oracle.gemm_relu_full(A, B, fmt=fmt, bias=bias, act=act), fmt)
+    assert np.all(np.isfinite(got))
+    err = np.abs(got - ref)
+    assert np.all(err <= 1e-2 + 1e-2 * np.abs(ref)), (M, fmt, act, float(err.max()))
