@@ -232,11 +232,13 @@ int gemm_relu_f16_forced_order(int64_t M, int64_t N, int64_t K,
  *     runs the pipelined kernel on the copies: two launches on the stream,
  *     one extra read and write of the copied operands.  Bit-exact against
  *     the other tile paths (same MFMA steps, same k order).
- *   - GR_PATH_SMALL_M_SPLIT.  For M <= 16 (with 16-byte rows of B) the K
- *     range is split so that each workgroup streams 256 columns of B over a
- *     part of K; the fp32 partial sums (splits x M x N) go to the workspace
- *     and a second launch adds them in split order, applies ReLU and rounds.
- *     Same result as GR_PATH_SMALL_M up to fp32 summation order.
+ *   - GR_PATH_SMALL_M_SPLIT.  For M <= 16 where the single pass would leave
+ *     CUs idle, the K range is split so that each workgroup streams 128
+ *     columns of B (256 columns on the register-staged kernel, for K % 32
+ *     != 0) over a part of K; the fp32 partial sums (splits x M x N) go to
+ *     the workspace and a second launch adds them in split order, applies
+ *     ReLU and rounds.  Same result as GR_PATH_SMALL_M up to fp32 summation
+ *     order.
  *   - GR_PATH_TILE_SPLIT.  For pipelined-path problems with too few 128x128
  *     tiles to fill the chip and a long K, each tile's K range is split; the
  *     fp32 partial sums go to the workspace and the same second launch sums
