@@ -530,6 +530,33 @@ __device__ __forceinline__ void stage_relu_tile(const f32x4 (&acc)[BM][BN], uint
     }
 }
 
+// Elements [s, s + L) (s >= 0, L >= 1, s + L <= 8) of the eight 16-bit
+// values in v, to dst[s], ..., dst[s + L - 1]: at most two stores of 4, 2 or
+// 1 elements, overlapping when L is not 4, 2 or 1 (the lane then writes the
+// shared elements twice, with the same bits).  Replaces up to eight 2-byte
+// stores per partial row segment of C.  The stores may be misaligned: the
+// memory system of this part splits a misaligned access itself (the
+// direct-to-LDS copies read from any 2-byte address on the same footing).
+__device__ __forceinline__ void store_run(uint16_t* dst, const u32x4& v, int s, int L) {
+    const uint64_t lo = (uint64_t)v[1] << 32 | v[0];
+    const uint64_t hi = (uint64_t)v[3] << 32 | v[2];
+    // elements j, j + 1, ... in the low bits (0 <= j <= 7; zeros past 7)
+    auto from = [&](int j) -> uint64_t {
+        if (j == 0) return lo;
+        if (j < 4) return (lo >> (16 * j)) | (hi << (64 - 16 * j));
+        return hi >> (16 * (j - 4));
+    };
+    if (L >= 4) {
+        *reinterpret_cast<uint64_t*>(dst + s) = from(s);
+        *reinterpret_cast<uint64_t*>(dst + s + L - 4) = from(s + L - 4);
+    } else if (L >= 2) {
+        *reinterpret_cast<uint32_t*>(dst + s) = (uint32_t)from(s);
+        *reinterpret_cast<uint32_t*>(dst + s + L - 2) = (uint32_t)from(s + L - 2);
+    } else {
+        dst[s] = (uint16_t)from(s);
+    }
+}
+
 // acc may be overwritten.
 // col_min: with EDGE, columns below it belong to the tile on the left (a last
 // tile column moved left to end at column N) and are not stored either.
@@ -570,9 +597,10 @@ __device__ __forceinline__ void store_wave_tile(Acc& acc, uint8_t* region, uint3
                     __builtin_nontemporal_store(u32x2{v[2], v[3]}, reinterpret_cast<u32x2*>(dst + 4));
                 }
             } else {
-#pragma unroll
-                for (int e = 0; e < 8; ++e)
-                    if (n + e < N && n + e >= col_min) dst[e] = (uint16_t)(v[e >> 1] >> (16 * (e & 1)));
+                // a partial row segment: the columns in [col_min, N)
+                const int64_t first = n < col_min ? col_min - n : 0;
+                const int64_t end = N - n < 8 ? N - n : 8;
+                if (end > first) store_run(dst, v, (int)first, (int)(end - first));
             }
         }
     } else {

@@ -73,12 +73,14 @@ int vec_width(uintptr_t p, int64_t ld) {
     return 1;
 }
 
-// Widest store into C (fp16 elements): 8 (16-byte rows), 4 (8-byte rows) or 1.
-int vec_width_c(uintptr_t p, int64_t ld) {
-    if (p % 16 == 0 && ld % 8 == 0) return 8;
-    if (p % 8 == 0 && ld % 4 == 0) return 4;
-    return 1;
-}
+// Width of the stores into C (16-bit elements): 8, wherever C's rows start.
+// The memory system of this part splits a misaligned access itself (the
+// direct-to-LDS copies read from any 2-byte address on the same footing),
+// and one 16-byte store per 8 elements beats eight 2-byte ones: at 4099 x
+// 3071 x 2050 with a row pitch of 3071, 2-byte stores cost 13.7 us more.
+// Partial row segments at the edges of C take at most two stores
+// (epi::store_run).
+int vec_width_c(uintptr_t, int64_t) { return 8; }
 
 // Argument checks.  The workspace (ws, ws_bytes) is optional: a size of 0
 // means none; a negative size or a misaligned workspace is GR_ERR_INVALID_ARG,
@@ -201,7 +203,8 @@ bool tile_fast_ok(int64_t M, int64_t N, int64_t K, uintptr_t A, int64_t lda, uin
 }
 
 // The persistent tile loop: whole 256 x 256 tiles, K % 64 == 0 (the 64-deep
-// A strips), 16-byte rows of C (its 32-row epilogue writes 16-byte segments).
+// A strips), 16-byte stores into C (its 32-row epilogue writes 16-byte
+// segments).
 constexpr int64_t kPersistentWorkgroups = 256;  // one per CU
 bool tile_persistent_ok(int64_t M, int64_t N, int64_t K, uintptr_t A, int64_t lda, uintptr_t B, int64_t ldb,
                         uintptr_t C, int64_t ldc) {

@@ -67,28 +67,16 @@ struct Frags {
     f16x8 b[FN];
 };
 
-// Tail of K for misaligned rows (UA): the first T = (K - 1) % 64 + 1 columns
-// of A and rows of B, loaded element by element with guards (zero past k = T)
-// and written to LDS in the layout of one A strip and two B strips.  Thread t
-// owns 8 chunks of 8 elements of each operand: A rows t/8 + 32 i, chunk t%8;
-// B rows t/32 + 8 i, chunk t%32.
-template <typename F>
-__device__ __forceinline__ u32x4 load8_guarded(const uint16_t* p, int64_t valid, F&& ok) {
-    uint32_t h[8];
-#pragma unroll
-    for (int e = 0; e < 8; ++e) h[e] = (e < valid && ok()) ? (uint32_t)p[e] : 0u;
-    return u32x4{h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16), h[6] | (h[7] << 16)};
-}
-
 // E: element type (ElemF16 or ElemBF16; only the MFMA and the rounding
 // differ) or Epi<...> for bias + activation.
 // UA (with EDGE, M >= 256, N >= 256, K > 128): rows of A and B need not be
 // 16-byte aligned and K need not be a multiple of 64.  The direct-to-LDS
 // copies read any 2-byte aligned address (measured on this part: every
-// offset gives the bytes of the offset address); the first T = (K - 1) % 64
-// + 1 steps of k are staged through registers with guards and multiplied
-// before the pipeline starts, and the pipeline then runs over the remaining
-// K - T (a multiple of 64).  The last tile column is moved left to end at
+// offset gives the bytes of the offset address); the last T = (K - 1) % 64 +
+// 1 steps of k are copied like a strip from k = K - 64 and multiplied, with
+// the elements at k < K - T zeroed in both operands' fragments, before the
+// pipeline starts, and the pipeline then runs over [0, K - T) (a multiple of
+// 64).  The last tile column is moved left to end at
 // column N, like the last tile row, so every copy reads inside [0, M) x
 // [T, K) of A and [T, K) x [0, N) of B: nothing outside the operands is ever
 // read, whatever their alignment.  Tail first means a different k order
@@ -138,7 +126,8 @@ __global__ __launch_bounds__(THREADS, 1) void gemm_relu_tile3_kernel(
     int64_t m0 = EDGE ? edge::shifted_row0(m_tile, M, BM) : m_tile;
     const int64_t n_tile = (int64_t)tn * BN;
     int64_t n0 = UA ? edge::shifted_col0(n_tile, N, BN) : n_tile;
-    // UA: the K tail handled first (1..64 deep); the pipeline covers [T, K).
+    // UA: the last T = 1..64 steps of k handled first; the pipeline covers
+    // [0, K - T).
     const int64_t T = UA ? (K - 1) % BKA + 1 : 0;
 
     // ---- copies -------------------------------------------------------------
@@ -147,8 +136,8 @@ __global__ __launch_bounds__(THREADS, 1) void gemm_relu_tile3_kernel(
     // one.  lane -> row lane/8, slot lane%8 (chunk slot XOR (row/2)%8).
     // B strip (16 KiB) = 16 blocks of 2 rows x 512 bytes; this wave fills
     // blocks 4w .. 4w+3.  lane -> row lane/32, slot lane%32.
-    const uint8_t* base_a = reinterpret_cast<const uint8_t*>(A + m0 * lda + T);
-    const uint8_t* base_b = reinterpret_cast<const uint8_t*>(B + T * ldb + n0);  // PERSIST: next tile's later
+    const uint8_t* base_a = reinterpret_cast<const uint8_t*>(A + m0 * lda);
+    const uint8_t* base_b = reinterpret_cast<const uint8_t*>(B + n0);  // PERSIST: next tile's later
     const int64_t step_a = BKA * 2;
     const int64_t step_b = (int64_t)BK * ldb * 2;
     // The odd-step half (blocks +4, rows +32) only adds a wave-uniform
@@ -238,20 +227,31 @@ __global__ __launch_bounds__(THREADS, 1) void gemm_relu_tile3_kernel(
     uint32_t KT = (uint32_t)((K - T) / BK);  // even, >= 2 (UA: >= 4)
     uint32_t KTA = KT / 2;
 
-    // UA: the tail's guarded loads go out first, so that they complete before
-    // the prologue copies behind them.
-    u32x4 tail_a[8], tail_b[8];
+    // UA: the tail strip, k in [K - 64, K) (inside the operands, as K >
+    // 128), is copied first into the slots the prologue leaves free: A slot
+    // 2, and B slots 3 (k < K - 32, needed only when T > 32) and 2 (k >= K -
+    // 32).  Its elements at k < K - T belong to the pipeline's last strip:
+    // they are zeroed in the fragments of both operands after the reads, so
+    // they add nothing, whatever their values.  The pipeline then starts at
+    // k = 0, where the rows start: on rows aligned to 128 bytes its copies
+    // read whole cache lines, whatever K.
     if constexpr (UA) {
+        const uint8_t* tail_a = reinterpret_cast<const uint8_t*>(A + m0 * lda + (K - BKA));
+        const uint8_t* tail_b = reinterpret_cast<const uint8_t*>(B + (K - BKA) * ldb + n0);
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const uint32_t r = tid / 8 + 32 * i, c = tid % 8;
-            tail_a[i] = load8_guarded(A + (m0 + r) * lda + 8 * c, T - 8 * (int64_t)c, [] { return true; });
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+            for (int c = 0; c < 4; ++c)
+                dma16(tail_a + h * half_a, off_a[c],
+                      lds_base + A_BASE + 2 * A_SLOT_BYTES + (8u * wave + 4u * h + (uint32_t)c) * 1024u);
+        if (T > BK) {
+#pragma unroll
+            for (int c = 0; c < 4; ++c)
+                dma16(tail_b, off_b[c], lds_base + 3 * B_SLOT_BYTES + (4u * wave + (uint32_t)c) * 1024u);
         }
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const uint32_t k = tid / 32 + 8 * i, c = tid % 32;
-            tail_b[i] = load8_guarded(B + k * ldb + n0 + 8 * c, 8, [&] { return (int64_t)k < T; });
-        }
+        for (int c = 0; c < 4; ++c)
+            dma16(tail_b + step_b, off_b[c], lds_base + 2 * B_SLOT_BYTES + (4u * wave + (uint32_t)c) * 1024u);
     }
 
     // Prologue copies, in this order: A0, B0, B1, A1, B2.
@@ -281,35 +281,34 @@ __global__ __launch_bounds__(THREADS, 1) void gemm_relu_tile3_kernel(
     };
     prologue_a0_b0_b1_a1();
     if constexpr (UA) {
-        // The tail's loads have landed once at most the 24 copies above
-        // (A0, B0, B1, A1) remain.  A tail -> A slot 2, B tail -> B slots 3
-        // (k < 32) and 2 (k >= 32): the slots the prologue leaves free.
+        // The tail's copies, issued before the 24 above (A0, B0, B1, A1),
+        // have landed once at most those 24 remain; the barrier makes every
+        // wave's part visible.
         wait_vmcnt<24>();
-        uint8_t* lds_a2 = lds + A_BASE + 2 * A_SLOT_BYTES;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const uint32_t r = tid / 8 + 32 * i, c = tid % 8;
-            *reinterpret_cast<u32x4*>(lds_a2 + a64_off(r, c)) = tail_a[i];
-        }
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const uint32_t k = tid / 32 + 8 * i, c = tid % 32;
-            uint8_t* slot = lds + (k < 32 ? 3 : 2) * B_SLOT_BYTES;
-            *reinterpret_cast<u32x4*>(slot + b_off(k & 31u, c)) = tail_b[i];
-        }
         __syncthreads();
-        Frags ft;
+        // In half H of the strip, both operands of this lane hold k = K - 64
+        // + 32 H + 8 (lane / 16) + e, e = 0..7: keep the elements with k >=
+        // K - T, i.e. e >= v below.
+        auto tail_half = [&](auto h_c, uint32_t bo) {
+            constexpr uint32_t H = decltype(h_c)::value;
+            const int v = (int)(BKA - T) - (int)(32u * H + 8u * (lane >> 4));
+            u32x4 keep;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) read_one(H0{}, ft, 2 * A_SLOT_BYTES, 3 * B_SLOT_BYTES, r);
+            for (int d = 0; d < 4; ++d)
+                keep[d] = (2 * d >= v ? 0x0000FFFFu : 0u) | (2 * d + 1 >= v ? 0xFFFF0000u : 0u);
+            Frags ft;
 #pragma unroll
-        for (int t = 0; t < 64; ++t) mfma_one(ft, t);
-        if (T > BK) {
+            for (int r = 0; r < 16; ++r) read_one(h_c, ft, 2 * A_SLOT_BYTES, bo, r);
 #pragma unroll
-            for (int r = 0; r < 16; ++r) read_one(H1{}, ft, 2 * A_SLOT_BYTES, 2 * B_SLOT_BYTES, r);
+            for (int i = 0; i < FM; ++i) ft.a[i] = __builtin_bit_cast(f16x8, __builtin_bit_cast(u32x4, ft.a[i]) & keep);
+#pragma unroll
+            for (int j = 0; j < FN; ++j) ft.b[j] = __builtin_bit_cast(f16x8, __builtin_bit_cast(u32x4, ft.b[j]) & keep);
 #pragma unroll
             for (int t = 0; t < 64; ++t) mfma_one(ft, t);
-        }
-        // every wave is done with B slot 2 before B strip 2 is copied into it
+        };
+        if (T > BK) tail_half(H0{}, 3 * B_SLOT_BYTES);
+        tail_half(H1{}, 2 * B_SLOT_BYTES);
+        // every wave is done with the tail's slots before strips are copied into them
         __syncthreads();
     }
     prologue_b2();

@@ -124,7 +124,8 @@ typedef struct gr_plan_t {
     int64_t grid;        /* workgroups launched (1-D grid)                            */
     int32_t vec_a;       /* fp16 elements per global load of A (8, 4, 2 or 1)         */
     int32_t vec_b;       /* fp16 elements per global load of B                        */
-    int32_t vec_c;       /* fp16 elements per global store of C (8, 4 or 1)           */
+    int32_t vec_c;       /* fp16 elements per global store of C (8 at any alignment; 1
+                            on the small-M paths, which store elements)               */
     int32_t group_m;     /* tile rows per workgroup-order group (L2 reuse)           */
     int32_t packed;      /* GR_PATH_TILE_PACKED: bit 0 = A copied, bit 1 = B copied     */
     int64_t workspace;   /* bytes of the caller's workspace the path uses (else 0)     */

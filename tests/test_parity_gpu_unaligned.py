@@ -1,9 +1,10 @@
 """GPU parity of the pipelined 256 x 256 kernel on misaligned rows and ragged K
 (GR_PATH_TILE_UNALIGNED) against the CPU oracle.
 
-The path copies operand rows into LDS from any 2-byte aligned address, stages
-the first (K - 1) % 64 + 1 steps of k through registers with zero guards
-(the pages' rule that out-of-range elements of both operands read as zero,
+The path copies operand rows into LDS from any 2-byte aligned address,
+multiplies the last (K - 1) % 64 + 1 steps of k first, from a strip copied
+from k = K - 64 whose elements before the tail are zeroed in both operands (the
+pages' rule that out-of-range elements of both operands read as zero,
 TileLang tutorial, chapter "动态形状与变长序列"), and moves the last tile row
 and column to end at M and N.  Bar as everywhere: |gpu - oracle| <= 1e-2 +
 1e-2 |oracle| per element, no NaN or Inf, padding of C and rows past M never
@@ -33,6 +34,11 @@ CASES = [
     (260, 520, 319, 320, 522, 520, (5, 3, 0)),      # tail 63
     (520, 260, 192, 192, 262, 261, (0, 7, 0)),      # tail 64 (K % 64 == 0, rows misaligned)
     (1024, 1024, 4100, 4100, 1024, 1024, (0, 0, 0)),  # aligned rows, K % 64 == 4, long K
+    # 16-byte rows of C (16-byte stores) while the last tile column, moved
+    # left to end at N, starts at an odd column (267, 515): its stores are
+    # 2-byte aligned and must still leave columns N.. of C alone
+    (300, 523, 130, 130, 528, 528, (0, 0, 0)),      # tail 2
+    (513, 771, 200, 200, 776, 776, (0, 0, 8)),      # tail 8, C offset by 16 bytes
 ]
 
 
