@@ -39,6 +39,7 @@ GR_PATH_SMALL_M_SPLIT = 5
 GR_PATH_TILE_SPLIT = 6
 GR_PATH_TILE_UNALIGNED = 7
 GR_PATH_TILE_PERSISTENT = 8
+GR_PATH_TILE_STREAM = 9
 GR_READ_CONTIGUOUS = 0
 GR_READ_ROW_PIECES = 1
 
@@ -59,7 +60,8 @@ ACT_CODES = {"none": GR_ACT_NONE, "relu": GR_ACT_RELU, "gelu": GR_ACT_GELU, "gel
 PATH_NAMES = {GR_PATH_NONE: "none", GR_PATH_TILE: "tile", GR_PATH_TILE_EDGE: "tile_edge",
               GR_PATH_SMALL_M: "small_m", GR_PATH_TILE_PACKED: "tile_packed",
               GR_PATH_SMALL_M_SPLIT: "small_m_split", GR_PATH_TILE_SPLIT: "tile_split",
-              GR_PATH_TILE_UNALIGNED: "tile_unaligned", GR_PATH_TILE_PERSISTENT: "tile_persistent"}
+              GR_PATH_TILE_UNALIGNED: "tile_unaligned", GR_PATH_TILE_PERSISTENT: "tile_persistent",
+              GR_PATH_TILE_STREAM: "tile_stream"}
 
 
 class gr_plan_t(ctypes.Structure):

@@ -133,10 +133,13 @@ bool smallm_rows_ok(int64_t M, int64_t N, int64_t K, uintptr_t A, int64_t lda, u
 constexpr int kStreamNB = 64, kStreamW = 4, kStreamR = 2;  // single pass: 64-column blocks, 4 waves x 2 slots
 constexpr int kStreamSplitNB = 128, kStreamSplitW = 2, kStreamSplitR = 2;  // split: 128 columns, 2 waves x 2 slots
 constexpr int kStreamTaW = 8;  // A given transposed (gathered into registers): 8 waves x 1 slot
+// The copy offsets are 32-bit: 32 rows of B and at most 64 rows of A per
+// workgroup keep them below 2^32 for pitches up to 2^25 elements.
+constexpr int64_t kStreamMaxLd = int64_t(1) << 25;
 bool smallm_stream_ok(int64_t M, int64_t N, int64_t K, uintptr_t A, int64_t lda, int64_t ldb, int64_t nb,
                       int64_t max_rows = kSmallMThreshold) {
     return M >= 1 && M <= max_rows && K > 0 && K % 32 == 0 && A % 16 == 0 && lda % 8 == 0 && N >= nb &&
-           ldb <= gr::tile2::MAX_LDB;
+           lda <= kStreamMaxLd && ldb <= kStreamMaxLd;
 }
 
 // Split-K layout of the small-M path: S splits of k_per_split (a multiple of
@@ -231,6 +234,28 @@ bool use_large_tiles(int64_t M, int64_t N) {
     if (M < BM) return false;
     const int64_t tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
     return tiles > kSmallTileMaxLargeTiles;
+}
+
+// Blocks of 64 rows x 64 columns on the streaming kernel (TILE_STREAM): in
+// each workgroup the 4 waves take the 32-row slots of K in turn through
+// rings of their own, with no barrier in the loop, and add their partial
+// sums in LDS at the end.  Where 128 x 128 tiles would be fewer than 128,
+// this gives four times as many workgroups and a quarter of the K steps per
+// wave.  Measured (us, back to back): 1024^3 8.45 against 12.1 for the 128
+// x 128 kernel, 1024 x 1024 x 4096 19.8 against 38.3, 512 x 1024 x 1024 8.4
+// against 12.6; from 128 tiles on the 128 x 128 kernel is as fast or faster
+// (1024 x 2048 x 1024: 12.8 against 12.3; 2048^3: 35.9 against 22.6).
+// Needs what the streaming kernel needs: K % 32 == 0, 16-byte rows of A,
+// N >= 64; B of any alignment.
+constexpr int64_t kTileStreamRows = 64;  // 4 blocks of 16 rows per workgroup
+constexpr int64_t kTileStreamMaxSmallTiles = 128;
+bool tile_stream_ok(int64_t M, int64_t N, int64_t K, uintptr_t A, int64_t lda, int64_t ldb) {
+    return smallm_stream_ok(M, N, K, A, lda, ldb, kStreamNB, kMaxDim);
+}
+bool tile_stream_wanted(int64_t M, int64_t N) {
+    using namespace gr::tile128;
+    return M > kSmallMMaxRows && !use_large_tiles(M, N) &&
+           ((M + BM - 1) / BM) * ((N + BN - 1) / BN) < kTileStreamMaxSmallTiles;
 }
 
 bool tile_unaligned_ok(int64_t M, int64_t N, int64_t K, int64_t lda, int64_t ldb) {
@@ -384,6 +409,18 @@ void fill_plan(int path, int64_t M, int64_t N, int64_t K, uintptr_t A, int64_t l
         p->group_m = 1;
         p->workspace = sp.bytes;
         p->split_k = (int32_t)sp.splits;
+    } else if (path == GR_PATH_TILE_STREAM) {
+        p->block_m = (int32_t)kTileStreamRows;
+        p->block_n = kStreamNB;
+        p->block_k = gr::smallm::KSTEP;
+        p->stages = kStreamR;
+        p->threads = 64 * kStreamW;
+        p->grid = ((N + kStreamNB - 1) / kStreamNB) * ((M + kTileStreamRows - 1) / kTileStreamRows);
+        p->vec_a = 8;
+        p->vec_b = 8;  // 16-byte copies from any 2-byte address
+        p->vec_c = 1;
+        p->group_m = 1;
+        p->split_k = 1;
     } else if (path == GR_PATH_SMALL_M) {
         using namespace gr::smallm;
         // the streaming kernel where it applies (vec_b 8: 16-byte copies of B
@@ -422,6 +459,7 @@ int choose_path(int64_t M, int64_t N, int64_t K, uintptr_t A, int64_t lda, uintp
         (smallm_rows_ok(M, N, K, A, lda, B, ldb) || smallm_stream_ok(M, N, K, A, lda, ldb, kStreamNB, kSmallMMaxRows)) &&
         (N + gr::smallm::NB - 1) / gr::smallm::NB <= 256)
         return GR_PATH_SMALL_M;
+    if (tile_stream_wanted(M, N) && tile_stream_ok(M, N, K, A, lda, ldb)) return GR_PATH_TILE_STREAM;
     if (fast) return GR_PATH_TILE;
     if (tile_unaligned_ok(M, N, K, lda, ldb) && use_large_tiles(M, N)) return GR_PATH_TILE_UNALIGNED;
     if (ws_bytes > 0 && pack_layout(M, N, K, A, lda, B, ldb, pk) && pk->bytes <= ws_bytes &&
@@ -653,6 +691,14 @@ int run(const gr_plan_t& p, int64_t M, int64_t N, int64_t K, const uint16_t* A, 
                 case 2: return launch_tile_vb<true, 2, E>(p, M, N, K, A, lda, B, ldb, C, ldc, ep, stream);
                 default: return launch_tile_vb<true, 1, E>(p, M, N, K, A, lda, B, ldb, C, ldc, ep, stream);
             }
+        case GR_PATH_TILE_STREAM: {
+            using namespace gr::smallm;
+            const uint32_t nb = (uint32_t)((N + kStreamNB - 1) / kStreamNB);
+            static_assert(kTileStreamRows == 4 * MAX_M, "4 blocks of 16 rows per workgroup");
+            return launch(gemm_relu_smallm_stream_kernel<kStreamNB, kStreamW, kStreamR, stream::WHOLE, E, false, 4, true>,
+                          p.grid, p.threads, stream, A, B, C, static_cast<float*>(nullptr), M, N, K, lda, ldb, ldc, K,
+                          nb, ep);
+        }
         case GR_PATH_SMALL_M: {
             using namespace gr::smallm;
             if (p.vec_b == 8) {
@@ -728,6 +774,8 @@ int plan_call(int64_t M, int64_t N, int64_t K, uintptr_t a, int64_t lda, uintptr
                 return GR_ERR_INVALID_PATH;
         } else if (forced == GR_PATH_SMALL_M_SPLIT) {
             if (!smallm_split_layout(M, N, K, a, lda, b, ldb, sp) || sp->bytes > ws_bytes) return GR_ERR_INVALID_PATH;
+        } else if (forced == GR_PATH_TILE_STREAM) {
+            if (!tile_stream_ok(M, N, K, a, lda, ldb)) return GR_ERR_INVALID_PATH;
         } else if (forced != GR_PATH_TILE_EDGE) {
             return GR_ERR_INVALID_PATH;
         }
@@ -811,7 +859,7 @@ int entry_epi(int64_t M, int64_t N, int64_t K, const uint16_t* A, int64_t lda, c
 bool known_path(int path) {
     return path == GR_PATH_TILE || path == GR_PATH_TILE_EDGE || path == GR_PATH_SMALL_M ||
            path == GR_PATH_TILE_PACKED || path == GR_PATH_SMALL_M_SPLIT || path == GR_PATH_TILE_SPLIT ||
-           path == GR_PATH_TILE_UNALIGNED || path == GR_PATH_TILE_PERSISTENT;
+           path == GR_PATH_TILE_UNALIGNED || path == GR_PATH_TILE_PERSISTENT || path == GR_PATH_TILE_STREAM;
 }
 
 bool needs_workspace(int path) {

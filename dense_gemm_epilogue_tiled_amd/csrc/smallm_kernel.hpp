@@ -251,12 +251,19 @@ __device__ __forceinline__ uint32_t chunk_slot(uint32_t row, uint32_t c) { retur
 
 }  // namespace stream
 
-template <int NB, int W, int R, int MODE, typename E = ElemF16, bool AT = false, int MB = 1>
+template <int NB, int W, int R, int MODE, typename E = ElemF16, bool AT = false, int MB = 1, bool RBLK = false>
 __global__ __launch_bounds__(64 * W, 1) void gemm_relu_smallm_stream_kernel(
     const uint16_t* __restrict__ A, const uint16_t* __restrict__ B, uint16_t* __restrict__ C,
     float* __restrict__ part, int64_t M, int64_t N, int64_t K, int64_t lda, int64_t ldb, int64_t ldc,
     int64_t k_per_split, uint32_t n_blocks, EpiArgs ep) {
-    using tile2::dma16_nt;
+    // RBLK: blocks of 16 MB rows over all of M, one per workgroup row of the
+    // grid (workgroup (cb, rb) = blockIdx cb + n_blocks rb), all of K, the
+    // copies cached (every operand block is read by several workgroups).
+    static_assert(!RBLK || (MODE == stream::WHOLE && !AT), "row blocks: one pass, A row-major");
+    auto copy16 = [](const void* base, uint32_t voff, uint32_t lds_addr) {
+        if constexpr (RBLK) tile2::dma16(base, voff, lds_addr);
+        else tile2::dma16_nt(base, voff, lds_addr);
+    };
     constexpr bool ADMA = !AT;                           // A copied into the slot beside B
     constexpr int ROWB = 2 * NB;                         // bytes of one row piece
     constexpr int CH = NB / 8;                           // 16-byte chunks per row piece
@@ -277,7 +284,13 @@ __global__ __launch_bounds__(64 * W, 1) void gemm_relu_smallm_stream_kernel(
     const uint32_t tid = threadIdx.x, lane = tid & 63u;
     const uint32_t w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const uint32_t cb = blockIdx.x % n_blocks;
-    const int64_t s = blockIdx.x / n_blocks;
+    int64_t s = blockIdx.x / n_blocks;
+    if constexpr (RBLK) {
+        A += s * ROWS * lda;
+        C += s * ROWS * ldc;
+        M = M - s * ROWS < ROWS ? M - s * ROWS : ROWS;
+        s = 0;
+    }
     const int64_t n_own = (int64_t)cb * NB;
     const int64_t n0 = n_own + NB <= N ? n_own : N - NB;  // the last block ends at column N
     const int64_t k_begin = s * k_per_split;
@@ -326,12 +339,12 @@ __global__ __launch_bounds__(64 * W, 1) void gemm_relu_smallm_stream_kernel(
         const uint32_t dst = ring + (uint32_t)(q % R) * SLOT;
         const uint8_t* src = reinterpret_cast<const uint8_t*>(b_range + t * stream::SLOT_ROWS * ldb);
 #pragma unroll
-        for (int i = 0; i < DPS; ++i) dma16_nt(src, voff[i], dst + i * 1024);
+        for (int i = 0; i < DPS; ++i) copy16(src, voff[i], dst + i * 1024);
         if constexpr (ADMA) {
 #pragma unroll
             for (int mb = 0; mb < MB; ++mb)
-                dma16_nt(reinterpret_cast<const uint8_t*>(A + k_begin + t * stream::SLOT_ROWS), aoff[mb],
-                         dst + BSLOT + 1024 * mb);
+                copy16(reinterpret_cast<const uint8_t*>(A + k_begin + t * stream::SLOT_ROWS), aoff[mb],
+                       dst + BSLOT + 1024 * mb);
         } else {
             const int64_t k = k_begin + t * stream::SLOT_ROWS + 8 * ag;
             uint32_t h[8];

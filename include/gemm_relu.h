@@ -105,13 +105,22 @@ extern "C" {
 #define GR_PATH_TILE_UNALIGNED 7 /* the pipelined 256x256 kernel in place on rows that are  */
                                  /* not 16-byte aligned and/or K % 64 != 0: direct-to-LDS */
                                  /* copies from any 2-byte address, the K tail (1..64)    */
-                                 /* staged with guards first; M, N >= 256, K > 128, more  */
-                                 /* than 128 tiles (planner); no workspace                 */
+                                 /* copied as one strip and masked; M, N >= 256, K > 128, */
+                                 /* more than 128 tiles (planner); no workspace            */
 #define GR_PATH_TILE_PERSISTENT 8 /* the pipelined 256x256 kernel as a persistent tile loop: */
                                   /* at most one workgroup per CU, each storing a finished */
                                   /* tile while the next tile's first copies are in flight */
                                   /* (TileLang tutorial, "Persistent kernel"); whole tiles, */
-                                  /* K % 64 == 0, 16-byte rows of A, B and C               */
+                                  /* K % 64 == 0, 16-byte rows of A and B                  */
+#define GR_PATH_TILE_STREAM 9 /* blocks of 64 rows x 64 columns on the streaming kernel:  */
+                              /* the block's 4 waves split K between them (rings of      */
+                              /* direct-to-LDS copies of their own, no barrier in the    */
+                              /* loop) and add their partial sums in order at the end;   */
+                              /* K % 32 == 0, 16-byte rows of A, N >= 64, B of any       */
+                              /* alignment; the planner's choice where 128x128 tiles     */
+                              /* would number fewer than 128 (few tiles: the split-K    */
+                              /* remedy of the TileLang tutorial's "性能取证", within one */
+                              /* workgroup); no workspace                                 */
 
 /* What the planner decided for one problem.  Filled by gemm_relu_f16_plan. */
 typedef struct gr_plan_t {

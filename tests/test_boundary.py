@@ -134,7 +134,7 @@ def test_span_overflow_is_too_large():
 
 def test_plan_for_each_workload():
     expect = {
-        "square1024": gr.GR_PATH_TILE,
+        "square1024": gr.GR_PATH_TILE_STREAM,
         "square4096": gr.GR_PATH_TILE,
         "ragged4099x3071x2050": gr.GR_PATH_TILE_UNALIGNED,
         "mlp8192x28672x8192": gr.GR_PATH_TILE,
@@ -144,11 +144,52 @@ def test_plan_for_each_workload():
         st, p = plan(w.M, w.N, w.K)
         assert st == gr.GR_OK
         assert p["path"] == expect[name], (name, p)
-        if p["path"] in (gr.GR_PATH_TILE, gr.GR_PATH_TILE_EDGE, gr.GR_PATH_TILE_UNALIGNED):
+        if p["path"] in (gr.GR_PATH_TILE, gr.GR_PATH_TILE_EDGE, gr.GR_PATH_TILE_UNALIGNED, gr.GR_PATH_TILE_STREAM):
             tiles = -(-w.M // p["block_m"]) * -(-w.N // p["block_n"])
             assert p["grid"] == tiles
         else:
             assert p["grid"] == -(-w.N // p["block_n"])
+
+
+def test_plan_tile_stream_where_128_tiles_are_few():
+    # 64 x 64 blocks on the streaming kernel where 128 x 128 tiles would be
+    # fewer than 128 (and M > 64: fewer rows are the small-M path)
+    for M, N, K in ((1024, 1024, 1024), (512, 1024, 1024), (1000, 1000, 1024), (65, 4096, 512),
+                    (1024, 1024, 16384)):
+        st, p = plan(M, N, K)
+        assert st == gr.GR_OK and p["path"] == gr.GR_PATH_TILE_STREAM, (M, N, K, p)
+        assert (p["block_m"], p["block_n"], p["threads"]) == (64, 64, 256)
+        assert p["grid"] == -(-M // 64) * -(-N // 64)
+    # 128 tiles and more: the 128 x 128 (or 256 x 256) tile kernel
+    for M, N, K in ((1024, 2048, 1024), (2048, 2048, 2048), (4096, 4096, 4096)):
+        assert plan(M, N, K)[1]["path"] == gr.GR_PATH_TILE, (M, N, K)
+    # up to 64 rows: the small-M path
+    assert plan(64, 1024, 1024)[1]["path"] == gr.GR_PATH_SMALL_M
+    # what the streaming kernel cannot take goes elsewhere: K % 32 != 0,
+    # rows of A not 16-byte aligned, N < 64
+    assert plan(1024, 1024, 1000)[1]["path"] != gr.GR_PATH_TILE_STREAM
+    assert plan(1024, 1024, 1024, lda=1028)[1]["path"] != gr.GR_PATH_TILE_STREAM
+    assert plan(1024, 1024, 1024, a=BASE_A + 2)[1]["path"] != gr.GR_PATH_TILE_STREAM
+    assert plan(1024, 48, 1024)[1]["path"] != gr.GR_PATH_TILE_STREAM
+    # B of any alignment stays on it
+    assert plan(1024, 1024, 1024, ldb=1027)[1]["path"] == gr.GR_PATH_TILE_STREAM
+
+
+def test_tile_stream_forced_checks():
+    """Forcing the row-blocked streaming path checks what its kernel needs
+    before any HIP call."""
+    base = (0x100000, 0x200000000000, 0x400000000000)
+
+    def forced(M, N, K, lda, ldb, ldc, a=base[0]):
+        return gr.gemm_relu_f16_forced(M, N, K, a, lda, base[1], ldb, base[2], ldc, None, gr.GR_PATH_TILE_STREAM)
+    assert forced(1024, 1024, 1000, 1000, 1024, 1024) == gr.GR_ERR_INVALID_PATH   # K % 32 != 0
+    assert forced(1024, 1024, 1024, 1028, 1024, 1024) == gr.GR_ERR_INVALID_PATH   # rows of A not 16-byte
+    assert forced(1024, 1024, 1024, 1024, 1024, 1024, a=base[0] + 8) == gr.GR_ERR_INVALID_PATH
+    assert forced(1024, 63, 1024, 1024, 63, 63) == gr.GR_ERR_INVALID_PATH         # N < 64
+    assert forced(4, 64, 32, (1 << 25) + 8, 64, 64) == gr.GR_ERR_INVALID_PATH      # 32-bit copy offsets
+    # accepted shapes fail only at the device check here (no GPU)
+    assert forced(1024, 1024, 1024, 1024, 1027, 1024) not in (gr.GR_ERR_INVALID_PATH, gr.GR_OK)
+    assert forced(4096, 4096, 4096, 4096, 4096, 4096) not in (gr.GR_ERR_INVALID_PATH, gr.GR_OK)
 
 
 def test_plan_ragged_vector_widths():
@@ -170,8 +211,10 @@ def test_plan_partial_tiles_take_the_pipelined_kernel():
     assert st == gr.GR_OK and p["path"] == gr.GR_PATH_TILE and p["grid"] == 17 * 12 and p["vec_c"] == 8
     assert plan(256, 1, 32, ldb=8)[1]["path"] == gr.GR_PATH_TILE
     # up to 64 rows of A and at most 256 column strips: the small-M stream
-    # (2 or 4 row blocks); more rows or wider C: the pipelined kernel (rows
-    # past M clamped); K % 32 != 0 or rows not 16-byte aligned: guarded kernel
+    # (2 or 4 row blocks); more rows: 64 x 64 blocks on the streaming kernel
+    # while 128 x 128 tiles would be fewer than 128 (B of any alignment),
+    # else the pipelined kernel (rows past M clamped); K % 32 != 0 or rows
+    # of A not 16-byte aligned: guarded kernel
     st, p = plan(17, 512, 512)
     assert p["path"] == gr.GR_PATH_SMALL_M and (p["block_m"], p["grid"]) == (32, 8)
     st, p = plan(64, 16384, 512)
@@ -179,10 +222,14 @@ def test_plan_partial_tiles_take_the_pipelined_kernel():
     st, p = plan(64, 16448, 512)
     assert p["path"] == gr.GR_PATH_TILE and (p["block_m"], p["grid"]) == (128, 129)
     st, p = plan(65, 512, 512)
-    assert p["path"] == gr.GR_PATH_TILE and (p["block_m"], p["grid"]) == (128, 4)
+    assert p["path"] == gr.GR_PATH_TILE_STREAM and (p["block_m"], p["grid"]) == (64, 16)
+    st, p = plan(65, 16384, 512)
+    assert p["path"] == gr.GR_PATH_TILE and (p["block_m"], p["grid"]) == (128, 128)
     assert plan(512, 512, 48)[1]["path"] == gr.GR_PATH_TILE_EDGE
-    assert plan(512, 500, 512)[1]["path"] == gr.GR_PATH_TILE_EDGE
-    assert plan(512, 512, 512, b=BASE_B + 8)[1]["path"] == gr.GR_PATH_TILE_EDGE
+    assert plan(512, 500, 512)[1]["path"] == gr.GR_PATH_TILE_STREAM
+    assert plan(512, 512, 512, b=BASE_B + 8)[1]["path"] == gr.GR_PATH_TILE_STREAM
+    assert plan(512, 500, 512, lda=516)[1]["path"] == gr.GR_PATH_TILE_EDGE
+    assert plan(512, 512, 512, a=BASE_A + 8)[1]["path"] == gr.GR_PATH_TILE_EDGE
 
 
 def ws_size(M, N, K, lda=None, ldb=None, ldc=None, a=BASE_A, b=BASE_B, c=BASE_C):
@@ -319,9 +366,10 @@ def test_tile_split_plan():
     assert ws_size(1024, 1024, 256) == (gr.GR_OK, 0)
     assert ws_size(4096, 4096, 4096) == (gr.GR_OK, 0)
     assert plan_ws(2048, 2048, 2048, 1 << 30)[1]["path"] == gr.GR_PATH_TILE
-    # without a workspace, or one too small: the unsplit kernel
-    assert plan(1024, 1024, 16384)[1]["path"] == gr.GR_PATH_TILE
-    assert plan_ws(1024, 1024, 16384, size - 1)[1]["path"] == gr.GR_PATH_TILE
+    # without a workspace, or one too small: 64 x 64 blocks on the streaming
+    # kernel (K split between the waves of each workgroup instead)
+    assert plan(1024, 1024, 16384)[1]["path"] == gr.GR_PATH_TILE_STREAM
+    assert plan_ws(1024, 1024, 16384, size - 1)[1]["path"] == gr.GR_PATH_TILE_STREAM
     # forced without a workspace is refused
     assert gr.gemm_relu_f16_forced(1024, 1024, 1024, BASE_A, 1024, BASE_B, 1024, BASE_C, 1024, None,
                                    gr.GR_PATH_TILE_SPLIT) == gr.GR_ERR_INVALID_PATH
@@ -348,13 +396,17 @@ def test_workspace_argument_checks():
 
 def test_plan_tile_size_choice():
     # fewer than half a wave of 256 x 256 tiles (or M < 256): 128 x 128 tiles
-    for (M, N), (bm, grid) in {(1024, 1024): (128, 64), (2048, 2048): (128, 256), (128, 4096): (128, 32),
-                               (200, 304): (128, 6), (4096, 4096): (256, 256), (2816, 2816): (128, 484),
+    for (M, N), (bm, grid) in {(2048, 2048): (128, 256), (4096, 4096): (256, 256), (2816, 2816): (128, 484),
                                (4099, 3071): (256, 204), (2048, 4096): (128, 512),
-                               (2304, 4096): (256, 144)}.items():
+                               (2304, 4096): (256, 144), (1024, 2048): (128, 128)}.items():
         st, p = plan(M, N, 512, ldb=rup(N, 8), ldc=rup(N, 8))
         assert st == gr.GR_OK and p["path"] == gr.GR_PATH_TILE, (M, N, p)
         assert (p["block_m"], p["block_n"], p["grid"]) == (bm, bm, grid), (M, N, p)
+    # fewer than 128 of those: 64 x 64 blocks on the streaming kernel
+    for (M, N), grid in {(1024, 1024): 256, (128, 4096): 128, (200, 304): 20}.items():
+        st, p = plan(M, N, 512, ldb=rup(N, 8), ldc=rup(N, 8))
+        assert st == gr.GR_OK and p["path"] == gr.GR_PATH_TILE_STREAM, (M, N, p)
+        assert (p["block_m"], p["block_n"], p["grid"]) == (64, 64, grid), (M, N, p)
 
 
 def test_plan_empty_and_k_zero():
@@ -368,7 +420,7 @@ def test_plan_small_m_threshold():
     assert plan(16, 4096, 4096)[1]["path"] == gr.GR_PATH_SMALL_M
     assert plan(17, 4096, 4096)[1]["path"] == gr.GR_PATH_SMALL_M   # two row blocks
     assert plan(64, 4096, 4096)[1]["path"] == gr.GR_PATH_SMALL_M   # four row blocks
-    assert plan(65, 4096, 4096)[1]["path"] == gr.GR_PATH_TILE
+    assert plan(65, 4096, 4096)[1]["path"] == gr.GR_PATH_TILE_STREAM  # 64 x 64 blocks
     assert plan(1, 1, 1)[1]["path"] == gr.GR_PATH_TILE_EDGE  # B row pitch 1: not 8-byte aligned
 
 
@@ -407,6 +459,10 @@ def test_planner_invariants_on_random_problems():
         elif p["path"] == gr.GR_PATH_SMALL_M:
             assert 1 <= M <= 64 and K > 0 and p["grid"] == -(-N // 64), key
             assert M <= 16 or -(-N // 64) <= 256, key  # wider C with more rows: the tile kernel
+        elif p["path"] == gr.GR_PATH_TILE_STREAM:
+            assert M > 64 and K > 0 and K % 32 == 0 and a % 16 == 0 and lda % 8 == 0 and N >= 64, key
+            assert -(-M // 128) * -(-N // 128) < 128, key  # few 128 x 128 tiles
+            assert p["block_m"] == 64 and p["grid"] == -(-M // 64) * -(-N // 64), key
         elif p["path"] == gr.GR_PATH_TILE_UNALIGNED:
             assert not (aligned and K % 32 == 0), key
             assert M >= 256 and N >= 256 and K > 128, key

@@ -244,13 +244,17 @@ def test_tile_and_edge_paths_bitwise_equal(M, N, K):
 @pytest.mark.parametrize("K", [32, 64, 96, 128, 160, 192, 224, 256, 288, 320, 384, 448, 512, 1056, 1088])
 def test_tile_pipeline_every_strip_count(M, N, K):
     """Whole tiles through the pipelined kernels (128 x 128 tiles at 512 x 256,
-    256 x 256 tiles at 2304 x 4096: the 32- and 64-deep variants), for every
-    K-loop length up to the steady state plus odd and even tails, bitwise
-    against the guarded kernel (all accumulate the same 16-deep MFMA steps in
-    the same order).  The large shape is checked against the oracle on edge
-    rows and columns, the small one in full."""
+    forced: the planner gives that shape to the streaming kernel; 256 x 256
+    tiles at 2304 x 4096: the 32- and 64-deep variants), for every K-loop
+    length up to the steady state plus odd and even tails, bitwise against
+    the guarded kernel (all accumulate the same 16-deep MFMA steps in the
+    same order).  The large shape is checked against the oracle on edge rows
+    and columns, the small one in full."""
     st, plan = gr.gemm_relu_f16_plan(M, N, K, 0x100000, K, 0x200000000000, N, 0x400000000000, N)
-    assert plan["block_m"] == (128 if M == 512 else 256), plan
+    if M == 512:
+        assert plan["path"] == gr.GR_PATH_TILE_STREAM, plan
+    else:
+        assert plan["path"] == gr.GR_PATH_TILE and plan["block_m"] == 256, plan
     A, B = synth.random_operands(M, N, K, seed=K)
     C1 = run_full(A, B, M, N, K, path=gr.GR_PATH_TILE)
     C2 = run_full(A, B, M, N, K, path=gr.GR_PATH_TILE_EDGE)
@@ -289,11 +293,13 @@ def test_pipelined_kernel_partial_tiles(M, N, K, lda, ldb, ldc):
     the result must equal the register-staged guarded kernel's bit for bit
     (same MFMA steps in the same k order)."""
     st, plan = gr.gemm_relu_f16_plan(M, N, K, 0x100000, lda, 0x200000000000, ldb, 0x400000000000, ldc)
-    assert st == gr.GR_OK and plan["path"] == gr.GR_PATH_TILE, plan
-    log("partial %dx%dx%d tile %d" % (M, N, K, plan["block_m"]))
+    # the planner's choice, or 64 x 64 blocks on the streaming kernel where
+    # 128 x 128 tiles would be few: the pipelined kernel is forced here
+    assert st == gr.GR_OK and plan["path"] in (gr.GR_PATH_TILE, gr.GR_PATH_TILE_STREAM), plan
+    log("partial %dx%dx%d plan %s" % (M, N, K, plan["path_name"]))
     A, B = synth.random_operands(M, N, K, seed=M + 3 * N + 7 * K, lda=lda, ldb=ldb)
     extra_rows = 2
-    C1 = run_full(A, B, M, N, K, lda=lda, ldb=ldb, ldc=ldc, c_rows=M + extra_rows)
+    C1 = run_full(A, B, M, N, K, lda=lda, ldb=ldb, ldc=ldc, c_rows=M + extra_rows, path=gr.GR_PATH_TILE)
     C = C1[:M * ldc].reshape(M, ldc)
     assert_parity(C[:, :N], oracle.gemm_relu_full(A, B, M=M, N=N, K=K, lda=lda, ldb=ldb),
                   "pipelined partial %dx%dx%d" % (M, N, K))
@@ -729,10 +735,12 @@ def test_transposed_b_parity(M, N, K, lda, ldbt, ldc, path):
 @pytest.mark.parametrize("M,N,K", [(512, 768, 256), (4096, 2304, 256), (300, 250, 96)])
 def test_transposed_b_matches_plain_layout_bitwise(M, N, K):
     """The same product through B (K x N) and through Bt (N x K) gives the same
-    bits: both layouts feed the same MFMA sequence."""
+    bits: both layouts feed the same MFMA sequence on the tile kernels (the
+    plain layout forced onto them: the planner gives small shapes to the
+    streaming kernel, which splits K between waves)."""
     A, Bt, B = bt_operands(M, N, K, seed=K + 3, lda=K, ldbt=K)
     Cbt = run_bt(A, Bt, M, N, K, K, K, N)
-    Cnn = run_full(A, B, M, N, K)
+    Cnn = run_full(A, B, M, N, K, path=gr.GR_PATH_TILE if N % 8 == 0 else gr.GR_PATH_TILE_EDGE)
     assert np.array_equal(Cbt[:M * N], Cnn[:M * N])
 
 

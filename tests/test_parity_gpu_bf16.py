@@ -133,10 +133,11 @@ KERNEL_CASES = [
 def test_kernel_parity(M, N, K, lda, ldb, ldc, path, what):
     """Full comparison with the oracle, padding of A and B poisoned with the
     largest finite bfloat16, C canaries beside and below the window."""
-    assert plan_path(M, N, K, lda, ldb, ldc)["path"] == path
+    planned = plan_path(M, N, K, lda, ldb, ldc)["path"]
+    assert planned == path or (path == gr.GR_PATH_TILE and planned == gr.GR_PATH_TILE_STREAM), (planned, path)
     A, B = operands(M, N, K, seed=M * 7 + N + K, lda=lda, ldb=ldb, b_scale=K ** -0.5)
     extra = 2
-    Cflat = run(A, B, M, N, K, lda, ldb, ldc, c_rows=M + extra)
+    Cflat = run(A, B, M, N, K, lda, ldb, ldc, path=path, c_rows=M + extra)
     C = Cflat[:M * ldc].reshape(M, ldc)
     assert no_nan_inf(C[:, :N])
     assert_parity(C[:, :N], ref_full(A, B, M, N, K, lda, ldb), what, fmt=FMT)
@@ -180,10 +181,11 @@ def test_unaligned_base_pointers(offs):
 def test_all_ones_rounding(M, N, K, expect, path):
     """Sum of K ones is exactly K in fp32 on every path; the kernel's final
     rounding to bfloat16 must land where the worked cases say."""
-    assert plan_path(M, N, K, K, N, N)["path"] == path
+    planned = plan_path(M, N, K, K, N, N)["path"]
+    assert planned == path or (path == gr.GR_PATH_TILE and planned == gr.GR_PATH_TILE_STREAM), (planned, path)
     A = np.full((M, K), ONE, dtype=np.uint16)
     B = np.full((K, N), ONE, dtype=np.uint16)
-    C = window(run(A, B, M, N, K), M, N, N)
+    C = window(run(A, B, M, N, K, path=path), M, N, N)
     assert np.all(as_f64(C, FMT) == expect)
 
 

@@ -1,0 +1,155 @@
+"""GPU parity of the row-blocked streaming path (GR_PATH_TILE_STREAM) against
+the CPU oracle.
+
+Blocks of 64 rows x 64 columns of C, one per workgroup; the workgroup's four
+waves take the 32-row slots of K in turn through rings of direct-to-LDS
+copies of their own and add their fp32 partial sums in wave order at the
+end, so ReLU sees the complete sum (the split-K of the TileLang tutorial's
+chapter "性能取证", kept inside one workgroup).  The planner takes it where
+128 x 128 tiles would number fewer than 128, e.g. the 1024^3 workload.
+Bar: |gpu - oracle| <= 1e-2 + 1e-2 |oracle| per element, no NaN or Inf,
+C's padding and rows past M untouched.
+"""
+import numpy as np
+import pytest
+
+import dense_gemm_epilogue_tiled_amd as gr
+import oracle
+import synth
+from gpu_util import as_f64, assert_parity, call, from_dev, full_dev, log, to_dev
+
+pytestmark = [pytest.mark.gpu, pytest.mark.usefixtures("oracle_lib")]
+
+SENTINEL = 0x7E5A
+
+# M, N, K, lda, ldb, ldc, element offsets of A, B, C (A's rows 16-byte
+# aligned: lda and A's offset multiples of 8)
+CASES = [
+    (65, 64, 32, 32, 64, 64, (0, 0, 0)),            # 2 row blocks (the second 1 row), 1 slot: 3 idle waves
+    (130, 65, 64, 64, 65, 70, (0, 1, 3)),           # last column block moved left to column 1, B odd pitch
+    (1000, 1000, 1024, 1032, 1003, 1005, (8, 3, 1)),  # ragged M and N, B and C misaligned
+    (200, 300, 96, 104, 301, 300, (0, 5, 0)),        # 3 slots, 4 waves
+    (64, 128, 4096, 4096, 128, 128, (0, 0, 0)),      # one row block, long K
+    (513, 200, 160, 168, 200, 203, (16, 0, 2)),      # 5 slots, a 1-row last block
+]
+
+
+def _run(M, N, K, lda, ldb, ldc, offs, path, seed):
+    A, B = synth.random_operands(M, N, K, seed=seed, lda=lda, ldb=ldb)
+    Ap = np.concatenate([np.zeros(offs[0], np.uint16), A.ravel()])
+    Bp = np.concatenate([np.full(offs[1], 0x7BFF, np.uint16), B.ravel()])
+    extra = 2
+    dC = full_dev((offs[2] + (M + extra) * ldc,), SENTINEL)
+    log("tile_stream %dx%dx%d lda=%d ldb=%d ldc=%d offs=%s path=%s" % (M, N, K, lda, ldb, ldc, offs, path))
+    st = call(M, N, K, to_dev(Ap), lda, to_dev(Bp), ldb, dC, ldc, path=path, offsets=offs)
+    assert st == gr.GR_OK, gr.gemm_relu_status_string(st)
+    Cflat = from_dev(dC)
+    C = Cflat[offs[2]:offs[2] + M * ldc].reshape(M, ldc)
+    assert np.all(Cflat[:offs[2]] == SENTINEL), "an element before C was written"
+    assert np.all(C[:, N:] == SENTINEL), "a padding column of C was written"
+    assert np.all(Cflat[offs[2] + M * ldc:] == SENTINEL), "a row past M was written"
+    return A, B, C[:, :N]
+
+
+@pytest.mark.parametrize("M,N,K,lda,ldb,ldc,offs", CASES)
+def test_tile_stream_parity(M, N, K, lda, ldb, ldc, offs):
+    """Forced row-blocked streaming path on padded, misaligned operands: full
+    oracle check, padding of B poisoned with 65504."""
+    A, B, C = _run(M, N, K, lda, ldb, ldc, offs, gr.GR_PATH_TILE_STREAM, seed=M * 31 + N + K)
+    ref = oracle.gemm_relu_full(A, B, M=M, N=N, K=K, lda=lda, ldb=ldb)
+    log("parity %s" % (assert_parity(C, ref, "tile_stream %dx%dx%d" % (M, N, K)),))
+
+
+def test_square1024_workload_takes_tile_stream_and_matches_oracle():
+    """The 1024^3 workload through the plain call: the planner picks the
+    row-blocked streaming path (256 workgroups where 128 x 128 tiles give
+    64); full oracle check; two calls agree bit for bit."""
+    w = synth.WORKLOADS["square1024"]
+    M, N, K = w.M, w.N, w.K
+    st, p = gr.gemm_relu_f16_plan(M, N, K, 0x100000, K, 0x200000000000, N, 0x400000000000, N)
+    assert st == gr.GR_OK and p["path"] == gr.GR_PATH_TILE_STREAM and p["grid"] == 256
+    A, B = synth.operands(w)
+    dA, dB = to_dev(A), to_dev(B)
+    dC1 = full_dev((M * N,), SENTINEL)
+    dC2 = full_dev((M * N,), SENTINEL)
+    assert call(M, N, K, dA, K, dB, N, dC1, N) == gr.GR_OK
+    assert call(M, N, K, dA, K, dB, N, dC2, N) == gr.GR_OK
+    C = from_dev(dC1).reshape(M, N)
+    assert np.array_equal(C, from_dev(dC2).reshape(M, N)), "two runs differ"
+    log("parity %s" % (assert_parity(C, oracle.gemm_relu_full(A, B), "square1024"),))
+
+
+def test_tile_stream_and_tile_kernel_agree():
+    """The same problem on the row-blocked streaming path and on the 128 x 128
+    tile kernel: both within the bar of the oracle, and within a few fp16
+    ulps of each other (they add the k terms in different orders)."""
+    M, N, K = 384, 640, 1024
+    A, B = synth.random_operands(M, N, K, seed=123)
+    dA, dB = to_dev(A), to_dev(B)
+    out = {}
+    for path in (gr.GR_PATH_TILE_STREAM, gr.GR_PATH_TILE):
+        dC = full_dev((M * N,), SENTINEL)
+        assert call(M, N, K, dA, K, dB, N, dC, N, path=path) == gr.GR_OK
+        out[path] = from_dev(dC).reshape(M, N)
+    ref = oracle.gemm_relu_full(A, B)
+    for path, C in out.items():
+        assert_parity(C, ref, "path %d" % path)
+    c1 = out[gr.GR_PATH_TILE_STREAM].view(np.float16).astype(np.float64)
+    c2 = out[gr.GR_PATH_TILE].view(np.float16).astype(np.float64)
+    assert np.all(np.abs(c1 - c2) <= 1e-2 + 1e-2 * np.abs(c2))
+
+
+def test_all_ones_exact_on_tile_stream():
+    """All-ones operands give exactly K in every element (every partial sum
+    is an integer below 2^24, whatever the order of the waves' sums)."""
+    for M, N, K in ((130, 200, 32), (300, 520, 1024), (64, 64, 2080)):
+        A = np.full((M, K), 0x3C00, np.uint16)
+        B = np.full((K, N), 0x3C00, np.uint16)
+        dC = full_dev((M * N,), SENTINEL)
+        assert call(M, N, K, to_dev(A), K, to_dev(B), N, dC, N, path=gr.GR_PATH_TILE_STREAM) == gr.GR_OK
+        assert np.all(from_dev(dC) == np.float16(K).view(np.uint16)), (M, N, K)
+
+
+@pytest.mark.parametrize("fmt,act", [("f16", "relu"), ("bf16", "relu"), ("f16", "gelu"), ("bf16", "silu"),
+                                     ("f16", "none")])
+def test_tile_stream_with_bias_and_activation(fmt, act):
+    """The bias + activation epilogue and bfloat16 on the row-blocked
+    streaming path, against the oracle's double-precision epilogue."""
+    import torch as t
+    M, N, K = 300, 1000, 512
+    A, B = synth.random_operands(M, N, K, seed=97, b_scale=K ** -0.5, fmt=fmt)
+    bias = synth.random_operands(1, N, 1, seed=98, fmt=fmt)[1].reshape(N)
+    dA, dB, db = to_dev(A), to_dev(B), to_dev(bias)
+    dC = full_dev(((M + 2) * N,), SENTINEL)
+    s = t.cuda.current_stream().cuda_stream
+    fn = gr.gemm_bias_act_f16_forced if fmt == "f16" else gr.gemm_bias_act_bf16_forced
+    st = fn(M, N, K, dA.data_ptr(), K, dB.data_ptr(), N, db.data_ptr(), gr.ACT_CODES[act], dC.data_ptr(), N, s,
+            gr.GR_PATH_TILE_STREAM)
+    t.cuda.synchronize()
+    assert st == gr.GR_OK
+    Cflat = from_dev(dC)
+    assert np.all(Cflat[M * N:] == SENTINEL), "a row past M was written"
+    got = as_f64(Cflat[:M * N].reshape(M, N), fmt)
+    ref = as_f64(oracle.gemm_relu_full(A, B, fmt=fmt, bias=bias, act=act), fmt)
+    assert np.all(np.isfinite(got))
+    err = np.abs(got - ref)
+    assert np.all(err <= 1e-2 + 1e-2 * np.abs(ref)), (fmt, act, float(err.max()))
+
+
+def test_bf16_plain_call_takes_tile_stream():
+    """gemm_relu_bf16 on a 1024^3 problem plans the same path and matches the
+    oracle's bfloat16 result on sampled elements."""
+    import torch as t
+    M = N = K = 1024
+    A, B = synth.random_operands(M, N, K, seed=99, fmt="bf16")
+    dA, dB = to_dev(A), to_dev(B)
+    dC = full_dev((M * N,), SENTINEL)
+    st = gr.gemm_relu_bf16(M, N, K, dA.data_ptr(), K, dB.data_ptr(), N, dC.data_ptr(), N,
+                           t.cuda.current_stream().cuda_stream)
+    t.cuda.synchronize()
+    assert st == gr.GR_OK
+    ii, jj = synth.sample_indices(M, N, 4096, 99)
+    got = as_f64(from_dev(dC).reshape(M, N)[ii, jj], "bf16")
+    ref = as_f64(oracle.gemm_relu_elems(A, B, ii, jj, fmt="bf16"), "bf16")
+    err = np.abs(got - ref)
+    assert np.all(err <= 1e-2 + 1e-2 * np.abs(ref)), float(err.max())
