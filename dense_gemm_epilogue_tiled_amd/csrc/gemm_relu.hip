@@ -887,8 +887,8 @@ int validate_bt(int64_t M, int64_t N, int64_t K, uintptr_t A, int64_t lda, uintp
     return GR_OK;
 }
 
-// Largest pitch for which the direct-to-LDS small-M Bt kernel's per-lane copy
-// offsets (64 rows of Bt) fit in 32 bits.
+// Largest pitch for which the streaming small-M Bt kernel's per-lane copy
+// offsets (16 rows of Bt or A from a wave's base) fit in 32 bits, with room.
 constexpr int64_t kBtLdsMaxPitch = (int64_t(1) << 32) / (64 * 2) - 512;
 
 // Small-M kernel for Bt: 16-byte rows of A and of Bt.
@@ -960,14 +960,24 @@ int run_bt(const gr_plan_t& p, int64_t M, int64_t N, int64_t K, const uint16_t* 
         case GR_PATH_NONE: return GR_OK;
         case GR_PATH_SMALL_M: {
             using namespace gr::smallm;
-            if (K % BTL_KC == 0 && ldbt <= kBtLdsMaxPitch && lda <= kBtLdsMaxPitch) {
-                // K in whole 256-deep chunks: the direct-to-LDS variant
-                const int64_t grid = (N + BTL_NB - 1) / BTL_NB;
-                if (N % BTL_NB == 0)
-                    return launch(gemm_relu_smallm_bt_lds_kernel<false, E>, grid, 256, stream, A, Bt, C, M, N, K, lda,
-                                  ldbt, ldc, ep);
-                return launch(gemm_relu_smallm_bt_lds_kernel<true, E>, grid, 256, stream, A, Bt, C, M, N, K, lda,
-                              ldbt, ldc, ep);
+            if (K % BTS_KC == 0 && ldbt <= kBtLdsMaxPitch && lda <= kBtLdsMaxPitch) {
+                // K in whole 256-deep chunks: the streaming variant, 4 waves
+                // of 16 columns each, with 8 rows of A per slot for M <= 8
+                constexpr int W = 4;
+                const int64_t grid = (N + 16 * W - 1) / (16 * W);
+                const bool whole = N % (16 * W) == 0;
+                if (M <= 8) {
+                    if (whole)
+                        return launch(gemm_relu_smallm_bt_stream_kernel<false, E, W, 8>, grid, 64 * W, stream, A, Bt,
+                                      C, M, N, K, lda, ldbt, ldc, ep);
+                    return launch(gemm_relu_smallm_bt_stream_kernel<true, E, W, 8>, grid, 64 * W, stream, A, Bt, C, M,
+                                  N, K, lda, ldbt, ldc, ep);
+                }
+                if (whole)
+                    return launch(gemm_relu_smallm_bt_stream_kernel<false, E, W, 16>, grid, 64 * W, stream, A, Bt, C,
+                                  M, N, K, lda, ldbt, ldc, ep);
+                return launch(gemm_relu_smallm_bt_stream_kernel<true, E, W, 16>, grid, 64 * W, stream, A, Bt, C, M,
+                              N, K, lda, ldbt, ldc, ep);
             }
             const bool whole = N % BT_NB == 0 && K % KSTEP == 0;
             if (whole)

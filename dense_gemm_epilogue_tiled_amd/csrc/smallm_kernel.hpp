@@ -710,103 +710,107 @@ __global__ __launch_bounds__(64 * BT_WAVES) void gemm_relu_smallm_bt_kernel(
 
 // Bt version with direct-to-LDS copies, for K a multiple of 256: loading MFMA
 // operands straight from global memory (above) reads every Bt row in 64-byte
-// pieces and re-reads A for every column group.  Here a workgroup of 4 waves
-// owns 64 columns; K moves in 256-deep chunks (512 bytes of each Bt row)
-// through a 4-slot LDS ring (all 160 KiB), three chunks ahead:
-//   * each wave copies its own 16 Bt rows (8 global_load_lds_dwordx4 per
-//     chunk, 2 rows x 512 contiguous bytes each) and 4 of the 16 rows of the
-//     A chunk (rows past M read row M-1: they only feed columns of C^T that
-//     are never stored);
-//   * LDS rows are 512 bytes; the 16-byte chunk c of row r sits at slot
-//     c XOR (r % 16) (the permutation is applied on the global side, inside
-//     the row), so the 16 rows a fragment read touches hit 16 bank groups;
-//   * per chunk each wave runs 8 v_mfma_f32_16x16x32_f16 on fragments read
-//     with ds_read_b128, then ReLU, fp16 and the store at the end.
-constexpr int BTL_KC = 256;                    // K per chunk
-constexpr int BTL_ROW_BYTES = BTL_KC * 2;      // 512
-constexpr int BTL_NB = 64;                     // columns (Bt rows) per workgroup
-constexpr int BTL_BT_BYTES = BTL_NB * BTL_ROW_BYTES;  // 32 KiB
-constexpr int BTL_A_BYTES = MAX_M * BTL_ROW_BYTES;    // 8 KiB
-constexpr int BTL_SLOT = BTL_BT_BYTES + BTL_A_BYTES;
-constexpr int BTL_SLOTS = 4;
-constexpr int BTL_COPIES = 10;  // copies per wave per chunk: 8 (Bt) + 2 (A)
+// pieces and re-reads A for every column group.  Measured at 8 x 16384 x 8192
+// with Bt cold (four rotating copies), back to back: a workgroup of 4 waves
+// sharing each 256-deep chunk of Bt and A through a ring of 4 (2) slots, with
+// a barrier per chunk, 55.3 (52.7) us; 128-deep chunks 65-68 us; the
+// variant below, with a ring per wave and no barrier, 52.1 us (and 9.2
+// against 10.7 us at 16 x 4096 x 4096 with 8 rows).  With Bt warm (one copy,
+// mostly in the last-level cache) the two are within 1%: 49.5-51.0 us.
+// Bt streaming variant (no barrier): the workgroup's W waves each own 16 Bt
+// rows (16 columns of C) and stream them through a 2-slot ring of their own,
+// one 256-deep chunk ahead (512 bytes of each row per chunk), as the
+// row-major streaming kernel does for B; each slot also takes the chunk of
+// the first MA rows of A (rows >= M copy row M - 1; lanes of rows >= MA read
+// row MA - 1: their outputs are never stored).  A wave reads back only what
+// it copied itself, so there is no barrier; every copy is a direct-to-LDS
+// one, whose completion the hand-placed waits count.
+constexpr int BTS_KC = 256;
+constexpr int BTS_ROWB = BTS_KC * 2;  // 512 bytes of a row per chunk
 
-template <bool GUARD, typename E = ElemF16>
-__global__ __launch_bounds__(256, 1) void gemm_relu_smallm_bt_lds_kernel(
+template <bool GUARD, typename E = ElemF16, int W = 4, int MA = 16>
+__global__ __launch_bounds__(64 * W, 1) void gemm_relu_smallm_bt_stream_kernel(
     const uint16_t* __restrict__ A, const uint16_t* __restrict__ Bt, uint16_t* __restrict__ C, int64_t M, int64_t N,
     int64_t K, int64_t lda, int64_t ldbt, int64_t ldc, EpiArgs ep) {
-    __shared__ __attribute__((aligned(1024))) uint8_t lds[BTL_SLOTS * BTL_SLOT];
+    static_assert(MA == 2 || MA == 4 || MA == 8 || MA == 16, "rows of A per slot");
+    constexpr int BT_BYTES = 16 * BTS_ROWB;                // 8 KiB: the wave's 16 Bt rows
+    constexpr int WSLOT = BT_BYTES + MA * BTS_ROWB;
+    constexpr int CP_A = MA / 2;
+    constexpr int OPS = 8 + CP_A;                          // copies per chunk
+    __shared__ __attribute__((aligned(1024))) uint8_t lds[W * 2 * WSLOT];
 
     const uint32_t lane = threadIdx.x & 63u;
     const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int64_t n_wg = (int64_t)blockIdx.x * BTL_NB;
+    const int64_t n_w = (int64_t)blockIdx.x * (16 * W) + 16 * wave;  // this wave's first column
 
-    // Copy i of a chunk: LDS rows 2i, 2i+1 of the Bt block (this wave: rows
-    // 16w .. 16w+15) or of the A block (rows 4w .. 4w+3); lane -> row
-    // 2i + lane/32, slot lane%32, which holds global chunk slot ^ (row % 16).
-    uint32_t off_bt[8], off_a[2];
+    // Copy i of a chunk: rows 2i, 2i+1 (of the wave's 16 Bt rows, or of the
+    // MA rows of A); lane -> row 2i + lane/32, LDS piece lane%32, which
+    // holds global piece (lane%32) ^ (row % 16) of the row's 32.
+    // (a wave wholly past N copies row N - 1 for all its rows, from a base
+    // moved to that row; none of them is stored)
+    const bool past = GUARD && n_w >= N;
+    const int64_t n_first = past ? N - 1 : n_w;
+    uint32_t off_bt[8], off_a[CP_A];
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-        const uint32_t row = 16u * wave + 2u * i + (lane >> 5);
-        const uint32_t chunk = (lane & 31u) ^ (row & 15u);
-        int64_t n = n_wg + row;
+        const uint32_t row = 2u * i + (lane >> 5);
+        const uint32_t piece = (lane & 31u) ^ (row & 15u);
+        int64_t n = n_w + row;
         if (GUARD && n >= N) n = N - 1;
-        off_bt[i] = (uint32_t)((n - n_wg) * ldbt * 2 + chunk * 16);
+        off_bt[i] = past ? piece * 16u : (uint32_t)((n - n_w) * ldbt * 2 + piece * 16);
     }
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-        const uint32_t row = 4u * wave + 2u * i + (lane >> 5);
-        const uint32_t chunk = (lane & 31u) ^ (row & 15u);
+    for (int i = 0; i < CP_A; ++i) {
+        const uint32_t row = 2u * i + (lane >> 5);
+        const uint32_t piece = (lane & 31u) ^ (row & 15u);
         const int64_t m = (int64_t)row < M ? (int64_t)row : M - 1;
-        off_a[i] = (uint32_t)(m * lda * 2 + chunk * 16);
+        off_a[i] = (uint32_t)(m * lda * 2 + piece * 16);
     }
-    const uint8_t* base_bt = reinterpret_cast<const uint8_t*>(Bt + n_wg * ldbt);
+    const uint8_t* base_bt = reinterpret_cast<const uint8_t*>(Bt + n_first * ldbt);
     const uint8_t* base_a = reinterpret_cast<const uint8_t*>(A);
-    const uint32_t lds_base = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t*)lds);
+    const uint32_t ring = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t*)lds + wave * 2 * WSLOT;
+
     auto issue = [&](int64_t kc) {
-        const uint32_t slot = lds_base + (uint32_t)(kc % BTL_SLOTS) * BTL_SLOT;
-        const int64_t kb = kc * BTL_ROW_BYTES;
+        const uint32_t dst = ring + (uint32_t)(kc & 1) * WSLOT;
+        const int64_t kb = kc * BTS_ROWB;
 #pragma unroll
-        for (int i = 0; i < 8; ++i) tile2::dma16(base_bt + kb, off_bt[i], slot + (16u * wave + 2u * i) * 512u);
+        for (int i = 0; i < 8; ++i) tile2::dma16(base_bt + kb, off_bt[i], dst + i * 1024u);
 #pragma unroll
-        for (int i = 0; i < 2; ++i)
-            tile2::dma16(base_a + kb, off_a[i], slot + BTL_BT_BYTES + (4u * wave + 2u * i) * 512u);
+        for (int i = 0; i < CP_A; ++i) tile2::dma16(base_a + kb, off_a[i], dst + BT_BYTES + i * 1024u);
     };
 
-    // Fragment addresses: Bt operand of step s = row 16w + l%16, chunk
-    // 4s + l/16; A operand = row l%16, same chunk.
+    // Operands of step s: Bt row l%16 and A row min(l%16, MA - 1), piece
+    // 4 s + l/16 of the chunk.
     const uint32_t li = lane & 15u, lg = lane >> 4;
-    const uint32_t bt_row = 16u * wave + li;
+    const uint32_t ar = li < (uint32_t)MA ? li : (uint32_t)MA - 1u;
     f32x4 acc0 = f32x4{}, acc1 = f32x4{};
-
-    const int64_t chunks = K / BTL_KC;
-    for (int64_t c = 0; c < BTL_SLOTS - 1 && c < chunks; ++c) issue(c);
+    const int64_t chunks = K / BTS_KC;
+    if (chunks > 0) issue(0);
     for (int64_t kc = 0; kc < chunks; ++kc) {
-        // chunk kc landed; the (up to BTL_SLOTS - 2) chunks after it may still be in flight
-        const int64_t ahead = chunks - 1 - kc < BTL_SLOTS - 2 ? chunks - 1 - kc : BTL_SLOTS - 2;
-        if (ahead >= 2) tile2::wait_vmcnt<2 * BTL_COPIES>();
-        else if (ahead == 1) tile2::wait_vmcnt<BTL_COPIES>();
-        else tile2::wait_vmcnt<0>();
-        tile2::barrier();
-        if (kc + BTL_SLOTS - 1 < chunks) issue(kc + BTL_SLOTS - 1);
-        const uint8_t* slot = lds + (kc % BTL_SLOTS) * BTL_SLOT;
+        if (kc + 1 < chunks) {
+            issue(kc + 1);  // into the slot chunk kc - 1 used, whose reads its MFMAs consumed
+            tile2::wait_vmcnt<OPS>();
+        } else {
+            tile2::wait_vmcnt<0>();
+        }
+        const uint8_t* slot = lds + wave * 2 * WSLOT + (kc & 1) * WSLOT;
 #pragma unroll
-        for (int st = 0; st < BTL_KC / KSTEP; ++st) {
-            const uint32_t chunk = 4u * st + lg;
-            const f16x8 b = *reinterpret_cast<const f16x8*>(slot + bt_row * 512u + ((chunk ^ (bt_row & 15u)) << 4));
-            const f16x8 a = *reinterpret_cast<const f16x8*>(slot + BTL_BT_BYTES + li * 512u + ((chunk ^ li) << 4));
+        for (int st = 0; st < BTS_KC / KSTEP; ++st) {
+            const uint32_t piece = 4u * st + lg;
+            const f16x8 b = *reinterpret_cast<const f16x8*>(slot + li * BTS_ROWB + ((piece ^ li) << 4));
+            const f16x8 a = *reinterpret_cast<const f16x8*>(slot + BT_BYTES + ar * BTS_ROWB + ((piece ^ ar) << 4));
             if (st & 1) acc1 = E::mfma16(b, a, acc1);
             else acc0 = E::mfma16(b, a, acc0);
         }
     }
 
     // acc holds C^T: lane l, register r is C[m][n] with m = l%16 and
-    // n = n_wg + 16w + 4(l/16) + r.
+    // n = n_w + 4(l/16) + r.
     const int64_t m = li;
     if (m < M) {
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-            const int64_t n = n_wg + 16 * wave + 4 * lg + r;
+            const int64_t n = n_w + 4 * lg + r;
             if (!GUARD || n < N) C[m * ldc + n] = epi_value<E>(acc0[r] + acc1[r], n, N, ep);
         }
     }

@@ -697,6 +697,8 @@ BT_CASES = [
     (1, 100, 96, 96, 96, 100, gr.GR_PATH_SMALL_M),
     (5, 4096, 256, 256, 264, 4096, gr.GR_PATH_SMALL_M),        # one 256-deep chunk, padded Bt
     (3, 64, 512, 520, 512, 65, gr.GR_PATH_SMALL_M),            # one workgroup, two chunks, odd ldc
+    (12, 70, 512, 512, 520, 71, gr.GR_PATH_SMALL_M),           # 16 rows of A per slot; 3 waves past N
+    (8, 130, 768, 776, 768, 130, gr.GR_PATH_SMALL_M),          # 8 rows of A per slot, 3 chunks, N % 64 = 2
     (512, 768, 256, 256, 256, 768, gr.GR_PATH_TILE),           # 128 x 128 tiles
     (4096, 2304, 512, 512, 520, 2304, gr.GR_PATH_TILE),        # 256 x 256 tiles, padded Bt
     (300, 250, 96, 104, 96, 251, gr.GR_PATH_TILE),             # partial tiles, rows of Bt clamped
