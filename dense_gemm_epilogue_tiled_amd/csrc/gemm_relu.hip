@@ -962,17 +962,10 @@ int run_bt(const gr_plan_t& p, int64_t M, int64_t N, int64_t K, const uint16_t* 
             using namespace gr::smallm;
             if (K % BTS_KC == 0 && ldbt <= kBtLdsMaxPitch && lda <= kBtLdsMaxPitch) {
                 // K in whole 256-deep chunks: the streaming variant, 4 waves
-                // of 16 columns each, with 8 rows of A per slot for M <= 8
+                // of 16 columns each
                 constexpr int W = 4;
                 const int64_t grid = (N + 16 * W - 1) / (16 * W);
                 const bool whole = N % (16 * W) == 0;
-                if (M <= 8) {
-                    if (whole)
-                        return launch(gemm_relu_smallm_bt_stream_kernel<false, E, W, 8>, grid, 64 * W, stream, A, Bt,
-                                      C, M, N, K, lda, ldbt, ldc, ep);
-                    return launch(gemm_relu_smallm_bt_stream_kernel<true, E, W, 8>, grid, 64 * W, stream, A, Bt, C, M,
-                                  N, K, lda, ldbt, ldc, ep);
-                }
                 if (whole)
                     return launch(gemm_relu_smallm_bt_stream_kernel<false, E, W, 16>, grid, 64 * W, stream, A, Bt, C,
                                   M, N, K, lda, ldbt, ldc, ep);

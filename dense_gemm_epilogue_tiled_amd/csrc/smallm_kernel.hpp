@@ -713,13 +713,15 @@ __global__ __launch_bounds__(64 * BT_WAVES) void gemm_relu_smallm_bt_kernel(
 // pieces and re-reads A for every column group.  Measured at 8 x 16384 x 8192
 // with Bt cold (four rotating copies), back to back: a workgroup of 4 waves
 // sharing each 256-deep chunk of Bt and A through a ring of 4 (2) slots, with
-// a barrier per chunk, 55.3 (52.7) us; 128-deep chunks 65-68 us; the
-// variant below, with a ring per wave and no barrier, 52.1 us (and 9.2
-// against 10.7 us at 16 x 4096 x 4096 with 8 rows).  With Bt warm (one copy,
-// mostly in the last-level cache) the two are within 1%: 49.5-51.0 us.
+// a barrier per chunk, 55.3 (52.7) us; 128-deep chunks 65-68 us; the variant
+// below, with a 2-slot ring per wave and no barrier, 52.2 us; with Bt warm
+// (one copy, mostly in the last-level cache) 47.8-49.5 against 49.6-50.3 us.
+// At 16 x 4096 x 4096 the two are equal (10.9 and 10.7 us).  Rings of 3 or 4
+// slots, 2 waves per workgroup, or only 8 rows of A per slot for M <= 8 were
+// no faster (52.8-61 us cold).
 // Bt streaming variant (no barrier): the workgroup's W waves each own 16 Bt
-// rows (16 columns of C) and stream them through a 2-slot ring of their own,
-// one 256-deep chunk ahead (512 bytes of each row per chunk), as the
+// rows (16 columns of C) and stream them through a ring of R slots of their
+// own, R - 1 256-deep chunks ahead (512 bytes of each row per chunk), as the
 // row-major streaming kernel does for B; each slot also takes the chunk of
 // the first MA rows of A (rows >= M copy row M - 1; lanes of rows >= MA read
 // row MA - 1: their outputs are never stored).  A wave reads back only what
@@ -728,16 +730,17 @@ __global__ __launch_bounds__(64 * BT_WAVES) void gemm_relu_smallm_bt_kernel(
 constexpr int BTS_KC = 256;
 constexpr int BTS_ROWB = BTS_KC * 2;  // 512 bytes of a row per chunk
 
-template <bool GUARD, typename E = ElemF16, int W = 4, int MA = 16>
+template <bool GUARD, typename E = ElemF16, int W = 4, int MA = 16, int R = 2>
 __global__ __launch_bounds__(64 * W, 1) void gemm_relu_smallm_bt_stream_kernel(
     const uint16_t* __restrict__ A, const uint16_t* __restrict__ Bt, uint16_t* __restrict__ C, int64_t M, int64_t N,
     int64_t K, int64_t lda, int64_t ldbt, int64_t ldc, EpiArgs ep) {
     static_assert(MA == 2 || MA == 4 || MA == 8 || MA == 16, "rows of A per slot");
+    static_assert(R >= 2 && R <= 4, "ring entries per wave");
     constexpr int BT_BYTES = 16 * BTS_ROWB;                // 8 KiB: the wave's 16 Bt rows
     constexpr int WSLOT = BT_BYTES + MA * BTS_ROWB;
     constexpr int CP_A = MA / 2;
     constexpr int OPS = 8 + CP_A;                          // copies per chunk
-    __shared__ __attribute__((aligned(1024))) uint8_t lds[W * 2 * WSLOT];
+    __shared__ __attribute__((aligned(1024))) uint8_t lds[W * R * WSLOT];
 
     const uint32_t lane = threadIdx.x & 63u;
     const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -768,10 +771,10 @@ __global__ __launch_bounds__(64 * W, 1) void gemm_relu_smallm_bt_stream_kernel(
     }
     const uint8_t* base_bt = reinterpret_cast<const uint8_t*>(Bt + n_first * ldbt);
     const uint8_t* base_a = reinterpret_cast<const uint8_t*>(A);
-    const uint32_t ring = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t*)lds + wave * 2 * WSLOT;
+    const uint32_t ring = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t*)lds + wave * R * WSLOT;
 
     auto issue = [&](int64_t kc) {
-        const uint32_t dst = ring + (uint32_t)(kc & 1) * WSLOT;
+        const uint32_t dst = ring + (uint32_t)(kc % R) * WSLOT;
         const int64_t kb = kc * BTS_ROWB;
 #pragma unroll
         for (int i = 0; i < 8; ++i) tile2::dma16(base_bt + kb, off_bt[i], dst + i * 1024u);
@@ -785,15 +788,15 @@ __global__ __launch_bounds__(64 * W, 1) void gemm_relu_smallm_bt_stream_kernel(
     const uint32_t ar = li < (uint32_t)MA ? li : (uint32_t)MA - 1u;
     f32x4 acc0 = f32x4{}, acc1 = f32x4{};
     const int64_t chunks = K / BTS_KC;
-    if (chunks > 0) issue(0);
+    for (int64_t c = 0; c < R - 1 && c < chunks; ++c) issue(c);
     for (int64_t kc = 0; kc < chunks; ++kc) {
-        if (kc + 1 < chunks) {
-            issue(kc + 1);  // into the slot chunk kc - 1 used, whose reads its MFMAs consumed
-            tile2::wait_vmcnt<OPS>();
+        if (kc + R - 1 < chunks) {
+            issue(kc + R - 1);  // into the slot chunk kc - 1 used, whose reads its MFMAs consumed
+            tile2::wait_vmcnt<(R - 1) * OPS>();
         } else {
             tile2::wait_vmcnt<0>();
         }
-        const uint8_t* slot = lds + wave * 2 * WSLOT + (kc & 1) * WSLOT;
+        const uint8_t* slot = lds + wave * R * WSLOT + (kc % R) * WSLOT;
 #pragma unroll
         for (int st = 0; st < BTS_KC / KSTEP; ++st) {
             const uint32_t piece = 4u * st + lg;
