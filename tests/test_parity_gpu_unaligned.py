@@ -128,3 +128,27 @@ def test_ragged_workload_runs_in_place_with_or_without_workspace():
     cols = [0, 255, 256, 2559, 2560, 2815, 2816, 3070]
     assert_parity(C[rows, :], oracle.gemm_relu_rows(A, B, rows), "ragged rows")
     assert_parity(C[:, cols].T, oracle.gemm_relu_cols(A, B, cols), "ragged cols")
+
+
+@pytest.mark.parametrize("r", range(1, 8))
+@pytest.mark.parametrize("path", [gr.GR_PATH_TILE_UNALIGNED, gr.GR_PATH_TILE])
+def test_partial_row_segments_of_every_length(r, path):
+    """N = 512 + r: the last 8-column segment of each row of C holds r columns
+    (and, on the unaligned path, the last tile column moved left to end at N
+    starts r columns into a segment, so its first segment holds 8 - r of
+    them).  Each partial segment is written with at most two overlapping
+    stores; the full result must match the oracle and C's padding columns
+    must keep the sentinel."""
+    M, N = 300, 512 + r
+    K, lda = (130, 130) if path == gr.GR_PATH_TILE_UNALIGNED else (128, 128)
+    ldb = ldc = N + (-N) % 8  # 16-byte rows of B and C
+    A, B = synth.random_operands(M, N, K, seed=17 * r + K, lda=lda, ldb=ldb)
+    dC = full_dev(((M + 1) * ldc,), SENTINEL)
+    log("partial segments %dx%dx%d path=%d" % (M, N, K, path))
+    st = call(M, N, K, to_dev(A), lda, to_dev(B), ldb, dC, ldc, path=path)
+    assert st == gr.GR_OK, gr.gemm_relu_status_string(st)
+    Cflat = from_dev(dC)
+    C = Cflat[:M * ldc].reshape(M, ldc)
+    assert_parity(C[:, :N], oracle.gemm_relu_full(A, B, M=M, N=N, K=K, lda=lda, ldb=ldb), "segments r=%d" % r)
+    assert np.all(C[:, N:] == SENTINEL), "a padding column of C was written"
+    assert np.all(Cflat[M * ldc:] == SENTINEL), "a row past M was written"
