@@ -80,6 +80,7 @@ class gr_plan_t(ctypes.Structure):
         ("packed", ctypes.c_int32),
         ("workspace", ctypes.c_int64),
         ("split_k", ctypes.c_int32),
+        ("plain_order", ctypes.c_int32),
     ]
 
 

@@ -33,7 +33,7 @@ static __device__ __align__(256) uint8_t scratch[GR_NOALLOC_SCRATCH_BYTES];
 
 namespace {
 
-constexpr int kVersion = 100;  // 0.1.0
+constexpr int kVersion = 200;  // 0.2.0: gr_plan_t.plain_order
 constexpr int64_t kMaxDim = (int64_t(1) << 31) - 1;
 constexpr int64_t kMaxSpanBytes = int64_t(1) << 62;
 constexpr int kGroupM = 4;          // tile rows per workgroup-order group
@@ -221,8 +221,9 @@ bool tile_persistent_ok(int64_t M, int64_t N, int64_t K, uintptr_t A, int64_t ld
 // (the last tile row and column move to end at M and N), K > 128 (the tail
 // of 1..64 plus at least two 64-deep strips) and pitches within its 32-bit
 // copy offsets.  The planner takes it when there are also more than 128
-// tiles (as for the aligned 256 x 256 kernel); the forced hook only needs
-// the kernel's own conditions.
+// tiles (as for the aligned 256 x 256 kernel), and with fewer where neither
+// the packed copy (workspace) nor the streaming kernel applies; the forced
+// hook only needs the kernel's own conditions.
 bool tile_unaligned_ok(int64_t M, int64_t N, int64_t K, int64_t lda, int64_t ldb);
 
 // 256 x 256 tiles unless they would fill less than half of one wave of
@@ -239,23 +240,54 @@ bool use_large_tiles(int64_t M, int64_t N) {
 // Blocks of 64 rows x 64 columns on the streaming kernel (TILE_STREAM): in
 // each workgroup the 4 waves take the 32-row slots of K in turn through
 // rings of their own, with no barrier in the loop, and add their partial
-// sums in LDS at the end.  Where 128 x 128 tiles would be fewer than 128,
-// this gives four times as many workgroups and a quarter of the K steps per
-// wave.  Measured (us, back to back): 1024^3 8.45 against 12.1 for the 128
-// x 128 kernel, 1024 x 1024 x 4096 19.8 against 38.3, 512 x 1024 x 1024 8.4
-// against 12.6; from 128 tiles on the 128 x 128 kernel is as fast or faster
-// (1024 x 2048 x 1024: 12.8 against 12.3; 2048^3: 35.9 against 22.6).
+// sums in LDS at the end.  Against 128 x 128 tiles this gives four times as
+// many workgroups and a quarter of the K steps per wave.  A block holds 64
+// KiB of LDS, so two are resident per CU and 512 fill one round of the 256
+// CUs.  Where it is planned (blocks = ceil(M / 64) x ceil(N / 64); us, back
+// to back):
+//  * aligned rows, against the 128 x 128 tile kernel: blocks <= 256 from
+//    K = 512 (1024^3 8.4 against 12.3, 1024^2 x 512 7.3 against 7.8; at
+//    K = 256 6.6 against 5.6), <= 384 from K = 1024 (1024 x 1344 x 1024
+//    12.5 against 12.6; 1152 x 1792 x 1024, 504 blocks: 13.1 against 12.3)
+//    and <= 512 from K = 2048 (1024 x 2048 x 2048 20.3 against 21.2, x
+//    8192 59.5 against 73.7).  Beyond one round the tiles win (1536^2 x
+//    4096, 576 blocks: 49.3 against 38.5).  With a workspace the split-K
+//    tile path comes first where it splits: it is faster still (1024^2 x
+//    8192 29.4, 1024 x 2048 x 8192 48.3).
+//  * rows of B not 16-byte aligned: the alternatives are the in-place
+//    unaligned 256 x 256 kernel, the packed path (workspace) and the
+//    guarded kernel.  Streaming wins up to one round at any K (1024 x 2048
+//    x 4096: 49.3 against 82.8 unaligned, 48.5 packed, 176 guarded) and, with
+//    no workspace, up to two rounds for K <= 2048 (2048^2 x 1024: 29.5
+//    against 31.6 unaligned; x 4096: 93.0 against 83.0).
 // Needs what the streaming kernel needs: K % 32 == 0, 16-byte rows of A,
 // N >= 64; B of any alignment.
 constexpr int64_t kTileStreamRows = 64;  // 4 blocks of 16 rows per workgroup
-constexpr int64_t kTileStreamMaxSmallTiles = 128;
+constexpr int64_t kTileStreamRound = 512;  // resident blocks: 2 per CU x 256 CUs
+// Workgroup order of the row-blocked grid.  All blocks of a launch that fits
+// one round are resident together, so what counts is how many distinct
+// column blocks of B (and row blocks of A) each XCD's L2 holds.  In plain
+// row-major order (workgroup j nb + cb runs block (j, cb) on XCD (j nb + cb)
+// mod 8) XCD x gets, over the row blocks j, the column blocks cb with cb = x
+// - j nb (mod 8): 8 / gcd(nb, 8) of the 8 residues, so an eighth of B when
+// nb % 8 == 0, a quarter when nb % 8 == 4, half when nb % 4 == 2 and all of
+// B when nb is odd.  Unless nb % 4 == 0 the XCD renumbering with groups of 4
+// row blocks is faster (1088 x 1856 x 8192, nb = 29: 95.5 us against 66.3;
+// 1024 x 1984 x 4096, nb = 31: 50.0 against 33.8; nb = 18, 22, 30: 10-20%
+// faster at K = 8192); with nb % 4 == 0 plain order is as fast or faster
+// (1152 x 1792 x 8192: 63.0 against 70.5; 960 x 2048 x 8192: 57.1 against
+// 67.5).
+constexpr int32_t kTileStreamGroupM = 4;
+bool tile_stream_plain_order(int64_t N) { return ((N + kStreamNB - 1) / kStreamNB) % 4 == 0; }
 bool tile_stream_ok(int64_t M, int64_t N, int64_t K, uintptr_t A, int64_t lda, int64_t ldb) {
     return smallm_stream_ok(M, N, K, A, lda, ldb, kStreamNB, kMaxDim);
 }
-bool tile_stream_wanted(int64_t M, int64_t N) {
-    using namespace gr::tile128;
-    return M > kSmallMMaxRows && !use_large_tiles(M, N) &&
-           ((M + BM - 1) / BM) * ((N + BN - 1) / BN) < kTileStreamMaxSmallTiles;
+int64_t tile_stream_blocks(int64_t M, int64_t N) {
+    return ((M + kTileStreamRows - 1) / kTileStreamRows) * ((N + kStreamNB - 1) / kStreamNB);
+}
+// Aligned rows: where the streaming path beats the 128 x 128 tile kernel.
+bool tile_stream_beats_tiles(int64_t blocks, int64_t K) {
+    return (blocks <= 256 && K >= 512) || (blocks <= 384 && K >= 1024) || (blocks <= kTileStreamRound && K >= 2048);
 }
 
 bool tile_unaligned_ok(int64_t M, int64_t N, int64_t K, int64_t lda, int64_t ldb) {
@@ -419,7 +451,8 @@ void fill_plan(int path, int64_t M, int64_t N, int64_t K, uintptr_t A, int64_t l
         p->vec_a = 8;
         p->vec_b = 8;  // 16-byte copies from any 2-byte address
         p->vec_c = 1;
-        p->group_m = 1;
+        p->plain_order = tile_stream_plain_order(N);
+        p->group_m = p->plain_order ? 1 : kTileStreamGroupM;  // plain: row-major
         p->split_k = 1;
     } else if (path == GR_PATH_SMALL_M) {
         using namespace gr::smallm;
@@ -459,12 +492,21 @@ int choose_path(int64_t M, int64_t N, int64_t K, uintptr_t A, int64_t lda, uintp
         (smallm_rows_ok(M, N, K, A, lda, B, ldb) || smallm_stream_ok(M, N, K, A, lda, ldb, kStreamNB, kSmallMMaxRows)) &&
         (N + gr::smallm::NB - 1) / gr::smallm::NB <= 256)
         return GR_PATH_SMALL_M;
-    if (tile_stream_wanted(M, N) && tile_stream_ok(M, N, K, A, lda, ldb)) return GR_PATH_TILE_STREAM;
+    const bool stream = M > kSmallMMaxRows && tile_stream_ok(M, N, K, A, lda, ldb);
+    const int64_t blocks = stream ? tile_stream_blocks(M, N) : 0;
+    if (stream && (fast ? tile_stream_beats_tiles(blocks, K) : blocks <= kTileStreamRound))
+        return GR_PATH_TILE_STREAM;
     if (fast) return GR_PATH_TILE;
     if (tile_unaligned_ok(M, N, K, lda, ldb) && use_large_tiles(M, N)) return GR_PATH_TILE_UNALIGNED;
     if (ws_bytes > 0 && pack_layout(M, N, K, A, lda, B, ldb, pk) && pk->bytes <= ws_bytes &&
         (double)M * (double)N * (double)K >= (double)kPackMinMacs)
         return GR_PATH_TILE_PACKED;
+    if (stream && blocks <= 2 * kTileStreamRound && K <= 2048) return GR_PATH_TILE_STREAM;
+    // Misaligned rows or a ragged K without a workspace: the in-place
+    // unaligned kernel wherever it applies (1024 x 2048 x 4096 with A's rows
+    // misaligned: 83.6 us against 417 for the guarded kernel; 512 x 1024 x
+    // 256 with B's: 18.3 against 21.5).
+    if (tile_unaligned_ok(M, N, K, lda, ldb)) return GR_PATH_TILE_UNALIGNED;
     return GR_PATH_TILE_EDGE;
 }
 
@@ -522,6 +564,12 @@ int launch(void (*kernel)(Args...), int64_t grid, int threads, hipStream_t strea
     return e == hipSuccess ? GR_OK : GR_ERR_LAUNCH;
 }
 
+// The order word the tile kernels take (tile_of_workgroup): the group of tile
+// rows, bit 31 set for the plain order (tile order follows the workgroup id).
+uint32_t order_word(const gr_plan_t& p) {
+    return (uint32_t)p.group_m | (p.plain_order ? gr::kNoXcdRemap : 0u);
+}
+
 // Second pass of every split path: sum the fp32 partial sums in order and
 // apply the epilogue (4 outputs per thread when rows hold a multiple of 4).
 template <typename E>
@@ -546,7 +594,7 @@ int launch_tile(const gr_plan_t& p, int64_t M, int64_t N, int64_t K, const uint1
     const uint32_t tiles_m = (uint32_t)((M + BM - 1) / BM);
     const uint32_t tiles_n = (uint32_t)((N + BN - 1) / BN);
     return launch(gemm_relu_tile_kernel<GUARD, VA, VB, false, E>, p.grid, THREADS, stream, A, B, C, M, N, K, lda,
-                  ldb, ldc, tiles_m, tiles_n, (uint32_t)p.group_m, (int)p.vec_c, ep);
+                  ldb, ldc, tiles_m, tiles_n, order_word(p), (int)p.vec_c, ep);
 }
 
 template <bool GUARD, int VA, typename E>
@@ -595,7 +643,7 @@ int run(const gr_plan_t& p, int64_t M, int64_t N, int64_t K, const uint16_t* A, 
                 const int st = launch(
                     gemm_relu_smallm_stream_kernel<kStreamSplitNB, kStreamSplitW, kStreamSplitR, stream::PARTIAL, E>,
                     p.grid, p.threads, stream, A, B, C, part, M, N, K, lda, ldb, ldc, sp.k_per_split,
-                    (uint32_t)sp.n_blocks, ep);
+                    (uint32_t)sp.n_blocks, 0u, ep);
                 if (st != GR_OK) return st;
                 return launch_reduce<E>(part, C, M, N, ldc, sp.splits, p.vec_c, ep, stream);
             }
@@ -614,7 +662,7 @@ int run(const gr_plan_t& p, int64_t M, int64_t N, int64_t K, const uint16_t* A, 
             const bool whole = tile_whole(M, N, BM, BN);
             const uint32_t tiles_m = (uint32_t)((M + BM - 1) / BM);
             const uint32_t tiles_n = (uint32_t)((N + BN - 1) / BN);
-            const uint32_t gm = (uint32_t)p.group_m;
+            const uint32_t gm = order_word(p);
             const int vc = p.vec_c;
             const int64_t kps = ts.k_per_split;
             int st = whole ? launch(gemm_relu_tile128_kernel<false, true, false, E>, p.grid, THREADS, stream, A, B,
@@ -638,7 +686,7 @@ int run(const gr_plan_t& p, int64_t M, int64_t N, int64_t K, const uint16_t* A, 
             const bool whole = tile_whole(M, N, bm, bn);
             const uint32_t tiles_m = (uint32_t)((M + bm - 1) / bm);
             const uint32_t tiles_n = (uint32_t)((N + bn - 1) / bn);
-            const uint32_t gm = (uint32_t)p.group_m;
+            const uint32_t gm = order_word(p);
             const int vc = p.vec_c;
             if (bm == gr::tile128::BM) {
                 using namespace gr::tile128;
@@ -672,10 +720,10 @@ int run(const gr_plan_t& p, int64_t M, int64_t N, int64_t K, const uint16_t* A, 
                 // the bias + activation epilogue stages fp32 blocks through
                 // all of LDS: the same tiles, one workgroup each
                 return launch(gemm_relu_tile3_kernel<false, E>, (int64_t)tiles_m * tiles_n, THREADS, stream, A, B, C,
-                              M, N, K, lda, ldb, ldc, tiles_m, tiles_n, (uint32_t)p.group_m, (int)p.vec_c, ep);
+                              M, N, K, lda, ldb, ldc, tiles_m, tiles_n, order_word(p), (int)p.vec_c, ep);
             } else {
                 return launch(gemm_relu_tile3_kernel<false, E, false, true>, p.grid, THREADS, stream, A, B, C, M, N,
-                              K, lda, ldb, ldc, tiles_m, tiles_n, (uint32_t)p.group_m, (int)p.vec_c, ep);
+                              K, lda, ldb, ldc, tiles_m, tiles_n, order_word(p), (int)p.vec_c, ep);
             }
         }
         case GR_PATH_TILE_UNALIGNED: {
@@ -683,7 +731,7 @@ int run(const gr_plan_t& p, int64_t M, int64_t N, int64_t K, const uint16_t* A, 
             const uint32_t tiles_m = (uint32_t)((M + BM - 1) / BM);
             const uint32_t tiles_n = (uint32_t)((N + BN - 1) / BN);
             return launch(gemm_relu_tile3_kernel<true, E, true>, p.grid, THREADS, stream, A, B, C, M, N, K, lda, ldb,
-                          ldc, tiles_m, tiles_n, (uint32_t)p.group_m, (int)p.vec_c, ep);
+                          ldc, tiles_m, tiles_n, order_word(p), (int)p.vec_c, ep);
         }
         case GR_PATH_TILE_EDGE:
             switch (p.vec_a) {
@@ -697,7 +745,7 @@ int run(const gr_plan_t& p, int64_t M, int64_t N, int64_t K, const uint16_t* A, 
             static_assert(kTileStreamRows == 4 * MAX_M, "4 blocks of 16 rows per workgroup");
             return launch(gemm_relu_smallm_stream_kernel<kStreamNB, kStreamW, kStreamR, stream::WHOLE, E, false, 4, true>,
                           p.grid, p.threads, stream, A, B, C, static_cast<float*>(nullptr), M, N, K, lda, ldb, ldc, K,
-                          nb, ep);
+                          nb, order_word(p), ep);
         }
         case GR_PATH_SMALL_M: {
             using namespace gr::smallm;
@@ -707,14 +755,14 @@ int run(const gr_plan_t& p, int64_t M, int64_t N, int64_t K, const uint16_t* A, 
                 if (M <= MAX_M)
                     return launch(gemm_relu_smallm_stream_kernel<kStreamNB, kStreamW, kStreamR, stream::WHOLE, E>,
                                   p.grid, p.threads, stream, A, B, C, no_part, M, N, K, lda, ldb, ldc, K,
-                                  (uint32_t)p.grid, ep);
+                                  (uint32_t)p.grid, 0u, ep);
                 if (M <= 2 * MAX_M)
                     return launch(
                         gemm_relu_smallm_stream_kernel<kStreamNB, kStreamW, kStreamR, stream::WHOLE, E, false, 2>,
-                        p.grid, p.threads, stream, A, B, C, no_part, M, N, K, lda, ldb, ldc, K, (uint32_t)p.grid, ep);
+                        p.grid, p.threads, stream, A, B, C, no_part, M, N, K, lda, ldb, ldc, K, (uint32_t)p.grid, 0u, ep);
                 return launch(gemm_relu_smallm_stream_kernel<kStreamNB, kStreamW, kStreamR, stream::WHOLE, E, false, 4>,
                               p.grid, p.threads, stream, A, B, C, no_part, M, N, K, lda, ldb, ldc, K,
-                              (uint32_t)p.grid, ep);
+                              (uint32_t)p.grid, 0u, ep);
             }
             const bool whole = N % NB == 0 && K % KSTEP == 0;
             constexpr int W = kSmallMWaves, U = kSmallMUnroll;
@@ -805,7 +853,10 @@ int entry(int64_t M, int64_t N, int64_t K, const uint16_t* A, int64_t lda, const
     int st = plan_call(M, N, K, (uintptr_t)A, lda, (uintptr_t)B, ldb, (uintptr_t)C, ldc, (uintptr_t)ws, ws_bytes,
                        true, forced, &pk, &sp, &ts, &p);
     if (st != GR_OK) return st;
-    if (order >= 0) p.group_m = (int32_t)(uint32_t)order;
+    if (order >= 0) {
+        p.group_m = (int32_t)((uint32_t)order & ~gr::kNoXcdRemap);
+        p.plain_order = ((uint32_t)order & gr::kNoXcdRemap) != 0;
+    }
     if (p.path == GR_PATH_NONE) return GR_OK;
     st = check_device();
     if (st != GR_OK) return st;
@@ -949,7 +1000,7 @@ int launch_tile_bt(const gr_plan_t& p, int64_t M, int64_t N, int64_t K, const ui
     const uint32_t tiles_m = (uint32_t)((M + BM - 1) / BM);
     const uint32_t tiles_n = (uint32_t)((N + BN - 1) / BN);
     return launch(gemm_relu_tile_kernel<true, VA, VB, true, E>, p.grid, THREADS, stream, A, Bt, C, M, N, K, lda, ldbt,
-                  ldc, tiles_m, tiles_n, (uint32_t)p.group_m, (int)p.vec_c, ep);
+                  ldc, tiles_m, tiles_n, order_word(p), (int)p.vec_c, ep);
 }
 
 // E: ElemF16 (the fused ReLU; ep is ignored) or Epi<ElemF16 / ElemBF16>.
@@ -984,7 +1035,7 @@ int run_bt(const gr_plan_t& p, int64_t M, int64_t N, int64_t K, const uint16_t* 
             const bool whole = tile_whole(M, N, bm, bn);
             const uint32_t tiles_m = (uint32_t)((M + bm - 1) / bm);
             const uint32_t tiles_n = (uint32_t)((N + bn - 1) / bn);
-            const uint32_t gm = (uint32_t)p.group_m;
+            const uint32_t gm = order_word(p);
             const int vc = p.vec_c;
             if (bm == gr::tile128::BM) {
                 using namespace gr::tile128;
@@ -1164,7 +1215,7 @@ int launch_tile_ta(const gr_plan_t& p, int64_t M, int64_t N, int64_t K, const ui
     const uint32_t tiles_m = (uint32_t)((M + BM - 1) / BM);
     const uint32_t tiles_n = (uint32_t)((N + BN - 1) / BN);
     return launch(gemm_relu_tile_kernel<true, VA, VB, false, gr::ElemF16, true>, p.grid, THREADS, stream, At, B, C,
-                  M, N, K, ldat, ldb, ldc, tiles_m, tiles_n, (uint32_t)p.group_m, (int)p.vec_c, kReluOnly);
+                  M, N, K, ldat, ldb, ldc, tiles_m, tiles_n, order_word(p), (int)p.vec_c, kReluOnly);
 }
 
 int run_ta(const gr_plan_t& p, int64_t M, int64_t N, int64_t K, const uint16_t* At, int64_t ldat, const uint16_t* B,
@@ -1177,14 +1228,14 @@ int run_ta(const gr_plan_t& p, int64_t M, int64_t N, int64_t K, const uint16_t* 
             return launch(gr::smallm::gemm_relu_smallm_stream_kernel<kStreamNB, kStreamTaW, 1,
                                                                      gr::smallm::stream::WHOLE, E, true>,
                           p.grid, p.threads, stream, At, B, C, no_part, M, N, K, ldat, ldb, ldc, K, (uint32_t)p.grid,
-                          kReluOnly);
+                          0u, kReluOnly);
         }
         case GR_PATH_TILE: {
             using namespace gr::tile2;
             const bool whole = tile_whole(M, N, BM, BN);
             const uint32_t tiles_m = (uint32_t)((M + BM - 1) / BM);
             const uint32_t tiles_n = (uint32_t)((N + BN - 1) / BN);
-            const uint32_t gm = (uint32_t)p.group_m;
+            const uint32_t gm = order_word(p);
             const int vc = p.vec_c;
             if (whole)
                 return launch(gemm_relu_tile2_kernel<false, false, E, true>, p.grid, THREADS, stream, At, B, C, M, N,
@@ -1405,7 +1456,7 @@ int run_fp8(const gr_plan_t& p, int64_t M, int64_t N, int64_t K, const uint8_t* 
         float* part = reinterpret_cast<float*>(ws);
         const uint32_t tiles_m = (uint32_t)((M + 127) / 128);
         const uint32_t tiles_n = (uint32_t)((N + 127) / 128);
-        const uint32_t gm = (uint32_t)p.group_m;
+        const uint32_t gm = order_word(p);
         const int vc = (int)p.vec_c;
         const int64_t kps = ts.k_per_split;
         const bool whole = M % 128 == 0 && N % 128 == 0;
@@ -1421,7 +1472,7 @@ int run_fp8(const gr_plan_t& p, int64_t M, int64_t N, int64_t K, const uint8_t* 
         const uint32_t tiles_m = (uint32_t)((M + bm - 1) / bm);
         const uint32_t tiles_n = (uint32_t)((N + bm - 1) / bm);
         const bool whole = M % bm == 0 && N % bm == 0;
-        const uint32_t gm = (uint32_t)p.group_m;
+        const uint32_t gm = order_word(p);
         const int vc = (int)p.vec_c;
         if (bm == 256) {
             if (whole)
@@ -1537,7 +1588,7 @@ int run_mx(const gr_plan_t& p, int64_t M, int64_t N, int64_t Kb, const uint8_t* 
         const uint32_t tiles_m = (uint32_t)((M + bm - 1) / bm);
         const uint32_t tiles_n = (uint32_t)((N + bm - 1) / bm);
         const bool whole = M % bm == 0 && N % bm == 0;
-        const uint32_t gm = (uint32_t)p.group_m;
+        const uint32_t gm = order_word(p);
         const int vc = (int)p.vec_c;
         if (bm == 256) {
             if (whole)
@@ -1697,6 +1748,9 @@ int gemm_relu_f16_workspace_size(int64_t M, int64_t N, int64_t K, const uint16_t
         if (!use_large_tiles(M, N) && tile_split_layout(M, N, K, false, &ts)) *bytes = ts.bytes;
     } else if (tile_unaligned_ok(M, N, K, lda, ldb) && use_large_tiles(M, N)) {
         // the pipelined kernel runs in place on these rows: no workspace
+    } else if (M > kSmallMMaxRows && tile_stream_ok(M, N, K, a, lda, ldb) &&
+               tile_stream_blocks(M, N) <= kTileStreamRound) {
+        // one round of the streaming kernel, planned ahead of the packed copy
     } else if (pack_layout(M, N, K, a, lda, b, ldb, &pk)) {
         *bytes = pk.bytes;
     }

@@ -255,10 +255,13 @@ template <int NB, int W, int R, int MODE, typename E = ElemF16, bool AT = false,
 __global__ __launch_bounds__(64 * W, 1) void gemm_relu_smallm_stream_kernel(
     const uint16_t* __restrict__ A, const uint16_t* __restrict__ B, uint16_t* __restrict__ C,
     float* __restrict__ part, int64_t M, int64_t N, int64_t K, int64_t lda, int64_t ldb, int64_t ldc,
-    int64_t k_per_split, uint32_t n_blocks, EpiArgs ep) {
-    // RBLK: blocks of 16 MB rows over all of M, one per workgroup row of the
-    // grid (workgroup (cb, rb) = blockIdx cb + n_blocks rb), all of K, the
-    // copies cached (every operand block is read by several workgroups).
+    int64_t k_per_split, uint32_t n_blocks, uint32_t order, EpiArgs ep) {
+    // RBLK: blocks of 16 MB rows over all of M, all of K, the copies cached
+    // (every operand block is read by several workgroups).  The grid is
+    // ceil(M / 16 MB) row blocks x n_blocks column blocks; the workgroup's
+    // block comes from tile_of_workgroup with the order word `order` (groups
+    // of row blocks, XCD renumbering unless bit 31 is set; group 1 with bit
+    // 31 is plain row-major order).  The other modes ignore `order`.
     static_assert(!RBLK || (MODE == stream::WHOLE && !AT), "row blocks: one pass, A row-major");
     auto copy16 = [](const void* base, uint32_t voff, uint32_t lds_addr) {
         if constexpr (RBLK) tile2::dma16(base, voff, lds_addr);
@@ -283,9 +286,13 @@ __global__ __launch_bounds__(64 * W, 1) void gemm_relu_smallm_stream_kernel(
 
     const uint32_t tid = threadIdx.x, lane = tid & 63u;
     const uint32_t w = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const uint32_t cb = blockIdx.x % n_blocks;
+    uint32_t cb = blockIdx.x % n_blocks;
     int64_t s = blockIdx.x / n_blocks;
     if constexpr (RBLK) {
+        uint32_t rb, nb;
+        tile_of_workgroup(blockIdx.x, gridDim.x, gridDim.x / n_blocks, n_blocks, order, rb, nb);
+        cb = nb;
+        s = rb;
         A += s * ROWS * lda;
         C += s * ROWS * ldc;
         M = M - s * ROWS < ROWS ? M - s * ROWS : ROWS;

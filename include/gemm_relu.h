@@ -105,8 +105,10 @@ extern "C" {
 #define GR_PATH_TILE_UNALIGNED 7 /* the pipelined 256x256 kernel in place on rows that are  */
                                  /* not 16-byte aligned and/or K % 64 != 0: direct-to-LDS */
                                  /* copies from any 2-byte address, the K tail (1..64)    */
-                                 /* copied as one strip and masked; M, N >= 256, K > 128, */
-                                 /* more than 128 tiles (planner); no workspace            */
+                                 /* copied as one strip and masked; M, N >= 256, K > 128; */
+                                 /* the planner's choice for such rows with more than 128 */
+                                 /* tiles, and with fewer when no workspace lets it pack  */
+                                 /* and the streaming kernel does not apply; no workspace */
 #define GR_PATH_TILE_PERSISTENT 8 /* the pipelined 256x256 kernel as a persistent tile loop: */
                                   /* at most one workgroup per CU, each storing a finished */
                                   /* tile while the next tile's first copies are in flight */
@@ -117,8 +119,13 @@ extern "C" {
                               /* direct-to-LDS copies of their own, no barrier in the    */
                               /* loop) and add their partial sums in order at the end;   */
                               /* K % 32 == 0, 16-byte rows of A, N >= 64, B of any       */
-                              /* alignment; the planner's choice where 128x128 tiles     */
-                              /* would number fewer than 128 (few tiles: the split-K    */
+                              /* alignment; blocks placed for L2 reuse per XCD          */
+                              /* (plain_order).  The planner's choice for few blocks     */
+                              /* (ceil(M/64) x ceil(N/64), 512 fill one round): with     */
+                              /* aligned B up to 256 of them from K = 512, 384 from      */
+                              /* K = 1024, 512 from K = 2048; with B's rows misaligned   */
+                              /* up to 512, and 1024 for K <= 2048 when no workspace     */
+                              /* lets the operands be packed (few tiles: the split-K    */
                               /* remedy of the TileLang tutorial's "性能取证", within one */
                               /* workgroup); no workspace                                 */
 
@@ -140,6 +147,11 @@ typedef struct gr_plan_t {
     int64_t workspace;   /* bytes of the caller's workspace the path uses (else 0)     */
     int32_t split_k;     /* K splits (the *_SPLIT paths); 1 for the tile and small-M  */
                          /* paths                                                       */
+    int32_t plain_order; /* workgroup order of the tiled grids: 0 = each XCD takes a   */
+                         /* contiguous range of tiles, walked in groups of group_m     */
+                         /* tile rows; 1 = tile order follows the workgroup id         */
+                         /* (GR_PATH_TILE_STREAM when its number of 64-column blocks   */
+                         /* is a multiple of 4)                                        */
 } gr_plan_t;
 
 /*
@@ -210,9 +222,11 @@ int gemm_relu_f16_forced(int64_t M, int64_t N, int64_t K,
 /*
  * gemm_relu_f16_forced_order -- gemm_relu_f16_forced with the workgroup order
  * of the tile kernels chosen by the caller: `group_m` tile rows per group of
- * the grid-level swizzle (>= 1; the planner uses 4) and `xcd_remap` 1 (the
- * planner's choice: each XCD takes a contiguous range of tiles) or 0 (tile
- * order follows the workgroup id).  The order decides only when each tile
+ * the grid-level swizzle (>= 1; the planner uses 4) and `xcd_remap` 1 (each
+ * XCD takes a contiguous range of tiles: the planner's choice, plain_order =
+ * 0) or 0 (tile order follows the workgroup id: plain_order = 1, which the
+ * planner takes for GR_PATH_TILE_STREAM when its number of 64-column blocks
+ * is a multiple of 4).  The order decides only when each tile
  * runs, never what it computes, so every setting must give the same bits:
  * the test hook that checks exactly that.  The pages give the grid swizzle
  * (panel size, ordering) as a free scheduling choice for L2 reuse (TileLang

@@ -199,8 +199,11 @@ def test_plan_ragged_vector_widths():
     st, p = plan(4099, 3071, 2050)
     assert st == gr.GR_OK and p["path"] == gr.GR_PATH_TILE_UNALIGNED
     assert (p["vec_a"], p["vec_b"], p["vec_c"]) == (2, 1, 8)
-    # misaligned base pointer drops to narrower loads
+    # misaligned base pointer: the unaligned kernel copies in place; where it
+    # does not apply (M < 256) the guarded kernel drops to narrower loads
     st, p = plan(512, 512, 512, a=BASE_A + 2)
+    assert p["path"] == gr.GR_PATH_TILE_UNALIGNED and p["vec_a"] == 1
+    st, p = plan(200, 512, 512, a=BASE_A + 2)
     assert p["path"] == gr.GR_PATH_TILE_EDGE and p["vec_a"] == 1
 
 
@@ -212,9 +215,10 @@ def test_plan_partial_tiles_take_the_pipelined_kernel():
     assert plan(256, 1, 32, ldb=8)[1]["path"] == gr.GR_PATH_TILE
     # up to 64 rows of A and at most 256 column strips: the small-M stream
     # (2 or 4 row blocks); more rows: 64 x 64 blocks on the streaming kernel
-    # while 128 x 128 tiles would be fewer than 128 (B of any alignment),
-    # else the pipelined kernel (rows past M clamped); K % 32 != 0 or rows
-    # of A not 16-byte aligned: guarded kernel
+    # where they beat the pipelined kernel (few blocks, K long enough; B of
+    # any alignment), else the pipelined kernel (rows past M clamped); K % 32
+    # != 0 or rows of A not 16-byte aligned: the unaligned kernel (M, N >=
+    # 256, K > 128), else the guarded kernel
     st, p = plan(17, 512, 512)
     assert p["path"] == gr.GR_PATH_SMALL_M and (p["block_m"], p["grid"]) == (32, 8)
     st, p = plan(64, 16384, 512)
@@ -228,8 +232,57 @@ def test_plan_partial_tiles_take_the_pipelined_kernel():
     assert plan(512, 512, 48)[1]["path"] == gr.GR_PATH_TILE_EDGE
     assert plan(512, 500, 512)[1]["path"] == gr.GR_PATH_TILE_STREAM
     assert plan(512, 512, 512, b=BASE_B + 8)[1]["path"] == gr.GR_PATH_TILE_STREAM
-    assert plan(512, 500, 512, lda=516)[1]["path"] == gr.GR_PATH_TILE_EDGE
-    assert plan(512, 512, 512, a=BASE_A + 8)[1]["path"] == gr.GR_PATH_TILE_EDGE
+    assert plan(512, 500, 512, lda=516)[1]["path"] == gr.GR_PATH_TILE_UNALIGNED
+    assert plan(512, 512, 512, a=BASE_A + 8)[1]["path"] == gr.GR_PATH_TILE_UNALIGNED
+    assert plan(255, 512, 512, a=BASE_A + 8)[1]["path"] == gr.GR_PATH_TILE_EDGE
+    assert plan(512, 512, 128, lda=130)[1]["path"] == gr.GR_PATH_TILE_EDGE
+
+
+@pytest.mark.parametrize("M,N,K,stream", [
+    # aligned rows: up to 256 blocks of 64 x 64 from K = 512, 384 from
+    # K = 1024, 512 (one round: two per CU) from K = 2048
+    (1024, 1024, 256, False), (1024, 1024, 480, False), (1024, 1024, 512, True), (65, 64, 512, True),
+    (1024, 1536, 512, False), (1024, 1536, 1024, True), (1024, 1600, 1024, False),
+    (1024, 2048, 1024, False), (1024, 2048, 2048, True), (1088, 1856, 8192, True),
+    (1088, 2048, 8192, False), (1536, 1536, 4096, False),
+])
+def test_tile_stream_thresholds(M, N, K, stream):
+    st, p = plan(M, N, K)
+    assert st == gr.GR_OK
+    assert p["path"] == (gr.GR_PATH_TILE_STREAM if stream else gr.GR_PATH_TILE), (M, N, K, p)
+
+
+@pytest.mark.parametrize("M,N,K,ws,path,asks", [
+    # B's rows misaligned (odd pitch): one round at any K, with or without a
+    # workspace (none is asked for); up to two rounds for K <= 2048 without
+    # one (with one: the packed copy); beyond that the unaligned kernel in
+    # place
+    (1024, 2048, 4096, False, gr.GR_PATH_TILE_STREAM, False),
+    (1024, 2048, 4096, True, gr.GR_PATH_TILE_STREAM, False),
+    (1024, 1024, 256, False, gr.GR_PATH_TILE_STREAM, False),
+    (2048, 2048, 2048, False, gr.GR_PATH_TILE_STREAM, True),
+    (2048, 2048, 2048, True, gr.GR_PATH_TILE_PACKED, True),
+    (2048, 2048, 2080, False, gr.GR_PATH_TILE_UNALIGNED, True),
+    (2048, 2112, 1024, False, gr.GR_PATH_TILE_UNALIGNED, True),
+])
+def test_tile_stream_with_misaligned_b(M, N, K, ws, path, asks):
+    st, size = ws_size(M, N, K, ldb=N + 1)
+    assert st == gr.GR_OK and (size > 0) == asks, size
+    st, p = plan_ws(M, N, K, size, ldb=N + 1) if ws else plan(M, N, K, ldb=N + 1)
+    assert st == gr.GR_OK and p["path"] == path, (M, N, K, ws, p)
+
+
+@pytest.mark.parametrize("N,plain", [(1024, True), (1792, True), (1856, False), (1920, False), (1984, False),
+                                     (1000, True), (960, False)])
+def test_tile_stream_workgroup_order(N, plain):
+    # plain row-major order when the number of 64-column blocks is a multiple
+    # of 4 (each XCD then holds a quarter or an eighth of B's columns), else
+    # the XCD renumbering with groups of 4 row blocks
+    st, p = plan(1024, N, 4096)
+    assert st == gr.GR_OK and p["path"] == gr.GR_PATH_TILE_STREAM, p
+    assert p["plain_order"] == (1 if plain else 0) and p["group_m"] == (1 if plain else 4), p
+    # every other path keeps the XCD renumbering
+    assert plan(4096, 4096, 4096)[1]["plain_order"] == 0
 
 
 def ws_size(M, N, K, lda=None, ldb=None, ldc=None, a=BASE_A, b=BASE_B, c=BASE_C):
@@ -262,13 +315,18 @@ def test_unaligned_path_takes_large_misaligned_problems_in_place():
     assert plan(4096, 3071, 2048)[1]["path"] == gr.GR_PATH_TILE_UNALIGNED
     assert plan(4096, 4096, 4096, a=BASE_A + 2)[1]["path"] == gr.GR_PATH_TILE_UNALIGNED
     assert plan(4096, 4096, 4100)[1]["path"] == gr.GR_PATH_TILE_UNALIGNED
-    # its limits: one tile in M and N, K > 128, more than 128 tiles
+    # its limits: one tile in M and N, K > 128
     assert plan(4096, 255, 4100)[1]["path"] == gr.GR_PATH_TILE_EDGE
     assert plan(255, 65536, 4100)[1]["path"] == gr.GR_PATH_TILE_EDGE
     assert plan(4096, 4096, 127)[1]["path"] == gr.GR_PATH_TILE_EDGE
     assert plan(4096, 4096, 129)[1]["path"] == gr.GR_PATH_TILE_UNALIGNED
-    assert plan(2048, 4096, 4100)[1]["path"] == gr.GR_PATH_TILE_EDGE  # 128 tiles
-    assert plan(2304, 4096, 4100)[1]["path"] == gr.GR_PATH_TILE_UNALIGNED  # 144 tiles
+    # with more than 128 tiles it needs no workspace; with fewer a workspace
+    # lets the operands be packed instead, and without one it runs in place
+    assert ws_size(2304, 4096, 4100) == (gr.GR_OK, 0)  # 144 tiles
+    st, size = ws_size(2048, 4096, 4100)  # 128 tiles
+    assert st == gr.GR_OK and size > 0
+    assert plan(2048, 4096, 4100)[1]["path"] == gr.GR_PATH_TILE_UNALIGNED
+    assert plan_ws(2048, 4096, 4100, size)[1]["path"] == gr.GR_PATH_TILE_PACKED
 
 
 def test_workspace_size_and_packed_plan():
@@ -279,9 +337,9 @@ def test_workspace_size_and_packed_plan():
     st, p = plan_ws(2048, 2048, 1000, size, lda=1001, ldb=2049)
     assert st == gr.GR_OK and p["path"] == gr.GR_PATH_TILE_PACKED and p["packed"] == 3
     assert p["workspace"] == size and p["grid"] == 16 * 16  # 128 x 128 tiles (64 large ones are too few)
-    # one byte short, or no workspace: the guarded kernel
-    assert plan_ws(2048, 2048, 1000, size - 1, lda=1001, ldb=2049)[1]["path"] == gr.GR_PATH_TILE_EDGE
-    assert plan(2048, 2048, 1000, lda=1001, ldb=2049)[1]["path"] == gr.GR_PATH_TILE_EDGE
+    # one byte short, or no workspace: the unaligned kernel in place
+    assert plan_ws(2048, 2048, 1000, size - 1, lda=1001, ldb=2049)[1]["path"] == gr.GR_PATH_TILE_UNALIGNED
+    assert plan(2048, 2048, 1000, lda=1001, ldb=2049)[1]["path"] == gr.GR_PATH_TILE_UNALIGNED
     # K % 32 == 0 with only B misaligned: only B is copied, K unchanged
     st, size = ws_size(2048, 3071, 2048)
     assert size == 2048 * rup(3071, 8) * 2
@@ -293,9 +351,12 @@ def test_workspace_size_and_packed_plan():
     # aligned K % 64 != 0 (but K % 32 != 0 too): both padded
     st, size = ws_size(1024, 1024, 1000)
     assert size == 1024 * 1024 * 2 + 1024 * 1024 * 2
-    # below the size threshold the planner keeps the single-launch kernel
+    # below the size threshold the planner keeps a single-launch kernel (the
+    # size still tells a forced packed call what it needs)
     st, size = ws_size(300, 300, 300)
-    assert size > 0 and plan_ws(300, 300, 300, size)[1]["path"] == gr.GR_PATH_TILE_EDGE
+    assert size > 0 and plan_ws(300, 300, 300, size)[1]["path"] == gr.GR_PATH_TILE_UNALIGNED
+    st, size = ws_size(200, 300, 300)
+    assert size > 0 and plan_ws(200, 300, 300, size)[1]["path"] == gr.GR_PATH_TILE_EDGE
 
 
 def test_workspace_not_used_where_it_cannot_help():
@@ -358,7 +419,9 @@ def test_tile_split_plan():
     assert plan_ws(1024, 1024, 4096, 1 << 30)[1]["split_k"] == 4
     # 128 tiles: 2 splits; at K = 4096 they save 64 of 128 strips, just enough
     assert plan_ws(256, 8192, 4096, 1 << 30)[1]["split_k"] == 2
-    assert plan_ws(256, 8192, 2048, 1 << 30)[1]["path"] == gr.GR_PATH_TILE
+    # at K = 2048 two splits save too little: the streaming kernel (512
+    # blocks of 64 x 64, one round) instead
+    assert plan_ws(256, 8192, 2048, 1 << 30)[1]["path"] == gr.GR_PATH_TILE_STREAM
     # a split must save at least 64 strips: not at 1024^3 (4 splits save 24)
     # nor 2048^3 (256 tiles); large tiles that fill the chip never split
     assert ws_size(1024, 1024, 1024) == (gr.GR_OK, 0)
@@ -461,16 +524,25 @@ def test_planner_invariants_on_random_problems():
             assert M <= 16 or -(-N // 64) <= 256, key  # wider C with more rows: the tile kernel
         elif p["path"] == gr.GR_PATH_TILE_STREAM:
             assert M > 64 and K > 0 and K % 32 == 0 and a % 16 == 0 and lda % 8 == 0 and N >= 64, key
-            assert -(-M // 128) * -(-N // 128) < 128, key  # few 128 x 128 tiles
-            assert p["block_m"] == 64 and p["grid"] == -(-M // 64) * -(-N // 64), key
+            blocks = -(-M // 64) * -(-N // 64)
+            if aligned:  # few blocks, K long enough to beat the 128 x 128 tiles
+                assert (blocks <= 256 and K >= 512) or (blocks <= 384 and K >= 1024) or \
+                    (blocks <= 512 and K >= 2048), key
+            else:  # B misaligned: one round, or two for K <= 2048
+                assert blocks <= 512 or (blocks <= 1024 and K <= 2048), key
+                assert size == 0 or blocks > 512, key  # within one round no workspace is asked for
+            assert p["block_m"] == 64 and p["grid"] == blocks, key
+            assert p["plain_order"] == (1 if -(-N // 64) % 4 == 0 else 0), key
         elif p["path"] == gr.GR_PATH_TILE_UNALIGNED:
             assert not (aligned and K % 32 == 0), key
             assert M >= 256 and N >= 256 and K > 128, key
             tiles = -(-M // 256) * -(-N // 256)
-            assert tiles > 128 and p["grid"] == tiles and p["block_m"] == 256 and size == 0, key
+            assert p["grid"] == tiles and p["block_m"] == 256, key
+            assert tiles <= 128 or size == 0, key  # more than 128 tiles: never packed
         else:
             assert p["path"] == gr.GR_PATH_TILE_EDGE, key
             assert not (aligned and K % 32 == 0 and K > 0), key
+            assert not (M >= 256 and N >= 256 and K > 128), key  # else the unaligned kernel
         # the workspace plan differs from the plain one only where a workspace was asked for
         if size == 0:
             assert pw["path"] == p["path"] and pw["workspace"] == 0, key

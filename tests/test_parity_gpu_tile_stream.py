@@ -5,8 +5,11 @@ Blocks of 64 rows x 64 columns of C, one per workgroup; the workgroup's four
 waves take the 32-row slots of K in turn through rings of direct-to-LDS
 copies of their own and add their fp32 partial sums in wave order at the
 end, so ReLU sees the complete sum (the split-K of the TileLang tutorial's
-chapter "性能取证", kept inside one workgroup).  The planner takes it where
-128 x 128 tiles would number fewer than 128, e.g. the 1024^3 workload.
+chapter "性能取证", kept inside one workgroup).  The planner takes it for few
+blocks with K long enough (e.g. the 1024^3 workload) and, for B's rows
+misaligned, up to one or two rounds of blocks; the workgroup order (plain
+row-major, or XCD renumbering with groups of 4 row blocks) never changes a
+bit.
 Bar: |gpu - oracle| <= 1e-2 + 1e-2 |oracle| per element, no NaN or Inf,
 C's padding and rows past M untouched.
 """
@@ -97,6 +100,34 @@ def test_tile_stream_and_tile_kernel_agree():
     c1 = out[gr.GR_PATH_TILE_STREAM].view(np.float16).astype(np.float64)
     c2 = out[gr.GR_PATH_TILE].view(np.float16).astype(np.float64)
     assert np.all(np.abs(c1 - c2) <= 1e-2 + 1e-2 * np.abs(c2))
+
+
+@pytest.mark.parametrize("M,N,K,ldb", [(1088, 1856, 2048, 1856), (1024, 2048, 512, 2049), (700, 1100, 128, 1101)])
+def test_planned_tile_stream_matches_oracle(M, N, K, ldb):
+    """The plain call where the planner picks the streaming path: 29 column
+    blocks (XCD renumbering, 493 workgroups), B's rows misaligned over one
+    full round (512 blocks, plain order) and a short K with misaligned B and
+    18 column blocks (XCD renumbering); sampled oracle check, and every
+    workgroup order gives the same bits."""
+    import torch as t
+    A, B = synth.random_operands(M, N, K, seed=M + K, ldb=ldb)
+    st, p = gr.gemm_relu_f16_plan(M, N, K, 0x100000, K, 0x200000000000, ldb, 0x400000000000, N)
+    assert st == gr.GR_OK and p["path"] == gr.GR_PATH_TILE_STREAM, p
+    dA, dB = to_dev(A), to_dev(B)
+    dC = full_dev((M * N,), SENTINEL)
+    log("planned tile_stream %dx%dx%d ldb=%d order=%d/%d" % (M, N, K, ldb, p["group_m"], p["plain_order"]))
+    assert call(M, N, K, dA, K, dB, ldb, dC, N) == gr.GR_OK
+    C = from_dev(dC).reshape(M, N)
+    ii, jj = synth.sample_indices(M, N, 4096, M)
+    ref = oracle.gemm_relu_elems(A, B, ii, jj, M=M, N=N, K=K, lda=K, ldb=ldb)
+    log("parity %s" % (assert_parity(C[ii, jj], ref, "planned tile_stream %dx%dx%d" % (M, N, K)),))
+    for gm, remap in ((1, 0), (4, 1), (3, 1), (64, 0)):
+        dC2 = full_dev((M * N,), SENTINEL)
+        assert gr.gemm_relu_f16_forced_order(M, N, K, dA.data_ptr(), K, dB.data_ptr(), ldb, dC2.data_ptr(), N,
+                                             t.cuda.current_stream().cuda_stream, gr.GR_PATH_TILE_STREAM, gm,
+                                             remap) == gr.GR_OK
+        t.cuda.synchronize()
+        assert np.array_equal(C, from_dev(dC2).reshape(M, N)), (gm, remap)
 
 
 def test_all_ones_exact_on_tile_stream():
