@@ -257,9 +257,9 @@ bool use_large_tiles(int64_t M, int64_t N) {
 //  * rows of B not 16-byte aligned: the alternatives are the in-place
 //    unaligned 256 x 256 kernel, the packed path (workspace) and the
 //    guarded kernel.  Streaming wins up to one round at any K (1024 x 2048
-//    x 4096: 49.3 against 82.8 unaligned, 48.5 packed, 176 guarded) and, with
-//    no workspace, up to two rounds for K <= 2048 (2048^2 x 1024: 29.5
-//    against 31.6 unaligned; x 4096: 93.0 against 83.0).
+//    x 4096: 43.5 against 83.1 unaligned, 48.5 packed, 176 guarded) and, with
+//    no workspace, up to two rounds for K <= 2048 (2048^2 x 2048: 45.8
+//    against 48.8 unaligned, 32.1 packed; x 4096: 82.0 against 83.4).
 // Needs what the streaming kernel needs: K % 32 == 0, 16-byte rows of A,
 // N >= 64; B of any alignment.
 constexpr int64_t kTileStreamRows = 64;  // 4 blocks of 16 rows per workgroup

@@ -286,13 +286,20 @@ __global__ __launch_bounds__(64 * W, 1) void gemm_relu_smallm_stream_kernel(
 
     const uint32_t tid = threadIdx.x, lane = tid & 63u;
     const uint32_t w = __builtin_amdgcn_readfirstlane(tid >> 6);
-    uint32_t cb = blockIdx.x % n_blocks;
-    int64_t s = blockIdx.x / n_blocks;
-    if constexpr (RBLK) {
+    uint32_t cb;
+    int64_t s;
+    if (RBLK && order != (kNoXcdRemap | 1u)) {
         uint32_t rb, nb;
         tile_of_workgroup(blockIdx.x, gridDim.x, gridDim.x / n_blocks, n_blocks, order, rb, nb);
         cb = nb;
         s = rb;
+    } else {
+        // plain row-major order without the general mapping's divisions
+        // (they delay the first copies: 1024^3 8.70 -> 8.60 us)
+        cb = blockIdx.x % n_blocks;
+        s = blockIdx.x / n_blocks;
+    }
+    if constexpr (RBLK) {
         A += s * ROWS * lda;
         C += s * ROWS * ldc;
         M = M - s * ROWS < ROWS ? M - s * ROWS : ROWS;
