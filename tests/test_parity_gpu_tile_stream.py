@@ -102,13 +102,15 @@ def test_tile_stream_and_tile_kernel_agree():
     assert np.all(np.abs(c1 - c2) <= 1e-2 + 1e-2 * np.abs(c2))
 
 
-@pytest.mark.parametrize("M,N,K,ldb", [(1088, 1856, 2048, 1856), (1024, 2048, 512, 2049), (700, 1100, 128, 1101)])
+@pytest.mark.parametrize("M,N,K,ldb", [(1088, 1856, 2048, 1856), (1024, 2048, 512, 2049), (700, 1100, 128, 1101),
+                                     (2048, 2048, 256, 2049)])
 def test_planned_tile_stream_matches_oracle(M, N, K, ldb):
     """The plain call where the planner picks the streaming path: 29 column
     blocks (XCD renumbering, 493 workgroups), B's rows misaligned over one
-    full round (512 blocks, plain order) and a short K with misaligned B and
-    18 column blocks (XCD renumbering); sampled oracle check, and every
-    workgroup order gives the same bits."""
+    full round (512 blocks, plain order), a short K with misaligned B and 18
+    column blocks (XCD renumbering), and misaligned B over two rounds (1024
+    blocks, no workspace); sampled oracle check, and every workgroup order
+    gives the same bits."""
     import torch as t
     A, B = synth.random_operands(M, N, K, seed=M + K, ldb=ldb)
     st, p = gr.gemm_relu_f16_plan(M, N, K, 0x100000, K, 0x200000000000, ldb, 0x400000000000, N)

@@ -130,6 +130,31 @@ def test_ragged_workload_runs_in_place_with_or_without_workspace():
     assert_parity(C[:, cols].T, oracle.gemm_relu_cols(A, B, cols), "ragged cols")
 
 
+@pytest.mark.parametrize("M,N,K,lda,ldb,offs", [
+    (512, 512, 512, 512, 512, (1, 0, 0)),     # A's base pointer misaligned
+    (300, 300, 300, 300, 300, (0, 0, 0)),     # 600-byte rows: 8-byte aligned only
+    (1000, 700, 1000, 1001, 700, (0, 0, 0)),  # ragged K, odd pitch of A
+    (256, 2000, 130, 130, 2003, (0, 3, 0)),   # one tile row, tail 2, B misaligned
+])
+def test_plain_call_takes_the_unaligned_kernel_on_misaligned_mid_size_problems(M, N, K, lda, ldb, offs):
+    """Without a workspace, misaligned rows or a ragged K with M, N >= 256 and
+    K > 128 run on the unaligned kernel in place (the guarded kernel was 2-5x
+    slower there): full oracle check."""
+    A, B = synth.random_operands(M, N, K, seed=M + 2 * N + K, lda=lda, ldb=ldb)
+    Ap = np.concatenate([np.full(offs[0], 0x7BFF, np.uint16), A.ravel()])
+    Bp = np.concatenate([np.full(offs[1], 0x7BFF, np.uint16), B.ravel()])
+    st, p = gr.gemm_relu_f16_plan(M, N, K, 0x100000 + 2 * offs[0], lda, 0x200000000000 + 2 * offs[1], ldb,
+                                  0x400000000000, N)
+    assert st == gr.GR_OK and p["path"] == gr.GR_PATH_TILE_UNALIGNED, p
+    dC = full_dev(((M + 2) * N,), SENTINEL)
+    log("planned unaligned %dx%dx%d lda=%d ldb=%d offsets=%s" % (M, N, K, lda, ldb, offs))
+    assert call(M, N, K, to_dev(Ap), lda, to_dev(Bp), ldb, dC, N, offsets=offs) == gr.GR_OK
+    Cflat = from_dev(dC)
+    assert np.all(Cflat[M * N:] == SENTINEL), "a row past M was written"
+    assert_parity(Cflat[:M * N].reshape(M, N), oracle.gemm_relu_full(A, B, M=M, N=N, K=K, lda=lda, ldb=ldb),
+                  "planned unaligned %dx%dx%d" % (M, N, K))
+
+
 @pytest.mark.parametrize("r", range(1, 8))
 @pytest.mark.parametrize("path", [gr.GR_PATH_TILE_UNALIGNED, gr.GR_PATH_TILE])
 def test_partial_row_segments_of_every_length(r, path):
