@@ -956,9 +956,30 @@ bool tile_bt_ok(int64_t M, int64_t N, int64_t K, uintptr_t A, int64_t lda, uintp
            lda <= MAX_LDA && ldbt <= MAX_LDA;
 }
 
+// The row-blocked streaming kernel with B given transposed (its BT mode):
+// blocks of 16 rows of Bt are copied and read like those of A, so Bt needs
+// what A needs (16-byte rows, pitch within the 32-bit copy offsets).  M > 16:
+// fewer rows take the transposed-B small-M kernels.
+bool tile_stream_bt_ok(int64_t M, int64_t N, int64_t K, uintptr_t A, int64_t lda, uintptr_t Bt, int64_t ldbt) {
+    return M > kSmallMThreshold && smallm_stream_ok(M, N, K, A, lda, ldbt, kStreamNB, kMaxDim) && Bt % 16 == 0 &&
+           ldbt % 8 == 0;
+}
+// Where it beats the transposed-B tile kernels.  Its copies of Bt move 64
+// bytes of each row per slot (row-major B: 128), so with two blocks per CU it
+// trails the row-major streaming path (us, back to back): 1024^2 x 1024 8.6
+// against 12.0 for the tiles, 32 x 4096 x 4096 17.1 against 35.6, but 1024 x
+// 2048 x 2048 (512 blocks) 23.7 against 20.7, 1536 x 1216 x 4096 (456) 39.0
+// against 37.2; from K = 8192 it wins there too (1024 x 2048 x 8192: 67.0
+// against 71.8).
+bool tile_stream_bt_beats_tiles(int64_t blocks, int64_t K) {
+    return (blocks <= 256 && K >= 512) || (blocks <= kTileStreamRound && K >= 8192);
+}
+
 int choose_path_bt(int64_t M, int64_t N, int64_t K, uintptr_t A, int64_t lda, uintptr_t Bt, int64_t ldbt) {
     if (M == 0 || N == 0) return GR_PATH_NONE;
     if (smallm_bt_ok(M, K, A, lda, Bt, ldbt)) return GR_PATH_SMALL_M;
+    if (tile_stream_bt_ok(M, N, K, A, lda, Bt, ldbt) && tile_stream_bt_beats_tiles(tile_stream_blocks(M, N), K))
+        return GR_PATH_TILE_STREAM;
     if (tile_bt_ok(M, N, K, A, lda, Bt, ldbt)) return GR_PATH_TILE;
     return GR_PATH_TILE_EDGE;
 }
@@ -1062,6 +1083,14 @@ int run_bt(const gr_plan_t& p, int64_t M, int64_t N, int64_t K, const uint16_t* 
             return launch(gemm_relu_tile2_kernel<true, true, E>, p.grid, THREADS, stream, A, Bt, C, M, N, K, lda,
                           ldbt, ldc, tiles_m, tiles_n, gm, vc, ep);
         }
+        case GR_PATH_TILE_STREAM: {
+            using namespace gr::smallm;
+            const uint32_t nb = (uint32_t)((N + kStreamNB - 1) / kStreamNB);
+            return launch(
+                gemm_relu_smallm_stream_kernel<kStreamNB, kStreamW, kStreamR, stream::WHOLE, E, false, 4, true, true>,
+                p.grid, p.threads, stream, A, Bt, C, static_cast<float*>(nullptr), M, N, K, lda, ldbt, ldc, K, nb,
+                order_word(p), ep);
+        }
         case GR_PATH_TILE_EDGE: {
             const int va = p.vec_a, vb = p.vec_b;
             if (va == 8 && vb == 8) return launch_tile_bt<8, 8, E>(p, M, N, K, A, lda, Bt, ldbt, C, ldc, ep, stream);
@@ -1088,6 +1117,8 @@ int plan_call_bt(int64_t M, int64_t N, int64_t K, uintptr_t a, int64_t lda, uint
             if (!tile_bt_ok(M, N, K, a, lda, bt, ldbt)) return GR_ERR_INVALID_PATH;
         } else if (forced == GR_PATH_SMALL_M) {
             if (!smallm_bt_ok(M, K, a, lda, bt, ldbt)) return GR_ERR_INVALID_PATH;
+        } else if (forced == GR_PATH_TILE_STREAM) {
+            if (!tile_stream_bt_ok(M, N, K, a, lda, bt, ldbt)) return GR_ERR_INVALID_PATH;
         } else if (forced != GR_PATH_TILE_EDGE) {
             return GR_ERR_INVALID_PATH;
         }
@@ -1704,7 +1735,8 @@ int gemm_relu_f16_bt(int64_t M, int64_t N, int64_t K, const uint16_t* A, int64_t
 
 int gemm_relu_f16_bt_forced(int64_t M, int64_t N, int64_t K, const uint16_t* A, int64_t lda, const uint16_t* Bt,
                             int64_t ldbt, uint16_t* C, int64_t ldc, void* stream, int path) {
-    if (path != GR_PATH_TILE && path != GR_PATH_TILE_EDGE && path != GR_PATH_SMALL_M) return GR_ERR_INVALID_PATH;
+    if (path != GR_PATH_TILE && path != GR_PATH_TILE_EDGE && path != GR_PATH_SMALL_M && path != GR_PATH_TILE_STREAM)
+        return GR_ERR_INVALID_PATH;
     return entry_bt(M, N, K, A, lda, Bt, ldbt, C, ldc, stream, path);
 }
 
@@ -1782,7 +1814,8 @@ int gemm_relu_f16_plan_ws(int64_t M, int64_t N, int64_t K, const uint16_t* A, in
 int gemm_bias_act_bt(int64_t M, int64_t N, int64_t K, const uint16_t* A, int64_t lda, const uint16_t* Bt,
                      int64_t ldbt, const uint16_t* bias, int act, uint16_t* C, int64_t ldc, int fmt, void* stream,
                      int path) {
-    if (path != -1 && path != GR_PATH_TILE && path != GR_PATH_TILE_EDGE && path != GR_PATH_SMALL_M)
+    if (path != -1 && path != GR_PATH_TILE && path != GR_PATH_TILE_EDGE && path != GR_PATH_SMALL_M &&
+        path != GR_PATH_TILE_STREAM)
         return GR_ERR_INVALID_PATH;
     if (fmt == GR_FMT_BF16)
         return entry_bt_epi<gr::ElemBF16>(M, N, K, A, lda, Bt, ldbt, bias, act, C, ldc, stream, path);

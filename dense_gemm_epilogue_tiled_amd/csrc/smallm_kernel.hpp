@@ -251,7 +251,8 @@ __device__ __forceinline__ uint32_t chunk_slot(uint32_t row, uint32_t c) { retur
 
 }  // namespace stream
 
-template <int NB, int W, int R, int MODE, typename E = ElemF16, bool AT = false, int MB = 1, bool RBLK = false>
+template <int NB, int W, int R, int MODE, typename E = ElemF16, bool AT = false, int MB = 1, bool RBLK = false,
+          bool BT = false>
 __global__ __launch_bounds__(64 * W, 1) void gemm_relu_smallm_stream_kernel(
     const uint16_t* __restrict__ A, const uint16_t* __restrict__ B, uint16_t* __restrict__ C,
     float* __restrict__ part, int64_t M, int64_t N, int64_t K, int64_t lda, int64_t ldb, int64_t ldc,
@@ -262,7 +263,12 @@ __global__ __launch_bounds__(64 * W, 1) void gemm_relu_smallm_stream_kernel(
     // block comes from tile_of_workgroup with the order word `order` (groups
     // of row blocks, XCD renumbering unless bit 31 is set; group 1 with bit
     // 31 is plain row-major order).  The other modes ignore `order`.
+    // BT (row blocks only): B is given transposed, N x K with pitch ldb; a
+    // slot's B is NB / 16 blocks of 16 rows of Bt x 32 k, copied and read
+    // like the blocks of A (the MFMA's B operand wants 8 consecutive k of one
+    // column per lane, which is a row piece of Bt).
     static_assert(!RBLK || (MODE == stream::WHOLE && !AT), "row blocks: one pass, A row-major");
+    static_assert(!BT || RBLK, "B transposed: row blocks only");
     auto copy16 = [](const void* base, uint32_t voff, uint32_t lds_addr) {
         if constexpr (RBLK) tile2::dma16(base, voff, lds_addr);
         else tile2::dma16_nt(base, voff, lds_addr);
@@ -278,7 +284,8 @@ __global__ __launch_bounds__(64 * W, 1) void gemm_relu_smallm_stream_kernel(
     constexpr int RPI = 1024 / ROWB;                     // rows per copy instruction
     constexpr int NBLK = NB / 16;                        // MFMA column blocks per slot
     constexpr int T = 64 * W;
-    static_assert(CH >= 8 && DPS * RPI == stream::SLOT_ROWS, "whole rows per copy instruction");
+    static_assert(BT || (CH >= 8 && DPS * RPI == stream::SLOT_ROWS), "whole rows per copy instruction");
+    static_assert(!BT || DPS == NB / 16, "one copy instruction per 16 rows of Bt");
     static_assert(ROWS * NB * 4 <= R * SLOT, "the cross-wave sum fits a wave's slots");
     static_assert(!AT || (R == 1 && MB == 1), "A gathered into registers: one slot per wave, 16 rows");
     static_assert(MB == 1 || MB == 2 || MB == 4, "1, 2 or 4 blocks of 16 rows");
@@ -315,18 +322,23 @@ __global__ __launch_bounds__(64 * W, 1) void gemm_relu_smallm_stream_kernel(
 
     // copy instruction i of a slot: lane -> row i RPI + lane / CH, chunk slot
     // lane % CH, which holds chunk (lane % CH) XOR 2 (row mod 4)
-    uint32_t voff[DPS];
-#pragma unroll
-    for (int i = 0; i < DPS; ++i) {
-        const uint32_t row = i * RPI + lane / CH;
-        voff[i] = (uint32_t)((row * ldb + 8 * stream::chunk_slot(row, lane % CH)) * 2);
-    }
-    const uint16_t* b_range = B + k_begin * ldb + n0;
     // A copy of a slot (ADMA), one per block of 16 rows: lane -> row 16 mb +
     // lane / 4 (rows >= M read row M - 1; their outputs are never stored),
     // chunk slot lane % 4 holding chunk (lane % 4) XOR (row / 4) % 4 of the
-    // row's 32 k.
+    // row's 32 k.  BT: the blocks of Bt (rows n0 + 16 i + lane / 4, all < N)
+    // the same way.
     const uint32_t arow = lane >> 2, apos = lane & 3u;
+    uint32_t voff[DPS];
+#pragma unroll
+    for (int i = 0; i < DPS; ++i) {
+        if constexpr (BT) {
+            voff[i] = (uint32_t)(((16 * i + arow) * ldb + 8 * (apos ^ ((arow >> 2) & 3u))) * 2);
+        } else {
+            const uint32_t row = i * RPI + lane / CH;
+            voff[i] = (uint32_t)((row * ldb + 8 * stream::chunk_slot(row, lane % CH)) * 2);
+        }
+    }
+    const uint16_t* b_range = BT ? B + n0 * ldb + k_begin : B + k_begin * ldb + n0;
     uint32_t aoff[MB];
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb) {
@@ -351,7 +363,7 @@ __global__ __launch_bounds__(64 * W, 1) void gemm_relu_smallm_stream_kernel(
     auto issue = [&](int64_t q) {
         const int64_t t = (int64_t)w + (int64_t)W * q;
         const uint32_t dst = ring + (uint32_t)(q % R) * SLOT;
-        const uint8_t* src = reinterpret_cast<const uint8_t*>(b_range + t * stream::SLOT_ROWS * ldb);
+        const uint8_t* src = reinterpret_cast<const uint8_t*>(b_range + t * stream::SLOT_ROWS * (BT ? 1 : ldb));
 #pragma unroll
         for (int i = 0; i < DPS; ++i) copy16(src, voff[i], dst + i * 1024);
         if constexpr (ADMA) {
@@ -389,15 +401,21 @@ __global__ __launch_bounds__(64 * W, 1) void gemm_relu_smallm_stream_kernel(
         }
 #pragma unroll
         for (int j = 0; j < NBLK; ++j) {
-            const uint32_t c = 2 * j + ((fi >> 1) & 1u);
-            const uint32_t p0 = base + frow * ROWB + (stream::chunk_slot(frow, c) << 4) + 8 * (fi & 1u);
-            const uint32_t p1 = base + (frow + 4) * ROWB + (stream::chunk_slot(frow + 4, c) << 4) + 8 * (fi & 1u);
-            typedef short s16x4 __attribute__((ext_vector_type(4)));
-            const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                (__attribute__((address_space(3))) s16x4*)(uintptr_t)p0);
-            const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                (__attribute__((address_space(3))) s16x4*)(uintptr_t)p1);
-            const f16x8 b = __builtin_bit_cast(f16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+            f16x8 b;
+            if constexpr (BT) {
+                b = *reinterpret_cast<const __attribute__((address_space(3))) f16x8*>(
+                    (uintptr_t)(base + 1024 * j + am * 64 + ((ag ^ ((am >> 2) & 3u)) << 4)));
+            } else {
+                const uint32_t c = 2 * j + ((fi >> 1) & 1u);
+                const uint32_t p0 = base + frow * ROWB + (stream::chunk_slot(frow, c) << 4) + 8 * (fi & 1u);
+                const uint32_t p1 = base + (frow + 4) * ROWB + (stream::chunk_slot(frow + 4, c) << 4) + 8 * (fi & 1u);
+                typedef short s16x4 __attribute__((ext_vector_type(4)));
+                const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                    (__attribute__((address_space(3))) s16x4*)(uintptr_t)p0);
+                const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                    (__attribute__((address_space(3))) s16x4*)(uintptr_t)p1);
+                b = __builtin_bit_cast(f16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+            }
 #pragma unroll
             for (int mb = 0; mb < MB; ++mb) acc[mb][j] = E::mfma16(b, a[mb], acc[mb][j]);
         }

@@ -354,6 +354,12 @@ int gemm_relu_f16_plan_ws(int64_t M, int64_t N, int64_t K,
  *   GR_PATH_SMALL_M   M <= 16, 16-byte rows of A and Bt: each wave streams 16
  *                     rows of Bt, whose 16-byte pieces are MFMA operands as
  *                     they stand;
+ *   GR_PATH_TILE_STREAM  M > 16, 16-byte rows of A and Bt, K % 32 == 0,
+ *                     N >= 64: the row-blocked streaming kernel (64 x 64
+ *                     blocks, K split between a block's 4 waves) with blocks
+ *                     of 16 rows of Bt copied and read like those of A; the
+ *                     planner takes it for up to 256 blocks from K = 512
+ *                     and up to 512 from K = 8192;
  *   GR_PATH_TILE      16-byte rows of A and Bt, K % 32 == 0, pitches of at
  *                     most 2^22 elements: the pipelined kernel with Bt staged
  *                     like A;
@@ -373,9 +379,9 @@ int gemm_relu_f16_bt_plan(int64_t M, int64_t N, int64_t K,
                           const uint16_t* C, int64_t ldc,
                           gr_plan_t* out);
 
-/* gemm_relu_f16_bt on a given path (GR_PATH_TILE, GR_PATH_TILE_EDGE or
-   GR_PATH_SMALL_M; GR_ERR_INVALID_PATH when the path's conditions do not
-   hold).  Test hook. */
+/* gemm_relu_f16_bt on a given path (GR_PATH_TILE, GR_PATH_TILE_EDGE,
+   GR_PATH_SMALL_M or GR_PATH_TILE_STREAM; GR_ERR_INVALID_PATH when the path's
+   conditions do not hold).  Test hook. */
 int gemm_relu_f16_bt_forced(int64_t M, int64_t N, int64_t K,
                             const uint16_t* A, int64_t lda,
                             const uint16_t* Bt, int64_t ldbt,
@@ -560,10 +566,10 @@ int gemm_bias_act_ws(int64_t M, int64_t N, int64_t K,
  * N x K row-major, pitch ldbt; the layout of a linear layer's weight), in
  * fp16 or bfloat16 (fmt: GR_FMT_F16 / GR_FMT_BF16, the format of A, Bt, bias
  * and C): the epilogue of gemm_bias_act_f16 on the paths of gemm_relu_f16_bt
- * (GR_PATH_SMALL_M, GR_PATH_TILE, GR_PATH_TILE_EDGE, chosen as
- * gemm_relu_f16_bt_plan says).  path -1 lets the planner choose; one of those
- * three forces it (test hook; GR_ERR_INVALID_PATH when its conditions do not
- * hold).  Errors as gemm_bias_act_f16, plus GR_ERR_INVALID_ARG for an unknown
+ * (GR_PATH_SMALL_M, GR_PATH_TILE_STREAM, GR_PATH_TILE, GR_PATH_TILE_EDGE,
+ * chosen as gemm_relu_f16_bt_plan says).  path -1 lets the planner choose;
+ * one of those four forces it (test hook; GR_ERR_INVALID_PATH when its
+ * conditions do not hold).  Errors as gemm_bias_act_f16, plus GR_ERR_INVALID_ARG for an unknown
  * fmt.
  */
 int gemm_bias_act_bt(int64_t M, int64_t N, int64_t K,

@@ -579,8 +579,18 @@ def test_transposed_b_planner_and_checks():
     assert p["path"] == gr.GR_PATH_SMALL_M and p["grid"] == 16384 // 64
     st, p = plan_bt(4096, 4096, 4096)
     assert p["path"] == gr.GR_PATH_TILE and p["block_m"] == 256 and p["grid"] == 256
+    # few blocks of 64 x 64 with K long enough: the streaming kernel with Bt
+    # copied like A (up to 256 blocks from K = 512, 512 from K = 8192); M > 16
     st, p = plan_bt(1024, 1024, 1024)
+    assert p["path"] == gr.GR_PATH_TILE_STREAM and (p["block_m"], p["block_n"], p["grid"]) == (64, 64, 256)
+    assert p["plain_order"] == 1
+    st, p = plan_bt(32, 4000, 4096)
+    assert p["path"] == gr.GR_PATH_TILE_STREAM and p["grid"] == 63 and p["plain_order"] == 0
+    st, p = plan_bt(1024, 1024, 256)
     assert p["path"] == gr.GR_PATH_TILE and p["block_m"] == 128
+    assert plan_bt(1024, 1024, 512)[1]["path"] == gr.GR_PATH_TILE_STREAM
+    assert plan_bt(1024, 2048, 4096)[1]["path"] == gr.GR_PATH_TILE  # 512 blocks from K = 8192 only
+    assert plan_bt(1024, 2048, 8192)[1]["path"] == gr.GR_PATH_TILE_STREAM
     assert plan_bt(4096, 4096, 4100)[1]["path"] == gr.GR_PATH_TILE_EDGE          # K % 32 != 0
     assert plan_bt(4096, 4096, 4096, ldbt=4100)[1]["path"] == gr.GR_PATH_TILE_EDGE  # Bt rows not 16-B
     assert plan_bt(8, 4096, 4096, b=BASE_B + 8)[1]["path"] == gr.GR_PATH_TILE_EDGE  # Bt rows not 16-B
@@ -592,6 +602,9 @@ def test_transposed_b_planner_and_checks():
                                       gr.GR_PATH_SMALL_M) == gr.GR_ERR_INVALID_PATH
     assert gr.gemm_relu_f16_bt_forced(8, 256, 64, BASE_A, 64, BASE_B, 64, BASE_C, 256, None,
                                       gr.GR_PATH_TILE_PACKED) == gr.GR_ERR_INVALID_PATH
+    for M, K, ldbt, b in ((16, 64, 64, BASE_B), (300, 48, 48, BASE_B), (300, 64, 68, BASE_B), (300, 64, 64, BASE_B + 8)):
+        assert gr.gemm_relu_f16_bt_forced(M, 256, K, BASE_A, K, b, ldbt, BASE_C, 256, None,
+                                          gr.GR_PATH_TILE_STREAM) == gr.GR_ERR_INVALID_PATH, (M, K, ldbt)
 
 
 def test_bf16_argument_checks_need_no_gpu():

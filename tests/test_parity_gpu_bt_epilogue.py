@@ -29,6 +29,7 @@ CASES = [
     (4096, 3072, 96, 96, 96, 3072, (gr.GR_PATH_TILE, 256), "256 tiles, 32-deep strips"),
     (300, 270, 256, 264, 256, 273, (gr.GR_PATH_TILE, 128), "128 tiles, partial"),
     (300, 270, 100, 101, 103, 273, (gr.GR_PATH_TILE_EDGE, None), "guarded, odd pitches"),
+    (300, 1000, 1024, 1032, 1032, 1001, (gr.GR_PATH_TILE_STREAM, 64), "row-blocked streaming, Bt copied like A"),
 ]
 
 

@@ -132,6 +132,50 @@ def test_planned_tile_stream_matches_oracle(M, N, K, ldb):
         assert np.array_equal(C, from_dev(dC2).reshape(M, N)), (gm, remap)
 
 
+BT_CASES = [
+    # M, N, K, lda, ldbt, ldc, element offsets of A, Bt, C (16-byte rows of A and Bt)
+    (17, 64, 32, 32, 32, 64, (0, 0, 0)),             # one row block of 17 rows, one slot
+    (130, 65, 64, 64, 72, 70, (0, 8, 3)),            # last column block moved left, Bt padded
+    (1000, 1000, 1024, 1032, 1024, 1005, (8, 0, 1)),  # ragged M and N, C misaligned
+    (300, 300, 96, 104, 104, 300, (0, 16, 0)),        # 3 slots
+    (64, 128, 4096, 4096, 4096, 128, (0, 0, 0)),      # one row block, long K
+]
+
+
+@pytest.mark.parametrize("M,N,K,lda,ldbt,ldc,offs", BT_CASES)
+def test_tile_stream_transposed_b_parity(M, N, K, lda, ldbt, ldc, offs):
+    """The streaming kernel with B given as N x K (16-row blocks of Bt copied
+    and read like those of A): full oracle check on padded operands (Bt's
+    padding poisoned with 65504), C's padding and rows past M untouched, and
+    the same bits as the row-major layout on the same kernel (the same MFMA
+    sequence on the same fragment values)."""
+    import torch as t
+    A, B = synth.random_operands(M, N, K, seed=7 * M + N + K, lda=lda)
+    Bt = np.full((N, ldbt), 0x7BFF, np.uint16)
+    Bt[:, :K] = B[:K, :N].T
+    Ap = np.concatenate([np.zeros(offs[0], np.uint16), A.ravel()])
+    Btp = np.concatenate([np.full(offs[1], 0x7BFF, np.uint16), Bt.ravel()])
+    dC = full_dev((offs[2] + (M + 2) * ldc,), SENTINEL)
+    dA, dBt = to_dev(Ap), to_dev(Btp)
+    s = t.cuda.current_stream().cuda_stream
+    log("tile_stream bt %dx%dx%d lda=%d ldbt=%d ldc=%d offs=%s" % (M, N, K, lda, ldbt, ldc, offs))
+    st = gr.gemm_relu_f16_bt_forced(M, N, K, dA.data_ptr() + 2 * offs[0], lda, dBt.data_ptr() + 2 * offs[1], ldbt,
+                                    dC.data_ptr() + 2 * offs[2], ldc, s, gr.GR_PATH_TILE_STREAM)
+    t.cuda.synchronize()
+    assert st == gr.GR_OK, gr.gemm_relu_status_string(st)
+    Cflat = from_dev(dC)
+    C = Cflat[offs[2]:offs[2] + M * ldc].reshape(M, ldc)
+    assert np.all(Cflat[:offs[2]] == SENTINEL), "an element before C was written"
+    assert np.all(C[:, N:] == SENTINEL), "a padding column of C was written"
+    assert np.all(Cflat[offs[2] + M * ldc:] == SENTINEL), "a row past M was written"
+    ref = oracle.gemm_relu_full(A, B, M=M, N=N, K=K, lda=lda, ldb=N)
+    log("parity %s" % (assert_parity(C[:, :N], ref, "tile_stream bt %dx%dx%d" % (M, N, K)),))
+    dC2 = full_dev((M * N,), SENTINEL)
+    assert call(M, N, K, to_dev(A), lda, to_dev(np.ascontiguousarray(B[:K, :N])), N, dC2, N,
+                path=gr.GR_PATH_TILE_STREAM) == gr.GR_OK
+    assert np.array_equal(C[:, :N], from_dev(dC2).reshape(M, N)), "transposed and row-major B differ"
+
+
 def test_all_ones_exact_on_tile_stream():
     """All-ones operands give exactly K in every element (every partial sum
     is an integer below 2^24, whatever the order of the waves' sums)."""
