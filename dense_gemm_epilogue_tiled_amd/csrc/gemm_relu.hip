@@ -246,14 +246,13 @@ bool use_large_tiles(int64_t M, int64_t N) {
 // CUs.  Where it is planned (blocks = ceil(M / 64) x ceil(N / 64); us, back
 // to back):
 //  * aligned rows, against the 128 x 128 tile kernel: blocks <= 256 from
-//    K = 512 (1024^3 8.4 against 12.3, 1024^2 x 512 7.3 against 7.8; at
-//    K = 256 6.6 against 5.6), <= 384 from K = 1024 (1024 x 1344 x 1024
-//    12.5 against 12.6; 1152 x 1792 x 1024, 504 blocks: 13.1 against 12.3)
-//    and <= 512 from K = 2048 (1024 x 2048 x 2048 20.3 against 21.2, x
-//    8192 59.5 against 73.7).  Beyond one round the tiles win (1536^2 x
-//    4096, 576 blocks: 49.3 against 38.5).  With a workspace the split-K
-//    tile path comes first where it splits: it is faster still (1024^2 x
-//    8192 29.4, 1024 x 2048 x 8192 48.3).
+//    K = 256 (1024^3 7.4 against 12.3, 1024^2 x 256 5.4 against 5.6; at
+//    K = 128 5.1 against 4.5) and <= 512 from K = 512 (1024 x 1536 x 512
+//    7.4 against 8.0, 1024 x 2048 x 1024 10.4 against 12.4, x 8192 59.5
+//    against 73.7; 1024 x 1536 x 256 6.4 against 5.8).  Beyond one round the
+//    tiles win (1536^2 x 1024, 576 blocks: 14.9 against 12.6).  With a
+//    workspace the split-K tile path comes first where it splits: it is
+//    faster still at long K (1024^2 x 8192 29.4, 1024 x 2048 x 8192 48.3).
 //  * rows of B not 16-byte aligned: the alternatives are the in-place
 //    unaligned 256 x 256 kernel, the packed path (workspace) and the
 //    guarded kernel.  Streaming wins up to one round at any K (1024 x 2048
@@ -287,7 +286,7 @@ int64_t tile_stream_blocks(int64_t M, int64_t N) {
 }
 // Aligned rows: where the streaming path beats the 128 x 128 tile kernel.
 bool tile_stream_beats_tiles(int64_t blocks, int64_t K) {
-    return (blocks <= 256 && K >= 512) || (blocks <= 384 && K >= 1024) || (blocks <= kTileStreamRound && K >= 2048);
+    return (blocks <= 256 && K >= 256) || (blocks <= kTileStreamRound && K >= 512);
 }
 
 bool tile_unaligned_ok(int64_t M, int64_t N, int64_t K, int64_t lda, int64_t ldb) {
@@ -966,13 +965,12 @@ bool tile_stream_bt_ok(int64_t M, int64_t N, int64_t K, uintptr_t A, int64_t lda
 }
 // Where it beats the transposed-B tile kernels.  Its copies of Bt move 64
 // bytes of each row per slot (row-major B: 128), so with two blocks per CU it
-// trails the row-major streaming path (us, back to back): 1024^2 x 1024 8.6
-// against 12.0 for the tiles, 32 x 4096 x 4096 17.1 against 35.6, but 1024 x
-// 2048 x 2048 (512 blocks) 23.7 against 20.7, 1536 x 1216 x 4096 (456) 39.0
-// against 37.2; from K = 8192 it wins there too (1024 x 2048 x 8192: 67.0
-// against 71.8).
+// needs a longer K than the row-major streaming path (us, back to back):
+// 1024^2 x 256 5.3 against 5.6 for the tiles, 32 x 4096 x 4096 17.1 against
+// 35.6; with 384-512 blocks from K = 1024 (1024 x 2048 x 1024 11.2 against
+// 12.4, x 2048 21.1 against 20.8, x 4096 33.5 against 37.8).
 bool tile_stream_bt_beats_tiles(int64_t blocks, int64_t K) {
-    return (blocks <= 256 && K >= 512) || (blocks <= kTileStreamRound && K >= 8192);
+    return (blocks <= 256 && K >= 256) || (blocks <= kTileStreamRound && K >= 1024);
 }
 
 int choose_path_bt(int64_t M, int64_t N, int64_t K, uintptr_t A, int64_t lda, uintptr_t Bt, int64_t ldbt) {

@@ -287,6 +287,7 @@ __global__ __launch_bounds__(64 * W, 1) void gemm_relu_smallm_stream_kernel(
     static_assert(BT || (CH >= 8 && DPS * RPI == stream::SLOT_ROWS), "whole rows per copy instruction");
     static_assert(!BT || DPS == NB / 16, "one copy instruction per 16 rows of Bt");
     static_assert(ROWS * NB * 4 <= R * SLOT, "the cross-wave sum fits a wave's slots");
+    static_assert(NB % 64 == 0, "the sum's column-group XOR (up to 15) stays inside a row");
     static_assert(!AT || (R == 1 && MB == 1), "A gathered into registers: one slot per wave, 16 rows");
     static_assert(MB == 1 || MB == 2 || MB == 4, "1, 2 or 4 blocks of 16 rows");
     __shared__ __attribute__((aligned(1024))) uint8_t lds[W * R * SLOT];
@@ -423,17 +424,20 @@ __global__ __launch_bounds__(64 * W, 1) void gemm_relu_smallm_stream_kernel(
 
     // acc[j] holds C^T: lane l, register r is row m = l%16, column 16j +
     // 4(l/16) + r of the block.  Sum the waves in order through LDS (each
-    // wave's partials in its own slot).
+    // wave's partials in its own slot, [ROWS][NB] fp32).  Column group c (4
+    // floats) of row m sits at group c XOR (m mod 16): the 16 lanes that
+    // store one register group hold 16 rows, which without the XOR all fall
+    // in the same 4 of the 64 banks (rows are NB floats apart); with it they
+    // cover all 64.
     __syncthreads();
-    float* red = reinterpret_cast<float*>(lds);  // wave w at w * R * SLOT: [ROWS][NB]
+    float* red = reinterpret_cast<float*>(lds);  // wave w at w * R * SLOT
+    auto red_at = [](uint32_t m, uint32_t c) { return m * NB + (c ^ ((m & 15u) << 2)); };
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
         for (int j = 0; j < NBLK; ++j)
-#pragma unroll
-            for (int r = 0; r < 4; ++r)
-                red[w * (R * SLOT / 4) + (16 * mb + (lane & 15u)) * NB + 16 * j + 4 * (lane >> 4) + r] =
-                    acc[mb][j][r];
+            *reinterpret_cast<f32x4*>(red + w * (R * SLOT / 4) +
+                                      red_at(16 * mb + (lane & 15u), 16 * j + 4 * (lane >> 4))) = acc[mb][j];
     __syncthreads();
     for (uint32_t o = tid; o < (uint32_t)(ROWS * NB); o += T) {
         const uint32_t m = o / NB, nl = o % NB;
@@ -441,7 +445,7 @@ __global__ __launch_bounds__(64 * W, 1) void gemm_relu_smallm_stream_kernel(
         if ((int64_t)m >= M || n < n_own) continue;
         float v = 0.0f;
 #pragma unroll
-        for (int ww = 0; ww < W; ++ww) v += red[ww * (R * SLOT / 4) + m * NB + nl];
+        for (int ww = 0; ww < W; ++ww) v += red[ww * (R * SLOT / 4) + red_at(m, nl)];
         if constexpr (MODE == stream::WHOLE) C[(int64_t)m * ldc + n] = epi_value<E>(v, n, N, ep);
         else part[(s * M + m) * N + n] = v;
     }

@@ -122,8 +122,8 @@ extern "C" {
                               /* alignment; blocks placed for L2 reuse per XCD          */
                               /* (plain_order).  The planner's choice for few blocks     */
                               /* (ceil(M/64) x ceil(N/64), 512 fill one round): with     */
-                              /* aligned B up to 256 of them from K = 512, 384 from      */
-                              /* K = 1024, 512 from K = 2048; with B's rows misaligned   */
+                              /* aligned B up to 256 of them from K = 256 and 512 from   */
+                              /* K = 512; with B's rows misaligned                       */
                               /* up to 512, and 1024 for K <= 2048 when no workspace     */
                               /* lets the operands be packed (few tiles: the split-K    */
                               /* remedy of the TileLang tutorial's "性能取证", within one */
@@ -358,8 +358,8 @@ int gemm_relu_f16_plan_ws(int64_t M, int64_t N, int64_t K,
  *                     N >= 64: the row-blocked streaming kernel (64 x 64
  *                     blocks, K split between a block's 4 waves) with blocks
  *                     of 16 rows of Bt copied and read like those of A; the
- *                     planner takes it for up to 256 blocks from K = 512
- *                     and up to 512 from K = 8192;
+ *                     planner takes it for up to 256 blocks from K = 256
+ *                     and up to 512 from K = 1024;
  *   GR_PATH_TILE      16-byte rows of A and Bt, K % 32 == 0, pitches of at
  *                     most 2^22 elements: the pipelined kernel with Bt staged
  *                     like A;

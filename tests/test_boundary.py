@@ -152,16 +152,17 @@ def test_plan_for_each_workload():
 
 
 def test_plan_tile_stream_where_128_tiles_are_few():
-    # 64 x 64 blocks on the streaming kernel where 128 x 128 tiles would be
-    # fewer than 128 (and M > 64: fewer rows are the small-M path)
+    # 64 x 64 blocks on the streaming kernel where they are few (one round of
+    # two per CU) and K is long enough (and M > 64: fewer rows are the small-M
+    # path)
     for M, N, K in ((1024, 1024, 1024), (512, 1024, 1024), (1000, 1000, 1024), (65, 4096, 512),
-                    (1024, 1024, 16384)):
+                    (1024, 1024, 16384), (1024, 2048, 1024)):
         st, p = plan(M, N, K)
         assert st == gr.GR_OK and p["path"] == gr.GR_PATH_TILE_STREAM, (M, N, K, p)
         assert (p["block_m"], p["block_n"], p["threads"]) == (64, 64, 256)
         assert p["grid"] == -(-M // 64) * -(-N // 64)
-    # 128 tiles and more: the 128 x 128 (or 256 x 256) tile kernel
-    for M, N, K in ((1024, 2048, 1024), (2048, 2048, 2048), (4096, 4096, 4096)):
+    # more than one round of blocks: the 128 x 128 (or 256 x 256) tile kernel
+    for M, N, K in ((1088, 2048, 1024), (2048, 2048, 2048), (4096, 4096, 4096)):
         assert plan(M, N, K)[1]["path"] == gr.GR_PATH_TILE, (M, N, K)
     # up to 64 rows: the small-M path
     assert plan(64, 1024, 1024)[1]["path"] == gr.GR_PATH_SMALL_M
@@ -228,6 +229,8 @@ def test_plan_partial_tiles_take_the_pipelined_kernel():
     st, p = plan(65, 512, 512)
     assert p["path"] == gr.GR_PATH_TILE_STREAM and (p["block_m"], p["grid"]) == (64, 16)
     st, p = plan(65, 16384, 512)
+    assert p["path"] == gr.GR_PATH_TILE_STREAM and (p["block_m"], p["grid"]) == (64, 512)
+    st, p = plan(65, 16384, 480)
     assert p["path"] == gr.GR_PATH_TILE and (p["block_m"], p["grid"]) == (128, 128)
     assert plan(512, 512, 48)[1]["path"] == gr.GR_PATH_TILE_EDGE
     assert plan(512, 500, 512)[1]["path"] == gr.GR_PATH_TILE_STREAM
@@ -239,12 +242,11 @@ def test_plan_partial_tiles_take_the_pipelined_kernel():
 
 
 @pytest.mark.parametrize("M,N,K,stream", [
-    # aligned rows: up to 256 blocks of 64 x 64 from K = 512, 384 from
-    # K = 1024, 512 (one round: two per CU) from K = 2048
-    (1024, 1024, 256, False), (1024, 1024, 480, False), (1024, 1024, 512, True), (65, 64, 512, True),
-    (1024, 1536, 512, False), (1024, 1536, 1024, True), (1024, 1600, 1024, False),
-    (1024, 2048, 1024, False), (1024, 2048, 2048, True), (1088, 1856, 8192, True),
-    (1088, 2048, 8192, False), (1536, 1536, 4096, False),
+    # aligned rows: up to 256 blocks of 64 x 64 from K = 256, 512 (one round:
+    # two per CU) from K = 512
+    (1024, 1024, 224, False), (1024, 1024, 256, True), (65, 64, 256, True), (512, 1024, 128, False),
+    (1024, 1536, 256, False), (1024, 1536, 480, False), (1024, 1536, 512, True), (1024, 2048, 512, True),
+    (1088, 1856, 8192, True), (1088, 2048, 8192, False), (1536, 1536, 4096, False),
 ])
 def test_tile_stream_thresholds(M, N, K, stream):
     st, p = plan(M, N, K)
@@ -461,12 +463,12 @@ def test_plan_tile_size_choice():
     # fewer than half a wave of 256 x 256 tiles (or M < 256): 128 x 128 tiles
     for (M, N), (bm, grid) in {(2048, 2048): (128, 256), (4096, 4096): (256, 256), (2816, 2816): (128, 484),
                                (4099, 3071): (256, 204), (2048, 4096): (128, 512),
-                               (2304, 4096): (256, 144), (1024, 2048): (128, 128)}.items():
+                               (2304, 4096): (256, 144), (1088, 2048): (128, 144)}.items():
         st, p = plan(M, N, 512, ldb=rup(N, 8), ldc=rup(N, 8))
         assert st == gr.GR_OK and p["path"] == gr.GR_PATH_TILE, (M, N, p)
         assert (p["block_m"], p["block_n"], p["grid"]) == (bm, bm, grid), (M, N, p)
-    # fewer than 128 of those: 64 x 64 blocks on the streaming kernel
-    for (M, N), grid in {(1024, 1024): 256, (128, 4096): 128, (200, 304): 20}.items():
+    # one round of 64 x 64 blocks or less (K >= 512): the streaming kernel
+    for (M, N), grid in {(1024, 1024): 256, (128, 4096): 128, (200, 304): 20, (1024, 2048): 512}.items():
         st, p = plan(M, N, 512, ldb=rup(N, 8), ldc=rup(N, 8))
         assert st == gr.GR_OK and p["path"] == gr.GR_PATH_TILE_STREAM, (M, N, p)
         assert (p["block_m"], p["block_n"], p["grid"]) == (64, 64, grid), (M, N, p)
@@ -526,8 +528,7 @@ def test_planner_invariants_on_random_problems():
             assert M > 64 and K > 0 and K % 32 == 0 and a % 16 == 0 and lda % 8 == 0 and N >= 64, key
             blocks = -(-M // 64) * -(-N // 64)
             if aligned:  # few blocks, K long enough to beat the 128 x 128 tiles
-                assert (blocks <= 256 and K >= 512) or (blocks <= 384 and K >= 1024) or \
-                    (blocks <= 512 and K >= 2048), key
+                assert (blocks <= 256 and K >= 256) or (blocks <= 512 and K >= 512), key
             else:  # B misaligned: one round, or two for K <= 2048
                 assert blocks <= 512 or (blocks <= 1024 and K <= 2048), key
                 assert size == 0 or blocks > 512, key  # within one round no workspace is asked for
@@ -580,17 +581,17 @@ def test_transposed_b_planner_and_checks():
     st, p = plan_bt(4096, 4096, 4096)
     assert p["path"] == gr.GR_PATH_TILE and p["block_m"] == 256 and p["grid"] == 256
     # few blocks of 64 x 64 with K long enough: the streaming kernel with Bt
-    # copied like A (up to 256 blocks from K = 512, 512 from K = 8192); M > 16
+    # copied like A (up to 256 blocks from K = 256, 512 from K = 1024); M > 16
     st, p = plan_bt(1024, 1024, 1024)
     assert p["path"] == gr.GR_PATH_TILE_STREAM and (p["block_m"], p["block_n"], p["grid"]) == (64, 64, 256)
     assert p["plain_order"] == 1
     st, p = plan_bt(32, 4000, 4096)
     assert p["path"] == gr.GR_PATH_TILE_STREAM and p["grid"] == 63 and p["plain_order"] == 0
-    st, p = plan_bt(1024, 1024, 256)
+    st, p = plan_bt(1024, 1024, 128)
     assert p["path"] == gr.GR_PATH_TILE and p["block_m"] == 128
-    assert plan_bt(1024, 1024, 512)[1]["path"] == gr.GR_PATH_TILE_STREAM
-    assert plan_bt(1024, 2048, 4096)[1]["path"] == gr.GR_PATH_TILE  # 512 blocks from K = 8192 only
-    assert plan_bt(1024, 2048, 8192)[1]["path"] == gr.GR_PATH_TILE_STREAM
+    assert plan_bt(1024, 1024, 256)[1]["path"] == gr.GR_PATH_TILE_STREAM
+    assert plan_bt(1024, 2048, 512)[1]["path"] == gr.GR_PATH_TILE  # 512 blocks from K = 1024 only
+    assert plan_bt(1024, 2048, 1024)[1]["path"] == gr.GR_PATH_TILE_STREAM
     assert plan_bt(4096, 4096, 4100)[1]["path"] == gr.GR_PATH_TILE_EDGE          # K % 32 != 0
     assert plan_bt(4096, 4096, 4096, ldbt=4100)[1]["path"] == gr.GR_PATH_TILE_EDGE  # Bt rows not 16-B
     assert plan_bt(8, 4096, 4096, b=BASE_B + 8)[1]["path"] == gr.GR_PATH_TILE_EDGE  # Bt rows not 16-B

@@ -244,7 +244,7 @@ def test_tile_and_edge_paths_bitwise_equal(M, N, K):
 @pytest.mark.parametrize("K", [32, 64, 96, 128, 160, 192, 224, 256, 288, 320, 384, 448, 512, 1056, 1088])
 def test_tile_pipeline_every_strip_count(M, N, K):
     """Whole tiles through the pipelined kernels (128 x 128 tiles at 512 x 256,
-    forced: the planner gives that shape to the streaming kernel from K = 512
+    forced: the planner gives that shape to the streaming kernel from K = 256
     on; 256 x 256
     tiles at 2304 x 4096: the 32- and 64-deep variants), for every K-loop
     length up to the steady state plus odd and even tails, bitwise against
@@ -253,7 +253,7 @@ def test_tile_pipeline_every_strip_count(M, N, K):
     and columns, the small one in full."""
     st, plan = gr.gemm_relu_f16_plan(M, N, K, 0x100000, K, 0x200000000000, N, 0x400000000000, N)
     if M == 512:
-        assert plan["path"] == (gr.GR_PATH_TILE_STREAM if K >= 512 else gr.GR_PATH_TILE), plan
+        assert plan["path"] == (gr.GR_PATH_TILE_STREAM if K >= 256 else gr.GR_PATH_TILE), plan
     else:
         assert plan["path"] == gr.GR_PATH_TILE and plan["block_m"] == 256, plan
     A, B = synth.random_operands(M, N, K, seed=K)
@@ -700,7 +700,7 @@ BT_CASES = [
     (3, 64, 512, 520, 512, 65, gr.GR_PATH_SMALL_M),            # one workgroup, two chunks, odd ldc
     (12, 70, 512, 512, 520, 71, gr.GR_PATH_SMALL_M),           # 16 rows of A per slot; 3 waves past N
     (8, 130, 768, 776, 768, 130, gr.GR_PATH_SMALL_M),          # 8 rows of A per slot, 3 chunks, N % 64 = 2
-    (512, 768, 256, 256, 256, 768, gr.GR_PATH_TILE),           # 128 x 128 tiles
+    (512, 768, 224, 224, 224, 768, gr.GR_PATH_TILE),           # 128 x 128 tiles
     (4096, 2304, 512, 512, 520, 2304, gr.GR_PATH_TILE),        # 256 x 256 tiles, padded Bt
     (300, 250, 96, 104, 96, 251, gr.GR_PATH_TILE),             # partial tiles, rows of Bt clamped
     (2400, 4000, 96, 96, 96, 4001, gr.GR_PATH_TILE),           # large partial tiles
@@ -735,7 +735,7 @@ def test_transposed_b_parity(M, N, K, lda, ldbt, ldc, path):
         assert np.array_equal(C1, C2)
 
 
-@pytest.mark.parametrize("M,N,K", [(512, 768, 256), (4096, 2304, 256), (300, 250, 96)])
+@pytest.mark.parametrize("M,N,K", [(512, 768, 224), (4096, 2304, 256), (300, 250, 96)])
 def test_transposed_b_matches_plain_layout_bitwise(M, N, K):
     """The same product through B (K x N) and through Bt (N x K) gives the same
     bits: both layouts feed the same MFMA sequence on the tile kernels (the

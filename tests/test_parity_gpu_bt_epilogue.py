@@ -27,7 +27,7 @@ CASES = [
     (13, 1000, 1000, 1000, 1000, 1001, (gr.GR_PATH_SMALL_M, None), "small-M from memory, partial"),
     (2600, 3000, 128, 128, 136, 3001, (gr.GR_PATH_TILE, 256), "256 tiles, 64-deep A strips, partial"),
     (4096, 3072, 96, 96, 96, 3072, (gr.GR_PATH_TILE, 256), "256 tiles, 32-deep strips"),
-    (300, 270, 256, 264, 256, 273, (gr.GR_PATH_TILE, 128), "128 tiles, partial"),
+    (300, 270, 224, 232, 224, 273, (gr.GR_PATH_TILE, 128), "128 tiles, partial"),
     (300, 270, 100, 101, 103, 273, (gr.GR_PATH_TILE_EDGE, None), "guarded, odd pitches"),
     (300, 1000, 1024, 1032, 1032, 1001, (gr.GR_PATH_TILE_STREAM, 64), "row-blocked streaming, Bt copied like A"),
 ]
