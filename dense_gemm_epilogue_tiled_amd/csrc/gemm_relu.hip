@@ -253,14 +253,16 @@ bool use_large_tiles(int64_t M, int64_t N) {
 //    tiles win (1536^2 x 1024, 576 blocks: 14.9 against 12.6).  With a
 //    workspace the split-K tile path comes first where it splits: it is
 //    faster still at long K (1024^2 x 8192 29.4, 1024 x 2048 x 8192 48.3).
-//  * rows of B not 16-byte aligned: the alternatives are the in-place
+//  * rows of A or B not 16-byte aligned: the alternatives are the in-place
 //    unaligned 256 x 256 kernel, the packed path (workspace) and the
-//    guarded kernel.  Streaming wins up to one round at any K (1024 x 2048
-//    x 4096: 43.5 against 83.1 unaligned, 48.5 packed, 176 guarded) and, with
-//    no workspace, up to two rounds for K <= 2048 (2048^2 x 2048: 45.8
-//    against 48.8 unaligned, 32.1 packed; x 4096: 82.0 against 83.4).
-// Needs what the streaming kernel needs: K % 32 == 0, 16-byte rows of A,
-// N >= 64; B of any alignment.
+//    guarded kernel.  Streaming wins up to one round (A misaligned, 1024^3:
+//    7.9 against 31.5 unaligned, 16.2 packed, 75.5 guarded; 1024 x 2048 x
+//    4096: 39.7 against 83.8, 45.6, 417) and, with no workspace, up to two
+//    rounds (2048^2 x 4096: 74.1 against 84.1 unaligned; with a workspace
+//    the packed path, 49.4).
+// Needs K % 32 == 0 (whole slots) and N >= 64; its direct-to-LDS copies read
+// any 2-byte aligned address (as the unaligned tile kernel's do), so rows of
+// A and B of any alignment.
 constexpr int64_t kTileStreamRows = 64;  // 4 blocks of 16 rows per workgroup
 constexpr int64_t kTileStreamRound = 512;  // resident blocks: 2 per CU x 256 CUs
 // Workgroup order of the row-blocked grid.  All blocks of a launch that fits
@@ -278,8 +280,8 @@ constexpr int64_t kTileStreamRound = 512;  // resident blocks: 2 per CU x 256 CU
 // 67.5).
 constexpr int32_t kTileStreamGroupM = 4;
 bool tile_stream_plain_order(int64_t N) { return ((N + kStreamNB - 1) / kStreamNB) % 4 == 0; }
-bool tile_stream_ok(int64_t M, int64_t N, int64_t K, uintptr_t A, int64_t lda, int64_t ldb) {
-    return smallm_stream_ok(M, N, K, A, lda, ldb, kStreamNB, kMaxDim);
+bool tile_stream_ok(int64_t M, int64_t N, int64_t K, int64_t lda, int64_t ldb) {
+    return M >= 1 && K > 0 && K % 32 == 0 && N >= kStreamNB && lda <= kStreamMaxLd && ldb <= kStreamMaxLd;
 }
 int64_t tile_stream_blocks(int64_t M, int64_t N) {
     return ((M + kTileStreamRows - 1) / kTileStreamRows) * ((N + kStreamNB - 1) / kStreamNB);
@@ -491,7 +493,7 @@ int choose_path(int64_t M, int64_t N, int64_t K, uintptr_t A, int64_t lda, uintp
         (smallm_rows_ok(M, N, K, A, lda, B, ldb) || smallm_stream_ok(M, N, K, A, lda, ldb, kStreamNB, kSmallMMaxRows)) &&
         (N + gr::smallm::NB - 1) / gr::smallm::NB <= 256)
         return GR_PATH_SMALL_M;
-    const bool stream = M > kSmallMMaxRows && tile_stream_ok(M, N, K, A, lda, ldb);
+    const bool stream = M > kSmallMMaxRows && tile_stream_ok(M, N, K, lda, ldb);
     const int64_t blocks = stream ? tile_stream_blocks(M, N) : 0;
     if (stream && (fast ? tile_stream_beats_tiles(blocks, K) : blocks <= kTileStreamRound))
         return GR_PATH_TILE_STREAM;
@@ -500,7 +502,7 @@ int choose_path(int64_t M, int64_t N, int64_t K, uintptr_t A, int64_t lda, uintp
     if (ws_bytes > 0 && pack_layout(M, N, K, A, lda, B, ldb, pk) && pk->bytes <= ws_bytes &&
         (double)M * (double)N * (double)K >= (double)kPackMinMacs)
         return GR_PATH_TILE_PACKED;
-    if (stream && blocks <= 2 * kTileStreamRound && K <= 2048) return GR_PATH_TILE_STREAM;
+    if (stream && blocks <= 2 * kTileStreamRound) return GR_PATH_TILE_STREAM;
     // Misaligned rows or a ragged K without a workspace: the in-place
     // unaligned kernel wherever it applies (1024 x 2048 x 4096 with A's rows
     // misaligned: 83.6 us against 417 for the guarded kernel; 512 x 1024 x
@@ -822,7 +824,7 @@ int plan_call(int64_t M, int64_t N, int64_t K, uintptr_t a, int64_t lda, uintptr
         } else if (forced == GR_PATH_SMALL_M_SPLIT) {
             if (!smallm_split_layout(M, N, K, a, lda, b, ldb, sp) || sp->bytes > ws_bytes) return GR_ERR_INVALID_PATH;
         } else if (forced == GR_PATH_TILE_STREAM) {
-            if (!tile_stream_ok(M, N, K, a, lda, ldb)) return GR_ERR_INVALID_PATH;
+            if (!tile_stream_ok(M, N, K, lda, ldb)) return GR_ERR_INVALID_PATH;
         } else if (forced != GR_PATH_TILE_EDGE) {
             return GR_ERR_INVALID_PATH;
         }
@@ -956,12 +958,11 @@ bool tile_bt_ok(int64_t M, int64_t N, int64_t K, uintptr_t A, int64_t lda, uintp
 }
 
 // The row-blocked streaming kernel with B given transposed (its BT mode):
-// blocks of 16 rows of Bt are copied and read like those of A, so Bt needs
-// what A needs (16-byte rows, pitch within the 32-bit copy offsets).  M > 16:
+// blocks of 16 rows of Bt are copied and read like those of A, with the same
+// conditions (any alignment, pitch within the 32-bit copy offsets).  M > 16:
 // fewer rows take the transposed-B small-M kernels.
-bool tile_stream_bt_ok(int64_t M, int64_t N, int64_t K, uintptr_t A, int64_t lda, uintptr_t Bt, int64_t ldbt) {
-    return M > kSmallMThreshold && smallm_stream_ok(M, N, K, A, lda, ldbt, kStreamNB, kMaxDim) && Bt % 16 == 0 &&
-           ldbt % 8 == 0;
+bool tile_stream_bt_ok(int64_t M, int64_t N, int64_t K, int64_t lda, int64_t ldbt) {
+    return M > kSmallMThreshold && tile_stream_ok(M, N, K, lda, ldbt);
 }
 // Where it beats the transposed-B tile kernels.  Its copies of Bt move 64
 // bytes of each row per slot (row-major B: 128), so with two blocks per CU it
@@ -976,7 +977,11 @@ bool tile_stream_bt_beats_tiles(int64_t blocks, int64_t K) {
 int choose_path_bt(int64_t M, int64_t N, int64_t K, uintptr_t A, int64_t lda, uintptr_t Bt, int64_t ldbt) {
     if (M == 0 || N == 0) return GR_PATH_NONE;
     if (smallm_bt_ok(M, K, A, lda, Bt, ldbt)) return GR_PATH_SMALL_M;
-    if (tile_stream_bt_ok(M, N, K, A, lda, Bt, ldbt) && tile_stream_bt_beats_tiles(tile_stream_blocks(M, N), K))
+    // Rows of A or Bt not 16-byte aligned: the alternative is the guarded
+    // kernel, which streaming beats at any size (1024^3 8.2 against 72.9 us,
+    // 4096^2 x 1024, 4096 blocks: 72.9 against 108.7).
+    if (tile_stream_bt_ok(M, N, K, lda, ldbt) &&
+        (!tile_bt_ok(M, N, K, A, lda, Bt, ldbt) || tile_stream_bt_beats_tiles(tile_stream_blocks(M, N), K)))
         return GR_PATH_TILE_STREAM;
     if (tile_bt_ok(M, N, K, A, lda, Bt, ldbt)) return GR_PATH_TILE;
     return GR_PATH_TILE_EDGE;
@@ -1116,7 +1121,7 @@ int plan_call_bt(int64_t M, int64_t N, int64_t K, uintptr_t a, int64_t lda, uint
         } else if (forced == GR_PATH_SMALL_M) {
             if (!smallm_bt_ok(M, K, a, lda, bt, ldbt)) return GR_ERR_INVALID_PATH;
         } else if (forced == GR_PATH_TILE_STREAM) {
-            if (!tile_stream_bt_ok(M, N, K, a, lda, bt, ldbt)) return GR_ERR_INVALID_PATH;
+            if (!tile_stream_bt_ok(M, N, K, lda, ldbt)) return GR_ERR_INVALID_PATH;
         } else if (forced != GR_PATH_TILE_EDGE) {
             return GR_ERR_INVALID_PATH;
         }
@@ -1778,7 +1783,7 @@ int gemm_relu_f16_workspace_size(int64_t M, int64_t N, int64_t K, const uint16_t
         if (!use_large_tiles(M, N) && tile_split_layout(M, N, K, false, &ts)) *bytes = ts.bytes;
     } else if (tile_unaligned_ok(M, N, K, lda, ldb) && use_large_tiles(M, N)) {
         // the pipelined kernel runs in place on these rows: no workspace
-    } else if (M > kSmallMMaxRows && tile_stream_ok(M, N, K, a, lda, ldb) &&
+    } else if (M > kSmallMMaxRows && tile_stream_ok(M, N, K, lda, ldb) &&
                tile_stream_blocks(M, N) <= kTileStreamRound) {
         // one round of the streaming kernel, planned ahead of the packed copy
     } else if (pack_layout(M, N, K, a, lda, b, ldb, &pk)) {

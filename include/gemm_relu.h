@@ -118,14 +118,14 @@ extern "C" {
                               /* the block's 4 waves split K between them (rings of      */
                               /* direct-to-LDS copies of their own, no barrier in the    */
                               /* loop) and add their partial sums in order at the end;   */
-                              /* K % 32 == 0, 16-byte rows of A, N >= 64, B of any       */
-                              /* alignment; blocks placed for L2 reuse per XCD          */
+                              /* K % 32 == 0, N >= 64, rows of A and B of any alignment; */
+                              /* blocks placed for L2 reuse per XCD                     */
                               /* (plain_order).  The planner's choice for few blocks     */
                               /* (ceil(M/64) x ceil(N/64), 512 fill one round): with     */
-                              /* aligned B up to 256 of them from K = 256 and 512 from   */
-                              /* K = 512; with B's rows misaligned                       */
-                              /* up to 512, and 1024 for K <= 2048 when no workspace     */
-                              /* lets the operands be packed (few tiles: the split-K    */
+                              /* aligned rows up to 256 of them from K = 256 and 512     */
+                              /* from K = 512; with rows of A or B misaligned up to      */
+                              /* 512, and 1024 when no workspace lets the operands be    */
+                              /* packed (few tiles: the split-K                          */
                               /* remedy of the TileLang tutorial's "性能取证", within one */
                               /* workgroup); no workspace                                 */
 
@@ -354,12 +354,13 @@ int gemm_relu_f16_plan_ws(int64_t M, int64_t N, int64_t K,
  *   GR_PATH_SMALL_M   M <= 16, 16-byte rows of A and Bt: each wave streams 16
  *                     rows of Bt, whose 16-byte pieces are MFMA operands as
  *                     they stand;
- *   GR_PATH_TILE_STREAM  M > 16, 16-byte rows of A and Bt, K % 32 == 0,
- *                     N >= 64: the row-blocked streaming kernel (64 x 64
- *                     blocks, K split between a block's 4 waves) with blocks
- *                     of 16 rows of Bt copied and read like those of A; the
- *                     planner takes it for up to 256 blocks from K = 256
- *                     and up to 512 from K = 1024;
+ *   GR_PATH_TILE_STREAM  M > 16, K % 32 == 0, N >= 64, rows of A and Bt
+ *                     of any alignment: the row-blocked streaming kernel (64 x
+ *                     64 blocks, K split between a block's 4 waves) with
+ *                     blocks of 16 rows of Bt copied and read like those of
+ *                     A; the planner takes it for up to 256 blocks from K =
+ *                     256 and up to 512 from K = 1024, and at any size when
+ *                     rows of A or Bt are not 16-byte aligned;
  *   GR_PATH_TILE      16-byte rows of A and Bt, K % 32 == 0, pitches of at
  *                     most 2^22 elements: the pipelined kernel with Bt staged
  *                     like A;

@@ -166,14 +166,13 @@ def test_plan_tile_stream_where_128_tiles_are_few():
         assert plan(M, N, K)[1]["path"] == gr.GR_PATH_TILE, (M, N, K)
     # up to 64 rows: the small-M path
     assert plan(64, 1024, 1024)[1]["path"] == gr.GR_PATH_SMALL_M
-    # what the streaming kernel cannot take goes elsewhere: K % 32 != 0,
-    # rows of A not 16-byte aligned, N < 64
+    # what the streaming kernel cannot take goes elsewhere: K % 32 != 0, N < 64
     assert plan(1024, 1024, 1000)[1]["path"] != gr.GR_PATH_TILE_STREAM
-    assert plan(1024, 1024, 1024, lda=1028)[1]["path"] != gr.GR_PATH_TILE_STREAM
-    assert plan(1024, 1024, 1024, a=BASE_A + 2)[1]["path"] != gr.GR_PATH_TILE_STREAM
     assert plan(1024, 48, 1024)[1]["path"] != gr.GR_PATH_TILE_STREAM
-    # B of any alignment stays on it
+    # rows of A or B of any alignment stay on it
     assert plan(1024, 1024, 1024, ldb=1027)[1]["path"] == gr.GR_PATH_TILE_STREAM
+    assert plan(1024, 1024, 1024, lda=1028)[1]["path"] == gr.GR_PATH_TILE_STREAM
+    assert plan(1024, 1024, 1024, a=BASE_A + 2)[1]["path"] == gr.GR_PATH_TILE_STREAM
 
 
 def test_tile_stream_forced_checks():
@@ -184,12 +183,13 @@ def test_tile_stream_forced_checks():
     def forced(M, N, K, lda, ldb, ldc, a=base[0]):
         return gr.gemm_relu_f16_forced(M, N, K, a, lda, base[1], ldb, base[2], ldc, None, gr.GR_PATH_TILE_STREAM)
     assert forced(1024, 1024, 1000, 1000, 1024, 1024) == gr.GR_ERR_INVALID_PATH   # K % 32 != 0
-    assert forced(1024, 1024, 1024, 1028, 1024, 1024) == gr.GR_ERR_INVALID_PATH   # rows of A not 16-byte
-    assert forced(1024, 1024, 1024, 1024, 1024, 1024, a=base[0] + 8) == gr.GR_ERR_INVALID_PATH
     assert forced(1024, 63, 1024, 1024, 63, 63) == gr.GR_ERR_INVALID_PATH         # N < 64
     assert forced(4, 64, 32, (1 << 25) + 8, 64, 64) == gr.GR_ERR_INVALID_PATH      # 32-bit copy offsets
     # accepted shapes fail only at the device check here (no GPU)
     assert forced(1024, 1024, 1024, 1024, 1027, 1024) not in (gr.GR_ERR_INVALID_PATH, gr.GR_OK)
+    # rows of A of any alignment too (the copies read any 2-byte address)
+    assert forced(1024, 1024, 1024, 1028, 1024, 1024) not in (gr.GR_ERR_INVALID_PATH, gr.GR_OK)
+    assert forced(1024, 1024, 1024, 1024, 1024, 1024, a=base[0] + 2) not in (gr.GR_ERR_INVALID_PATH, gr.GR_OK)
     assert forced(4096, 4096, 4096, 4096, 4096, 4096) not in (gr.GR_ERR_INVALID_PATH, gr.GR_OK)
 
 
@@ -200,11 +200,13 @@ def test_plan_ragged_vector_widths():
     st, p = plan(4099, 3071, 2050)
     assert st == gr.GR_OK and p["path"] == gr.GR_PATH_TILE_UNALIGNED
     assert (p["vec_a"], p["vec_b"], p["vec_c"]) == (2, 1, 8)
-    # misaligned base pointer: the unaligned kernel copies in place; where it
-    # does not apply (M < 256) the guarded kernel drops to narrower loads
-    st, p = plan(512, 512, 512, a=BASE_A + 2)
+    # misaligned base pointer: the streaming kernel (K % 32 == 0, few blocks),
+    # else the unaligned kernel in place; where neither applies (K % 32 != 0,
+    # M < 256) the guarded kernel drops to narrower loads
+    assert plan(512, 512, 512, a=BASE_A + 2)[1]["path"] == gr.GR_PATH_TILE_STREAM
+    st, p = plan(512, 512, 500, a=BASE_A + 2)
     assert p["path"] == gr.GR_PATH_TILE_UNALIGNED and p["vec_a"] == 1
-    st, p = plan(200, 512, 512, a=BASE_A + 2)
+    st, p = plan(200, 512, 500, a=BASE_A + 2)
     assert p["path"] == gr.GR_PATH_TILE_EDGE and p["vec_a"] == 1
 
 
@@ -216,10 +218,10 @@ def test_plan_partial_tiles_take_the_pipelined_kernel():
     assert plan(256, 1, 32, ldb=8)[1]["path"] == gr.GR_PATH_TILE
     # up to 64 rows of A and at most 256 column strips: the small-M stream
     # (2 or 4 row blocks); more rows: 64 x 64 blocks on the streaming kernel
-    # where they beat the pipelined kernel (few blocks, K long enough; B of
-    # any alignment), else the pipelined kernel (rows past M clamped); K % 32
-    # != 0 or rows of A not 16-byte aligned: the unaligned kernel (M, N >=
-    # 256, K > 128), else the guarded kernel
+    # where they beat the pipelined kernel (few blocks, K long enough; rows
+    # of any alignment), else the pipelined kernel (rows past M clamped); K %
+    # 32 != 0: the unaligned kernel (M, N >= 256, K > 128), else the guarded
+    # kernel
     st, p = plan(17, 512, 512)
     assert p["path"] == gr.GR_PATH_SMALL_M and (p["block_m"], p["grid"]) == (32, 8)
     st, p = plan(64, 16384, 512)
@@ -235,10 +237,11 @@ def test_plan_partial_tiles_take_the_pipelined_kernel():
     assert plan(512, 512, 48)[1]["path"] == gr.GR_PATH_TILE_EDGE
     assert plan(512, 500, 512)[1]["path"] == gr.GR_PATH_TILE_STREAM
     assert plan(512, 512, 512, b=BASE_B + 8)[1]["path"] == gr.GR_PATH_TILE_STREAM
-    assert plan(512, 500, 512, lda=516)[1]["path"] == gr.GR_PATH_TILE_UNALIGNED
-    assert plan(512, 512, 512, a=BASE_A + 8)[1]["path"] == gr.GR_PATH_TILE_UNALIGNED
-    assert plan(255, 512, 512, a=BASE_A + 8)[1]["path"] == gr.GR_PATH_TILE_EDGE
-    assert plan(512, 512, 128, lda=130)[1]["path"] == gr.GR_PATH_TILE_EDGE
+    assert plan(512, 500, 512, lda=516)[1]["path"] == gr.GR_PATH_TILE_STREAM
+    assert plan(512, 512, 512, a=BASE_A + 8)[1]["path"] == gr.GR_PATH_TILE_STREAM
+    assert plan(512, 500, 500, lda=516)[1]["path"] == gr.GR_PATH_TILE_UNALIGNED
+    assert plan(255, 512, 500, a=BASE_A + 8)[1]["path"] == gr.GR_PATH_TILE_EDGE
+    assert plan(512, 512, 100, lda=130)[1]["path"] == gr.GR_PATH_TILE_EDGE
 
 
 @pytest.mark.parametrize("M,N,K,stream", [
@@ -256,15 +259,14 @@ def test_tile_stream_thresholds(M, N, K, stream):
 
 @pytest.mark.parametrize("M,N,K,ws,path,asks", [
     # B's rows misaligned (odd pitch): one round at any K, with or without a
-    # workspace (none is asked for); up to two rounds for K <= 2048 without
-    # one (with one: the packed copy); beyond that the unaligned kernel in
-    # place
+    # workspace (none is asked for); up to two rounds without one (with one:
+    # the packed copy); beyond that the unaligned kernel in place
     (1024, 2048, 4096, False, gr.GR_PATH_TILE_STREAM, False),
     (1024, 2048, 4096, True, gr.GR_PATH_TILE_STREAM, False),
     (1024, 1024, 256, False, gr.GR_PATH_TILE_STREAM, False),
     (2048, 2048, 2048, False, gr.GR_PATH_TILE_STREAM, True),
     (2048, 2048, 2048, True, gr.GR_PATH_TILE_PACKED, True),
-    (2048, 2048, 2080, False, gr.GR_PATH_TILE_UNALIGNED, True),
+    (2048, 2048, 4096, False, gr.GR_PATH_TILE_STREAM, True),
     (2048, 2112, 1024, False, gr.GR_PATH_TILE_UNALIGNED, True),
 ])
 def test_tile_stream_with_misaligned_b(M, N, K, ws, path, asks):
@@ -525,12 +527,12 @@ def test_planner_invariants_on_random_problems():
             assert 1 <= M <= 64 and K > 0 and p["grid"] == -(-N // 64), key
             assert M <= 16 or -(-N // 64) <= 256, key  # wider C with more rows: the tile kernel
         elif p["path"] == gr.GR_PATH_TILE_STREAM:
-            assert M > 64 and K > 0 and K % 32 == 0 and a % 16 == 0 and lda % 8 == 0 and N >= 64, key
+            assert M > 64 and K > 0 and K % 32 == 0 and N >= 64, key
             blocks = -(-M // 64) * -(-N // 64)
             if aligned:  # few blocks, K long enough to beat the 128 x 128 tiles
                 assert (blocks <= 256 and K >= 256) or (blocks <= 512 and K >= 512), key
-            else:  # B misaligned: one round, or two for K <= 2048
-                assert blocks <= 512 or (blocks <= 1024 and K <= 2048), key
+            else:  # rows misaligned: one round, or two without a workspace
+                assert blocks <= 1024, key
                 assert size == 0 or blocks > 512, key  # within one round no workspace is asked for
             assert p["block_m"] == 64 and p["grid"] == blocks, key
             assert p["plain_order"] == (1 if -(-N // 64) % 4 == 0 else 0), key
@@ -540,10 +542,13 @@ def test_planner_invariants_on_random_problems():
             tiles = -(-M // 256) * -(-N // 256)
             assert p["grid"] == tiles and p["block_m"] == 256, key
             assert tiles <= 128 or size == 0, key  # more than 128 tiles: never packed
+            # the streaming kernel takes two rounds or less of what it can take
+            assert tiles > 128 or not (K % 32 == 0 and N >= 64 and -(-M // 64) * -(-N // 64) <= 1024), key
         else:
             assert p["path"] == gr.GR_PATH_TILE_EDGE, key
             assert not (aligned and K % 32 == 0 and K > 0), key
             assert not (M >= 256 and N >= 256 and K > 128), key  # else the unaligned kernel
+            assert not (M > 64 and K > 0 and K % 32 == 0 and N >= 64 and -(-M // 64) * -(-N // 64) <= 1024), key
         # the workspace plan differs from the plain one only where a workspace was asked for
         if size == 0:
             assert pw["path"] == p["path"] and pw["workspace"] == 0, key
@@ -593,7 +598,9 @@ def test_transposed_b_planner_and_checks():
     assert plan_bt(1024, 2048, 512)[1]["path"] == gr.GR_PATH_TILE  # 512 blocks from K = 1024 only
     assert plan_bt(1024, 2048, 1024)[1]["path"] == gr.GR_PATH_TILE_STREAM
     assert plan_bt(4096, 4096, 4100)[1]["path"] == gr.GR_PATH_TILE_EDGE          # K % 32 != 0
-    assert plan_bt(4096, 4096, 4096, ldbt=4100)[1]["path"] == gr.GR_PATH_TILE_EDGE  # Bt rows not 16-B
+    assert plan_bt(4096, 4096, 4096, ldbt=4100)[1]["path"] == gr.GR_PATH_TILE_STREAM  # Bt rows not 16-B
+    assert plan_bt(1024, 1024, 1024, ldbt=1025)[1]["path"] == gr.GR_PATH_TILE_STREAM
+    assert plan_bt(4096, 4096, 4100, ldbt=4101)[1]["path"] == gr.GR_PATH_TILE_EDGE  # K % 32 != 0
     assert plan_bt(8, 4096, 4096, b=BASE_B + 8)[1]["path"] == gr.GR_PATH_TILE_EDGE  # Bt rows not 16-B
     assert plan_bt(0, 4096, 4096)[1]["path"] == gr.GR_PATH_NONE
     # forced paths are checked
@@ -603,9 +610,11 @@ def test_transposed_b_planner_and_checks():
                                       gr.GR_PATH_SMALL_M) == gr.GR_ERR_INVALID_PATH
     assert gr.gemm_relu_f16_bt_forced(8, 256, 64, BASE_A, 64, BASE_B, 64, BASE_C, 256, None,
                                       gr.GR_PATH_TILE_PACKED) == gr.GR_ERR_INVALID_PATH
-    for M, K, ldbt, b in ((16, 64, 64, BASE_B), (300, 48, 48, BASE_B), (300, 64, 68, BASE_B), (300, 64, 64, BASE_B + 8)):
-        assert gr.gemm_relu_f16_bt_forced(M, 256, K, BASE_A, K, b, ldbt, BASE_C, 256, None,
-                                          gr.GR_PATH_TILE_STREAM) == gr.GR_ERR_INVALID_PATH, (M, K, ldbt)
+    for M, N, K in ((16, 256, 64), (300, 256, 48), (300, 48, 64)):  # M <= 16, K % 32 != 0, N < 64
+        assert gr.gemm_relu_f16_bt_forced(M, N, K, BASE_A, K, BASE_B, K, BASE_C, N, None,
+                                          gr.GR_PATH_TILE_STREAM) == gr.GR_ERR_INVALID_PATH, (M, N, K)
+    assert gr.gemm_relu_f16_bt_forced(300, 256, 64, BASE_A, 65, BASE_B + 2, 67, BASE_C, 256, None,
+                                      gr.GR_PATH_TILE_STREAM) not in (gr.GR_ERR_INVALID_PATH, gr.GR_OK)
 
 
 def test_bf16_argument_checks_need_no_gpu():

@@ -54,6 +54,36 @@ def _run(M, N, K, lda, ldb, ldc, offs, path, seed):
     return A, B, C[:, :N]
 
 
+MISALIGNED_A_CASES = [
+    (65, 64, 32, 33, 64, 64, (1, 0, 0)),             # one slot, A's base and pitch odd
+    (130, 200, 96, 97, 201, 203, (1, 3, 5)),          # A, B and C misaligned, ragged edges
+    (1000, 1000, 1024, 1025, 1000, 1000, (3, 0, 0)),  # long K, A's rows 2-byte aligned only
+    (300, 520, 512, 516, 520, 520, (2, 0, 0)),        # A's rows 8-byte aligned
+]
+
+
+@pytest.mark.parametrize("M,N,K,lda,ldb,ldc,offs", MISALIGNED_A_CASES)
+def test_tile_stream_parity_misaligned_a(M, N, K, lda, ldb, ldc, offs):
+    """The streaming kernel copies A's rows from any 2-byte aligned address:
+    full oracle check with A's and B's padding poisoned with 65504."""
+    A, B = synth.random_operands(M, N, K, seed=M * 13 + N + K, lda=lda, ldb=ldb)
+    A = A.copy()
+    A.reshape(M, lda)[:, K:] = 0x7BFF
+    Ap = np.concatenate([np.full(offs[0], 0x7BFF, np.uint16), A.ravel()])
+    Bp = np.concatenate([np.full(offs[1], 0x7BFF, np.uint16), B.ravel()])
+    dC = full_dev((offs[2] + (M + 2) * ldc,), SENTINEL)
+    log("tile_stream misaligned A %dx%dx%d lda=%d ldb=%d ldc=%d offs=%s" % (M, N, K, lda, ldb, ldc, offs))
+    st = call(M, N, K, to_dev(Ap), lda, to_dev(Bp), ldb, dC, ldc, path=gr.GR_PATH_TILE_STREAM, offsets=offs)
+    assert st == gr.GR_OK, gr.gemm_relu_status_string(st)
+    Cflat = from_dev(dC)
+    C = Cflat[offs[2]:offs[2] + M * ldc].reshape(M, ldc)
+    assert np.all(Cflat[:offs[2]] == SENTINEL), "an element before C was written"
+    assert np.all(C[:, N:] == SENTINEL), "a padding column of C was written"
+    assert np.all(Cflat[offs[2] + M * ldc:] == SENTINEL), "a row past M was written"
+    ref = oracle.gemm_relu_full(A, B, M=M, N=N, K=K, lda=lda, ldb=ldb)
+    log("parity %s" % (assert_parity(C[:, :N], ref, "tile_stream misaligned A %dx%dx%d" % (M, N, K)),))
+
+
 @pytest.mark.parametrize("M,N,K,lda,ldb,ldc,offs", CASES)
 def test_tile_stream_parity(M, N, K, lda, ldb, ldc, offs):
     """Forced row-blocked streaming path on padded, misaligned operands: full
@@ -133,12 +163,14 @@ def test_planned_tile_stream_matches_oracle(M, N, K, ldb):
 
 
 BT_CASES = [
-    # M, N, K, lda, ldbt, ldc, element offsets of A, Bt, C (16-byte rows of A and Bt)
+    # M, N, K, lda, ldbt, ldc, element offsets of A, Bt, C
     (17, 64, 32, 32, 32, 64, (0, 0, 0)),             # one row block of 17 rows, one slot
     (130, 65, 64, 64, 72, 70, (0, 8, 3)),            # last column block moved left, Bt padded
     (1000, 1000, 1024, 1032, 1024, 1005, (8, 0, 1)),  # ragged M and N, C misaligned
     (300, 300, 96, 104, 104, 300, (0, 16, 0)),        # 3 slots
     (64, 128, 4096, 4096, 4096, 128, (0, 0, 0)),      # one row block, long K
+    (130, 65, 64, 65, 67, 70, (1, 1, 0)),             # rows of A and Bt 2-byte aligned only
+    (300, 300, 96, 97, 99, 300, (3, 5, 0)),           # odd pitches and offsets
 ]
 
 

@@ -131,15 +131,16 @@ def test_ragged_workload_runs_in_place_with_or_without_workspace():
 
 
 @pytest.mark.parametrize("M,N,K,lda,ldb,offs", [
-    (512, 512, 512, 512, 512, (1, 0, 0)),     # A's base pointer misaligned
+    (512, 512, 500, 500, 512, (1, 0, 0)),     # A's base pointer misaligned, ragged K
     (300, 300, 300, 300, 300, (0, 0, 0)),     # 600-byte rows: 8-byte aligned only
     (1000, 700, 1000, 1001, 700, (0, 0, 0)),  # ragged K, odd pitch of A
     (256, 2000, 130, 130, 2003, (0, 3, 0)),   # one tile row, tail 2, B misaligned
 ])
 def test_plain_call_takes_the_unaligned_kernel_on_misaligned_mid_size_problems(M, N, K, lda, ldb, offs):
-    """Without a workspace, misaligned rows or a ragged K with M, N >= 256 and
-    K > 128 run on the unaligned kernel in place (the guarded kernel was 2-5x
-    slower there): full oracle check."""
+    """Without a workspace, a ragged K (which the streaming kernel cannot
+    take) with M, N >= 256 and K > 128 runs on the unaligned kernel in place,
+    whatever the rows' alignment (the guarded kernel was 2-5x slower there):
+    full oracle check."""
     A, B = synth.random_operands(M, N, K, seed=M + 2 * N + K, lda=lda, ldb=ldb)
     Ap = np.concatenate([np.full(offs[0], 0x7BFF, np.uint16), A.ravel()])
     Bp = np.concatenate([np.full(offs[1], 0x7BFF, np.uint16), B.ravel()])
