@@ -265,6 +265,13 @@ bool use_large_tiles(int64_t M, int64_t N) {
 // A and B of any alignment.
 constexpr int64_t kTileStreamRows = 64;  // 4 blocks of 16 rows per workgroup
 constexpr int64_t kTileStreamRound = 512;  // resident blocks: 2 per CU x 256 CUs
+// Up to 256 blocks (one per CU) 8 waves take the slots of a block instead of
+// 4 (128 KiB of LDS: twice the copies in flight per CU).  Measured, back to
+// back: 1024^3 6.93 against 7.32 us, 512 x 1024 x 2048 8.44 against 9.74,
+// 1024^2 x 256 5.05 against 5.39; with 512 blocks they would take two rounds
+// (1024 x 2048 x 1024: 12.41 against 10.15).
+constexpr int kTileStreamWOne = 8;
+int tile_stream_waves(int64_t blocks) { return blocks <= 256 ? kTileStreamWOne : kStreamW; }
 // Workgroup order of the row-blocked grid.  All blocks of a launch that fits
 // one round are resident together, so what counts is how many distinct
 // column blocks of B (and row blocks of A) each XCD's L2 holds.  In plain
@@ -447,8 +454,8 @@ void fill_plan(int path, int64_t M, int64_t N, int64_t K, uintptr_t A, int64_t l
         p->block_n = kStreamNB;
         p->block_k = gr::smallm::KSTEP;
         p->stages = kStreamR;
-        p->threads = 64 * kStreamW;
         p->grid = ((N + kStreamNB - 1) / kStreamNB) * ((M + kTileStreamRows - 1) / kTileStreamRows);
+        p->threads = 64 * tile_stream_waves(p->grid);
         p->vec_a = 8;
         p->vec_b = 8;  // 16-byte copies from any 2-byte address
         p->vec_c = 1;
@@ -744,6 +751,11 @@ int run(const gr_plan_t& p, int64_t M, int64_t N, int64_t K, const uint16_t* A, 
             using namespace gr::smallm;
             const uint32_t nb = (uint32_t)((N + kStreamNB - 1) / kStreamNB);
             static_assert(kTileStreamRows == 4 * MAX_M, "4 blocks of 16 rows per workgroup");
+            if (p.threads == 64 * kTileStreamWOne)
+                return launch(
+                    gemm_relu_smallm_stream_kernel<kStreamNB, kTileStreamWOne, kStreamR, stream::WHOLE, E, false, 4, true>,
+                    p.grid, p.threads, stream, A, B, C, static_cast<float*>(nullptr), M, N, K, lda, ldb, ldc, K, nb,
+                    order_word(p), ep);
             return launch(gemm_relu_smallm_stream_kernel<kStreamNB, kStreamW, kStreamR, stream::WHOLE, E, false, 4, true>,
                           p.grid, p.threads, stream, A, B, C, static_cast<float*>(nullptr), M, N, K, lda, ldb, ldc, K,
                           nb, order_word(p), ep);
@@ -1089,6 +1101,11 @@ int run_bt(const gr_plan_t& p, int64_t M, int64_t N, int64_t K, const uint16_t* 
         case GR_PATH_TILE_STREAM: {
             using namespace gr::smallm;
             const uint32_t nb = (uint32_t)((N + kStreamNB - 1) / kStreamNB);
+            if (p.threads == 64 * kTileStreamWOne)
+                return launch(gemm_relu_smallm_stream_kernel<kStreamNB, kTileStreamWOne, kStreamR, stream::WHOLE, E, false,
+                                                             4, true, true>,
+                              p.grid, p.threads, stream, A, Bt, C, static_cast<float*>(nullptr), M, N, K, lda, ldbt, ldc,
+                              K, nb, order_word(p), ep);
             return launch(
                 gemm_relu_smallm_stream_kernel<kStreamNB, kStreamW, kStreamR, stream::WHOLE, E, false, 4, true, true>,
                 p.grid, p.threads, stream, A, Bt, C, static_cast<float*>(nullptr), M, N, K, lda, ldbt, ldc, K, nb,
