@@ -238,12 +238,12 @@ bool use_large_tiles(int64_t M, int64_t N) {
 }
 
 // Blocks of 64 rows x 64 columns on the streaming kernel (TILE_STREAM): in
-// each workgroup the 4 waves take the 32-row slots of K in turn through
-// rings of their own, with no barrier in the loop, and add their partial
-// sums in LDS at the end.  Against 128 x 128 tiles this gives four times as
-// many workgroups and a quarter of the K steps per wave.  A block holds 64
-// KiB of LDS, so two are resident per CU and 512 fill one round of the 256
-// CUs.  Where it is planned (blocks = ceil(M / 64) x ceil(N / 64); us, back
+// each workgroup the waves (4, or 8 up to 256 blocks: tile_stream_waves)
+// take the 32-row slots of K in turn through rings of their own, with no
+// barrier in the loop, and add their partial sums in LDS at the end.
+// Against 128 x 128 tiles this gives four times as many workgroups and a
+// quarter of the K steps per wave.  A 4-wave block holds 64 KiB of LDS, so
+// two are resident per CU and 512 fill one round of the 256 CUs.  Where it is planned (blocks = ceil(M / 64) x ceil(N / 64); us, back
 // to back):
 //  * aligned rows, against the 128 x 128 tile kernel: blocks <= 256 from
 //    K = 256 (1024^3 7.4 against 12.3, 1024^2 x 256 5.4 against 5.6; at

@@ -115,8 +115,8 @@ extern "C" {
                                   /* (TileLang tutorial, "Persistent kernel"); whole tiles, */
                                   /* K % 64 == 0, 16-byte rows of A and B                  */
 #define GR_PATH_TILE_STREAM 9 /* blocks of 64 rows x 64 columns on the streaming kernel:  */
-                              /* the block's 4 waves split K between them (rings of      */
-                              /* direct-to-LDS copies of their own, no barrier in the    */
+                              /* the block's 4 waves (8 up to 256 blocks) split K (rings */
+                              /* of direct-to-LDS copies of their own, no barrier in the */
                               /* loop) and add their partial sums in order at the end;   */
                               /* K % 32 == 0, N >= 64, rows of A and B of any alignment; */
                               /* blocks placed for L2 reuse per XCD                     */
@@ -356,7 +356,7 @@ int gemm_relu_f16_plan_ws(int64_t M, int64_t N, int64_t K,
  *                     they stand;
  *   GR_PATH_TILE_STREAM  M > 16, K % 32 == 0, N >= 64, rows of A and Bt
  *                     of any alignment: the row-blocked streaming kernel (64 x
- *                     64 blocks, K split between a block's 4 waves) with
+ *                     64 blocks, K split between a block's 4 or 8 waves) with
  *                     blocks of 16 rows of Bt copied and read like those of
  *                     A; the planner takes it for up to 256 blocks from K =
  *                     256 and up to 512 from K = 1024, and at any size when

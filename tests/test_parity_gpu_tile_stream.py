@@ -1,15 +1,15 @@
 """GPU parity of the row-blocked streaming path (GR_PATH_TILE_STREAM) against
 the CPU oracle.
 
-Blocks of 64 rows x 64 columns of C, one per workgroup; the workgroup's four
-waves take the 32-row slots of K in turn through rings of direct-to-LDS
-copies of their own and add their fp32 partial sums in wave order at the
-end, so ReLU sees the complete sum (the split-K of the TileLang tutorial's
-chapter "性能取证", kept inside one workgroup).  The planner takes it for few
-blocks with K long enough (e.g. the 1024^3 workload) and, for B's rows
-misaligned, up to one or two rounds of blocks; the workgroup order (plain
-row-major, or XCD renumbering with groups of 4 row blocks) never changes a
-bit.
+Blocks of 64 rows x 64 columns of C, one per workgroup; the workgroup's
+waves (4, or 8 up to 256 blocks) take the 32-row slots of K in turn through
+rings of direct-to-LDS copies of their own and add their fp32 partial sums
+in wave order at the end, so ReLU sees the complete sum (the split-K of the
+TileLang tutorial's chapter "性能取证", kept inside one workgroup).  The
+planner takes it for few blocks with K long enough (e.g. the 1024^3
+workload) and, for misaligned rows, up to one or two rounds of blocks; the
+workgroup order (plain row-major, or XCD renumbering with groups of 4 row
+blocks) never changes a bit.
 Bar: |gpu - oracle| <= 1e-2 + 1e-2 |oracle| per element, no NaN or Inf,
 C's padding and rows past M untouched.
 """
@@ -28,10 +28,10 @@ SENTINEL = 0x7E5A
 # M, N, K, lda, ldb, ldc, element offsets of A, B, C (A's rows 16-byte
 # aligned: lda and A's offset multiples of 8)
 CASES = [
-    (65, 64, 32, 32, 64, 64, (0, 0, 0)),            # 2 row blocks (the second 1 row), 1 slot: 3 idle waves
+    (65, 64, 32, 32, 64, 64, (0, 0, 0)),            # 2 row blocks (the second 1 row), 1 slot: 7 idle waves
     (130, 65, 64, 64, 65, 70, (0, 1, 3)),           # last column block moved left to column 1, B odd pitch
     (1000, 1000, 1024, 1032, 1003, 1005, (8, 3, 1)),  # ragged M and N, B and C misaligned
-    (200, 300, 96, 104, 301, 300, (0, 5, 0)),        # 3 slots, 4 waves
+    (200, 300, 96, 104, 301, 300, (0, 5, 0)),        # 3 slots, 8 waves (5 idle)
     (64, 128, 4096, 4096, 128, 128, (0, 0, 0)),      # one row block, long K
     (513, 200, 160, 168, 200, 203, (16, 0, 2)),      # 5 slots, a 1-row last block
 ]
