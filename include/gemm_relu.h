@@ -439,11 +439,14 @@ int gemm_relu_f16_ta_forced(int64_t M, int64_t N, int64_t K,
  * CUDA core", names fp16 and bf16 as the inputs a GEMM feeds to the matrix
  * engines; the epilogue is the one defined above.  Every convention above
  * holds (layouts, pitches, edges, errors, streams); the paths are those of
- * gemm_relu_f16 without a workspace:
- *   GR_PATH_SMALL_M   M <= 16, 16-byte rows of A and B;
- *   GR_PATH_TILE      16-byte rows of A and B, K % 32 == 0 (256x256 or
- *                     128x128 tiles, as for fp16);
- *   GR_PATH_TILE_EDGE everything else (guarded register-staged kernel).
+ * gemm_relu_f16 without a workspace, chosen by the same rules:
+ *   GR_PATH_SMALL_M        M <= 64, the small-M kernels;
+ *   GR_PATH_TILE_STREAM    64 x 64 blocks on the streaming kernel (few
+ *                          blocks; rows of any alignment, K % 32 == 0);
+ *   GR_PATH_TILE           16-byte rows of A and B, K % 32 == 0 (256x256 or
+ *                          128x128 tiles);
+ *   GR_PATH_TILE_UNALIGNED misaligned rows or K % 64 != 0, in place;
+ *   GR_PATH_TILE_EDGE      everything else (guarded register-staged kernel).
  * gemm_relu_f16_plan describes the plan these calls follow (the path does not
  * depend on the element format).  gemm_relu_bf16_ws takes a caller workspace
  * exactly like gemm_relu_f16_ws (same sizes: gemm_relu_f16_workspace_size)
