@@ -297,6 +297,17 @@ int64_t tile_stream_blocks(int64_t M, int64_t N) {
 bool tile_stream_beats_tiles(int64_t blocks, int64_t K) {
     return (blocks <= 256 && K >= 256) || (blocks <= kTileStreamRound && K >= 512);
 }
+// With a workspace the split-K tile path usually beats the streaming path
+// (1024^2 x 8192: 30.2 against 32.5 us; 512 x 1024 x 8192, 128 blocks: 22.0
+// against 30.5), but where the streaming path fills every CU with one 8-wave
+// block (129-256 blocks) up to K = 4096 it is the faster one (1024^2 x 4096:
+// 18.9 against 20.6; 128 x 8192 x 4096: 18.9 against 23.2).  There the
+// planner streams and asks for no workspace.
+bool tile_stream_before_split(int64_t M, int64_t N, int64_t K, int64_t lda, int64_t ldb) {
+    const int64_t blocks = tile_stream_blocks(M, N);
+    return M > kSmallMMaxRows && tile_stream_ok(M, N, K, lda, ldb) && blocks > 128 && blocks <= 256 && K <= 4096 &&
+           tile_stream_beats_tiles(blocks, K);
+}
 
 bool tile_unaligned_ok(int64_t M, int64_t N, int64_t K, int64_t lda, int64_t ldb) {
     using namespace gr::tile3;
@@ -493,8 +504,8 @@ int choose_path(int64_t M, int64_t N, int64_t K, uintptr_t A, int64_t lda, uintp
         return GR_PATH_SMALL_M;
     }
     const bool fast = tile_fast_ok(M, N, K, A, lda, B, ldb);
-    if (fast && ws_bytes > 0 && !use_large_tiles(M, N) && tile_split_layout(M, N, K, false, ts) &&
-        ts->bytes <= ws_bytes)
+    if (fast && ws_bytes > 0 && !use_large_tiles(M, N) && !tile_stream_before_split(M, N, K, lda, ldb) &&
+        tile_split_layout(M, N, K, false, ts) && ts->bytes <= ws_bytes)
         return GR_PATH_TILE_SPLIT;
     if (K > 0 &&
         (smallm_rows_ok(M, N, K, A, lda, B, ldb) || smallm_stream_ok(M, N, K, A, lda, ldb, kStreamNB, kSmallMMaxRows)) &&
@@ -1797,7 +1808,9 @@ int gemm_relu_f16_workspace_size(int64_t M, int64_t N, int64_t K, const uint16_t
     if (K > 0 && (smallm_ok(M, N, K, a, lda, b, ldb) || smallm_stream_ok(M, N, K, a, lda, ldb, kStreamNB))) {
         if (smallm_split_layout(M, N, K, a, lda, b, ldb, &sp) && smallm_split_wanted(N, sp)) *bytes = sp.bytes;
     } else if (tile_fast_ok(M, N, K, a, lda, b, ldb)) {
-        if (!use_large_tiles(M, N) && tile_split_layout(M, N, K, false, &ts)) *bytes = ts.bytes;
+        if (!use_large_tiles(M, N) && !tile_stream_before_split(M, N, K, lda, ldb) &&
+            tile_split_layout(M, N, K, false, &ts))
+            *bytes = ts.bytes;
     } else if (tile_unaligned_ok(M, N, K, lda, ldb) && use_large_tiles(M, N)) {
         // the pipelined kernel runs in place on these rows: no workspace
     } else if (M > kSmallMMaxRows && tile_stream_ok(M, N, K, lda, ldb) &&

@@ -420,8 +420,14 @@ def test_tile_split_plan():
     st, p = plan_ws(1024, 1024, 16384, size)
     assert p["path"] == gr.GR_PATH_TILE_SPLIT and p["split_k"] == 4 and p["grid"] == 256
     assert p["block_m"] == 128 and p["workspace"] == size
-    # K = 4096: 4 splits of 1024 save 96 of 128 strips per workgroup
-    assert plan_ws(1024, 1024, 4096, 1 << 30)[1]["split_k"] == 4
+    # K = 8192: 4 splits of 2048 save 192 of 256 strips per workgroup
+    assert plan_ws(1024, 1024, 8192, 1 << 30)[1]["split_k"] == 4
+    # up to K = 4096 with 129-256 blocks of 64 x 64 the streaming path (8
+    # waves per block, every CU) is faster: no workspace is asked for
+    assert ws_size(1024, 1024, 4096) == (gr.GR_OK, 0)
+    assert plan_ws(1024, 1024, 4096, 1 << 30)[1]["path"] == gr.GR_PATH_TILE_STREAM
+    assert plan_ws(128, 8192, 4096, 1 << 30)[1]["path"] == gr.GR_PATH_TILE_STREAM
+    assert plan_ws(512, 1024, 4096, 1 << 30)[1]["path"] == gr.GR_PATH_TILE_SPLIT  # 128 blocks
     # 128 tiles: 2 splits; at K = 4096 they save 64 of 128 strips, just enough
     assert plan_ws(256, 8192, 4096, 1 << 30)[1]["split_k"] == 2
     # at K = 2048 two splits save too little: the streaming kernel (512
