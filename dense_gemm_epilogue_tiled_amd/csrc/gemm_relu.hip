@@ -309,6 +309,23 @@ bool tile_stream_before_split(int64_t M, int64_t N, int64_t K, int64_t lda, int6
            tile_stream_beats_tiles(blocks, K);
 }
 
+// Up to 64 rows of A without a split: one row of 64 x 64 blocks on the
+// streaming kernel (8 waves per block up to 256 blocks: twice the copies in
+// flight of the small-M kernel's 4) where its blocks leave most CUs idle and
+// B is large enough for that to count.  Measured back to back (us, small-M
+// kernel / streaming): 64 x 4096 x 4096 30.5 / 19.1, 16 x 4096 x 4096 19.8 /
+// 14.5, 8 x 2048 x 4096 16.4 / 12.7, 8 x 8192 x 1024 6.53 / 6.06, 64 x 1024
+// x 256 5.00 / 4.90; but 8 x 1024 x 2048 5.85 / 7.55, 16 x 8192 x 512 4.34 /
+// 4.97, and with 256 blocks and B cold 8 x 16384 x 8192 46.4 / 51.9.
+bool tile_stream_small_m_pays(int64_t M, int64_t N, int64_t K, int64_t lda, int64_t ldb) {
+    if (!tile_stream_ok(M, N, K, lda, ldb)) return false;
+    const int64_t blocks = tile_stream_blocks(M, N);
+    if (blocks > 128) return false;
+    if (M > 32) return true;
+    const double kn = (double)K * (double)N;
+    return N >= 1024 && kn >= 8388608.0 && (blocks <= 64 || kn <= 33554432.0);
+}
+
 bool tile_unaligned_ok(int64_t M, int64_t N, int64_t K, int64_t lda, int64_t ldb) {
     using namespace gr::tile3;
     return M >= BM && N >= BN && K > 2 * BKA && lda <= MAX_LDA && ldb <= MAX_LDB;
@@ -501,7 +518,7 @@ int choose_path(int64_t M, int64_t N, int64_t K, uintptr_t A, int64_t lda, uintp
         if (ws_bytes > 0 && smallm_split_layout(M, N, K, A, lda, B, ldb, sp) && smallm_split_wanted(N, *sp) &&
             sp->bytes <= ws_bytes)
             return GR_PATH_SMALL_M_SPLIT;
-        return GR_PATH_SMALL_M;
+        return tile_stream_small_m_pays(M, N, K, lda, ldb) ? GR_PATH_TILE_STREAM : GR_PATH_SMALL_M;
     }
     const bool fast = tile_fast_ok(M, N, K, A, lda, B, ldb);
     if (fast && ws_bytes > 0 && !use_large_tiles(M, N) && !tile_stream_before_split(M, N, K, lda, ldb) &&
@@ -510,8 +527,12 @@ int choose_path(int64_t M, int64_t N, int64_t K, uintptr_t A, int64_t lda, uintp
     if (K > 0 &&
         (smallm_rows_ok(M, N, K, A, lda, B, ldb) || smallm_stream_ok(M, N, K, A, lda, ldb, kStreamNB, kSmallMMaxRows)) &&
         (N + gr::smallm::NB - 1) / gr::smallm::NB <= 256)
-        return GR_PATH_SMALL_M;
-    const bool stream = M > kSmallMMaxRows && tile_stream_ok(M, N, K, lda, ldb);
+        return tile_stream_small_m_pays(M, N, K, lda, ldb) ? GR_PATH_TILE_STREAM : GR_PATH_SMALL_M;
+    // Up to 64 rows reach here when the small-M kernels cannot take A's rows
+    // (not 16-byte aligned): the streaming kernel takes them in place (8 x
+    // 4096 x 4096 with A's rows odd: 14.3 us against 182 for the guarded
+    // kernel; 64 x 16384 x 4096 29.0 against 215).
+    const bool stream = (M > kSmallMMaxRows || !fast) && tile_stream_ok(M, N, K, lda, ldb);
     const int64_t blocks = stream ? tile_stream_blocks(M, N) : 0;
     if (stream && (fast ? tile_stream_beats_tiles(blocks, K) : blocks <= kTileStreamRound))
         return GR_PATH_TILE_STREAM;
@@ -1813,8 +1834,7 @@ int gemm_relu_f16_workspace_size(int64_t M, int64_t N, int64_t K, const uint16_t
             *bytes = ts.bytes;
     } else if (tile_unaligned_ok(M, N, K, lda, ldb) && use_large_tiles(M, N)) {
         // the pipelined kernel runs in place on these rows: no workspace
-    } else if (M > kSmallMMaxRows && tile_stream_ok(M, N, K, lda, ldb) &&
-               tile_stream_blocks(M, N) <= kTileStreamRound) {
+    } else if (tile_stream_ok(M, N, K, lda, ldb) && tile_stream_blocks(M, N) <= kTileStreamRound) {
         // one round of the streaming kernel, planned ahead of the packed copy
     } else if (pack_layout(M, N, K, a, lda, b, ldb, &pk)) {
         *bytes = pk.bytes;

@@ -127,7 +127,11 @@ extern "C" {
                               /* 512, and 1024 when no workspace lets the operands be    */
                               /* packed (few tiles: the split-K                          */
                               /* remedy of the TileLang tutorial's "性能取证", within one */
-                              /* workgroup); no workspace                                 */
+                              /* workgroup); no workspace.  Up to 64 rows without a     */
+                              /* split: one row of blocks where the small-M kernel's    */
+                              /* few blocks would leave CUs idle (at most 128 blocks;   */
+                              /* more than 32 rows, or K x N >= 2^23 with N >= 1024),   */
+                              /* and whenever A's rows are not 16-byte aligned          */
 
 /* What the planner decided for one problem.  Filled by gemm_relu_f16_plan. */
 typedef struct gr_plan_t {
@@ -442,7 +446,8 @@ int gemm_relu_f16_ta_forced(int64_t M, int64_t N, int64_t K,
  * gemm_relu_f16 without a workspace, chosen by the same rules:
  *   GR_PATH_SMALL_M        M <= 64, the small-M kernels;
  *   GR_PATH_TILE_STREAM    64 x 64 blocks on the streaming kernel (few
- *                          blocks; rows of any alignment, K % 32 == 0);
+ *                          blocks, also one row of them for M <= 64; rows
+ *                          of any alignment, K % 32 == 0);
  *   GR_PATH_TILE           16-byte rows of A and B, K % 32 == 0 (256x256 or
  *                          128x128 tiles);
  *   GR_PATH_TILE_UNALIGNED misaligned rows or K % 64 != 0, in place;

@@ -165,8 +165,11 @@ def test_plan_tile_stream_where_128_tiles_are_few():
     # more than one round of blocks: the 128 x 128 (or 256 x 256) tile kernel
     for M, N, K in ((1088, 2048, 1024), (2048, 2048, 2048), (4096, 4096, 4096)):
         assert plan(M, N, K)[1]["path"] == gr.GR_PATH_TILE, (M, N, K)
-    # up to 64 rows: the small-M path
-    assert plan(64, 1024, 1024)[1]["path"] == gr.GR_PATH_SMALL_M
+    # up to 64 rows: the small-M path, or one row of streaming blocks where
+    # they pay (more than 32 rows, or K x N large enough)
+    assert plan(16, 1024, 1024)[1]["path"] == gr.GR_PATH_SMALL_M
+    st, p = plan(64, 1024, 1024)
+    assert (p["path"], p["grid"], p["threads"]) == (gr.GR_PATH_TILE_STREAM, 16, 512)
     # what the streaming kernel cannot take goes elsewhere: K % 32 != 0, N < 64
     assert plan(1024, 1024, 1000)[1]["path"] != gr.GR_PATH_TILE_STREAM
     assert plan(1024, 48, 1024)[1]["path"] != gr.GR_PATH_TILE_STREAM
@@ -380,9 +383,12 @@ def test_small_m_split_plan():
     st, p = plan_ws(8, 4096, 8192, size)
     assert p["path"] == gr.GR_PATH_SMALL_M_SPLIT and p["split_k"] == 8 and p["grid"] == 256
     assert p["workspace"] == size and p["block_n"] == 128
-    # too small a workspace, or none: the single-pass small-M kernel
-    assert plan_ws(8, 4096, 8192, size - 1)[1]["path"] == gr.GR_PATH_SMALL_M
-    assert plan(8, 4096, 8192)[1]["path"] == gr.GR_PATH_SMALL_M
+    # too small a workspace, or none: one row of 64 x 64 blocks on the
+    # streaming kernel (64 blocks of 8 waves); with a shorter K the
+    # single-pass small-M kernel
+    assert plan_ws(8, 4096, 8192, size - 1)[1]["path"] == gr.GR_PATH_TILE_STREAM
+    assert plan(8, 4096, 8192)[1]["path"] == gr.GR_PATH_TILE_STREAM
+    assert plan(8, 4096, 1024)[1]["path"] == gr.GR_PATH_SMALL_M
     # the small-M workload: 128 column blocks x 2 splits (256-byte row pieces
     # over half of K each)
     st, size = ws_size(8, 16384, 8192)
@@ -394,7 +400,8 @@ def test_small_m_split_plan():
     # B needs no alignment on the streaming kernels
     assert ws_size(8, 4096, 8192, b=BASE_B + 8)[1] == 8 * 8 * 4096 * 4
     assert ws_size(8, 4096, 8192, ldb=4100)[1] == 8 * 8 * 4096 * 4
-    assert plan(8, 4096, 8192, b=BASE_B + 2)[1]["path"] == gr.GR_PATH_SMALL_M
+    assert plan(8, 4096, 8192, b=BASE_B + 2)[1]["path"] == gr.GR_PATH_TILE_STREAM
+    assert plan(8, 4096, 1024, b=BASE_B + 2)[1]["path"] == gr.GR_PATH_SMALL_M
     # K of fewer than four 32-deep steps is not split
     assert ws_size(8, 4096, 96) == (gr.GR_OK, 0)
     # K % 32 != 0: the register-staged split (256-column blocks, 16-byte rows
@@ -491,10 +498,44 @@ def test_plan_empty_and_k_zero():
 
 
 def test_plan_small_m_threshold():
-    assert plan(16, 4096, 4096)[1]["path"] == gr.GR_PATH_SMALL_M
-    assert plan(17, 4096, 4096)[1]["path"] == gr.GR_PATH_SMALL_M   # two row blocks
-    assert plan(64, 4096, 4096)[1]["path"] == gr.GR_PATH_SMALL_M   # four row blocks
+    assert plan(16, 4096, 512)[1]["path"] == gr.GR_PATH_SMALL_M
+    assert plan(17, 4096, 512)[1]["path"] == gr.GR_PATH_SMALL_M    # two row blocks
+    assert plan(64, 16384, 4096)[1]["path"] == gr.GR_PATH_SMALL_M  # four row blocks, 256 of them
     assert plan(65, 4096, 4096)[1]["path"] == gr.GR_PATH_TILE_STREAM  # 64 x 64 blocks
+
+
+@pytest.mark.parametrize("M,N,K,stream", [
+    (16, 4096, 4096, True), (17, 4096, 4096, True), (64, 4096, 4096, True), (1, 2048, 4096, True),
+    (32, 8192, 1024, True), (32, 8192, 4096, True), (32, 8192, 8192, False),  # 128 blocks: B up to 64 MiB
+    (8, 1024, 2048, False), (8, 1024, 8192, True), (8, 512, 32768, False),   # K x N >= 2^23, N >= 1024
+    (33, 256, 256, True), (64, 8192, 256, True), (64, 8256, 4096, False),    # more than 32 rows: 128 blocks
+    (16, 4096, 4016, False), (8, 16384, 8192, False)])
+def test_small_m_rows_on_the_streaming_kernel(M, N, K, stream):
+    """Up to 64 rows without a split: one row of streaming blocks (8 waves
+    each) where the small-M kernel's few blocks would leave CUs idle and B is
+    large, else the small-M kernel; a workspace still buys the split."""
+    st, p = plan(M, N, K)
+    assert st == gr.GR_OK
+    if stream:
+        assert (p["path"], p["block_m"], p["grid"], p["threads"]) == (gr.GR_PATH_TILE_STREAM, 64, -(-N // 64), 512)
+    else:
+        assert p["path"] == gr.GR_PATH_SMALL_M, p
+    if M <= 16:
+        st, size = ws_size(M, N, K)
+        if size > 0:
+            assert plan_ws(M, N, K, size)[1]["path"] == gr.GR_PATH_SMALL_M_SPLIT
+
+
+@pytest.mark.parametrize("M,N,K,a_off,lda_pad", [(8, 4096, 4096, 1, 1), (64, 16384, 4096, 1, 1), (32, 1024, 1024, 0, 3),
+                                                 (1, 64, 32, 4, 0)])
+def test_small_m_rows_misaligned_a_on_the_streaming_kernel(M, N, K, a_off, lda_pad):
+    """A's rows not 16-byte aligned: the small-M kernels cannot take them,
+    the streaming kernel does in place, with no workspace asked for."""
+    lda = K + lda_pad
+    a = BASE_A + 2 * a_off
+    st, p = plan(M, N, K, a=a, lda=lda)
+    assert st == gr.GR_OK and p["path"] == gr.GR_PATH_TILE_STREAM, p
+    assert ws_size(M, N, K, a=a, lda=lda) == (gr.GR_OK, 0)
     assert plan(1, 1, 1)[1]["path"] == gr.GR_PATH_TILE_EDGE  # B row pitch 1: not 8-byte aligned
 
 
@@ -534,9 +575,12 @@ def test_planner_invariants_on_random_problems():
             assert 1 <= M <= 64 and K > 0 and p["grid"] == -(-N // 64), key
             assert M <= 16 or -(-N // 64) <= 256, key  # wider C with more rows: the tile kernel
         elif p["path"] == gr.GR_PATH_TILE_STREAM:
-            assert M > 64 and K > 0 and K % 32 == 0 and N >= 64, key
+            assert K > 0 and K % 32 == 0 and N >= 64, key
             blocks = -(-M // 64) * -(-N // 64)
-            if aligned:  # few blocks, K long enough to beat the 128 x 128 tiles
+            if M <= 64 and a % 16 == 0 and lda % 8 == 0 and -(-N // 64) <= 256:
+                # the small-M kernel's rows: one row of blocks, where it pays
+                assert blocks <= 128 and (M > 32 or N >= 1024), key
+            elif aligned:  # few blocks, K long enough to beat the 128 x 128 tiles
                 assert (blocks <= 256 and K >= 256) or (blocks <= 512 and K >= 512), key
             else:  # rows misaligned: one round, or two without a workspace
                 assert blocks <= 1024, key

@@ -31,6 +31,8 @@ def planned_agrees(planned, path):
         return planned in (gr.GR_PATH_TILE, gr.GR_PATH_TILE_STREAM)
     if path == gr.GR_PATH_TILE_EDGE:
         return planned in (gr.GR_PATH_TILE_EDGE, gr.GR_PATH_TILE_UNALIGNED, gr.GR_PATH_TILE_STREAM)
+    if path == gr.GR_PATH_SMALL_M:
+        return planned in (gr.GR_PATH_SMALL_M, gr.GR_PATH_TILE_STREAM)
     return planned == path
 
 

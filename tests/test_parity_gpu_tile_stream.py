@@ -262,3 +262,26 @@ def test_bf16_plain_call_takes_tile_stream():
     ref = as_f64(oracle.gemm_relu_elems(A, B, ii, jj, fmt="bf16"), "bf16")
     err = np.abs(got - ref)
     assert np.all(err <= 1e-2 + 1e-2 * np.abs(ref)), float(err.max())
+
+
+SMALL_M_ROWS_CASES = [
+    # M, N, K, lda, ldb, ldc, offs: up to 64 rows planned onto one row of streaming blocks
+    (8, 1024, 8192, 8192, 1024, 1024, (0, 0, 0)),    # K x N = 2^23: 16 blocks of 8 waves, 32 slots each
+    (64, 1024, 1024, 1024, 1024, 1024, (0, 0, 0)),   # more than 32 rows
+    (40, 1100, 512, 512, 1100, 1103, (0, 2, 1)),     # ragged N, B and C misaligned
+    (5, 200, 96, 97, 200, 200, (1, 0, 0)),           # A's rows odd: the small-M kernels cannot take them
+    (33, 2048, 1024, 1030, 2056, 2048, (3, 8, 0)),   # A's rows 4-byte aligned, padded B
+]
+
+
+@pytest.mark.parametrize("M,N,K,lda,ldb,ldc,offs", SMALL_M_ROWS_CASES)
+def test_planned_small_m_rows_on_tile_stream(M, N, K, lda, ldb, ldc, offs):
+    """The plain call plans the streaming kernel for these few-row shapes
+    (rows past M read row M - 1 and are never stored): full oracle check,
+    canaries around C."""
+    base = (0x100000 + 2 * offs[0], 0x200000000000 + 2 * offs[1], 0x400000000000 + 2 * offs[2])
+    st, p = gr.gemm_relu_f16_plan(M, N, K, base[0], lda, base[1], ldb, base[2], ldc)
+    assert st == gr.GR_OK and p["path"] == gr.GR_PATH_TILE_STREAM, p
+    A, B, C = _run(M, N, K, lda, ldb, ldc, offs, None, seed=M * 13 + N + K)
+    ref = oracle.gemm_relu_full(A, B, M=M, N=N, K=K, lda=lda, ldb=ldb)
+    log("parity %s" % (assert_parity(C, ref, "planned few-row tile_stream %dx%dx%d" % (M, N, K)),))
