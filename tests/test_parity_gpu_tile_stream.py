@@ -285,3 +285,28 @@ def test_planned_small_m_rows_on_tile_stream(M, N, K, lda, ldb, ldc, offs):
     A, B, C = _run(M, N, K, lda, ldb, ldc, offs, None, seed=M * 13 + N + K)
     ref = oracle.gemm_relu_full(A, B, M=M, N=N, K=K, lda=lda, ldb=ldb)
     log("parity %s" % (assert_parity(C, ref, "planned few-row tile_stream %dx%dx%d" % (M, N, K)),))
+
+
+def test_bf16_plain_call_few_rows_takes_tile_stream():
+    """gemm_relu_bf16 with 24 rows and few columns (K x N = 2^23) plans one row
+    of streaming blocks, as for fp16, and matches the oracle's bfloat16
+    result on sampled elements; rows past M stay untouched."""
+    import torch as t
+    M, N, K = 24, 2048, 4096
+    st, p = gr.gemm_relu_f16_plan(M, N, K, 0x100000, K, 0x200000000000, N, 0x400000000000, N)
+    assert st == gr.GR_OK and p["path"] == gr.GR_PATH_TILE_STREAM, p
+    A, B = synth.random_operands(M, N, K, seed=24, fmt="bf16")
+    dA, dB = to_dev(A), to_dev(B)
+    dC = full_dev(((M + 1) * N,), SENTINEL)
+    log("bf16 few-row tile_stream %dx%dx%d" % (M, N, K))
+    st = gr.gemm_relu_bf16(M, N, K, dA.data_ptr(), K, dB.data_ptr(), N, dC.data_ptr(), N,
+                           t.cuda.current_stream().cuda_stream)
+    t.cuda.synchronize()
+    assert st == gr.GR_OK
+    Cf = from_dev(dC)
+    assert np.all(Cf[M * N:] == SENTINEL), "a row past M was written"
+    ii, jj = synth.sample_indices(M, N, 4096, 24)
+    got = as_f64(Cf[:M * N].reshape(M, N)[ii, jj], "bf16")
+    ref = as_f64(oracle.gemm_relu_elems(A, B, ii, jj, fmt="bf16"), "bf16")
+    err = np.abs(got - ref)
+    assert np.all(err <= 1e-2 + 1e-2 * np.abs(ref)), float(err.max())
